@@ -1,0 +1,246 @@
+"""Seeded synthetic inputs for the decode step and the prefill indexer.
+
+This module only draws numbers: it holds none of the method's arithmetic, and
+both the CPU oracle and the HIP library receive what it produces.  Every
+array comes from numpy's PCG64 seeded by (seed, array tag), so an array does
+not depend on the order others are drawn in.
+
+Workloads (the synthetic stand-ins for the long-context serving traces the
+ECHO page measures with; real traces and model weights are not used):
+
+  tiny      1 request x 4096 tokens, integer-grid q/k, k=256, pool = half of
+            all tokens (random), full
+  b8_64k    8 x 65536, integer-grid, k=2048, 90% of selected resident, pool
+            = N_H/8, full
+  b32_ragged 32 x U[16384,131072], general FP8 with per-token k scale,
+            k=2048, 70% of selected resident, host pool 8x GPU pool, full
+  prefill_32k  causal 32768 x 32768, integer grid, per-row top-2048
+  b64_128k  64 x 131072, general FP8 with k scale, k=2048, 50% of selected
+            resident, 131072 free slots kept for prefetch
+
+Value recipes:
+  integer grid: q, k uniform integers in [-8, 8] (exact in E4M3FN);
+                w uniform integers in [-4, 4] / 64
+  general:      q, k ~ N(0,1) rounded to E4M3FN (nearest even);
+                w ~ N(0,1)/8; k scale ~ U[0.5, 2]
+  latent rows:  576 bf16 bit patterns per token, uniform random with bit 14
+                cleared (finite, |x| < 2, never the 0xFFFF poison pattern);
+                the recall copies bits, so their distribution is immaterial
+  host slots:   the tokens of all requests occupy a seeded permutation of
+                the host pool
+  pool state:   a given fraction of each request's selected tokens is made
+                resident at random, the rest of the pool is filled with
+                random unselected tokens, occupied slots take distinct
+                random priorities from a permutation of [0, N_G) and the
+                step stamp is N_G; free slots hold the poison pattern
+"""
+
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+
+H_INDEX = 64
+D_INDEX = 128
+ROW_ELEMS = 576
+POISON = 0xFFFF
+INF = 2**31 - 1
+
+_TAGS = {"q": 1, "w": 2, "k": 3, "scale": 4, "len": 5, "perm": 6, "kv": 7,
+         "hit": 8, "fill": 9, "slots": 10, "prio": 11, "scores": 12}
+
+
+def rng_for(seed, tag):
+    return np.random.default_rng([int(seed), _TAGS[tag]])
+
+
+@dataclass
+class DecodeConfig:
+    name: str
+    batch: int
+    lengths: object            # int, or (lo, hi) for uniform per-request lengths
+    topk: int
+    grid: str                  # "int" or "general"
+    k_scale: bool
+    hit_rate: float            # fraction of selected tokens resident before the step
+    pool_div: int              # N_G = ceil(N_H / pool_div)
+    reserve: int = 0           # free slots kept empty (prefetch room)
+    resident_of_all: bool = False   # tiny: residency drawn over all tokens
+    prefetch: bool = False
+    seed: int = 1
+
+
+CONFIGS = {
+    "tiny": DecodeConfig("tiny", 1, 4096, 256, "int", False, 0.5, 2, seed=1,
+                         resident_of_all=True),
+    "b8_64k": DecodeConfig("b8_64k", 8, 65536, 2048, "int", False, 0.9, 8, seed=2),
+    "b32_ragged": DecodeConfig("b32_ragged", 32, (16384, 131072), 2048, "general", True,
+                               0.7, 8, seed=3),
+    "b64_128k": DecodeConfig("b64_128k", 64, 131072, 2048, "general", True, 0.5, 8,
+                             reserve=131072, prefetch=True, seed=5),
+}
+
+PREFILL = {"prefill_32k": dict(n=32768, topk=2048, grid="int", seed=4)}
+
+
+def _int_to_e4m3_table():
+    import torch
+    vals = torch.arange(-8, 9, dtype=torch.float32)
+    return vals.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+def e4m3_from_f32(x):
+    """Round float32 values to E4M3FN bytes (nearest even) with torch's conversion."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def fp8_values(seed, tag, shape, grid, chunk=1 << 26):
+    """uint8 E4M3FN array of the given shape, integer-grid or N(0,1)."""
+    n = int(np.prod(shape))
+    out = np.empty(n, np.uint8)
+    rng = rng_for(seed, tag)
+    table = _int_to_e4m3_table() if grid == "int" else None
+    for s in range(0, n, chunk):
+        m = min(chunk, n - s)
+        if grid == "int":
+            out[s:s + m] = table[rng.integers(0, 17, m, dtype=np.int8)]
+        else:
+            out[s:s + m] = e4m3_from_f32(rng.standard_normal(m, dtype=np.float32))
+    return out.reshape(shape)
+
+
+def head_weights(seed, n, grid):
+    rng = rng_for(seed, "w")
+    if grid == "int":
+        return (rng.integers(-4, 5, (n, H_INDEX)).astype(np.float32) / np.float32(64.0))
+    return (rng.standard_normal((n, H_INDEX), dtype=np.float32) / np.float32(8.0))
+
+
+def request_lengths(cfg):
+    if isinstance(cfg.lengths, (tuple, list)):
+        lo, hi = cfg.lengths
+        return rng_for(cfg.seed, "len").integers(lo, hi + 1, cfg.batch).astype(np.int32)
+    return np.full(cfg.batch, int(cfg.lengths), np.int32)
+
+
+def fill_latent_rows(seed, out, chunk_rows=1 << 18):
+    """Fill a uint16 [N, 576] array (may be pinned host memory) in place."""
+    rng = rng_for(seed, "kv")
+    n = out.shape[0]
+    for s in range(0, n, chunk_rows):
+        m = min(chunk_rows, n - s)
+        out[s:s + m] = rng.integers(0, 1 << 16, (m, ROW_ELEMS), dtype=np.uint16) & np.uint16(0xBFFF)
+    return out
+
+
+@dataclass
+class DecodeInputs:
+    cfg: DecodeConfig
+    q: np.ndarray            # uint8 [B, 64, 128]
+    w: np.ndarray            # float32 [B, 64]
+    k: np.ndarray            # uint8 [sum L, 128]
+    k_scale: object          # float32 [sum L] or None
+    key_begin: np.ndarray    # int64 [B]
+    key_len: np.ndarray      # int32 [B]
+    req_to_host: np.ndarray  # int32 [sum L]
+    n_host: int
+    n_gpu: int
+    extra: dict = field(default_factory=dict)
+
+
+def make_decode_inputs(cfg, lengths=None):
+    """Draw q, w, k, k scale and the token -> host-slot map for a config."""
+    key_len = request_lengths(cfg) if lengths is None else np.asarray(lengths, np.int32)
+    key_begin = np.zeros(len(key_len), np.int64)
+    key_begin[1:] = np.cumsum(key_len.astype(np.int64))[:-1]
+    n_tok = int(key_len.astype(np.int64).sum())
+    q = fp8_values(cfg.seed, "q", (len(key_len), H_INDEX, D_INDEX), cfg.grid)
+    w = head_weights(cfg.seed, len(key_len), cfg.grid)
+    k = fp8_values(cfg.seed, "k", (n_tok, D_INDEX), cfg.grid)
+    k_scale = None
+    if cfg.k_scale:
+        k_scale = rng_for(cfg.seed, "scale").uniform(0.5, 2.0, n_tok).astype(np.float32)
+    req_to_host = rng_for(cfg.seed, "perm").permutation(n_tok).astype(np.int32)
+    n_host = n_tok
+    n_gpu = int(math.ceil(n_host / cfg.pool_div))
+    return DecodeInputs(cfg, q, w, k, k_scale, key_begin, key_len, req_to_host, n_host, n_gpu)
+
+
+@dataclass
+class PoolArrays:
+    free: np.ndarray
+    priority: np.ndarray
+    to_host: np.ndarray
+    host_to_gpu: np.ndarray
+    indices_buf: np.ndarray
+    gpu_kv: np.ndarray
+    step_id: int
+
+
+def make_pool_state(inp, selected, host_kv, hit_rate=None, reserve=None):
+    """Initial pool for one step.
+
+    selected: int [B, k] token indices per request (-1 padded), the set the
+    step will select; a `hit_rate` fraction of each request's selected tokens
+    is made resident, the remaining capacity (minus `reserve` free slots) is
+    filled with random unselected tokens.  For the tiny workload the resident
+    set is a random half of all tokens instead.
+    """
+    cfg = inp.cfg
+    hit_rate = cfg.hit_rate if hit_rate is None else hit_rate
+    reserve = cfg.reserve if reserve is None else reserve
+    n_gpu, n_host = inp.n_gpu, inp.n_host
+    n_tok = inp.k.shape[0]
+    rng_hit, rng_fill = rng_for(cfg.seed, "hit"), rng_for(cfg.seed, "fill")
+    capacity = n_gpu - reserve
+    if cfg.resident_of_all:
+        resident_tok = rng_fill.permutation(n_tok)[:capacity]
+    else:
+        chosen = []
+        is_sel = np.zeros(n_tok, bool)
+        for r in range(selected.shape[0]):
+            s = selected[r][selected[r] >= 0].astype(np.int64) + int(inp.key_begin[r])
+            is_sel[s] = True
+            n_hit = int(round(hit_rate * len(s)))
+            chosen.append(rng_hit.permutation(s)[:n_hit])
+        chosen = np.concatenate(chosen) if chosen else np.zeros(0, np.int64)
+        if len(chosen) > capacity:
+            raise ValueError("pool too small for the requested hit rate")
+        others = np.flatnonzero(~is_sel)
+        n_fill = min(capacity - len(chosen), len(others))
+        filler = others[rng_fill.choice(len(others), n_fill, replace=False)] if n_fill else others[:0]
+        resident_tok = np.concatenate([chosen, filler])
+    hosts = inp.req_to_host[resident_tok].astype(np.int64)
+    slots = rng_for(cfg.seed, "slots").permutation(n_gpu)[:len(hosts)]
+    free = np.ones(n_gpu, np.uint8)
+    priority = np.full(n_gpu, -1, np.int32)
+    to_host = np.full(n_gpu, INF, np.int32)
+    host_to_gpu = np.full(n_host, INF, np.int32)
+    free[slots] = 0
+    to_host[slots] = hosts
+    host_to_gpu[hosts] = slots
+    priority[slots] = rng_for(cfg.seed, "prio").permutation(n_gpu)[:len(slots)]
+    gpu_kv = np.full((n_gpu, ROW_ELEMS), POISON, np.uint16)
+    gpu_kv[slots] = host_kv[hosts]
+    return PoolArrays(free, priority, to_host, host_to_gpu,
+                      np.full(n_gpu, -1, np.int32), gpu_kv, step_id=n_gpu)
+
+
+def random_scores(seed, n_rows, length, tie_frac=0.0, ld=None):
+    """float32 score rows for the top-k alone, with optional planted ties."""
+    rng = rng_for(seed, "scores")
+    ld = length if ld is None else ld
+    s = rng.standard_normal((n_rows, ld), dtype=np.float32)
+    if tie_frac > 0:
+        m = rng.random((n_rows, ld)) < tie_frac
+        s[m] = np.round(s[m] * 4) / 4          # coarse grid -> many equal values
+    return s
+
+
+def make_prefill_inputs(n, grid="int", seed=4):
+    q = fp8_values(seed, "q", (n, H_INDEX, D_INDEX), grid)
+    w = head_weights(seed, n, grid)
+    k = fp8_values(seed, "k", (n, D_INDEX), grid)
+    return q, w, k

@@ -1,0 +1,34 @@
+"""Plain, slow CPU oracle for the DSA-indexer + top-k + pool-residency decode step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or links
+this package; only the test-suite, the smoke check and the CPU-baseline leg of
+the benchmark use it.  It shares no code with the HIP library: it works on
+numpy arrays in float64, with library primitives (matmul, sort) used only as
+single steps of the definition.
+
+Citations name the web page and the section on it:
+
+* "ECHO page" = the blog review "OSDI'26 | ECHO：稀疏 attention 省了算力，
+  却把 HBM 撑爆了" (marsggbo.github.io, 2026-07-29), sections numbered as on
+  that page (§2 concepts, §5.1 metadata, §5.2 in-graph operations, §6.1
+  intra-query prefetching, §6.2 inter-query prefetching).
+
+Readings of points the page leaves open are listed in each module's docstring.
+Parity status of every function is stated in its docstring ("pinned by ...").
+"""
+
+from .fp8 import E4M3FN_TABLE, decode_e4m3fn
+from .scores import index_scores, error_scale, prefill_scores_rows
+from .topk import topk_row, topk_rows, sample_threshold, threshold_bin
+from .pool import (INF, ST_EXHAUSTED, ST_BAD_HOST, ST_DUP_HOST, PoolState,
+                   pool_step, allocate_with_ranks, metadata_bytes,
+                   check_pool_invariants, PoolInvariantError)
+from .decode import decode_step
+
+__all__ = [
+    "E4M3FN_TABLE", "decode_e4m3fn", "index_scores", "error_scale",
+    "prefill_scores_rows", "topk_row", "topk_rows", "sample_threshold",
+    "threshold_bin", "INF", "ST_EXHAUSTED", "ST_BAD_HOST", "ST_DUP_HOST",
+    "PoolState", "pool_step", "allocate_with_ranks", "metadata_bytes",
+    "check_pool_invariants", "PoolInvariantError", "decode_step",
+]
