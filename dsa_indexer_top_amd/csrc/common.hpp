@@ -1,0 +1,85 @@
+// Shared device/host helpers of the HIP library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/echo.h"
+
+#define ECHO_DEV __device__ __forceinline__
+
+namespace echo {
+
+constexpr int H = ECHO_H_INDEX;
+constexpr int D = ECHO_D_INDEX;
+constexpr int ROW = ECHO_ROW_ELEMS;
+constexpr int32_t INF = ECHO_INF;
+
+// ---------------------------------------------------------------- host-side error plumbing
+void set_error(const char *fmt, ...);
+int fail(int code, const char *fmt, ...);
+int check_launch(const char *what);
+
+inline hipStream_t S(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ---------------------------------------------------------------- ordering keys
+// Order-preserving map of a float to uint32: a < b  <=>  key(a) < key(b); -0.0 is folded onto
+// +0.0 first so the two compare equal (ties then go to the lower index).
+ECHO_DEV uint32_t f32_key(float x) {
+  uint32_t b = __float_as_uint(x + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+// int32 priority -> uint32 with the same order
+ECHO_DEV uint32_t i32_key(int32_t x) { return static_cast<uint32_t>(x) ^ 0x80000000u; }
+
+// ---------------------------------------------------------------- wave / block scans
+ECHO_DEV int lane_id() { return __lane_id(); }
+
+// inclusive prefix sum over the 64 lanes of a wave
+ECHO_DEV uint32_t wave_incl_scan(uint32_t v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t t = __shfl_up(v, off, 64);
+    if (l >= off) v += t;
+  }
+  return v;
+}
+
+ECHO_DEV uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Exclusive block-wide prefix sum for a block of NT threads (NT multiple of 64, <= 1024).
+// `tmp` is LDS scratch of at least NT/64 + 1 words.  Returns the exclusive prefix; *total
+// receives the block sum.  Contains __syncthreads(): every thread must call it.
+template <int NT>
+ECHO_DEV uint32_t block_excl_scan(uint32_t v, uint32_t *tmp, uint32_t *total) {
+  constexpr int NW = NT / 64;
+  const int w = threadIdx.x >> 6, l = lane_id();
+  uint32_t inc = wave_incl_scan(v);
+  if (l == 63) tmp[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    uint32_t s = (l < NW) ? tmp[l] : 0u;
+    uint32_t si = wave_incl_scan(s);
+    if (l < NW) tmp[l] = si - s;
+    if (l == NW - 1) tmp[NW] = si;
+  }
+  __syncthreads();
+  uint32_t res = tmp[w] + inc - v;
+  *total = tmp[NW];
+  __syncthreads();
+  return res;
+}
+
+template <int NT>
+ECHO_DEV uint32_t block_sum(uint32_t v, uint32_t *tmp) {
+  uint32_t total;
+  block_excl_scan<NT>(v, tmp, &total);
+  return total;
+}
+
+}  // namespace echo

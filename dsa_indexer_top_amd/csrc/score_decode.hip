@@ -1,0 +1,222 @@
+// Decode lightning-indexer scores on gfx950 (ECHO review page, §2: score of cached token s =
+// sum over the 64 indexer heads of w[h] * ReLU(q[h] . k[s]); FP8 q/k, one 128-byte key per
+// token shared by every head).  Optional fused threshold prefetch (§6.1): tokens scoring above
+// a per-request threshold that are not resident are appended to a capped candidate list.
+//
+// Work split: grid (token range, request).  A workgroup of 4 waves streams its token range in
+// chunks of 128 tokens (16 KB).  Each thread fetches 4 x 16 B of the chunk with fully
+// coalesced global loads (the next chunk is fetched into registers while the current one is
+// computed), and writes them into an LDS double buffer whose 16-byte segments are XOR-swizzled
+// by token so the MFMA-layout reads below are bank-conflict free.
+//
+// Contraction: v_mfma_f32_16x16x128_f8f6f4 with A = q of 16 heads (16 x 128) held in VGPRs for
+// the whole kernel and B = k of 16 tokens (128 x 16) read from LDS.  One MFMA covers the full
+// d = 128 dot product of 16 heads x 16 tokens; four MFMAs cover the 64 heads.  Lane l holds
+// output rows (heads) 4*(l/16) .. +3 of token l%16, so the ReLU * w head reduction is 16 FMAs
+// per lane followed by a two-step cross-lane sum (lanes l, l^16, l^32, l^48).
+//
+// The MFMA's K index is distributed over the 4 lane groups; A and B use the same lane-group
+// -> K mapping, so any assignment of the 128 bytes of a row to (group, byte) works as long as
+// q and k use the same one.  Here group g holds bytes [32g, 32g + 32) of both.
+#include "common.hpp"
+
+namespace echo {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int SD_THREADS = 256;
+constexpr int SD_CHUNK = 128;                                    // tokens per LDS stage
+constexpr int SD_UNITS = SD_CHUNK * D / 16;                      // 16-byte units per chunk
+constexpr int SD_LOADS = SD_UNITS / SD_THREADS;                  // per thread per chunk = 4
+
+struct PrefetchArgs {
+  const float *theta;        // [n_q]
+  const int32_t *req_to_host;// [n_k]
+  const int32_t *host_to_gpu;// [n_host]
+  int32_t *cand;             // [n_q, cap]
+  int32_t *cand_cnt;         // [n_q]
+  int32_t cap;
+  int32_t cap_div;
+};
+
+ECHO_DEV int swz(int tok, int seg) { return tok * 128 + ((seg ^ ((tok >> 1) & 7)) << 4); }
+
+template <bool HAS_SCALE, bool PREFETCH>
+__global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
+    const uint8_t *__restrict__ q, const float *__restrict__ w, const uint8_t *__restrict__ k,
+    const float *__restrict__ k_scale, const int64_t *__restrict__ key_begin,
+    const int32_t *__restrict__ key_len, int32_t max_len, int32_t tok_lo, int32_t tok_hi,
+    int32_t tokens_per_wg, float *__restrict__ scores, int64_t ld, PrefetchArgs pf) {
+  const int r = blockIdx.y;
+  const int32_t L = min(max(key_len[r], 0), max_len);
+  const int32_t hi = min(L, tok_hi);
+  const int32_t t_begin = tok_lo + static_cast<int32_t>(blockIdx.x) * tokens_per_wg;
+  if (t_begin >= hi) return;
+  const int32_t t_end = min(hi, t_begin + tokens_per_wg);
+  const int64_t kb = key_begin[r];
+  const uint8_t *__restrict__ kr = k + kb * D;
+  float *__restrict__ srow = scores + static_cast<int64_t>(r) * ld;
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][SD_CHUNK * D];
+
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
+  const int j = l & 15, g = l >> 4;
+
+  // A operand: q rows of heads hb*16 + j, bytes [32g, 32g+32)
+  v8i qa[4];
+  float wr[4][4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const int4 *p = reinterpret_cast<const int4 *>(q + ((static_cast<int64_t>(r) * H + hb * 16 + j) * D + 32 * g));
+    int4 a0 = p[0], a1 = p[1];
+    qa[hb] = v8i{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wr[hb][v] = w[r * H + hb * 16 + 4 * g + v];
+  }
+
+  float theta = 0.f;
+  int32_t cap_r = 0;
+  if constexpr (PREFETCH) {
+    theta = pf.theta[r];
+    cap_r = min(pf.cap, (L + pf.cap_div - 1) / pf.cap_div);
+  }
+
+  int4 pre[SD_LOADS];
+  auto fetch = [&](int32_t c0) {
+#pragma unroll
+    for (int m = 0; m < SD_LOADS; ++m) {
+      const int e = tid + m * SD_THREADS;
+      const int32_t t = c0 + (e >> 3);
+      if (t < t_end)
+        pre[m] = *reinterpret_cast<const int4 *>(kr + static_cast<int64_t>(t) * D + ((e & 7) << 4));
+      else
+        pre[m] = int4{0, 0, 0, 0};
+    }
+  };
+
+  fetch(t_begin);
+  int buf = 0;
+  for (int32_t c0 = t_begin; c0 < t_end; c0 += SD_CHUNK) {
+    uint8_t *sb = lds[buf];
+#pragma unroll
+    for (int m = 0; m < SD_LOADS; ++m) {
+      const int e = tid + m * SD_THREADS;
+      *reinterpret_cast<int4 *>(sb + swz(e >> 3, e & 7)) = pre[m];
+    }
+    __syncthreads();
+    if (c0 + SD_CHUNK < t_end) fetch(c0 + SD_CHUNK);
+
+    float part[2];
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      const int tt = wv * 32 + tile * 16 + j;
+      const int4 b0 = *reinterpret_cast<const int4 *>(sb + swz(tt, 2 * g));
+      const int4 b1 = *reinterpret_cast<const int4 *>(sb + swz(tt, 2 * g + 1));
+      const v8i bv = v8i{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      float acc = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) {
+        v4f c = {0.f, 0.f, 0.f, 0.f};
+        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[hb], bv, c, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc = fmaf(wr[hb][v], fmaxf(c[v], 0.f), acc);
+      }
+      part[tile] = acc;
+    }
+#pragma unroll
+    for (int tile = 0; tile < 2; ++tile) {
+      part[tile] += __shfl_xor(part[tile], 16, 64);
+      part[tile] += __shfl_xor(part[tile], 32, 64);
+    }
+    if (g < 2) {
+      const int32_t t = c0 + wv * 32 + g * 16 + j;
+      if (t < t_end) {
+        float s = (g == 0) ? part[0] : part[1];
+        if constexpr (HAS_SCALE) s *= k_scale[kb + t];
+        srow[t] = s;
+        if constexpr (PREFETCH) {
+          if (s > theta) {
+            const int32_t h = pf.req_to_host[kb + t];
+            if (pf.host_to_gpu[h] == INF) {
+              const int32_t pos = atomicAdd(&pf.cand_cnt[r], 1);
+              if (pos < cap_r) pf.cand[static_cast<int64_t>(r) * pf.cap + pos] = t;
+            }
+          }
+        }
+      }
+    }
+    buf ^= 1;
+  }
+}
+
+// Tokens per workgroup: enough workgroups to put several on every CU, whole chunks each.
+static int32_t pick_tokens_per_wg(int64_t total_tokens, int32_t max_len) {
+  int64_t target = total_tokens / (256 * 4);
+  int32_t t = SD_CHUNK;
+  while (t < target && t < 8192) t <<= 1;
+  if (t > max_len) t = ((max_len + SD_CHUNK - 1) / SD_CHUNK) * SD_CHUNK;
+  return t < SD_CHUNK ? SD_CHUNK : t;
+}
+
+int launch_score_decode(const uint8_t *q, const float *w, const uint8_t *k, const float *k_scale,
+                        const int64_t *key_begin, const int32_t *key_len, int32_t n_q,
+                        int32_t max_len, int32_t tok_lo, int32_t tok_hi, float *scores,
+                        int64_t ld, const PrefetchArgs *pf, hipStream_t st) {
+  tok_hi = tok_hi < max_len ? tok_hi : max_len;
+  if (n_q == 0 || tok_hi <= tok_lo) return ECHO_OK;
+  const int32_t tpw = pick_tokens_per_wg(static_cast<int64_t>(n_q) * (tok_hi - tok_lo), tok_hi - tok_lo);
+  dim3 grid((tok_hi - tok_lo + tpw - 1) / tpw, n_q);
+  PrefetchArgs none{};
+  const PrefetchArgs &p = pf ? *pf : none;
+  if (pf) {
+    if (k_scale)
+      score_decode_kernel<true, true><<<grid, SD_THREADS, 0, st>>>(q, w, k, k_scale, key_begin, key_len, max_len, tok_lo, tok_hi, tpw, scores, ld, p);
+    else
+      score_decode_kernel<false, true><<<grid, SD_THREADS, 0, st>>>(q, w, k, k_scale, key_begin, key_len, max_len, tok_lo, tok_hi, tpw, scores, ld, p);
+  } else {
+    if (k_scale)
+      score_decode_kernel<true, false><<<grid, SD_THREADS, 0, st>>>(q, w, k, k_scale, key_begin, key_len, max_len, tok_lo, tok_hi, tpw, scores, ld, p);
+    else
+      score_decode_kernel<false, false><<<grid, SD_THREADS, 0, st>>>(q, w, k, k_scale, key_begin, key_len, max_len, tok_lo, tok_hi, tpw, scores, ld, p);
+  }
+  return check_launch("score_decode");
+}
+
+}  // namespace echo
+
+using namespace echo;
+
+extern "C" int echo_index_scores(const uint8_t *q, const float *w, const uint8_t *k,
+                                 const float *k_scale, const int64_t *key_begin,
+                                 const int32_t *key_len, int32_t n_q, int32_t max_key_len,
+                                 float *scores, int64_t ld, void *stream) {
+  if (n_q < 0 || max_key_len < 0) return fail(ECHO_EINVAL, "echo_index_scores: negative n_q or max_key_len");
+  if (ld < max_key_len) return fail(ECHO_EINVAL, "echo_index_scores: ld %lld < max_key_len %d", (long long)ld, max_key_len);
+  if (n_q > 65535) return fail(ECHO_EUNSUPPORTED, "echo_index_scores: n_q %d > 65535", n_q);
+  if (n_q > 0 && (!q || !w || !key_begin || !key_len || !scores || (max_key_len > 0 && !k)))
+    return fail(ECHO_EINVAL, "echo_index_scores: NULL pointer");
+  return launch_score_decode(q, w, k, k_scale, key_begin, key_len, n_q, max_key_len, 0,
+                             max_key_len, scores, ld, nullptr, S(stream));
+}
+
+extern "C" int echo_index_scores_prefetch(const uint8_t *q, const float *w, const uint8_t *k,
+                                          const float *k_scale, const int64_t *key_begin,
+                                          const int32_t *key_len, int32_t n_q,
+                                          int32_t max_key_len, int32_t tok_lo, int32_t tok_hi,
+                                          float *scores, int64_t ld, const float *theta,
+                                          const int32_t *req_to_host, const int32_t *host_to_gpu,
+                                          int32_t *cand, int32_t *cand_cnt, int32_t cap,
+                                          int32_t cap_div, void *stream) {
+  if (n_q < 0 || max_key_len < 0) return fail(ECHO_EINVAL, "echo_index_scores_prefetch: negative n_q or max_key_len");
+  if (ld < max_key_len) return fail(ECHO_EINVAL, "echo_index_scores_prefetch: ld < max_key_len");
+  if (n_q > 65535) return fail(ECHO_EUNSUPPORTED, "echo_index_scores_prefetch: n_q > 65535");
+  if (tok_lo < 0 || tok_hi < tok_lo) return fail(ECHO_EINVAL, "echo_index_scores_prefetch: bad token range");
+  if (cap < 0 || cap_div < 1) return fail(ECHO_EINVAL, "echo_index_scores_prefetch: cap < 0 or cap_div < 1");
+  if (n_q > 0 && (!q || !w || !key_begin || !key_len || !scores || !theta || !req_to_host ||
+                  !host_to_gpu || !cand_cnt || (cap > 0 && !cand) || (max_key_len > 0 && !k)))
+    return fail(ECHO_EINVAL, "echo_index_scores_prefetch: NULL pointer");
+  PrefetchArgs pf{theta, req_to_host, host_to_gpu, cand, cand_cnt, cap, cap_div};
+  return launch_score_decode(q, w, k, k_scale, key_begin, key_len, n_q, max_key_len, tok_lo,
+                             tok_hi, scores, ld, &pf, S(stream));
+}

@@ -1,0 +1,308 @@
+/*
+ * echo.h — C ABI of the MI355X (gfx950) DSA-indexer + top-k + pool-residency decode step.
+ *
+ * What the library computes follows the ECHO review page ("OSDI'26 | ECHO：稀疏 attention
+ * 省了算力，却把 HBM 撑爆了"):
+ *   §2    the lightning-indexer score of a cached token s for query t is the sum over the
+ *         64 indexer heads of w[h,t] * ReLU(q[h,t] . k[s]) (d = 128, FP8 q/k, one key per
+ *         token shared by all heads), followed by an exact top-k;
+ *   §5.1  the pool metadata (free bitmap, per-slot eviction priority, fixed-length result
+ *         buffer, the two slot<->host maps with an infinity sentinel);
+ *   §5.2  the in-graph allocate / free / recall operations, with the recall copying rows
+ *         straight out of host memory from a GPU kernel;
+ *   §6.1  threshold prefetch during scoring, made lossless by the guaranteed recall.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked [host].  The caller owns every buffer and
+ *     stream; no entry point allocates device memory, frees it, or synchronises, except
+ *     echo_recall in ECHO_RECALL_MEMCPY mode and the echo_graph_* / echo_host_* helpers,
+ *     which say so.  Everything else only enqueues work on the given stream(s), so it can be
+ *     captured into a hipGraph.
+ *   - Streams are hipStream_t passed as void* (NULL = the null stream).
+ *   - FP8 = OCP E4M3FN bytes.  H = 64 heads and D = 128 are fixed.
+ *   - Return codes: ECHO_OK, or a negative ECHO_E* code when an argument is rejected on the
+ *     host (nothing is enqueued then) or a launch fails; echo_last_error() gives the text
+ *     (thread-local).  Failures that depend on device data (pool exhausted, bad host index,
+ *     duplicate host index) never trap: they OR bits into the pool's device status word.
+ *   - "inf" in the pool maps is INT32_MAX (ECHO_INF).
+ */
+#ifndef ECHO_H
+#define ECHO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ECHO_H_INDEX 64
+#define ECHO_D_INDEX 128
+#define ECHO_ROW_ELEMS 576 /* MLA latent row: 512 compressed + 64 RoPE values (bf16 bits) */
+#define ECHO_INF 0x7FFFFFFF
+#define ECHO_MAX_TOPK 4096
+
+enum {
+  ECHO_OK = 0,
+  ECHO_EINVAL = -1,      /* bad argument or shape; nothing enqueued */
+  ECHO_EUNSUPPORTED = -2,/* outside the supported range; nothing enqueued */
+  ECHO_EHIP = -3,        /* a HIP call or kernel launch failed */
+  ECHO_EWORKSPACE = -4   /* workspace smaller than the matching *_workspace_bytes() */
+};
+
+/* Sticky device status bits (pool->status). */
+enum {
+  ECHO_ST_EXHAUSTED = 1, /* the misses need more slots than free + evictable; pool untouched */
+  ECHO_ST_BAD_HOST = 2,  /* a selected token maps to a host index outside [0, n_host); pool untouched */
+  ECHO_ST_DUP_HOST = 4   /* two selected misses share a host index (caller precondition broken);
+                            pool state afterwards is unspecified */
+};
+
+/* Recall modes for echo_recall. */
+enum {
+  ECHO_RECALL_GATHER = 0, /* GPU kernel reads mapped pinned host memory; graph-capturable */
+  ECHO_RECALL_MEMCPY = 1  /* host reads the miss list (synchronises the stream) and issues one
+                             hipMemcpyAsync per row; NOT graph-capturable */
+};
+
+/*
+ * GPU pool of one layer plus its host backup (§5.1).  All members are device pointers the
+ * caller allocated; sizes: gpu_free/gpu_priority/gpu_to_host/indices_buf [n_gpu],
+ * host_to_gpu [n_host], gpu_kv [n_gpu * 576], host_kv [n_host * 576], status [1].
+ *   gpu_free      1 = slot free, 0 = occupied (GPUTokenFree).  The library uses the value 2
+ *                 transiently inside one call to mark protected slots; it is 0/1 between calls.
+ *   gpu_priority  eviction priority, lowest evicted first, -1 for a free slot (GPUTokenPriority)
+ *   gpu_to_host   host index held by the slot, ECHO_INF when empty (GPUTokenToHost)
+ *   host_to_gpu   slot holding the host index, ECHO_INF when not resident (HostTokenToGPU)
+ *   indices_buf   fixed-length result list: slot given to the i-th miss, -1 after the last
+ *                 (GPUIndicesBuffer); see echo_pool_lookup_alloc for how far it is written
+ *   gpu_kv        latent rows of the slots, bf16 bits, 1152 bytes per row
+ *   host_kv       the host backup: a DEVICE-ACCESSIBLE pointer to pinned, mapped host
+ *                 memory (echo_host_alloc gives one), read by GPU kernels over the host link
+ *   status        sticky ECHO_ST_* bits; cleared only by echo_pool_init / echo_status_clear
+ */
+typedef struct {
+  int32_t n_gpu;
+  int32_t n_host;
+  uint8_t *gpu_free;
+  int32_t *gpu_priority;
+  int32_t *gpu_to_host;
+  int32_t *host_to_gpu;
+  int32_t *indices_buf;
+  uint16_t *gpu_kv;
+  const uint16_t *host_kv;
+  int32_t *status;
+} echo_pool;
+
+/* Bytes of pool metadata: 4*n_host + 13*n_gpu (§5.1). */
+size_t echo_pool_metadata_bytes(int32_t n_host, int32_t n_gpu);
+
+/* Resets a pool to empty: free = 1, priority = -1, both maps = ECHO_INF, indices_buf = -1,
+ * status = 0.  Rows are left as they are.  Enqueued on `stream`. */
+int echo_pool_init(echo_pool *pool, void *stream);
+
+/* Sets *status = 0 (enqueued). */
+int echo_status_clear(int32_t *status, void *stream);
+
+/*
+ * Decode indexer scores (§2).  For every query (request) r in [0, n_q) and key s in
+ * [0, key_len[r]):
+ *     scores[r*ld + s] = sum_h w[r*64 + h] * ReLU(scale(s) * (q[r,h,:] . k[key_begin[r] + s, :]))
+ * with scale(s) = k_scale[key_begin[r] + s] when k_scale != NULL, else 1 (k_scale dequantises
+ * the FP8 key; the library applies it after the head sum, which is equal in exact arithmetic
+ * because scale > 0).  Products are exact, sums are fp32.
+ *   q        [n_q, 64, 128] FP8 bytes     w       [n_q, 64] fp32
+ *   k        [n_k, 128] FP8 bytes, 128-byte rows; request r owns rows key_begin[r] .. +key_len[r]
+ *   k_scale  [n_k] fp32 > 0, or NULL
+ *   key_begin [n_q] int64, key_len [n_q] int32 (0 <= key_len[r] <= max_key_len)
+ *   scores   [n_q, ld] fp32, ld >= max_key_len; entries s >= key_len[r] are not written.
+ * Errors: EINVAL for n_q < 0, max_key_len < 0, ld < max_key_len or NULL pointers.
+ * Device-side lengths above max_key_len are clamped to max_key_len (never read out of range).
+ */
+int echo_index_scores(const uint8_t *q, const float *w, const uint8_t *k, const float *k_scale,
+                      const int64_t *key_begin, const int32_t *key_len, int32_t n_q,
+                      int32_t max_key_len, float *scores, int64_t ld, void *stream);
+
+/*
+ * Threshold prefetch fused into scoring (§6.1).  The same scores as echo_index_scores, and in
+ * addition every scored token s of request r with score > theta[r] that is not resident
+ * (host_to_gpu[req_to_host[key_begin[r] + s]] == ECHO_INF) is appended to cand[r*cap + j]
+ * while the per-request counter cand_cnt[r] is below cap_r = min(cap, ceil(key_len[r] /
+ * cap_div)).  The counter keeps counting past cap_r (it reports demand); only the first cap_r
+ * slots are written.  Which over-threshold tokens win the slots depends on timing; the set of
+ * scores never does.  Tokens [tok_lo, tok_hi) of every request are scored by this call, so a
+ * step can be split into chunks that a side stream consumes (echo_prefetch_gather).
+ *   theta [n_q] fp32; req_to_host [n_k] int32; host_to_gpu [n_host]; cand [n_q, cap] int32;
+ *   cand_cnt [n_q] int32 (caller zeroes it before the first chunk).
+ */
+int echo_index_scores_prefetch(const uint8_t *q, const float *w, const uint8_t *k,
+                               const float *k_scale, const int64_t *key_begin,
+                               const int32_t *key_len, int32_t n_q, int32_t max_key_len,
+                               int32_t tok_lo, int32_t tok_hi, float *scores, int64_t ld,
+                               const float *theta, const int32_t *req_to_host,
+                               const int32_t *host_to_gpu, int32_t *cand, int32_t *cand_cnt,
+                               int32_t cap, int32_t cap_div, void *stream);
+
+/*
+ * Per-request prefetch threshold: theta[r] = the nearest-rank `percentile` of the scores of
+ * request r at the n_sample positions floor(i * key_len[r] / n_sample), i < n_sample
+ * (the stand-in for the page's per-layer EMA prediction of the k-th score, §6.1, on a single
+ * step with no history).  theta[r] = +inf when key_len[r] == 0.  n_sample must be a power of
+ * two in [64, 4096].  Computes the sampled scores itself from q, w, k, k_scale.
+ */
+int echo_prefetch_threshold(const uint8_t *q, const float *w, const uint8_t *k,
+                            const float *k_scale, const int64_t *key_begin,
+                            const int32_t *key_len, int32_t n_q, int32_t n_sample,
+                            float percentile, float *theta, void *stream);
+
+/*
+ * Prefill (causal) indexer scores (§3.4: quadratic in the context).  Query rows t in
+ * [0, n_q) sit at absolute positions q_pos0 + t and see keys s in [0, min(n_k, q_pos0+t+1)):
+ *     scores[t*ld + s] = sum_h w[t*64+h] * ReLU(q[t,h,:] . k[s,:])
+ *   q [n_q, 64, 128] FP8; w [n_q, 64] fp32; k [n_k, 128] FP8; scores [n_q, ld] fp32,
+ *   ld >= n_k; entries past a row's causal length are not written.
+ */
+int echo_index_scores_prefill(const uint8_t *q, const float *w, const uint8_t *k, int32_t n_q,
+                              int32_t n_k, int32_t q_pos0, float *scores, int64_t ld,
+                              void *stream);
+
+/*
+ * Exact top-k per row (§2).  Row r holds len[r] scores at scores[r*ld ...].  Selects the
+ * min(k, len[r]) highest scores; ties go to the lower index; -0.0 equals +0.0.  Writes
+ * idx[r*k + j], the selected token indices in ascending order, -1 padded to k.
+ * NaN scores are outside the contract.  1 <= k <= ECHO_MAX_TOPK.
+ *   ws: device workspace of at least echo_topk_workspace_bytes(n_rows, max_len) bytes.
+ * len[r] above max_len is clamped to max_len.
+ */
+size_t echo_topk_workspace_bytes(int32_t n_rows, int32_t max_len);
+int echo_topk(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
+              int32_t max_len, int32_t k, int32_t *idx, void *ws, size_t ws_bytes,
+              void *stream);
+
+/*
+ * Residency lookup + eviction + allocation for the selected tokens (§5.2 free/allocate and
+ * the lookup half of recall), without the row copy.  For the entries idx[r*k + j] >= 0 taken
+ * in (r, j) order: h = req_to_host[key_begin[r] + idx]; hit iff host_to_gpu[h] != ECHO_INF.
+ *   - every hit slot is protected for this call;
+ *   - need = max(0, n_miss - #free); the `need` unprotected occupied slots with the smallest
+ *     (priority, slot index) are evicted: free = 1, priority = -1, both maps = ECHO_INF; their
+ *     rows are not touched (the host holds the backup);
+ *   - the i-th miss gets the i-th free slot in ascending slot order: free = 0, maps set,
+ *     priority = step_id; miss_host[i] = h, miss_slot[i] = slot, indices_buf[i] = slot;
+ *     miss_host/miss_slot entries past n_miss and indices_buf entries [n_miss,
+ *     min(n_gpu, n_rows*k)) are -1;
+ *   - every selected slot's priority = step_id; topk_slot[r*k + j] = its slot (-1 where
+ *     idx is -1); *n_miss = number of misses.
+ * On ECHO_ST_EXHAUSTED or ECHO_ST_BAD_HOST the pool is left untouched and topk_slot,
+ * miss_*, n_miss are unspecified.  Rows of missed tokens still have to be copied by
+ * echo_recall.  step_id must exceed every priority already in the pool for the policy to be
+ * least-recently-selected-first (not checked).
+ *   ws: device workspace of at least echo_pool_workspace_bytes(n_rows, k, pool->n_gpu).
+ */
+size_t echo_pool_workspace_bytes(int32_t n_rows, int32_t k, int32_t n_gpu);
+int echo_pool_lookup_alloc(const echo_pool *pool, const int32_t *idx, const int64_t *key_begin,
+                           const int32_t *req_to_host, int32_t n_rows, int32_t k,
+                           int32_t step_id, int32_t *topk_slot, int32_t *miss_host,
+                           int32_t *miss_slot, int32_t *n_miss, void *ws, size_t ws_bytes,
+                           void *stream);
+
+/*
+ * Recall (§5.2): gpu_kv[miss_slot[i]] = host_kv[miss_host[i]] bitwise (1152 bytes) for
+ * i < *n_miss (n_miss is read on the device; max_miss bounds it).
+ *   ECHO_RECALL_GATHER: one kernel reads the rows straight from mapped pinned host memory.
+ *   ECHO_RECALL_MEMCPY: synchronises `stream`, reads n_miss and the lists to the host and
+ *     issues one hipMemcpyAsync (host -> device) per row on `stream`; returns after enqueueing.
+ * Skipped entirely when the pool status word is nonzero.
+ */
+int echo_recall(const echo_pool *pool, const int32_t *miss_host, const int32_t *miss_slot,
+                const int32_t *n_miss, int32_t max_miss, int32_t mode, void *stream);
+
+/*
+ * Prefetch side of the overlap (§6.1, §5.2): allocates free slots to the prefetch candidates
+ * appended since the previous call (cand/cand_cnt from echo_index_scores_prefetch; `done`
+ * [n_q] int32 remembers how many of each request's candidates were already handled, zeroed
+ * by the caller before the first call), sets the maps, gives the slots priority 0, and gathers
+ * their rows from host memory.  Never evicts: candidates beyond the free slots are dropped.
+ * The free slots come from free_list[0 .. *n_free_list) (ascending free slots listed once per
+ * step by echo_prefetch_begin), consumed through the counter *free_taken.
+ */
+int echo_prefetch_begin(const echo_pool *pool, int32_t *free_list, int32_t *n_free_list,
+                        int32_t *free_taken, int32_t *cand_cnt, int32_t *done, int32_t n_q,
+                        void *ws, size_t ws_bytes, void *stream);
+int echo_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
+                         const int32_t *req_to_host, const int32_t *cand,
+                         const int32_t *cand_cnt, int32_t *done, int32_t n_q, int32_t cap,
+                         const int32_t *key_len, int32_t cap_div, const int32_t *free_list,
+                         const int32_t *n_free_list, int32_t *free_taken, int32_t *n_prefetched,
+                         void *stream);
+
+/*
+ * The whole decode step (§4): scores -> [threshold prefetch overlapped on `side`] -> exact
+ * top-k -> lookup/evict/allocate -> recall gather -> priorities.  Pure enqueue on `main`
+ * (and `side` when prefetch is on; side may equal main), so the call can be captured into one
+ * hipGraph (echo_graph_capture_decode).
+ */
+typedef struct {
+  const uint8_t *q;          /* [n_rows, 64, 128] FP8 */
+  const float *w;            /* [n_rows, 64] */
+  const uint8_t *k;          /* [n_k, 128] FP8 */
+  const float *k_scale;      /* [n_k] or NULL */
+  const int64_t *key_begin;  /* [n_rows] */
+  const int32_t *key_len;    /* [n_rows] */
+  const int32_t *req_to_host;/* [n_k] host index of every cached token */
+  int32_t n_rows;
+  int32_t max_key_len;
+  int32_t topk;
+  int32_t step_id;
+  /* prefetch (off when prefetch == 0) */
+  int32_t prefetch;
+  int32_t n_chunks;          /* scoring split into this many token ranges (1..16) */
+  int32_t n_sample;          /* threshold sample size (power of two, 64..4096) */
+  float percentile;          /* threshold percentile, e.g. 95 */
+  int32_t cap;               /* per-request candidate cap bound */
+  int32_t cap_div;           /* cap_r = min(cap, ceil(L_r / cap_div)) */
+} echo_decode_args;
+
+typedef struct {             /* device outputs of one step */
+  float *scores;             /* [n_rows, max_key_len] */
+  int32_t *topk_idx;         /* [n_rows, topk] */
+  int32_t *topk_slot;        /* [n_rows, topk] */
+  int32_t *miss_host;        /* [n_rows * topk] */
+  int32_t *miss_slot;        /* [n_rows * topk] */
+  int32_t *counters;         /* [8]: 0 n_miss, 1 n_prefetch_candidates (sum of demand),
+                                2 n_prefetched, 3 n_prefetched_and_selected (filled by
+                                echo_decode_stats), 4..7 reserved */
+} echo_decode_out;
+
+size_t echo_decode_workspace_bytes(const echo_decode_args *a, int32_t n_gpu);
+int echo_decode_select(const echo_decode_args *a, const echo_pool *pool,
+                       const echo_decode_out *out, void *ws, size_t ws_bytes, void *main_stream,
+                       void *side_stream);
+
+/* Graph helpers (host side; they create HIP objects).  Capture one echo_decode_select into a
+ * hipGraph on `main_stream` (and `side_stream`), instantiate it, and replay it.  The graph
+ * reads and writes the buffers that were passed at capture time. */
+typedef struct echo_graph_s *echo_graph;
+int echo_graph_capture_decode(const echo_decode_args *a, const echo_pool *pool,
+                              const echo_decode_out *out, void *ws, size_t ws_bytes,
+                              void *main_stream, void *side_stream, echo_graph *graph);
+int echo_graph_launch(echo_graph graph, void *stream);
+int echo_graph_destroy(echo_graph graph);
+
+/* Pinned, device-mapped host memory for the host backup (hipHostMalloc, mapped; coherent when
+ * `coherent` != 0).  *host receives the host pointer, *dev the device-side pointer to pass as
+ * echo_pool.host_kv.  Free with echo_host_free. */
+int echo_host_alloc(size_t bytes, int coherent, void **host, void **dev);
+int echo_host_free(void *host);
+
+/* Text of the last error on this thread ("" if none). */
+const char *echo_last_error(void);
+
+/* Library version string. */
+const char *echo_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ECHO_H */

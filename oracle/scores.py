@@ -32,8 +32,11 @@ import numpy as np
 from .fp8 import decode_e4m3fn
 
 
-def _request_keys(k_dec, k_scale, begin, length):
-    kr = k_dec[begin:begin + length]
+def _request_keys(k, k_scale, begin, length, absolute=False):
+    """Decoded (float64) key rows of one request and their scales (None = 1)."""
+    kr = decode_e4m3fn(k[begin:begin + length])
+    if absolute:
+        kr = np.abs(kr)
     sc = None if k_scale is None else np.asarray(k_scale[begin:begin + length], dtype=np.float64)
     return kr, sc
 
@@ -46,11 +49,10 @@ def index_scores(q, w, k, k_scale, key_begin, key_len):
     Returns a list of float64 arrays, one per query, of length key_len[r].
     """
     q_dec = decode_e4m3fn(q)                       # [n_q, H, D]
-    k_dec = decode_e4m3fn(k)                       # [n_k, D]
     w64 = np.asarray(w, dtype=np.float64)          # [n_q, H]
     out = []
     for r in range(q_dec.shape[0]):
-        kr, sc = _request_keys(k_dec, k_scale, int(key_begin[r]), int(key_len[r]))
+        kr, sc = _request_keys(k, k_scale, int(key_begin[r]), int(key_len[r]))
         dots = kr @ q_dec[r].T                     # [L, H]: q[h] . k[s], exact
         if sc is not None:
             dots = dots * sc[:, None]              # dequantised key
@@ -65,11 +67,10 @@ def error_scale(q, w, k, k_scale, key_begin, key_len):
     inputs are stated relative to it (|gpu - oracle| <= 1e-4 * T).
     """
     q_abs = np.abs(decode_e4m3fn(q))
-    k_abs = np.abs(decode_e4m3fn(k))
     w_abs = np.abs(np.asarray(w, dtype=np.float64))
     out = []
     for r in range(q_abs.shape[0]):
-        kr, sc = _request_keys(k_abs, k_scale, int(key_begin[r]), int(key_len[r]))
+        kr, sc = _request_keys(k, k_scale, int(key_begin[r]), int(key_len[r]), absolute=True)
         t = (kr @ q_abs[r].T) @ w_abs[r]
         if sc is not None:
             t = t * sc
