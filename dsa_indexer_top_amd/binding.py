@@ -60,8 +60,8 @@ _SIGS = {
     "echo_topk_workspace_bytes": (SZ, [I32, I32]),
     "echo_topk": (C.c_int, [P, I64, P, I32, I32, I32, P, P, SZ, P]),
     "echo_pool_workspace_bytes": (SZ, [I32, I32, I32]),
-    "echo_pool_lookup_alloc": (C.c_int, [C.POINTER(Pool), P, P, P, I32, I32, I32, P, P, P, P,
-                                         P, SZ, P]),
+    "echo_pool_lookup_alloc": (C.c_int, [C.POINTER(Pool), P, P, P, I64, I32, I32, I32, P, P, P,
+                                         P, P, SZ, P]),
     "echo_recall": (C.c_int, [C.POINTER(Pool), P, P, P, I32, I32, P]),
     "echo_prefetch_begin": (C.c_int, [C.POINTER(Pool), P, P, P, P, P, I32, P, SZ, P]),
     "echo_prefetch_gather": (C.c_int, [C.POINTER(Pool), P, P, P, P, P, I32, I32, P, I32, P,
@@ -186,7 +186,7 @@ def pool_workspace_bytes(n_rows, k, n_gpu):
 def pool_lookup_alloc(pool, idx, key_begin, req_to_host, step_id, topk_slot, miss_host,
                       miss_slot, n_miss, ws, stream=None):
     _call("echo_pool_lookup_alloc", C.byref(pool), ptr(idx), ptr(key_begin), ptr(req_to_host),
-          idx.shape[0], idx.shape[1], step_id, ptr(topk_slot), ptr(miss_host), ptr(miss_slot),
+          req_to_host.shape[0], idx.shape[0], idx.shape[1], step_id, ptr(topk_slot), ptr(miss_host), ptr(miss_slot),
           ptr(n_miss), ptr(ws), ws.numel() * ws.element_size(), stream_handle(stream))
 
 

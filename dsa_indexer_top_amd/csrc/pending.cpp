@@ -2,15 +2,8 @@
 #include "common.hpp"
 using namespace echo;
 extern "C" {
-int echo_pool_init(echo_pool *, void *) { return fail(ECHO_EUNSUPPORTED, "echo_pool_init: not built yet"); }
-int echo_status_clear(int32_t *, void *) { return fail(ECHO_EUNSUPPORTED, "not built yet"); }
 int echo_prefetch_threshold(const uint8_t *, const float *, const uint8_t *, const float *, const int64_t *, const int32_t *, int32_t, int32_t, float, float *, void *) { return fail(ECHO_EUNSUPPORTED, "not built yet"); }
 int echo_index_scores_prefill(const uint8_t *, const float *, const uint8_t *, int32_t, int32_t, int32_t, float *, int64_t, void *) { return fail(ECHO_EUNSUPPORTED, "not built yet"); }
-size_t echo_topk_workspace_bytes(int32_t, int32_t) { return 0; }
-int echo_topk(const float *, int64_t, const int32_t *, int32_t, int32_t, int32_t, int32_t *, void *, size_t, void *) { return fail(ECHO_EUNSUPPORTED, "not built yet"); }
-size_t echo_pool_workspace_bytes(int32_t, int32_t, int32_t) { return 0; }
-int echo_pool_lookup_alloc(const echo_pool *, const int32_t *, const int64_t *, const int32_t *, int32_t, int32_t, int32_t, int32_t *, int32_t *, int32_t *, int32_t *, void *, size_t, void *) { return fail(ECHO_EUNSUPPORTED, "not built yet"); }
-int echo_recall(const echo_pool *, const int32_t *, const int32_t *, const int32_t *, int32_t, int32_t, void *) { return fail(ECHO_EUNSUPPORTED, "not built yet"); }
 int echo_prefetch_begin(const echo_pool *, int32_t *, int32_t *, int32_t *, int32_t *, int32_t *, int32_t, void *, size_t, void *) { return fail(ECHO_EUNSUPPORTED, "not built yet"); }
 int echo_prefetch_gather(const echo_pool *, const int64_t *, const int32_t *, const int32_t *, const int32_t *, int32_t *, int32_t, int32_t, const int32_t *, int32_t, const int32_t *, const int32_t *, int32_t *, int32_t *, void *) { return fail(ECHO_EUNSUPPORTED, "not built yet"); }
 size_t echo_decode_workspace_bytes(const echo_decode_args *, int32_t) { return 0; }

@@ -193,6 +193,8 @@ int echo_topk(const float *scores, int64_t ld, const int32_t *len, int32_t n_row
  *     min(n_gpu, n_rows*k)) are -1;
  *   - every selected slot's priority = step_id; topk_slot[r*k + j] = its slot (-1 where
  *     idx is -1); *n_miss = number of misses.
+ * req_to_host has n_k entries; a token index key_begin[r] + idx outside [0, n_k), a host index
+ * outside [0, n_host) or a HostTokenToGPU entry outside [0, n_gpu) sets ECHO_ST_BAD_HOST.
  * On ECHO_ST_EXHAUSTED or ECHO_ST_BAD_HOST the pool is left untouched and topk_slot,
  * miss_*, n_miss are unspecified.  Rows of missed tokens still have to be copied by
  * echo_recall.  step_id must exceed every priority already in the pool for the policy to be
@@ -201,7 +203,7 @@ int echo_topk(const float *scores, int64_t ld, const int32_t *len, int32_t n_row
  */
 size_t echo_pool_workspace_bytes(int32_t n_rows, int32_t k, int32_t n_gpu);
 int echo_pool_lookup_alloc(const echo_pool *pool, const int32_t *idx, const int64_t *key_begin,
-                           const int32_t *req_to_host, int32_t n_rows, int32_t k,
+                           const int32_t *req_to_host, int64_t n_k, int32_t n_rows, int32_t k,
                            int32_t step_id, int32_t *topk_slot, int32_t *miss_host,
                            int32_t *miss_slot, int32_t *n_miss, void *ws, size_t ws_bytes,
                            void *stream);
