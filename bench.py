@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the decode hot path on one MI355X.
+
+One step = one replay of the captured hipGraph of the whole decode step (indexer scores,
+exact top-k, residency lookup / eviction / allocation, recall gather from pinned host memory,
+priorities) over the default workload: 8 requests x 65536 cached tokens, H=64, d=128 FP8
+integer-grid q/k, top-2048, 90% of the selected tokens resident in a full GPU pool of
+65536 slots, misses recalled from a pinned host pool of 524288 rows.  All inputs are seeded
+and synthetic and resident in HBM / pinned host memory before timing starts.
+
+Before every replay the pool is restored from a pristine device copy on the same stream;
+the restore is outside the per-step HIP-event timing (it is inside the wall-clock bracket,
+which is reported separately).
+
+Prints ONE JSON line.  --gpus N > 1 is refused: this path runs on one GPU.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+WORKLOADS = {
+    "b8_64k": "decode step: 8 requests x 65536 tokens, H=64 d=128 FP8 (integer grid) q/k, "
+              "top-2048, 90% pool hit rate, N_G=65536, N_H=524288",
+    "b32_ragged": "decode step: 32 requests x U[16384,131072] tokens, general FP8 q/k with "
+                  "per-token scale, top-2048, 70% pool hit rate, host pool 8x GPU pool",
+    "b64_128k": "decode step: 64 requests x 131072 tokens, general FP8 q/k with per-token "
+                "scale, top-2048, 50% pool hit rate, threshold prefetch overlapped on a side "
+                "stream, N_G=1048576, N_H=8388608",
+    "tiny": "decode step: 1 request x 4096 tokens, integer grid, top-256, half of all tokens resident",
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_time_us(torch, stream, fn, reps):
+    """Average duration of fn()'s launches on `stream`, from HIP events on that stream."""
+    fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(reps):
+        fn()
+    e.record(stream)
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) * 1000.0 / reps
+
+
+def measure_link_gbs(torch, nbytes=256 << 20, reps=5):
+    """Best-of-5 pinned host -> device copy rate (the host-link reference for recall)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        dst.copy_(src, non_blocking=True)
+        e.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (s.elapsed_time(e) / 1e3) / 1e9)
+    return best
+
+
+def cpu_baseline(inp, host_kv, pool_arrays, budget_s=12.0):
+    """The oracle, as it is, on a bounded sample of the same workload: whole requests in order
+    (scores in float64, exact top-k) until the budget is spent, then the oracle pool step for
+    the sampled requests' selections against the full pool."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    t0 = time.perf_counter()
+    sel, tokens, n = [], 0, 0
+    for r in range(len(inp.key_len)):
+        sl = slice(r, r + 1)
+        s = oracle.index_scores(inp.q[sl], inp.w[sl], inp.k, inp.k_scale, inp.key_begin[sl],
+                                inp.key_len[sl])
+        sel.append(oracle.topk_rows(s, inp.cfg.topk)[0])
+        tokens += int(inp.key_len[r])
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    st = oracle.PoolState(pool_arrays.free, pool_arrays.priority, pool_arrays.to_host,
+                          pool_arrays.host_to_gpu, pool_arrays.indices_buf, pool_arrays.gpu_kv)
+    oracle.pool_step(st, host_kv, np.stack(sel), inp.key_begin[:n], inp.req_to_host,
+                     pool_arrays.step_id)
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "indexed tokens/s", "cores": int(cores),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "oracle decode step (float64 scores, exact top-k, canonical pool step "
+                      "incl. recall copy) on requests 0..%d of the workload (%d tokens)" % (n - 1, tokens)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="b8_64k", choices=sorted(WORKLOADS))
+    ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefetch", choices=("auto", "on", "off"), default="auto")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this decode path runs on one GPU; --gpus %d is not supported "
+              "(the batch shards across GPUs with no exchange, see the design notes)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from dsa_indexer_top_amd import binding as B, inputs as gen
+    from dsa_indexer_top_amd.runner import DecodeRunner
+
+    cfg = gen.CONFIGS[args.workload]
+    prefetch = cfg.prefetch if args.prefetch == "auto" else args.prefetch == "on"
+    log("workload", args.workload, "prefetch", prefetch)
+    t_setup = time.perf_counter()
+    inp = gen.make_decode_inputs(cfg)
+    hb = B.HostBuffer(inp.n_host * 576 * 2)
+    host_kv = hb.array.view(np.uint16).reshape(inp.n_host, 576)
+    gen.fill_latent_rows(cfg.seed, host_kv)
+    log("inputs drawn in %.1fs" % (time.perf_counter() - t_setup))
+
+    # the resident set is drawn around the step's own selection (computed once, untimed)
+    n_rows, max_len = len(inp.key_len), int(inp.key_len.max())
+    dq, dw, dk = (torch.from_numpy(a).cuda() for a in (inp.q, inp.w, inp.k))
+    dks = None if inp.k_scale is None else torch.from_numpy(inp.k_scale).cuda()
+    dkb, dkl = torch.from_numpy(inp.key_begin).cuda(), torch.from_numpy(inp.key_len).cuda()
+    sc = torch.empty((n_rows, max_len), dtype=torch.float32, device="cuda")
+    sel = torch.empty((n_rows, cfg.topk), dtype=torch.int32, device="cuda")
+    tws = torch.empty(B.topk_workspace_bytes(n_rows, max_len), dtype=torch.uint8, device="cuda")
+    B.index_scores(dq, dw, dk, dks, dkb, dkl, max_len, sc)
+    B.topk(sc, dkl, max_len, cfg.topk, sel, tws)
+    pool = gen.make_pool_state(inp, sel.cpu().numpy(), host_kv)
+    del sc, sel, tws
+    rn = DecodeRunner(inp, pool, host_buf=hb, prefetch=prefetch)
+    rn.capture()
+    log("setup done in %.1fs" % (time.perf_counter() - t_setup))
+
+    main_s = rn.main
+    for _ in range(args.warmup):
+        rn.restore()
+        rn.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for s, e in ev:
+        rn.restore()
+        s.record(main_s)
+        rn.replay()
+        e.record(main_s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    step_ms = np.array([s.elapsed_time(e) for s, e in ev])
+    res = rn.results()
+    assert res["status"] == 0, "pool status %d" % res["status"]
+    n_miss = int(res["counters"][0])
+    tokens = int(inp.key_len.astype(np.int64).sum())
+    ms = float(step_ms.mean())
+    value = tokens / (ms / 1e3)
+    log("step %.1f us (median %.1f, min %.1f), wall incl. restores %.1f us/step" % (
+        ms * 1e3, np.median(step_ms) * 1e3, step_ms.min() * 1e3, wall / args.steps * 1e6))
+
+    # ---- live kernel timings on the main stream (same launch configuration as the step)
+    reps = args.kernel_reps
+    score_bytes = tokens * 128 + (tokens * 4 if inp.k_scale is not None else 0)
+    t_score = kernel_time_us(torch, main_s, lambda: B.index_scores(
+        rn.q, rn.w, rn.k, rn.k_scale, rn.key_begin, rn.key_len, rn.max_len, rn.scores,
+        stream=main_s), reps)
+    tws = torch.empty(B.topk_workspace_bytes(n_rows, rn.max_len), dtype=torch.uint8, device="cuda")
+    t_topk = kernel_time_us(torch, main_s, lambda: B.topk(
+        rn.scores, rn.key_len, rn.max_len, rn.topk, rn.topk_idx, tws, stream=main_s), reps)
+    # recall gather alone, re-copying the step's miss list
+    rn.restore()
+    rn.replay()
+    torch.cuda.synchronize()
+    t_recall = kernel_time_us(torch, main_s, lambda: B.recall(
+        rn.pool, rn.miss_host, rn.miss_slot, rn.counters[0:1], n_rows * rn.topk, stream=main_s), reps)
+    recall_bytes = n_miss * 576 * 2
+    link = measure_link_gbs(torch)
+    score_gbs = score_bytes / (t_score / 1e6) / 1e9
+    recall_gbs = recall_bytes / (t_recall / 1e6) / 1e9 if t_recall > 0 else 0.0
+    log("scoring %.1f us (%.0f GB/s), top-k %.1f us, recall %.1f us (%.1f GB/s of %.1f link)" % (
+        t_score, score_gbs, t_topk, t_recall, recall_gbs, link))
+
+    out = {
+        "metric": "indexed tokens/sec (score+top-k+recall) and % of HBM peak at L=64K-128K, 1 GPU",
+        "value": round(value, 1),
+        "unit": "indexed tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded)",
+        "config": {"workload": args.workload, "description": WORKLOADS[args.workload],
+                   "batch": n_rows, "tokens": tokens, "topk": rn.topk, "n_gpu_slots": rn.n_gpu,
+                   "n_host_slots": rn.n_host, "prefetch": bool(prefetch),
+                   "timing": "HIP events around each graph replay on its stream; pool restored "
+                             "from a pristine copy between replays, outside the events"},
+        "roofline": {"bound": "hbm", "kernel": "score_decode_kernel",
+                     "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": score_bytes, "us_per_launch": round(t_score, 2)},
+        "recall": {"bound": "host link", "kernel": "recall_gather_kernel",
+                   "achieved": round(recall_gbs, 2), "peak_measured_h2d": round(link, 2),
+                   "unit": "GB/s", "frac": round(recall_gbs / link, 4) if link else None,
+                   "rows": n_miss, "bytes_per_launch": recall_bytes,
+                   "us_per_launch": round(t_recall, 2)},
+        "breakdown_us": {"step": round(ms * 1e3, 2), "score": round(t_score, 2),
+                         "topk": round(t_topk, 2), "recall": round(t_recall, 2),
+                         "wall_per_step_incl_restore": round(wall / args.steps * 1e6, 2)},
+        "counters": {"n_miss": n_miss, "prefetch_demand": int(res["counters"][1]),
+                     "prefetched": int(res["counters"][2])},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(inp, host_kv, pool)
+    rn.close()
+    hb.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -54,7 +54,7 @@ _SIGS = {
     "echo_status_clear": (C.c_int, [P, P]),
     "echo_index_scores": (C.c_int, [P, P, P, P, P, P, I32, I32, P, I64, P]),
     "echo_index_scores_prefetch": (C.c_int, [P, P, P, P, P, P, I32, I32, I32, I32, P, I64,
-                                             P, P, P, P, P, I32, I32, P]),
+                                             P, P, P, P, P, P, I32, I32, P]),
     "echo_prefetch_threshold": (C.c_int, [P, P, P, P, P, P, I32, I32, F32, P, P]),
     "echo_index_scores_prefill": (C.c_int, [P, P, P, I32, I32, I32, P, I64, P]),
     "echo_topk_workspace_bytes": (SZ, [I32, I32]),
@@ -63,9 +63,8 @@ _SIGS = {
     "echo_pool_lookup_alloc": (C.c_int, [C.POINTER(Pool), P, P, P, I64, I32, I32, I32, P, P, P,
                                          P, P, SZ, P]),
     "echo_recall": (C.c_int, [C.POINTER(Pool), P, P, P, I32, I32, P]),
-    "echo_prefetch_begin": (C.c_int, [C.POINTER(Pool), P, P, P, P, P, I32, P, SZ, P]),
-    "echo_prefetch_gather": (C.c_int, [C.POINTER(Pool), P, P, P, P, P, I32, I32, P, I32, P,
-                                       P, P, P, P]),
+    "echo_prefetch_begin": (C.c_int, [C.POINTER(Pool), P, P, P]),
+    "echo_prefetch_gather": (C.c_int, [C.POINTER(Pool), P, P, P, P, I32, I32, P, P, P, P]),
     "echo_decode_workspace_bytes": (SZ, [C.POINTER(DecodeArgs), I32]),
     "echo_decode_select": (C.c_int, [C.POINTER(DecodeArgs), C.POINTER(Pool),
                                      C.POINTER(DecodeOut), P, SZ, P, P]),
@@ -134,13 +133,25 @@ def index_scores(q, w, k, k_scale, key_begin, key_len, max_key_len, scores, ld=N
 
 
 def index_scores_prefetch(q, w, k, k_scale, key_begin, key_len, max_key_len, tok_lo, tok_hi,
-                          scores, theta, req_to_host, host_to_gpu, cand, cand_cnt, cap,
-                          cap_div, ld=None, stream=None):
+                          scores, theta, req_to_host, host_to_gpu, cand, cand_cnt, total_cnt,
+                          cap, cap_div, ld=None, stream=None):
     ld = scores.shape[-1] if ld is None else ld
     _call("echo_index_scores_prefetch", ptr(q), ptr(w), ptr(k), ptr(k_scale), ptr(key_begin),
           ptr(key_len), q.shape[0], max_key_len, tok_lo, tok_hi, ptr(scores), ld, ptr(theta),
-          ptr(req_to_host), ptr(host_to_gpu), ptr(cand), ptr(cand_cnt), cap, cap_div,
+          ptr(req_to_host), ptr(host_to_gpu), ptr(cand), ptr(cand_cnt), ptr(total_cnt), cap,
+          cap_div, stream_handle(stream))
+
+
+def prefetch_begin(pool, free_list, free_count, stream=None):
+    _call("echo_prefetch_begin", C.byref(pool), ptr(free_list), ptr(free_count),
           stream_handle(stream))
+
+
+def prefetch_gather(pool, key_begin, req_to_host, cand, cand_cnt, cap, free_list, free_count,
+                    n_prefetched, stream=None):
+    _call("echo_prefetch_gather", C.byref(pool), ptr(key_begin), ptr(req_to_host), ptr(cand),
+          ptr(cand_cnt), cand_cnt.shape[0], cap, ptr(free_list), ptr(free_count),
+          ptr(n_prefetched), stream_handle(stream))
 
 
 def prefetch_threshold(q, w, k, k_scale, key_begin, key_len, n_sample, percentile, theta,

@@ -1,0 +1,239 @@
+// The whole decode step (ECHO review page §4): indexer scores -> [threshold prefetch on a
+// side stream, §6.1] -> exact top-k -> lookup / evict / allocate (§5.2) -> recall gather ->
+// priorities.  Every call only enqueues work, so the step can be captured into one hipGraph
+// (§2: graph execution forbids host control and dynamically sized tensors inside the step).
+//
+// With prefetch, scoring is split into n_chunks token ranges.  After each range the main
+// stream records an event; the side stream waits for it and runs the prefetch gather of that
+// range's candidates while the main stream scores the next range.  The main stream waits for
+// the side stream's last gather before the guaranteed lookup/allocation, which must see every
+// row prefetch made resident.
+#include <mutex>
+#include <vector>
+
+#include "internal.hpp"
+
+namespace echo {
+
+static size_t al(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+struct DecodeWs {
+  void *topk_ws;
+  size_t topk_bytes;
+  void *pool_ws;
+  size_t pool_bytes;
+  float *theta;        // [n_rows]
+  int32_t *cand;       // [n_chunks][n_rows][cap]
+  int32_t *cand_cnt;   // [n_chunks][n_rows]
+  int32_t *total_cnt;  // [n_rows]
+  int32_t *free_list;  // [n_gpu]
+  int32_t *free_count; // [2]
+};
+
+static size_t decode_ws_layout(const echo_decode_args *a, int32_t n_gpu, void *base, DecodeWs *w) {
+  size_t off = 0;
+  auto take = [&](size_t b) { size_t o = off; off += al(b); return o; };
+  const size_t tb = topk_ws_bytes(a->n_rows, a->max_key_len);
+  const size_t pb = pool_ws_bytes(a->n_rows, a->topk, n_gpu);
+  const size_t o_t = take(tb), o_p = take(pb);
+  size_t o_th = 0, o_c = 0, o_cc = 0, o_tc = 0, o_fl = 0, o_fc = 0;
+  if (a->prefetch) {
+    const size_t nc = static_cast<size_t>(a->n_chunks), nr = static_cast<size_t>(a->n_rows);
+    o_th = take(nr * 4);
+    o_c = take(nc * nr * static_cast<size_t>(a->cap) * 4);
+    o_cc = take(nc * nr * 4);
+    o_tc = take(nr * 4);
+    o_fl = take(static_cast<size_t>(n_gpu) * 4);
+    o_fc = take(2 * 4);
+  }
+  if (w && base) {
+    char *b = static_cast<char *>(base);
+    w->topk_ws = b + o_t;
+    w->topk_bytes = tb;
+    w->pool_ws = b + o_p;
+    w->pool_bytes = pb;
+    if (a->prefetch) {
+      w->theta = reinterpret_cast<float *>(b + o_th);
+      w->cand = reinterpret_cast<int32_t *>(b + o_c);
+      w->cand_cnt = reinterpret_cast<int32_t *>(b + o_cc);
+      w->total_cnt = reinterpret_cast<int32_t *>(b + o_tc);
+      w->free_list = reinterpret_cast<int32_t *>(b + o_fl);
+      w->free_count = reinterpret_cast<int32_t *>(b + o_fc);
+    }
+  }
+  return off;
+}
+
+// Fork/join events, created once per thread and reused (never during a capture).
+static thread_local std::vector<hipEvent_t> t_events;
+
+static int ensure_events(size_t n) {
+  while (t_events.size() < n) {
+    hipEvent_t e;
+    hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (err != hipSuccess) return fail(ECHO_EHIP, "hipEventCreate: %s", hipGetErrorString(err));
+    t_events.push_back(e);
+  }
+  return ECHO_OK;
+}
+
+static int validate(const echo_decode_args *a, const echo_pool *pool, const echo_decode_out *o) {
+  if (!a || !pool || !o) return fail(ECHO_EINVAL, "echo_decode_select: NULL argument");
+  if (a->n_rows < 1 || a->n_rows > 65535) return fail(ECHO_EUNSUPPORTED, "echo_decode_select: n_rows %d outside [1, 65535]", a->n_rows);
+  if (a->max_key_len < 0) return fail(ECHO_EINVAL, "echo_decode_select: max_key_len < 0");
+  if (a->topk < 1 || a->topk > ECHO_MAX_TOPK) return fail(ECHO_EUNSUPPORTED, "echo_decode_select: topk %d outside [1, %d]", a->topk, ECHO_MAX_TOPK);
+  if (!a->q || !a->w || !a->key_begin || !a->key_len || !a->req_to_host || (a->max_key_len > 0 && !a->k))
+    return fail(ECHO_EINVAL, "echo_decode_select: NULL input");
+  if (!o->scores || !o->topk_idx || !o->topk_slot || !o->miss_host || !o->miss_slot || !o->counters)
+    return fail(ECHO_EINVAL, "echo_decode_select: NULL output");
+  if (pool->n_gpu < 1 || pool->n_host < 1 || !pool->gpu_free || !pool->gpu_priority || !pool->gpu_to_host ||
+      !pool->host_to_gpu || !pool->indices_buf || !pool->gpu_kv || !pool->host_kv || !pool->status)
+    return fail(ECHO_EINVAL, "echo_decode_select: incomplete pool");
+  if (a->prefetch) {
+    if (a->n_chunks < 1 || a->n_chunks > 16) return fail(ECHO_EUNSUPPORTED, "echo_decode_select: n_chunks %d outside [1, 16]", a->n_chunks);
+    if (a->n_sample < 64 || a->n_sample > 4096 || (a->n_sample & (a->n_sample - 1)))
+      return fail(ECHO_EUNSUPPORTED, "echo_decode_select: n_sample must be a power of two in [64, 4096]");
+    if (!(a->percentile > 0.f && a->percentile <= 100.f)) return fail(ECHO_EINVAL, "echo_decode_select: percentile outside (0, 100]");
+    if (a->cap < 1 || a->cap_div < 1) return fail(ECHO_EINVAL, "echo_decode_select: cap and cap_div must be >= 1");
+  }
+  return ECHO_OK;
+}
+
+static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
+                              const echo_decode_out *o, void *ws, size_t ws_bytes,
+                              hipStream_t m, hipStream_t sd) {
+  int rc = validate(a, pool, o);
+  if (rc) return rc;
+  DecodeWs W{};
+  const size_t need = decode_ws_layout(a, pool->n_gpu, ws, &W);
+  if (!ws || ws_bytes < need) return fail(ECHO_EWORKSPACE, "echo_decode_select: workspace %zu < %zu", ws_bytes, need);
+  const int64_t n_k_max = INT64_MAX;   // token indices come from our own top-k: always in range
+  const int32_t n_ent = a->n_rows * a->topk;
+  const bool pf = a->prefetch != 0;
+  const bool split = pf && sd != m;
+
+  if ((rc = launch_zero_i32(o->counters, 8, m))) return rc;
+  if (pf) {
+    const int nc = a->n_chunks;
+    if ((rc = ensure_events(static_cast<size_t>(nc) + 1))) return rc;
+    if ((rc = launch_zero_i32(W.cand_cnt, static_cast<int64_t>(nc) * a->n_rows, m))) return rc;
+    if ((rc = launch_zero_i32(W.total_cnt, a->n_rows, m))) return rc;
+    if ((rc = launch_prefetch_threshold(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len,
+                                        a->n_rows, a->n_sample, a->percentile, W.theta, m)))
+      return rc;
+    if ((rc = launch_prefetch_begin(pool, W.free_list, W.free_count, m))) return rc;
+    const int32_t span = (a->max_key_len + nc - 1) / nc;
+    for (int c = 0; c < nc; ++c) {
+      const int32_t lo = c * span, hi = (c + 1 == nc) ? a->max_key_len : (c + 1) * span;
+      PrefetchArgs P{W.theta, a->req_to_host, pool->host_to_gpu,
+                     W.cand + static_cast<int64_t>(c) * a->n_rows * a->cap,
+                     W.cand_cnt + static_cast<int64_t>(c) * a->n_rows, W.total_cnt, a->cap, a->cap_div};
+      if ((rc = launch_score_decode(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len, a->n_rows,
+                                    a->max_key_len, lo, hi, o->scores, a->max_key_len, &P, m)))
+        return rc;
+      hipStream_t gs = m;
+      if (split) {
+        hipError_t e = hipEventRecord(t_events[c], m);
+        if (e == hipSuccess) e = hipStreamWaitEvent(sd, t_events[c], 0);
+        if (e != hipSuccess) return fail(ECHO_EHIP, "decode fork: %s", hipGetErrorString(e));
+        gs = sd;
+      }
+      if ((rc = launch_prefetch_gather(pool, a->key_begin, a->req_to_host, P.cand, P.cand_cnt,
+                                       a->n_rows, a->cap, W.free_list, W.free_count,
+                                       o->counters + 2, gs)))
+        return rc;
+    }
+  } else {
+    if ((rc = launch_score_decode(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len, a->n_rows,
+                                  a->max_key_len, 0, a->max_key_len, o->scores, a->max_key_len,
+                                  nullptr, m)))
+      return rc;
+  }
+  if ((rc = launch_topk(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len, a->topk,
+                        o->topk_idx, W.topk_ws, W.topk_bytes, m)))
+    return rc;
+  if (pf && (rc = launch_sum_i32(W.total_cnt, a->n_rows, o->counters + 1, m))) return rc;
+  if (split) {
+    hipEvent_t join = t_events[a->n_chunks];
+    hipError_t e = hipEventRecord(join, sd);
+    if (e == hipSuccess) e = hipStreamWaitEvent(m, join, 0);
+    if (e != hipSuccess) return fail(ECHO_EHIP, "decode join: %s", hipGetErrorString(e));
+  }
+  if ((rc = launch_pool_lookup_alloc(pool, o->topk_idx, a->key_begin, a->req_to_host, n_k_max,
+                                     a->n_rows, a->topk, a->step_id, o->topk_slot, o->miss_host,
+                                     o->miss_slot, o->counters + 0, W.pool_ws, W.pool_bytes, m)))
+    return rc;
+  if ((rc = launch_recall_gather(pool, o->miss_host, o->miss_slot, o->counters + 0, n_ent, m))) return rc;
+  return ECHO_OK;
+}
+
+struct GraphHandle {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+}  // namespace echo
+
+using namespace echo;
+
+struct echo_graph_s : GraphHandle {};
+
+extern "C" size_t echo_decode_workspace_bytes(const echo_decode_args *a, int32_t n_gpu) {
+  if (!a || n_gpu < 0 || a->n_rows < 0 || a->topk < 0 || a->max_key_len < 0) return 0;
+  if (a->prefetch && (a->n_chunks < 1 || a->cap < 0)) return 0;
+  return decode_ws_layout(a, n_gpu, nullptr, nullptr);
+}
+
+extern "C" int echo_decode_select(const echo_decode_args *a, const echo_pool *pool,
+                                  const echo_decode_out *out, void *ws, size_t ws_bytes,
+                                  void *main_stream, void *side_stream) {
+  return decode_select_impl(a, pool, out, ws, ws_bytes, S(main_stream), S(side_stream));
+}
+
+extern "C" int echo_graph_capture_decode(const echo_decode_args *a, const echo_pool *pool,
+                                         const echo_decode_out *out, void *ws, size_t ws_bytes,
+                                         void *main_stream, void *side_stream, echo_graph *graph) {
+  if (!graph) return fail(ECHO_EINVAL, "echo_graph_capture_decode: NULL graph");
+  *graph = nullptr;
+  if (!main_stream) return fail(ECHO_EINVAL, "echo_graph_capture_decode: capture needs a non-null main stream");
+  int rc = validate(a, pool, out);
+  if (rc) return rc;
+  if (a->prefetch && (rc = ensure_events(static_cast<size_t>(a->n_chunks) + 1))) return rc;
+  hipStream_t m = S(main_stream);
+  hipError_t e = hipStreamBeginCapture(m, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return fail(ECHO_EHIP, "hipStreamBeginCapture: %s", hipGetErrorString(e));
+  rc = decode_select_impl(a, pool, out, ws, ws_bytes, m, S(side_stream));
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(m, &g);
+  if (rc) {
+    if (g) (void)hipGraphDestroy(g);
+    return rc;
+  }
+  if (e != hipSuccess) return fail(ECHO_EHIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+  hipGraphExec_t ex = nullptr;
+  e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return fail(ECHO_EHIP, "hipGraphInstantiate: %s", hipGetErrorString(e));
+  }
+  echo_graph_s *h = new echo_graph_s;
+  h->graph = g;
+  h->exec = ex;
+  *graph = h;
+  return ECHO_OK;
+}
+
+extern "C" int echo_graph_launch(echo_graph graph, void *stream) {
+  if (!graph) return fail(ECHO_EINVAL, "echo_graph_launch: NULL graph");
+  hipError_t e = hipGraphLaunch(graph->exec, S(stream));
+  if (e != hipSuccess) return fail(ECHO_EHIP, "hipGraphLaunch: %s", hipGetErrorString(e));
+  return ECHO_OK;
+}
+
+extern "C" int echo_graph_destroy(echo_graph graph) {
+  if (!graph) return ECHO_OK;
+  (void)hipGraphExecDestroy(graph->exec);
+  (void)hipGraphDestroy(graph->graph);
+  delete graph;
+  return ECHO_OK;
+}

@@ -1,0 +1,53 @@
+// Launch helpers shared between the library's translation units (host side).
+#pragma once
+
+#include "common.hpp"
+
+namespace echo {
+
+struct PrefetchArgs {
+  const float *theta;        // [n_q]
+  const int32_t *req_to_host;// [n_k]
+  const int32_t *host_to_gpu;// [n_host]
+  int32_t *cand;             // [n_q, cap] this call's list
+  int32_t *cand_cnt;         // [n_q] this call's list lengths
+  int32_t *total_cnt;        // [n_q] over-threshold non-resident tokens of the step so far
+  int32_t cap;
+  int32_t cap_div;
+};
+
+int launch_score_decode(const uint8_t *q, const float *w, const uint8_t *k, const float *k_scale,
+                        const int64_t *key_begin, const int32_t *key_len, int32_t n_q,
+                        int32_t max_len, int32_t tok_lo, int32_t tok_hi, float *scores,
+                        int64_t ld, const PrefetchArgs *pf, hipStream_t st);
+
+size_t topk_ws_bytes(int32_t n_rows, int32_t max_len);
+int launch_topk(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
+                int32_t max_len, int32_t k, int32_t *idx, void *ws, size_t ws_bytes,
+                hipStream_t st);
+
+size_t pool_ws_bytes(int32_t n_rows, int32_t k, int32_t n_gpu);
+int launch_pool_lookup_alloc(const echo_pool *pool, const int32_t *idx, const int64_t *key_begin,
+                             const int32_t *req_to_host, int64_t n_k, int32_t n_rows, int32_t k,
+                             int32_t step_id, int32_t *topk_slot, int32_t *miss_host,
+                             int32_t *miss_slot, int32_t *n_miss, void *ws, size_t ws_bytes,
+                             hipStream_t st);
+
+int launch_recall_gather(const echo_pool *pool, const int32_t *miss_host, const int32_t *miss_slot,
+                         const int32_t *n_miss, int32_t max_miss, hipStream_t st);
+
+int launch_prefetch_threshold(const uint8_t *q, const float *w, const uint8_t *k,
+                              const float *k_scale, const int64_t *key_begin,
+                              const int32_t *key_len, int32_t n_q, int32_t n_sample,
+                              float percentile, float *theta, hipStream_t st);
+int launch_prefetch_begin(const echo_pool *pool, int32_t *free_list, int32_t *free_count,
+                          hipStream_t st);
+int launch_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
+                           const int32_t *req_to_host, const int32_t *cand,
+                           const int32_t *cand_cnt, int32_t n_q, int32_t cap,
+                           const int32_t *free_list, int32_t *free_count, int32_t *n_prefetched,
+                           hipStream_t st);
+int launch_zero_i32(int32_t *p, int64_t n, hipStream_t st);
+int launch_sum_i32(const int32_t *v, int32_t n, int32_t *out, hipStream_t st);
+
+}  // namespace echo

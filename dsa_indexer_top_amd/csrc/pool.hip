@@ -17,6 +17,7 @@
 // Data-dependent failures set status bits; every later kernel then leaves the pool alone.
 #include <algorithm>
 
+#include "internal.hpp"
 #include "select.cuh"
 
 namespace echo {

@@ -13,7 +13,7 @@
 #include <algorithm>
 #include <vector>
 
-#include "common.hpp"
+#include "internal.hpp"
 
 namespace echo {
 

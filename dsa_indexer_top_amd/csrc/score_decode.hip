@@ -9,36 +9,22 @@
 // computed), and writes them into an LDS double buffer whose 16-byte segments are XOR-swizzled
 // by token so the MFMA-layout reads below are bank-conflict free.
 //
-// Contraction: v_mfma_f32_16x16x128_f8f6f4 with A = q of 16 heads (16 x 128) held in VGPRs for
-// the whole kernel and B = k of 16 tokens (128 x 16) read from LDS.  One MFMA covers the full
-// d = 128 dot product of 16 heads x 16 tokens; four MFMAs cover the 64 heads.  Lane l holds
-// output rows (heads) 4*(l/16) .. +3 of token l%16, so the ReLU * w head reduction is 16 FMAs
-// per lane followed by a two-step cross-lane sum (lanes l, l^16, l^32, l^48).
+// Contraction (score_tile.cuh): v_mfma_f32_16x16x128_f8f6f4, A = q of 16 heads held in VGPRs
+// for the whole kernel, B = k of 16 tokens read from LDS; four MFMAs cover the 64 heads and
+// the ReLU * w head reduction is 16 FMAs per lane plus a two-step cross-lane sum.
 //
-// The MFMA's K index is distributed over the 4 lane groups; A and B use the same lane-group
-// -> K mapping, so any assignment of the 128 bytes of a row to (group, byte) works as long as
-// q and k use the same one.  Here group g holds bytes [32g, 32g + 32) of both.
-#include "common.hpp"
+// Prefetch candidates: each call appends to its own list (cand, cand_cnt), so a consumer on
+// another stream that waits for this kernel sees a complete list; the per-request cap is a
+// counter shared by all calls of one step (total_cnt).
+#include "internal.hpp"
+#include "score_tile.cuh"
 
 namespace echo {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int SD_THREADS = 256;
 constexpr int SD_CHUNK = 128;                                    // tokens per LDS stage
 constexpr int SD_UNITS = SD_CHUNK * D / 16;                      // 16-byte units per chunk
 constexpr int SD_LOADS = SD_UNITS / SD_THREADS;                  // per thread per chunk = 4
-
-struct PrefetchArgs {
-  const float *theta;        // [n_q]
-  const int32_t *req_to_host;// [n_k]
-  const int32_t *host_to_gpu;// [n_host]
-  int32_t *cand;             // [n_q, cap]
-  int32_t *cand_cnt;         // [n_q]
-  int32_t cap;
-  int32_t cap_div;
-};
 
 ECHO_DEV int swz(int tok, int seg) { return tok * 128 + ((seg ^ ((tok >> 1) & 7)) << 4); }
 
@@ -63,17 +49,8 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
   const int j = l & 15, g = l >> 4;
 
-  // A operand: q rows of heads hb*16 + j, bytes [32g, 32g+32)
-  v8i qa[4];
-  float wr[4][4];
-#pragma unroll
-  for (int hb = 0; hb < 4; ++hb) {
-    const int4 *p = reinterpret_cast<const int4 *>(q + ((static_cast<int64_t>(r) * H + hb * 16 + j) * D + 32 * g));
-    int4 a0 = p[0], a1 = p[1];
-    qa[hb] = v8i{a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-    for (int v = 0; v < 4; ++v) wr[hb][v] = w[r * H + hb * 16 + 4 * g + v];
-  }
+  QOperand qo;
+  load_q_operand(q, w, r, qo);
 
   float theta = 0.f;
   int32_t cap_r = 0;
@@ -113,21 +90,7 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
       const int tt = wv * 32 + tile * 16 + j;
       const int4 b0 = *reinterpret_cast<const int4 *>(sb + swz(tt, 2 * g));
       const int4 b1 = *reinterpret_cast<const int4 *>(sb + swz(tt, 2 * g + 1));
-      const v8i bv = v8i{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      float acc = 0.f;
-#pragma unroll
-      for (int hb = 0; hb < 4; ++hb) {
-        v4f c = {0.f, 0.f, 0.f, 0.f};
-        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[hb], bv, c, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc = fmaf(wr[hb][v], fmaxf(c[v], 0.f), acc);
-      }
-      part[tile] = acc;
-    }
-#pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      part[tile] += __shfl_xor(part[tile], 16, 64);
-      part[tile] += __shfl_xor(part[tile], 32, 64);
+      part[tile] = reduce_groups(score_tile_partial(qo, v8i{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w}));
     }
     if (g < 2) {
       const int32_t t = c0 + wv * 32 + g * 16 + j;
@@ -139,8 +102,10 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
           if (s > theta) {
             const int32_t h = pf.req_to_host[kb + t];
             if (pf.host_to_gpu[h] == INF) {
-              const int32_t pos = atomicAdd(&pf.cand_cnt[r], 1);
-              if (pos < cap_r) pf.cand[static_cast<int64_t>(r) * pf.cap + pos] = t;
+              if (atomicAdd(&pf.total_cnt[r], 1) < cap_r) {
+                const int32_t pos = atomicAdd(&pf.cand_cnt[r], 1);
+                pf.cand[static_cast<int64_t>(r) * pf.cap + pos] = t;
+              }
             }
           }
         }
@@ -206,17 +171,17 @@ extern "C" int echo_index_scores_prefetch(const uint8_t *q, const float *w, cons
                                           int32_t max_key_len, int32_t tok_lo, int32_t tok_hi,
                                           float *scores, int64_t ld, const float *theta,
                                           const int32_t *req_to_host, const int32_t *host_to_gpu,
-                                          int32_t *cand, int32_t *cand_cnt, int32_t cap,
-                                          int32_t cap_div, void *stream) {
+                                          int32_t *cand, int32_t *cand_cnt, int32_t *total_cnt,
+                                          int32_t cap, int32_t cap_div, void *stream) {
   if (n_q < 0 || max_key_len < 0) return fail(ECHO_EINVAL, "echo_index_scores_prefetch: negative n_q or max_key_len");
   if (ld < max_key_len) return fail(ECHO_EINVAL, "echo_index_scores_prefetch: ld < max_key_len");
   if (n_q > 65535) return fail(ECHO_EUNSUPPORTED, "echo_index_scores_prefetch: n_q > 65535");
   if (tok_lo < 0 || tok_hi < tok_lo) return fail(ECHO_EINVAL, "echo_index_scores_prefetch: bad token range");
   if (cap < 0 || cap_div < 1) return fail(ECHO_EINVAL, "echo_index_scores_prefetch: cap < 0 or cap_div < 1");
   if (n_q > 0 && (!q || !w || !key_begin || !key_len || !scores || !theta || !req_to_host ||
-                  !host_to_gpu || !cand_cnt || (cap > 0 && !cand) || (max_key_len > 0 && !k)))
+                  !host_to_gpu || !cand_cnt || !total_cnt || (cap > 0 && !cand) || (max_key_len > 0 && !k)))
     return fail(ECHO_EINVAL, "echo_index_scores_prefetch: NULL pointer");
-  PrefetchArgs pf{theta, req_to_host, host_to_gpu, cand, cand_cnt, cap, cap_div};
+  PrefetchArgs pf{theta, req_to_host, host_to_gpu, cand, cand_cnt, total_cnt, cap, cap_div};
   return launch_score_decode(q, w, k, k_scale, key_begin, key_len, n_q, max_key_len, tok_lo,
                              tok_hi, scores, ld, &pf, S(stream));
 }

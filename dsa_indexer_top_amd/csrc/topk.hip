@@ -8,6 +8,7 @@
 // workgroup): three histogram passes, one count pass, one apply pass.
 #include <algorithm>
 
+#include "internal.hpp"
 #include "select.cuh"
 
 namespace echo {
@@ -30,6 +31,13 @@ __global__ void zero_u32_kernel(uint32_t *p, int64_t n) {
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x)
     p[i] = 0u;
+}
+
+int launch_zero_i32(int32_t *p, int64_t n, hipStream_t st) {
+  if (n <= 0) return ECHO_OK;
+  zero_u32_kernel<<<static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 4096)), 256, 0, st>>>(
+      reinterpret_cast<uint32_t *>(p), n);
+  return check_launch("zero");
 }
 
 template <int DIG>
@@ -142,6 +150,10 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_apply_kernel(TopkSrc src, Se
   }
 }
 
+size_t topk_ws_bytes(int32_t n_rows, int32_t max_len) {
+  return sel_ws_bytes(n_rows, std::max(1, (max_len + SEL_CHUNK - 1) / SEL_CHUNK));
+}
+
 int launch_topk(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
                 int32_t max_len, int32_t k, int32_t *idx, void *ws, size_t ws_bytes,
                 hipStream_t st) {
@@ -172,7 +184,7 @@ using namespace echo;
 
 extern "C" size_t echo_topk_workspace_bytes(int32_t n_rows, int32_t max_len) {
   if (n_rows < 0 || max_len < 0) return 0;
-  return sel_ws_bytes(n_rows, std::max(1, (max_len + SEL_CHUNK - 1) / SEL_CHUNK));
+  return topk_ws_bytes(n_rows, max_len);
 }
 
 extern "C" int echo_topk(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,

@@ -23,8 +23,9 @@ Value recipes:
                 w uniform integers in [-4, 4] / 64
   general:      q, k ~ N(0,1) rounded to E4M3FN (nearest even);
                 w ~ N(0,1)/8; k scale ~ U[0.5, 2]
-  latent rows:  576 bf16 bit patterns per token, uniform random with bit 14
-                cleared (finite, |x| < 2, never the 0xFFFF poison pattern);
+  latent rows:  576 bf16 bit patterns per token, uniform random bits (PCG64 raw
+                output) with bit 14 cleared (finite, |x| < 2, never the 0xFFFF
+                poison pattern);
                 the recall copies bits, so their distribution is immaterial
   host slots:   the tokens of all requests occupy a seeded permutation of
                 the host pool
@@ -96,18 +97,35 @@ def e4m3_from_f32(x):
         torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
-def fp8_values(seed, tag, shape, grid, chunk=1 << 26):
-    """uint8 E4M3FN array of the given shape, integer-grid or N(0,1)."""
+def fp8_values(seed, tag, shape, grid, chunk=1 << 24, workers=None):
+    """uint8 E4M3FN array of the given shape, integer-grid or N(0,1).
+
+    Drawn in chunks of `chunk` values, chunk c from PCG64 seeded by (seed, tag, c), so the
+    content does not depend on the number of worker threads.
+    """
+    import concurrent.futures as cf
+    import os
     n = int(np.prod(shape))
     out = np.empty(n, np.uint8)
-    rng = rng_for(seed, tag)
     table = _int_to_e4m3_table() if grid == "int" else None
-    for s in range(0, n, chunk):
+
+    def one(c):
+        s = c * chunk
         m = min(chunk, n - s)
+        rng = np.random.default_rng([int(seed), _TAGS[tag], c])
         if grid == "int":
             out[s:s + m] = table[rng.integers(0, 17, m, dtype=np.int8)]
         else:
             out[s:s + m] = e4m3_from_f32(rng.standard_normal(m, dtype=np.float32))
+
+    n_chunks = (n + chunk - 1) // chunk
+    workers = workers or min(16, os.cpu_count() or 1)
+    if n_chunks <= 1 or workers <= 1:
+        for c in range(n_chunks):
+            one(c)
+    else:
+        with cf.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one, range(n_chunks)))
     return out.reshape(shape)
 
 
@@ -125,13 +143,32 @@ def request_lengths(cfg):
     return np.full(cfg.batch, int(cfg.lengths), np.int32)
 
 
-def fill_latent_rows(seed, out, chunk_rows=1 << 18):
-    """Fill a uint16 [N, 576] array (may be pinned host memory) in place."""
-    rng = rng_for(seed, "kv")
+def fill_latent_rows(seed, out, chunk_rows=1 << 16, workers=None):
+    """Fill a uint16 [N, 576] array (may be pinned host memory) in place.
+
+    Rows are drawn in chunks of `chunk_rows`, chunk c from PCG64 seeded by (seed, tag, c), so
+    the content does not depend on the number of worker threads.
+    """
+    import concurrent.futures as cf
+    import os
     n = out.shape[0]
-    for s in range(0, n, chunk_rows):
+    flat = out.reshape(n, ROW_ELEMS)
+
+    def one(c):
+        s = c * chunk_rows
         m = min(chunk_rows, n - s)
-        out[s:s + m] = rng.integers(0, 1 << 16, (m, ROW_ELEMS), dtype=np.uint16) & np.uint16(0xBFFF)
+        bg = np.random.default_rng([int(seed), _TAGS["kv"], c]).bit_generator
+        raw = bg.random_raw(m * ROW_ELEMS // 4).view(np.uint16).reshape(m, ROW_ELEMS)
+        np.bitwise_and(raw, np.uint16(0xBFFF), out=flat[s:s + m])
+
+    n_chunks = (n + chunk_rows - 1) // chunk_rows
+    workers = workers or min(16, os.cpu_count() or 1)
+    if n_chunks <= 1 or workers <= 1:
+        for c in range(n_chunks):
+            one(c)
+    else:
+        with cf.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one, range(n_chunks)))
     return out
 
 

@@ -1,0 +1,112 @@
+"""Device-buffer plumbing for one decode step: holds the inputs, the pool (with a pristine
+copy to restore between timed replays), the outputs and the workspace, and calls the C ABI
+(eagerly or through a captured hipGraph).  No arithmetic of the method lives here.
+"""
+
+import numpy as np
+
+from . import binding as B
+
+DEFAULT_PREFETCH = dict(n_chunks=4, n_sample=4096, percentile=95.0, cap=2048, cap_div=1024)
+
+
+def _dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+class DecodeRunner:
+    """inp: inputs.DecodeInputs; pool: inputs.PoolArrays; host_kv: uint16 [N_H, 576] numpy
+    array, or a binding.HostBuffer already holding it (pass host_buf=...)."""
+
+    def __init__(self, inp, pool, host_kv=None, host_buf=None, prefetch=False, pf=None,
+                 topk=None, step_id=None):
+        import torch
+        self.torch = torch
+        cfg = inp.cfg
+        self.inp = inp
+        self.n_rows = len(inp.key_len)
+        self.max_len = int(inp.key_len.max())
+        self.topk = cfg.topk if topk is None else topk
+        self.step_id = pool.step_id if step_id is None else step_id
+        self.q, self.w, self.k = _dev(inp.q), _dev(inp.w), _dev(inp.k)
+        self.k_scale = None if inp.k_scale is None else _dev(inp.k_scale)
+        self.key_begin, self.key_len = _dev(inp.key_begin), _dev(inp.key_len)
+        self.req_to_host = _dev(inp.req_to_host)
+        # pool + pristine copy
+        names = ("free", "priority", "to_host", "host_to_gpu", "indices_buf", "gpu_kv")
+        self.pristine = {n: _dev(getattr(pool, n)) for n in names}
+        self.live = {n: t.clone() for n, t in self.pristine.items()}
+        self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        if host_buf is None:
+            host_buf = B.HostBuffer(host_kv.nbytes)
+            host_buf.array.view(np.uint16).reshape(host_kv.shape)[...] = host_kv
+            self._own_buf = True
+        else:
+            self._own_buf = False
+        self.host_buf = host_buf
+        self.n_gpu, self.n_host = len(pool.free), len(pool.host_to_gpu)
+        L = self.live
+        self.pool = B.make_pool(self.n_gpu, self.n_host, L["free"], L["priority"], L["to_host"],
+                                L["host_to_gpu"], L["indices_buf"], L["gpu_kv"],
+                                host_buf.dev_ptr, self.status)
+        # outputs
+        i32 = torch.int32
+        self.scores = torch.empty((self.n_rows, max(self.max_len, 1)), dtype=torch.float32, device="cuda")
+        self.topk_idx = torch.empty((self.n_rows, self.topk), dtype=i32, device="cuda")
+        self.topk_slot = torch.empty((self.n_rows, self.topk), dtype=i32, device="cuda")
+        self.miss_host = torch.empty(self.n_rows * self.topk, dtype=i32, device="cuda")
+        self.miss_slot = torch.empty(self.n_rows * self.topk, dtype=i32, device="cuda")
+        self.counters = torch.zeros(8, dtype=i32, device="cuda")
+        self.out = B.DecodeOut(self.scores.data_ptr(), self.topk_idx.data_ptr(),
+                               self.topk_slot.data_ptr(), self.miss_host.data_ptr(),
+                               self.miss_slot.data_ptr(), self.counters.data_ptr())
+        p = dict(DEFAULT_PREFETCH)
+        p.update(pf or {})
+        self.args = B.DecodeArgs(
+            self.q.data_ptr(), self.w.data_ptr(), self.k.data_ptr(),
+            None if self.k_scale is None else self.k_scale.data_ptr(),
+            self.key_begin.data_ptr(), self.key_len.data_ptr(), self.req_to_host.data_ptr(),
+            self.n_rows, self.max_len, self.topk, self.step_id, 1 if prefetch else 0,
+            p["n_chunks"], p["n_sample"], p["percentile"], p["cap"], p["cap_div"])
+        nbytes = B.decode_workspace_bytes(self.args, self.n_gpu)
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        self.main = torch.cuda.Stream()
+        self.side = torch.cuda.Stream() if prefetch else self.main
+        self.graph = None
+
+    def restore(self):
+        """Put the pool back to its state before the step (outside any timed region)."""
+        with self.torch.cuda.stream(self.main):
+            for n, t in self.pristine.items():
+                self.live[n].copy_(t)
+            self.status.zero_()
+
+    def run_eager(self):
+        B.decode_select(self.args, self.pool, self.out, self.ws, self.main, self.side)
+
+    def capture(self):
+        self.torch.cuda.synchronize()
+        self.graph = B.Graph(self.args, self.pool, self.out, self.ws, self.main, self.side)
+        return self.graph
+
+    def replay(self):
+        self.graph.launch(self.main)
+
+    def sync(self):
+        self.torch.cuda.synchronize()
+
+    def results(self):
+        self.sync()
+        h = lambda t: t.cpu().numpy()
+        return dict(scores=h(self.scores), topk_idx=h(self.topk_idx), topk_slot=h(self.topk_slot),
+                    miss_host=h(self.miss_host), miss_slot=h(self.miss_slot),
+                    counters=h(self.counters), status=int(h(self.status)[0]),
+                    pool={n: h(t) for n, t in self.live.items()})
+
+    def close(self):
+        if self.graph is not None:
+            self.graph.close()
+            self.graph = None
+        if self._own_buf:
+            self.host_buf.close()

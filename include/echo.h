@@ -124,16 +124,18 @@ int echo_index_scores(const uint8_t *q, const float *w, const uint8_t *k, const 
                       int32_t max_key_len, float *scores, int64_t ld, void *stream);
 
 /*
- * Threshold prefetch fused into scoring (§6.1).  The same scores as echo_index_scores, and in
- * addition every scored token s of request r with score > theta[r] that is not resident
- * (host_to_gpu[req_to_host[key_begin[r] + s]] == ECHO_INF) is appended to cand[r*cap + j]
- * while the per-request counter cand_cnt[r] is below cap_r = min(cap, ceil(key_len[r] /
- * cap_div)).  The counter keeps counting past cap_r (it reports demand); only the first cap_r
- * slots are written.  Which over-threshold tokens win the slots depends on timing; the set of
- * scores never does.  Tokens [tok_lo, tok_hi) of every request are scored by this call, so a
- * step can be split into chunks that a side stream consumes (echo_prefetch_gather).
+ * Threshold prefetch fused into scoring (§6.1).  Scores tokens [tok_lo, tok_hi) of every
+ * request exactly as echo_index_scores does, and in addition appends every scored token s with
+ * score > theta[r] that is not resident (host_to_gpu[req_to_host[key_begin[r] + s]] ==
+ * ECHO_INF) to this call's list cand[r*cap + j], j < cand_cnt[r], as long as the step-wide
+ * per-request counter total_cnt[r] is below cap_r = min(cap, ceil(key_len[r] / cap_div)) (the
+ * page's global prefetch counter, bounded in proportion to the context length).  total_cnt
+ * keeps counting past the cap (it reports demand).  Which over-threshold tokens win the slots
+ * depends on timing; the scores never do.  Because each call has its own list, a consumer on
+ * another stream that waits for this call sees a complete list (echo_prefetch_gather).
  *   theta [n_q] fp32; req_to_host [n_k] int32; host_to_gpu [n_host]; cand [n_q, cap] int32;
- *   cand_cnt [n_q] int32 (caller zeroes it before the first chunk).
+ *   cand_cnt [n_q] (zeroed by the caller before this call); total_cnt [n_q] (zeroed once per
+ *   step).
  */
 int echo_index_scores_prefetch(const uint8_t *q, const float *w, const uint8_t *k,
                                const float *k_scale, const int64_t *key_begin,
@@ -141,7 +143,7 @@ int echo_index_scores_prefetch(const uint8_t *q, const float *w, const uint8_t *
                                int32_t tok_lo, int32_t tok_hi, float *scores, int64_t ld,
                                const float *theta, const int32_t *req_to_host,
                                const int32_t *host_to_gpu, int32_t *cand, int32_t *cand_cnt,
-                               int32_t cap, int32_t cap_div, void *stream);
+                               int32_t *total_cnt, int32_t cap, int32_t cap_div, void *stream);
 
 /*
  * Per-request prefetch threshold: theta[r] = the nearest-rank `percentile` of the scores of
@@ -220,22 +222,21 @@ int echo_recall(const echo_pool *pool, const int32_t *miss_host, const int32_t *
                 const int32_t *n_miss, int32_t max_miss, int32_t mode, void *stream);
 
 /*
- * Prefetch side of the overlap (§6.1, §5.2): allocates free slots to the prefetch candidates
- * appended since the previous call (cand/cand_cnt from echo_index_scores_prefetch; `done`
- * [n_q] int32 remembers how many of each request's candidates were already handled, zeroed
- * by the caller before the first call), sets the maps, gives the slots priority 0, and gathers
- * their rows from host memory.  Never evicts: candidates beyond the free slots are dropped.
- * The free slots come from free_list[0 .. *n_free_list) (ascending free slots listed once per
- * step by echo_prefetch_begin), consumed through the counter *free_taken.
+ * Prefetch side of the overlap (§6.1 with the §5.2 allocate and UVM copy).
+ * echo_prefetch_begin lists the pool's free slots (in no particular order) into free_list
+ * [n_gpu] and sets free_count[0] = their number, free_count[1] = 0 (taken so far).
+ * echo_prefetch_gather takes the candidates of one echo_index_scores_prefetch call (cand,
+ * cand_cnt), gives each a slot from free_list (counter free_count[1]; never evicts: candidates
+ * beyond the free slots are dropped), sets both maps, gives the slot priority 0 (first to go
+ * when space is short later), copies the row from host memory, and adds the number of rows it
+ * moved to *n_prefetched.  Skipped when the pool status word is nonzero.
  */
-int echo_prefetch_begin(const echo_pool *pool, int32_t *free_list, int32_t *n_free_list,
-                        int32_t *free_taken, int32_t *cand_cnt, int32_t *done, int32_t n_q,
-                        void *ws, size_t ws_bytes, void *stream);
+int echo_prefetch_begin(const echo_pool *pool, int32_t *free_list, int32_t *free_count,
+                        void *stream);
 int echo_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
                          const int32_t *req_to_host, const int32_t *cand,
-                         const int32_t *cand_cnt, int32_t *done, int32_t n_q, int32_t cap,
-                         const int32_t *key_len, int32_t cap_div, const int32_t *free_list,
-                         const int32_t *n_free_list, int32_t *free_taken, int32_t *n_prefetched,
+                         const int32_t *cand_cnt, int32_t n_q, int32_t cap,
+                         const int32_t *free_list, int32_t *free_count, int32_t *n_prefetched,
                          void *stream);
 
 /*
@@ -271,9 +272,9 @@ typedef struct {             /* device outputs of one step */
   int32_t *topk_slot;        /* [n_rows, topk] */
   int32_t *miss_host;        /* [n_rows * topk] */
   int32_t *miss_slot;        /* [n_rows * topk] */
-  int32_t *counters;         /* [8]: 0 n_miss, 1 n_prefetch_candidates (sum of demand),
-                                2 n_prefetched, 3 n_prefetched_and_selected (filled by
-                                echo_decode_stats), 4..7 reserved */
+  int32_t *counters;         /* [8]: 0 n_miss (guaranteed recall), 1 prefetch demand (tokens
+                                above threshold and not resident, summed over requests),
+                                2 rows prefetched, 3..7 reserved (zero) */
 } echo_decode_out;
 
 size_t echo_decode_workspace_bytes(const echo_decode_args *a, int32_t n_gpu);
