@@ -75,6 +75,50 @@ ECHO_DEV uint32_t block_excl_scan(uint32_t v, uint32_t *tmp, uint32_t *total) {
   return res;
 }
 
+// Exclusive prefix, in (group j, thread t) order, of per-thread per-group counts: an item of
+// (j, t) comes after every item of groups < j and after group j's items of threads < t.  This
+// is index order when thread t owns the elements [4t + G*j, 4t + G*j + 4) (G = 4*NT), the
+// layout that keeps every 16-byte load of a wave contiguous.  lds: >= J*NT/64 + NT/64 + 2
+// words.  Block-wide; *total = sum of all counts.
+template <int NT, int J>
+ECHO_DEV void group_excl_scan(const uint32_t (&cnt)[J], uint32_t (&base)[J], uint32_t *lds,
+                              uint32_t *total) {
+  constexpr int NW = NT / 64;
+  constexpr int NTOT = J * NW;
+  static_assert(NTOT <= NT, "too many groups for one block scan");
+  const int w = threadIdx.x >> 6, l = lane_id();
+  uint32_t incl[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    incl[j] = wave_incl_scan(cnt[j]);
+    if (l == 63) lds[j * NW + w] = incl[j];
+  }
+  __syncthreads();
+  const uint32_t v = threadIdx.x < NTOT ? lds[threadIdx.x] : 0u;
+  __syncthreads();
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan<NT>(v, lds + NTOT, &tot);
+  if (threadIdx.x < NTOT) lds[threadIdx.x] = ex;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < J; ++j) base[j] = lds[j * NW + w] + incl[j] - cnt[j];
+  *total = tot;
+  __syncthreads();
+}
+
+// LDS histogram add with the wave's most common bin peeled off first: the keys being
+// counted (top bits of scores, step-stamp priorities) concentrate in few bins, and
+// same-address LDS atomics within one instruction serialise.
+ECHO_DEV void hist_add_peeled(uint32_t *hist, uint32_t bin, bool act) {
+  const uint64_t m_act = __ballot(act);
+  if (!m_act) return;
+  const int leader = __ffsll(static_cast<unsigned long long>(m_act)) - 1;
+  const uint32_t lead_bin = __shfl(bin, leader, 64);
+  const uint64_t same = __ballot(act && bin == lead_bin);
+  if (lane_id() == leader) atomicAdd(&hist[lead_bin], static_cast<uint32_t>(__popcll(same)));
+  if (act && bin != lead_bin) atomicAdd(&hist[bin], 1u);
+}
+
 template <int NT>
 ECHO_DEV uint32_t block_sum(uint32_t v, uint32_t *tmp) {
   uint32_t total;

@@ -22,6 +22,7 @@ struct DecodeWs {
   size_t topk_bytes;
   void *pool_ws;
   size_t pool_bytes;
+  uint32_t *hist0;     // [n_rows][2048] digit-0 histograms of the top-k keys
   float *theta;        // [n_rows]
   int32_t *cand;       // [n_chunks][n_rows][cap]
   int32_t *cand_cnt;   // [n_chunks][n_rows]
@@ -36,6 +37,7 @@ static size_t decode_ws_layout(const echo_decode_args *a, int32_t n_gpu, void *b
   const size_t tb = topk_ws_bytes(a->n_rows, a->max_key_len);
   const size_t pb = pool_ws_bytes(a->n_rows, a->topk, n_gpu);
   const size_t o_t = take(tb), o_p = take(pb);
+  const size_t o_h = take(static_cast<size_t>(a->n_rows) * 2048 * 4);
   size_t o_th = 0, o_c = 0, o_cc = 0, o_tc = 0, o_fl = 0, o_fc = 0;
   if (a->prefetch) {
     const size_t nc = static_cast<size_t>(a->n_chunks), nr = static_cast<size_t>(a->n_rows);
@@ -52,6 +54,7 @@ static size_t decode_ws_layout(const echo_decode_args *a, int32_t n_gpu, void *b
     w->topk_bytes = tb;
     w->pool_ws = b + o_p;
     w->pool_bytes = pb;
+    w->hist0 = reinterpret_cast<uint32_t *>(b + o_h);
     if (a->prefetch) {
       w->theta = reinterpret_cast<float *>(b + o_th);
       w->cand = reinterpret_cast<int32_t *>(b + o_c);
@@ -112,7 +115,9 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
   const bool pf = a->prefetch != 0;
   const bool split = pf && sd != m;
 
-  if ((rc = launch_zero_i32(o->counters, 8, m))) return rc;
+  if ((rc = launch_zero2_i32(o->counters, 8, reinterpret_cast<int32_t *>(W.hist0),
+                              static_cast<int64_t>(a->n_rows) * 2048, m)))
+    return rc;
   if (pf) {
     const int nc = a->n_chunks;
     if ((rc = ensure_events(static_cast<size_t>(nc) + 1))) return rc;
@@ -129,7 +134,8 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
                      W.cand + static_cast<int64_t>(c) * a->n_rows * a->cap,
                      W.cand_cnt + static_cast<int64_t>(c) * a->n_rows, W.total_cnt, a->cap, a->cap_div};
       if ((rc = launch_score_decode(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len, a->n_rows,
-                                    a->max_key_len, lo, hi, o->scores, a->max_key_len, &P, m)))
+                                    a->max_key_len, lo, hi, o->scores, a->max_key_len, &P,
+                                    W.hist0, m)))
         return rc;
       hipStream_t gs = m;
       if (split) {
@@ -146,11 +152,11 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
   } else {
     if ((rc = launch_score_decode(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len, a->n_rows,
                                   a->max_key_len, 0, a->max_key_len, o->scores, a->max_key_len,
-                                  nullptr, m)))
+                                  nullptr, W.hist0, m)))
       return rc;
   }
-  if ((rc = launch_topk(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len, a->topk,
-                        o->topk_idx, W.topk_ws, W.topk_bytes, m)))
+  if ((rc = launch_topk_rows(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,
+                             a->topk, W.hist0, o->topk_idx, m)))
     return rc;
   if (pf && (rc = launch_sum_i32(W.total_cnt, a->n_rows, o->counters + 1, m))) return rc;
   if (split) {

@@ -16,12 +16,27 @@ struct PrefetchArgs {
   int32_t cap_div;
 };
 
+struct PoolArgs {
+  uint8_t *free_;
+  int32_t *priority;
+  int32_t *to_host;
+  int32_t *host_to_gpu;
+  int32_t *indices_buf;
+  int32_t *status;
+  int32_t n_gpu, n_host;
+};
+
+// hist0 (optional, [n_q][2048]): digit-0 histogram of the top-k keys of the scores, added to
 int launch_score_decode(const uint8_t *q, const float *w, const uint8_t *k, const float *k_scale,
                         const int64_t *key_begin, const int32_t *key_len, int32_t n_q,
                         int32_t max_len, int32_t tok_lo, int32_t tok_hi, float *scores,
-                        int64_t ld, const PrefetchArgs *pf, hipStream_t st);
+                        int64_t ld, const PrefetchArgs *pf, uint32_t *hist0, hipStream_t st);
 
 size_t topk_ws_bytes(int32_t n_rows, int32_t max_len);
+// hist0: optional digit-0 histograms from launch_score_decode
+int launch_topk_rows(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
+                     int32_t max_len, int32_t k, const uint32_t *hist0, int32_t *idx,
+                     hipStream_t st);
 int launch_topk(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
                 int32_t max_len, int32_t k, int32_t *idx, void *ws, size_t ws_bytes,
                 hipStream_t st);
@@ -32,6 +47,12 @@ int launch_pool_lookup_alloc(const echo_pool *pool, const int32_t *idx, const in
                              int32_t step_id, int32_t *topk_slot, int32_t *miss_host,
                              int32_t *miss_slot, int32_t *n_miss, void *ws, size_t ws_bytes,
                              hipStream_t st);
+
+bool pool_small_fits(int32_t n_gpu);
+int launch_pool_small(const echo_pool *pool, int32_t *miss_entry_ws, const int32_t *idx,
+                      const int64_t *key_begin, const int32_t *req_to_host, int64_t n_k,
+                      int32_t n_rows, int32_t k, int32_t step_id, int32_t *topk_slot,
+                      int32_t *miss_host, int32_t *miss_slot, int32_t *n_miss, hipStream_t st);
 
 int launch_recall_gather(const echo_pool *pool, const int32_t *miss_host, const int32_t *miss_slot,
                          const int32_t *n_miss, int32_t max_miss, hipStream_t st);
@@ -48,6 +69,7 @@ int launch_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
                            const int32_t *free_list, int32_t *free_count, int32_t *n_prefetched,
                            hipStream_t st);
 int launch_zero_i32(int32_t *p, int64_t n, hipStream_t st);
+int launch_zero2_i32(int32_t *p, int64_t n, int32_t *q, int64_t m, hipStream_t st);
 int launch_sum_i32(const int32_t *v, int32_t n, int32_t *out, hipStream_t st);
 
 }  // namespace echo

@@ -37,16 +37,6 @@ struct PoolWs {
   int32_t n_lookup_wg;
 };
 
-struct PoolArgs {
-  uint8_t *free_;
-  int32_t *priority;
-  int32_t *to_host;
-  int32_t *host_to_gpu;
-  int32_t *indices_buf;
-  int32_t *status;
-  int32_t n_gpu, n_host;
-};
-
 static size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 static void pool_ws_layout(int32_t n_rows, int32_t k, int32_t n_gpu, void *base, PoolWs *w,
@@ -383,6 +373,9 @@ int launch_pool_lookup_alloc(const echo_pool *pool, const int32_t *idx, const in
   size_t need;
   pool_ws_layout(n_rows, k, pool->n_gpu, ws, &W, &need);
   if (ws_bytes < need) return fail(ECHO_EWORKSPACE, "echo_pool_lookup_alloc: workspace %zu < %zu", ws_bytes, need);
+  if (pool_small_fits(pool->n_gpu))
+    return launch_pool_small(pool, W.miss_entry, idx, key_begin, req_to_host, n_k, n_rows, k,
+                             step_id, topk_slot, miss_host, miss_slot, n_miss, st);
   PoolArgs P{pool->gpu_free, pool->gpu_priority, pool->gpu_to_host, pool->host_to_gpu,
              pool->indices_buf, pool->status, pool->n_gpu, pool->n_host};
   const int64_t n_ent = static_cast<int64_t>(n_rows) * k;

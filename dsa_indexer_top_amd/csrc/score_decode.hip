@@ -28,12 +28,13 @@ constexpr int SD_LOADS = SD_UNITS / SD_THREADS;                  // per thread p
 
 ECHO_DEV int swz(int tok, int seg) { return tok * 128 + ((seg ^ ((tok >> 1) & 7)) << 4); }
 
-template <bool HAS_SCALE, bool PREFETCH>
+template <bool HAS_SCALE, bool PREFETCH, bool HIST>
 __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
     const uint8_t *__restrict__ q, const float *__restrict__ w, const uint8_t *__restrict__ k,
     const float *__restrict__ k_scale, const int64_t *__restrict__ key_begin,
     const int32_t *__restrict__ key_len, int32_t max_len, int32_t tok_lo, int32_t tok_hi,
-    int32_t tokens_per_wg, float *__restrict__ scores, int64_t ld, PrefetchArgs pf) {
+    int32_t tokens_per_wg, float *__restrict__ scores, int64_t ld, PrefetchArgs pf,
+    uint32_t *__restrict__ hist0) {
   const int r = blockIdx.y;
   const int32_t L = min(max(key_len[r], 0), max_len);
   const int32_t hi = min(L, tok_hi);
@@ -45,6 +46,7 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
   float *__restrict__ srow = scores + static_cast<int64_t>(r) * ld;
 
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][SD_CHUNK * D];
+  __shared__ uint32_t hl[HIST ? 2048 : 1];
 
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
   const int j = l & 15, g = l >> 4;
@@ -72,6 +74,8 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
     }
   };
 
+  if constexpr (HIST)
+    for (int b = threadIdx.x; b < 2048; b += SD_THREADS) hl[b] = 0;   // ordered by the first barrier
   fetch(t_begin);
   int buf = 0;
   for (int32_t c0 = t_begin; c0 < t_end; c0 += SD_CHUNK) {
@@ -92,26 +96,32 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
       const int4 b1 = *reinterpret_cast<const int4 *>(sb + swz(tt, 2 * g + 1));
       part[tile] = reduce_groups(score_tile_partial(qo, v8i{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w}));
     }
-    if (g < 2) {
-      const int32_t t = c0 + wv * 32 + g * 16 + j;
-      if (t < t_end) {
-        float s = (g == 0) ? part[0] : part[1];
-        if constexpr (HAS_SCALE) s *= k_scale[kb + t];
-        srow[t] = s;
-        if constexpr (PREFETCH) {
-          if (s > theta) {
-            const int32_t h = pf.req_to_host[kb + t];
-            if (pf.host_to_gpu[h] == INF) {
-              if (atomicAdd(&pf.total_cnt[r], 1) < cap_r) {
-                const int32_t pos = atomicAdd(&pf.cand_cnt[r], 1);
-                pf.cand[static_cast<int64_t>(r) * pf.cap + pos] = t;
-              }
+    const int32_t t_out = c0 + wv * 32 + g * 16 + j;
+    const bool writer = g < 2 && t_out < t_end;
+    float s_out = (g == 0) ? part[0] : part[1];
+    if (writer) {
+      if constexpr (HAS_SCALE) s_out *= k_scale[kb + t_out];
+      srow[t_out] = s_out;
+      if constexpr (PREFETCH) {
+        if (s_out > theta) {
+          const int32_t h = pf.req_to_host[kb + t_out];
+          if (pf.host_to_gpu[h] == INF) {
+            if (atomicAdd(&pf.total_cnt[r], 1) < cap_r) {
+              const int32_t pos = atomicAdd(&pf.cand_cnt[r], 1);
+              pf.cand[static_cast<int64_t>(r) * pf.cap + pos] = t_out;
             }
           }
         }
       }
     }
+    if constexpr (HIST) hist_add_peeled(hl, (~f32_key(s_out)) >> 21, writer);
     buf ^= 1;
+  }
+  if constexpr (HIST) {
+    __syncthreads();
+    uint32_t *gh = hist0 + static_cast<int64_t>(r) * 2048;
+    for (int b = threadIdx.x; b < 2048; b += SD_THREADS)
+      if (hl[b]) atomicAdd(&gh[b], hl[b]);
   }
 }
 
@@ -127,24 +137,27 @@ static int32_t pick_tokens_per_wg(int64_t total_tokens, int32_t max_len) {
 int launch_score_decode(const uint8_t *q, const float *w, const uint8_t *k, const float *k_scale,
                         const int64_t *key_begin, const int32_t *key_len, int32_t n_q,
                         int32_t max_len, int32_t tok_lo, int32_t tok_hi, float *scores,
-                        int64_t ld, const PrefetchArgs *pf, hipStream_t st) {
+                        int64_t ld, const PrefetchArgs *pf, uint32_t *hist0, hipStream_t st) {
   tok_hi = tok_hi < max_len ? tok_hi : max_len;
   if (n_q == 0 || tok_hi <= tok_lo) return ECHO_OK;
   const int32_t tpw = pick_tokens_per_wg(static_cast<int64_t>(n_q) * (tok_hi - tok_lo), tok_hi - tok_lo);
   dim3 grid((tok_hi - tok_lo + tpw - 1) / tpw, n_q);
   PrefetchArgs none{};
   const PrefetchArgs &p = pf ? *pf : none;
-  if (pf) {
-    if (k_scale)
-      score_decode_kernel<true, true><<<grid, SD_THREADS, 0, st>>>(q, w, k, k_scale, key_begin, key_len, max_len, tok_lo, tok_hi, tpw, scores, ld, p);
-    else
-      score_decode_kernel<false, true><<<grid, SD_THREADS, 0, st>>>(q, w, k, k_scale, key_begin, key_len, max_len, tok_lo, tok_hi, tpw, scores, ld, p);
-  } else {
-    if (k_scale)
-      score_decode_kernel<true, false><<<grid, SD_THREADS, 0, st>>>(q, w, k, k_scale, key_begin, key_len, max_len, tok_lo, tok_hi, tpw, scores, ld, p);
-    else
-      score_decode_kernel<false, false><<<grid, SD_THREADS, 0, st>>>(q, w, k, k_scale, key_begin, key_len, max_len, tok_lo, tok_hi, tpw, scores, ld, p);
-  }
+#define ECHO_SD(SC, PF, HI)                                                                     \
+  score_decode_kernel<SC, PF, HI><<<grid, SD_THREADS, 0, st>>>(q, w, k, k_scale, key_begin,       \
+                                                               key_len, max_len, tok_lo, tok_hi,  \
+                                                               tpw, scores, ld, p, hist0)
+  const bool sc = k_scale != nullptr, pfo = pf != nullptr, hi = hist0 != nullptr;
+  if (sc && pfo && hi) ECHO_SD(true, true, true);
+  else if (sc && pfo) ECHO_SD(true, true, false);
+  else if (sc && hi) ECHO_SD(true, false, true);
+  else if (sc) ECHO_SD(true, false, false);
+  else if (pfo && hi) ECHO_SD(false, true, true);
+  else if (pfo) ECHO_SD(false, true, false);
+  else if (hi) ECHO_SD(false, false, true);
+  else ECHO_SD(false, false, false);
+#undef ECHO_SD
   return check_launch("score_decode");
 }
 
@@ -162,7 +175,7 @@ extern "C" int echo_index_scores(const uint8_t *q, const float *w, const uint8_t
   if (n_q > 0 && (!q || !w || !key_begin || !key_len || !scores || (max_key_len > 0 && !k)))
     return fail(ECHO_EINVAL, "echo_index_scores: NULL pointer");
   return launch_score_decode(q, w, k, k_scale, key_begin, key_len, n_q, max_key_len, 0,
-                             max_key_len, scores, ld, nullptr, S(stream));
+                             max_key_len, scores, ld, nullptr, nullptr, S(stream));
 }
 
 extern "C" int echo_index_scores_prefetch(const uint8_t *q, const float *w, const uint8_t *k,
@@ -183,5 +196,5 @@ extern "C" int echo_index_scores_prefetch(const uint8_t *q, const float *w, cons
     return fail(ECHO_EINVAL, "echo_index_scores_prefetch: NULL pointer");
   PrefetchArgs pf{theta, req_to_host, host_to_gpu, cand, cand_cnt, total_cnt, cap, cap_div};
   return launch_score_decode(q, w, k, k_scale, key_begin, key_len, n_q, max_key_len, tok_lo,
-                             tok_hi, scores, ld, &pf, S(stream));
+                             tok_hi, scores, ld, &pf, nullptr, S(stream));
 }

@@ -79,6 +79,11 @@ def _compare(case, step_id=10**6, mode=B.RECALL_GATHER):
     (4, 9000, 60000, 8000, 5, 512, 10000, 50),
     (5, 20000, 100000, 19990, 8, 1024, 12000, None),
     (6, 16, 64, 16, 1, 1, 64, 1),             # single selection, all priorities equal
+    (11, 65536, 300000, 65536, 8, 2048, 30000, None),   # largest single-workgroup pool
+    (12, 65537, 300000, 65537, 4, 2048, 30000, 100),    # smallest multi-kernel pool
+    (13, 150000, 600000, 149000, 6, 2048, 50000, 3000), # ties, several slot batches
+    (14, 150000, 600000, 150000, 6, 2048, 50000, 3),    # threshold bin overflows the LDS list
+    (15, 300000, 1200000, 299000, 4, 2048, 300000, 5000),  # multi-kernel path
 ])
 def test_pool_step_random(seed, n_gpu, n_host, n_occ, rows, k, L, levels):
     announce("pool", seed, n_gpu, n_host, rows, k)
