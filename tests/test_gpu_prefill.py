@@ -1,0 +1,84 @@
+"""GPU parity of the causal prefill indexer (echo_index_scores_prefill) and its per-row top-k
+against the oracle: bit-exact on integer-grid inputs; sampled rows at the full 32768^2 size."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dsa_indexer_top_amd import binding as B, inputs as gen
+from gpu_util import announce, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(q, w, k, q_pos0=0, ld=None):
+    n_q, n_k = q.shape[0], k.shape[0]
+    ld = n_k + 3 if ld is None else ld
+    sc = torch.full((n_q, ld), float("nan"), dtype=torch.float32, device="cuda")
+    B.index_scores_prefill(dev(q), dev(w), dev(k), sc, q_pos0=q_pos0, ld=ld)
+    return sc
+
+
+def _check_rows(q, w, k, got, rows, q_pos0=0):
+    """got: [n_q, ld] array, or a dict row -> row array."""
+    n_k = k.shape[0]
+    for t in rows:
+        lim = min(n_k, q_pos0 + t + 1)
+        want = oracle.index_scores(q[t:t + 1], w[t:t + 1], k, None, np.array([0]), np.array([lim]))[0]
+        row = got[t]
+        g = row[:lim].astype(np.float64)
+        bad = np.flatnonzero(g != want)
+        assert len(bad) == 0, "row %d: %d mismatches (first s=%d gpu %r oracle %r)" % (
+            t, len(bad), bad[0], g[bad[0]], want[bad[0]])
+        assert np.isnan(row[lim:]).all(), "row %d wrote past its causal limit" % t
+
+
+@pytest.mark.parametrize("n", [1, 17, 300, 1000])
+def test_prefill_small_exact(n):
+    announce("prefill", n)
+    q, w, k = gen.make_prefill_inputs(n, seed=60 + n)
+    got = host(_run(q, w, k))
+    _check_rows(q, w, k, got, range(n))
+
+
+def test_prefill_chunk_offset_exact():
+    announce("prefill chunk offset")
+    q_all, w_all, k = gen.make_prefill_inputs(1500, seed=71)
+    q, w = q_all[1000:1300], w_all[1000:1300]           # a chunk of 300 queries at 1000..1299
+    got = host(_run(q, w, k, q_pos0=1000))
+    _check_rows(q, w, k, got, range(300), q_pos0=1000)
+
+
+def test_prefill_topk_rows_exact():
+    announce("prefill + top-k 3000 rows")
+    n, kk = 3000, 256
+    q, w, k = gen.make_prefill_inputs(n, seed=73)
+    sc = _run(q, w, k, ld=n)
+    lens = torch.arange(1, n + 1, dtype=torch.int32, device="cuda")
+    idx = torch.empty((n, kk), dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(B.topk_workspace_bytes(n, n), 256), dtype=torch.uint8, device="cuda")
+    B.topk(sc, lens, n, kk, idx, ws, ld=n)
+    got = host(idx)
+    for t in [0, 1, 254, 255, 256, 257, 1000, 2999]:
+        want_s = oracle.index_scores(q[t:t + 1], w[t:t + 1], k, None, np.array([0]), np.array([t + 1]))[0]
+        assert np.array_equal(got[t], oracle.topk_row(want_s, kk)), t
+
+
+def test_prefill_32k_full_sampled():
+    announce("prefill 32768^2 full size")
+    cfg = gen.PREFILL["prefill_32k"]
+    n = cfg["n"]
+    q, w, k = gen.make_prefill_inputs(n, seed=cfg["seed"])
+    sc = _run(q, w, k, ld=n)
+    rows = [0, 1, 15, 16, 2046, 2047, 2048, 16383, 16384, 30000, 32766, 32767]
+    got_rows = sc[rows].cpu().numpy()
+    _check_rows(q, w, k, {t: got_rows[i] for i, t in enumerate(rows)}, rows)
+    lens = torch.arange(1, n + 1, dtype=torch.int32, device="cuda")
+    idx = torch.empty((n, cfg["topk"]), dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(B.topk_workspace_bytes(n, n), 256), dtype=torch.uint8, device="cuda")
+    B.topk(sc, lens, n, cfg["topk"], idx, ws, ld=n)
+    got_idx = idx[rows].cpu().numpy()
+    for i, t in enumerate(rows):
+        want_s = oracle.index_scores(q[t:t + 1], w[t:t + 1], k, None, np.array([0]), np.array([t + 1]))[0]
+        assert np.array_equal(got_idx[i], oracle.topk_row(want_s, cfg["topk"])), t
