@@ -75,6 +75,33 @@ def measure_link_gbs(torch, nbytes=256 << 20, reps=5):
     return best
 
 
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published
+
+
+def prefill_measure(torch, B, gen, reps=5):
+    """Causal prefill indexer on 32768 x 32768 (integer grid): achieved fp8 MFMA TFLOP/s on the
+    algorithmic flops (16384 per causal pair), plus the per-row top-2048 time."""
+    cfg = gen.PREFILL["prefill_32k"]
+    n = cfg["n"]
+    q, w, k = gen.make_prefill_inputs(n, seed=cfg["seed"])
+    dq, dw, dk = (torch.from_numpy(a).cuda() for a in (q, w, k))
+    sc = torch.empty((n, n), dtype=torch.float32, device="cuda")
+    st = torch.cuda.Stream()
+    t_score = kernel_time_us(torch, st, lambda: B.index_scores_prefill(dq, dw, dk, sc, ld=n, stream=st), reps)
+    lens = torch.arange(1, n + 1, dtype=torch.int32, device="cuda")
+    idx = torch.empty((n, cfg["topk"]), dtype=torch.int32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    t_topk = kernel_time_us(torch, st, lambda: B.topk(sc, lens, n, cfg["topk"], idx, ws, ld=n, stream=st), reps)
+    flops = 16384.0 * n * (n + 1) / 2
+    tfs = flops / (t_score / 1e6) / 1e12
+    del sc
+    return {"bound": "mfma", "kernel": "score_prefill_kernel", "workload": "prefill_32k: causal "
+            "32768 x 32768, H=64 d=128 fp8 integer grid", "achieved": round(tfs, 1),
+            "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tfs / FP8_PEAK_TFLOPS, 4),
+            "flops_per_launch": flops, "us_per_launch": round(t_score, 1),
+            "topk_rows_us": round(t_topk, 1)}
+
+
 def cpu_baseline(inp, host_kv, pool_arrays, budget_s=12.0):
     """The oracle, as it is, on a bounded sample of the same workload: whole requests in order
     (scores in float64, exact top-k) until the budget is spent, then the oracle pool step for
@@ -115,6 +142,7 @@ def main():
     ap.add_argument("--workload", default="b8_64k", choices=sorted(WORKLOADS))
     ap.add_argument("--kernel-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefetch", choices=("auto", "on", "off"), default="auto")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -234,6 +262,12 @@ def main():
         "counters": {"n_miss": n_miss, "prefetch_demand": int(res["counters"][1]),
                      "prefetched": int(res["counters"][2])},
     }
+    if not args.no_prefill:
+        log("prefill indexer (32768^2) ...")
+        out["prefill"] = prefill_measure(torch, B, gen)
+        log("prefill %.1f us = %.0f TFLOP/s (%.1f%% of fp8 peak), top-k rows %.1f us" % (
+            out["prefill"]["us_per_launch"], out["prefill"]["achieved"],
+            100 * out["prefill"]["frac"], out["prefill"]["topk_rows_us"]))
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(inp, host_kv, pool)

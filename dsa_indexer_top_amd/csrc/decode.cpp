@@ -1,14 +1,19 @@
-// The whole decode step (ECHO review page §4): indexer scores -> [threshold prefetch on a
-// side stream, §6.1] -> exact top-k -> lookup / evict / allocate (§5.2) -> recall gather ->
-// priorities.  Every call only enqueues work, so the step can be captured into one hipGraph
-// (§2: graph execution forbids host control and dynamically sized tensors inside the step).
+// The whole decode step (ECHO review page §4): indexer scores -> exact top-k -> residency
+// lookup / eviction / allocation (§5.2) -> recall gather -> priorities, with optional
+// threshold prefetch (§6.1).  Every call only enqueues work, so the step can be captured into
+// one hipGraph (§2: graph execution forbids host control and dynamically sized tensors inside
+// the step).
 //
-// With prefetch, scoring is split into n_chunks token ranges.  After each range the main
-// stream records an event; the side stream waits for it and runs the prefetch gather of that
-// range's candidates while the main stream scores the next range.  The main stream waits for
-// the side stream's last gather before the guaranteed lookup/allocation, which must see every
-// row prefetch made resident.
-#include <mutex>
+// Streams.  `main` carries the critical path.  `side` (when different) first computes the
+// pool statistics (free count, priority histogram), which do not depend on the selection, while
+// `main` scores; with prefetch, scoring is split into n_chunks token ranges and after each
+// range `side` allocates and gathers that range's candidates while `main` scores the next one.
+// `main` waits for `side` before the top-k finish, whose fused lookup updates the statistics.
+//
+//   main: zero -> [threshold, free list] -> score(+top-k histogram) [x chunks] -> top-k split
+//         -> join -> top-k finish + lookup -> evict-1 -> evict-2 + allocate -> recall gather
+//   side: pool stats -> [prefetch gather per chunk]
+#include <algorithm>
 #include <vector>
 
 #include "internal.hpp"
@@ -18,51 +23,49 @@ namespace echo {
 static size_t al(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
 
 struct DecodeWs {
-  void *topk_ws;
-  size_t topk_bytes;
-  void *pool_ws;
-  size_t pool_bytes;
-  uint32_t *hist0;     // [n_rows][2048] digit-0 histograms of the top-k keys
+  uint32_t *hist0;     // [n_rows][2048] digit-0 histograms of the top-k keys   (zeroed)
+  int32_t *cand_cnt;   // [n_chunks][n_rows]                                     (zeroed)
+  int32_t *total_cnt;  // [n_rows]                                               (zeroed)
+  PoolFastWs pool;     // starts with its zeroed region
+  int64_t zero_words;  // hist0 .. end of the pool's zeroed region
+  void *split;
   float *theta;        // [n_rows]
   int32_t *cand;       // [n_chunks][n_rows][cap]
-  int32_t *cand_cnt;   // [n_chunks][n_rows]
-  int32_t *total_cnt;  // [n_rows]
   int32_t *free_list;  // [n_gpu]
   int32_t *free_count; // [2]
 };
 
 static size_t decode_ws_layout(const echo_decode_args *a, int32_t n_gpu, void *base, DecodeWs *w) {
+  const bool pf = a->prefetch != 0;
+  const size_t nr = static_cast<size_t>(a->n_rows), nc = pf ? static_cast<size_t>(a->n_chunks) : 0;
   size_t off = 0;
   auto take = [&](size_t b) { size_t o = off; off += al(b); return o; };
-  const size_t tb = topk_ws_bytes(a->n_rows, a->max_key_len);
-  const size_t pb = pool_ws_bytes(a->n_rows, a->topk, n_gpu);
-  const size_t o_t = take(tb), o_p = take(pb);
-  const size_t o_h = take(static_cast<size_t>(a->n_rows) * 2048 * 4);
-  size_t o_th = 0, o_c = 0, o_cc = 0, o_tc = 0, o_fl = 0, o_fc = 0;
-  if (a->prefetch) {
-    const size_t nc = static_cast<size_t>(a->n_chunks), nr = static_cast<size_t>(a->n_rows);
+  const size_t o_h = take(nr * 2048 * 4), o_cc = take(nc * nr * 4), o_tc = take(nr * 4);
+  PoolFastWs pw;
+  size_t pbytes;
+  pool_fast_ws_layout(a->n_rows, a->topk, n_gpu, nullptr, &pw, &pbytes);
+  const size_t o_pool = take(pbytes);
+  const size_t zero_end = o_pool + static_cast<size_t>(pw.zero_words) * 4;
+  const size_t o_split = take(topk_split_ws_bytes(a->n_rows, a->max_key_len, a->topk));
+  size_t o_th = 0, o_c = 0, o_fl = 0, o_fc = 0;
+  if (pf) {
     o_th = take(nr * 4);
     o_c = take(nc * nr * static_cast<size_t>(a->cap) * 4);
-    o_cc = take(nc * nr * 4);
-    o_tc = take(nr * 4);
     o_fl = take(static_cast<size_t>(n_gpu) * 4);
     o_fc = take(2 * 4);
   }
   if (w && base) {
     char *b = static_cast<char *>(base);
-    w->topk_ws = b + o_t;
-    w->topk_bytes = tb;
-    w->pool_ws = b + o_p;
-    w->pool_bytes = pb;
     w->hist0 = reinterpret_cast<uint32_t *>(b + o_h);
-    if (a->prefetch) {
-      w->theta = reinterpret_cast<float *>(b + o_th);
-      w->cand = reinterpret_cast<int32_t *>(b + o_c);
-      w->cand_cnt = reinterpret_cast<int32_t *>(b + o_cc);
-      w->total_cnt = reinterpret_cast<int32_t *>(b + o_tc);
-      w->free_list = reinterpret_cast<int32_t *>(b + o_fl);
-      w->free_count = reinterpret_cast<int32_t *>(b + o_fc);
-    }
+    w->cand_cnt = reinterpret_cast<int32_t *>(b + o_cc);
+    w->total_cnt = reinterpret_cast<int32_t *>(b + o_tc);
+    pool_fast_ws_layout(a->n_rows, a->topk, n_gpu, b + o_pool, &w->pool, &pbytes);
+    w->zero_words = static_cast<int64_t>(zero_end / 4);
+    w->split = b + o_split;
+    w->theta = reinterpret_cast<float *>(b + o_th);
+    w->cand = reinterpret_cast<int32_t *>(b + o_c);
+    w->free_list = reinterpret_cast<int32_t *>(b + o_fl);
+    w->free_count = reinterpret_cast<int32_t *>(b + o_fc);
   }
   return off;
 }
@@ -80,11 +83,20 @@ static int ensure_events(size_t n) {
   return ECHO_OK;
 }
 
+static int edge(hipStream_t from, hipStream_t to, size_t ev) {
+  hipError_t e = hipEventRecord(t_events[ev], from);
+  if (e == hipSuccess) e = hipStreamWaitEvent(to, t_events[ev], 0);
+  if (e != hipSuccess) return fail(ECHO_EHIP, "decode step fork/join: %s", hipGetErrorString(e));
+  return ECHO_OK;
+}
+
 static int validate(const echo_decode_args *a, const echo_pool *pool, const echo_decode_out *o) {
   if (!a || !pool || !o) return fail(ECHO_EINVAL, "echo_decode_select: NULL argument");
   if (a->n_rows < 1 || a->n_rows > 65535) return fail(ECHO_EUNSUPPORTED, "echo_decode_select: n_rows %d outside [1, 65535]", a->n_rows);
   if (a->max_key_len < 0) return fail(ECHO_EINVAL, "echo_decode_select: max_key_len < 0");
+  if (a->max_key_len > (1 << 22)) return fail(ECHO_EUNSUPPORTED, "echo_decode_select: max_key_len above 4M");
   if (a->topk < 1 || a->topk > ECHO_MAX_TOPK) return fail(ECHO_EUNSUPPORTED, "echo_decode_select: topk %d outside [1, %d]", a->topk, ECHO_MAX_TOPK);
+  if (static_cast<int64_t>(a->n_rows) * a->topk > (1LL << 30)) return fail(ECHO_EUNSUPPORTED, "echo_decode_select: too many selections");
   if (!a->q || !a->w || !a->key_begin || !a->key_len || !a->req_to_host || (a->max_key_len > 0 && !a->k))
     return fail(ECHO_EINVAL, "echo_decode_select: NULL input");
   if (!o->scores || !o->topk_idx || !o->topk_slot || !o->miss_host || !o->miss_slot || !o->counters)
@@ -92,6 +104,7 @@ static int validate(const echo_decode_args *a, const echo_pool *pool, const echo
   if (pool->n_gpu < 1 || pool->n_host < 1 || !pool->gpu_free || !pool->gpu_priority || !pool->gpu_to_host ||
       !pool->host_to_gpu || !pool->indices_buf || !pool->gpu_kv || !pool->host_kv || !pool->status)
     return fail(ECHO_EINVAL, "echo_decode_select: incomplete pool");
+  if (pool->n_gpu > (1 << 22)) return fail(ECHO_EUNSUPPORTED, "echo_decode_select: more than 4M GPU slots");
   if (a->prefetch) {
     if (a->n_chunks < 1 || a->n_chunks > 16) return fail(ECHO_EUNSUPPORTED, "echo_decode_select: n_chunks %d outside [1, 16]", a->n_chunks);
     if (a->n_sample < 64 || a->n_sample > 4096 || (a->n_sample & (a->n_sample - 1)))
@@ -110,19 +123,21 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
   DecodeWs W{};
   const size_t need = decode_ws_layout(a, pool->n_gpu, ws, &W);
   if (!ws || ws_bytes < need) return fail(ECHO_EWORKSPACE, "echo_decode_select: workspace %zu < %zu", ws_bytes, need);
-  const int64_t n_k_max = INT64_MAX;   // token indices come from our own top-k: always in range
   const int32_t n_ent = a->n_rows * a->topk;
   const bool pf = a->prefetch != 0;
-  const bool split = pf && sd != m;
+  const bool split = sd != m;
+  const int nc = pf ? a->n_chunks : 1;
+  if (split && (rc = ensure_events(static_cast<size_t>(nc) + 2))) return rc;
+  const size_t ev_fork = 0, ev_join = 1;
 
-  if ((rc = launch_zero2_i32(o->counters, 8, reinterpret_cast<int32_t *>(W.hist0),
-                              static_cast<int64_t>(a->n_rows) * 2048, m)))
-    return rc;
+  if ((rc = launch_zero2_i32(o->counters, 8, reinterpret_cast<int32_t *>(W.hist0), W.zero_words, m))) return rc;
+  hipStream_t ss = m;
+  if (split) {
+    if ((rc = edge(m, sd, ev_fork))) return rc;
+    ss = sd;
+  }
+  if ((rc = launch_pool_stats(pool, W.pool, a->step_id, ss))) return rc;
   if (pf) {
-    const int nc = a->n_chunks;
-    if ((rc = ensure_events(static_cast<size_t>(nc) + 1))) return rc;
-    if ((rc = launch_zero_i32(W.cand_cnt, static_cast<int64_t>(nc) * a->n_rows, m))) return rc;
-    if ((rc = launch_zero_i32(W.total_cnt, a->n_rows, m))) return rc;
     if ((rc = launch_prefetch_threshold(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len,
                                         a->n_rows, a->n_sample, a->percentile, W.theta, m)))
       return rc;
@@ -134,19 +149,12 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
                      W.cand + static_cast<int64_t>(c) * a->n_rows * a->cap,
                      W.cand_cnt + static_cast<int64_t>(c) * a->n_rows, W.total_cnt, a->cap, a->cap_div};
       if ((rc = launch_score_decode(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len, a->n_rows,
-                                    a->max_key_len, lo, hi, o->scores, a->max_key_len, &P,
-                                    W.hist0, m)))
+                                    a->max_key_len, lo, hi, o->scores, a->max_key_len, &P, W.hist0, m)))
         return rc;
-      hipStream_t gs = m;
-      if (split) {
-        hipError_t e = hipEventRecord(t_events[c], m);
-        if (e == hipSuccess) e = hipStreamWaitEvent(sd, t_events[c], 0);
-        if (e != hipSuccess) return fail(ECHO_EHIP, "decode fork: %s", hipGetErrorString(e));
-        gs = sd;
-      }
+      if (split && (rc = edge(m, sd, 2 + c))) return rc;
       if ((rc = launch_prefetch_gather(pool, a->key_begin, a->req_to_host, P.cand, P.cand_cnt,
-                                       a->n_rows, a->cap, W.free_list, W.free_count,
-                                       o->counters + 2, gs)))
+                                       a->n_rows, a->cap, W.free_list, W.free_count, o->counters + 2,
+                                       &W.pool, a->step_id, ss)))
         return rc;
     }
   } else {
@@ -155,21 +163,19 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
                                   nullptr, W.hist0, m)))
       return rc;
   }
-  if ((rc = launch_topk_rows(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,
-                             a->topk, W.hist0, o->topk_idx, m)))
+  if ((rc = launch_topk_split(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,
+                              a->topk, W.hist0, W.split, m)))
     return rc;
-  if (pf && (rc = launch_sum_i32(W.total_cnt, a->n_rows, o->counters + 1, m))) return rc;
-  if (split) {
-    hipEvent_t join = t_events[a->n_chunks];
-    hipError_t e = hipEventRecord(join, sd);
-    if (e == hipSuccess) e = hipStreamWaitEvent(m, join, 0);
-    if (e != hipSuccess) return fail(ECHO_EHIP, "decode join: %s", hipGetErrorString(e));
-  }
-  if ((rc = launch_pool_lookup_alloc(pool, o->topk_idx, a->key_begin, a->req_to_host, n_k_max,
-                                     a->n_rows, a->topk, a->step_id, o->topk_slot, o->miss_host,
-                                     o->miss_slot, o->counters + 0, W.pool_ws, W.pool_bytes, m)))
+  if (split && (rc = edge(sd, m, ev_join))) return rc;
+  if ((rc = launch_topk_finish(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,
+                               a->topk, W.hist0, W.split, o->topk_idx, pool, &W.pool, a->key_begin,
+                               a->req_to_host, a->step_id, o->topk_slot, m)))
+    return rc;
+  if ((rc = launch_pool_evict(pool, W.pool, o->topk_idx, a->n_rows, a->topk, a->step_id, o->topk_slot,
+                              o->miss_host, o->miss_slot, o->counters + 0, m)))
     return rc;
   if ((rc = launch_recall_gather(pool, o->miss_host, o->miss_slot, o->counters + 0, n_ent, m))) return rc;
+  if (pf && (rc = launch_sum_i32(W.total_cnt, a->n_rows, o->counters + 1, m))) return rc;
   return ECHO_OK;
 }
 
@@ -204,7 +210,9 @@ extern "C" int echo_graph_capture_decode(const echo_decode_args *a, const echo_p
   if (!main_stream) return fail(ECHO_EINVAL, "echo_graph_capture_decode: capture needs a non-null main stream");
   int rc = validate(a, pool, out);
   if (rc) return rc;
-  if (a->prefetch && (rc = ensure_events(static_cast<size_t>(a->n_chunks) + 1))) return rc;
+  if (side_stream != main_stream &&
+      (rc = ensure_events(static_cast<size_t>(a->prefetch ? a->n_chunks : 1) + 2)))
+    return rc;
   hipStream_t m = S(main_stream);
   hipError_t e = hipStreamBeginCapture(m, hipStreamCaptureModeThreadLocal);
   if (e != hipSuccess) return fail(ECHO_EHIP, "hipStreamBeginCapture: %s", hipGetErrorString(e));

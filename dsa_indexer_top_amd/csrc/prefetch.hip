@@ -17,6 +17,7 @@
 #include <cmath>
 
 #include "internal.hpp"
+#include "pool_common.cuh"
 #include "score_tile.cuh"
 
 namespace echo {
@@ -125,7 +126,8 @@ __global__ __launch_bounds__(PG_THREADS) void prefetch_gather_kernel(
     int32_t n_gpu, int32_t n_host, const int64_t *__restrict__ key_begin,
     const int32_t *__restrict__ req_to_host, const int32_t *__restrict__ cand,
     const int32_t *__restrict__ cand_cnt, int32_t cap, const int32_t *__restrict__ free_list,
-    int32_t *free_count, int32_t *n_prefetched) {
+    int32_t *free_count, int32_t *n_prefetched, int32_t *st_free, uint32_t *st_fine,
+    uint32_t *st_coarse, int32_t step_id) {
   __shared__ int32_t s_base, s_n;
   __shared__ int32_t s_host[128], s_slot[128];
   const int r = blockIdx.x;
@@ -157,6 +159,12 @@ __global__ __launch_bounds__(PG_THREADS) void prefetch_gather_kernel(
         host_to_gpu[h] = slot;
         priority[slot] = 0;
         ok_h = h;
+        if (st_free) {                      // keep the pool-step statistics current
+          atomicSub(st_free, 1);
+          const uint32_t b = prio_bin(0, step_id);
+          atomicAdd(&st_fine[b], 1u);
+          atomicAdd(&st_coarse[b >> 5], 1u);
+        }
       }
       s_host[t] = ok_h;
       s_slot[t] = slot;
@@ -176,12 +184,13 @@ int launch_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
                            const int32_t *req_to_host, const int32_t *cand,
                            const int32_t *cand_cnt, int32_t n_q, int32_t cap,
                            const int32_t *free_list, int32_t *free_count, int32_t *n_prefetched,
-                           hipStream_t st) {
+                           const PoolFastWs *pw, int32_t step_id, hipStream_t st) {
   if (n_q == 0 || cap == 0) return ECHO_OK;
   prefetch_gather_kernel<<<n_q, PG_THREADS, 0, st>>>(
       pool->host_kv, pool->gpu_kv, pool->gpu_free, pool->gpu_priority, pool->gpu_to_host,
       pool->host_to_gpu, pool->status, pool->n_gpu, pool->n_host, key_begin, req_to_host, cand,
-      cand_cnt, cap, free_list, free_count, n_prefetched);
+      cand_cnt, cap, free_list, free_count, n_prefetched, pw ? pw->counters : nullptr,
+      pw ? pw->fine : nullptr, pw ? pw->coarse : nullptr, step_id);
   return check_launch("prefetch_gather");
 }
 
@@ -232,5 +241,5 @@ extern "C" int echo_prefetch_gather(const echo_pool *pool, const int64_t *key_be
   if (n_q > 0 && cap > 0 && (!key_begin || !req_to_host || !cand || !cand_cnt || !free_list || !free_count || !n_prefetched))
     return fail(ECHO_EINVAL, "echo_prefetch_gather: NULL pointer");
   return launch_prefetch_gather(pool, key_begin, req_to_host, cand, cand_cnt, n_q, cap, free_list,
-                                free_count, n_prefetched, S(stream));
+                                free_count, n_prefetched, nullptr, 0, S(stream));
 }

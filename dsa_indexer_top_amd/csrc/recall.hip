@@ -6,7 +6,8 @@
 // Gather kernel: the rows of 1152 bytes (72 x 16 B) of up to 32 misses per workgroup
 // iteration are read with 16-byte loads straight from mapped pinned host memory, nine loads
 // in flight per thread before any store, then written to their GPU slots.  The miss count is
-// read on the device, so the launch has a fixed grid sized for the maximum.
+// read on the device, so the launch has a fixed grid sized for the maximum.  It also checks
+// that HostTokenToGPU points back at each miss's slot (duplicate host indices otherwise).
 //
 // Memcpy mode (the host-driven baseline): the host waits for the stream, reads the miss list
 // and enqueues one hipMemcpyAsync per row.
@@ -27,8 +28,8 @@ constexpr int RC_PER_THREAD = RC_ROWS * RC_UNITS_PER_ROW / RC_THREADS;   // 9
 __global__ __launch_bounds__(RC_THREADS) void recall_gather_kernel(
     const uint16_t *__restrict__ host_kv, uint16_t *__restrict__ gpu_kv,
     const int32_t *__restrict__ miss_host, const int32_t *__restrict__ miss_slot,
-    const int32_t *__restrict__ n_miss_p, int32_t max_miss, const int32_t *__restrict__ status,
-    int32_t n_host, int32_t n_gpu) {
+    const int32_t *__restrict__ n_miss_p, int32_t max_miss, int32_t *__restrict__ status,
+    const int32_t *__restrict__ host_to_gpu, int32_t n_host, int32_t n_gpu) {
   if (*(volatile const int32_t *)status) return;
   const int32_t n = min(*n_miss_p, max_miss);
   const v4i *src = reinterpret_cast<const v4i *>(host_kv);
@@ -47,6 +48,8 @@ __global__ __launch_bounds__(RC_THREADS) void recall_gather_kernel(
         if (h >= 0 && h < n_host && s >= 0 && s < n_gpu) {
           v[m] = __builtin_nontemporal_load(src + static_cast<int64_t>(h) * RC_UNITS_PER_ROW + part);
           d_off[m] = static_cast<int64_t>(s) * RC_UNITS_PER_ROW + part;
+          // two misses sharing a host index leave the map pointing at only one of their slots
+          if (part == 0 && host_to_gpu[h] != s) atomicOr(status, ECHO_ST_DUP_HOST);
         }
       }
     }
@@ -61,8 +64,8 @@ int launch_recall_gather(const echo_pool *pool, const int32_t *miss_host, const 
   if (max_miss <= 0) return ECHO_OK;
   const int blocks = std::min(2048, (max_miss + RC_ROWS - 1) / RC_ROWS);
   recall_gather_kernel<<<blocks, RC_THREADS, 0, st>>>(pool->host_kv, pool->gpu_kv, miss_host, miss_slot,
-                                                      n_miss, max_miss, pool->status, pool->n_host,
-                                                      pool->n_gpu);
+                                                      n_miss, max_miss, pool->status, pool->host_to_gpu,
+                                                      pool->n_host, pool->n_gpu);
   return check_launch("recall_gather");
 }
 

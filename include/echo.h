@@ -69,8 +69,7 @@ enum {
  * GPU pool of one layer plus its host backup (§5.1).  All members are device pointers the
  * caller allocated; sizes: gpu_free/gpu_priority/gpu_to_host/indices_buf [n_gpu],
  * host_to_gpu [n_host], gpu_kv [n_gpu * 576], host_kv [n_host * 576], status [1].
- *   gpu_free      1 = slot free, 0 = occupied (GPUTokenFree).  The library uses the value 2
- *                 transiently inside one call to mark protected slots; it is 0/1 between calls.
+ *   gpu_free      1 = slot free, 0 = occupied (GPUTokenFree)
  *   gpu_priority  eviction priority, lowest evicted first, -1 for a free slot (GPUTokenPriority)
  *   gpu_to_host   host index held by the slot, ECHO_INF when empty (GPUTokenToHost)
  *   host_to_gpu   slot holding the host index, ECHO_INF when not resident (HostTokenToGPU)
@@ -185,7 +184,7 @@ int echo_topk(const float *scores, int64_t ld, const int32_t *len, int32_t n_row
  * Residency lookup + eviction + allocation for the selected tokens (§5.2 free/allocate and
  * the lookup half of recall), without the row copy.  For the entries idx[r*k + j] >= 0 taken
  * in (r, j) order: h = req_to_host[key_begin[r] + idx]; hit iff host_to_gpu[h] != ECHO_INF.
- *   - every hit slot is protected for this call;
+ *   - every hit slot is protected for this call (a bitmap in the workspace);
  *   - need = max(0, n_miss - #free); the `need` unprotected occupied slots with the smallest
  *     (priority, slot index) are evicted: free = 1, priority = -1, both maps = ECHO_INF; their
  *     rows are not touched (the host holds the backup);
@@ -200,7 +199,7 @@ int echo_topk(const float *scores, int64_t ld, const int32_t *len, int32_t n_row
  * On ECHO_ST_EXHAUSTED or ECHO_ST_BAD_HOST the pool is left untouched and topk_slot,
  * miss_*, n_miss are unspecified.  Rows of missed tokens still have to be copied by
  * echo_recall.  step_id must exceed every priority already in the pool for the policy to be
- * least-recently-selected-first (not checked).
+ * least-recently-selected-first (not checked).  1 <= k <= ECHO_MAX_TOPK; n_gpu <= 2^22.
  *   ws: device workspace of at least echo_pool_workspace_bytes(n_rows, k, pool->n_gpu).
  */
 size_t echo_pool_workspace_bytes(int32_t n_rows, int32_t k, int32_t n_gpu);
