@@ -144,6 +144,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefetch", choices=("auto", "on", "off"), default="auto")
+    ap.add_argument("--streams", type=int, choices=(1, 2), default=2,
+                    help="streams the captured step uses (2: overlap work on a side stream)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this decode path runs on one GPU; --gpus %d is not supported "
@@ -178,6 +180,8 @@ def main():
     pool = gen.make_pool_state(inp, sel.cpu().numpy(), host_kv)
     del sc, sel, tws
     rn = DecodeRunner(inp, pool, host_buf=hb, prefetch=prefetch)
+    if args.streams == 1:
+        rn.side = rn.main
     rn.capture()
     log("setup done in %.1fs" % (time.perf_counter() - t_setup))
 

@@ -35,21 +35,53 @@ ECHO_DEV uint32_t i32_key(int32_t x) { return static_cast<uint32_t>(x) ^ 0x80000
 // ---------------------------------------------------------------- wave / block scans
 ECHO_DEV int lane_id() { return __lane_id(); }
 
+// One DPP move: lane i receives the CTRL-selected lane's v; lanes outside ROW_MASK, and lanes
+// whose source is outside its row, receive `old`.  Every lane of the wave must be active.
+template <int CTRL, int ROW_MASK>
+ECHO_DEV uint32_t dpp_mov(uint32_t old, uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v),
+                                                           CTRL, ROW_MASK, 0xF, false));
+}
+constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118;
+constexpr int DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
+
+// Inclusive scan of OP over the 64 lanes: Hillis-Steele inside each 16-lane row with row
+// shifts, then each row's total carried into the following rows with the row broadcasts.
+template <typename OP>
+ECHO_DEV uint32_t wave_incl_scan_op(uint32_t v, uint32_t identity, OP op) {
+  v = op(v, dpp_mov<DPP_ROW_SHR1, 0xF>(identity, v));
+  v = op(v, dpp_mov<DPP_ROW_SHR2, 0xF>(identity, v));
+  v = op(v, dpp_mov<DPP_ROW_SHR4, 0xF>(identity, v));
+  v = op(v, dpp_mov<DPP_ROW_SHR8, 0xF>(identity, v));
+  v = op(v, dpp_mov<DPP_ROW_BCAST15, 0xA>(identity, v));
+  v = op(v, dpp_mov<DPP_ROW_BCAST31, 0xC>(identity, v));
+  return v;
+}
+
+struct OpAdd { ECHO_DEV uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct OpMin { ECHO_DEV uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
+struct OpMax { ECHO_DEV uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
+
 // inclusive prefix sum over the 64 lanes of a wave
-ECHO_DEV uint32_t wave_incl_scan(uint32_t v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t t = __shfl_up(v, off, 64);
-    if (l >= off) v += t;
-  }
+ECHO_DEV uint32_t wave_incl_scan(uint32_t v) { return wave_incl_scan_op(v, 0u, OpAdd{}); }
+
+// inclusive prefix sum inside each 16-lane row (lane 15 of a row holds the row's total)
+ECHO_DEV uint32_t row16_incl_scan(uint32_t v) {
+  v += dpp_mov<DPP_ROW_SHR1, 0xF>(0u, v);
+  v += dpp_mov<DPP_ROW_SHR2, 0xF>(0u, v);
+  v += dpp_mov<DPP_ROW_SHR4, 0xF>(0u, v);
+  v += dpp_mov<DPP_ROW_SHR8, 0xF>(0u, v);
   return v;
 }
 
 ECHO_DEV uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_incl_scan(v)), 63));
+}
+ECHO_DEV uint32_t wave_min(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_incl_scan_op(v, ~0u, OpMin{})), 63));
+}
+ECHO_DEV uint32_t wave_max(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wave_incl_scan_op(v, 0u, OpMax{})), 63));
 }
 
 // Exclusive block-wide prefix sum for a block of NT threads (NT multiple of 64, <= 1024).
@@ -113,7 +145,7 @@ ECHO_DEV void hist_add_peeled(uint32_t *hist, uint32_t bin, bool act) {
   const uint64_t m_act = __ballot(act);
   if (!m_act) return;
   const int leader = __ffsll(static_cast<unsigned long long>(m_act)) - 1;
-  const uint32_t lead_bin = __shfl(bin, leader, 64);
+  const uint32_t lead_bin = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), leader));
   const uint64_t same = __ballot(act && bin == lead_bin);
   if (lane_id() == leader) atomicAdd(&hist[lead_bin], static_cast<uint32_t>(__popcll(same)));
   if (act && bin != lead_bin) atomicAdd(&hist[bin], 1u);

@@ -4,17 +4,17 @@
 // one hipGraph (§2: graph execution forbids host control and dynamically sized tensors inside
 // the step).
 //
-// Streams.  `main` carries the critical path.  `side` (when different) first computes the
-// pool statistics (free count, priority histogram), which do not depend on the selection, while
-// `main` scores; with prefetch, scoring is split into n_chunks token ranges and after each
-// range `side` allocates and gathers that range's candidates while `main` scores the next one.
-// `main` waits for `side` before the top-k finish, whose fused lookup updates the statistics.
+// One stream.  Kernel boundaries on one queue cost next to nothing, while dependencies between
+// queues inside a graph cost microseconds each, so work that can overlap the critical path
+// rides along in the same launches as extra workgroups instead of on a second stream:
 //
-//   main: zero -> [threshold, free list] -> score(+top-k histogram) [x chunks] -> top-k split
-//         -> join -> top-k finish + lookup -> evict-1 -> evict-2 + allocate -> recall gather
-//   side: pool stats -> [prefetch gather per chunk]
+//   zero -> score (+ pool statistics) -> top-k split -> top-k finish + lookup
+//        -> evict-1 (+ recall staging, first half of the requests)
+//        -> evict-2 + allocate (+ recall staging, second half) -> recall scatter
+//
+// With prefetch, scoring is split into n_chunks token ranges: the launch of range c also
+// gathers range c-1's candidates, and the top-k split launch gathers the last range's.
 #include <algorithm>
-#include <vector>
 
 #include "internal.hpp"
 
@@ -33,6 +33,7 @@ struct DecodeWs {
   int32_t *cand;       // [n_chunks][n_rows][cap]
   int32_t *free_list;  // [n_gpu]
   int32_t *free_count; // [2]
+  uint16_t *stage;     // [n_rows * topk][ROW] recalled rows before they go to their slots
 };
 
 static size_t decode_ws_layout(const echo_decode_args *a, int32_t n_gpu, void *base, DecodeWs *w) {
@@ -47,6 +48,7 @@ static size_t decode_ws_layout(const echo_decode_args *a, int32_t n_gpu, void *b
   const size_t o_pool = take(pbytes);
   const size_t zero_end = o_pool + static_cast<size_t>(pw.zero_words) * 4;
   const size_t o_split = take(topk_split_ws_bytes(a->n_rows, a->max_key_len, a->topk));
+  const size_t o_st = take(nr * static_cast<size_t>(a->topk) * ROW * 2);
   size_t o_th = 0, o_c = 0, o_fl = 0, o_fc = 0;
   if (pf) {
     o_th = take(nr * 4);
@@ -62,32 +64,13 @@ static size_t decode_ws_layout(const echo_decode_args *a, int32_t n_gpu, void *b
     pool_fast_ws_layout(a->n_rows, a->topk, n_gpu, b + o_pool, &w->pool, &pbytes);
     w->zero_words = static_cast<int64_t>(zero_end / 4);
     w->split = b + o_split;
+    w->stage = reinterpret_cast<uint16_t *>(b + o_st);
     w->theta = reinterpret_cast<float *>(b + o_th);
     w->cand = reinterpret_cast<int32_t *>(b + o_c);
     w->free_list = reinterpret_cast<int32_t *>(b + o_fl);
     w->free_count = reinterpret_cast<int32_t *>(b + o_fc);
   }
   return off;
-}
-
-// Fork/join events, created once per thread and reused (never during a capture).
-static thread_local std::vector<hipEvent_t> t_events;
-
-static int ensure_events(size_t n) {
-  while (t_events.size() < n) {
-    hipEvent_t e;
-    hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableTiming);
-    if (err != hipSuccess) return fail(ECHO_EHIP, "hipEventCreate: %s", hipGetErrorString(err));
-    t_events.push_back(e);
-  }
-  return ECHO_OK;
-}
-
-static int edge(hipStream_t from, hipStream_t to, size_t ev) {
-  hipError_t e = hipEventRecord(t_events[ev], from);
-  if (e == hipSuccess) e = hipStreamWaitEvent(to, t_events[ev], 0);
-  if (e != hipSuccess) return fail(ECHO_EHIP, "decode step fork/join: %s", hipGetErrorString(e));
-  return ECHO_OK;
 }
 
 static int validate(const echo_decode_args *a, const echo_pool *pool, const echo_decode_out *o) {
@@ -116,8 +99,7 @@ static int validate(const echo_decode_args *a, const echo_pool *pool, const echo
 }
 
 static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
-                              const echo_decode_out *o, void *ws, size_t ws_bytes,
-                              hipStream_t m, hipStream_t sd) {
+                              const echo_decode_out *o, void *ws, size_t ws_bytes, hipStream_t m) {
   int rc = validate(a, pool, o);
   if (rc) return rc;
   DecodeWs W{};
@@ -125,56 +107,64 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
   if (!ws || ws_bytes < need) return fail(ECHO_EWORKSPACE, "echo_decode_select: workspace %zu < %zu", ws_bytes, need);
   const int32_t n_ent = a->n_rows * a->topk;
   const bool pf = a->prefetch != 0;
-  const bool split = sd != m;
   const int nc = pf ? a->n_chunks : 1;
-  if (split && (rc = ensure_events(static_cast<size_t>(nc) + 2))) return rc;
-  const size_t ev_fork = 0, ev_join = 1;
 
   if ((rc = launch_zero2_i32(o->counters, 8, reinterpret_cast<int32_t *>(W.hist0), W.zero_words, m))) return rc;
-  hipStream_t ss = m;
-  if (split) {
-    if ((rc = edge(m, sd, ev_fork))) return rc;
-    ss = sd;
-  }
-  if ((rc = launch_pool_stats(pool, W.pool, a->step_id, ss))) return rc;
+  SideWork side{};
+  side.P = PoolArgs{pool->gpu_free, pool->gpu_priority, pool->gpu_to_host, pool->host_to_gpu,
+                    pool->indices_buf, pool->status, pool->n_gpu, pool->n_host};
+  side.W = W.pool;
+  side.step_id = a->step_id;
+  side.n_stats = W.pool.n_chunks;                   // statistics ride with the first scoring launch
   if (pf) {
     if ((rc = launch_prefetch_threshold(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len,
                                         a->n_rows, a->n_sample, a->percentile, W.theta, m)))
       return rc;
     if ((rc = launch_prefetch_begin(pool, W.free_list, W.free_count, m))) return rc;
     const int32_t span = (a->max_key_len + nc - 1) / nc;
-    for (int c = 0; c < nc; ++c) {
+    for (int c = 0; c <= nc; ++c) {
+      if (c > 0) {                                   // gather range c-1's candidates
+        side.n_gather = a->n_rows;
+        side.G = make_gather_args(pool, a->key_begin, a->req_to_host,
+                                  W.cand + static_cast<int64_t>(c - 1) * a->n_rows * a->cap,
+                                  W.cand_cnt + static_cast<int64_t>(c - 1) * a->n_rows, a->cap,
+                                  W.free_list, W.free_count, o->counters + 2, &W.pool, a->step_id);
+      }
+      if (c == nc) {
+        if ((rc = launch_topk_split(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,
+                                    a->topk, W.hist0, W.split, &side, m)))
+          return rc;
+        break;
+      }
       const int32_t lo = c * span, hi = (c + 1 == nc) ? a->max_key_len : (c + 1) * span;
       PrefetchArgs P{W.theta, a->req_to_host, pool->host_to_gpu,
                      W.cand + static_cast<int64_t>(c) * a->n_rows * a->cap,
                      W.cand_cnt + static_cast<int64_t>(c) * a->n_rows, W.total_cnt, a->cap, a->cap_div};
       if ((rc = launch_score_decode(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len, a->n_rows,
-                                    a->max_key_len, lo, hi, o->scores, a->max_key_len, &P, W.hist0, m)))
+                                    a->max_key_len, lo, hi, o->scores, a->max_key_len, &P, W.hist0,
+                                    &side, m)))
         return rc;
-      if (split && (rc = edge(m, sd, 2 + c))) return rc;
-      if ((rc = launch_prefetch_gather(pool, a->key_begin, a->req_to_host, P.cand, P.cand_cnt,
-                                       a->n_rows, a->cap, W.free_list, W.free_count, o->counters + 2,
-                                       &W.pool, a->step_id, ss)))
-        return rc;
+      side.n_stats = 0;
     }
   } else {
     if ((rc = launch_score_decode(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len, a->n_rows,
                                   a->max_key_len, 0, a->max_key_len, o->scores, a->max_key_len,
-                                  nullptr, W.hist0, m)))
+                                  nullptr, W.hist0, &side, m)))
+      return rc;
+    if ((rc = launch_topk_split(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,
+                                a->topk, W.hist0, W.split, nullptr, m)))
       return rc;
   }
-  if ((rc = launch_topk_split(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,
-                              a->topk, W.hist0, W.split, m)))
-    return rc;
-  if (split && (rc = edge(sd, m, ev_join))) return rc;
   if ((rc = launch_topk_finish(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,
                                a->topk, W.hist0, W.split, o->topk_idx, pool, &W.pool, a->key_begin,
-                               a->req_to_host, a->step_id, o->topk_slot, m)))
+                               a->req_to_host, a->step_id, o->topk_slot, true, m)))
     return rc;
   if ((rc = launch_pool_evict(pool, W.pool, o->topk_idx, a->n_rows, a->topk, a->step_id, o->topk_slot,
-                              o->miss_host, o->miss_slot, o->counters + 0, m)))
+                              o->miss_host, o->miss_slot, o->counters + 0, W.stage, m)))
     return rc;
-  if ((rc = launch_recall_gather(pool, o->miss_host, o->miss_slot, o->counters + 0, n_ent, m))) return rc;
+  if ((rc = launch_recall_scatter(pool, W.pool, o->miss_host, o->miss_slot, o->counters + 0, n_ent,
+                                  W.stage, m)))
+    return rc;
   if (pf && (rc = launch_sum_i32(W.total_cnt, a->n_rows, o->counters + 1, m))) return rc;
   return ECHO_OK;
 }
@@ -199,7 +189,8 @@ extern "C" size_t echo_decode_workspace_bytes(const echo_decode_args *a, int32_t
 extern "C" int echo_decode_select(const echo_decode_args *a, const echo_pool *pool,
                                   const echo_decode_out *out, void *ws, size_t ws_bytes,
                                   void *main_stream, void *side_stream) {
-  return decode_select_impl(a, pool, out, ws, ws_bytes, S(main_stream), S(side_stream));
+  (void)side_stream;                       // reserved: the step runs on main_stream
+  return decode_select_impl(a, pool, out, ws, ws_bytes, S(main_stream));
 }
 
 extern "C" int echo_graph_capture_decode(const echo_decode_args *a, const echo_pool *pool,
@@ -208,15 +199,13 @@ extern "C" int echo_graph_capture_decode(const echo_decode_args *a, const echo_p
   if (!graph) return fail(ECHO_EINVAL, "echo_graph_capture_decode: NULL graph");
   *graph = nullptr;
   if (!main_stream) return fail(ECHO_EINVAL, "echo_graph_capture_decode: capture needs a non-null main stream");
+  (void)side_stream;                       // reserved: the step runs on main_stream
   int rc = validate(a, pool, out);
   if (rc) return rc;
-  if (side_stream != main_stream &&
-      (rc = ensure_events(static_cast<size_t>(a->prefetch ? a->n_chunks : 1) + 2)))
-    return rc;
   hipStream_t m = S(main_stream);
   hipError_t e = hipStreamBeginCapture(m, hipStreamCaptureModeThreadLocal);
   if (e != hipSuccess) return fail(ECHO_EHIP, "hipStreamBeginCapture: %s", hipGetErrorString(e));
-  rc = decode_select_impl(a, pool, out, ws, ws_bytes, m, S(side_stream));
+  rc = decode_select_impl(a, pool, out, ws, ws_bytes, m);
   hipGraph_t g = nullptr;
   e = hipStreamEndCapture(m, &g);
   if (rc) {

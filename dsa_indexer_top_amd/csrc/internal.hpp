@@ -27,10 +27,12 @@ struct PoolArgs {
 };
 
 // hist0 (optional, [n_q][2048]): digit-0 histogram of the top-k keys of the scores, added to
+// side (optional): pool work carried by the same launch as leading workgroups
 int launch_score_decode(const uint8_t *q, const float *w, const uint8_t *k, const float *k_scale,
                         const int64_t *key_begin, const int32_t *key_len, int32_t n_q,
                         int32_t max_len, int32_t tok_lo, int32_t tok_hi, float *scores,
-                        int64_t ld, const PrefetchArgs *pf, uint32_t *hist0, hipStream_t st);
+                        int64_t ld, const PrefetchArgs *pf, uint32_t *hist0, const struct SideWork *side,
+                        hipStream_t st);
 
 size_t topk_ws_bytes(int32_t n_rows, int32_t max_len);
 // hist0: optional digit-0 histograms from launch_score_decode
@@ -44,9 +46,9 @@ int launch_topk(const float *scores, int64_t ld, const int32_t *len, int32_t n_r
 // Workspace of the multi-workgroup pool step (pool_fast.hip).  The first zero_words 32-bit
 // words (counters, priority histograms, protection bitmap) must be zeroed before each step.
 struct PoolFastWs {
-  int32_t *counters;      // [16]: 0 free slots (stats; prefetch decrements)
-  uint32_t *fine;         // [65536] occupied, unprotected slots per priority bin
-  uint32_t *coarse;       // [2048]  the same, 32 fine bins per coarse bin
+  int32_t *counters;      // [16]: 0 free slots, 2 threshold fine bin, 3 evictable slots below it
+  uint32_t *fine;         // [32768] occupied, unprotected slots per priority bin
+  uint32_t *coarse;       // [1024]  the same, 32 fine bins per coarse bin
   uint32_t *prot;         // [ceil(n_gpu/32)] protection bitmap (slots holding a selected token)
   uint32_t *row_miss_cnt; // [n_rows]
   int32_t *row_miss_h;    // [n_rows * k] ordered misses of each request: host index
@@ -55,21 +57,69 @@ struct PoolFastWs {
   uint32_t *chunk_cand;   // [n_chunks] threshold-bin slots per chunk
   uint64_t *cand;         // [n_chunks * 4096] (priority key << 32 | slot), per chunk in slot order
   int32_t *miss_entry;    // [n_rows * k] entry (r*k + j) of the i-th miss
+  int32_t *miss_stage;    // [n_rows * k] r*k + (position in request r's miss list) of the i-th miss
   void *base;
   int32_t n_chunks;
   int64_t zero_words;
 };
+// Prefetch gather of one scoring range's candidates (one workgroup per request).
+struct GatherArgs {
+  const uint16_t *host_kv;
+  uint16_t *gpu_kv;
+  uint8_t *free_;
+  int32_t *priority, *to_host, *host_to_gpu;
+  const int32_t *status;
+  int32_t n_gpu, n_host;
+  const int64_t *key_begin;
+  const int32_t *req_to_host;
+  const int32_t *cand;        // [n_q, cap] token indices of one scoring range's candidates
+  const int32_t *cand_cnt;    // [n_q]
+  int32_t cap;
+  const int32_t *free_list;   // free slots in ascending order
+  int32_t *free_count;        // [2]: free slots listed, slots taken so far
+  int32_t *n_prefetched;
+  int32_t *st_free;           // optional pool-step statistics to keep current
+  uint32_t *st_fine, *st_coarse;
+  int32_t step_id;
+};
+GatherArgs make_gather_args(const echo_pool *pool, const int64_t *key_begin,
+                            const int32_t *req_to_host, const int32_t *cand,
+                            const int32_t *cand_cnt, int32_t cap, const int32_t *free_list,
+                            int32_t *free_count, int32_t *n_prefetched, const PoolFastWs *pw,
+                            int32_t step_id);
+
+// Work that rides along in another kernel's launch as extra leading workgroups of 256 threads:
+// n_stats pool-statistics chunks (every occupied slot), then n_gather prefetch-gather requests.
+struct SideWork {
+  PoolArgs P;
+  PoolFastWs W;
+  int32_t step_id;
+  int32_t n_stats;
+  int32_t n_gather;
+  GatherArgs G;
+};
 void pool_fast_ws_layout(int32_t n_rows, int32_t k, int32_t n_gpu, void *base, PoolFastWs *w,
                          size_t *bytes);
 size_t pool_fast_ws_bytes(int32_t n_rows, int32_t k, int32_t n_gpu);
-int launch_pool_stats(const echo_pool *pool, const PoolFastWs &W, int32_t step_id, hipStream_t st);
+// excl_prot: histogram only unprotected slots (after the lookup); otherwise all occupied
+// slots, and the lookup subtracts what it protects.
+int launch_pool_stats(const echo_pool *pool, const PoolFastWs &W, int32_t step_id, bool excl_prot,
+                      hipStream_t st);
 int launch_pool_lookup_rows(const echo_pool *pool, const PoolFastWs &W, const int32_t *idx,
                             const int64_t *key_begin, const int32_t *req_to_host, int64_t n_k,
                             int32_t n_rows, int32_t k, int32_t step_id, int32_t *topk_slot,
                             hipStream_t st);
+// Missed rows copied into a staging area by workgroups riding along in the eviction launches.
+struct StageArgs {
+  const uint16_t *host_kv;
+  uint16_t *stage;            // [n_rows * k][ROW]; NULL: no staging
+  int32_t rows_a;             // requests staged during evict-1; the rest during evict-2
+};
+// stage (optional): read the missed rows into stage[r*k + i] while evicting (the caller then
+// runs launch_recall_scatter)
 int launch_pool_evict(const echo_pool *pool, const PoolFastWs &W, const int32_t *idx, int32_t n_rows,
                       int32_t k, int32_t step_id, int32_t *topk_slot, int32_t *miss_host,
-                      int32_t *miss_slot, int32_t *n_miss, hipStream_t st);
+                      int32_t *miss_slot, int32_t *n_miss, uint16_t *stage, hipStream_t st);
 
 int launch_pool_step(const echo_pool *pool, const int32_t *idx, const int64_t *key_begin,
                      const int32_t *req_to_host, int64_t n_k, int32_t n_rows, int32_t k,
@@ -77,20 +127,26 @@ int launch_pool_step(const echo_pool *pool, const int32_t *idx, const int64_t *k
                      int32_t *n_miss, void *ws, size_t ws_bytes, hipStream_t st);
 
 // Decode top-k: split (multi-workgroup) then finish (one workgroup per request); when pool is
-// not NULL the finish also performs the residency lookup into *pw (whose zeroed region and
-// statistics must be ready).
+// not NULL the finish also performs the residency lookup into *pw (whose zeroed region must be
+// ready); sub_prot: the histograms hold every occupied slot and the lookup subtracts the slots
+// it protects.
 size_t topk_split_ws_bytes(int32_t n_rows, int32_t max_len, int32_t k);
 int launch_topk_split(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
                       int32_t max_len, int32_t k, const uint32_t *hist0, void *split_ws,
-                      hipStream_t st);
+                      const SideWork *side, hipStream_t st);
 int launch_topk_finish(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
                        int32_t max_len, int32_t k, const uint32_t *hist0, void *split_ws,
                        int32_t *idx, const echo_pool *pool, const PoolFastWs *pw,
                        const int64_t *key_begin, const int32_t *req_to_host, int32_t step_id,
-                       int32_t *topk_slot, hipStream_t st);
+                       int32_t *topk_slot, bool sub_prot, hipStream_t st);
 
 int launch_recall_gather(const echo_pool *pool, const int32_t *miss_host, const int32_t *miss_slot,
                          const int32_t *n_miss, int32_t max_miss, hipStream_t st);
+// Staged recall, second half: moves staged rows (stage[miss_stage[rank]]) to their allocated
+// slots once allocation is done.
+int launch_recall_scatter(const echo_pool *pool, const PoolFastWs &W, const int32_t *miss_host,
+                          const int32_t *miss_slot, const int32_t *n_miss, int32_t max_miss,
+                          const uint16_t *stage, hipStream_t st);
 
 int launch_prefetch_threshold(const uint8_t *q, const float *w, const uint8_t *k,
                               const float *k_scale, const int64_t *key_begin,
@@ -98,8 +154,8 @@ int launch_prefetch_threshold(const uint8_t *q, const float *w, const uint8_t *k
                               float percentile, float *theta, hipStream_t st);
 int launch_prefetch_begin(const echo_pool *pool, int32_t *free_list, int32_t *free_count,
                           hipStream_t st);
-// pw (optional): pool-step statistics kept consistent with the allocations (free count, and
-// the priority histogram for the new slots' priority 0 relative to step_id)
+// pw (optional): pool-step statistics (free count, priority histograms) updated for the slots
+// this call fills (priority 0 relative to step_id)
 int launch_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
                            const int32_t *req_to_host, const int32_t *cand,
                            const int32_t *cand_cnt, int32_t n_q, int32_t cap,

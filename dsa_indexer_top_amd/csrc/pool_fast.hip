@@ -5,15 +5,16 @@
 // the `need` unprotected occupied slots with the smallest (priority, slot); the i-th miss (in
 // request, token order) takes the i-th free slot in ascending slot order.
 //
-//   stats    per slot: free count, and a 65536-bin histogram (plus a 2048-bin coarse one) of
-//            the occupied slots' priorities under a monotone "log-age" code relative to the
-//            step stamp (ages below 512 get a bin each, older ones bins 1/512 wide).  It does
-//            not depend on the selection, so the decode step runs it on a side stream while
-//            scoring.
 //   lookup   per selected entry: host index -> slot; a hit sets the slot's bit in a
-//            protection bitmap (the first setter removes the slot from the histogram), a miss
-//            goes to an ordered per-request list.  (The decode step fuses this into the top-k
-//            finish kernel.)
+//            protection bitmap, a miss goes to an ordered per-request list.  (The decode step
+//            fuses this into the top-k finish kernel.)
+//   stats    per 4096-slot chunk: free count, and a 32768-bin histogram (plus a 1024-bin
+//            coarse one) of the evictable (occupied, unprotected) slots' priorities under a
+//            monotone "log-age" code relative to the step stamp (ages below 512 get a bin
+//            each, older ones bins 1/512 of an octave wide).  Each workgroup counts its chunk in
+//            LDS (16-bit counters) and adds only its non-empty bins to the global histograms:
+//            priorities are step stamps, so whole chunks share a few bins and per-slot global
+//            atomics would serialise on them.
 //   evict-1  multi-workgroup: the misses are laid out in global order; every slot chunk
 //            finds the threshold bin from the histograms, evicts its unprotected slots below
 //            it (a set: order does not matter) and lists the threshold-bin slots in slot order.
@@ -30,10 +31,6 @@
 
 namespace echo {
 
-constexpr int PF_T = 256;                     // threads of the slot / entry workgroups
-constexpr int PF_CH = 4096;                   // slots per chunk
-constexpr int PF_FINE = 65536;
-constexpr int PF_COARSE = 2048;
 constexpr int PF_RES_T = 1024;                // threads of the resolving workgroups
 constexpr int PF_CAP = 8192;                  // threshold-bin slots resolved in LDS
 
@@ -53,7 +50,7 @@ void pool_fast_ws_layout(int32_t n_rows, int32_t k, int32_t n_gpu, void *base, P
                o_rmh = take(static_cast<size_t>(n_ent) * 4), o_rmj = take(static_cast<size_t>(n_ent) * 4),
                o_cf = take(static_cast<size_t>(n_chunks) * 4), o_cc = take(static_cast<size_t>(n_chunks) * 4),
                o_cand = take(static_cast<size_t>(n_chunks) * PF_CH * 8),
-               o_me = take(static_cast<size_t>(n_ent) * 4);
+               o_me = take(static_cast<size_t>(n_ent) * 4), o_ms = take(static_cast<size_t>(n_ent) * 4);
   *bytes = off;
   w->n_chunks = n_chunks;
   w->zero_words = static_cast<int64_t>(zero_end / 4);
@@ -70,6 +67,7 @@ void pool_fast_ws_layout(int32_t n_rows, int32_t k, int32_t n_gpu, void *base, P
     w->chunk_cand = reinterpret_cast<uint32_t *>(b + o_cc);
     w->cand = reinterpret_cast<uint64_t *>(b + o_cand);
     w->miss_entry = reinterpret_cast<int32_t *>(b + o_me);
+    w->miss_stage = reinterpret_cast<int32_t *>(b + o_ms);
     w->base = base;
   }
 }
@@ -81,40 +79,13 @@ size_t pool_fast_ws_bytes(int32_t n_rows, int32_t k, int32_t n_gpu) {
   return b;
 }
 
-// ---------------------------------------------------------------- stats (side stream)
+// ---------------------------------------------------------------- stats (after the lookup)
+// EXCL_PROT: leave protected slots out (stats taken after the lookup).  Without it the
+// histogram counts every occupied slot and the lookup subtracts the slots it protects.
+template <bool EXCL_PROT>
 __global__ __launch_bounds__(PF_T) void pool_stats_kernel(PoolArgs P, PoolFastWs W, int32_t step_id) {
-  __shared__ uint32_t tmp[48];
-  const int32_t c = blockIdx.x;
-  uint32_t nf = 0;
-  for (int j = 0; j < PF_CH / (4 * PF_T); ++j) {
-    const int32_t s0 = c * PF_CH + j * 4 * PF_T + threadIdx.x * 4;
-    uint32_t fw;
-    int4 pr;
-    if (s0 + 3 < P.n_gpu) {
-      fw = *reinterpret_cast<const uint32_t *>(P.free_ + s0);
-      pr = *reinterpret_cast<const int4 *>(P.priority + s0);
-    } else {
-      fw = 0xFFFFFFFFu;
-      pr = int4{0, 0, 0, 0};
-      for (int e = 0; e < 4; ++e)
-        if (s0 + e < P.n_gpu) {
-          fw = (fw & ~(0xFFu << (8 * e))) | (static_cast<uint32_t>(P.free_[s0 + e]) << (8 * e));
-          (&pr.x)[e] = P.priority[s0 + e];
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t f = (fw >> (8 * e)) & 0xFFu;
-      nf += f == 1;
-      if (f == 0) {
-        const uint32_t b = prio_bin((&pr.x)[e], step_id);
-        atomicAdd(&W.fine[b], 1u);
-        atomicAdd(&W.coarse[b >> 5], 1u);
-      }
-    }
-  }
-  nf = block_sum<PF_T>(nf, tmp);
-  if (threadIdx.x == 0 && nf) atomicAdd(&W.counters[0], static_cast<int32_t>(nf));
+  __shared__ uint32_t lds[STATS_LDS_WORDS];
+  stats_chunk<EXCL_PROT>(P, W, step_id, blockIdx.x, lds);
 }
 
 // Standalone lookup (echo_pool_lookup_alloc): one 1024-thread workgroup per request, entries in
@@ -141,7 +112,7 @@ __global__ __launch_bounds__(PF_RES_T) void pool_lookup_rows_kernel(
       }
     }
     if (has && h >= 0 && h < P.n_host) slot = P.host_to_gpu[h];
-    if (has) res = lookup_entry(P, W, h, slot, step_id);
+    if (has) res = lookup_entry(P, W, h, slot);
     const bool miss = res == INF;
     uint32_t tot;
     const uint32_t pos = n_miss + block_excl_scan<PF_RES_T>(miss ? 1u : 0u, tmp, &tot);
@@ -155,65 +126,76 @@ __global__ __launch_bounds__(PF_RES_T) void pool_lookup_rows_kernel(
   if (threadIdx.x == 0) W.row_miss_cnt[r] = n_miss;
 }
 
-// ---------------------------------------------------------------- shared step state
+// ---------------------------------------------------------------- step state
+// counters[] slots written by evict-1 (chunk 0) for evict-2
+constexpr int CT_FB = 2, CT_BELOW = 3, CT_NMISS = 4, CT_NEED = 5, CT_ABORT = 6;
+
 struct StepState {
-  uint32_t n_miss, n_free, need, evictable;
+  uint32_t n_miss, need, evictable, fb, below;
   bool abort;
 };
 
-ECHO_DEV StepState step_state(const PoolArgs &P, const PoolFastWs &W, int32_t n_rows, uint32_t *tmp) {
-  StepState s;
-  uint32_t nm = 0, ev = 0;
-  for (int r = threadIdx.x; r < n_rows; r += blockDim.x) nm += W.row_miss_cnt[r];
-  for (int b = threadIdx.x; b < PF_COARSE; b += blockDim.x) ev += W.coarse[b];
-  if (blockDim.x == PF_T) {
-    nm = block_sum<PF_T>(nm, tmp);
-    ev = block_sum<PF_T>(ev, tmp);
-  } else {
-    nm = block_sum<PF_RES_T>(nm, tmp);
-    ev = block_sum<PF_RES_T>(ev, tmp);
-  }
-  s.n_miss = nm;
-  s.evictable = ev;
-  s.n_free = static_cast<uint32_t>(W.counters[0]);
-  s.need = nm > s.n_free ? nm - s.n_free : 0u;
-  s.abort = (*(volatile int32_t *)P.status) != 0 || s.need > ev;
-  return s;
-}
-
-// Threshold fine bin: the bin holding the need-th smallest evictable priority, and the count
-// of evictable slots in lower bins.  256 threads.
-ECHO_DEV void prio_pick(const PoolFastWs &W, uint32_t need, uint32_t *tmp, uint32_t &fb,
-                        uint32_t &below) {
+// Totals, the abort decision and the threshold fine bin (the bin holding the need-th smallest
+// evictable priority, with the count of evictable slots in lower bins).  PF_T threads; every
+// independent global load is issued before the first wait.
+ECHO_DEV StepState step_pick(const PoolArgs &P, const PoolFastWs &W, int32_t n_rows, uint32_t *tmp) {
+  constexpr int PER = PF_COARSE / PF_T;
+  static_assert(PER == 4, "four coarse bins per thread");
   const int t = threadIdx.x;
-  uint32_t local = 0;
-  for (int i = 0; i < PF_COARSE / PF_T; ++i) local += W.coarse[t * (PF_COARSE / PF_T) + i];
-  uint32_t total;
-  const uint32_t before = block_excl_scan<PF_T>(local, tmp, &total);
+  uint32_t nm = 0;
+  for (int r = t; r < n_rows; r += PF_T) nm += W.row_miss_cnt[r];
+  const uint4 cv = *reinterpret_cast<const uint4 *>(W.coarse + t * PER);
+  const int32_t status = *(volatile int32_t *)P.status;
+  const uint32_t n_free = static_cast<uint32_t>(W.counters[0]);
+  const uint32_t local = cv.x + cv.y + cv.z + cv.w;
+  StepState s;
+  const uint32_t before = block_excl_scan<PF_T>(local, tmp, &s.evictable);
+  s.n_miss = block_sum<PF_T>(nm, tmp);
+  s.need = s.n_miss > n_free ? s.n_miss - n_free : 0u;
+  s.abort = status != 0 || s.need > s.evictable;
+  s.fb = 0xFFFFFFFFu;
+  s.below = 0;
+  if (s.abort || s.need == 0) return s;
+  const uint32_t need = s.need;
   if (before < need && need <= before + local) {
     uint32_t cum = before;
-    for (int i = 0; i < PF_COARSE / PF_T; ++i) {
-      const int cb = t * (PF_COARSE / PF_T) + i;
-      const uint32_t c = W.coarse[cb];
-      if (cum < need && need <= cum + c) {
-        for (int f = cb * 32; f < cb * 32 + 32; ++f) {
-          const uint32_t cf = W.fine[f];
-          if (cum < need && need <= cum + cf) {
-            tmp[40] = static_cast<uint32_t>(f);
-            tmp[41] = cum;
-            break;
-          }
-          cum += cf;
-        }
-        break;
-      }
-      cum += c;
+    int cb = t * PER;
+    const uint32_t c4[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (cum < need && need <= cum + c4[i]) { cb = t * PER + i; break; }
+      cum += c4[i];
+    }
+    tmp[40] = static_cast<uint32_t>(cb);
+    tmp[41] = cum;
+  }
+  __syncthreads();
+  if (t < 64) {
+    const uint32_t cb = tmp[40], cum = tmp[41];
+    const uint32_t v = t < 32 ? W.fine[cb * 32 + t] : 0u;
+    const uint32_t inc = wave_incl_scan(v);
+    if (t < 32 && cum + inc - v < need && need <= cum + inc) {
+      tmp[42] = cb * 32 + t;
+      tmp[43] = cum + inc - v;
     }
   }
   __syncthreads();
-  fb = tmp[40];
-  below = tmp[41];
+  s.fb = tmp[42];
+  s.below = tmp[43];
   __syncthreads();
+  return s;
+}
+
+// The same state as published by evict-1.
+ECHO_DEV StepState step_read(const PoolFastWs &W) {
+  StepState s;
+  s.fb = static_cast<uint32_t>(W.counters[CT_FB]);
+  s.below = static_cast<uint32_t>(W.counters[CT_BELOW]);
+  s.n_miss = static_cast<uint32_t>(W.counters[CT_NMISS]);
+  s.need = static_cast<uint32_t>(W.counters[CT_NEED]);
+  s.abort = W.counters[CT_ABORT] != 0;
+  s.evictable = 0;
+  return s;
 }
 
 ECHO_DEV void evict_slot(const PoolArgs &P, int32_t slot) {
@@ -229,9 +211,16 @@ ECHO_DEV void evict_slot(const PoolArgs &P, int32_t slot) {
 // slot chunks.
 __global__ __launch_bounds__(PF_T) void pool_evict1_kernel(PoolArgs P, PoolFastWs W, int32_t n_rows,
                                                            int32_t k, int32_t step_id,
-                                                           int32_t *__restrict__ miss_host) {
+                                                           int32_t *__restrict__ miss_host,
+                                                           StageArgs SA) {
   __shared__ uint32_t tmp[48];
   __shared__ uint32_t gscan[4 * (PF_T / 64) + PF_T / 64 + 2];
+  if (static_cast<int>(blockIdx.x) >= n_rows + W.n_chunks) {
+    // recall staging of requests [0, SA.rows_a), 32 entries per block
+    const int u = blockIdx.x - n_rows - W.n_chunks, per = (k + 31) / 32;
+    stage_rows<PF_T, 32>(SA.host_kv, SA.stage, W, P.status, k, P.n_host, u / per, (u % per) * 32);
+    return;
+  }
   if (static_cast<int>(blockIdx.x) < n_rows) {
     const int r = blockIdx.x;
     uint32_t before = 0;
@@ -241,25 +230,20 @@ __global__ __launch_bounds__(PF_T) void pool_evict1_kernel(PoolArgs P, PoolFastW
     for (uint32_t i = threadIdx.x; i < cnt; i += PF_T) {
       miss_host[before + i] = W.row_miss_h[static_cast<int64_t>(r) * k + i];
       W.miss_entry[before + i] = r * k + W.row_miss_j[static_cast<int64_t>(r) * k + i];
+      W.miss_stage[before + i] = r * k + static_cast<int32_t>(i);
     }
     return;
   }
   const int32_t c = blockIdx.x - n_rows;
-  const StepState st = step_state(P, W, n_rows, tmp);
-  if (st.abort) {
-    if (c == 0 && threadIdx.x == 0 && st.need > st.evictable && !(*(volatile int32_t *)P.status))
-      atomicOr(P.status, ECHO_ST_EXHAUSTED);
-    return;
-  }
-  uint32_t fb = 0xFFFFFFFFu, below = 0;
-  if (st.need > 0) prio_pick(W, st.need, tmp, fb, below);
-  // one pass over the chunk: evict below the threshold bin, list the threshold bin in order
-  uint32_t fre[4], cand[4];
+  const int t = threadIdx.x;
+  // the chunk's slots (16 per thread: slot c*PF_CH + 4*PF_T*j + 4*t + e), loaded before the
+  // step state is known
+  uint32_t fre[4], pw[4];
   int32_t pr[4][4];
-  uint32_t cc[4], nf = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int32_t s0 = c * PF_CH + j * 4 * PF_T + threadIdx.x * 4;
+    const int32_t s0 = c * PF_CH + j * 4 * PF_T + t * 4;
+    pw[j] = s0 < P.n_gpu ? (W.prot[s0 >> 5] >> (s0 & 31)) & 0xFu : 0xFu;   // s0 % 4 == 0
     if (s0 + 3 < P.n_gpu) {
       fre[j] = *reinterpret_cast<const uint32_t *>(P.free_ + s0);
       const int4 v = *reinterpret_cast<const int4 *>(P.priority + s0);
@@ -275,26 +259,52 @@ __global__ __launch_bounds__(PF_T) void pool_evict1_kernel(PoolArgs P, PoolFastW
       }
     }
   }
+  const StepState st = step_pick(P, W, n_rows, tmp);
+  if (c == 0 && t == 0) {                              // for evict-2
+    W.counters[CT_FB] = static_cast<int32_t>(st.fb);
+    W.counters[CT_BELOW] = static_cast<int32_t>(st.below);
+    W.counters[CT_NMISS] = static_cast<int32_t>(st.n_miss);
+    W.counters[CT_NEED] = static_cast<int32_t>(st.need);
+    W.counters[CT_ABORT] = st.abort ? 1 : 0;
+    if (st.abort && st.need > st.evictable && !(*(volatile int32_t *)P.status))
+      atomicOr(P.status, ECHO_ST_EXHAUSTED);
+  }
+  if (st.abort) return;
+  // classify: evict below the threshold bin (a set: order does not matter), list the
+  // threshold bin in slot order
+  uint32_t ev = 0, cand = 0, cc[4], nf = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    cand[j] = 0;
     cc[j] = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int32_t slot = c * PF_CH + j * 4 * PF_T + threadIdx.x * 4 + e;
       const uint32_t f = (fre[j] >> (8 * e)) & 0xFFu;
       if (f == 1) { ++nf; continue; }
-      if (f != 0 || st.need == 0 || is_protected(W.prot, slot)) continue;
+      if (f != 0 || st.need == 0 || ((pw[j] >> e) & 1u)) continue;
       const uint32_t b = prio_bin(pr[j][e], step_id);
-      if (b < fb) {
-        evict_slot(P, slot);
+      if (b < st.fb) {
+        ev |= 1u << (4 * j + e);
         ++nf;
-      } else if (b == fb) {
-        cand[j] |= 1u << e;
+      } else if (b == st.fb) {
+        cand |= 1u << (4 * j + e);
         ++cc[j];
       }
     }
   }
+  // evictions: every to_host load first, then the stores
+  int32_t th[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    th[i] = ((ev >> i) & 1u) ? P.to_host[c * PF_CH + (i >> 2) * 4 * PF_T + t * 4 + (i & 3)] : -1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if ((ev >> i) & 1u) {
+      const int32_t slot = c * PF_CH + (i >> 2) * 4 * PF_T + t * 4 + (i & 3);
+      if (th[i] >= 0 && th[i] < P.n_host) P.host_to_gpu[th[i]] = INF;
+      P.to_host[slot] = INF;
+      P.priority[slot] = -1;
+      P.free_[slot] = 1;                     // the row stays: the host holds the backup
+    }
   uint32_t co[4], tot;
   group_excl_scan<PF_T, 4>(cc, co, gscan, &tot);
 #pragma unroll
@@ -302,15 +312,15 @@ __global__ __launch_bounds__(PF_T) void pool_evict1_kernel(PoolArgs P, PoolFastW
     uint32_t pos = co[j];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if ((cand[j] >> e) & 1) {
-        const int32_t slot = c * PF_CH + j * 4 * PF_T + threadIdx.x * 4 + e;
+      if ((cand >> (4 * j + e)) & 1u) {
+        const int32_t slot = c * PF_CH + j * 4 * PF_T + t * 4 + e;
         W.cand[static_cast<int64_t>(c) * PF_CH + pos] =
             (static_cast<uint64_t>(i32_key(pr[j][e])) << 32) | static_cast<uint32_t>(slot);
         ++pos;
       }
   }
   nf = block_sum<PF_T>(nf, tmp);
-  if (threadIdx.x == 0) {
+  if (t == 0) {
     W.chunk_free[c] = nf;
     W.chunk_cand[c] = tot;
   }
@@ -340,7 +350,8 @@ struct CandView {
 __global__ __launch_bounds__(PF_RES_T) void pool_evict2_kernel(
     PoolArgs P, PoolFastWs W, int32_t n_rows, int32_t k, int32_t step_id,
     int32_t *__restrict__ miss_host, int32_t *__restrict__ miss_slot, int32_t *__restrict__ topk_slot,
-    int32_t *__restrict__ n_miss_out, const int32_t *__restrict__ idx) {
+    int32_t *__restrict__ n_miss_out, const int32_t *__restrict__ idx, int32_t entry_blocks,
+    StageArgs SA) {
   __shared__ uint32_t tmp[48];
   __shared__ uint64_t cl[PF_CAP];
   __shared__ uint32_t hist[2048];
@@ -349,9 +360,16 @@ __global__ __launch_bounds__(PF_RES_T) void pool_evict2_kernel(
   const int t = threadIdx.x;
   const int32_t n_chunks = W.n_chunks;
   const int64_t n_ent = static_cast<int64_t>(n_rows) * k;
+  if (static_cast<int>(blockIdx.x) >= n_chunks + entry_blocks) {
+    // recall staging of requests [SA.rows_a, n_rows), 128 entries per block
+    const int u = blockIdx.x - n_chunks - entry_blocks, per = (k + 127) / 128;
+    stage_rows<PF_RES_T, 128>(SA.host_kv, SA.stage, W, P.status, k, P.n_host, SA.rows_a + u / per,
+                              (u % per) * 128);
+    return;
+  }
   if (static_cast<int>(blockIdx.x) >= n_chunks) {
     // ---- entry workgroups: stamp hits, pad the fixed-length lists
-    const StepState st = step_state(P, W, n_rows, tmp);
+    const StepState st = step_read(W);
     const int64_t e = static_cast<int64_t>(blockIdx.x - n_chunks) * PF_RES_T + t;
     if (st.abort) return;
     if (e < n_ent && idx[e] >= 0) {
@@ -368,7 +386,7 @@ __global__ __launch_bounds__(PF_RES_T) void pool_evict2_kernel(
     return;
   }
   const int32_t c = blockIdx.x;
-  const StepState st = step_state(P, W, n_rows, tmp);
+  const StepState st = step_read(W);
   if (c == 0 && t == 0) *n_miss_out = static_cast<int32_t>(st.n_miss);
   if (st.abort) return;
   // chunk prefixes of the threshold-bin list (n_chunks <= 1024 per resolving pass)
@@ -389,36 +407,7 @@ __global__ __launch_bounds__(PF_RES_T) void pool_evict2_kernel(
   }
   __syncthreads();
   if (st.need > 0) {
-    uint32_t fb, below;
-    // the threshold bin and the count below it (same as evict-1, with 1024 threads)
-    {
-      uint32_t local = 0;
-      for (int i = 0; i < 2; ++i) local += W.coarse[t * 2 + i];
-      uint32_t total;
-      const uint32_t before = block_excl_scan<PF_RES_T>(local, tmp, &total);
-      if (before < st.need && st.need <= before + local) {
-        uint32_t cum = before;
-        for (int i = 0; i < 2; ++i) {
-          const int cb = t * 2 + i;
-          const uint32_t cnt = W.coarse[cb];
-          if (cum < st.need && st.need <= cum + cnt) {
-            for (int f = cb * 32; f < cb * 32 + 32; ++f) {
-              const uint32_t cf = W.fine[f];
-              if (cum < st.need && st.need <= cum + cf) { tmp[40] = f; tmp[41] = cum; break; }
-              cum += cf;
-            }
-            break;
-          }
-          cum += cnt;
-        }
-      }
-      __syncthreads();
-      fb = tmp[40];
-      below = tmp[41];
-      __syncthreads();
-    }
-    (void)fb;
-    uint32_t k_rem = st.need - below;          // slots of the threshold bin that go
+    uint32_t k_rem = st.need - st.below;          // slots of the threshold bin that go
     const bool in_lds = n_c <= PF_CAP;
     if (in_lds) {
       for (uint32_t i = t; i < n_c; i += PF_RES_T) {
@@ -514,10 +503,12 @@ __global__ __launch_bounds__(PF_RES_T) void pool_evict2_kernel(
   }
 }
 
-int launch_pool_stats(const echo_pool *pool, const PoolFastWs &W, int32_t step_id, hipStream_t st) {
+int launch_pool_stats(const echo_pool *pool, const PoolFastWs &W, int32_t step_id, bool excl_prot,
+                      hipStream_t st) {
   PoolArgs P{pool->gpu_free, pool->gpu_priority, pool->gpu_to_host, pool->host_to_gpu,
              pool->indices_buf, pool->status, pool->n_gpu, pool->n_host};
-  pool_stats_kernel<<<W.n_chunks, PF_T, 0, st>>>(P, W, step_id);
+  if (excl_prot) pool_stats_kernel<true><<<W.n_chunks, PF_T, 0, st>>>(P, W, step_id);
+  else pool_stats_kernel<false><<<W.n_chunks, PF_T, 0, st>>>(P, W, step_id);
   return check_launch("pool_stats");
 }
 
@@ -535,15 +526,20 @@ int launch_pool_lookup_rows(const echo_pool *pool, const PoolFastWs &W, const in
 
 int launch_pool_evict(const echo_pool *pool, const PoolFastWs &W, const int32_t *idx, int32_t n_rows,
                       int32_t k, int32_t step_id, int32_t *topk_slot, int32_t *miss_host,
-                      int32_t *miss_slot, int32_t *n_miss, hipStream_t st) {
+                      int32_t *miss_slot, int32_t *n_miss, uint16_t *stage, hipStream_t st) {
   if (W.n_chunks > 1024) return fail(ECHO_EUNSUPPORTED, "pool: more than 4M slots");
   PoolArgs P{pool->gpu_free, pool->gpu_priority, pool->gpu_to_host, pool->host_to_gpu,
              pool->indices_buf, pool->status, pool->n_gpu, pool->n_host};
-  pool_evict1_kernel<<<n_rows + W.n_chunks, PF_T, 0, st>>>(P, W, n_rows, k, step_id, miss_host);
+  // with a staging area, the first half of the requests' missed rows are read from host memory
+  // during evict-1 and the rest during evict-2
+  StageArgs SA{pool->host_kv, stage, stage ? (n_rows + 1) / 2 : 0};
+  const int s1 = stage ? SA.rows_a * ((k + 31) / 32) : 0;
+  const int s2 = stage ? (n_rows - SA.rows_a) * ((k + 127) / 128) : 0;
+  pool_evict1_kernel<<<n_rows + W.n_chunks + s1, PF_T, 0, st>>>(P, W, n_rows, k, step_id, miss_host, SA);
   const int64_t n_ent = static_cast<int64_t>(n_rows) * k;
   const int entry_blocks = static_cast<int>(std::max<int64_t>(1, (n_ent + PF_RES_T - 1) / PF_RES_T));
-  pool_evict2_kernel<<<W.n_chunks + entry_blocks, PF_RES_T, 0, st>>>(P, W, n_rows, k, step_id, miss_host,
-                                                                      miss_slot, topk_slot, n_miss, idx);
+  pool_evict2_kernel<<<W.n_chunks + entry_blocks + s2, PF_RES_T, 0, st>>>(
+      P, W, n_rows, k, step_id, miss_host, miss_slot, topk_slot, n_miss, idx, entry_blocks, SA);
   return check_launch("pool_evict");
 }
 
@@ -572,11 +568,12 @@ int launch_pool_step(const echo_pool *pool, const int32_t *idx, const int64_t *k
   if (ws_bytes < need) return fail(ECHO_EWORKSPACE, "echo_pool_lookup_alloc: workspace %zu < %zu", ws_bytes, need);
   int rc;
   if ((rc = launch_zero_i32(W.counters, W.zero_words, st))) return rc;
-  if ((rc = launch_pool_stats(pool, W, step_id, st))) return rc;
   if ((rc = launch_pool_lookup_rows(pool, W, idx, key_begin, req_to_host, n_k, n_rows, k, step_id,
                                     topk_slot, st)))
     return rc;
-  return launch_pool_evict(pool, W, idx, n_rows, k, step_id, topk_slot, miss_host, miss_slot, n_miss, st);
+  if ((rc = launch_pool_stats(pool, W, step_id, true, st))) return rc;
+  return launch_pool_evict(pool, W, idx, n_rows, k, step_id, topk_slot, miss_host, miss_slot, n_miss,
+                           nullptr, st);
 }
 
 }  // namespace echo

@@ -115,69 +115,22 @@ int launch_prefetch_begin(const echo_pool *pool, int32_t *free_list, int32_t *fr
   return check_launch("prefetch_begin");
 }
 
-// ------------------------------------------------------------------ side-stream gather
-constexpr int PG_THREADS = 256;
-constexpr int PG_UNITS = ROW * 2 / 16;   // 72 x 16 B per row
-typedef int v4i __attribute__((ext_vector_type(4)));
+// ------------------------------------------------------------------ prefetch gather
+__global__ __launch_bounds__(PG_THREADS) void prefetch_gather_kernel(GatherArgs G) {
+  __shared__ uint32_t lds[PG_LDS_WORDS];
+  gather_request(G, blockIdx.x, lds);
+}
 
-__global__ __launch_bounds__(PG_THREADS) void prefetch_gather_kernel(
-    const uint16_t *__restrict__ host_kv, uint16_t *__restrict__ gpu_kv, uint8_t *free_,
-    int32_t *priority, int32_t *to_host, int32_t *host_to_gpu, const int32_t *status,
-    int32_t n_gpu, int32_t n_host, const int64_t *__restrict__ key_begin,
-    const int32_t *__restrict__ req_to_host, const int32_t *__restrict__ cand,
-    const int32_t *__restrict__ cand_cnt, int32_t cap, const int32_t *__restrict__ free_list,
-    int32_t *free_count, int32_t *n_prefetched, int32_t *st_free, uint32_t *st_fine,
-    uint32_t *st_coarse, int32_t step_id) {
-  __shared__ int32_t s_base, s_n;
-  __shared__ int32_t s_host[128], s_slot[128];
-  const int r = blockIdx.x;
-  if (*(volatile const int32_t *)status) return;
-  const int32_t cnt = min(cand_cnt[r], cap);
-  if (cnt <= 0) return;
-  if (threadIdx.x == 0) {
-    const int32_t avail = free_count[0];
-    const int32_t b = atomicAdd(&free_count[1], cnt);
-    s_base = b;
-    s_n = max(0, min(cnt, avail - b));
-    if (s_n > 0) atomicAdd(n_prefetched, s_n);
-  }
-  __syncthreads();
-  const int32_t n = s_n, base = s_base;
-  const int64_t kb = key_begin[r];
-  const v4i *src = reinterpret_cast<const v4i *>(host_kv);
-  v4i *dst = reinterpret_cast<v4i *>(gpu_kv);
-  for (int32_t c0 = 0; c0 < n; c0 += 128) {
-    const int m = min(128, n - c0);
-    for (int t = threadIdx.x; t < m; t += PG_THREADS) {
-      const int32_t tok = cand[static_cast<int64_t>(r) * cap + c0 + t];
-      const int32_t h = req_to_host[kb + tok];
-      const int32_t slot = free_list[base + c0 + t];
-      int32_t ok_h = -1;
-      if (h >= 0 && h < n_host && slot >= 0 && slot < n_gpu && host_to_gpu[h] == INF) {
-        free_[slot] = 0;
-        to_host[slot] = h;
-        host_to_gpu[h] = slot;
-        priority[slot] = 0;
-        ok_h = h;
-        if (st_free) {                      // keep the pool-step statistics current
-          atomicSub(st_free, 1);
-          const uint32_t b = prio_bin(0, step_id);
-          atomicAdd(&st_fine[b], 1u);
-          atomicAdd(&st_coarse[b >> 5], 1u);
-        }
-      }
-      s_host[t] = ok_h;
-      s_slot[t] = slot;
-    }
-    __syncthreads();
-    for (int u = threadIdx.x; u < m * PG_UNITS; u += PG_THREADS) {
-      const int t = u / PG_UNITS, part = u % PG_UNITS;
-      if (s_host[t] >= 0)
-        dst[static_cast<int64_t>(s_slot[t]) * PG_UNITS + part] =
-            __builtin_nontemporal_load(src + static_cast<int64_t>(s_host[t]) * PG_UNITS + part);
-    }
-    __syncthreads();
-  }
+GatherArgs make_gather_args(const echo_pool *pool, const int64_t *key_begin,
+                            const int32_t *req_to_host, const int32_t *cand,
+                            const int32_t *cand_cnt, int32_t cap, const int32_t *free_list,
+                            int32_t *free_count, int32_t *n_prefetched, const PoolFastWs *pw,
+                            int32_t step_id) {
+  return GatherArgs{pool->host_kv, pool->gpu_kv, pool->gpu_free, pool->gpu_priority,
+                    pool->gpu_to_host, pool->host_to_gpu, pool->status, pool->n_gpu, pool->n_host,
+                    key_begin, req_to_host, cand, cand_cnt, cap, free_list, free_count,
+                    n_prefetched, pw ? pw->counters : nullptr, pw ? pw->fine : nullptr,
+                    pw ? pw->coarse : nullptr, step_id};
 }
 
 int launch_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
@@ -186,11 +139,8 @@ int launch_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
                            const int32_t *free_list, int32_t *free_count, int32_t *n_prefetched,
                            const PoolFastWs *pw, int32_t step_id, hipStream_t st) {
   if (n_q == 0 || cap == 0) return ECHO_OK;
-  prefetch_gather_kernel<<<n_q, PG_THREADS, 0, st>>>(
-      pool->host_kv, pool->gpu_kv, pool->gpu_free, pool->gpu_priority, pool->gpu_to_host,
-      pool->host_to_gpu, pool->status, pool->n_gpu, pool->n_host, key_begin, req_to_host, cand,
-      cand_cnt, cap, free_list, free_count, n_prefetched, pw ? pw->counters : nullptr,
-      pw ? pw->fine : nullptr, pw ? pw->coarse : nullptr, step_id);
+  prefetch_gather_kernel<<<n_q, PG_THREADS, 0, st>>>(make_gather_args(
+      pool, key_begin, req_to_host, cand, cand_cnt, cap, free_list, free_count, n_prefetched, pw, step_id));
   return check_launch("prefetch_gather");
 }
 

@@ -13,10 +13,16 @@
 // for the whole kernel, B = k of 16 tokens read from LDS; four MFMAs cover the 64 heads and
 // the ReLU * w head reduction is 16 FMAs per lane plus a two-step cross-lane sum.
 //
-// Prefetch candidates: each call appends to its own list (cand, cand_cnt), so a consumer on
-// another stream that waits for this kernel sees a complete list; the per-request cap is a
-// counter shared by all calls of one step (total_cnt).
+// Prefetch candidates: each call appends to its own list (cand, cand_cnt), so a later kernel
+// sees a complete list; the per-request cap is a counter shared by all calls of one step
+// (total_cnt).
+//
+// Side work (SIDE): the launch may carry extra leading workgroups that do independent pool
+// work (priority statistics, a previous range's prefetch gather) while the scoring workgroups
+// stream keys; the grid is one-dimensional and block b >= n_side scores (token block
+// (b - n_side) % gx of request (b - n_side) / gx).
 #include "internal.hpp"
+#include "pool_common.cuh"
 #include "score_tile.cuh"
 
 namespace echo {
@@ -28,25 +34,35 @@ constexpr int SD_LOADS = SD_UNITS / SD_THREADS;                  // per thread p
 
 ECHO_DEV int swz(int tok, int seg) { return tok * 128 + ((seg ^ ((tok >> 1) & 7)) << 4); }
 
-template <bool HAS_SCALE, bool PREFETCH, bool HIST>
+constexpr int SD_SCORE_WORDS = 2 * SD_CHUNK * D / 4;               // the LDS double buffer
+
+template <bool HAS_SCALE, bool PREFETCH, bool HIST, bool SIDE>
 __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
     const uint8_t *__restrict__ q, const float *__restrict__ w, const uint8_t *__restrict__ k,
     const float *__restrict__ k_scale, const int64_t *__restrict__ key_begin,
     const int32_t *__restrict__ key_len, int32_t max_len, int32_t tok_lo, int32_t tok_hi,
-    int32_t tokens_per_wg, float *__restrict__ scores, int64_t ld, PrefetchArgs pf,
-    uint32_t *__restrict__ hist0) {
-  const int r = blockIdx.y;
+    int32_t tokens_per_wg, int32_t gx, float *__restrict__ scores, int64_t ld, PrefetchArgs pf,
+    uint32_t *__restrict__ hist0, SideWork side) {
+  constexpr int WORDS = SD_SCORE_WORDS + (HIST ? 2048 : 0);
+  constexpr int ALL = SIDE && SIDE_LDS_WORDS > WORDS ? SIDE_LDS_WORDS : WORDS;
+  __shared__ __attribute__((aligned(16))) uint32_t smem[ALL];
+  int b = blockIdx.x;
+  if constexpr (SIDE) {
+    if (side_work(side, b, smem)) return;
+    b -= side.n_stats + side.n_gather;
+  }
+  const int r = b / gx;
   const int32_t L = min(max(key_len[r], 0), max_len);
   const int32_t hi = min(L, tok_hi);
-  const int32_t t_begin = tok_lo + static_cast<int32_t>(blockIdx.x) * tokens_per_wg;
+  const int32_t t_begin = tok_lo + (b % gx) * tokens_per_wg;
   if (t_begin >= hi) return;
   const int32_t t_end = min(hi, t_begin + tokens_per_wg);
   const int64_t kb = key_begin[r];
   const uint8_t *__restrict__ kr = k + kb * D;
   float *__restrict__ srow = scores + static_cast<int64_t>(r) * ld;
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][SD_CHUNK * D];
-  __shared__ uint32_t hl[HIST ? 2048 : 1];
+  uint8_t (*lds)[SD_CHUNK * D] = reinterpret_cast<uint8_t (*)[SD_CHUNK * D]>(smem);
+  uint32_t *hl = smem + SD_SCORE_WORDS;
 
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
   const int j = l & 15, g = l >> 4;
@@ -137,26 +153,41 @@ static int32_t pick_tokens_per_wg(int64_t total_tokens, int32_t max_len) {
 int launch_score_decode(const uint8_t *q, const float *w, const uint8_t *k, const float *k_scale,
                         const int64_t *key_begin, const int32_t *key_len, int32_t n_q,
                         int32_t max_len, int32_t tok_lo, int32_t tok_hi, float *scores,
-                        int64_t ld, const PrefetchArgs *pf, uint32_t *hist0, hipStream_t st) {
+                        int64_t ld, const PrefetchArgs *pf, uint32_t *hist0, const SideWork *side,
+                        hipStream_t st) {
   tok_hi = tok_hi < max_len ? tok_hi : max_len;
-  if (n_q == 0 || tok_hi <= tok_lo) return ECHO_OK;
-  const int32_t tpw = pick_tokens_per_wg(static_cast<int64_t>(n_q) * (tok_hi - tok_lo), tok_hi - tok_lo);
-  dim3 grid((tok_hi - tok_lo + tpw - 1) / tpw, n_q);
+  const int n_side = side ? side->n_stats + side->n_gather : 0;
+  const bool scoring = n_q > 0 && tok_hi > tok_lo;
+  if (!scoring && n_side == 0) return ECHO_OK;
+  const int32_t span = scoring ? tok_hi - tok_lo : 1;
+  const int32_t tpw = pick_tokens_per_wg(static_cast<int64_t>(n_q) * span, span);
+  const int32_t gx = (span + tpw - 1) / tpw;
+  const int64_t blocks = static_cast<int64_t>(n_side) + (scoring ? static_cast<int64_t>(gx) * n_q : 0);
+  if (blocks > 0x7FFFFFFF) return fail(ECHO_EUNSUPPORTED, "score_decode: grid too large");
   PrefetchArgs none{};
   const PrefetchArgs &p = pf ? *pf : none;
-#define ECHO_SD(SC, PF, HI)                                                                     \
-  score_decode_kernel<SC, PF, HI><<<grid, SD_THREADS, 0, st>>>(q, w, k, k_scale, key_begin,       \
-                                                               key_len, max_len, tok_lo, tok_hi,  \
-                                                               tpw, scores, ld, p, hist0)
-  const bool sc = k_scale != nullptr, pfo = pf != nullptr, hi = hist0 != nullptr;
-  if (sc && pfo && hi) ECHO_SD(true, true, true);
-  else if (sc && pfo) ECHO_SD(true, true, false);
-  else if (sc && hi) ECHO_SD(true, false, true);
-  else if (sc) ECHO_SD(true, false, false);
-  else if (pfo && hi) ECHO_SD(false, true, true);
-  else if (pfo) ECHO_SD(false, true, false);
-  else if (hi) ECHO_SD(false, false, true);
-  else ECHO_SD(false, false, false);
+  SideWork no_side{};
+  const SideWork &sw = side ? *side : no_side;
+#define ECHO_SD(SC, PF, HI, SI)                                                                 \
+  score_decode_kernel<SC, PF, HI, SI><<<static_cast<unsigned>(blocks), SD_THREADS, 0, st>>>(     \
+      q, w, k, k_scale, key_begin, key_len, max_len, tok_lo, scoring ? tok_hi : tok_lo, tpw, gx,  \
+      scores, ld, p, hist0, sw)
+  const bool sc = k_scale != nullptr, pfo = pf != nullptr, hi = hist0 != nullptr, si = n_side > 0;
+  if (si) {
+    // side work rides only with the decode step's scoring (histogram on)
+    if (!hi) return fail(ECHO_EINVAL, "score_decode: side work needs the top-k histogram");
+    if (sc && pfo) ECHO_SD(true, true, true, true);
+    else if (sc) ECHO_SD(true, false, true, true);
+    else if (pfo) ECHO_SD(false, true, true, true);
+    else ECHO_SD(false, false, true, true);
+  } else if (sc && pfo && hi) ECHO_SD(true, true, true, false);
+  else if (sc && pfo) ECHO_SD(true, true, false, false);
+  else if (sc && hi) ECHO_SD(true, false, true, false);
+  else if (sc) ECHO_SD(true, false, false, false);
+  else if (pfo && hi) ECHO_SD(false, true, true, false);
+  else if (pfo) ECHO_SD(false, true, false, false);
+  else if (hi) ECHO_SD(false, false, true, false);
+  else ECHO_SD(false, false, false, false);
 #undef ECHO_SD
   return check_launch("score_decode");
 }
@@ -175,7 +206,7 @@ extern "C" int echo_index_scores(const uint8_t *q, const float *w, const uint8_t
   if (n_q > 0 && (!q || !w || !key_begin || !key_len || !scores || (max_key_len > 0 && !k)))
     return fail(ECHO_EINVAL, "echo_index_scores: NULL pointer");
   return launch_score_decode(q, w, k, k_scale, key_begin, key_len, n_q, max_key_len, 0,
-                             max_key_len, scores, ld, nullptr, nullptr, S(stream));
+                             max_key_len, scores, ld, nullptr, nullptr, nullptr, S(stream));
 }
 
 extern "C" int echo_index_scores_prefetch(const uint8_t *q, const float *w, const uint8_t *k,
@@ -196,5 +227,5 @@ extern "C" int echo_index_scores_prefetch(const uint8_t *q, const float *w, cons
     return fail(ECHO_EINVAL, "echo_index_scores_prefetch: NULL pointer");
   PrefetchArgs pf{theta, req_to_host, host_to_gpu, cand, cand_cnt, total_cnt, cap, cap_div};
   return launch_score_decode(q, w, k, k_scale, key_begin, key_len, n_q, max_key_len, tok_lo,
-                             tok_hi, scores, ld, &pf, nullptr, S(stream));
+                             tok_hi, scores, ld, &pf, nullptr, nullptr, S(stream));
 }

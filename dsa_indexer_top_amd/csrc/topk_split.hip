@@ -47,27 +47,30 @@ ECHO_DEV void row_load4(const float *row, bool vec, int32_t n, int32_t i0, uint3
   }
 }
 
-// Bin of the m-th smallest key in a 2048-bin histogram and the count below it.  NT threads.
+// Bin of the m-th smallest key in a 2048-bin histogram, the count below it and the bin's own
+// count.  NT threads.
 template <int NT>
-ECHO_DEV void pick2048(const uint32_t *hist, uint32_t m, uint32_t *tmp, uint32_t &bin, uint32_t &below) {
+ECHO_DEV void pick2048(const uint32_t *hist, uint32_t m, uint32_t *tmp, uint32_t &bin, uint32_t &below,
+                       uint32_t &count) {
   constexpr int PER = 2048 / NT;
   const int t = threadIdx.x;
-  uint32_t local = 0;
+  uint32_t v[PER], local = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) local += hist[t * PER + i];
+  for (int i = 0; i < PER; ++i) { v[i] = hist[t * PER + i]; local += v[i]; }
   uint32_t total;
   const uint32_t before = block_excl_scan<NT>(local, tmp, &total);
   if (before < m && m <= before + local) {
     uint32_t cum = before;
+#pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const uint32_t c = hist[t * PER + i];
-      if (cum < m && m <= cum + c) { tmp[40] = t * PER + i; tmp[41] = cum; break; }
-      cum += c;
+      if (cum < m && m <= cum + v[i]) { tmp[40] = t * PER + i; tmp[41] = cum; tmp[42] = v[i]; break; }
+      cum += v[i];
     }
   }
   __syncthreads();
   bin = tmp[40];
   below = tmp[41];
+  count = tmp[42];
   __syncthreads();
 }
 
@@ -124,19 +127,27 @@ static SplitWs make_split_ws(void *base, int32_t n_rows, int32_t max_len, int32_
 }
 
 // ---------------------------------------------------------------- split
+// SIDE: leading workgroups of the launch run side work (a prefetch gather) instead.
+template <bool SIDE>
 __global__ __launch_bounds__(TS_T) void topk_split_kernel(const float *__restrict__ scores, int64_t ld,
                                                           const int32_t *__restrict__ len, int32_t max_len,
                                                           int32_t k, const uint32_t *__restrict__ hist0,
-                                                          SplitWs W) {
+                                                          SplitWs W, SideWork side) {
   __shared__ uint32_t tmp[48];
   __shared__ uint32_t gscan[4 * (TS_T / 64) + TS_T / 64 + 2];
-  const int r = blockIdx.y, c = blockIdx.x, t = threadIdx.x;
+  __shared__ uint32_t side_lds[SIDE ? SIDE_LDS_WORDS : 1];
+  int b = blockIdx.x;
+  if constexpr (SIDE) {
+    if (side_work(side, b, side_lds)) return;
+    b -= side.n_stats + side.n_gather;
+  }
+  const int r = b / W.nch, c = b % W.nch, t = threadIdx.x;
   const int32_t n = min(max(len[r], 0), max_len);
   const int32_t m = min(k, n);
   if (m == n || c * TS_CH >= n) return;
-  uint32_t b0, below0;
-  pick2048<TS_T>(hist0 + static_cast<int64_t>(r) * 2048, static_cast<uint32_t>(m), tmp, b0, below0);
-  const bool keep_cand = hist0[static_cast<int64_t>(r) * 2048 + b0] <= TF_CAP;
+  uint32_t b0, below0, c0;
+  pick2048<TS_T>(hist0 + static_cast<int64_t>(r) * 2048, static_cast<uint32_t>(m), tmp, b0, below0, c0);
+  const bool keep_cand = c0 <= TF_CAP;
   const float *row = scores + static_cast<int64_t>(r) * ld;
   const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
   uint32_t key[4][4];
@@ -187,11 +198,13 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
     int32_t k, const uint32_t *__restrict__ hist0, SplitWs W, int32_t *__restrict__ idx,
     // lookup (skipped when pool.n_gpu == 0)
     PoolArgs P, PoolFastWs PW, const int64_t *__restrict__ key_begin,
-    const int32_t *__restrict__ req_to_host, int32_t step_id, int32_t *__restrict__ topk_slot) {
+    const int32_t *__restrict__ req_to_host, int32_t step_id, int32_t *__restrict__ topk_slot,
+    bool sub_prot) {
   __shared__ uint32_t tmp[48];
   __shared__ uint32_t hist[2048];
-  __shared__ uint32_t ckey[TF_CAP];
-  __shared__ int32_t cidx[TF_CAP];
+  __shared__ uint32_t cbuf[2 * TF_CAP];               // candidates; later the lookup's histogram
+  uint32_t *ckey = cbuf;
+  int32_t *cidx = reinterpret_cast<int32_t *>(cbuf + TF_CAP);
   __shared__ int32_t sure[ECHO_MAX_TOPK];
   __shared__ int32_t sel[ECHO_MAX_TOPK];
   __shared__ int32_t fin[ECHO_MAX_TOPK];
@@ -205,17 +218,16 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
   if (m == n) {
     for (int j = t; j < m; j += TF_T) fin[j] = j;
   } else {
-    uint32_t b0, below0;
-    pick2048<TF_T>(hist0 + static_cast<int64_t>(r) * 2048, static_cast<uint32_t>(m), tmp, b0, below0);
-    uint32_t k_rem = static_cast<uint32_t>(m) - below0;
-    const uint32_t c0 = hist0[static_cast<int64_t>(r) * 2048 + b0];
-    uint32_t prefix = b0 << 21, mask = 0xFFE00000u;
     const int nch_r = (n + TS_CH - 1) / TS_CH;          // chunks of this request (<= 1024)
     const int64_t seg0 = static_cast<int64_t>(r) * W.nch;
-    // segment offsets (exclusive prefix over the request's chunks)
+    const uint32_t sc = t < nch_r ? W.sure_cnt[seg0 + t] : 0u;   // loaded with the histogram
+    const uint32_t cc = t < nch_r ? W.cand_cnt[seg0 + t] : 0u;
+    uint32_t b0, below0, c0;
+    pick2048<TF_T>(hist0 + static_cast<int64_t>(r) * 2048, static_cast<uint32_t>(m), tmp, b0, below0, c0);
+    uint32_t k_rem = static_cast<uint32_t>(m) - below0;
+    uint32_t prefix = b0 << 21, mask = 0xFFE00000u;
+    // segment offsets: exclusive prefixes over the request's chunks
     {
-      const uint32_t sc = t < nch_r ? W.sure_cnt[seg0 + t] : 0u;
-      const uint32_t cc = t < nch_r ? W.cand_cnt[seg0 + t] : 0u;
       uint32_t tot;
       const uint32_t so = block_excl_scan<TF_T>(sc, tmp, &tot);
       const uint32_t co = block_excl_scan<TF_T>(cc, tmp, &tot);
@@ -261,23 +273,30 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
         prefix |= b << sh;
         mask |= dm << sh;
       }
-      // candidates in index order: keys < K*, then the first k_rem ties
-      uint32_t n_sel = 0, eq_seen = 0;
-      for (uint32_t i0 = 0; i0 < n_cand; i0 += TF_T) {
-        const uint32_t i = i0 + t;
-        const bool in = i < n_cand;
-        const uint32_t kk = in ? ckey[i] : ~0u;
-        uint32_t tot;
-        const uint32_t er = eq_seen + block_excl_scan<TF_T>(in && kk == prefix, tmp, &tot);
-        const bool take = in && (kk < prefix || (kk == prefix && er < k_rem));
-        uint32_t tot2;
-        const uint32_t pos = n_sel + block_excl_scan<TF_T>(take, tmp, &tot2);
-        if (take && pos < ECHO_MAX_TOPK) sel[pos] = cidx[i];
-        n_sel += tot2;
-        eq_seen += tot;
+      // candidates in index order: every key < K*, then the first k_rem keys == K*.  One scan
+      // of the (less, equal) counts packed 16|16 (n_cand <= TF_CAP < 2^16) places them all:
+      // a taken candidate goes to (less before) + min(equal before, k_rem).
+      constexpr int SJ = TF_CAP / TF_T;
+      uint32_t cnt[SJ], cbase[SJ], ctot;
+#pragma unroll
+      for (int j = 0; j < SJ; ++j) {
+        const uint32_t i = j * TF_T + t;
+        const uint32_t kk = i < n_cand ? ckey[i] : ~0u;
+        cnt[j] = i < n_cand ? ((kk < prefix ? 1u : 0u) | (kk == prefix ? 0x10000u : 0u)) : 0u;
+      }
+      group_excl_scan<TF_T, SJ>(cnt, cbase, gscan, &ctot);
+#pragma unroll
+      for (int j = 0; j < SJ; ++j) {
+        const uint32_t i = j * TF_T + t;
+        const uint32_t lt_b = cbase[j] & 0xFFFFu, eq_b = cbase[j] >> 16;
+        const bool take = (cnt[j] & 0xFFFFu) || ((cnt[j] >> 16) && eq_b < k_rem);
+        if (take) {
+          const uint32_t pos = lt_b + min(eq_b, k_rem);
+          if (pos < ECHO_MAX_TOPK) sel[pos] = cidx[i];
+        }
       }
       __syncthreads();
-      n_sel = min(n_sel, static_cast<uint32_t>(ECHO_MAX_TOPK));
+      const uint32_t n_sel = min((ctot & 0xFFFFu) + min(ctot >> 16, k_rem), static_cast<uint32_t>(ECHO_MAX_TOPK));
       for (uint32_t a = t; a < n_sure; a += TF_T) {
         const int32_t v = sure[a];
         uint32_t lo = 0, hi = n_sel;
@@ -371,6 +390,7 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
   const int64_t kb = key_begin[r];
   constexpr int LJ = ECHO_MAX_TOPK / TF_T;          // entries per thread: j = t + TF_T * i
   int32_t h[LJ], slot[LJ], res[LJ];
+  bool hit[LJ];
 #pragma unroll
   for (int i = 0; i < LJ; ++i) {
     const int32_t j = t + TF_T * i;
@@ -381,37 +401,68 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
     const int32_t j = t + TF_T * i;
     slot[i] = (j < m && h[i] >= 0 && h[i] < P.n_host) ? P.host_to_gpu[h[i]] : -1;
   }
+  bool bad = false;
 #pragma unroll
   for (int i = 0; i < LJ; ++i) {
     const int32_t j = t + TF_T * i;
-    res[i] = j < m ? lookup_entry(P, PW, h[i], slot[i], step_id) : -1;
+    hit[i] = false;
+    res[i] = -1;
+    if (j < m) {
+      if (h[i] < 0 || h[i] >= P.n_host) bad = true;
+      else if (slot[i] == INF) res[i] = INF;
+      else if (slot[i] < 0 || slot[i] >= P.n_gpu) bad = true;
+      else { hit[i] = true; res[i] = slot[i]; }
+    }
   }
-  uint32_t n_miss = 0;
+  if (bad) atomicOr(P.status, ECHO_ST_BAD_HOST);
+  if (sub_prot) {
+    // protected slots leave the occupied-slot histogram: the first protector of each slot
+    // subtracts its priority bin (priorities do not change before the eviction kernels)
+    int32_t pr[LJ];
+    uint32_t old[LJ], pbin[LJ];
+#pragma unroll
+    for (int i = 0; i < LJ; ++i) pr[i] = hit[i] ? P.priority[slot[i]] : 0;
+#pragma unroll
+    for (int i = 0; i < LJ; ++i)
+      old[i] = hit[i] ? atomicOr(&PW.prot[slot[i] >> 5], 1u << (slot[i] & 31)) : ~0u;
+#pragma unroll
+    for (int i = 0; i < LJ; ++i)
+      pbin[i] = (hit[i] && !((old[i] >> (slot[i] & 31)) & 1u)) ? prio_bin(pr[i], step_id) : 0xFFFFFFFFu;
+    hist_flush_bins<TF_T, LJ, true, 2 * TF_CAP>(pbin, cbuf, tmp, PW.fine, PW.coarse);
+  } else {
+#pragma unroll
+    for (int i = 0; i < LJ; ++i)
+      if (hit[i]) atomicOr(&PW.prot[slot[i] >> 5], 1u << (slot[i] & 31));
+  }
+  uint32_t mc[LJ], mo[LJ], n_miss;
+#pragma unroll
+  for (int i = 0; i < LJ; ++i) mc[i] = res[i] == INF ? 1u : 0u;
+  group_excl_scan<TF_T, LJ>(mc, mo, gscan, &n_miss);
 #pragma unroll
   for (int i = 0; i < LJ; ++i) {
     const int32_t j = t + TF_T * i;
-    if (TF_T * i >= k) break;                       // uniform
-    const bool miss = res[i] == INF;
-    uint32_t tot;
-    const uint32_t pos = n_miss + block_excl_scan<TF_T>(miss ? 1u : 0u, tmp, &tot);
-    if (miss) {
-      PW.row_miss_h[static_cast<int64_t>(r) * k + pos] = h[i];
-      PW.row_miss_j[static_cast<int64_t>(r) * k + pos] = j;
+    if (mc[i]) {
+      PW.row_miss_h[static_cast<int64_t>(r) * k + mo[i]] = h[i];
+      PW.row_miss_j[static_cast<int64_t>(r) * k + mo[i]] = j;
     }
     if (j < k) slot_out[j] = (res[i] >= 0 && res[i] != INF) ? res[i] : -1;
-    n_miss += tot;
   }
   if (t == 0) PW.row_miss_cnt[r] = n_miss;
 }
 
 int launch_topk_split(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
                       int32_t max_len, int32_t k, const uint32_t *hist0, void *split_ws,
-                      hipStream_t st) {
-  if (n_rows == 0) return ECHO_OK;
+                      const SideWork *side, hipStream_t st) {
+  const int n_side = side ? side->n_stats + side->n_gather : 0;
+  if (n_rows == 0 && n_side == 0) return ECHO_OK;
   if ((max_len + TS_CH - 1) / TS_CH > 1024) return fail(ECHO_EUNSUPPORTED, "decode top-k: rows longer than 4M tokens");
   SplitWs W = make_split_ws(split_ws, n_rows, max_len, k);
-  dim3 g(W.nch, n_rows);
-  topk_split_kernel<<<g, TS_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W);
+  const int64_t blocks = static_cast<int64_t>(n_side) + static_cast<int64_t>(W.nch) * n_rows;
+  if (blocks > 0x7FFFFFFF) return fail(ECHO_EUNSUPPORTED, "decode top-k: grid too large");
+  if (n_side > 0)
+    topk_split_kernel<true><<<static_cast<unsigned>(blocks), TS_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W, *side);
+  else
+    topk_split_kernel<false><<<static_cast<unsigned>(blocks), TS_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W, SideWork{});
   return check_launch("topk_split");
 }
 
@@ -419,7 +470,7 @@ int launch_topk_finish(const float *scores, int64_t ld, const int32_t *len, int3
                        int32_t max_len, int32_t k, const uint32_t *hist0, void *split_ws,
                        int32_t *idx, const echo_pool *pool, const PoolFastWs *pw,
                        const int64_t *key_begin, const int32_t *req_to_host, int32_t step_id,
-                       int32_t *topk_slot, hipStream_t st) {
+                       int32_t *topk_slot, bool sub_prot, hipStream_t st) {
   if (n_rows == 0) return ECHO_OK;
   SplitWs W = make_split_ws(split_ws, n_rows, max_len, k);
   PoolArgs P{};
@@ -430,7 +481,8 @@ int launch_topk_finish(const float *scores, int64_t ld, const int32_t *len, int3
     PW = *pw;
   }
   topk_finish_kernel<<<n_rows, TF_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W, idx, P, PW,
-                                              key_begin, req_to_host, step_id, topk_slot);
+                                              key_begin, req_to_host, step_id, topk_slot,
+                                              sub_prot && pool != nullptr);
   return check_launch("topk_finish");
 }
 

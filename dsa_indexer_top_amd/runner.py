@@ -72,7 +72,7 @@ class DecodeRunner:
         nbytes = B.decode_workspace_bytes(self.args, self.n_gpu)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
         self.main = torch.cuda.Stream()
-        self.side = torch.cuda.Stream()      # pool statistics (and prefetch) overlap scoring
+        self.side = torch.cuda.Stream()      # prefetch gathers overlap scoring
         self.graph = None
 
     def restore(self):

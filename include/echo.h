@@ -239,10 +239,14 @@ int echo_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
                          void *stream);
 
 /*
- * The whole decode step (§4): scores -> [threshold prefetch overlapped on `side`] -> exact
- * top-k -> lookup/evict/allocate -> recall gather -> priorities.  Pure enqueue on `main`
- * (and `side` when prefetch is on; side may equal main), so the call can be captured into one
- * hipGraph (echo_graph_capture_decode).
+ * The whole decode step (§4): scores -> [threshold prefetch] -> exact top-k -> lookup /
+ * evict / allocate -> recall -> priorities.  Pure enqueue on `main_stream`, so the call can be
+ * captured into one hipGraph (echo_graph_capture_decode).  Work that overlaps the critical
+ * path (the pool's priority histogram, prefetch gathers, reading missed rows from host memory
+ * into a staging area of the workspace) rides along as extra workgroups of the same launches.
+ * `side_stream` is reserved and ignored (pass NULL or main_stream).  Workspace:
+ * echo_decode_workspace_bytes(a, pool->n_gpu) bytes (it includes n_rows * topk staged rows of
+ * ECHO_ROW_ELEMS bf16 values).
  */
 typedef struct {
   const uint8_t *q;          /* [n_rows, 64, 128] FP8 */
@@ -282,7 +286,7 @@ int echo_decode_select(const echo_decode_args *a, const echo_pool *pool,
                        void *side_stream);
 
 /* Graph helpers (host side; they create HIP objects).  Capture one echo_decode_select into a
- * hipGraph on `main_stream` (and `side_stream`), instantiate it, and replay it.  The graph
+ * hipGraph on `main_stream`, instantiate it, and replay it.  The graph
  * reads and writes the buffers that were passed at capture time. */
 typedef struct echo_graph_s *echo_graph;
 int echo_graph_capture_decode(const echo_decode_args *a, const echo_pool *pool,
