@@ -43,6 +43,26 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(root, summary="profiles/score_decode_b8_64k_hbm_traffic.md"):
+    """HBM bytes per scoring launch from the committed hardware-counter summary, or None when
+    the summary is missing or the kernel sources changed since the counters were taken."""
+    import hashlib
+    try:
+        fields = {}
+        for line in open(os.path.join(root, summary)):
+            if ":" in line:
+                key, _, val = line.strip().partition(":")
+                fields[key.strip()] = val.strip()
+        h = hashlib.sha256()
+        for f in fields["kernel_sources"].split():
+            h.update(open(os.path.join(root, f), "rb").read())
+        if h.hexdigest()[:16] != fields["kernel_sources_sha256_16"]:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def kernel_time_us(torch, stream, fn, reps):
     """Average duration of fn()'s launches on `stream`, from HIP events on that stream."""
     fn()
@@ -102,50 +122,69 @@ def prefill_measure(torch, B, gen, reps=5):
             "topk_rows_us": round(t_topk, 1)}
 
 
-def cpu_baseline(inp, host_kv, pool_arrays, budget_s=12.0):
-    """The oracle, as it is, on a bounded sample of the same workload: whole requests in order
-    (scores in float64, exact top-k) until the budget is spent, then the oracle pool step for
-    the sampled requests' selections against the full pool."""
+def cpu_baseline(inp, host_kv, pool_arrays, min_s=10.0, budget_s=30.0):
+    """The oracle, as it is, timed on the host cores on a bounded sample of the same workload:
+    the whole oracle decode step (float64 scores, exact top-k, canonical pool step with the
+    recall copy) repeated from the same pool state until at least min_s seconds have passed.
+    A workload whose single step would exceed the budget is sampled by whole requests instead
+    (scores and top-k request by request until the budget is spent, then the pool step for the
+    sampled requests)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     except Exception:
         cores = 1
+
+    def state():
+        return oracle.PoolState(pool_arrays.free.copy(), pool_arrays.priority.copy(),
+                                pool_arrays.to_host.copy(), pool_arrays.host_to_gpu.copy(),
+                                pool_arrays.indices_buf.copy(), pool_arrays.gpu_kv.copy())
+
     t0 = time.perf_counter()
-    sel, tokens, n = [], 0, 0
-    for r in range(len(inp.key_len)):
-        sl = slice(r, r + 1)
-        s = oracle.index_scores(inp.q[sl], inp.w[sl], inp.k, inp.k_scale, inp.key_begin[sl],
-                                inp.key_len[sl])
-        sel.append(oracle.topk_rows(s, inp.cfg.topk)[0])
-        tokens += int(inp.key_len[r])
-        n += 1
-        if time.perf_counter() - t0 > budget_s:
+    reps, tokens, n = 0, 0, len(inp.key_len)
+    while True:
+        sel, tok = [], 0
+        for r in range(len(inp.key_len)):
+            sl = slice(r, r + 1)
+            s = oracle.index_scores(inp.q[sl], inp.w[sl], inp.k, inp.k_scale, inp.key_begin[sl],
+                                    inp.key_len[sl])
+            sel.append(oracle.topk_rows(s, inp.cfg.topk)[0])
+            tok += int(inp.key_len[r])
+            if reps == 0 and time.perf_counter() - t0 > budget_s:
+                n = r + 1
+                break
+        oracle.pool_step(state(), host_kv, np.stack(sel), inp.key_begin[:n], inp.req_to_host,
+                         pool_arrays.step_id)
+        reps += 1
+        tokens += tok
+        if n < len(inp.key_len) or time.perf_counter() - t0 >= min_s:
             break
-    st = oracle.PoolState(pool_arrays.free, pool_arrays.priority, pool_arrays.to_host,
-                          pool_arrays.host_to_gpu, pool_arrays.indices_buf, pool_arrays.gpu_kv)
-    oracle.pool_step(st, host_kv, np.stack(sel), inp.key_begin[:n], inp.req_to_host,
-                     pool_arrays.step_id)
     dt = time.perf_counter() - t0
+    if n < len(inp.key_len):
+        sample = ("oracle decode step on requests 0..%d of the workload (%d tokens): scores in "
+                  "float64, exact top-k, canonical pool step incl. recall copy" % (n - 1, tokens))
+    else:
+        sample = ("%d repetitions of the whole oracle decode step on the workload (%d tokens "
+                  "each): scores in float64, exact top-k, canonical pool step incl. recall copy, "
+                  "from the same pool state" % (reps, tokens // reps))
     return {"value": tokens / dt, "unit": "indexed tokens/s", "cores": int(cores),
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": "oracle decode step (float64 scores, exact top-k, canonical pool step "
-                      "incl. recall copy) on requests 0..%d of the workload (%d tokens)" % (n - 1, tokens)}
+            "kind": "oracle", "seconds": round(dt, 3), "sample": sample}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="b8_64k", choices=sorted(WORKLOADS))
     ap.add_argument("--kernel-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefetch", choices=("auto", "on", "off"), default="auto")
-    ap.add_argument("--streams", type=int, choices=(1, 2), default=2,
-                    help="streams the captured step uses (2: overlap work on a side stream)")
+    ap.add_argument("--probe", choices=("score", "copy"), default=None,
+                    help="short program for hardware-counter runs: 20 launches of the scoring "
+                         "kernel on the workload, or 20 device copies of 256 MiB, then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this decode path runs on one GPU; --gpus %d is not supported "
@@ -157,8 +196,28 @@ def main():
     from dsa_indexer_top_amd import binding as B, inputs as gen
     from dsa_indexer_top_amd.runner import DecodeRunner
 
+    if args.probe == "copy":
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(20):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy probe: 20 x 256 MiB device copies")
+        return
     cfg = gen.CONFIGS[args.workload]
     prefetch = cfg.prefetch if args.prefetch == "auto" else args.prefetch == "on"
+    if args.probe == "score":
+        inp = gen.make_decode_inputs(cfg)
+        dq, dw, dk = (torch.from_numpy(x).cuda() for x in (inp.q, inp.w, inp.k))
+        dks = None if inp.k_scale is None else torch.from_numpy(inp.k_scale).cuda()
+        dkb, dkl = torch.from_numpy(inp.key_begin).cuda(), torch.from_numpy(inp.key_len).cuda()
+        max_len = int(inp.key_len.max())
+        sc = torch.empty((len(inp.key_len), max_len), dtype=torch.float32, device="cuda")
+        for _ in range(20):
+            B.index_scores(dq, dw, dk, dks, dkb, dkl, max_len, sc)
+        torch.cuda.synchronize()
+        log("score probe: 20 launches of echo_index_scores on", args.workload)
+        return
     log("workload", args.workload, "prefetch", prefetch)
     t_setup = time.perf_counter()
     inp = gen.make_decode_inputs(cfg)
@@ -180,8 +239,6 @@ def main():
     pool = gen.make_pool_state(inp, sel.cpu().numpy(), host_kv)
     del sc, sel, tws
     rn = DecodeRunner(inp, pool, host_buf=hb, prefetch=prefetch)
-    if args.streams == 1:
-        rn.side = rn.main
     rn.capture()
     log("setup done in %.1fs" % (time.perf_counter() - t_setup))
 
@@ -251,16 +308,20 @@ def main():
                    "n_host_slots": rn.n_host, "prefetch": bool(prefetch),
                    "timing": "HIP events around each graph replay on its stream; pool restored "
                              "from a pristine copy between replays, outside the events"},
-        "roofline": {"bound": "hbm", "kernel": "score_decode_kernel",
+        "roofline": {"bound": "hbm",
+                     "kernel": "score_decode_kernel<false, false, false, false> (echo_index_scores)",
                      "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(score_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__)))
+                     if args.workload == "b8_64k" else None,
                      "bytes_per_launch": score_bytes, "us_per_launch": round(t_score, 2)},
         "recall": {"bound": "host link", "kernel": "recall_gather_kernel",
                    "achieved": round(recall_gbs, 2), "peak_measured_h2d": round(link, 2),
                    "unit": "GB/s", "frac": round(recall_gbs / link, 4) if link else None,
                    "rows": n_miss, "bytes_per_launch": recall_bytes,
                    "us_per_launch": round(t_recall, 2)},
-        "breakdown_us": {"step": round(ms * 1e3, 2), "score": round(t_score, 2),
+        "breakdown_us": {"step": round(ms * 1e3, 2), "step_median": round(float(np.median(step_ms)) * 1e3, 2),
+                         "score": round(t_score, 2),
                          "topk": round(t_topk, 2), "recall": round(t_recall, 2),
                          "wall_per_step_incl_restore": round(wall / args.steps * 1e6, 2)},
         "counters": {"n_miss": n_miss, "prefetch_demand": int(res["counters"][1]),
