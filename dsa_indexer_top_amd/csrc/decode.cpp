@@ -8,12 +8,12 @@
 // queues inside a graph cost microseconds each, so work that can overlap the critical path
 // rides along in the same launches as extra workgroups instead of on a second stream:
 //
-//   zero -> score (+ pool statistics) -> top-k split -> top-k finish + lookup
-//        -> evict-1 (+ recall staging, first half of the requests)
-//        -> evict-2 + allocate (+ recall staging, second half) -> recall scatter
+//   zero -> score (+ pool statistics) -> top-k split + early lookup of the sure selections
+//        -> top-k finish + lookup of the rest (+ staging of the split's misses from host memory)
+//        -> evict-1 (+ staging of the finish's misses) -> evict-2 + allocate -> recall scatter
 //
 // With prefetch, scoring is split into n_chunks token ranges: the launch of range c also
-// gathers range c-1's candidates, and the top-k split launch gathers the last range's.
+// gathers range c-1's candidates, and a gather launch for the last range precedes the split.
 #include <algorithm>
 
 #include "internal.hpp"
@@ -122,19 +122,13 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
       return rc;
     if ((rc = launch_prefetch_begin(pool, W.free_list, W.free_count, m))) return rc;
     const int32_t span = (a->max_key_len + nc - 1) / nc;
-    for (int c = 0; c <= nc; ++c) {
+    for (int c = 0; c < nc; ++c) {
       if (c > 0) {                                   // gather range c-1's candidates
         side.n_gather = a->n_rows;
         side.G = make_gather_args(pool, a->key_begin, a->req_to_host,
                                   W.cand + static_cast<int64_t>(c - 1) * a->n_rows * a->cap,
                                   W.cand_cnt + static_cast<int64_t>(c - 1) * a->n_rows, a->cap,
                                   W.free_list, W.free_count, o->counters + 2, &W.pool, a->step_id);
-      }
-      if (c == nc) {
-        if ((rc = launch_topk_split(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,
-                                    a->topk, W.hist0, W.split, &side, m)))
-          return rc;
-        break;
       }
       const int32_t lo = c * span, hi = (c + 1 == nc) ? a->max_key_len : (c + 1) * span;
       PrefetchArgs P{W.theta, a->req_to_host, pool->host_to_gpu,
@@ -146,18 +140,25 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
         return rc;
       side.n_stats = 0;
     }
+    // the last range's gather must finish before the top-k split looks selections up
+    const int64_t last = static_cast<int64_t>(nc - 1) * a->n_rows;
+    if ((rc = launch_prefetch_gather(pool, a->key_begin, a->req_to_host, W.cand + last * a->cap,
+                                     W.cand_cnt + last, a->n_rows, a->cap, W.free_list, W.free_count,
+                                     o->counters + 2, &W.pool, a->step_id, m)))
+      return rc;
   } else {
     if ((rc = launch_score_decode(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len, a->n_rows,
                                   a->max_key_len, 0, a->max_key_len, o->scores, a->max_key_len,
                                   nullptr, W.hist0, &side, m)))
       return rc;
-    if ((rc = launch_topk_split(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,
-                                a->topk, W.hist0, W.split, nullptr, m)))
-      return rc;
   }
+  if ((rc = launch_topk_split(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,
+                              a->topk, W.hist0, W.split, pool, &W.pool, a->key_begin, a->req_to_host,
+                              a->step_id, m)))
+    return rc;
   if ((rc = launch_topk_finish(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,
                                a->topk, W.hist0, W.split, o->topk_idx, pool, &W.pool, a->key_begin,
-                               a->req_to_host, a->step_id, o->topk_slot, true, m)))
+                               a->req_to_host, a->step_id, o->topk_slot, true, W.stage, m)))
     return rc;
   if ((rc = launch_pool_evict(pool, W.pool, o->topk_idx, a->n_rows, a->topk, a->step_id, o->topk_slot,
                               o->miss_host, o->miss_slot, o->counters + 0, W.stage, m)))

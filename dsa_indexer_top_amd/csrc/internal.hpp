@@ -47,17 +47,21 @@ int launch_topk(const float *scores, int64_t ld, const int32_t *len, int32_t n_r
 // words (counters, priority histograms, protection bitmap) must be zeroed before each step.
 struct PoolFastWs {
   int32_t *counters;      // [16]: 0 free slots, 2 threshold fine bin, 3 evictable slots below it
-  uint32_t *fine;         // [32768] occupied, unprotected slots per priority bin
-  uint32_t *coarse;       // [1024]  the same, 32 fine bins per coarse bin
+  uint32_t *fine;         // [32768] occupied, unprotected slots per priority bin (spread layout)
+  uint32_t *coarse;       // [32768 words, 1024 used] the same, 32 fine bins per coarse bin
   uint32_t *prot;         // [ceil(n_gpu/32)] protection bitmap (slots holding a selected token)
+  uint32_t *stage_a;      // [n_rows] (zeroed) misses found by the early lookup in the top-k split
   uint32_t *row_miss_cnt; // [n_rows]
   int32_t *row_miss_h;    // [n_rows * k] ordered misses of each request: host index
-  int32_t *row_miss_j;    // [n_rows * k] ... and column in the request's selection
+  int32_t *row_miss_j;    // [n_rows * k] ... column in the request's selection
+  int32_t *row_miss_s;    // [n_rows * k] ... and staging row
+  uint32_t *stage_b;      // [n_rows] misses found by the top-k finish (staging rows r*k + stage_a[r] ...)
+  int32_t *stage_h;       // [n_rows * k] host index of each staging row r*k + i
   uint32_t *chunk_free;   // [n_chunks] free slots per 4096-slot chunk after the first evictions
   uint32_t *chunk_cand;   // [n_chunks] threshold-bin slots per chunk
   uint64_t *cand;         // [n_chunks * 4096] (priority key << 32 | slot), per chunk in slot order
   int32_t *miss_entry;    // [n_rows * k] entry (r*k + j) of the i-th miss
-  int32_t *miss_stage;    // [n_rows * k] r*k + (position in request r's miss list) of the i-th miss
+  int32_t *miss_stage;    // [n_rows * k] staging row of the i-th miss
   void *base;
   int32_t n_chunks;
   int64_t zero_words;
@@ -109,14 +113,14 @@ int launch_pool_lookup_rows(const echo_pool *pool, const PoolFastWs &W, const in
                             const int64_t *key_begin, const int32_t *req_to_host, int64_t n_k,
                             int32_t n_rows, int32_t k, int32_t step_id, int32_t *topk_slot,
                             hipStream_t st);
-// Missed rows copied into a staging area by workgroups riding along in the eviction launches.
+// Missed rows copied into a staging area by workgroups riding along in the eviction launch.
 struct StageArgs {
   const uint16_t *host_kv;
   uint16_t *stage;            // [n_rows * k][ROW]; NULL: no staging
-  int32_t rows_a;             // requests staged during evict-1; the rest during evict-2
 };
-// stage (optional): read the missed rows into stage[r*k + i] while evicting (the caller then
-// runs launch_recall_scatter)
+// stage (optional): evict-1 also reads the misses the top-k finish found (staging rows
+// r*k + [stage_a[r], stage_a[r] + stage_b[r])) into the staging area; the caller then runs
+// launch_recall_scatter.
 int launch_pool_evict(const echo_pool *pool, const PoolFastWs &W, const int32_t *idx, int32_t n_rows,
                       int32_t k, int32_t step_id, int32_t *topk_slot, int32_t *miss_host,
                       int32_t *miss_slot, int32_t *n_miss, uint16_t *stage, hipStream_t st);
@@ -126,19 +130,23 @@ int launch_pool_step(const echo_pool *pool, const int32_t *idx, const int64_t *k
                      int32_t step_id, int32_t *topk_slot, int32_t *miss_host, int32_t *miss_slot,
                      int32_t *n_miss, void *ws, size_t ws_bytes, hipStream_t st);
 
-// Decode top-k: split (multi-workgroup) then finish (one workgroup per request); when pool is
-// not NULL the finish also performs the residency lookup into *pw (whose zeroed region must be
-// ready); sub_prot: the histograms hold every occupied slot and the lookup subtracts the slots
-// it protects.
+// Decode top-k: split (multi-workgroup) then finish (one workgroup per request).  With a pool,
+// the split looks the sure selections up early (protection, priority-histogram removal,
+// misses queued at staging rows r*k + [0, stage_a[r])), and the finish looks up the rest,
+// lists every request's misses in order and queues its own misses after the split's; with a
+// staging area the finish launch also reads the split's queued misses from host memory.  The
+// pool workspace's zeroed region must be ready and its histograms must hold every occupied
+// slot.
 size_t topk_split_ws_bytes(int32_t n_rows, int32_t max_len, int32_t k);
 int launch_topk_split(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
                       int32_t max_len, int32_t k, const uint32_t *hist0, void *split_ws,
-                      const SideWork *side, hipStream_t st);
+                      const echo_pool *pool, const PoolFastWs *pw, const int64_t *key_begin,
+                      const int32_t *req_to_host, int32_t step_id, hipStream_t st);
 int launch_topk_finish(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
                        int32_t max_len, int32_t k, const uint32_t *hist0, void *split_ws,
                        int32_t *idx, const echo_pool *pool, const PoolFastWs *pw,
                        const int64_t *key_begin, const int32_t *req_to_host, int32_t step_id,
-                       int32_t *topk_slot, bool sub_prot, hipStream_t st);
+                       int32_t *topk_slot, bool early, uint16_t *stage, hipStream_t st);
 
 int launch_recall_gather(const echo_pool *pool, const int32_t *miss_host, const int32_t *miss_slot,
                          const int32_t *n_miss, int32_t max_miss, hipStream_t st);

@@ -9,6 +9,14 @@ constexpr int PF_T = 256;                     // threads of the slot / entry wor
 constexpr int PF_CH = 4096;                   // slots per chunk
 constexpr int PF_FINE = 32768;                // fine priority bins
 constexpr int PF_COARSE = 1024;               // coarse bins (32 fine bins each)
+constexpr int PF_HIST_WORDS = 32768;          // words of each histogram array (layout below)
+
+// Histogram layout: bin b lives at word (b % 32) * 1024 + b / 32, so consecutive bins are 4 KB
+// apart and land in different memory channels.  The bins that collect most updates are
+// neighbours (priorities are step stamps), and device-scope atomics confined to one channel
+// run several times slower than spread ones.  The coarse array uses the same map (1024 of its
+// 32768 words are used).
+ECHO_DEV uint32_t hist_at(uint32_t b) { return (b & 31u) * 1024u + (b >> 5); }
 constexpr int STATS_HW = 8192;               // LDS histogram window (words) of a stats chunk
 constexpr int STATS_LDS_WORDS = STATS_HW + 48;
 
@@ -89,10 +97,12 @@ ECHO_DEV void hist_flush_bins(const uint32_t (&bins)[NB], uint32_t *h, uint32_t 
       const int w = w0 + static_cast<int>(threadIdx.x);
       const uint32_t v = w <= top ? h[w - base] : 0u;
       const uint32_t a = v & 0xFFFFu, b = v >> 16;
-      if (a) { if (SUB) atomicSub(&fine[2 * w], a); else atomicAdd(&fine[2 * w], a); }
-      if (b) { if (SUB) atomicSub(&fine[2 * w + 1], b); else atomicAdd(&fine[2 * w + 1], b); }
+      if (a) { if (SUB) atomicSub(&fine[hist_at(2 * w)], a); else atomicAdd(&fine[hist_at(2 * w)], a); }
+      if (b) { if (SUB) atomicSub(&fine[hist_at(2 * w + 1)], b); else atomicAdd(&fine[hist_at(2 * w + 1)], b); }
       const uint32_t sum = row16_incl_scan(a + b);     // lane 15 of the row: the coarse bin's total
-      if ((threadIdx.x & 15) == 15 && sum) { if (SUB) atomicSub(&coarse[w >> 4], sum); else atomicAdd(&coarse[w >> 4], sum); }
+      if ((threadIdx.x & 15) == 15 && sum) {
+        if (SUB) atomicSub(&coarse[hist_at(w >> 4)], sum); else atomicAdd(&coarse[hist_at(w >> 4)], sum);
+      }
     }
     __syncthreads();
   }
@@ -225,8 +235,8 @@ ECHO_DEV void gather_request(const GatherArgs &G, int r, uint32_t *lds) {
     if (threadIdx.x == 0 && n_ok) {
       const uint32_t b = prio_bin(0, G.step_id);
       atomicSub(G.st_free, static_cast<int32_t>(n_ok));
-      atomicAdd(&G.st_fine[b], n_ok);
-      atomicAdd(&G.st_coarse[b >> 5], n_ok);
+      atomicAdd(&G.st_fine[hist_at(b)], n_ok);
+      atomicAdd(&G.st_coarse[hist_at(b >> 5)], n_ok);
     }
   }
 }
@@ -249,20 +259,21 @@ ECHO_DEV bool side_work(const SideWork &S, int b, uint32_t *lds) {
 
 
 // ---------------------------------------------------------------- recall staging
-// Copies missed rows of request r, entries [i0, i0 + ROWS) of its miss list, from host memory
-// into stage[r*k + i] (NT threads, ROWS * 72 / NT sixteen-byte loads each, all in flight
-// before the first store).
+// Copies staging rows r*k + i, i in [i0, i0 + ROWS) and in [lo, hi), from host memory:
+// stage[r*k + i] = host_kv[stage_h[r*k + i]] (NT threads, ROWS * 72 / NT sixteen-byte loads
+// each, all in flight before the first store).
 template <int NT, int ROWS>
 ECHO_DEV void stage_rows(const uint16_t *__restrict__ host_kv, uint16_t *__restrict__ stage,
-                         const PoolFastWs &W, const int32_t *status, int32_t k, int32_t n_host, int r,
-                         int32_t i0) {
+                         const int32_t *__restrict__ stage_h, const int32_t *status, int32_t k,
+                         int32_t n_host, int r, int32_t i0, int32_t lo, int32_t hi) {
   typedef int v4i __attribute__((ext_vector_type(4)));
   constexpr int UNITS = ROW * 2 / 16;
   constexpr int PER = ROWS * UNITS / NT;
   static_assert(PER * NT == ROWS * UNITS, "whole rows per block");
   if (*(volatile const int32_t *)status) return;
-  const int32_t cnt = min(static_cast<int32_t>(W.row_miss_cnt[r]), k);
-  if (i0 >= cnt) return;
+  lo = max(lo, i0);
+  hi = min(min(hi, i0 + ROWS), k);
+  if (lo >= hi) return;
   const v4i *src = reinterpret_cast<const v4i *>(host_kv);
   v4i *dst = reinterpret_cast<v4i *>(stage);
   const int64_t e0 = static_cast<int64_t>(r) * k;
@@ -274,8 +285,8 @@ ECHO_DEV void stage_rows(const uint16_t *__restrict__ host_kv, uint16_t *__restr
     const int32_t i = i0 + u / UNITS;
     const int part = u % UNITS;
     d_off[m] = -1;
-    if (i < cnt) {
-      const int32_t h = W.row_miss_h[e0 + i];
+    if (i >= lo && i < hi) {
+      const int32_t h = stage_h[e0 + i];
       if (h >= 0 && h < n_host) {
         v[m] = __builtin_nontemporal_load(src + static_cast<int64_t>(h) * UNITS + part);
         d_off[m] = (e0 + i) * UNITS + part;

@@ -43,11 +43,14 @@ void pool_fast_ws_layout(int32_t n_rows, int32_t k, int32_t n_gpu, void *base, P
   size_t off = 0;
   auto take = [&](size_t b) { size_t o = off; off += al(b); return o; };
   // zeroed region first (one fill per step): counters, histograms, protection bits
-  const size_t o_cnt = take(16 * 4), o_fine = take(PF_FINE * 4), o_coarse = take(PF_COARSE * 4),
-               o_prot = take(static_cast<size_t>((n_gpu + 31) / 32) * 4);
+  const size_t o_cnt = take(16 * 4), o_fine = take(PF_HIST_WORDS * 4), o_coarse = take(PF_HIST_WORDS * 4),
+               o_prot = take(static_cast<size_t>((n_gpu + 31) / 32) * 4),
+               o_sa = take(static_cast<size_t>(n_rows) * 4);
   const size_t zero_end = off;
   const size_t o_rmc = take(static_cast<size_t>(n_rows) * 4),
                o_rmh = take(static_cast<size_t>(n_ent) * 4), o_rmj = take(static_cast<size_t>(n_ent) * 4),
+               o_rms = take(static_cast<size_t>(n_ent) * 4), o_sb = take(static_cast<size_t>(n_rows) * 4),
+               o_sh = take(static_cast<size_t>(n_ent) * 4),
                o_cf = take(static_cast<size_t>(n_chunks) * 4), o_cc = take(static_cast<size_t>(n_chunks) * 4),
                o_cand = take(static_cast<size_t>(n_chunks) * PF_CH * 8),
                o_me = take(static_cast<size_t>(n_ent) * 4), o_ms = take(static_cast<size_t>(n_ent) * 4);
@@ -60,9 +63,13 @@ void pool_fast_ws_layout(int32_t n_rows, int32_t k, int32_t n_gpu, void *base, P
     w->fine = reinterpret_cast<uint32_t *>(b + o_fine);
     w->coarse = reinterpret_cast<uint32_t *>(b + o_coarse);
     w->prot = reinterpret_cast<uint32_t *>(b + o_prot);
+    w->stage_a = reinterpret_cast<uint32_t *>(b + o_sa);
     w->row_miss_cnt = reinterpret_cast<uint32_t *>(b + o_rmc);
     w->row_miss_h = reinterpret_cast<int32_t *>(b + o_rmh);
     w->row_miss_j = reinterpret_cast<int32_t *>(b + o_rmj);
+    w->row_miss_s = reinterpret_cast<int32_t *>(b + o_rms);
+    w->stage_b = reinterpret_cast<uint32_t *>(b + o_sb);
+    w->stage_h = reinterpret_cast<int32_t *>(b + o_sh);
     w->chunk_free = reinterpret_cast<uint32_t *>(b + o_cf);
     w->chunk_cand = reinterpret_cast<uint32_t *>(b + o_cc);
     w->cand = reinterpret_cast<uint64_t *>(b + o_cand);
@@ -119,6 +126,7 @@ __global__ __launch_bounds__(PF_RES_T) void pool_lookup_rows_kernel(
     if (miss) {
       W.row_miss_h[static_cast<int64_t>(r) * k + pos] = h;
       W.row_miss_j[static_cast<int64_t>(r) * k + pos] = j;
+      W.row_miss_s[static_cast<int64_t>(r) * k + pos] = r * k + static_cast<int32_t>(pos);
     }
     if (j < k) topk_slot[static_cast<int64_t>(r) * k + j] = (res >= 0 && res != INF) ? res : -1;
     n_miss += tot;
@@ -144,7 +152,8 @@ ECHO_DEV StepState step_pick(const PoolArgs &P, const PoolFastWs &W, int32_t n_r
   const int t = threadIdx.x;
   uint32_t nm = 0;
   for (int r = t; r < n_rows; r += PF_T) nm += W.row_miss_cnt[r];
-  const uint4 cv = *reinterpret_cast<const uint4 *>(W.coarse + t * PER);
+  const uint4 cv{W.coarse[hist_at(t * PER)], W.coarse[hist_at(t * PER + 1)], W.coarse[hist_at(t * PER + 2)],
+                 W.coarse[hist_at(t * PER + 3)]};
   const int32_t status = *(volatile int32_t *)P.status;
   const uint32_t n_free = static_cast<uint32_t>(W.counters[0]);
   const uint32_t local = cv.x + cv.y + cv.z + cv.w;
@@ -172,7 +181,7 @@ ECHO_DEV StepState step_pick(const PoolArgs &P, const PoolFastWs &W, int32_t n_r
   __syncthreads();
   if (t < 64) {
     const uint32_t cb = tmp[40], cum = tmp[41];
-    const uint32_t v = t < 32 ? W.fine[cb * 32 + t] : 0u;
+    const uint32_t v = t < 32 ? W.fine[hist_at(cb * 32 + t)] : 0u;
     const uint32_t inc = wave_incl_scan(v);
     if (t < 32 && cum + inc - v < need && need <= cum + inc) {
       tmp[42] = cb * 32 + t;
@@ -216,9 +225,11 @@ __global__ __launch_bounds__(PF_T) void pool_evict1_kernel(PoolArgs P, PoolFastW
   __shared__ uint32_t tmp[48];
   __shared__ uint32_t gscan[4 * (PF_T / 64) + PF_T / 64 + 2];
   if (static_cast<int>(blockIdx.x) >= n_rows + W.n_chunks) {
-    // recall staging of requests [0, SA.rows_a), 32 entries per block
-    const int u = blockIdx.x - n_rows - W.n_chunks, per = (k + 31) / 32;
-    stage_rows<PF_T, 32>(SA.host_kv, SA.stage, W, P.status, k, P.n_host, u / per, (u % per) * 32);
+    // recall staging of the misses the top-k finish found, 32 staging rows per block
+    const int u = blockIdx.x - n_rows - W.n_chunks, per = (k + 31) / 32, r = u / per;
+    const int32_t lo = static_cast<int32_t>(W.stage_a[r]);
+    stage_rows<PF_T, 32>(SA.host_kv, SA.stage, W.stage_h, P.status, k, P.n_host, r,
+                         lo + (u % per) * 32, lo, lo + static_cast<int32_t>(W.stage_b[r]));
     return;
   }
   if (static_cast<int>(blockIdx.x) < n_rows) {
@@ -230,7 +241,7 @@ __global__ __launch_bounds__(PF_T) void pool_evict1_kernel(PoolArgs P, PoolFastW
     for (uint32_t i = threadIdx.x; i < cnt; i += PF_T) {
       miss_host[before + i] = W.row_miss_h[static_cast<int64_t>(r) * k + i];
       W.miss_entry[before + i] = r * k + W.row_miss_j[static_cast<int64_t>(r) * k + i];
-      W.miss_stage[before + i] = r * k + static_cast<int32_t>(i);
+      W.miss_stage[before + i] = W.row_miss_s[static_cast<int64_t>(r) * k + i];
     }
     return;
   }
@@ -350,8 +361,7 @@ struct CandView {
 __global__ __launch_bounds__(PF_RES_T) void pool_evict2_kernel(
     PoolArgs P, PoolFastWs W, int32_t n_rows, int32_t k, int32_t step_id,
     int32_t *__restrict__ miss_host, int32_t *__restrict__ miss_slot, int32_t *__restrict__ topk_slot,
-    int32_t *__restrict__ n_miss_out, const int32_t *__restrict__ idx, int32_t entry_blocks,
-    StageArgs SA) {
+    int32_t *__restrict__ n_miss_out, const int32_t *__restrict__ idx) {
   __shared__ uint32_t tmp[48];
   __shared__ uint64_t cl[PF_CAP];
   __shared__ uint32_t hist[2048];
@@ -360,13 +370,6 @@ __global__ __launch_bounds__(PF_RES_T) void pool_evict2_kernel(
   const int t = threadIdx.x;
   const int32_t n_chunks = W.n_chunks;
   const int64_t n_ent = static_cast<int64_t>(n_rows) * k;
-  if (static_cast<int>(blockIdx.x) >= n_chunks + entry_blocks) {
-    // recall staging of requests [SA.rows_a, n_rows), 128 entries per block
-    const int u = blockIdx.x - n_chunks - entry_blocks, per = (k + 127) / 128;
-    stage_rows<PF_RES_T, 128>(SA.host_kv, SA.stage, W, P.status, k, P.n_host, SA.rows_a + u / per,
-                              (u % per) * 128);
-    return;
-  }
   if (static_cast<int>(blockIdx.x) >= n_chunks) {
     // ---- entry workgroups: stamp hits, pad the fixed-length lists
     const StepState st = step_read(W);
@@ -530,16 +533,14 @@ int launch_pool_evict(const echo_pool *pool, const PoolFastWs &W, const int32_t 
   if (W.n_chunks > 1024) return fail(ECHO_EUNSUPPORTED, "pool: more than 4M slots");
   PoolArgs P{pool->gpu_free, pool->gpu_priority, pool->gpu_to_host, pool->host_to_gpu,
              pool->indices_buf, pool->status, pool->n_gpu, pool->n_host};
-  // with a staging area, the first half of the requests' missed rows are read from host memory
-  // during evict-1 and the rest during evict-2
-  StageArgs SA{pool->host_kv, stage, stage ? (n_rows + 1) / 2 : 0};
-  const int s1 = stage ? SA.rows_a * ((k + 31) / 32) : 0;
-  const int s2 = stage ? (n_rows - SA.rows_a) * ((k + 127) / 128) : 0;
+  // with a staging area, evict-1 also reads the misses the top-k finish found from host memory
+  StageArgs SA{pool->host_kv, stage};
+  const int s1 = stage ? n_rows * ((k + 31) / 32) : 0;
   pool_evict1_kernel<<<n_rows + W.n_chunks + s1, PF_T, 0, st>>>(P, W, n_rows, k, step_id, miss_host, SA);
   const int64_t n_ent = static_cast<int64_t>(n_rows) * k;
   const int entry_blocks = static_cast<int>(std::max<int64_t>(1, (n_ent + PF_RES_T - 1) / PF_RES_T));
-  pool_evict2_kernel<<<W.n_chunks + entry_blocks + s2, PF_RES_T, 0, st>>>(
-      P, W, n_rows, k, step_id, miss_host, miss_slot, topk_slot, n_miss, idx, entry_blocks, SA);
+  pool_evict2_kernel<<<W.n_chunks + entry_blocks, PF_RES_T, 0, st>>>(
+      P, W, n_rows, k, step_id, miss_host, miss_slot, topk_slot, n_miss, idx);
   return check_launch("pool_evict");
 }
 

@@ -6,12 +6,18 @@
 //   split   grid (4096-score chunk, request): every workgroup re-derives the threshold bin b0
 //           of the request from the digit-0 histogram the scoring kernel built, and writes the
 //           indices of its chunk below b0 ("sure") and the (key, index) pairs in b0
-//           ("candidates") into per-chunk segments, in index order.
+//           ("candidates") into per-chunk segments, in index order.  In the decode step it
+//           also looks the sure selections up in the pool right away (they are selected
+//           whatever the remaining digits decide): hits are protected and leave the priority
+//           histogram, misses are queued for staging from host memory, and each sure
+//           selection's result goes to sure_code.
 //   finish  one 1024-thread workgroup per request: concatenates the segments in chunk order
 //           (so both lists are ascending), resolves the remaining key digits on the
 //           candidates in LDS, takes the keys below the threshold key and the lowest-index
 //           ties, merges the two ascending lists into the selection, writes it, and looks each
-//           selected token up in the pool (hits are protected, misses listed in order).
+//           selected token up in the pool (the sure ones by their split result, the others
+//           now), lists the misses in order and queues the new ones for staging.  Extra
+//           workgroups of the same launch read the split's queued misses from host memory.
 //           A threshold bin too large for LDS is resolved with passes over the request's
 //           scores instead.
 #include <algorithm>
@@ -28,6 +34,7 @@ constexpr int TF_CAP = 8192;                     // candidates resolved in LDS
 constexpr int TF_J = 8;                          // overflow passes: groups per thread per batch
 constexpr int TF_STEP = 4 * TF_T;
 constexpr int TF_BATCH = TF_J * TF_STEP;
+constexpr int TS_HW = 2048;                      // LDS histogram window of a split workgroup
 
 ECHO_DEV uint32_t score_key(float x) { return ~f32_key(x); }   // ascending key = descending score
 
@@ -101,7 +108,7 @@ size_t topk_split_ws_bytes(int32_t n_rows, int32_t max_len, int32_t k) {
   const int64_t nch = std::max(1, (max_len + TS_CH - 1) / TS_CH);
   const int64_t segs = static_cast<int64_t>(n_rows) * nch;
   auto al = [](int64_t b) { return (b + 255) & ~static_cast<int64_t>(255); };
-  return static_cast<size_t>(al(segs * 4) * 2 + al(segs * k * 4) + al(segs * TS_CH * 8));
+  return static_cast<size_t>(al(segs * 4) * 2 + al(segs * k * 4) * 2 + al(segs * TS_CH * 8));
 }
 
 struct SplitWs {
@@ -109,7 +116,17 @@ struct SplitWs {
   uint32_t *cand_cnt;   // [n_rows * nch]
   int32_t *sure;        // [n_rows * nch * k]
   uint64_t *cand;       // [n_rows * nch * 4096]  (key << 32 | index)
+  int32_t *sure_code;   // [n_rows * nch * k] early lookup: slot (hit), -2 - staging row (miss), -1 (bad)
   int32_t nch;
+};
+
+// Early residency lookup of the sure selections (decode step).
+struct SplitLookup {
+  PoolArgs P;
+  PoolFastWs W;
+  const int64_t *key_begin;
+  const int32_t *req_to_host;
+  int32_t step_id;
 };
 
 static SplitWs make_split_ws(void *base, int32_t n_rows, int32_t max_len, int32_t k) {
@@ -122,26 +139,23 @@ static SplitWs make_split_ws(void *base, int32_t n_rows, int32_t max_len, int32_
   w.cand_cnt = reinterpret_cast<uint32_t *>(b + al(segs * 4));
   w.sure = reinterpret_cast<int32_t *>(b + 2 * al(segs * 4));
   w.cand = reinterpret_cast<uint64_t *>(b + 2 * al(segs * 4) + al(segs * k * 4));
+  w.sure_code = reinterpret_cast<int32_t *>(b + 2 * al(segs * 4) + al(segs * k * 4) + al(segs * TS_CH * 8));
   w.nch = static_cast<int32_t>(nch);
   return w;
 }
 
 // ---------------------------------------------------------------- split
-// SIDE: leading workgroups of the launch run side work (a prefetch gather) instead.
-template <bool SIDE>
+// LOOKUP: the early residency lookup of the sure selections (see the file comment).
+template <bool LOOKUP>
 __global__ __launch_bounds__(TS_T) void topk_split_kernel(const float *__restrict__ scores, int64_t ld,
                                                           const int32_t *__restrict__ len, int32_t max_len,
                                                           int32_t k, const uint32_t *__restrict__ hist0,
-                                                          SplitWs W, SideWork side) {
+                                                          SplitWs W, SplitLookup L) {
   __shared__ uint32_t tmp[48];
   __shared__ uint32_t gscan[4 * (TS_T / 64) + TS_T / 64 + 2];
-  __shared__ uint32_t side_lds[SIDE ? SIDE_LDS_WORDS : 1];
-  int b = blockIdx.x;
-  if constexpr (SIDE) {
-    if (side_work(side, b, side_lds)) return;
-    b -= side.n_stats + side.n_gather;
-  }
-  const int r = b / W.nch, c = b % W.nch, t = threadIdx.x;
+  __shared__ int32_t sl[LOOKUP ? ECHO_MAX_TOPK : 1];     // this chunk's sure indices, ascending
+  __shared__ uint32_t hl[LOOKUP ? TS_HW : 1];
+  const int r = blockIdx.x / W.nch, c = blockIdx.x % W.nch, t = threadIdx.x;
   const int32_t n = min(max(len[r], 0), max_len);
   const int32_t m = min(k, n);
   if (m == n || c * TS_CH >= n) return;
@@ -178,7 +192,10 @@ __global__ __launch_bounds__(TS_T) void topk_split_kernel(const float *__restric
       if ((valid[j] >> e) & 1) {
         const uint32_t b = key[j][e] >> 21;
         if (b < b0) {
-          if (ps < static_cast<uint32_t>(k)) W.sure[seg * k + ps] = i0 + e;
+          if (ps < static_cast<uint32_t>(k)) {
+            W.sure[seg * k + ps] = i0 + e;
+            if (LOOKUP) sl[ps] = i0 + e;
+          }
           ++ps;
         } else if (b == b0 && keep_cand) {
           W.cand[seg * TS_CH + pc] = (static_cast<uint64_t>(key[j][e]) << 32) | static_cast<uint32_t>(i0 + e);
@@ -190,6 +207,67 @@ __global__ __launch_bounds__(TS_T) void topk_split_kernel(const float *__restric
     W.sure_cnt[seg] = tot & 0xFFFF;
     W.cand_cnt[seg] = tot >> 16;
   }
+  if constexpr (LOOKUP) {
+    if (L.P.n_gpu == 0) return;
+    __syncthreads();
+    const PoolArgs &P = L.P;
+    const uint32_t n_s = min(tot & 0xFFFFu, static_cast<uint32_t>(k));
+    const int64_t kb = L.key_begin[r];
+    for (uint32_t base = 0; base < n_s; base += 4 * TS_T) {      // uniform
+      int32_t h[4], slot[4], code[4], pr[4];
+      uint32_t miss[4], old[4], bins[4];
+      bool hit[4], bad = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t p = base + i * TS_T + t;
+        h[i] = p < n_s ? L.req_to_host[kb + sl[p]] : -1;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t p = base + i * TS_T + t;
+        slot[i] = (p < n_s && h[i] >= 0 && h[i] < P.n_host) ? P.host_to_gpu[h[i]] : -1;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t p = base + i * TS_T + t;
+        hit[i] = false;
+        miss[i] = 0;
+        code[i] = -1;
+        if (p < n_s) {
+          if (h[i] < 0 || h[i] >= P.n_host) bad = true;
+          else if (slot[i] == INF) miss[i] = 1;
+          else if (slot[i] < 0 || slot[i] >= P.n_gpu) bad = true;
+          else { hit[i] = true; code[i] = slot[i]; }
+        }
+      }
+      if (bad) atomicOr(P.status, ECHO_ST_BAD_HOST);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = hit[i] ? P.priority[slot[i]] : 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        old[i] = hit[i] ? atomicOr(&L.W.prot[slot[i] >> 5], 1u << (slot[i] & 31)) : ~0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        bins[i] = (hit[i] && !((old[i] >> (slot[i] & 31)) & 1u)) ? prio_bin(pr[i], L.step_id) : 0xFFFFFFFFu;
+      // misses: staging rows r*k + [stage_a[r], ...), reserved once per workgroup
+      uint32_t mo[4], n_m;
+      group_excl_scan<TS_T, 4>(miss, mo, gscan, &n_m);
+      if (t == 0) tmp[44] = n_m ? atomicAdd(&L.W.stage_a[r], n_m) : 0u;
+      __syncthreads();
+      const uint32_t sbase = tmp[44];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t p = base + i * TS_T + t;
+        if (miss[i]) {
+          const int64_t srow = static_cast<int64_t>(r) * k + sbase + mo[i];
+          L.W.stage_h[srow] = h[i];
+          code[i] = -2 - static_cast<int32_t>(srow);
+        }
+        if (p < n_s) W.sure_code[seg * k + p] = code[i];
+      }
+      hist_flush_bins<TS_T, 4, true, TS_HW>(bins, hl, tmp, L.W.fine, L.W.coarse);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- finish + lookup
@@ -199,13 +277,21 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
     // lookup (skipped when pool.n_gpu == 0)
     PoolArgs P, PoolFastWs PW, const int64_t *__restrict__ key_begin,
     const int32_t *__restrict__ req_to_host, int32_t step_id, int32_t *__restrict__ topk_slot,
-    bool sub_prot) {
+    bool sub_prot, bool early, int32_t n_rows, StageArgs SA) {
+  if (static_cast<int>(blockIdx.x) >= n_rows) {
+    // staging of the misses the split's early lookup found: rows r*k + [0, stage_a[r])
+    const int u = blockIdx.x - n_rows, per = (k + 127) / 128, rr = u / per;
+    stage_rows<TF_T, 128>(SA.host_kv, SA.stage, PW.stage_h, P.status, k, P.n_host, rr,
+                          (u % per) * 128, 0, static_cast<int32_t>(PW.stage_a[rr]));
+    return;
+  }
   __shared__ uint32_t tmp[48];
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t cbuf[2 * TF_CAP];               // candidates; later the lookup's histogram
   uint32_t *ckey = cbuf;
   int32_t *cidx = reinterpret_cast<int32_t *>(cbuf + TF_CAP);
   __shared__ int32_t sure[ECHO_MAX_TOPK];
+  __shared__ int32_t scode[ECHO_MAX_TOPK];            // early-lookup result of each sure selection
   __shared__ int32_t sel[ECHO_MAX_TOPK];
   __shared__ int32_t fin[ECHO_MAX_TOPK];
   __shared__ uint32_t segoff[2][1024];
@@ -214,6 +300,7 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
   const int32_t n = min(max(len[r], 0), max_len);
   const int32_t m = min(k, n);
   const float *row = scores + static_cast<int64_t>(r) * ld;
+  uint32_t n_sure_sel = 0;                           // sure selections listed in sure[]
 
   if (m == n) {
     for (int j = t; j < m; j += TF_T) fin[j] = j;
@@ -243,9 +330,12 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
       return lo;
     };
     const uint32_t n_sure = min(below0, static_cast<uint32_t>(ECHO_MAX_TOPK));
+    n_sure_sel = n_sure;
     for (uint32_t p = t; p < n_sure; p += TF_T) {
       const int q = seg_of(0, p);
-      sure[p] = W.sure[(seg0 + q) * k + (p - segoff[0][q])];
+      const int64_t at = (seg0 + q) * k + (p - segoff[0][q]);
+      sure[p] = W.sure[at];
+      if (early) scode[p] = W.sure_code[at];
     }
     if (c0 <= TF_CAP) {
       const uint32_t n_cand = c0;
@@ -388,30 +478,46 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
   if (P.n_gpu == 0) return;
   int32_t *slot_out = topk_slot + static_cast<int64_t>(r) * k;
   const int64_t kb = key_begin[r];
+  const uint32_t sa = early ? PW.stage_a[r] : 0u;
   constexpr int LJ = ECHO_MAX_TOPK / TF_T;          // entries per thread: j = t + TF_T * i
-  int32_t h[LJ], slot[LJ], res[LJ];
-  bool hit[LJ];
+  int32_t h[LJ], slot[LJ], res[LJ], srow[LJ], code[LJ];
+  bool cand[LJ], hit[LJ];
+  // a sure selection carries the split's result; the others are looked up here
 #pragma unroll
   for (int i = 0; i < LJ; ++i) {
     const int32_t j = t + TF_T * i;
-    h[i] = j < m ? req_to_host[kb + fin[j]] : -1;
+    cand[i] = j < m;
+    code[i] = -1;
+    if (early && j < m && n_sure_sel > 0) {
+      const int32_t tok = fin[j];
+      uint32_t lo = 0, hi = n_sure_sel;
+      while (lo < hi) { const uint32_t md = (lo + hi) >> 1; if (sure[md] < tok) lo = md + 1; else hi = md; }
+      if (lo < n_sure_sel && sure[lo] == tok) { cand[i] = false; code[i] = scode[lo]; }
+    }
   }
 #pragma unroll
   for (int i = 0; i < LJ; ++i) {
     const int32_t j = t + TF_T * i;
-    slot[i] = (j < m && h[i] >= 0 && h[i] < P.n_host) ? P.host_to_gpu[h[i]] : -1;
+    h[i] = cand[i] ? req_to_host[kb + fin[j]] : (code[i] <= -2 ? PW.stage_h[-2 - code[i]] : -1);
   }
+#pragma unroll
+  for (int i = 0; i < LJ; ++i)
+    slot[i] = (cand[i] && h[i] >= 0 && h[i] < P.n_host) ? P.host_to_gpu[h[i]] : -1;
   bool bad = false;
 #pragma unroll
   for (int i = 0; i < LJ; ++i) {
     const int32_t j = t + TF_T * i;
     hit[i] = false;
     res[i] = -1;
-    if (j < m) {
+    srow[i] = -1;
+    if (cand[i]) {
       if (h[i] < 0 || h[i] >= P.n_host) bad = true;
       else if (slot[i] == INF) res[i] = INF;
       else if (slot[i] < 0 || slot[i] >= P.n_gpu) bad = true;
       else { hit[i] = true; res[i] = slot[i]; }
+    } else if (j < m) {
+      if (code[i] >= 0) res[i] = code[i];                        // hit, protected by the split
+      else if (code[i] <= -2) { res[i] = INF; srow[i] = -2 - code[i]; }   // miss, already queued
     }
   }
   if (bad) atomicOr(P.status, ECHO_ST_BAD_HOST);
@@ -434,7 +540,18 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
     for (int i = 0; i < LJ; ++i)
       if (hit[i]) atomicOr(&PW.prot[slot[i] >> 5], 1u << (slot[i] & 31));
   }
-  uint32_t mc[LJ], mo[LJ], n_miss;
+  // misses found here take the staging rows after the split's, in column order
+  uint32_t cm[LJ], cmo[LJ], n_cm, mc[LJ], mo[LJ], n_miss;
+#pragma unroll
+  for (int i = 0; i < LJ; ++i) cm[i] = (cand[i] && res[i] == INF) ? 1u : 0u;
+  group_excl_scan<TF_T, LJ>(cm, cmo, gscan, &n_cm);
+#pragma unroll
+  for (int i = 0; i < LJ; ++i)
+    if (cm[i]) {
+      srow[i] = r * k + static_cast<int32_t>(sa + cmo[i]);
+      PW.stage_h[srow[i]] = h[i];
+    }
+  if (t == 0) PW.stage_b[r] = n_cm;
 #pragma unroll
   for (int i = 0; i < LJ; ++i) mc[i] = res[i] == INF ? 1u : 0u;
   group_excl_scan<TF_T, LJ>(mc, mo, gscan, &n_miss);
@@ -444,6 +561,7 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
     if (mc[i]) {
       PW.row_miss_h[static_cast<int64_t>(r) * k + mo[i]] = h[i];
       PW.row_miss_j[static_cast<int64_t>(r) * k + mo[i]] = j;
+      PW.row_miss_s[static_cast<int64_t>(r) * k + mo[i]] = srow[i];
     }
     if (j < k) slot_out[j] = (res[i] >= 0 && res[i] != INF) ? res[i] : -1;
   }
@@ -452,17 +570,25 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
 
 int launch_topk_split(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
                       int32_t max_len, int32_t k, const uint32_t *hist0, void *split_ws,
-                      const SideWork *side, hipStream_t st) {
-  const int n_side = side ? side->n_stats + side->n_gather : 0;
-  if (n_rows == 0 && n_side == 0) return ECHO_OK;
+                      const echo_pool *pool, const PoolFastWs *pw, const int64_t *key_begin,
+                      const int32_t *req_to_host, int32_t step_id, hipStream_t st) {
+  if (n_rows == 0) return ECHO_OK;
   if ((max_len + TS_CH - 1) / TS_CH > 1024) return fail(ECHO_EUNSUPPORTED, "decode top-k: rows longer than 4M tokens");
   SplitWs W = make_split_ws(split_ws, n_rows, max_len, k);
-  const int64_t blocks = static_cast<int64_t>(n_side) + static_cast<int64_t>(W.nch) * n_rows;
+  const int64_t blocks = static_cast<int64_t>(W.nch) * n_rows;
   if (blocks > 0x7FFFFFFF) return fail(ECHO_EUNSUPPORTED, "decode top-k: grid too large");
-  if (n_side > 0)
-    topk_split_kernel<true><<<static_cast<unsigned>(blocks), TS_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W, *side);
-  else
-    topk_split_kernel<false><<<static_cast<unsigned>(blocks), TS_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W, SideWork{});
+  SplitLookup L{};
+  if (pool) {
+    L.P = PoolArgs{pool->gpu_free, pool->gpu_priority, pool->gpu_to_host, pool->host_to_gpu,
+                   pool->indices_buf, pool->status, pool->n_gpu, pool->n_host};
+    L.W = *pw;
+    L.key_begin = key_begin;
+    L.req_to_host = req_to_host;
+    L.step_id = step_id;
+    topk_split_kernel<true><<<static_cast<unsigned>(blocks), TS_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W, L);
+  } else {
+    topk_split_kernel<false><<<static_cast<unsigned>(blocks), TS_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W, L);
+  }
   return check_launch("topk_split");
 }
 
@@ -470,19 +596,25 @@ int launch_topk_finish(const float *scores, int64_t ld, const int32_t *len, int3
                        int32_t max_len, int32_t k, const uint32_t *hist0, void *split_ws,
                        int32_t *idx, const echo_pool *pool, const PoolFastWs *pw,
                        const int64_t *key_begin, const int32_t *req_to_host, int32_t step_id,
-                       int32_t *topk_slot, bool sub_prot, hipStream_t st) {
+                       int32_t *topk_slot, bool early, uint16_t *stage, hipStream_t st) {
   if (n_rows == 0) return ECHO_OK;
   SplitWs W = make_split_ws(split_ws, n_rows, max_len, k);
   PoolArgs P{};
   PoolFastWs PW{};
+  StageArgs SA{nullptr, nullptr};
+  int extra = 0;
   if (pool) {
     P = PoolArgs{pool->gpu_free, pool->gpu_priority, pool->gpu_to_host, pool->host_to_gpu,
                  pool->indices_buf, pool->status, pool->n_gpu, pool->n_host};
     PW = *pw;
+    if (early && stage) {
+      SA = StageArgs{pool->host_kv, stage};
+      extra = n_rows * ((k + 127) / 128);
+    }
   }
-  topk_finish_kernel<<<n_rows, TF_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W, idx, P, PW,
-                                              key_begin, req_to_host, step_id, topk_slot,
-                                              sub_prot && pool != nullptr);
+  topk_finish_kernel<<<n_rows + extra, TF_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W, idx, P, PW,
+                                                      key_begin, req_to_host, step_id, topk_slot,
+                                                      pool != nullptr, early && pool != nullptr, n_rows, SA);
   return check_launch("topk_finish");
 }
 
