@@ -113,14 +113,14 @@ int launch_pool_lookup_rows(const echo_pool *pool, const PoolFastWs &W, const in
                             const int64_t *key_begin, const int32_t *req_to_host, int64_t n_k,
                             int32_t n_rows, int32_t k, int32_t step_id, int32_t *topk_slot,
                             hipStream_t st);
-// Missed rows copied into a staging area by workgroups riding along in the eviction launch.
+// Missed rows copied into a staging area by workgroups riding along in the eviction launches.
 struct StageArgs {
   const uint16_t *host_kv;
   uint16_t *stage;            // [n_rows * k][ROW]; NULL: no staging
 };
-// stage (optional): evict-1 also reads the misses the top-k finish found (staging rows
-// r*k + [stage_a[r], stage_a[r] + stage_b[r])) into the staging area; the caller then runs
-// launch_recall_scatter.
+// stage (optional): evict-1 and evict-2 also read their shares of the staging rows (the
+// stage_cut_f / stage_cut_e split of r*k + [0, stage_a[r] + stage_b[r])) from host memory;
+// the caller then runs launch_recall_scatter.
 int launch_pool_evict(const echo_pool *pool, const PoolFastWs &W, const int32_t *idx, int32_t n_rows,
                       int32_t k, int32_t step_id, int32_t *topk_slot, int32_t *miss_host,
                       int32_t *miss_slot, int32_t *n_miss, uint16_t *stage, hipStream_t st);

@@ -259,6 +259,16 @@ ECHO_DEV bool side_work(const SideWork &S, int b, uint32_t *lds) {
 
 
 // ---------------------------------------------------------------- recall staging
+// The host reads of a request's misses are spread over three launches so that the link works
+// through all of them: the top-k finish launch reads the first STAGE_F16/16 of the misses the
+// split found (rows [0, stage_cut_f)), evict-1 reads up to STAGE_E16/16 of all the request's
+// misses (rows [stage_cut_f, stage_cut_e)), evict-2 the rest.
+constexpr int STAGE_F16 = 12, STAGE_E16 = 14;
+ECHO_DEV int32_t stage_cut_f(int32_t a) { return (a * STAGE_F16 + 15) / 16; }
+ECHO_DEV int32_t stage_cut_e(int32_t a, int32_t total) {
+  return max(stage_cut_f(a), min(total, (total * STAGE_E16 + 15) / 16));
+}
+
 // Copies staging rows r*k + i, i in [i0, i0 + ROWS) and in [lo, hi), from host memory:
 // stage[r*k + i] = host_kv[stage_h[r*k + i]] (NT threads, ROWS * 72 / NT sixteen-byte loads
 // each, all in flight before the first store).

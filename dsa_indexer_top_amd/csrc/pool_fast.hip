@@ -225,11 +225,11 @@ __global__ __launch_bounds__(PF_T) void pool_evict1_kernel(PoolArgs P, PoolFastW
   __shared__ uint32_t tmp[48];
   __shared__ uint32_t gscan[4 * (PF_T / 64) + PF_T / 64 + 2];
   if (static_cast<int>(blockIdx.x) >= n_rows + W.n_chunks) {
-    // recall staging of the misses the top-k finish found, 32 staging rows per block
+    // recall staging, the middle share of every request's misses, 32 staging rows per block
     const int u = blockIdx.x - n_rows - W.n_chunks, per = (k + 31) / 32, r = u / per;
-    const int32_t lo = static_cast<int32_t>(W.stage_a[r]);
-    stage_rows<PF_T, 32>(SA.host_kv, SA.stage, W.stage_h, P.status, k, P.n_host, r,
-                         lo + (u % per) * 32, lo, lo + static_cast<int32_t>(W.stage_b[r]));
+    const int32_t a = static_cast<int32_t>(W.stage_a[r]), tot = a + static_cast<int32_t>(W.stage_b[r]);
+    const int32_t lo = stage_cut_f(a), hi = stage_cut_e(a, tot);
+    stage_rows<PF_T, 32>(SA.host_kv, SA.stage, W.stage_h, P.status, k, P.n_host, r, lo + (u % per) * 32, lo, hi);
     return;
   }
   if (static_cast<int>(blockIdx.x) < n_rows) {
@@ -361,7 +361,8 @@ struct CandView {
 __global__ __launch_bounds__(PF_RES_T) void pool_evict2_kernel(
     PoolArgs P, PoolFastWs W, int32_t n_rows, int32_t k, int32_t step_id,
     int32_t *__restrict__ miss_host, int32_t *__restrict__ miss_slot, int32_t *__restrict__ topk_slot,
-    int32_t *__restrict__ n_miss_out, const int32_t *__restrict__ idx) {
+    int32_t *__restrict__ n_miss_out, const int32_t *__restrict__ idx, int32_t entry_blocks,
+    StageArgs SA) {
   __shared__ uint32_t tmp[48];
   __shared__ uint64_t cl[PF_CAP];
   __shared__ uint32_t hist[2048];
@@ -370,6 +371,15 @@ __global__ __launch_bounds__(PF_RES_T) void pool_evict2_kernel(
   const int t = threadIdx.x;
   const int32_t n_chunks = W.n_chunks;
   const int64_t n_ent = static_cast<int64_t>(n_rows) * k;
+  if (static_cast<int>(blockIdx.x) >= n_chunks + entry_blocks) {
+    // recall staging, the last share of every request's misses, 128 staging rows per block
+    const int u = blockIdx.x - n_chunks - entry_blocks, per = (k + 127) / 128, r = u / per;
+    const int32_t a = static_cast<int32_t>(W.stage_a[r]), tot = a + static_cast<int32_t>(W.stage_b[r]);
+    const int32_t lo = stage_cut_e(a, tot);
+    stage_rows<PF_RES_T, 128>(SA.host_kv, SA.stage, W.stage_h, P.status, k, P.n_host, r,
+                              lo + (u % per) * 128, lo, tot);
+    return;
+  }
   if (static_cast<int>(blockIdx.x) >= n_chunks) {
     // ---- entry workgroups: stamp hits, pad the fixed-length lists
     const StepState st = step_read(W);
@@ -533,14 +543,15 @@ int launch_pool_evict(const echo_pool *pool, const PoolFastWs &W, const int32_t 
   if (W.n_chunks > 1024) return fail(ECHO_EUNSUPPORTED, "pool: more than 4M slots");
   PoolArgs P{pool->gpu_free, pool->gpu_priority, pool->gpu_to_host, pool->host_to_gpu,
              pool->indices_buf, pool->status, pool->n_gpu, pool->n_host};
-  // with a staging area, evict-1 also reads the misses the top-k finish found from host memory
+  // with a staging area, both launches also read shares of the misses from host memory
   StageArgs SA{pool->host_kv, stage};
   const int s1 = stage ? n_rows * ((k + 31) / 32) : 0;
+  const int s2 = stage ? n_rows * ((k + 127) / 128) : 0;
   pool_evict1_kernel<<<n_rows + W.n_chunks + s1, PF_T, 0, st>>>(P, W, n_rows, k, step_id, miss_host, SA);
   const int64_t n_ent = static_cast<int64_t>(n_rows) * k;
   const int entry_blocks = static_cast<int>(std::max<int64_t>(1, (n_ent + PF_RES_T - 1) / PF_RES_T));
-  pool_evict2_kernel<<<W.n_chunks + entry_blocks, PF_RES_T, 0, st>>>(
-      P, W, n_rows, k, step_id, miss_host, miss_slot, topk_slot, n_miss, idx);
+  pool_evict2_kernel<<<W.n_chunks + entry_blocks + s2, PF_RES_T, 0, st>>>(
+      P, W, n_rows, k, step_id, miss_host, miss_slot, topk_slot, n_miss, idx, entry_blocks, SA);
   return check_launch("pool_evict");
 }
 

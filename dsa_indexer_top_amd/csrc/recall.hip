@@ -74,46 +74,61 @@ int launch_recall_gather(const echo_pool *pool, const int32_t *miss_host, const 
   return check_launch("recall_gather");
 }
 
-__global__ __launch_bounds__(RC_THREADS) void recall_scatter_kernel(
+// Scatter: 64 threads move 8 staged rows; the count and the block's list entries are read
+// together, then the staged rows and the duplicate check, then the stores.
+constexpr int SC_THREADS = 64;
+constexpr int SC_ROWS = 8;
+constexpr int SC_PER = SC_ROWS * RC_UNITS_PER_ROW / SC_THREADS;   // 9
+
+__global__ __launch_bounds__(SC_THREADS) void recall_scatter_kernel(
     const uint16_t *__restrict__ stage, uint16_t *__restrict__ gpu_kv,
     const int32_t *__restrict__ miss_host, const int32_t *__restrict__ miss_slot,
     const int32_t *__restrict__ miss_stage, const int32_t *__restrict__ n_miss_p, int32_t max_miss,
     int32_t *__restrict__ status, const int32_t *__restrict__ host_to_gpu, int32_t n_host,
     int32_t n_gpu) {
-  if (*(volatile const int32_t *)status) return;
+  const int32_t r0 = blockIdx.x * SC_ROWS;
+  const int32_t st = *(volatile const int32_t *)status;
   const int32_t n = min(*n_miss_p, max_miss);
+  int32_t h[SC_PER], s[SC_PER], g[SC_PER];
+#pragma unroll
+  for (int m = 0; m < SC_PER; ++m) {
+    const int32_t row = r0 + (threadIdx.x + m * SC_THREADS) / RC_UNITS_PER_ROW;
+    const bool in = row < max_miss;
+    h[m] = in ? miss_host[row] : -1;
+    s[m] = in ? miss_slot[row] : -1;
+    g[m] = in ? miss_stage[row] : -1;
+  }
+  if (st != 0 || r0 >= n) return;
   const v4i *src = reinterpret_cast<const v4i *>(stage);
   v4i *dst = reinterpret_cast<v4i *>(gpu_kv);
-  for (int32_t r0 = blockIdx.x * RC_ROWS; r0 < n; r0 += gridDim.x * RC_ROWS) {
-    v4i v[RC_PER_THREAD];
-    int64_t d_off[RC_PER_THREAD];
+  v4i v[SC_PER];
+  int64_t d_off[SC_PER];
+  bool dup = false;
 #pragma unroll
-    for (int m = 0; m < RC_PER_THREAD; ++m) {
-      const int u = threadIdx.x + m * RC_THREADS;
-      const int32_t row = r0 + u / RC_UNITS_PER_ROW;
-      const int part = u % RC_UNITS_PER_ROW;
-      d_off[m] = -1;
-      if (row < n) {
-        const int32_t h = miss_host[row], s = miss_slot[row];
-        if (h >= 0 && h < n_host && s >= 0 && s < n_gpu) {
-          v[m] = src[static_cast<int64_t>(miss_stage[row]) * RC_UNITS_PER_ROW + part];
-          d_off[m] = static_cast<int64_t>(s) * RC_UNITS_PER_ROW + part;
-          if (part == 0 && host_to_gpu[h] != s) atomicOr(status, ECHO_ST_DUP_HOST);
-        }
-      }
+  for (int m = 0; m < SC_PER; ++m) {
+    const int u = threadIdx.x + m * SC_THREADS;
+    const int32_t row = r0 + u / RC_UNITS_PER_ROW;
+    const int part = u % RC_UNITS_PER_ROW;
+    d_off[m] = -1;
+    if (row < n && h[m] >= 0 && h[m] < n_host && s[m] >= 0 && s[m] < n_gpu && g[m] >= 0) {
+      v[m] = src[static_cast<int64_t>(g[m]) * RC_UNITS_PER_ROW + part];
+      d_off[m] = static_cast<int64_t>(s[m]) * RC_UNITS_PER_ROW + part;
+      // two misses sharing a host index leave the map pointing at only one of their slots
+      if (part == 0 && host_to_gpu[h[m]] != s[m]) dup = true;
     }
-#pragma unroll
-    for (int m = 0; m < RC_PER_THREAD; ++m)
-      if (d_off[m] >= 0) dst[d_off[m]] = v[m];
   }
+  if (dup) atomicOr(status, ECHO_ST_DUP_HOST);
+#pragma unroll
+  for (int m = 0; m < SC_PER; ++m)
+    if (d_off[m] >= 0) dst[d_off[m]] = v[m];
 }
 
 int launch_recall_scatter(const echo_pool *pool, const PoolFastWs &W, const int32_t *miss_host,
                           const int32_t *miss_slot, const int32_t *n_miss, int32_t max_miss,
                           const uint16_t *stage, hipStream_t st) {
   if (max_miss <= 0) return ECHO_OK;
-  const int blocks = std::min(2048, (max_miss + RC_ROWS - 1) / RC_ROWS);
-  recall_scatter_kernel<<<blocks, RC_THREADS, 0, st>>>(stage, pool->gpu_kv, miss_host, miss_slot, W.miss_stage,
+  const int blocks = (max_miss + SC_ROWS - 1) / SC_ROWS;
+  recall_scatter_kernel<<<blocks, SC_THREADS, 0, st>>>(stage, pool->gpu_kv, miss_host, miss_slot, W.miss_stage,
                                                        n_miss, max_miss, pool->status, pool->host_to_gpu,
                                                        pool->n_host, pool->n_gpu);
   return check_launch("recall_scatter");

@@ -279,10 +279,11 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
     const int32_t *__restrict__ req_to_host, int32_t step_id, int32_t *__restrict__ topk_slot,
     bool sub_prot, bool early, int32_t n_rows, StageArgs SA) {
   if (static_cast<int>(blockIdx.x) >= n_rows) {
-    // staging of the misses the split's early lookup found: rows r*k + [0, stage_a[r])
+    // staging of (most of) the misses the split's early lookup found
     const int u = blockIdx.x - n_rows, per = (k + 127) / 128, rr = u / per;
+    const int32_t hi = stage_cut_f(static_cast<int32_t>(PW.stage_a[rr]));
     stage_rows<TF_T, 128>(SA.host_kv, SA.stage, PW.stage_h, P.status, k, P.n_host, rr,
-                          (u % per) * 128, 0, static_cast<int32_t>(PW.stage_a[rr]));
+                          (u % per) * 128, 0, hi);
     return;
   }
   __shared__ uint32_t tmp[48];
