@@ -1,0 +1,160 @@
+"""Host-side logic of the C ABI, exercised without a GPU: every call here is rejected by its
+argument checks, or is a pure size query, before the library touches the HIP runtime.
+
+Checked: the documented error codes and the thread-local error text, the workspace-size
+queries (monotone in the sizes they depend on, zero for invalid sizes, large enough for the
+decode step's staging rows), and the pool metadata footprint against the oracle's formula
+(the ECHO page's 4 N_H + 13 N_G, §5.1)."""
+
+import ctypes as C
+import os
+import threading
+
+import pytest
+
+from dsa_indexer_top_amd import binding as B
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="library not built")
+
+FAKE = C.c_void_p(0x1000)      # never dereferenced: every call below fails before any access
+
+
+def _err():
+    return B.lib().echo_last_error().decode()
+
+
+def _decode_args(**kw):
+    a = B.DecodeArgs(FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 8, 65536, 2048, 7, 0, 4, 4096,
+                     95.0, 2048, 1024)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _pool(n_gpu=1024, n_host=4096):
+    return B.Pool(n_gpu, n_host, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def _out():
+    return B.DecodeOut(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def test_index_scores_argument_errors():
+    L = B.lib()
+    assert L.echo_index_scores(FAKE, FAKE, FAKE, None, FAKE, FAKE, -1, 16, FAKE, 16, None) == B.ECHO_EINVAL
+    assert "negative" in _err()
+    assert L.echo_index_scores(FAKE, FAKE, FAKE, None, FAKE, FAKE, 1, 16, FAKE, 8, None) == B.ECHO_EINVAL
+    assert "ld" in _err()
+    assert L.echo_index_scores(FAKE, FAKE, FAKE, None, FAKE, FAKE, 70000, 16, FAKE, 16, None) == B.ECHO_EUNSUPPORTED
+    assert L.echo_index_scores(None, FAKE, FAKE, None, FAKE, FAKE, 1, 16, FAKE, 16, None) == B.ECHO_EINVAL
+    assert "NULL" in _err()
+
+
+def test_prefill_and_topk_argument_errors():
+    L = B.lib()
+    assert L.echo_index_scores_prefill(FAKE, FAKE, FAKE, -1, 8, 0, FAKE, 8, None) == B.ECHO_EINVAL
+    assert L.echo_index_scores_prefill(FAKE, FAKE, FAKE, 8, 8, 0, FAKE, 4, None) == B.ECHO_EINVAL
+    assert L.echo_index_scores_prefill(None, FAKE, FAKE, 8, 8, 0, FAKE, 8, None) == B.ECHO_EINVAL
+    for k in (0, 4097):
+        assert L.echo_topk(FAKE, 64, FAKE, 1, 64, k, FAKE, None, 0, None) == B.ECHO_EUNSUPPORTED
+        assert "outside" in _err()
+    assert L.echo_topk(FAKE, 32, FAKE, 1, 64, 8, FAKE, None, 0, None) == B.ECHO_EINVAL
+    assert L.echo_topk(None, 64, FAKE, 1, 64, 8, FAKE, None, 0, None) == B.ECHO_EINVAL
+
+
+def test_pool_entry_point_errors():
+    L = B.lib()
+    none = C.POINTER(B.Pool)()
+    args = (FAKE, FAKE, FAKE, 4096, 1, 8, 3, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
+    assert L.echo_pool_lookup_alloc(none, *args) == B.ECHO_EINVAL
+    big = _pool(n_gpu=(1 << 22) + 1)
+    assert L.echo_pool_lookup_alloc(C.byref(big), *args) == B.ECHO_EUNSUPPORTED
+    p = _pool()
+    bad_k = (FAKE, FAKE, FAKE, 4096, 1, 5000, 3, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
+    assert L.echo_pool_lookup_alloc(C.byref(p), *bad_k) == B.ECHO_EINVAL
+    assert L.echo_recall(none, FAKE, FAKE, FAKE, 8, B.RECALL_GATHER, None) == B.ECHO_EINVAL
+    assert L.echo_recall(C.byref(p), FAKE, FAKE, FAKE, -1, B.RECALL_GATHER, None) == B.ECHO_EINVAL
+    assert L.echo_recall(C.byref(p), FAKE, FAKE, FAKE, 8, 7, None) == B.ECHO_EINVAL
+    assert "mode" in _err()
+    assert L.echo_status_clear(None, None) == B.ECHO_EINVAL
+    assert L.echo_pool_init(none, None) == B.ECHO_EINVAL
+
+
+def test_decode_select_argument_errors():
+    L = B.lib()
+    p, o = _pool(), _out()
+    cases = [
+        (dict(n_rows=0), B.ECHO_EUNSUPPORTED),
+        (dict(n_rows=70000), B.ECHO_EUNSUPPORTED),
+        (dict(topk=0), B.ECHO_EUNSUPPORTED),
+        (dict(topk=4097), B.ECHO_EUNSUPPORTED),
+        (dict(max_key_len=-1), B.ECHO_EINVAL),
+        (dict(q=None), B.ECHO_EINVAL),
+        (dict(prefetch=1, n_chunks=0), B.ECHO_EUNSUPPORTED),
+        (dict(prefetch=1, n_chunks=17), B.ECHO_EUNSUPPORTED),
+        (dict(prefetch=1, n_sample=1000), B.ECHO_EUNSUPPORTED),
+        (dict(prefetch=1, percentile=0.0), B.ECHO_EINVAL),
+        (dict(prefetch=1, cap=0), B.ECHO_EINVAL),
+    ]
+    for kw, code in cases:
+        a = _decode_args(**kw)
+        assert L.echo_decode_select(C.byref(a), C.byref(p), C.byref(o), FAKE, 1 << 30, None, None) == code, kw
+    a = _decode_args()
+    short = L.echo_decode_workspace_bytes(C.byref(a), p.n_gpu) - 1
+    assert L.echo_decode_select(C.byref(a), C.byref(p), C.byref(o), FAKE, short, None, None) == B.ECHO_EWORKSPACE
+    assert "workspace" in _err()
+    g = C.c_void_p()
+    assert L.echo_graph_capture_decode(C.byref(a), C.byref(p), C.byref(o), FAKE, 1 << 30, None, None,
+                                       None) == B.ECHO_EINVAL
+    assert L.echo_graph_capture_decode(C.byref(a), C.byref(p), C.byref(o), FAKE, 1 << 30, None, None,
+                                       C.byref(g)) == B.ECHO_EINVAL          # NULL main stream
+    assert not g.value
+    assert L.echo_graph_launch(None, None) == B.ECHO_EINVAL
+    assert L.echo_graph_destroy(None) == B.ECHO_OK
+
+
+def test_workspace_sizes():
+    L = B.lib()
+    assert L.echo_pool_workspace_bytes(-1, 8, 8) == 0
+    assert L.echo_topk_workspace_bytes(-1, 8) == 0
+    base = L.echo_pool_workspace_bytes(8, 2048, 65536)
+    assert L.echo_pool_workspace_bytes(16, 2048, 65536) > base
+    assert L.echo_pool_workspace_bytes(8, 2048, 1 << 20) > base
+    prev = 0
+    for n_rows, k in [(1, 256), (8, 2048), (32, 2048), (64, 2048)]:
+        a = _decode_args(n_rows=n_rows, topk=k, max_key_len=131072)
+        ws = L.echo_decode_workspace_bytes(C.byref(a), 1 << 20)
+        assert ws >= n_rows * k * 576 * 2          # the staged recall rows fit
+        assert ws > prev
+        prev = ws
+    a = _decode_args()
+    pf = _decode_args(prefetch=1)
+    assert L.echo_decode_workspace_bytes(C.byref(pf), 65536) > L.echo_decode_workspace_bytes(C.byref(a), 65536)
+    assert L.echo_decode_workspace_bytes(C.byref(_decode_args(n_rows=-1)), 65536) == 0
+    assert L.echo_decode_workspace_bytes(C.byref(a), -1) == 0
+
+
+def test_metadata_footprint_matches_oracle():
+    import oracle
+    L = B.lib()
+    for n_host, n_gpu in [(1, 1), (4096, 2048), (524288, 65536), (8388608, 1048576)]:
+        assert L.echo_pool_metadata_bytes(n_host, n_gpu) == oracle.metadata_bytes(n_host, n_gpu)
+
+
+def test_error_text_is_per_thread():
+    L = B.lib()
+    assert L.echo_topk(FAKE, 64, FAKE, 1, 64, 0, FAKE, None, 0, None) == B.ECHO_EUNSUPPORTED
+    here = _err()
+    seen = []
+
+    def other():
+        seen.append(B.lib().echo_last_error().decode())
+        B.lib().echo_index_scores(None, FAKE, FAKE, None, FAKE, FAKE, 1, 16, FAKE, 16, None)
+        seen.append(B.lib().echo_last_error().decode())
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen[0] == ""
+    assert "NULL" in seen[1]
+    assert _err() == here
