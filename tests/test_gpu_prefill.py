@@ -1,5 +1,7 @@
 """GPU parity of the causal prefill indexer (echo_index_scores_prefill) and its per-row top-k
-against the oracle: bit-exact on integer-grid inputs; sampled rows at the full 32768^2 size."""
+against the oracle: bit-exact on integer-grid inputs, within 1e-4 * T (T = the magnitude of all
+terms of a score) on general FP8 inputs and on head weights spread over a wide dynamic range;
+sampled rows at the full 32768^2 size."""
 
 import numpy as np
 import pytest
@@ -10,6 +12,7 @@ from dsa_indexer_top_amd import binding as B, inputs as gen
 from gpu_util import announce, dev, host
 
 pytestmark = pytest.mark.gpu
+TOL = 1e-4
 
 
 def _run(q, w, k, q_pos0=0, ld=None):
@@ -34,6 +37,18 @@ def _check_rows(q, w, k, got, rows, q_pos0=0):
         assert np.isnan(row[lim:]).all(), "row %d wrote past its causal limit" % t
 
 
+def _check_rows_tol(q, w, k, got, rows):
+    n_k = k.shape[0]
+    for t in rows:
+        lim = min(n_k, t + 1)
+        args = (q[t:t + 1], w[t:t + 1], k, None, np.array([0]), np.array([lim]))
+        want, T = oracle.index_scores(*args)[0], oracle.error_scale(*args)[0]
+        err = np.abs(got[t][:lim].astype(np.float64) - want)
+        worst = int(np.argmax(err - TOL * T))
+        assert (err <= TOL * T).all(), "row %d key %d: err %g > %g" % (t, worst, err[worst], TOL * T[worst])
+        assert np.isnan(got[t][lim:]).all(), "row %d wrote past its causal limit" % t
+
+
 @pytest.mark.parametrize("n", [1, 17, 300, 1000])
 def test_prefill_small_exact(n):
     announce("prefill", n)
@@ -48,6 +63,28 @@ def test_prefill_chunk_offset_exact():
     q, w = q_all[1000:1300], w_all[1000:1300]           # a chunk of 300 queries at 1000..1299
     got = host(_run(q, w, k, q_pos0=1000))
     _check_rows(q, w, k, got, range(300), q_pos0=1000)
+
+
+def test_prefill_general_fp8_tolerance():
+    announce("prefill general fp8")
+    q, w, k = gen.make_prefill_inputs(600, grid="normal", seed=81)
+    _check_rows_tol(q, w, k, host(_run(q, w, k)), range(600))
+
+
+def test_prefill_wide_weight_range_tolerance():
+    # Head weights from 2^-40 to 2^40 in magnitude, some queries with zero heads, and in every
+    # other query one key dimension fed only by a head of weight 2^-30, so that the
+    # head-weighted sum of q has one element about 2^-30 times the others.
+    announce("prefill wide weight range")
+    q, w, k = gen.make_prefill_inputs(300, grid="normal", seed=82)
+    rng = np.random.default_rng(83)
+    w = (w * np.exp2(rng.integers(-40, 41, w.shape))).astype(np.float32)
+    w[::3, :32] = 0.0
+    q = q.copy()
+    q[::2, :, 5] = 0
+    q[::2, 0, 5] = 0x38                                   # 1.0
+    w[::2, 0] = np.float32(2.0 ** -30)
+    _check_rows_tol(q, w, k, host(_run(q, w, k)), range(300))
 
 
 def test_prefill_topk_rows_exact():
