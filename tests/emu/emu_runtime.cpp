@@ -5,6 +5,8 @@
 #include <sanitizer/common_interface_defs.h>
 #include <sys/mman.h>
 
+#include <random>
+
 #include "hip_cpu.h"
 
 // x86-64 context switch: saves callee-saved registers on the current stack, stores its stack
@@ -68,6 +70,16 @@ static std::function<void()> *g_body = nullptr;
 static bool g_capturing = false;
 static std::vector<std::function<void()>> g_capture;
 static long long g_launches = 0;
+
+// ECHO_EMU_ORDER=<nonzero seed>: workgroups of a launch run in a seeded random order, and the
+// waves of a workgroup are taken in a fresh random order at every scheduling pass (lanes of a
+// wave stay in ascending order, as their lockstep execution is not modelled), so a result
+// that depends on the order of workgroups or waves shows up as a difference between seeds.
+static const unsigned long g_order_seed = [] {
+  const char *e = getenv("ECHO_EMU_ORDER");
+  return e ? strtoul(e, nullptr, 10) : 0ul;
+}();
+static std::mt19937 g_rng(static_cast<unsigned>(g_order_seed));
 
 Ctx *ctx() { return &g_cur->ctx; }
 
@@ -204,10 +216,15 @@ static void run_block(dim3 grid, dim3 block, dim3 bid) {
     f.state = RUN;
     f.fake = nullptr;
   }
+  const int n_waves = (n + 63) / 64;
+  int worder[MAXT / 64];
+  for (int v = 0; v < n_waves; ++v) worder[v] = v;
   while (g_live > 0) {
     bool progress = false;
-    for (int i = 0; i < n; ++i) {
-      if (g_f[i].state != RUN) continue;
+    if (g_order_seed) std::shuffle(worder, worder + n_waves, g_rng);
+    for (int ii = 0; ii < n; ++ii) {
+      const int i = worder[ii / 64] * 64 + ii % 64;        // waves in (shuffled) order, lanes ascending
+      if (i >= n || g_f[i].state != RUN) continue;
       g_cur = &g_f[i];
       void *fake = nullptr;
       __sanitizer_start_switch_fiber(&fake, g_cur->stack, STACK);
@@ -233,9 +250,12 @@ void launch(dim3 grid, dim3 block, std::function<void()> body) {
   ++g_launches;
   std::function<void()> b = body;
   g_body = &b;
+  std::vector<dim3> blocks;
   for (uint32_t z = 0; z < grid.z; ++z)
     for (uint32_t y = 0; y < grid.y; ++y)
-      for (uint32_t x = 0; x < grid.x; ++x) run_block(grid, block, dim3(x, y, z));
+      for (uint32_t x = 0; x < grid.x; ++x) blocks.push_back(dim3(x, y, z));
+  if (g_order_seed) std::shuffle(blocks.begin(), blocks.end(), g_rng);
+  for (const dim3 &bid : blocks) run_block(grid, block, bid);
   g_body = nullptr;
 }
 

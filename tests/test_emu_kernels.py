@@ -8,6 +8,8 @@ memory and LDS filled with garbage.  This catches, without a GPU:
   * any out-of-bounds access of a kernel (global memory, LDS, host rows);
   * a barrier or wave operation reached by only part of a workgroup or wave;
   * reads of LDS or workspace memory that the step did not write first;
+  * results that depend on the order in which workgroups, or the waves of a workgroup, run
+    (they run in a seeded random order here);
   * any result that differs from the oracle on the tests' own inputs.
 It does not model concurrency between workgroups or memory ordering; those stay with the GPU
 tests.  Skipped when clang's AddressSanitizer runtime is not installed.
@@ -40,7 +42,7 @@ SELECTION = [
 def test_kernels_on_cpu_under_address_sanitizer(tmp_path):
     lib = build_emu.build(out=os.path.join(ROOT, "_build", "emu"))
     env = dict(os.environ)
-    env.update(ECHO_EMU_LIB=lib, LD_PRELOAD=ASAN,
+    env.update(ECHO_EMU_LIB=lib, LD_PRELOAD=ASAN, ECHO_EMU_ORDER="1",
                PYTHONPATH=os.pathsep.join([os.path.join(HERE, "emu"), ROOT]),
                ASAN_OPTIONS="detect_leaks=0:detect_odr_violation=0:alloc_dealloc_mismatch=0:"
                             "detect_stack_use_after_return=0:abort_on_error=1")
