@@ -325,20 +325,30 @@ static void op_dpp(const unsigned char *in, unsigned char *out, size_t, size_t, 
 // of its second; v_permlane16_swap exchanges the odd 16-lane rows of the first with the even
 // rows of the second.  The builtins return {first, second} after the exchange.
 struct SwapIn { unsigned a, b; };
+// ECHO_EMU_SWAP_FLIP (bits 0 / 1) reverses the 16 / 32-lane exchange (first operand's even rows
+// with the second's odd rows; first operand's lower half with the second's upper half), to
+// check code that must not depend on the direction.
+static const int g_swap_flip = [] {
+  const char *e = getenv("ECHO_EMU_SWAP_FLIP");
+  return e ? atoi(e) : 0;
+}();
+
 static void op_swap(const unsigned char *in, unsigned char *out, size_t, size_t, const void *arg) {
   const int which = *static_cast<const int *>(arg);   // 16 or 32
+  const bool flip = (g_swap_flip >> (which == 32 ? 1 : 0)) & 1;
   for (int l = 0; l < 64; ++l) {
     SwapIn s;
     memcpy(&s, in + l * SLOT, sizeof s);
     unsigned na = s.a, nb = s.b;
     SwapIn o;
     if (which == 32) {
-      if (l >= 32) { memcpy(&o, in + (l - 32) * SLOT, sizeof o); na = o.b; }   // upper half of a <- lower half of b
-      else { memcpy(&o, in + (l + 32) * SLOT, sizeof o); nb = o.a; }           // lower half of b <- upper half of a
+      const bool upper = l >= 32;
+      if (upper != flip) { memcpy(&o, in + (upper ? l - 32 : l + 32) * SLOT, sizeof o); na = o.b; }
+      else { memcpy(&o, in + (upper ? l - 32 : l + 32) * SLOT, sizeof o); nb = o.a; }
     } else {
-      const int row = l / 16;
-      if (row & 1) { memcpy(&o, in + (l - 16) * SLOT, sizeof o); na = o.b; }  // odd rows of a <- even rows of b
-      else { memcpy(&o, in + (l + 16) * SLOT, sizeof o); nb = o.a; }          // even rows of b <- odd rows of a
+      const bool odd = (l / 16) & 1;
+      if (odd != flip) { memcpy(&o, in + (odd ? l - 16 : l + 16) * SLOT, sizeof o); na = o.b; }
+      else { memcpy(&o, in + (odd ? l - 16 : l + 16) * SLOT, sizeof o); nb = o.a; }
     }
     const unsigned r[2] = {na, nb};
     memcpy(out + l * SLOT, r, 8);
