@@ -182,9 +182,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefetch", choices=("auto", "on", "off"), default="auto")
-    ap.add_argument("--probe", choices=("score", "copy"), default=None,
-                    help="short program for hardware-counter runs: 20 launches of the scoring "
-                         "kernel on the workload, or 20 device copies of 256 MiB, then exit")
+    ap.add_argument("--probe", choices=("score", "copy", "prefill"), default=None,
+                    help="short program for hardware-counter runs, then exit: 20 launches of the "
+                         "scoring kernel on the workload, 20 device copies of 256 MiB, or 3 causal "
+                         "prefill launches on 32768^2")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this decode path runs on one GPU; --gpus %d is not supported "
@@ -206,6 +207,17 @@ def main():
         return
     cfg = gen.CONFIGS[args.workload]
     prefetch = cfg.prefetch if args.prefetch == "auto" else args.prefetch == "on"
+    if args.probe == "prefill":
+        pc = gen.PREFILL["prefill_32k"]
+        n = pc["n"]
+        q, w, k = gen.make_prefill_inputs(n, seed=pc["seed"])
+        dq, dw, dk = (torch.from_numpy(x).cuda() for x in (q, w, k))
+        sc = torch.empty((n, n), dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            B.index_scores_prefill(dq, dw, dk, sc, ld=n)
+        torch.cuda.synchronize()
+        log("prefill probe: 3 launches of echo_index_scores_prefill on 32768 x 32768")
+        return
     if args.probe == "score":
         inp = gen.make_decode_inputs(cfg)
         dq, dw, dk = (torch.from_numpy(x).cuda() for x in (inp.q, inp.w, inp.k))
