@@ -15,6 +15,7 @@
 // With prefetch, scoring is split into n_chunks token ranges: the launch of range c also
 // gathers range c-1's candidates, and a gather launch for the last range precedes the split.
 #include <algorithm>
+#include <new>
 
 #include "internal.hpp"
 
@@ -220,7 +221,12 @@ extern "C" int echo_graph_capture_decode(const echo_decode_args *a, const echo_p
     (void)hipGraphDestroy(g);
     return fail(ECHO_EHIP, "hipGraphInstantiate: %s", hipGetErrorString(e));
   }
-  echo_graph_s *h = new echo_graph_s;
+  echo_graph_s *h = new (std::nothrow) echo_graph_s;
+  if (!h) {
+    (void)hipGraphExecDestroy(ex);
+    (void)hipGraphDestroy(g);
+    return fail(ECHO_EHIP, "echo_graph_capture_decode: out of host memory");
+  }
   h->graph = g;
   h->exec = ex;
   *graph = h;

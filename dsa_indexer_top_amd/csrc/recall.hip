@@ -17,6 +17,7 @@
 // Memcpy mode (the host-driven baseline): the host waits for the stream, reads the miss list
 // and enqueues one hipMemcpyAsync per row.
 #include <algorithm>
+#include <new>
 #include <vector>
 
 #include "internal.hpp"
@@ -145,7 +146,13 @@ static int recall_memcpy(const echo_pool *pool, const int32_t *miss_host, const 
   if (status) return ECHO_OK;
   n = n < max_miss ? n : max_miss;
   if (n <= 0) return ECHO_OK;
-  std::vector<int32_t> h(n), s(n);
+  std::vector<int32_t> h, s;
+  try {
+    h.resize(n);
+    s.resize(n);
+  } catch (const std::bad_alloc &) {
+    return fail(ECHO_EHIP, "echo_recall(memcpy): out of host memory for %d list entries", n);
+  }
   if ((e = hipMemcpy(h.data(), miss_host, 4 * static_cast<size_t>(n), hipMemcpyDeviceToHost)) != hipSuccess ||
       (e = hipMemcpy(s.data(), miss_slot, 4 * static_cast<size_t>(n), hipMemcpyDeviceToHost)) != hipSuccess)
     return fail(ECHO_EHIP, "echo_recall(memcpy): read lists: %s", hipGetErrorString(e));
