@@ -186,7 +186,10 @@ extern "C" int echo_prefetch_gather(const echo_pool *pool, const int64_t *key_be
                                     const int32_t *cand_cnt, int32_t n_q, int32_t cap,
                                     const int32_t *free_list, int32_t *free_count,
                                     int32_t *n_prefetched, void *stream) {
-  if (!pool || !pool->gpu_kv || !pool->host_kv || !pool->status) return fail(ECHO_EINVAL, "echo_prefetch_gather: NULL pool member");
+  if (!pool || !pool->gpu_kv || !pool->host_kv || !pool->status || !pool->gpu_free || !pool->gpu_priority ||
+      !pool->gpu_to_host || !pool->host_to_gpu)
+    return fail(ECHO_EINVAL, "echo_prefetch_gather: NULL pool member");
+  if (pool->n_gpu < 1 || pool->n_host < 1) return fail(ECHO_EINVAL, "echo_prefetch_gather: empty pool");
   if (n_q < 0 || cap < 0) return fail(ECHO_EINVAL, "echo_prefetch_gather: negative size");
   if (n_q > 0 && cap > 0 && (!key_begin || !req_to_host || !cand || !cand_cnt || !free_list || !free_count || !n_prefetched))
     return fail(ECHO_EINVAL, "echo_prefetch_gather: NULL pointer");

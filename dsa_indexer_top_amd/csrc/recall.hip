@@ -173,8 +173,9 @@ using namespace echo;
 extern "C" int echo_recall(const echo_pool *pool, const int32_t *miss_host,
                            const int32_t *miss_slot, const int32_t *n_miss, int32_t max_miss,
                            int32_t mode, void *stream) {
-  if (!pool || !pool->gpu_kv || !pool->host_kv || !pool->status)
+  if (!pool || !pool->gpu_kv || !pool->host_kv || !pool->status || !pool->host_to_gpu)
     return fail(ECHO_EINVAL, "echo_recall: NULL pool member");
+  if (pool->n_gpu < 1 || pool->n_host < 1) return fail(ECHO_EINVAL, "echo_recall: empty pool");
   if (max_miss < 0) return fail(ECHO_EINVAL, "echo_recall: max_miss < 0");
   if (max_miss > 0 && (!miss_host || !miss_slot || !n_miss)) return fail(ECHO_EINVAL, "echo_recall: NULL list");
   if (mode == ECHO_RECALL_GATHER) return launch_recall_gather(pool, miss_host, miss_slot, n_miss, max_miss, S(stream));

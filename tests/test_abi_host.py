@@ -76,8 +76,20 @@ def test_pool_entry_point_errors():
     assert L.echo_recall(C.byref(p), FAKE, FAKE, FAKE, -1, B.RECALL_GATHER, None) == B.ECHO_EINVAL
     assert L.echo_recall(C.byref(p), FAKE, FAKE, FAKE, 8, 7, None) == B.ECHO_EINVAL
     assert "mode" in _err()
+    for member in ("gpu_kv", "host_kv", "status", "host_to_gpu"):
+        q = _pool()
+        setattr(q, member, None)
+        assert L.echo_recall(C.byref(q), FAKE, FAKE, FAKE, 8, B.RECALL_GATHER, None) == B.ECHO_EINVAL, member
+    assert L.echo_recall(C.byref(_pool(n_host=0)), FAKE, FAKE, FAKE, 8, B.RECALL_GATHER, None) == B.ECHO_EINVAL
     assert L.echo_status_clear(None, None) == B.ECHO_EINVAL
     assert L.echo_pool_init(none, None) == B.ECHO_EINVAL
+    gather = (FAKE, FAKE, FAKE, FAKE, 8, 16, FAKE, FAKE, FAKE, None)
+    for member in ("gpu_free", "gpu_priority", "gpu_to_host", "host_to_gpu", "gpu_kv", "host_kv", "status"):
+        q = _pool()
+        setattr(q, member, None)
+        assert L.echo_prefetch_gather(C.byref(q), *gather) == B.ECHO_EINVAL, member
+    assert L.echo_prefetch_gather(C.byref(_pool(n_gpu=0)), *gather) == B.ECHO_EINVAL
+    assert L.echo_prefetch_begin(C.byref(_pool()), None, FAKE, None) == B.ECHO_EINVAL
 
 
 def test_decode_select_argument_errors():
