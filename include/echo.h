@@ -215,7 +215,8 @@ int echo_pool_lookup_alloc(const echo_pool *pool, const int32_t *idx, const int6
  *   ECHO_RECALL_GATHER: one kernel reads the rows straight from mapped pinned host memory.
  *   ECHO_RECALL_MEMCPY: synchronises `stream`, reads n_miss and the lists to the host and
  *     issues one hipMemcpyAsync (host -> device) per row on `stream`; returns after enqueueing.
- * Skipped entirely when the pool status word is nonzero.
+ * Skipped entirely when the pool status word is nonzero.  ECHO_EINVAL for a pool with a
+ * NULL gpu_kv, host_kv, host_to_gpu or status, or with n_gpu or n_host below 1.
  */
 int echo_recall(const echo_pool *pool, const int32_t *miss_host, const int32_t *miss_slot,
                 const int32_t *n_miss, int32_t max_miss, int32_t mode, void *stream);
@@ -228,7 +229,8 @@ int echo_recall(const echo_pool *pool, const int32_t *miss_host, const int32_t *
  * cand_cnt), gives each a slot from free_list (counter free_count[1]; never evicts: candidates
  * beyond the free slots are dropped), sets both maps, gives the slot priority 0 (first to go
  * when space is short later), copies the row from host memory, and adds the number of rows it
- * moved to *n_prefetched.  Skipped when the pool status word is nonzero.
+ * moved to *n_prefetched.  Skipped when the pool status word is nonzero.  Both reject a pool
+ * with NULL members it uses or n_gpu (n_host) below 1 with ECHO_EINVAL.
  */
 int echo_prefetch_begin(const echo_pool *pool, int32_t *free_list, int32_t *free_count,
                         void *stream);
