@@ -27,6 +27,8 @@
 #define __forceinline__ inline
 #define __shared__ static
 #define __launch_bounds__(...)
+#define amdgpu_waves_per_eu(...)              // occupancy attributes mean nothing on the host
+#define amdgpu_flat_work_group_size(...)
 #define __align__(n) __attribute__((aligned(n)))
 
 struct dim3 {
