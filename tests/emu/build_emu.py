@@ -6,7 +6,7 @@ args)` becomes `emu::launch_kernel(dim3(grid), dim3(block), &kernel, args)`, and
 __shared__ object is registered for poisoning.  clang compiles the result as C++17 with
 -fsanitize=address into one shared library that exports the same C ABI as the GPU build.
 
-    python tests/emu/build_emu.py [CSRC_DIR INCLUDE_DIR OUT_DIR]
+    python tests/emu/build_emu.py [--thread] [CSRC_DIR INCLUDE_DIR OUT_DIR]
 
 Test infrastructure only: nothing in the package loads this library.
 """
@@ -25,15 +25,19 @@ DEFAULT_OUT = os.path.join(ROOT, "_build", "emu")
 LIB_NAME = "libecho_emu.so"
 
 
-def asan_runtime():
-    """Path of clang's shared AddressSanitizer runtime, or None."""
+def sanitizer_runtime(name="asan"):
+    """Path of clang's shared sanitizer runtime ("asan" or "tsan"), or None."""
     try:
         d = subprocess.run([CLANG, "-print-resource-dir"], capture_output=True, text=True,
                            check=True).stdout.strip()
     except (OSError, subprocess.CalledProcessError):
         return None
-    p = os.path.join(d, "lib", "linux", "libclang_rt.asan-x86_64.so")
+    p = os.path.join(d, "lib", "linux", "libclang_rt.%s-x86_64.so" % name)
     return p if os.path.exists(p) else None
+
+
+def asan_runtime():
+    return sanitizer_runtime("asan")
 
 
 def _match(s, i, open_c, close_c):
@@ -115,7 +119,9 @@ def transform(src):
     return "".join(out)
 
 
-def build(csrc=None, include=None, out=DEFAULT_OUT):
+def build(csrc=None, include=None, out=DEFAULT_OUT, sanitizer="address"):
+    """sanitizer: "address" (every source) or "thread" (the library's sources; the fiber
+    runtime itself stays uninstrumented and reports the fibers to ThreadSanitizer)."""
     csrc = os.path.abspath(csrc or os.path.join(ROOT, "dsa_indexer_top_amd", "csrc"))
     include = os.path.abspath(include or os.path.join(ROOT, "include"))
     out = os.path.abspath(out)
@@ -135,13 +141,22 @@ def build(csrc=None, include=None, out=DEFAULT_OUT):
             fh.write(s)
         if f.endswith((".hip", ".cpp")):
             units.append(os.path.join(cdir, f))
-    units.append(os.path.join(HERE, "emu_runtime.cpp"))
-    flags = ["-std=c++17", "-g", "-O1", "-fPIC", "-fsanitize=address", "-fno-omit-frame-pointer",
-             "-Wno-unused-variable", "-I", cdir]
+    runtime = os.path.join(HERE, "emu_runtime.cpp")
+    units.append(runtime)
+    flags = ["-std=c++17", "-g", "-O1", "-fPIC", "-fno-omit-frame-pointer", "-Wno-unused-variable",
+             "-I", cdir]
+    if sanitizer == "address":
+        kflags, rflags = ["-fsanitize=address"], ["-fsanitize=address", "-DEMU_ASAN"]
+    elif sanitizer == "thread":
+        kflags, rflags = ["-fsanitize=thread"], ["-DEMU_TSAN"]
+    else:
+        raise ValueError(sanitizer)
 
     def compile_one(u):
         o = os.path.join(out, os.path.basename(u) + ".o")
-        r = subprocess.run([CLANG, "-x", "c++", *flags, "-c", u, "-o", o], capture_output=True, text=True)
+        extra = rflags if u == runtime else kflags
+        r = subprocess.run([CLANG, "-x", "c++", *flags, *extra, "-c", u, "-o", o], capture_output=True,
+                           text=True)
         if r.returncode:
             raise RuntimeError("emulation build failed for %s:\n%s" % (u, r.stderr[-6000:]))
         return o
@@ -149,7 +164,7 @@ def build(csrc=None, include=None, out=DEFAULT_OUT):
     with cf.ThreadPoolExecutor(max_workers=min(8, len(units))) as ex:
         objs = list(ex.map(compile_one, units))
     lib = os.path.join(out, LIB_NAME)
-    r = subprocess.run([CLANG, "-shared", "-fsanitize=address", "-shared-libasan", "-o", lib, *objs],
+    r = subprocess.run([CLANG, "-shared", "-fsanitize=" + sanitizer, "-shared-libsan", "-o", lib, *objs],
                        capture_output=True, text=True)
     if r.returncode:
         raise RuntimeError("emulation link failed:\n%s" % r.stderr[-4000:])
@@ -158,4 +173,7 @@ def build(csrc=None, include=None, out=DEFAULT_OUT):
 
 if __name__ == "__main__":
     a = sys.argv[1:]
-    print(build(*a) if a else build())
+    san = "address"
+    if a and a[0] in ("--thread", "--address"):
+        san, a = a[0][2:], a[1:]
+    print(build(*a, sanitizer=san))

@@ -4,6 +4,9 @@
 // every workgroup start, and stream capture into replayable graphs.  Test infrastructure only.
 #include <sanitizer/common_interface_defs.h>
 #include <sys/mman.h>
+#if defined(EMU_TSAN)
+#include <sanitizer/tsan_interface.h>
+#endif
 
 #include <random>
 
@@ -83,6 +86,32 @@ static std::mt19937 g_rng(static_cast<unsigned>(g_order_seed));
 
 Ctx *ctx() { return &g_cur->ctx; }
 
+// ---- sanitizer views of the fibers
+// AddressSanitizer is told about every stack switch.  ThreadSanitizer sees one fiber per wave
+// (its lanes run in lockstep on the GPU, so they are one thread of execution): switches carry
+// no ordering of their own, workgroup barriers are release/acquire edges between the waves,
+// and the start and end of a workgroup are ordered with the host thread, so the check finds
+// memory shared by waves of one workgroup without a barrier in between.
+#if defined(EMU_TSAN)
+static void *g_tsan_host = nullptr;
+static void *g_tsan_wave[MAXT / 64];
+static char g_tsan_barrier;
+static void tsan_enter(int wave, bool sync) {
+  __tsan_switch_to_fiber(g_tsan_wave[wave], sync ? 0 : __tsan_switch_to_fiber_no_sync);
+}
+static void tsan_leave(bool sync) { __tsan_switch_to_fiber(g_tsan_host, sync ? 0 : __tsan_switch_to_fiber_no_sync); }
+#else
+static void tsan_enter(int, bool) {}
+static void tsan_leave(bool) {}
+#endif
+#if defined(EMU_ASAN)
+static void asan_start(void **fake, const void *bottom, size_t size) { __sanitizer_start_switch_fiber(fake, bottom, size); }
+static void asan_finish(void *fake, const void **bottom, size_t *size) { __sanitizer_finish_switch_fiber(fake, bottom, size); }
+#else
+static void asan_start(void **, const void *, size_t) {}
+static void asan_finish(void *, const void **, size_t *) {}
+#endif
+
 [[noreturn]] static void die(const char *msg) {
   fprintf(stderr, "EMU ERROR: %s (workgroup %u,%u thread %u)\n", msg, g_cur ? g_cur->ctx.bid.x : 0,
           g_cur ? g_cur->ctx.bid.y : 0, g_cur ? g_cur->ctx.tid.x : 0);
@@ -118,9 +147,10 @@ static void poison_lds() {
 }
 
 static void to_sched() {
-  __sanitizer_start_switch_fiber(&g_cur->fake, g_sched_bottom, g_sched_size);
+  asan_start(&g_cur->fake, g_sched_bottom, g_sched_size);
+  tsan_leave(false);
   emu_switch(&g_cur->sp, g_sched_sp);
-  __sanitizer_finish_switch_fiber(g_cur->fake, nullptr, nullptr);
+  asan_finish(g_cur->fake, nullptr, nullptr);
 }
 
 static void release_barrier_if_complete() {
@@ -132,7 +162,7 @@ static void release_barrier_if_complete() {
 }
 
 static void fiber_entry() {
-  __sanitizer_finish_switch_fiber(nullptr, &g_sched_bottom, &g_sched_size);
+  asan_finish(nullptr, &g_sched_bottom, &g_sched_size);
   (*g_body)();
   g_cur->state = DONE;
   --g_live;
@@ -140,7 +170,8 @@ static void fiber_entry() {
   Wave &w = g_w[g_cur->ctx.wave];
   if (w.arrived > 0) die("a lane ended while the rest of its wave waits in a wave op");
   release_barrier_if_complete();
-  __sanitizer_start_switch_fiber(nullptr, g_sched_bottom, g_sched_size);
+  asan_start(nullptr, g_sched_bottom, g_sched_size);
+  tsan_leave(true);                       // the host thread continues after the whole workgroup
   void *dead;
   emu_switch(&dead, g_sched_sp);
   abort();
@@ -148,10 +179,16 @@ static void fiber_entry() {
 
 void barrier() {
   if (g_w[g_cur->ctx.wave].arrived > 0) die("barrier while lanes of this wave wait in a wave op");
+#if defined(EMU_TSAN)
+  __tsan_release(&g_tsan_barrier);
+#endif
   g_cur->state = AT_BARRIER;
   ++g_bar;
   release_barrier_if_complete();
   if (g_cur->state == AT_BARRIER) to_sched();
+#if defined(EMU_TSAN)
+  __tsan_acquire(&g_tsan_barrier);
+#endif
 }
 
 static int live_lanes(int wave) {
@@ -217,6 +254,12 @@ static void run_block(dim3 grid, dim3 block, dim3 bid) {
     f.fake = nullptr;
   }
   const int n_waves = (n + 63) / 64;
+#if defined(EMU_TSAN)
+  g_tsan_host = __tsan_get_current_fiber();
+  for (int v = 0; v < n_waves; ++v) g_tsan_wave[v] = __tsan_create_fiber(0);
+#endif
+  bool started[MAXT];
+  for (int i = 0; i < n; ++i) started[i] = false;
   int worder[MAXT / 64];
   for (int v = 0; v < n_waves; ++v) worder[v] = v;
   while (g_live > 0) {
@@ -227,9 +270,11 @@ static void run_block(dim3 grid, dim3 block, dim3 bid) {
       if (i >= n || g_f[i].state != RUN) continue;
       g_cur = &g_f[i];
       void *fake = nullptr;
-      __sanitizer_start_switch_fiber(&fake, g_cur->stack, STACK);
+      asan_start(&fake, g_cur->stack, STACK);
+      tsan_enter(g_cur->ctx.wave, !started[i]);   // the workgroup starts after the host's setup
+      started[i] = true;
       emu_switch(&g_sched_sp, g_cur->sp);
-      __sanitizer_finish_switch_fiber(fake, nullptr, nullptr);
+      asan_finish(fake, nullptr, nullptr);
       progress = true;
     }
     if (!progress && g_live > 0) {
@@ -239,6 +284,9 @@ static void run_block(dim3 grid, dim3 block, dim3 bid) {
       if (!any) { g_cur = &g_f[0]; die("deadlock: no runnable thread (barrier / wave-op mismatch)"); }
     }
   }
+#if defined(EMU_TSAN)
+  for (int v = 0; v < n_waves; ++v) __tsan_destroy_fiber(g_tsan_wave[v]);
+#endif
   g_cur = nullptr;
 }
 

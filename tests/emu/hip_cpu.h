@@ -84,10 +84,11 @@ inline long long max(long long a, long long b) { return a > b ? a : b; }
 inline long min(long a, long b) { return a < b ? a : b; }
 inline long max(long a, long b) { return a > b ? a : b; }
 
-// atomics: fibers never interleave inside one, so plain read-modify-write is exact
-template <typename T> inline T atomicAdd(T *p, T v) { T o = *p; *p = o + v; return o; }
-template <typename T> inline T atomicSub(T *p, T v) { T o = *p; *p = o - v; return o; }
-template <typename T> inline T atomicOr(T *p, T v) { T o = *p; *p = o | v; return o; }
+// atomics: relaxed read-modify-writes (device-scope relaxed atomics on the GPU), visible as
+// atomics to ThreadSanitizer
+template <typename T> inline T atomicAdd(T *p, T v) { return __atomic_fetch_add(p, v, __ATOMIC_RELAXED); }
+template <typename T> inline T atomicSub(T *p, T v) { return __atomic_fetch_sub(p, v, __ATOMIC_RELAXED); }
+template <typename T> inline T atomicOr(T *p, T v) { return __atomic_fetch_or(p, v, __ATOMIC_RELAXED); }
 inline unsigned atomicAdd(unsigned *p, int v) { return atomicAdd<unsigned>(p, static_cast<unsigned>(v)); }
 inline int atomicAdd(int *p, unsigned v) { return atomicAdd<int>(p, static_cast<int>(v)); }
 inline unsigned atomicSub(unsigned *p, int v) { return atomicSub<unsigned>(p, static_cast<unsigned>(v)); }
