@@ -5,41 +5,133 @@
 // lim_t = min(n_k, q_pos0 + t + 1); the diagonal is included.
 //
 // Work split: one query per wave (its 64 x 128 FP8 q and 64 weights stay in VGPRs in MFMA
-// layout), 16 consecutive queries per 1024-thread workgroup.  The workgroup streams the keys
-// [0, lim of its last query) through an LDS double buffer of 256-key stages (32 KB, loaded
-// with coalesced 16-byte loads into the same swizzled layout the decode kernel uses), and
-// every wave scores its query against each 16-key tile with four
-// v_mfma_f32_16x16x128_f8f6f4 (one per 16-head block) followed by the ReLU * w reduction;
-// tiles entirely past a wave's causal limit are skipped.  Workgroups are launched heaviest
-// (latest queries) first.  Groups of four tiles are reduced so that the 64 lanes of a wave
-// write 64 consecutive scores.
+// layout), 12 consecutive queries per 768-thread workgroup (3 waves per SIMD; a wave needs
+// about 150 VGPRs).  The workgroup streams the keys [0, lim of its last query) through three
+// LDS buffers of 192-key stages (24 KB each, filled with coalesced 16-byte loads into the
+// swizzled layout the decode kernel uses; one barrier per stage): while stage n is scored,
+// stage n+1 is already in LDS and stage n+2 in registers.  Workgroups are launched heaviest
+// (latest queries) first.
+//
+// Per 64-key group a wave runs 16 units (four 16-key tiles x four 16-head blocks), each one
+// v_mfma_f32_16x16x128_f8f6f4 and its epilogue.  The kernel is bound by the ratio of epilogue
+// VALU work to MFMA work: every (head, key) product needs its ReLU and its weighted add, while
+// one MFMA covers 16 heads x 16 keys x 128 bytes in the time of about 8 wave-wide VALU
+// instructions.  So:
+//   * the epilogue is two VALU instructions per element: the ReLU is an integer max on the
+//     float's bits (a negative float, -0 included, has its sign bit set and so is below 0 as an
+//     int32; this avoids the NaN canonicalisation an IEEE float max costs), then one FMA;
+//   * the MFMA of unit u+2 is issued before the epilogue of unit u, across tile, group and
+//     stage boundaries, so the matrix core multiplies while the VALU reduces;
+//   * the four tiles' per-lane-group partial sums are combined with one butterfly of gfx950
+//     lane swaps (3 swaps + 3 adds per 64 keys), after which the 64 lanes hold 64 consecutive
+//     scores of the group.
+// The group that crosses a wave's causal limit is computed whole and its writes are masked.
 #include "internal.hpp"
 #include "score_tile.cuh"
 
 namespace echo {
 
-constexpr int PF_THREADS = 1024;
-constexpr int PF_QPB = PF_THREADS / 64;                 // 16 queries per workgroup
-constexpr int PF_STAGE = 256;                           // keys per LDS stage
-constexpr int PF_UNITS = PF_STAGE * D / 16;             // 2048 x 16 B
+constexpr int PF_THREADS = 768;
+constexpr int PF_QPB = PF_THREADS / 64;                 // 12 queries per workgroup
+constexpr int PF_STAGE = 192;                           // keys per LDS stage (3 groups of 64)
+constexpr int PF_UNITS = PF_STAGE * D / 16;             // 1536 x 16 B
 constexpr int PF_LOADS = PF_UNITS / PF_THREADS;         // 2 per thread
+constexpr int PF_BUFS = 3;                              // stage buffers in LDS (72 KB)
+static_assert(PF_STAGE % 64 == 0 && PF_UNITS % PF_THREADS == 0, "stage shape");
+
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 ECHO_DEV int pswz(int tok, int seg) { return tok * 128 + ((seg ^ ((tok >> 1) & 7)) << 4); }
+
+// ReLU(x) as an integer max on the bits: -0 and every negative float map to +0.
+ECHO_DEV float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+ECHO_DEV v4f unit_mfma(const v8i &qa, const v8i &bv) {
+  const v4f z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, bv, z, 0, 0, 0, 0, 0, 0);
+}
+// acc + sum over the lane's 4 rows of one head block: w * ReLU(c)
+ECHO_DEV float unit_epilogue(const float (&wr)[4], const v4f &c, float acc) {
+#pragma unroll
+  for (int v = 0; v < 4; ++v) acc = fmaf(wr[v], relu_bits(c[v]), acc);
+  return acc;
+}
+ECHO_DEV v8i tile_b(const uint8_t *sb, int tt, int g) {
+  const int4 b0 = *reinterpret_cast<const int4 *>(sb + pswz(tt, 2 * g));
+  const int4 b1 = *reinterpret_cast<const int4 *>(sb + pswz(tt, 2 * g + 1));
+  return v8i{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+}
+
+ECHO_DEV float swap_sum32(float a, float b) {
+  const v2u s = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+ECHO_DEV float swap_sum16(float a, float b) {
+  const v2u s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// One 64-key group of a wave: 16 units (4 tiles x 4 head blocks), one MFMA and 8 VALU
+// instructions each.  The MFMA of unit u+2 is issued before the epilogue of unit u, so the
+// matrix core multiplies while the VALU reduces and an epilogue never waits on the MFMA just
+// issued; ca and cb carry the two accumulator sets in flight and bt the B operand of the
+// current tile, from group to group and from stage to stage.  gb is the group's 64 keys in
+// LDS, nb the next group's (possibly in the next stage's buffer).  On entry ca, cb hold units
+// 0 and 1 of this group, on return those of the next one.  The body has no branch, so the
+// scheduling barriers hold within one basic block.  Returns this lane's score: key
+// 16*tsel + l%16 of the group.
+ECHO_DEV float prefill_group(const QOperand &qo, const uint8_t *gb, const uint8_t *nb, int j,
+                             int g, v8i &bt, v4f &ca, v4f &cb) {
+  float p[4];
+#pragma unroll
+  for (int tile = 0; tile < 4; ++tile) {
+    const v8i bn = tile < 3 ? tile_b(gb, (tile + 1) * 16 + j, g) : tile_b(nb, j, g);
+    float acc = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      // unit u+2 is head block hb+2 of this tile, or hb-2 of the next one
+      const v4f cn = unit_mfma(qo.qa[(hb + 2) & 3], hb < 2 ? bt : bn);
+      acc = unit_epilogue(qo.wr[hb], ca, acc);
+      ca = cb;
+      cb = cn;
+      // keep this order: hoisting every MFMA of the group to the top, which the scheduler
+      // otherwise does, holds 16 accumulator sets and spills the q operand
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    p[tile] = acc;
+    bt = bn;
+  }
+  // lanes of groups {g, g^2} exchange so each keeps two tiles summed over both groups, then
+  // groups {g, g^1} exchange so each keeps one tile summed over all four
+  const float a = swap_sum32(p[0], p[2]);
+  const float b = swap_sum32(p[1], p[3]);
+  return swap_sum16(a, b);
+}
 
 __global__ __launch_bounds__(PF_THREADS) void score_prefill_kernel(
     const uint8_t *__restrict__ q, const float *__restrict__ w, const uint8_t *__restrict__ k,
     int32_t n_q, int32_t n_k, int32_t q_pos0, float *__restrict__ scores, int64_t ld) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][PF_STAGE * D];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[PF_BUFS][PF_STAGE * D];
   const int nblk = (n_q + PF_QPB - 1) / PF_QPB;
   const int blk = nblk - 1 - static_cast<int>(blockIdx.x);     // heaviest first
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
   const int j = l & 15, g = l >> 4;
-  const int32_t t = blk * PF_QPB + wv;
+  const int32_t t = blk * PF_QPB + __builtin_amdgcn_readfirstlane(wv);    // one query per wave
   const bool active = t < n_q;
   const int32_t lim = active ? min(n_k, q_pos0 + t + 1) : 0;
   const int32_t t_last = min(n_q - 1, blk * PF_QPB + PF_QPB - 1);
   const int32_t wg_lim = min(n_k, q_pos0 + t_last + 1);
   if (wg_lim <= 0) return;
+
+  // Which tile of a 64-key group this lane's score belongs to after the butterfly.  A 32-lane
+  // swap pairs lane group g with g^2 and a 16-lane swap pairs g with g^1; the half (row) of
+  // the wave that keeps its own first operand depends on the swap direction, which one probe
+  // swap of known values reads (the sums themselves do not depend on it).
+  const v2u p32 = __builtin_amdgcn_permlane32_swap(0u, 1u, false, false);
+  const v2u p16 = __builtin_amdgcn_permlane16_swap(0u, 1u, false, false);
+  const int flip32 = __builtin_amdgcn_readfirstlane(static_cast<int>(p32[0]));
+  const int flip16 = __builtin_amdgcn_readfirstlane(static_cast<int>(p16[0]));
+  const int tsel = ((((g >> 1) ^ flip32) & 1) << 1) | ((g ^ flip16) & 1);
 
   QOperand qo;
   if (active) load_q_operand(q, w, t, qo);
@@ -58,39 +150,46 @@ __global__ __launch_bounds__(PF_THREADS) void score_prefill_kernel(
     }
   };
 
-  fetch(0);
-  int buf = 0;
-  for (int32_t c0 = 0; c0 < wg_lim; c0 += PF_STAGE) {
-    uint8_t *sb = lds[buf];
+  auto stash = [&](uint8_t *sb) {
 #pragma unroll
     for (int m = 0; m < PF_LOADS; ++m) {
       const int e = tid + m * PF_THREADS;
       *reinterpret_cast<int4 *>(sb + pswz(e >> 3, e & 7)) = pre[m];
     }
+  };
+
+  // Three stage buffers: while stage n is scored, stage n+1 is already published (the
+  // look-ahead of a wave's last group of stage n reads it) and stage n+2 is in registers.
+  fetch(0);
+  stash(lds[0]);
+  __syncthreads();
+  if (PF_STAGE < wg_lim) fetch(PF_STAGE);
+
+  const int ngw = (lim + 63) >> 6;                // 64-key groups this wave scores
+  v8i bt = {0, 0, 0, 0, 0, 0, 0, 0};
+  v4f ca = {0.f, 0.f, 0.f, 0.f}, cb = ca;
+  if (ngw > 0) {
+    bt = tile_b(lds[0], j, g);
+    ca = unit_mfma(qo.qa[0], bt);
+    cb = unit_mfma(qo.qa[1], bt);
+  }
+  int cur = 0;
+  for (int32_t c0 = 0; c0 < wg_lim; c0 += PF_STAGE) {
+    const int nxt = cur == PF_BUFS - 1 ? 0 : cur + 1;
+    // lds[nxt] was last read while stage c0 - 2*PF_STAGE was scored, before the last barrier
+    if (c0 + PF_STAGE < wg_lim) stash(lds[nxt]);
     __syncthreads();
-    if (c0 + PF_STAGE < wg_lim) fetch(c0 + PF_STAGE);
-    // four 16-key tiles at a time: lane group g writes tile g's 16 scores
-    for (int q4 = 0; q4 < PF_STAGE / 64; ++q4) {
-      const int32_t base = c0 + q4 * 64;
-      if (base >= lim) break;                       // wave-uniform: causal skip
-      float part[4];
-#pragma unroll
-      for (int tile = 0; tile < 4; ++tile) {
-        const int tt = q4 * 64 + tile * 16 + j;
-        if (base + tile * 16 < lim) {
-          const int4 b0 = *reinterpret_cast<const int4 *>(sb + pswz(tt, 2 * g));
-          const int4 b1 = *reinterpret_cast<const int4 *>(sb + pswz(tt, 2 * g + 1));
-          part[tile] = reduce_groups(score_tile_partial(qo, v8i{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w}));
-        } else {
-          part[tile] = 0.f;
-        }
-      }
-      const int32_t s = base + g * 16 + j;
-      const float v = g == 0 ? part[0] : (g == 1 ? part[1] : (g == 2 ? part[2] : part[3]));
+    if (c0 + 2 * PF_STAGE < wg_lim) fetch(c0 + 2 * PF_STAGE);
+    const int G0 = c0 >> 6, G1 = min(ngw, G0 + PF_STAGE / 64);   // wave-uniform causal skip
+    for (int G = G0; G < G1; ++G) {
+      const int gi = G - G0;
+      const uint8_t *gb = lds[cur] + gi * 64 * D;
+      const uint8_t *nb = gi == PF_STAGE / 64 - 1 ? lds[nxt] : gb + 64 * D;
+      const float v = prefill_group(qo, gb, nb, j, g, bt, ca, cb);
+      const int32_t s = G * 64 + tsel * 16 + j;      // the group crossing lim is masked here
       if (s < lim) srow[s] = v;
     }
-    __syncthreads();
-    buf ^= 1;
+    cur = nxt;
   }
 }
 

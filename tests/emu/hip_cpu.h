@@ -104,6 +104,7 @@ int emu_readlane_i(int v, int lane);
 inline int emu_amdgcn_readlane(int v, int lane) { return emu_readlane_i(v, lane); }
 inline int emu_amdgcn_readfirstlane(int v) { return emu_readlane_i(v, 0); }   // full waves only
 inline void emu_amdgcn_sched_group_barrier(int, int, int) {}                 // scheduling hint
+inline void emu_amdgcn_sched_barrier(int) {}                                  // scheduling hint
 float __shfl_xor(float v, int mask, int width = 64);
 int __shfl_xor(int v, int mask, int width = 64);
 unsigned __shfl_xor(unsigned v, int mask, int width = 64);

@@ -49,7 +49,8 @@ def _check_rows_tol(q, w, k, got, rows):
         assert np.isnan(got[t][lim:]).all(), "row %d wrote past its causal limit" % t
 
 
-@pytest.mark.parametrize("n", [1, 17, 300, 1000])
+# 12 queries per workgroup and 192-key stages of 64-key groups: sizes on both sides of each
+@pytest.mark.parametrize("n", [1, 13, 17, 63, 64, 65, 191, 192, 193, 300, 385, 1000])
 def test_prefill_small_exact(n):
     announce("prefill", n)
     q, w, k = gen.make_prefill_inputs(n, seed=60 + n)
@@ -63,6 +64,15 @@ def test_prefill_chunk_offset_exact():
     q, w = q_all[1000:1300], w_all[1000:1300]           # a chunk of 300 queries at 1000..1299
     got = host(_run(q, w, k, q_pos0=1000))
     _check_rows(q, w, k, got, range(300), q_pos0=1000)
+
+
+def test_prefill_keys_shorter_than_positions_exact():
+    # queries at positions 500..899 over only 700 keys: rows from position 699 on see all keys
+    announce("prefill keys shorter than positions")
+    q_all, w_all, k_all = gen.make_prefill_inputs(900, seed=74)
+    q, w, k = q_all[500:900], w_all[500:900], k_all[:700]
+    got = host(_run(q, w, k, q_pos0=500))
+    _check_rows(q, w, k, got, range(400), q_pos0=500)
 
 
 def test_prefill_general_fp8_tolerance():
