@@ -17,6 +17,9 @@ ECHO page measures with; real traces and model weights are not used):
   prefill_32k  causal 32768 x 32768, integer grid, per-row top-2048
   b64_128k  64 x 131072, general FP8 with k scale, k=2048, 50% of selected
             resident, 131072 free slots kept for prefetch
+  multi-step loops (make_multistep_inputs): B requests of a given length run
+            several decode steps; every step draws a new query and one new
+            token per request (key, key scale, latent row, a fresh host row)
 
 Value recipes:
   integer grid: q, k uniform integers in [-8, 8] (exact in E4M3FN);
@@ -48,7 +51,7 @@ POISON = 0xFFFF
 INF = 2**31 - 1
 
 _TAGS = {"q": 1, "w": 2, "k": 3, "scale": 4, "len": 5, "perm": 6, "kv": 7,
-         "hit": 8, "fill": 9, "slots": 10, "prio": 11, "scores": 12}
+         "hit": 8, "fill": 9, "slots": 10, "prio": 11, "scores": 12, "step": 13}
 
 
 def rng_for(seed, tag):
@@ -281,3 +284,81 @@ def make_prefill_inputs(n, grid="int", seed=4):
     w = head_weights(seed, n, grid)
     k = fp8_values(seed, "k", (n, D_INDEX), grid)
     return q, w, k
+
+
+@dataclass
+class MultiStepInputs:
+    k: np.ndarray            # uint8 [B * capacity, 128]; rows past key_len are zero
+    k_scale: object          # float32 [B * capacity] or None
+    key_begin: np.ndarray    # int64 [B]: r * capacity
+    key_len: np.ndarray      # int32 [B]: initial lengths
+    req_to_host: np.ndarray  # int32 [B * capacity]; rows past key_len hold -1
+    capacity: int
+    n_host: int
+    n_gpu: int
+    pool: PoolArrays         # initial pool; step stamps start at pool.step_id
+    steps: list              # dicts: q, w, new_k, new_scale, new_kv, new_host, step_id
+
+
+def make_multistep_inputs(batch, length, n_steps, n_gpu, grid="int", k_scale=False, seed=11):
+    """A loop of n_steps decode steps over `batch` requests that start with `length` tokens.
+
+    Host rows: the initial tokens occupy a seeded permutation of [0, batch*length), the new
+    tokens a seeded permutation of the following batch*n_steps rows.  The pool starts full
+    (n_gpu random tokens resident, distinct random priorities from a permutation of
+    [0, n_gpu)); step stamps are n_gpu, n_gpu + 1, ...  Latent rows of the initial tokens come
+    from fill_latent_rows(seed, ...); the host rows of the new tokens hold the poison pattern
+    until their token is appended, and the new tokens' own rows come from
+    fill_latent_rows(seed + 7919, ...).  Returns (MultiStepInputs, host_kv)."""
+    cap = length + n_steps
+    n0 = batch * length
+    n_host = n0 + batch * n_steps
+    cfg = DecodeConfig("multistep", batch, length, 0, grid, k_scale, 0.0, 1, seed=seed)
+    base = make_decode_inputs(cfg)
+    key_begin = np.arange(batch, dtype=np.int64) * cap
+    k = np.zeros((batch * cap, D_INDEX), np.uint8)
+    req_to_host = np.full(batch * cap, -1, np.int32)
+    ks = np.zeros(batch * cap, np.float32) if k_scale else None
+    for r in range(batch):
+        src = slice(r * length, (r + 1) * length)
+        dst = slice(r * cap, r * cap + length)
+        k[dst] = base.k[src]
+        req_to_host[dst] = base.req_to_host[src]
+        if k_scale:
+            ks[dst] = base.k_scale[src]
+    host_kv = fill_latent_rows(seed, np.empty((n_host, ROW_ELEMS), np.uint16))
+    host_kv[n0:] = POISON                      # rows of tokens not generated yet
+    new_kv = fill_latent_rows(seed + 7919, np.empty((batch * n_steps, ROW_ELEMS), np.uint16))
+    # initial pool: random resident tokens, all slots used
+    n_res = min(n_gpu, n0)
+    tok = rng_for(seed, "fill").permutation(n0)[:n_res]
+    hosts = base.req_to_host[tok].astype(np.int64)
+    slots = rng_for(seed, "slots").permutation(n_gpu)[:n_res]
+    free = np.ones(n_gpu, np.uint8)
+    priority = np.full(n_gpu, -1, np.int32)
+    to_host = np.full(n_gpu, INF, np.int32)
+    host_to_gpu = np.full(n_host, INF, np.int32)
+    free[slots] = 0
+    to_host[slots] = hosts
+    host_to_gpu[hosts] = slots
+    priority[slots] = rng_for(seed, "prio").permutation(n_gpu)[:n_res]
+    gpu_kv = np.full((n_gpu, ROW_ELEMS), POISON, np.uint16)
+    gpu_kv[slots] = host_kv[hosts]
+    pool = PoolArrays(free, priority, to_host, host_to_gpu, np.full(n_gpu, -1, np.int32),
+                      gpu_kv, step_id=n_gpu)
+    new_hosts = (n0 + rng_for(seed, "step").permutation(batch * n_steps)).astype(np.int32)
+    steps = []
+    for t in range(n_steps):
+        s_seed = seed * 1000 + t + 1
+        nh = new_hosts[t * batch:(t + 1) * batch]
+        steps.append(dict(
+            q=fp8_values(s_seed, "q", (batch, H_INDEX, D_INDEX), grid),
+            w=head_weights(s_seed, batch, grid),
+            new_k=fp8_values(s_seed, "k", (batch, D_INDEX), grid),
+            new_scale=(rng_for(s_seed, "scale").uniform(0.5, 2.0, batch).astype(np.float32)
+                       if k_scale else None),
+            new_kv=new_kv[t * batch:(t + 1) * batch].copy(),
+            new_host=nh.copy(),
+            step_id=n_gpu + t))
+    return MultiStepInputs(k, ks, key_begin, np.full(batch, length, np.int32), req_to_host,
+                           cap, n_host, n_gpu, pool, steps), host_kv

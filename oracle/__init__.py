@@ -13,6 +13,11 @@ Citations name the web page and the section on it:
   that page (§2 concepts, §5.1 metadata, §5.2 in-graph operations, §6.1
   intra-query prefetching, §6.2 inter-query prefetching).
 
+Modules: fp8 (E4M3FN decoding), scores (indexer scores and their error
+scale), topk (exact top-k, sample threshold), pool (the residency step),
+decode (one whole step), multistep (steps in a row: new tokens with
+write-through, the EMA threshold).
+
 Readings of points the page leaves open are listed in each module's docstring.
 Parity status of every function is stated in its docstring ("pinned by ...").
 """
@@ -24,11 +29,14 @@ from .pool import (INF, ST_EXHAUSTED, ST_BAD_HOST, ST_DUP_HOST, PoolState,
                    pool_step, allocate_with_ranks, metadata_bytes,
                    check_pool_invariants, PoolInvariantError)
 from .decode import decode_step
+from .multistep import (KeyCache, ST_CACHE_FULL, append_tokens, kth_scores, ema_update,
+                        decode_loop)
 
 __all__ = [
     "E4M3FN_TABLE", "decode_e4m3fn", "index_scores", "error_scale",
     "prefill_scores_rows", "topk_row", "topk_rows", "sample_threshold",
     "threshold_bin", "INF", "ST_EXHAUSTED", "ST_BAD_HOST", "ST_DUP_HOST",
     "PoolState", "pool_step", "allocate_with_ranks", "metadata_bytes",
-    "check_pool_invariants", "PoolInvariantError", "decode_step",
+    "check_pool_invariants", "PoolInvariantError", "decode_step", "KeyCache",
+    "ST_CACHE_FULL", "append_tokens", "kth_scores", "ema_update", "decode_loop",
 ]
