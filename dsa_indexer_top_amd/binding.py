@@ -13,7 +13,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libecho.so")
 
 ECHO_OK, ECHO_EINVAL, ECHO_EUNSUPPORTED, ECHO_EHIP, ECHO_EWORKSPACE = 0, -1, -2, -3, -4
-ST_EXHAUSTED, ST_BAD_HOST, ST_DUP_HOST = 1, 2, 4
+ST_EXHAUSTED, ST_BAD_HOST, ST_DUP_HOST, ST_CACHE_FULL = 1, 2, 4, 8
 RECALL_GATHER, RECALL_MEMCPY = 0, 1
 INF = 0x7FFFFFFF
 ROW_ELEMS = 576
@@ -38,12 +38,19 @@ class DecodeArgs(C.Structure):
     _fields_ = [("q", P), ("w", P), ("k", P), ("k_scale", P), ("key_begin", P),
                 ("key_len", P), ("req_to_host", P), ("n_rows", I32), ("max_key_len", I32),
                 ("topk", I32), ("step_id", I32), ("prefetch", I32), ("n_chunks", I32),
-                ("n_sample", I32), ("percentile", F32), ("cap", I32), ("cap_div", I32)]
+                ("n_sample", I32), ("percentile", F32), ("cap", I32), ("cap_div", I32),
+                ("theta_ema", P), ("ema_alpha", F32)]
 
 
 class DecodeOut(C.Structure):
     _fields_ = [("scores", P), ("topk_idx", P), ("topk_slot", P), ("miss_host", P),
-                ("miss_slot", P), ("counters", P)]
+                ("miss_slot", P), ("counters", P), ("kth", P)]
+
+
+class AppendArgs(C.Structure):
+    _fields_ = [("n_rows", I32), ("capacity", I32), ("n_k", I64), ("new_k", P), ("new_scale", P),
+                ("new_kv", P), ("new_host", P), ("k", P), ("k_scale", P), ("key_begin", P),
+                ("key_len", P), ("req_to_host", P), ("host_kv_w", P), ("step_id", I32)]
 
 
 _SIGS = {
@@ -68,6 +75,8 @@ _SIGS = {
     "echo_decode_workspace_bytes": (SZ, [C.POINTER(DecodeArgs), I32]),
     "echo_decode_select": (C.c_int, [C.POINTER(DecodeArgs), C.POINTER(Pool),
                                      C.POINTER(DecodeOut), P, SZ, P, P]),
+    "echo_append_workspace_bytes": (SZ, [I32, I32]),
+    "echo_decode_append": (C.c_int, [C.POINTER(AppendArgs), C.POINTER(Pool), P, P, SZ, P]),
     "echo_graph_capture_decode": (C.c_int, [C.POINTER(DecodeArgs), C.POINTER(Pool),
                                             C.POINTER(DecodeOut), P, SZ, P, P, C.POINTER(P)]),
     "echo_graph_launch": (C.c_int, [P, P]),
@@ -214,6 +223,15 @@ def decode_select(args, pool, out, ws, main=None, side=None):
     _call("echo_decode_select", C.byref(args), C.byref(pool), C.byref(out), ptr(ws),
           ws.numel() * ws.element_size(), stream_handle(main),
           stream_handle(side) if side is not None else stream_handle(main))
+
+
+def append_workspace_bytes(n_rows, n_gpu):
+    return lib().echo_append_workspace_bytes(n_rows, n_gpu)
+
+
+def decode_append(args, pool, new_slot, ws, stream=None):
+    _call("echo_decode_append", C.byref(args), C.byref(pool), ptr(new_slot), ptr(ws),
+          ws.numel() * ws.element_size(), stream_handle(stream))
 
 
 class Graph:

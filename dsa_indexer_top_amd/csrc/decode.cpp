@@ -14,6 +14,8 @@
 //
 // With prefetch, scoring is split into n_chunks token ranges: the launch of range c also
 // gathers range c-1's candidates, and a gather launch for the last range precedes the split.
+// With the EMA threshold (§6.1) a last small launch takes each request's k-th score and updates
+// the caller's estimate for the next step.
 #include <algorithm>
 #include <new>
 
@@ -96,6 +98,8 @@ static int validate(const echo_decode_args *a, const echo_pool *pool, const echo
     if (!(a->percentile > 0.f && a->percentile <= 100.f)) return fail(ECHO_EINVAL, "echo_decode_select: percentile outside (0, 100]");
     if (a->cap < 1 || a->cap_div < 1) return fail(ECHO_EINVAL, "echo_decode_select: cap and cap_div must be >= 1");
   }
+  if (a->theta_ema && !(a->ema_alpha >= 0.f && a->ema_alpha <= 1.f))
+    return fail(ECHO_EINVAL, "echo_decode_select: ema_alpha outside [0, 1]");
   return ECHO_OK;
 }
 
@@ -117,8 +121,12 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
   side.W = W.pool;
   side.step_id = a->step_id;
   side.n_stats = W.pool.n_chunks;                   // statistics ride with the first scoring launch
+  // prefetch threshold: the caller's EMA estimate (§6.1), or a sample percentile of this
+  // step's scores when there is no history
+  const float *theta = a->theta_ema ? a->theta_ema : W.theta;
   if (pf) {
-    if ((rc = launch_prefetch_threshold(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len,
+    if (!a->theta_ema &&
+        (rc = launch_prefetch_threshold(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len,
                                         a->n_rows, a->n_sample, a->percentile, W.theta, m)))
       return rc;
     if ((rc = launch_prefetch_begin(pool, W.free_list, W.free_count, m))) return rc;
@@ -132,7 +140,7 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
                                   W.free_list, W.free_count, o->counters + 2, &W.pool, a->step_id);
       }
       const int32_t lo = c * span, hi = (c + 1 == nc) ? a->max_key_len : (c + 1) * span;
-      PrefetchArgs P{W.theta, a->req_to_host, pool->host_to_gpu,
+      PrefetchArgs P{theta, a->req_to_host, pool->host_to_gpu,
                      W.cand + static_cast<int64_t>(c) * a->n_rows * a->cap,
                      W.cand_cnt + static_cast<int64_t>(c) * a->n_rows, W.total_cnt, a->cap, a->cap_div};
       if ((rc = launch_score_decode(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len, a->n_rows,
@@ -168,7 +176,8 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
                                   W.stage, m)))
     return rc;
   if (pf && (rc = launch_sum_i32(W.total_cnt, a->n_rows, o->counters + 1, m))) return rc;
-  return ECHO_OK;
+  return launch_kth_ema(o->scores, a->max_key_len, o->topk_idx, a->n_rows, a->topk, a->ema_alpha,
+                        a->theta_ema, o->kth, m);
 }
 
 struct GraphHandle {

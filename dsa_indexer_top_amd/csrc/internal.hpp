@@ -172,5 +172,9 @@ int launch_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
 int launch_zero_i32(int32_t *p, int64_t n, hipStream_t st);
 int launch_zero2_i32(int32_t *p, int64_t n, int32_t *q, int64_t m, hipStream_t st);
 int launch_sum_i32(const int32_t *v, int32_t n, int32_t *out, hipStream_t st);
+// kth[r] = smallest score among row r's selections (NaN if none); theta (optional) updated by
+// the EMA of the k-th score
+int launch_kth_ema(const float *scores, int64_t ld, const int32_t *idx, int32_t n_rows, int32_t k,
+                   float alpha, float *theta, float *kth, hipStream_t st);
 
 }  // namespace echo

@@ -300,12 +300,14 @@ class MultiStepInputs:
     steps: list              # dicts: q, w, new_k, new_scale, new_kv, new_host, step_id
 
 
-def make_multistep_inputs(batch, length, n_steps, n_gpu, grid="int", k_scale=False, seed=11):
+def make_multistep_inputs(batch, length, n_steps, n_gpu, grid="int", k_scale=False, seed=11,
+                          reserve=0):
     """A loop of n_steps decode steps over `batch` requests that start with `length` tokens.
 
     Host rows: the initial tokens occupy a seeded permutation of [0, batch*length), the new
-    tokens a seeded permutation of the following batch*n_steps rows.  The pool starts full
-    (n_gpu random tokens resident, distinct random priorities from a permutation of
+    tokens a seeded permutation of the following batch*n_steps rows.  The pool starts full but
+    for `reserve` free slots (random tokens resident, distinct random priorities from a
+    permutation of
     [0, n_gpu)); step stamps are n_gpu, n_gpu + 1, ...  Latent rows of the initial tokens come
     from fill_latent_rows(seed, ...); the host rows of the new tokens hold the poison pattern
     until their token is appended, and the new tokens' own rows come from
@@ -330,7 +332,7 @@ def make_multistep_inputs(batch, length, n_steps, n_gpu, grid="int", k_scale=Fal
     host_kv[n0:] = POISON                      # rows of tokens not generated yet
     new_kv = fill_latent_rows(seed + 7919, np.empty((batch * n_steps, ROW_ELEMS), np.uint16))
     # initial pool: random resident tokens, all slots used
-    n_res = min(n_gpu, n0)
+    n_res = min(n_gpu - reserve, n0)
     tok = rng_for(seed, "fill").permutation(n0)[:n_res]
     hosts = base.req_to_host[tok].astype(np.int64)
     slots = rng_for(seed, "slots").permutation(n_gpu)[:n_res]

@@ -110,3 +110,109 @@ class DecodeRunner:
             self.graph = None
         if self._own_buf:
             self.host_buf.close()
+
+
+class LoopRunner:
+    """Device buffers of several decode steps in a row (inputs.MultiStepInputs): the K cache with
+    room for the new tokens, the pool, the pinned host backup (the appends write through to it),
+    one step's inputs and the EMA estimate of the k-th score.  run_step(st) uploads step st's
+    query and new tokens, then enqueues echo_decode_append and echo_decode_select.  No arithmetic
+    of the method lives here."""
+
+    def __init__(self, m, host_kv, topk, prefetch=False, pf=None, alpha=0.5, ema=True):
+        import torch
+        self.torch = torch
+        self.m = m
+        B_, cap = len(m.key_len), m.capacity
+        self.n_rows, self.cap, self.topk = B_, cap, topk
+        self.k = _dev(m.k)
+        self.k_scale = None if m.k_scale is None else _dev(m.k_scale)
+        self.key_begin, self.key_len = _dev(m.key_begin), _dev(m.key_len)
+        self.req_to_host = _dev(m.req_to_host)
+        names = ("free", "priority", "to_host", "host_to_gpu", "indices_buf", "gpu_kv")
+        self.live = {n: _dev(getattr(m.pool, n)) for n in names}
+        self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.host_buf = B.HostBuffer(host_kv.nbytes)
+        self.host_kv = self.host_buf.array.view(np.uint16).reshape(host_kv.shape)
+        self.host_kv[...] = host_kv
+        self.n_gpu, self.n_host = len(m.pool.free), len(m.pool.host_to_gpu)
+        L = self.live
+        self.pool = B.make_pool(self.n_gpu, self.n_host, L["free"], L["priority"], L["to_host"],
+                                L["host_to_gpu"], L["indices_buf"], L["gpu_kv"],
+                                self.host_buf.dev_ptr, self.status)
+        i32, f32 = torch.int32, torch.float32
+        dev = "cuda"
+        # one step's inputs
+        self.q = torch.empty((B_, 64, 128), dtype=torch.uint8, device=dev)
+        self.w = torch.empty((B_, 64), dtype=f32, device=dev)
+        self.new_k = torch.empty((B_, 128), dtype=torch.uint8, device=dev)
+        self.new_scale = None if m.k_scale is None else torch.empty(B_, dtype=f32, device=dev)
+        self.new_kv = torch.empty((B_, 576), dtype=torch.int16, device=dev)
+        self.new_host = torch.empty(B_, dtype=i32, device=dev)
+        # outputs
+        self.scores = torch.empty((B_, cap), dtype=f32, device=dev)
+        self.topk_idx = torch.empty((B_, topk), dtype=i32, device=dev)
+        self.topk_slot = torch.empty((B_, topk), dtype=i32, device=dev)
+        self.miss_host = torch.empty(B_ * topk, dtype=i32, device=dev)
+        self.miss_slot = torch.empty(B_ * topk, dtype=i32, device=dev)
+        self.counters = torch.zeros(8, dtype=i32, device=dev)
+        self.kth = torch.empty(B_, dtype=f32, device=dev)
+        self.new_slot = torch.empty(B_, dtype=i32, device=dev)
+        self.theta = torch.full((B_,), float("nan"), dtype=f32, device=dev)
+        self.out = B.DecodeOut(self.scores.data_ptr(), self.topk_idx.data_ptr(),
+                               self.topk_slot.data_ptr(), self.miss_host.data_ptr(),
+                               self.miss_slot.data_ptr(), self.counters.data_ptr(),
+                               self.kth.data_ptr())
+        p = dict(DEFAULT_PREFETCH)
+        p.update(pf or {})
+        self.args = B.DecodeArgs(
+            self.q.data_ptr(), self.w.data_ptr(), self.k.data_ptr(),
+            None if self.k_scale is None else self.k_scale.data_ptr(),
+            self.key_begin.data_ptr(), self.key_len.data_ptr(), self.req_to_host.data_ptr(),
+            B_, cap, topk, 0, 1 if prefetch else 0, p["n_chunks"], p["n_sample"],
+            p["percentile"], p["cap"], p["cap_div"],
+            self.theta.data_ptr() if ema else None, alpha)
+        self.app = B.AppendArgs(
+            B_, cap, self.k.shape[0], self.new_k.data_ptr(),
+            None if self.new_scale is None else self.new_scale.data_ptr(),
+            self.new_kv.data_ptr(), self.new_host.data_ptr(), self.k.data_ptr(),
+            None if self.k_scale is None else self.k_scale.data_ptr(),
+            self.key_begin.data_ptr(), self.key_len.data_ptr(), self.req_to_host.data_ptr(),
+            self.host_buf.dev_ptr, 0)
+        self.ws = torch.empty(max(B.decode_workspace_bytes(self.args, self.n_gpu), 256),
+                              dtype=torch.uint8, device=dev)
+        self.ws_app = torch.empty(max(B.append_workspace_bytes(B_, self.n_gpu), 256),
+                                  dtype=torch.uint8, device=dev)
+        self.main = torch.cuda.Stream()
+
+    def load_step(self, st):
+        t = self.torch
+        with t.cuda.stream(self.main):
+            self.q.copy_(t.from_numpy(np.ascontiguousarray(st["q"])))
+            self.w.copy_(t.from_numpy(np.ascontiguousarray(st["w"])))
+            self.new_k.copy_(t.from_numpy(np.ascontiguousarray(st["new_k"])))
+            if self.new_scale is not None:
+                self.new_scale.copy_(t.from_numpy(np.ascontiguousarray(st["new_scale"])))
+            self.new_kv.copy_(t.from_numpy(np.ascontiguousarray(st["new_kv"]).view(np.int16)))
+            self.new_host.copy_(t.from_numpy(np.ascontiguousarray(st["new_host"], np.int32)))
+
+    def run_step(self, st):
+        self.load_step(st)
+        self.app.step_id = self.args.step_id = int(st["step_id"])
+        B.decode_append(self.app, self.pool, self.new_slot, self.ws_app, self.main)
+        B.decode_select(self.args, self.pool, self.out, self.ws, self.main)
+
+    def results(self):
+        self.torch.cuda.synchronize()
+        h = lambda t: t.cpu().numpy()
+        return dict(scores=h(self.scores), topk_idx=h(self.topk_idx), topk_slot=h(self.topk_slot),
+                    miss_host=h(self.miss_host), miss_slot=h(self.miss_slot),
+                    counters=h(self.counters), kth=h(self.kth), theta=h(self.theta),
+                    new_slot=h(self.new_slot), status=int(h(self.status)[0]),
+                    key_len=h(self.key_len), k=h(self.k), req_to_host=h(self.req_to_host),
+                    k_scale=None if self.k_scale is None else h(self.k_scale),
+                    pool={n: h(t) for n, t in self.live.items()},
+                    host_kv=self.host_kv.copy())
+
+    def close(self):
+        self.host_buf.close()

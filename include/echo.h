@@ -54,8 +54,10 @@ enum {
 enum {
   ECHO_ST_EXHAUSTED = 1, /* the misses need more slots than free + evictable; pool untouched */
   ECHO_ST_BAD_HOST = 2,  /* a selected token maps to a host index outside [0, n_host); pool untouched */
-  ECHO_ST_DUP_HOST = 4   /* two selected misses share a host index (caller precondition broken);
+  ECHO_ST_DUP_HOST = 4,  /* two selected misses share a host index (caller precondition broken);
                             pool state afterwards is unspecified */
+  ECHO_ST_CACHE_FULL = 8 /* echo_decode_append: a request's key range is full; its token was not
+                            appended */
 };
 
 /* Recall modes for echo_recall. */
@@ -269,6 +271,14 @@ typedef struct {
   float percentile;          /* threshold percentile, e.g. 95 */
   int32_t cap;               /* per-request candidate cap bound */
   int32_t cap_div;           /* cap_r = min(cap, ceil(L_r / cap_div)) */
+  /* EMA threshold (§6.1; off when theta_ema == NULL).  theta_ema [n_rows] is the caller's
+     per-request estimate of the k-th largest score, kept from step to step.  With prefetch on
+     it replaces the sample percentile as the threshold (NaN = no estimate yet: nothing is
+     prefetched).  At the end of the step it is updated from this step's k-th score kth (the
+     smallest selected score): theta = kth if theta is NaN, else
+     fmaf(ema_alpha, theta, (1 - ema_alpha) * kth); a request with no selection keeps it. */
+  float *theta_ema;
+  float ema_alpha;           /* the page uses 0.5 */
 } echo_decode_args;
 
 typedef struct {             /* device outputs of one step */
@@ -280,12 +290,53 @@ typedef struct {             /* device outputs of one step */
   int32_t *counters;         /* [8]: 0 n_miss (guaranteed recall), 1 prefetch demand (tokens
                                 above threshold and not resident, summed over requests),
                                 2 rows prefetched, 3..7 reserved (zero) */
+  float *kth;                /* [n_rows] or NULL: smallest selected score per request (the k-th
+                                largest when key_len >= topk; NaN when nothing is selected) */
 } echo_decode_out;
 
 size_t echo_decode_workspace_bytes(const echo_decode_args *a, int32_t n_gpu);
 int echo_decode_select(const echo_decode_args *a, const echo_pool *pool,
                        const echo_decode_out *out, void *ws, size_t ws_bytes, void *main_stream,
                        void *side_stream);
+
+/*
+ * One new token per request, before its query is scored (§2: a token's latent row is backed up
+ * to host memory when it is generated, so eviction never moves data; §5.2: allocate serves
+ * newly generated KV as well as recalled tokens).  For every request r with
+ * p = key_len[r] < capacity and key_begin[r] + p < n_k:
+ *   k[key_begin[r] + p] = new_k[r] (128 FP8 bytes); k_scale[...] = new_scale[r] when given;
+ *   req_to_host[key_begin[r] + p] = new_host[r]; key_len[r] = p + 1 (on the device);
+ *   host_kv_w[new_host[r]] = new_kv[r] (576 bf16 values written through the host link);
+ * a request at capacity appends nothing and sets ECHO_ST_CACHE_FULL.  Then the appended tokens,
+ * in request order, get GPU slots exactly as misses of echo_pool_lookup_alloc with k = 1
+ * (nothing protected, eviction of the lowest (priority, slot) when no slot is free, priority
+ * step_id), and their rows are copied from new_kv into those slots.  new_slot[r] receives the
+ * slot (-1 for a request that appended nothing); it is unspecified when the pool status word
+ * is nonzero afterwards.  new_host[r] must lie in [0, n_host), be distinct and not be resident
+ * (ECHO_ST_BAD_HOST / ECHO_ST_DUP_HOST otherwise; the pool is then left untouched, the key
+ * cache and host rows are still written).  Pure enqueue on `stream`; workspace:
+ * echo_append_workspace_bytes(n_rows, pool->n_gpu).
+ */
+typedef struct {
+  int32_t n_rows;
+  int32_t capacity;          /* key rows reserved per request (key_len never exceeds it) */
+  int64_t n_k;               /* rows of k, k_scale and req_to_host */
+  const uint8_t *new_k;      /* [n_rows, 128] FP8 */
+  const float *new_scale;    /* [n_rows], or NULL when k_scale is NULL */
+  const uint16_t *new_kv;    /* [n_rows, 576] bf16 bits, device memory */
+  const int32_t *new_host;   /* [n_rows] host row of each new token */
+  uint8_t *k;                /* [n_k, 128] the indexer K cache */
+  float *k_scale;            /* [n_k] or NULL */
+  const int64_t *key_begin;  /* [n_rows] */
+  int32_t *key_len;          /* [n_rows], incremented */
+  int32_t *req_to_host;      /* [n_k] */
+  uint16_t *host_kv_w;       /* WRITABLE device-mapped pointer to the pool's host backup
+                                (the same memory as echo_pool.host_kv) */
+  int32_t step_id;
+} echo_append_args;
+size_t echo_append_workspace_bytes(int32_t n_rows, int32_t n_gpu);
+int echo_decode_append(const echo_append_args *a, const echo_pool *pool, int32_t *new_slot,
+                       void *ws, size_t ws_bytes, void *stream);
 
 /* Graph helpers (host side; they create HIP objects).  Capture one echo_decode_select into a
  * hipGraph on `main_stream`, instantiate it, and replay it.  The graph

@@ -125,6 +125,49 @@ def test_decode_select_argument_errors():
     assert L.echo_graph_destroy(None) == B.ECHO_OK
 
 
+def _append_args(**kw):
+    a = B.AppendArgs(4, 1024, 4096, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 9)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_decode_append_and_ema_argument_errors():
+    L = B.lib()
+    p = _pool()
+    slot = FAKE
+    cases = [
+        (dict(n_rows=0), B.ECHO_EUNSUPPORTED),
+        (dict(n_rows=70000), B.ECHO_EUNSUPPORTED),
+        (dict(capacity=0), B.ECHO_EINVAL),
+        (dict(n_k=0), B.ECHO_EINVAL),
+        (dict(new_kv=None), B.ECHO_EINVAL),
+        (dict(host_kv_w=None), B.ECHO_EINVAL),
+        (dict(key_len=None), B.ECHO_EINVAL),
+        (dict(k_scale=FAKE), B.ECHO_EINVAL),              # a key scale with no new scales
+        (dict(new_scale=FAKE), B.ECHO_EINVAL),
+    ]
+    for kw, code in cases:
+        a = _append_args(**kw)
+        assert L.echo_decode_append(C.byref(a), C.byref(p), slot, FAKE, 1 << 30, None) == code, kw
+    a = _append_args()
+    assert L.echo_decode_append(C.byref(a), C.byref(p), None, FAKE, 1 << 30, None) == B.ECHO_EINVAL
+    assert L.echo_decode_append(C.byref(a), C.POINTER(B.Pool)(), slot, FAKE, 1 << 30, None) == B.ECHO_EINVAL
+    q = _pool()
+    q.gpu_kv = None
+    assert L.echo_decode_append(C.byref(a), C.byref(q), slot, FAKE, 1 << 30, None) == B.ECHO_EINVAL
+    short = L.echo_append_workspace_bytes(4, p.n_gpu) - 1
+    assert L.echo_decode_append(C.byref(a), C.byref(p), slot, FAKE, short, None) == B.ECHO_EWORKSPACE
+    assert L.echo_append_workspace_bytes(-1, 8) == 0
+    assert L.echo_append_workspace_bytes(8, 1 << 20) > L.echo_append_workspace_bytes(8, 1024)
+    # the EMA weight must lie in [0, 1] when an estimate buffer is given
+    for alpha in (-0.5, 1.5, float("nan")):
+        d = _decode_args(theta_ema=FAKE, ema_alpha=alpha)
+        assert L.echo_decode_select(C.byref(d), C.byref(p), C.byref(_out()), FAKE, 1 << 30, None,
+                                    None) == B.ECHO_EINVAL, alpha
+        assert "ema_alpha" in _err()
+
+
 def test_workspace_sizes():
     L = B.lib()
     assert L.echo_pool_workspace_bytes(-1, 8, 8) == 0

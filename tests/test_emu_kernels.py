@@ -35,7 +35,7 @@ pytestmark = pytest.mark.skipif(ASAN is None, reason="clang AddressSanitizer run
 # The small and medium GPU parity cases; the full-size workloads take too long on one core.
 SELECTION = [
     "tests/test_gpu_scores.py", "tests/test_gpu_topk.py", "tests/test_gpu_pool.py",
-    "tests/test_gpu_decode.py", "tests/test_gpu_prefill.py",
+    "tests/test_gpu_decode.py", "tests/test_gpu_prefill.py", "tests/test_gpu_multistep.py",
     "-k", "not full and not b8_64k and not b32 and not 32k and not topk_rows_exact "
           "and not 150000 and not 300000 and not small_exact[1000]",
 ]
