@@ -122,6 +122,54 @@ def prefill_measure(torch, B, gen, reps=5):
             "topk_rows_us": round(t_topk, 1)}
 
 
+def loop_measure(torch, B, gen, batch=8, length=65536, n_steps=16, topk=2048, drift=0.05):
+    """Decode steps in a row: every step appends one token per request (key, host row written
+    through, GPU slot) and runs the decode step with prefetch against the EMA estimate of the
+    k-th score (alpha = 0.5).  8 requests x 65536 tokens, integer grid, top-2048, N_G = 131072
+    with 65536 slots free at the start, consecutive queries alike (5% of q's bytes redrawn per
+    step).  Timed per step with HIP events around the two enqueues on their stream (the upload
+    of the step's query and new tokens precedes the start event).  Reports the pool hit rate of
+    the guaranteed recall, the rows prefetched and the EMA's prediction error per step."""
+    from dsa_indexer_top_amd.runner import LoopRunner
+    n_gpu = batch * length // 4
+    m, host_kv = gen.make_multistep_inputs(batch, length, n_steps, n_gpu, seed=51,
+                                           reserve=n_gpu // 2, drift=drift)
+    rn = LoopRunner(m, host_kv, topk, prefetch=True, pf=dict(n_chunks=4, cap=2048, cap_div=32))
+    steps = []
+    try:
+        for st in m.steps:
+            theta_used = rn.theta.cpu().numpy().astype(np.float64)
+            rn.load_step(st)
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            rn.app.step_id = rn.args.step_id = int(st["step_id"])
+            s.record(rn.main)
+            B.decode_append(rn.app, rn.pool, rn.new_slot, rn.ws_app, rn.main)
+            B.decode_select(rn.args, rn.pool, rn.out, rn.ws, rn.main)
+            e.record(rn.main)
+            torch.cuda.synchronize()
+            c = rn.counters.cpu().numpy()
+            kth = rn.kth.cpu().numpy().astype(np.float64)
+            assert int(rn.status.cpu()[0]) == 0, "pool status after a loop step"
+            err = (np.abs(theta_used - kth) / np.maximum(np.abs(kth), 1e-30)
+                   if not np.isnan(theta_used).any() else None)
+            steps.append({"us": round(s.elapsed_time(e) * 1000.0, 1),
+                          "hit_rate": round(1.0 - int(c[0]) / float(batch * topk), 4),
+                          "misses": int(c[0]), "prefetch_demand": int(c[1]),
+                          "prefetched": int(c[2]),
+                          "ema_rel_err_median": None if err is None else round(float(np.median(err)), 4)})
+    finally:
+        rn.close()
+    later = steps[1:]
+    return {"workload": "%d requests x %d tokens, %d steps, top-%d, integer grid, q drift %.2f, "
+                        "N_G=%d (half free at the start), prefetch against the EMA estimate"
+                        % (batch, length, n_steps, topk, drift, n_gpu),
+            "timing": "eager enqueue of echo_decode_append + echo_decode_select per step, HIP events",
+            "us_per_step_median": round(float(np.median([x["us"] for x in later])), 1),
+            "hit_rate_median": round(float(np.median([x["hit_rate"] for x in later])), 4),
+            "steps": steps}
+
+
 def cpu_baseline(inp, host_kv, pool_arrays, min_s=10.0, budget_s=30.0):
     """The oracle, as it is, timed on the host cores on a bounded sample of the same workload:
     the whole oracle decode step (float64 scores, exact top-k, canonical pool step with the
@@ -181,6 +229,7 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-loop", action="store_true", help="skip the decode-loop measurement")
     ap.add_argument("--prefetch", choices=("auto", "on", "off"), default="auto")
     ap.add_argument("--probe", choices=("score", "copy", "prefill"), default=None,
                     help="short program for hardware-counter runs, then exit: 20 launches of the "
@@ -345,6 +394,11 @@ def main():
         log("prefill %.1f us = %.0f TFLOP/s (%.1f%% of fp8 peak), top-k rows %.1f us" % (
             out["prefill"]["us_per_launch"], out["prefill"]["achieved"],
             100 * out["prefill"]["frac"], out["prefill"]["topk_rows_us"]))
+    if not args.no_loop:
+        log("decode loop (EMA threshold, new tokens every step) ...")
+        out["loop"] = loop_measure(torch, B, gen)
+        log("loop: median %.1f us/step, hit rate %.3f" % (out["loop"]["us_per_step_median"],
+                                                          out["loop"]["hit_rate_median"]))
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(inp, host_kv, pool)

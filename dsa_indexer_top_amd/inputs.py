@@ -301,7 +301,7 @@ class MultiStepInputs:
 
 
 def make_multistep_inputs(batch, length, n_steps, n_gpu, grid="int", k_scale=False, seed=11,
-                          reserve=0):
+                          reserve=0, drift=None):
     """A loop of n_steps decode steps over `batch` requests that start with `length` tokens.
 
     Host rows: the initial tokens occupy a seeded permutation of [0, batch*length), the new
@@ -311,7 +311,10 @@ def make_multistep_inputs(batch, length, n_steps, n_gpu, grid="int", k_scale=Fal
     [0, n_gpu)); step stamps are n_gpu, n_gpu + 1, ...  Latent rows of the initial tokens come
     from fill_latent_rows(seed, ...); the host rows of the new tokens hold the poison pattern
     until their token is appended, and the new tokens' own rows come from
-    fill_latent_rows(seed + 7919, ...).  Returns (MultiStepInputs, host_kv)."""
+    fill_latent_rows(seed + 7919, ...).  Queries: independent draws per step, or with
+    `drift` = f the first step's q and w carried on with a fraction f of q's bytes redrawn each
+    step (consecutive decode queries of a request are alike, so their selections overlap).
+    Returns (MultiStepInputs, host_kv)."""
     cap = length + n_steps
     n0 = batch * length
     n_host = n0 + batch * n_steps
@@ -350,12 +353,23 @@ def make_multistep_inputs(batch, length, n_steps, n_gpu, grid="int", k_scale=Fal
                       gpu_kv, step_id=n_gpu)
     new_hosts = (n0 + rng_for(seed, "step").permutation(batch * n_steps)).astype(np.int32)
     steps = []
+    q_prev = w0 = None
     for t in range(n_steps):
         s_seed = seed * 1000 + t + 1
         nh = new_hosts[t * batch:(t + 1) * batch]
+        q_t = fp8_values(s_seed, "q", (batch, H_INDEX, D_INDEX), grid)
+        w_t = head_weights(s_seed, batch, grid)
+        if drift is not None:
+            if q_prev is None:
+                w0 = w_t
+            else:
+                keep = rng_for(s_seed, "hit").random(q_t.shape) >= drift
+                q_t = np.where(keep, q_prev, q_t)
+                w_t = w0
+            q_prev = q_t
         steps.append(dict(
-            q=fp8_values(s_seed, "q", (batch, H_INDEX, D_INDEX), grid),
-            w=head_weights(s_seed, batch, grid),
+            q=q_t,
+            w=w_t,
             new_k=fp8_values(s_seed, "k", (batch, D_INDEX), grid),
             new_scale=(rng_for(s_seed, "scale").uniform(0.5, 2.0, batch).astype(np.float32)
                        if k_scale else None),
