@@ -127,25 +127,26 @@ def loop_measure(torch, B, gen, batch=8, length=65536, n_steps=16, topk=2048, dr
     through, GPU slot) and runs the decode step with prefetch against the EMA estimate of the
     k-th score (alpha = 0.5).  8 requests x 65536 tokens, integer grid, top-2048, N_G = 131072
     with 65536 slots free at the start, consecutive queries alike (5% of q's bytes redrawn per
-    step).  Timed per step with HIP events around the two enqueues on their stream (the upload
-    of the step's query and new tokens precedes the start event).  Reports the pool hit rate of
+    step).  The whole step (stamp advance, append, decode step) is one captured graph replayed
+    every step; timed per step with HIP events around the replay on its stream (the upload of
+    the step's query and new tokens precedes the start event).  Reports the pool hit rate of
     the guaranteed recall, the rows prefetched and the EMA's prediction error per step."""
     from dsa_indexer_top_amd.runner import LoopRunner
     n_gpu = batch * length // 4
     m, host_kv = gen.make_multistep_inputs(batch, length, n_steps, n_gpu, seed=51,
                                            reserve=n_gpu // 2, drift=drift)
-    rn = LoopRunner(m, host_kv, topk, prefetch=True, pf=dict(n_chunks=4, cap=2048, cap_div=32))
+    rn = LoopRunner(m, host_kv, topk, prefetch=True, pf=dict(n_chunks=4, cap=2048, cap_div=32),
+                    device_step=True)
     steps = []
     try:
+        rn.capture()
         for st in m.steps:
             theta_used = rn.theta.cpu().numpy().astype(np.float64)
             rn.load_step(st)
             s = torch.cuda.Event(enable_timing=True)
             e = torch.cuda.Event(enable_timing=True)
-            rn.app.step_id = rn.args.step_id = int(st["step_id"])
             s.record(rn.main)
-            B.decode_append(rn.app, rn.pool, rn.new_slot, rn.ws_app, rn.main)
-            B.decode_select(rn.args, rn.pool, rn.out, rn.ws, rn.main)
+            rn.graph.launch(rn.main)
             e.record(rn.main)
             torch.cuda.synchronize()
             c = rn.counters.cpu().numpy()
@@ -164,7 +165,9 @@ def loop_measure(torch, B, gen, batch=8, length=65536, n_steps=16, topk=2048, dr
     return {"workload": "%d requests x %d tokens, %d steps, top-%d, integer grid, q drift %.2f, "
                         "N_G=%d (half free at the start), prefetch against the EMA estimate"
                         % (batch, length, n_steps, topk, drift, n_gpu),
-            "timing": "eager enqueue of echo_decode_append + echo_decode_select per step, HIP events",
+            "timing": "one captured graph (echo_step_advance + echo_decode_append + "
+                      "echo_decode_select, step stamp on the device) replayed per step; HIP "
+                      "events around each replay",
             "us_per_step_median": round(float(np.median([x["us"] for x in later])), 1),
             "hit_rate_median": round(float(np.median([x["hit_rate"] for x in later])), 4),
             "steps": steps}

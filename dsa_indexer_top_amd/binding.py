@@ -39,7 +39,7 @@ class DecodeArgs(C.Structure):
                 ("key_len", P), ("req_to_host", P), ("n_rows", I32), ("max_key_len", I32),
                 ("topk", I32), ("step_id", I32), ("prefetch", I32), ("n_chunks", I32),
                 ("n_sample", I32), ("percentile", F32), ("cap", I32), ("cap_div", I32),
-                ("theta_ema", P), ("ema_alpha", F32)]
+                ("theta_ema", P), ("ema_alpha", F32), ("step_dev", P)]
 
 
 class DecodeOut(C.Structure):
@@ -50,7 +50,8 @@ class DecodeOut(C.Structure):
 class AppendArgs(C.Structure):
     _fields_ = [("n_rows", I32), ("capacity", I32), ("n_k", I64), ("new_k", P), ("new_scale", P),
                 ("new_kv", P), ("new_host", P), ("k", P), ("k_scale", P), ("key_begin", P),
-                ("key_len", P), ("req_to_host", P), ("host_kv_w", P), ("step_id", I32)]
+                ("key_len", P), ("req_to_host", P), ("host_kv_w", P), ("step_id", I32),
+                ("step_dev", P)]
 
 
 _SIGS = {
@@ -79,6 +80,9 @@ _SIGS = {
     "echo_decode_append": (C.c_int, [C.POINTER(AppendArgs), C.POINTER(Pool), P, P, SZ, P]),
     "echo_graph_capture_decode": (C.c_int, [C.POINTER(DecodeArgs), C.POINTER(Pool),
                                             C.POINTER(DecodeOut), P, SZ, P, P, C.POINTER(P)]),
+    "echo_step_advance": (C.c_int, [P, P]),
+    "echo_graph_begin": (C.c_int, [P]),
+    "echo_graph_end": (C.c_int, [P, C.POINTER(P)]),
     "echo_graph_launch": (C.c_int, [P, P]),
     "echo_graph_destroy": (C.c_int, [P]),
     "echo_host_alloc": (C.c_int, [SZ, C.c_int, C.POINTER(P), C.POINTER(P)]),
@@ -232,6 +236,39 @@ def append_workspace_bytes(n_rows, n_gpu):
 def decode_append(args, pool, new_slot, ws, stream=None):
     _call("echo_decode_append", C.byref(args), C.byref(pool), ptr(new_slot), ptr(ws),
           ws.numel() * ws.element_size(), stream_handle(stream))
+
+
+def step_advance(step_dev, stream=None):
+    _call("echo_step_advance", ptr(step_dev), stream_handle(stream))
+
+
+class CapturedGraph:
+    """Whatever echo_* calls `enqueue(stream)` makes, captured into one graph
+    (echo_graph_begin / echo_graph_end); replay with launch()."""
+
+    def __init__(self, enqueue, stream):
+        self._h = P()
+        _call("echo_graph_begin", stream_handle(stream))
+        try:
+            enqueue(stream)
+        except Exception:
+            lib().echo_graph_end(stream_handle(stream), C.byref(P()))
+            raise
+        _call("echo_graph_end", stream_handle(stream), C.byref(self._h))
+
+    def launch(self, stream=None):
+        _call("echo_graph_launch", self._h, stream_handle(stream))
+
+    def close(self):
+        if self._h:
+            _call("echo_graph_destroy", self._h)
+            self._h = P()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class Graph:

@@ -115,11 +115,12 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
   const int nc = pf ? a->n_chunks : 1;
 
   if ((rc = launch_zero2_i32(o->counters, 8, reinterpret_cast<int32_t *>(W.hist0), W.zero_words, m))) return rc;
+  const Stamp stamp{a->step_id, a->step_dev};
   SideWork side{};
   side.P = PoolArgs{pool->gpu_free, pool->gpu_priority, pool->gpu_to_host, pool->host_to_gpu,
                     pool->indices_buf, pool->status, pool->n_gpu, pool->n_host};
   side.W = W.pool;
-  side.step_id = a->step_id;
+  side.stamp = stamp;
   side.n_stats = W.pool.n_chunks;                   // statistics ride with the first scoring launch
   // prefetch threshold: the caller's EMA estimate (§6.1), or a sample percentile of this
   // step's scores when there is no history
@@ -137,7 +138,7 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
         side.G = make_gather_args(pool, a->key_begin, a->req_to_host,
                                   W.cand + static_cast<int64_t>(c - 1) * a->n_rows * a->cap,
                                   W.cand_cnt + static_cast<int64_t>(c - 1) * a->n_rows, a->cap,
-                                  W.free_list, W.free_count, o->counters + 2, &W.pool, a->step_id);
+                                  W.free_list, W.free_count, o->counters + 2, &W.pool, stamp);
       }
       const int32_t lo = c * span, hi = (c + 1 == nc) ? a->max_key_len : (c + 1) * span;
       PrefetchArgs P{theta, a->req_to_host, pool->host_to_gpu,
@@ -153,7 +154,7 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
     const int64_t last = static_cast<int64_t>(nc - 1) * a->n_rows;
     if ((rc = launch_prefetch_gather(pool, a->key_begin, a->req_to_host, W.cand + last * a->cap,
                                      W.cand_cnt + last, a->n_rows, a->cap, W.free_list, W.free_count,
-                                     o->counters + 2, &W.pool, a->step_id, m)))
+                                     o->counters + 2, &W.pool, stamp, m)))
       return rc;
   } else {
     if ((rc = launch_score_decode(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len, a->n_rows,
@@ -163,13 +164,13 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
   }
   if ((rc = launch_topk_split(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,
                               a->topk, W.hist0, W.split, pool, &W.pool, a->key_begin, a->req_to_host,
-                              a->step_id, m)))
+                              stamp, m)))
     return rc;
   if ((rc = launch_topk_finish(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,
                                a->topk, W.hist0, W.split, o->topk_idx, pool, &W.pool, a->key_begin,
-                               a->req_to_host, a->step_id, o->topk_slot, true, W.stage, m)))
+                               a->req_to_host, stamp, o->topk_slot, true, W.stage, m)))
     return rc;
-  if ((rc = launch_pool_evict(pool, W.pool, o->topk_idx, a->n_rows, a->topk, a->step_id, o->topk_slot,
+  if ((rc = launch_pool_evict(pool, W.pool, o->topk_idx, a->n_rows, a->topk, stamp, o->topk_slot,
                               o->miss_host, o->miss_slot, o->counters + 0, W.stage, m)))
     return rc;
   if ((rc = launch_recall_scatter(pool, W.pool, o->miss_host, o->miss_slot, o->counters + 0, n_ent,
@@ -235,6 +236,44 @@ extern "C" int echo_graph_capture_decode(const echo_decode_args *a, const echo_p
     (void)hipGraphExecDestroy(ex);
     (void)hipGraphDestroy(g);
     return fail(ECHO_EHIP, "echo_graph_capture_decode: out of host memory");
+  }
+  h->graph = g;
+  h->exec = ex;
+  *graph = h;
+  return ECHO_OK;
+}
+
+extern "C" int echo_graph_begin(void *stream) {
+  if (!stream) return fail(ECHO_EINVAL, "echo_graph_begin: capture needs a non-null stream");
+  hipError_t e = hipStreamBeginCapture(S(stream), hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return fail(ECHO_EHIP, "hipStreamBeginCapture: %s", hipGetErrorString(e));
+  return ECHO_OK;
+}
+
+extern "C" int echo_graph_end(void *stream, echo_graph *graph) {
+  if (graph) *graph = nullptr;
+  if (!stream) return fail(ECHO_EINVAL, "echo_graph_end: NULL stream");
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamEndCapture(S(stream), &g);
+  if (e != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    return fail(ECHO_EHIP, "hipStreamEndCapture: %s", hipGetErrorString(e));
+  }
+  if (!graph) {
+    (void)hipGraphDestroy(g);
+    return fail(ECHO_EINVAL, "echo_graph_end: NULL graph");
+  }
+  hipGraphExec_t ex = nullptr;
+  e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return fail(ECHO_EHIP, "hipGraphInstantiate: %s", hipGetErrorString(e));
+  }
+  echo_graph_s *h = new (std::nothrow) echo_graph_s;
+  if (!h) {
+    (void)hipGraphExecDestroy(ex);
+    (void)hipGraphDestroy(g);
+    return fail(ECHO_EHIP, "echo_graph_end: out of host memory");
   }
   h->graph = g;
   h->exec = ex;

@@ -5,6 +5,15 @@
 
 namespace echo {
 
+// The step stamp, the priority given to the slots a step selects or fills: a host value, or a
+// device word that the caller advances between steps, so that one captured graph can serve every
+// step.  Kernels read it once at their start.
+struct Stamp {
+  int32_t value;
+  const int32_t *dev;        // nullptr: use value
+};
+ECHO_DEV int32_t stamp_of(const Stamp &s) { return s.dev ? *s.dev : s.value; }
+
 struct PrefetchArgs {
   const float *theta;        // [n_q]
   const int32_t *req_to_host;// [n_k]
@@ -84,20 +93,20 @@ struct GatherArgs {
   int32_t *n_prefetched;
   int32_t *st_free;           // optional pool-step statistics to keep current
   uint32_t *st_fine, *st_coarse;
-  int32_t step_id;
+  Stamp stamp;
 };
 GatherArgs make_gather_args(const echo_pool *pool, const int64_t *key_begin,
                             const int32_t *req_to_host, const int32_t *cand,
                             const int32_t *cand_cnt, int32_t cap, const int32_t *free_list,
                             int32_t *free_count, int32_t *n_prefetched, const PoolFastWs *pw,
-                            int32_t step_id);
+                            Stamp stamp);
 
 // Work that rides along in another kernel's launch as extra leading workgroups of 256 threads:
 // n_stats pool-statistics chunks (every occupied slot), then n_gather prefetch-gather requests.
 struct SideWork {
   PoolArgs P;
   PoolFastWs W;
-  int32_t step_id;
+  Stamp stamp;
   int32_t n_stats;
   int32_t n_gather;
   GatherArgs G;
@@ -107,11 +116,11 @@ void pool_fast_ws_layout(int32_t n_rows, int32_t k, int32_t n_gpu, void *base, P
 size_t pool_fast_ws_bytes(int32_t n_rows, int32_t k, int32_t n_gpu);
 // excl_prot: histogram only unprotected slots (after the lookup); otherwise all occupied
 // slots, and the lookup subtracts what it protects.
-int launch_pool_stats(const echo_pool *pool, const PoolFastWs &W, int32_t step_id, bool excl_prot,
+int launch_pool_stats(const echo_pool *pool, const PoolFastWs &W, Stamp stamp, bool excl_prot,
                       hipStream_t st);
 int launch_pool_lookup_rows(const echo_pool *pool, const PoolFastWs &W, const int32_t *idx,
                             const int64_t *key_begin, const int32_t *req_to_host, int64_t n_k,
-                            int32_t n_rows, int32_t k, int32_t step_id, int32_t *topk_slot,
+                            int32_t n_rows, int32_t k, Stamp stamp, int32_t *topk_slot,
                             hipStream_t st);
 // Missed rows copied into a staging area by workgroups riding along in the eviction launches.
 struct StageArgs {
@@ -122,12 +131,12 @@ struct StageArgs {
 // stage_cut_f / stage_cut_e split of r*k + [0, stage_a[r] + stage_b[r])) from host memory;
 // the caller then runs launch_recall_scatter.
 int launch_pool_evict(const echo_pool *pool, const PoolFastWs &W, const int32_t *idx, int32_t n_rows,
-                      int32_t k, int32_t step_id, int32_t *topk_slot, int32_t *miss_host,
+                      int32_t k, Stamp stamp, int32_t *topk_slot, int32_t *miss_host,
                       int32_t *miss_slot, int32_t *n_miss, uint16_t *stage, hipStream_t st);
 
 int launch_pool_step(const echo_pool *pool, const int32_t *idx, const int64_t *key_begin,
                      const int32_t *req_to_host, int64_t n_k, int32_t n_rows, int32_t k,
-                     int32_t step_id, int32_t *topk_slot, int32_t *miss_host, int32_t *miss_slot,
+                     Stamp stamp, int32_t *topk_slot, int32_t *miss_host, int32_t *miss_slot,
                      int32_t *n_miss, void *ws, size_t ws_bytes, hipStream_t st);
 
 // Decode top-k: split (multi-workgroup) then finish (one workgroup per request).  With a pool,
@@ -141,11 +150,11 @@ size_t topk_split_ws_bytes(int32_t n_rows, int32_t max_len, int32_t k);
 int launch_topk_split(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
                       int32_t max_len, int32_t k, const uint32_t *hist0, void *split_ws,
                       const echo_pool *pool, const PoolFastWs *pw, const int64_t *key_begin,
-                      const int32_t *req_to_host, int32_t step_id, hipStream_t st);
+                      const int32_t *req_to_host, Stamp stamp, hipStream_t st);
 int launch_topk_finish(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
                        int32_t max_len, int32_t k, const uint32_t *hist0, void *split_ws,
                        int32_t *idx, const echo_pool *pool, const PoolFastWs *pw,
-                       const int64_t *key_begin, const int32_t *req_to_host, int32_t step_id,
+                       const int64_t *key_begin, const int32_t *req_to_host, Stamp stamp,
                        int32_t *topk_slot, bool early, uint16_t *stage, hipStream_t st);
 
 int launch_recall_gather(const echo_pool *pool, const int32_t *miss_host, const int32_t *miss_slot,
@@ -163,12 +172,12 @@ int launch_prefetch_threshold(const uint8_t *q, const float *w, const uint8_t *k
 int launch_prefetch_begin(const echo_pool *pool, int32_t *free_list, int32_t *free_count,
                           hipStream_t st);
 // pw (optional): pool-step statistics (free count, priority histograms) updated for the slots
-// this call fills (priority 0 relative to step_id)
+// this call fills (priority 0 relative to the step stamp)
 int launch_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
                            const int32_t *req_to_host, const int32_t *cand,
                            const int32_t *cand_cnt, int32_t n_q, int32_t cap,
                            const int32_t *free_list, int32_t *free_count, int32_t *n_prefetched,
-                           const PoolFastWs *pw, int32_t step_id, hipStream_t st);
+                           const PoolFastWs *pw, Stamp stamp, hipStream_t st);
 int launch_zero_i32(int32_t *p, int64_t n, hipStream_t st);
 int launch_zero2_i32(int32_t *p, int64_t n, int32_t *q, int64_t m, hipStream_t st);
 int launch_sum_i32(const int32_t *v, int32_t n, int32_t *out, hipStream_t st);

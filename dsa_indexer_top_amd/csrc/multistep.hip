@@ -171,7 +171,7 @@ static int append_impl(const echo_append_args *a, const echo_pool *pool, int32_t
   int rc = check_launch("append");
   if (rc) return rc;
   if ((rc = launch_pool_step(pool, W.pos, a->key_begin, a->req_to_host, a->n_k, a->n_rows, 1,
-                             a->step_id, new_slot, W.miss_host, W.miss_slot, W.n_miss, W.pool,
+                             Stamp{a->step_id, a->step_dev}, new_slot, W.miss_host, W.miss_slot, W.n_miss, W.pool,
                              W.pool_bytes, st)))
     return rc;
   append_fill_kernel<<<a->n_rows, AP_THREADS, 0, st>>>(a->new_kv, new_slot, pool->gpu_kv,
@@ -179,9 +179,17 @@ static int append_impl(const echo_append_args *a, const echo_pool *pool, int32_t
   return check_launch("append_fill");
 }
 
+__global__ void step_advance_kernel(int32_t *step) { *step += 1; }
+
 }  // namespace echo
 
 using namespace echo;
+
+extern "C" int echo_step_advance(int32_t *step_dev, void *stream) {
+  if (!step_dev) return fail(ECHO_EINVAL, "echo_step_advance: NULL");
+  step_advance_kernel<<<1, 1, 0, S(stream)>>>(step_dev);
+  return check_launch("step_advance");
+}
 
 extern "C" size_t echo_append_workspace_bytes(int32_t n_rows, int32_t n_gpu) {
   if (n_rows < 0 || n_gpu < 0) return 0;

@@ -233,7 +233,7 @@ ECHO_DEV void gather_request(const GatherArgs &G, int r, uint32_t *lds) {
   if (G.st_free) {          // the new slots are occupied with priority 0 (pool-step statistics)
     n_ok = block_sum<PG_THREADS>(n_ok, tmp);
     if (threadIdx.x == 0 && n_ok) {
-      const uint32_t b = prio_bin(0, G.step_id);
+      const uint32_t b = prio_bin(0, stamp_of(G.stamp));
       atomicSub(G.st_free, static_cast<int32_t>(n_ok));
       atomicAdd(&G.st_fine[hist_at(b)], n_ok);
       atomicAdd(&G.st_coarse[hist_at(b >> 5)], n_ok);
@@ -247,7 +247,7 @@ constexpr int SIDE_LDS_WORDS = STATS_LDS_WORDS > PG_LDS_WORDS ? STATS_LDS_WORDS 
 ECHO_DEV bool side_work(const SideWork &S, int b, uint32_t *lds) {
   static_assert(PF_T == PG_THREADS, "side work shares one block size");
   if (b < S.n_stats) {
-    stats_chunk<false>(S.P, S.W, S.step_id, b, lds);
+    stats_chunk<false>(S.P, S.W, stamp_of(S.stamp), b, lds);
     return true;
   }
   if (b < S.n_stats + S.n_gather) {

@@ -90,17 +90,16 @@ size_t pool_fast_ws_bytes(int32_t n_rows, int32_t k, int32_t n_gpu) {
 // EXCL_PROT: leave protected slots out (stats taken after the lookup).  Without it the
 // histogram counts every occupied slot and the lookup subtracts the slots it protects.
 template <bool EXCL_PROT>
-__global__ __launch_bounds__(PF_T) void pool_stats_kernel(PoolArgs P, PoolFastWs W, int32_t step_id) {
+__global__ __launch_bounds__(PF_T) void pool_stats_kernel(PoolArgs P, PoolFastWs W, Stamp stamp) {
   __shared__ uint32_t lds[STATS_LDS_WORDS];
-  stats_chunk<EXCL_PROT>(P, W, step_id, blockIdx.x, lds);
+  stats_chunk<EXCL_PROT>(P, W, stamp_of(stamp), blockIdx.x, lds);
 }
 
 // Standalone lookup (echo_pool_lookup_alloc): one 1024-thread workgroup per request, entries in
 // order; misses go to the request's ordered list.
 __global__ __launch_bounds__(PF_RES_T) void pool_lookup_rows_kernel(
     PoolArgs P, PoolFastWs W, const int32_t *__restrict__ idx, const int64_t *__restrict__ key_begin,
-    const int32_t *__restrict__ req_to_host, int64_t n_k, int32_t k, int32_t step_id,
-    int32_t *__restrict__ topk_slot) {
+    const int32_t *__restrict__ req_to_host, int64_t n_k, int32_t k, int32_t *__restrict__ topk_slot) {
   __shared__ uint32_t tmp[48];
   const int r = blockIdx.x;
   uint32_t n_miss = 0;
@@ -219,9 +218,10 @@ ECHO_DEV void evict_slot(const PoolArgs &P, int32_t slot) {
 // blocks [0, n_rows): lay the misses out in global order; blocks [n_rows, n_rows + n_chunks):
 // slot chunks.
 __global__ __launch_bounds__(PF_T) void pool_evict1_kernel(PoolArgs P, PoolFastWs W, int32_t n_rows,
-                                                           int32_t k, int32_t step_id,
+                                                           int32_t k, Stamp stamp,
                                                            int32_t *__restrict__ miss_host,
                                                            StageArgs SA) {
+  const int32_t step_id = stamp_of(stamp);
   __shared__ uint32_t tmp[48];
   __shared__ uint32_t gscan[4 * (PF_T / 64) + PF_T / 64 + 2];
   if (static_cast<int>(blockIdx.x) >= n_rows + W.n_chunks) {
@@ -359,10 +359,11 @@ struct CandView {
 };
 
 __global__ __launch_bounds__(PF_RES_T) void pool_evict2_kernel(
-    PoolArgs P, PoolFastWs W, int32_t n_rows, int32_t k, int32_t step_id,
+    PoolArgs P, PoolFastWs W, int32_t n_rows, int32_t k, Stamp stamp,
     int32_t *__restrict__ miss_host, int32_t *__restrict__ miss_slot, int32_t *__restrict__ topk_slot,
     int32_t *__restrict__ n_miss_out, const int32_t *__restrict__ idx, int32_t entry_blocks,
     StageArgs SA) {
+  const int32_t step_id = stamp_of(stamp);
   __shared__ uint32_t tmp[48];
   __shared__ uint64_t cl[PF_CAP];
   __shared__ uint32_t hist[2048];
@@ -516,29 +517,30 @@ __global__ __launch_bounds__(PF_RES_T) void pool_evict2_kernel(
   }
 }
 
-int launch_pool_stats(const echo_pool *pool, const PoolFastWs &W, int32_t step_id, bool excl_prot,
+int launch_pool_stats(const echo_pool *pool, const PoolFastWs &W, Stamp stamp, bool excl_prot,
                       hipStream_t st) {
   PoolArgs P{pool->gpu_free, pool->gpu_priority, pool->gpu_to_host, pool->host_to_gpu,
              pool->indices_buf, pool->status, pool->n_gpu, pool->n_host};
-  if (excl_prot) pool_stats_kernel<true><<<W.n_chunks, PF_T, 0, st>>>(P, W, step_id);
-  else pool_stats_kernel<false><<<W.n_chunks, PF_T, 0, st>>>(P, W, step_id);
+  if (excl_prot) pool_stats_kernel<true><<<W.n_chunks, PF_T, 0, st>>>(P, W, stamp);
+  else pool_stats_kernel<false><<<W.n_chunks, PF_T, 0, st>>>(P, W, stamp);
   return check_launch("pool_stats");
 }
 
 int launch_pool_lookup_rows(const echo_pool *pool, const PoolFastWs &W, const int32_t *idx,
                             const int64_t *key_begin, const int32_t *req_to_host, int64_t n_k,
-                            int32_t n_rows, int32_t k, int32_t step_id, int32_t *topk_slot,
+                            int32_t n_rows, int32_t k, Stamp stamp, int32_t *topk_slot,
                             hipStream_t st) {
   PoolArgs P{pool->gpu_free, pool->gpu_priority, pool->gpu_to_host, pool->host_to_gpu,
              pool->indices_buf, pool->status, pool->n_gpu, pool->n_host};
   if (n_rows > 0)
     pool_lookup_rows_kernel<<<n_rows, PF_RES_T, 0, st>>>(P, W, idx, key_begin, req_to_host, n_k, k,
-                                                         step_id, topk_slot);
+                                                         topk_slot);
+  (void)stamp;                             // the lookup itself stamps nothing
   return check_launch("pool_lookup_rows");
 }
 
 int launch_pool_evict(const echo_pool *pool, const PoolFastWs &W, const int32_t *idx, int32_t n_rows,
-                      int32_t k, int32_t step_id, int32_t *topk_slot, int32_t *miss_host,
+                      int32_t k, Stamp stamp, int32_t *topk_slot, int32_t *miss_host,
                       int32_t *miss_slot, int32_t *n_miss, uint16_t *stage, hipStream_t st) {
   if (W.n_chunks > 1024) return fail(ECHO_EUNSUPPORTED, "pool: more than 4M slots");
   PoolArgs P{pool->gpu_free, pool->gpu_priority, pool->gpu_to_host, pool->host_to_gpu,
@@ -547,11 +549,11 @@ int launch_pool_evict(const echo_pool *pool, const PoolFastWs &W, const int32_t 
   StageArgs SA{pool->host_kv, stage};
   const int s1 = stage ? n_rows * ((k + 31) / 32) : 0;
   const int s2 = stage ? n_rows * ((k + 127) / 128) : 0;
-  pool_evict1_kernel<<<n_rows + W.n_chunks + s1, PF_T, 0, st>>>(P, W, n_rows, k, step_id, miss_host, SA);
+  pool_evict1_kernel<<<n_rows + W.n_chunks + s1, PF_T, 0, st>>>(P, W, n_rows, k, stamp, miss_host, SA);
   const int64_t n_ent = static_cast<int64_t>(n_rows) * k;
   const int entry_blocks = static_cast<int>(std::max<int64_t>(1, (n_ent + PF_RES_T - 1) / PF_RES_T));
   pool_evict2_kernel<<<W.n_chunks + entry_blocks + s2, PF_RES_T, 0, st>>>(
-      P, W, n_rows, k, step_id, miss_host, miss_slot, topk_slot, n_miss, idx, entry_blocks, SA);
+      P, W, n_rows, k, stamp, miss_host, miss_slot, topk_slot, n_miss, idx, entry_blocks, SA);
   return check_launch("pool_evict");
 }
 
@@ -572,7 +574,7 @@ __global__ void status_clear_kernel(int32_t *s) { *s = 0; }
 
 int launch_pool_step(const echo_pool *pool, const int32_t *idx, const int64_t *key_begin,
                      const int32_t *req_to_host, int64_t n_k, int32_t n_rows, int32_t k,
-                     int32_t step_id, int32_t *topk_slot, int32_t *miss_host, int32_t *miss_slot,
+                     Stamp stamp, int32_t *topk_slot, int32_t *miss_host, int32_t *miss_slot,
                      int32_t *n_miss, void *ws, size_t ws_bytes, hipStream_t st) {
   PoolFastWs W;
   size_t need;
@@ -580,11 +582,11 @@ int launch_pool_step(const echo_pool *pool, const int32_t *idx, const int64_t *k
   if (ws_bytes < need) return fail(ECHO_EWORKSPACE, "echo_pool_lookup_alloc: workspace %zu < %zu", ws_bytes, need);
   int rc;
   if ((rc = launch_zero_i32(W.counters, W.zero_words, st))) return rc;
-  if ((rc = launch_pool_lookup_rows(pool, W, idx, key_begin, req_to_host, n_k, n_rows, k, step_id,
+  if ((rc = launch_pool_lookup_rows(pool, W, idx, key_begin, req_to_host, n_k, n_rows, k, stamp,
                                     topk_slot, st)))
     return rc;
-  if ((rc = launch_pool_stats(pool, W, step_id, true, st))) return rc;
-  return launch_pool_evict(pool, W, idx, n_rows, k, step_id, topk_slot, miss_host, miss_slot, n_miss,
+  if ((rc = launch_pool_stats(pool, W, stamp, true, st))) return rc;
+  return launch_pool_evict(pool, W, idx, n_rows, k, stamp, topk_slot, miss_host, miss_slot, n_miss,
                            nullptr, st);
 }
 
@@ -619,7 +621,7 @@ extern "C" int echo_pool_lookup_alloc(const echo_pool *pool, const int32_t *idx,
   if (static_cast<int64_t>(n_rows) * k > (1LL << 30)) return fail(ECHO_EUNSUPPORTED, "echo_pool_lookup_alloc: too many entries");
   if (!idx || !key_begin || !req_to_host || !topk_slot || !miss_host || !miss_slot || !n_miss || !ws)
     return fail(ECHO_EINVAL, "echo_pool_lookup_alloc: NULL pointer");
-  return launch_pool_step(pool, idx, key_begin, req_to_host, n_k, n_rows, k, step_id, topk_slot,
+  return launch_pool_step(pool, idx, key_begin, req_to_host, n_k, n_rows, k, Stamp{step_id, nullptr}, topk_slot,
                           miss_host, miss_slot, n_miss, ws, ws_bytes, S(stream));
 }
 

@@ -125,22 +125,22 @@ GatherArgs make_gather_args(const echo_pool *pool, const int64_t *key_begin,
                             const int32_t *req_to_host, const int32_t *cand,
                             const int32_t *cand_cnt, int32_t cap, const int32_t *free_list,
                             int32_t *free_count, int32_t *n_prefetched, const PoolFastWs *pw,
-                            int32_t step_id) {
+                            Stamp stamp) {
   return GatherArgs{pool->host_kv, pool->gpu_kv, pool->gpu_free, pool->gpu_priority,
                     pool->gpu_to_host, pool->host_to_gpu, pool->status, pool->n_gpu, pool->n_host,
                     key_begin, req_to_host, cand, cand_cnt, cap, free_list, free_count,
                     n_prefetched, pw ? pw->counters : nullptr, pw ? pw->fine : nullptr,
-                    pw ? pw->coarse : nullptr, step_id};
+                    pw ? pw->coarse : nullptr, stamp};
 }
 
 int launch_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
                            const int32_t *req_to_host, const int32_t *cand,
                            const int32_t *cand_cnt, int32_t n_q, int32_t cap,
                            const int32_t *free_list, int32_t *free_count, int32_t *n_prefetched,
-                           const PoolFastWs *pw, int32_t step_id, hipStream_t st) {
+                           const PoolFastWs *pw, Stamp stamp, hipStream_t st) {
   if (n_q == 0 || cap == 0) return ECHO_OK;
   prefetch_gather_kernel<<<n_q, PG_THREADS, 0, st>>>(make_gather_args(
-      pool, key_begin, req_to_host, cand, cand_cnt, cap, free_list, free_count, n_prefetched, pw, step_id));
+      pool, key_begin, req_to_host, cand, cand_cnt, cap, free_list, free_count, n_prefetched, pw, stamp));
   return check_launch("prefetch_gather");
 }
 
@@ -194,5 +194,5 @@ extern "C" int echo_prefetch_gather(const echo_pool *pool, const int64_t *key_be
   if (n_q > 0 && cap > 0 && (!key_begin || !req_to_host || !cand || !cand_cnt || !free_list || !free_count || !n_prefetched))
     return fail(ECHO_EINVAL, "echo_prefetch_gather: NULL pointer");
   return launch_prefetch_gather(pool, key_begin, req_to_host, cand, cand_cnt, n_q, cap, free_list,
-                                free_count, n_prefetched, nullptr, 0, S(stream));
+                                free_count, n_prefetched, nullptr, Stamp{0, nullptr}, S(stream));
 }

@@ -126,7 +126,7 @@ struct SplitLookup {
   PoolFastWs W;
   const int64_t *key_begin;
   const int32_t *req_to_host;
-  int32_t step_id;
+  Stamp stamp;
 };
 
 static SplitWs make_split_ws(void *base, int32_t n_rows, int32_t max_len, int32_t k) {
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(TS_T) void topk_split_kernel(const float *__restric
         old[i] = hit[i] ? atomicOr(&L.W.prot[slot[i] >> 5], 1u << (slot[i] & 31)) : ~0u;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        bins[i] = (hit[i] && !((old[i] >> (slot[i] & 31)) & 1u)) ? prio_bin(pr[i], L.step_id) : 0xFFFFFFFFu;
+        bins[i] = (hit[i] && !((old[i] >> (slot[i] & 31)) & 1u)) ? prio_bin(pr[i], stamp_of(L.stamp)) : 0xFFFFFFFFu;
       // misses: staging rows r*k + [stage_a[r], ...), reserved once per workgroup
       uint32_t mo[4], n_m;
       group_excl_scan<TS_T, 4>(miss, mo, gscan, &n_m);
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
     int32_t k, const uint32_t *__restrict__ hist0, SplitWs W, int32_t *__restrict__ idx,
     // lookup (skipped when pool.n_gpu == 0)
     PoolArgs P, PoolFastWs PW, const int64_t *__restrict__ key_begin,
-    const int32_t *__restrict__ req_to_host, int32_t step_id, int32_t *__restrict__ topk_slot,
+    const int32_t *__restrict__ req_to_host, Stamp stamp, int32_t *__restrict__ topk_slot,
     bool sub_prot, bool early, int32_t n_rows, StageArgs SA) {
   if (static_cast<int>(blockIdx.x) >= n_rows) {
     // staging of (most of) the misses the split's early lookup found
@@ -534,7 +534,7 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
       old[i] = hit[i] ? atomicOr(&PW.prot[slot[i] >> 5], 1u << (slot[i] & 31)) : ~0u;
 #pragma unroll
     for (int i = 0; i < LJ; ++i)
-      pbin[i] = (hit[i] && !((old[i] >> (slot[i] & 31)) & 1u)) ? prio_bin(pr[i], step_id) : 0xFFFFFFFFu;
+      pbin[i] = (hit[i] && !((old[i] >> (slot[i] & 31)) & 1u)) ? prio_bin(pr[i], stamp_of(stamp)) : 0xFFFFFFFFu;
     hist_flush_bins<TF_T, LJ, true, 2 * TF_CAP>(pbin, cbuf, tmp, PW.fine, PW.coarse);
   } else {
 #pragma unroll
@@ -572,7 +572,7 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
 int launch_topk_split(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
                       int32_t max_len, int32_t k, const uint32_t *hist0, void *split_ws,
                       const echo_pool *pool, const PoolFastWs *pw, const int64_t *key_begin,
-                      const int32_t *req_to_host, int32_t step_id, hipStream_t st) {
+                      const int32_t *req_to_host, Stamp stamp, hipStream_t st) {
   if (n_rows == 0) return ECHO_OK;
   if ((max_len + TS_CH - 1) / TS_CH > 1024) return fail(ECHO_EUNSUPPORTED, "decode top-k: rows longer than 4M tokens");
   SplitWs W = make_split_ws(split_ws, n_rows, max_len, k);
@@ -585,7 +585,7 @@ int launch_topk_split(const float *scores, int64_t ld, const int32_t *len, int32
     L.W = *pw;
     L.key_begin = key_begin;
     L.req_to_host = req_to_host;
-    L.step_id = step_id;
+    L.stamp = stamp;
     topk_split_kernel<true><<<static_cast<unsigned>(blocks), TS_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W, L);
   } else {
     topk_split_kernel<false><<<static_cast<unsigned>(blocks), TS_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W, L);
@@ -596,7 +596,7 @@ int launch_topk_split(const float *scores, int64_t ld, const int32_t *len, int32
 int launch_topk_finish(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
                        int32_t max_len, int32_t k, const uint32_t *hist0, void *split_ws,
                        int32_t *idx, const echo_pool *pool, const PoolFastWs *pw,
-                       const int64_t *key_begin, const int32_t *req_to_host, int32_t step_id,
+                       const int64_t *key_begin, const int32_t *req_to_host, Stamp stamp,
                        int32_t *topk_slot, bool early, uint16_t *stage, hipStream_t st) {
   if (n_rows == 0) return ECHO_OK;
   SplitWs W = make_split_ws(split_ws, n_rows, max_len, k);
@@ -614,7 +614,7 @@ int launch_topk_finish(const float *scores, int64_t ld, const int32_t *len, int3
     }
   }
   topk_finish_kernel<<<n_rows + extra, TF_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W, idx, P, PW,
-                                                      key_begin, req_to_host, step_id, topk_slot,
+                                                      key_begin, req_to_host, stamp, topk_slot,
                                                       pool != nullptr, early && pool != nullptr, n_rows, SA);
   return check_launch("topk_finish");
 }

@@ -116,10 +116,14 @@ class LoopRunner:
     """Device buffers of several decode steps in a row (inputs.MultiStepInputs): the K cache with
     room for the new tokens, the pool, the pinned host backup (the appends write through to it),
     one step's inputs and the EMA estimate of the k-th score.  run_step(st) uploads step st's
-    query and new tokens, then enqueues echo_decode_append and echo_decode_select.  No arithmetic
-    of the method lives here."""
+    query and new tokens, then enqueues echo_decode_append and echo_decode_select.  With
+    device_step=True the step stamp lives on the device; capture() then records
+    echo_step_advance + echo_decode_append + echo_decode_select as one graph, and
+    replay_step(st) uploads step st's inputs and replays it.  No arithmetic of the method lives
+    here."""
 
-    def __init__(self, m, host_kv, topk, prefetch=False, pf=None, alpha=0.5, ema=True):
+    def __init__(self, m, host_kv, topk, prefetch=False, pf=None, alpha=0.5, ema=True,
+                 device_step=False):
         import torch
         self.torch = torch
         self.m = m
@@ -184,6 +188,29 @@ class LoopRunner:
         self.ws_app = torch.empty(max(B.append_workspace_bytes(B_, self.n_gpu), 256),
                                   dtype=torch.uint8, device=dev)
         self.main = torch.cuda.Stream()
+        self.step_dev = None
+        self.graph = None
+        if device_step:
+            # advanced to the first step's stamp by the first replay
+            first = int(m.steps[0]["step_id"]) if m.steps else int(m.pool.step_id)
+            self.step_dev = torch.full((1,), first - 1, dtype=i32, device=dev)
+            self.args.step_dev = self.app.step_dev = self.step_dev.data_ptr()
+
+    def _enqueue_step(self, stream):
+        if self.step_dev is not None:
+            B.step_advance(self.step_dev, stream)
+        B.decode_append(self.app, self.pool, self.new_slot, self.ws_app, stream)
+        B.decode_select(self.args, self.pool, self.out, self.ws, stream)
+
+    def capture(self):
+        assert self.step_dev is not None, "a replayable step needs the stamp on the device"
+        self.torch.cuda.synchronize()
+        self.graph = B.CapturedGraph(self._enqueue_step, self.main)
+        return self.graph
+
+    def replay_step(self, st):
+        self.load_step(st)
+        self.graph.launch(self.main)
 
     def load_step(self, st):
         t = self.torch
@@ -199,8 +226,7 @@ class LoopRunner:
     def run_step(self, st):
         self.load_step(st)
         self.app.step_id = self.args.step_id = int(st["step_id"])
-        B.decode_append(self.app, self.pool, self.new_slot, self.ws_app, self.main)
-        B.decode_select(self.args, self.pool, self.out, self.ws, self.main)
+        self._enqueue_step(self.main)
 
     def results(self):
         self.torch.cuda.synchronize()
@@ -215,4 +241,7 @@ class LoopRunner:
                     host_kv=self.host_kv.copy())
 
     def close(self):
+        if self.graph is not None:
+            self.graph.close()
+            self.graph = None
         self.host_buf.close()

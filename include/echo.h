@@ -279,6 +279,9 @@ typedef struct {
      fmaf(ema_alpha, theta, (1 - ema_alpha) * kth); a request with no selection keeps it. */
   float *theta_ema;
   float ema_alpha;           /* the page uses 0.5 */
+  /* [1] or NULL: when given, the step stamp is read on the device from *step_dev instead of
+     step_id, so that one captured graph can serve every step (echo_step_advance moves it on) */
+  const int32_t *step_dev;
 } echo_decode_args;
 
 typedef struct {             /* device outputs of one step */
@@ -333,10 +336,18 @@ typedef struct {
   uint16_t *host_kv_w;       /* WRITABLE device-mapped pointer to the pool's host backup
                                 (the same memory as echo_pool.host_kv) */
   int32_t step_id;
+  const int32_t *step_dev;   /* [1] or NULL: the step stamp read on the device (as in
+                                echo_decode_args) */
 } echo_append_args;
 size_t echo_append_workspace_bytes(int32_t n_rows, int32_t n_gpu);
 int echo_decode_append(const echo_append_args *a, const echo_pool *pool, int32_t *new_slot,
                        void *ws, size_t ws_bytes, void *stream);
+
+/* *step_dev += 1, enqueued on `stream` (one thread).  With the stamp on the device, a captured
+ * sequence echo_step_advance -> echo_decode_append -> echo_decode_select is one whole decode
+ * step that can be replayed for every step (the caller refreshes the step's query and new
+ * tokens in the same device buffers between replays).  ECHO_EINVAL for NULL. */
+int echo_step_advance(int32_t *step_dev, void *stream);
 
 /* Graph helpers (host side; they create HIP objects).  Capture one echo_decode_select into a
  * hipGraph on `main_stream`, instantiate it, and replay it.  The graph
@@ -347,6 +358,14 @@ int echo_graph_capture_decode(const echo_decode_args *a, const echo_pool *pool,
                               void *main_stream, void *side_stream, echo_graph *graph);
 int echo_graph_launch(echo_graph graph, void *stream);
 int echo_graph_destroy(echo_graph graph);
+
+/* Capture of any sequence of echo_* calls enqueued on `stream` between the two calls (host side;
+ * they create HIP objects): echo_graph_begin starts a stream capture, echo_graph_end ends it and
+ * instantiates the graph (launch with echo_graph_launch, free with echo_graph_destroy).  Calls
+ * that synchronise (echo_recall in ECHO_RECALL_MEMCPY mode) cannot be captured.  A failed
+ * echo_graph_end leaves *graph NULL and the stream no longer capturing. */
+int echo_graph_begin(void *stream);
+int echo_graph_end(void *stream, echo_graph *graph);
 
 /* Pinned, device-mapped host memory for the host backup (hipHostMalloc, mapped; coherent when
  * `coherent` != 0).  *host receives the host pointer, *dev the device-side pointer to pass as

@@ -160,6 +160,9 @@ def test_decode_append_and_ema_argument_errors():
     assert L.echo_decode_append(C.byref(a), C.byref(p), slot, FAKE, short, None) == B.ECHO_EWORKSPACE
     assert L.echo_append_workspace_bytes(-1, 8) == 0
     assert L.echo_append_workspace_bytes(8, 1 << 20) > L.echo_append_workspace_bytes(8, 1024)
+    assert L.echo_step_advance(None, None) == B.ECHO_EINVAL
+    assert L.echo_graph_begin(None) == B.ECHO_EINVAL
+    assert L.echo_graph_end(None, None) == B.ECHO_EINVAL
     # the EMA weight must lie in [0, 1] when an estimate buffer is given
     for alpha in (-0.5, 1.5, float("nan")):
         d = _decode_args(theta_ema=FAKE, ema_alpha=alpha)

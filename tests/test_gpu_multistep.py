@@ -40,17 +40,26 @@ def _theta_close(got, want, kth_hist):
     assert (np.abs(got.astype(np.float64) - want) <= 2.0 ** -20 * scale).all(), (got, want)
 
 
-@pytest.mark.parametrize("B_,L,T,k,n_gpu", [(3, 300, 5, 32, 120), (2, 1100, 4, 256, 600)])
-def test_multistep_exact(B_, L, T, k, n_gpu):
-    announce("multistep exact", B_, L, T, k, n_gpu)
+@pytest.mark.parametrize("B_,L,T,k,n_gpu,mode", [
+    (3, 300, 5, 32, 120, "eager"), (2, 1100, 4, 256, 600, "eager"),
+    (3, 300, 5, 32, 120, "graph"), (2, 1100, 4, 256, 600, "graph")])
+def test_multistep_exact(B_, L, T, k, n_gpu, mode):
+    # graph: the stamp on the device, advance + append + step captured once and replayed for
+    # every step, with the step's uploads and the checks (eager work) between replays
+    announce("multistep exact", B_, L, T, k, n_gpu, mode)
     m, host_kv = gen.make_multistep_inputs(B_, L, T, n_gpu, seed=31 + L)
     cache, st = _oracle_start(m)
     _, _, hk_want, recs = ms.decode_loop(cache, st, host_kv, m.steps, k)
-    rn = LoopRunner(m, host_kv, k)
+    rn = LoopRunner(m, host_kv, k, device_step=mode == "graph")
     try:
+        if mode == "graph":
+            rn.capture()
         kth_hist = []
         for t, s in enumerate(m.steps):
-            rn.run_step(s)
+            if mode == "graph":
+                rn.replay_step(s)
+            else:
+                rn.run_step(s)
             got = rn.results()
             rec = recs[t]
             assert got["status"] == 0, "step %d status %d" % (t, got["status"])
