@@ -123,9 +123,10 @@ class StepRecord:
     append_status: int
 
 
-def decode_loop(cache, state, host_kv, steps, topk_k, alpha=0.5, theta0=None):
+def decode_loop(cache, state, host_kv, steps, topk_k, alpha=0.5, theta0=None, reserve=0):
     """Runs the steps in order.  steps: list of dicts with q [B,64,128], w [B,64], new_k [B,128],
-    new_scale [B] or None, new_kv [B,576], new_host [B], step_id.  Returns
+    new_scale [B] or None, new_kv [B,576], new_host [B], step_id.  reserve: free slots each
+    step's guaranteed recall leaves for the next step's prefetch (pool.pool_step).  Returns
     (cache, state, host_kv, [StepRecord])."""
     n_rows = len(cache.key_len)
     theta = np.full(n_rows, np.nan) if theta0 is None else np.asarray(theta0, np.float64)
@@ -138,7 +139,7 @@ def decode_loop(cache, state, host_kv, steps, topk_k, alpha=0.5, theta0=None):
                               cache.key_len)
         idx = topk_rows(scores, topk_k)
         state, res = pool_step(state, host_kv, idx, cache.key_begin, cache.req_to_host,
-                               st["step_id"])
+                               st["step_id"], reserve)
         kth = kth_scores(scores, idx)
         nxt = ema_update(theta, kth, alpha)
         records.append(StepRecord(scores, idx, kth, theta, nxt, slot, state, res, ast))

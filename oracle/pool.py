@@ -24,7 +24,11 @@ Readings where the page is silent or leaves several results correct:
 * Eviction happens only when the free slots do not cover the misses: evict
   need = |M| - #free unprotected occupied slots, those with the smallest
   (priority, slot index).  Too few candidates -> status EXHAUSTED and the
-  pool is left untouched.
+  pool is left untouched.  With a reserve R > 0 (room for the next step's
+  prefetch, which only takes free slots), the step evicts as many more of the
+  same order as it takes to leave R slots free after the allocation, as far
+  as unprotected occupied slots allow: need = min(max(0, |M| + R - #free),
+  #candidates); only |M| - #free > #candidates is EXHAUSTED.
 * Allocation order: the atomic-rank result depends on thread timing, so
   several results are correct.  The canonical rule used for parity: the i-th
   miss takes the i-th free slot in ascending slot order (after eviction).
@@ -115,13 +119,14 @@ def _selected(sel_idx, key_begin, req_to_host):
     return rows.astype(np.int64), cols.astype(np.int64), hosts
 
 
-def pool_step(state, host_kv, sel_idx, key_begin, req_to_host, step_id):
+def pool_step(state, host_kv, sel_idx, key_begin, req_to_host, step_id, reserve=0):
     """One guaranteed-residency step for the selected tokens.
 
     state is not modified; returns (new_state, PoolStepResult).
     sel_idx: int [n_rows, k] token indices per request (-1 = none);
     key_begin[r]: offset of request r in req_to_host; req_to_host: int [n_k]
-    host index of every cached token; host_kv: uint16 [N_H, 576].
+    host index of every cached token; host_kv: uint16 [N_H, 576]; reserve:
+    free slots to leave after the allocation (see the module notes).
     """
     n_rows, k = sel_idx.shape
     n_list = n_rows * k
@@ -148,10 +153,10 @@ def pool_step(state, host_kv, sel_idx, key_begin, req_to_host, step_id):
     protected = np.zeros(state.n_gpu, bool)
     protected[slot_of[hit]] = True
     n_free = int((state.free == 1).sum())
-    need = max(0, n_miss - n_free)
     cand = np.flatnonzero((state.free == 0) & ~protected)
-    if need > len(cand):
+    if max(0, n_miss - n_free) > len(cand):
         return state, PoolStepResult(out_slot, miss_host, miss_slot, n_miss, 0, ST_EXHAUSTED)
+    need = min(max(0, n_miss + int(reserve) - n_free), len(cand))
     new = state.copy()
     # smallest (priority, slot): lexsort keys, last key is primary
     evict = cand[np.lexsort((cand, state.priority[cand]))[:need]]

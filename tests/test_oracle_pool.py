@@ -107,6 +107,40 @@ def test_eviction_brute_force_tiny():
                               protected_before=sorted(protected))
 
 
+@pytest.mark.parametrize("reserve", [1, 3, 8])
+def test_eviction_reserve_brute_force_tiny(reserve):
+    # with room kept for prefetch, the step evicts further down the same (priority, slot)
+    # order until `reserve` slots stay free after the allocation, as far as unprotected slots go
+    rng = np.random.default_rng(40 + reserve)
+    for trial in range(60):
+        n_gpu, n_host = 8, 24
+        st, host_kv = _random_pool(rng, n_gpu, n_host, n_occ=int(rng.integers(5, 9)))
+        sel, kb, r2h = _one_request(rng, n_host, n_sel=int(rng.integers(1, 6)))
+        hosts = r2h[sel[0]]
+        protected = {int(st.host_to_gpu[h]) for h in hosts if st.host_to_gpu[h] != INF}
+        n_miss = sum(1 for h in hosts if st.host_to_gpu[h] == INF)
+        n_free = int(st.free.sum())
+        n_cand = sum(1 for e in range(n_gpu) if st.free[e] == 0 and e not in protected)
+        new, res = pool_step(st, host_kv, sel, kb, r2h, step_id=100, reserve=reserve)
+        if n_miss - n_free > n_cand:
+            assert res.status == ST_EXHAUSTED
+            continue
+        need = min(max(0, n_miss + reserve - n_free), n_cand)
+        assert res.status == 0 and res.n_evicted == need
+        evicted = {e for e in range(n_gpu) if st.free[e] == 0 and e not in protected
+                   and new.to_host[e] != st.to_host[e]}
+        assert evicted == _brute_force_evicted(st, protected, need)
+        # free slots afterwards: at least the reserve, or every unprotected slot gone
+        left = int(new.free.sum())
+        assert left == max(reserve, n_free - n_miss) or (left < reserve and need == n_cand)
+        check_pool_invariants(new, host_kv, hosts, res.topk_slot[0][res.topk_slot[0] >= 0],
+                              protected_before=sorted(protected))
+        # reserve 0 reduces to the plain step
+        if reserve == 1:
+            plain, r0 = pool_step(st, host_kv, sel, kb, r2h, step_id=100)
+            assert r0.n_evicted == max(0, n_miss - n_free)
+
+
 def test_step_postconditions_random():
     rng = np.random.default_rng(22)
     for trial in range(20):
