@@ -125,18 +125,18 @@ def prefill_measure(torch, B, gen, reps=5):
 def loop_measure(torch, B, gen, batch=8, length=65536, n_steps=16, topk=2048, drift=0.05):
     """Decode steps in a row: every step appends one token per request (key, host row written
     through, GPU slot) and runs the decode step with prefetch against the EMA estimate of the
-    k-th score (alpha = 0.5).  8 requests x 65536 tokens, integer grid, top-2048, N_G = 131072
-    with 65536 slots free at the start, consecutive queries alike (5% of q's bytes redrawn per
-    step).  The whole step (stamp advance, append, decode step) is one captured graph replayed
+    k-th score (alpha = 0.5).  8 requests x 65536 tokens, integer grid, top-2048, a full pool of
+    N_G = 65536 slots whose guaranteed recall leaves 8 x 2048 slots free for the next step's
+    prefetch, consecutive queries alike (5% of q's bytes redrawn per step).  The whole step (stamp advance, append, decode step) is one captured graph replayed
     every step; timed per step with HIP events around the replay on its stream (the upload of
     the step's query and new tokens precedes the start event).  Reports the pool hit rate of
     the guaranteed recall, the rows prefetched and the EMA's prediction error per step."""
     from dsa_indexer_top_amd.runner import LoopRunner
-    n_gpu = batch * length // 4
-    m, host_kv = gen.make_multistep_inputs(batch, length, n_steps, n_gpu, seed=51,
-                                           reserve=n_gpu // 2, drift=drift)
+    n_gpu = batch * length // 8
+    reserve = batch * topk                     # room for a full step of prefetch
+    m, host_kv = gen.make_multistep_inputs(batch, length, n_steps, n_gpu, seed=51, drift=drift)
     rn = LoopRunner(m, host_kv, topk, prefetch=True, pf=dict(n_chunks=4, cap=2048, cap_div=32),
-                    device_step=True)
+                    device_step=True, reserve=reserve)
     steps = []
     try:
         rn.capture()
@@ -163,8 +163,8 @@ def loop_measure(torch, B, gen, batch=8, length=65536, n_steps=16, topk=2048, dr
         rn.close()
     later = steps[1:]
     return {"workload": "%d requests x %d tokens, %d steps, top-%d, integer grid, q drift %.2f, "
-                        "N_G=%d (half free at the start), prefetch against the EMA estimate"
-                        % (batch, length, n_steps, topk, drift, n_gpu),
+                        "full pool N_G=%d with %d slots kept free for prefetch, prefetch against "
+                        "the EMA estimate" % (batch, length, n_steps, topk, drift, n_gpu, reserve),
             "timing": "one captured graph (echo_step_advance + echo_decode_append + "
                       "echo_decode_select, step stamp on the device) replayed per step; HIP "
                       "events around each replay",

@@ -39,7 +39,7 @@ class DecodeArgs(C.Structure):
                 ("key_len", P), ("req_to_host", P), ("n_rows", I32), ("max_key_len", I32),
                 ("topk", I32), ("step_id", I32), ("prefetch", I32), ("n_chunks", I32),
                 ("n_sample", I32), ("percentile", F32), ("cap", I32), ("cap_div", I32),
-                ("theta_ema", P), ("ema_alpha", F32), ("step_dev", P)]
+                ("theta_ema", P), ("ema_alpha", F32), ("step_dev", P), ("reserve_free", I32)]
 
 
 class DecodeOut(C.Structure):

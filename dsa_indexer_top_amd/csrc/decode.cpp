@@ -100,6 +100,8 @@ static int validate(const echo_decode_args *a, const echo_pool *pool, const echo
   }
   if (a->theta_ema && !(a->ema_alpha >= 0.f && a->ema_alpha <= 1.f))
     return fail(ECHO_EINVAL, "echo_decode_select: ema_alpha outside [0, 1]");
+  if (a->reserve_free < 0 || a->reserve_free > pool->n_gpu)
+    return fail(ECHO_EINVAL, "echo_decode_select: reserve_free outside [0, n_gpu]");
   return ECHO_OK;
 }
 
@@ -110,6 +112,7 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
   DecodeWs W{};
   const size_t need = decode_ws_layout(a, pool->n_gpu, ws, &W);
   if (!ws || ws_bytes < need) return fail(ECHO_EWORKSPACE, "echo_decode_select: workspace %zu < %zu", ws_bytes, need);
+  W.pool.reserve = static_cast<uint32_t>(a->reserve_free);
   const int32_t n_ent = a->n_rows * a->topk;
   const bool pf = a->prefetch != 0;
   const int nc = pf ? a->n_chunks : 1;

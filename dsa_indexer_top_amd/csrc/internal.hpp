@@ -74,6 +74,7 @@ struct PoolFastWs {
   void *base;
   int32_t n_chunks;
   int64_t zero_words;
+  uint32_t reserve;       // free slots the eviction leaves after allocation (prefetch room)
 };
 // Prefetch gather of one scoring range's candidates (one workgroup per request).
 struct GatherArgs {

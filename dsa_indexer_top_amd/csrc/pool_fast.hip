@@ -57,6 +57,7 @@ void pool_fast_ws_layout(int32_t n_rows, int32_t k, int32_t n_gpu, void *base, P
   *bytes = off;
   w->n_chunks = n_chunks;
   w->zero_words = static_cast<int64_t>(zero_end / 4);
+  w->reserve = 0;
   if (base) {
     char *b = static_cast<char *>(base);
     w->counters = reinterpret_cast<int32_t *>(b + o_cnt);
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(PF_RES_T) void pool_lookup_rows_kernel(
 constexpr int CT_FB = 2, CT_BELOW = 3, CT_NMISS = 4, CT_NEED = 5, CT_ABORT = 6;
 
 struct StepState {
-  uint32_t n_miss, need, evictable, fb, below;
+  uint32_t n_miss, must, need, evictable, fb, below;
   bool abort;
 };
 
@@ -159,8 +160,12 @@ ECHO_DEV StepState step_pick(const PoolArgs &P, const PoolFastWs &W, int32_t n_r
   StepState s;
   const uint32_t before = block_excl_scan<PF_T>(local, tmp, &s.evictable);
   s.n_miss = block_sum<PF_T>(nm, tmp);
-  s.need = s.n_miss > n_free ? s.n_miss - n_free : 0u;
-  s.abort = status != 0 || s.need > s.evictable;
+  // must: evictions the misses need; need: those plus the ones that leave W.reserve slots free
+  // for the next step's prefetch, as far as evictable slots allow
+  const uint32_t want = s.n_miss + W.reserve;
+  s.must = s.n_miss > n_free ? s.n_miss - n_free : 0u;
+  s.need = min(want > n_free ? want - n_free : 0u, s.evictable);
+  s.abort = status != 0 || s.must > s.evictable;
   s.fb = 0xFFFFFFFFu;
   s.below = 0;
   if (s.abort || s.need == 0) return s;
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(PF_T) void pool_evict1_kernel(PoolArgs P, PoolFastW
     W.counters[CT_NMISS] = static_cast<int32_t>(st.n_miss);
     W.counters[CT_NEED] = static_cast<int32_t>(st.need);
     W.counters[CT_ABORT] = st.abort ? 1 : 0;
-    if (st.abort && st.need > st.evictable && !(*(volatile int32_t *)P.status))
+    if (st.abort && st.must > st.evictable && !(*(volatile int32_t *)P.status))
       atomicOr(P.status, ECHO_ST_EXHAUSTED);
   }
   if (st.abort) return;

@@ -20,7 +20,7 @@ class DecodeRunner:
     array, or a binding.HostBuffer already holding it (pass host_buf=...)."""
 
     def __init__(self, inp, pool, host_kv=None, host_buf=None, prefetch=False, pf=None,
-                 topk=None, step_id=None):
+                 topk=None, step_id=None, reserve=0):
         import torch
         self.torch = torch
         cfg = inp.cfg
@@ -69,6 +69,7 @@ class DecodeRunner:
             self.key_begin.data_ptr(), self.key_len.data_ptr(), self.req_to_host.data_ptr(),
             self.n_rows, self.max_len, self.topk, self.step_id, 1 if prefetch else 0,
             p["n_chunks"], p["n_sample"], p["percentile"], p["cap"], p["cap_div"])
+        self.args.reserve_free = reserve
         nbytes = B.decode_workspace_bytes(self.args, self.n_gpu)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
         self.main = torch.cuda.Stream()
@@ -123,7 +124,7 @@ class LoopRunner:
     here."""
 
     def __init__(self, m, host_kv, topk, prefetch=False, pf=None, alpha=0.5, ema=True,
-                 device_step=False):
+                 device_step=False, reserve=0):
         import torch
         self.torch = torch
         self.m = m
@@ -176,6 +177,7 @@ class LoopRunner:
             B_, cap, topk, 0, 1 if prefetch else 0, p["n_chunks"], p["n_sample"],
             p["percentile"], p["cap"], p["cap_div"],
             self.theta.data_ptr() if ema else None, alpha)
+        self.args.reserve_free = reserve
         self.app = B.AppendArgs(
             B_, cap, self.k.shape[0], self.new_k.data_ptr(),
             None if self.new_scale is None else self.new_scale.data_ptr(),

@@ -282,6 +282,11 @@ typedef struct {
   /* [1] or NULL: when given, the step stamp is read on the device from *step_dev instead of
      step_id, so that one captured graph can serve every step (echo_step_advance moves it on) */
   const int32_t *step_dev;
+  /* Free slots the guaranteed recall leaves after its allocation, as room for the next step's
+     prefetch (which only takes free slots): it evicts further down the same (priority, slot)
+     order until reserve_free slots stay free, as far as unprotected slots allow.  0 = evict
+     only what the misses need.  0 <= reserve_free <= n_gpu. */
+  int32_t reserve_free;
 } echo_decode_args;
 
 typedef struct {             /* device outputs of one step */

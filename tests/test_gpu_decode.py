@@ -41,9 +41,10 @@ def _check_exact(inp, host_kv, scores, idx, pool, got):
     _check_pool_exact(inp, host_kv, idx, pool, got)
 
 
-def _check_pool_exact(inp, host_kv, idx, pool, got):
+def _check_pool_exact(inp, host_kv, idx, pool, got, reserve=0):
     st0 = _oracle_state(pool)
-    want_state, want = oracle.pool_step(st0, host_kv, idx, inp.key_begin, inp.req_to_host, pool.step_id)
+    want_state, want = oracle.pool_step(st0, host_kv, idx, inp.key_begin, inp.req_to_host, pool.step_id,
+                                        reserve)
     assert np.array_equal(got["topk_idx"], idx)
     assert got["status"] == want.status
     if want.status:
@@ -108,6 +109,24 @@ def test_decode_small_ragged_exact(lens, k, hit, div, one_stream):
         rn.side = rn.main
     rn.run_eager()
     _check_exact(inp, host_kv, scores, idx, pool, rn.results())
+    rn.close()
+
+
+@pytest.mark.parametrize("reserve", [1, 500, 5000, 100000])
+def test_decode_reserve_exact(reserve):
+    # the guaranteed recall leaves `reserve` slots free (as far as unprotected slots allow):
+    # the same canonical pool step as the oracle's with that reserve, bit for bit; 100000 is
+    # more than the evictable slots, so everything unprotected goes
+    announce("decode reserve", reserve)
+    lens = [3000, 700, 9000]
+    cfg = gen.DecodeConfig("r", 3, 0, 256, "int", False, 0.5, 4, seed=39)
+    inp, host_kv, scores, idx, pool = _setup(cfg, lengths=lens)
+    rn = DecodeRunner(inp, pool, host_kv, reserve=min(reserve, inp.n_gpu))
+    rn.capture()
+    rn.replay()
+    got = rn.results()
+    assert got["status"] == 0
+    _check_pool_exact(inp, host_kv, idx, pool, got, reserve=min(reserve, inp.n_gpu))
     rn.close()
 
 

@@ -147,6 +147,49 @@ def test_multistep_prefetch_against_ema_is_lossless():
         rn.close()
 
 
+def test_multistep_full_pool_prefetch_with_reserve():
+    # the pool starts full; each step's guaranteed recall leaves free room for the next
+    # step's prefetch: the loop without prefetch equals the oracle's loop with that reserve
+    # bit for bit, and with prefetch rows move in steady state while the selections stay
+    announce("multistep full pool, reserve for prefetch")
+    B_, L, T, k, R = 3, 2000, 5, 64, 300
+    m, host_kv = gen.make_multistep_inputs(B_, L, T, 900, seed=47, drift=0.05)
+    cache, st = _oracle_start(m)
+    _, _, _, recs = ms.decode_loop(cache, st, host_kv, m.steps, k, reserve=R)
+    plain = LoopRunner(m, host_kv, k, device_step=True, reserve=R)
+    try:
+        plain.capture()
+        for t, s in enumerate(m.steps):
+            plain.replay_step(s)
+            got = plain.results()
+            assert got["status"] == 0
+            assert np.array_equal(got["topk_idx"], recs[t].idx)
+            assert_pool_equal(_as_state(got["pool"]), recs[t].state, "step %d" % t)
+            assert int(got["pool"]["free"].sum()) >= min(R, 900 - B_ * (k + 1))
+    finally:
+        plain.close()
+    pf = LoopRunner(m, host_kv, k, prefetch=True, pf=dict(n_chunks=2, cap=256, cap_div=8),
+                    device_step=True, reserve=R)
+    moved = 0
+    try:
+        pf.capture()
+        for t, s in enumerate(m.steps):
+            pf.replay_step(s)
+            got = pf.results()
+            assert got["status"] == 0
+            assert np.array_equal(got["topk_idx"], recs[t].idx), "step %d selection" % t
+            if t >= 1:
+                moved += int(got["counters"][2])
+            idx = got["topk_idx"]
+            rows, cols = np.nonzero(idx >= 0)
+            hosts = got["req_to_host"][m.key_begin[rows] + idx[rows, cols]]
+            oracle.check_pool_invariants(_as_state(got["pool"]), got["host_kv"], hosts,
+                                         got["topk_slot"][rows, cols])
+        assert moved > 0, "no prefetch in a full pool despite the reserve"
+    finally:
+        pf.close()
+
+
 def test_append_cache_full_and_bad_host():
     announce("append errors")
     B_, L, T, k = 2, 100, 2, 16
