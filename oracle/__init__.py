@@ -16,7 +16,8 @@ Citations name the web page and the section on it:
 Modules: fp8 (E4M3FN decoding), scores (indexer scores and their error
 scale), topk (exact top-k, sample threshold), pool (the residency step),
 decode (one whole step), multistep (steps in a row: new tokens with
-write-through, the EMA threshold).
+write-through, the EMA threshold), interquery (the chunked prefill's
+approximate top-k subsets under the shifted histogram, and its unions).
 
 Readings of points the page leaves open are listed in each module's docstring.
 Parity status of every function is stated in its docstring ("pinned by ...").
@@ -31,6 +32,7 @@ from .pool import (INF, ST_EXHAUSTED, ST_BAD_HOST, ST_DUP_HOST, PoolState,
 from .decode import decode_step
 from .multistep import (KeyCache, ST_CACHE_FULL, append_tokens, kth_scores, ema_update,
                         decode_loop)
+from .interquery import approx_subset, union_segments, prefill_chunk_loop
 
 __all__ = [
     "E4M3FN_TABLE", "decode_e4m3fn", "index_scores", "error_scale",
@@ -39,4 +41,5 @@ __all__ = [
     "PoolState", "pool_step", "allocate_with_ranks", "metadata_bytes",
     "check_pool_invariants", "PoolInvariantError", "decode_step", "KeyCache",
     "ST_CACHE_FULL", "append_tokens", "kth_scores", "ema_update", "decode_loop",
+    "approx_subset", "union_segments", "prefill_chunk_loop",
 ]
