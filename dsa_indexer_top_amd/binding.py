@@ -67,6 +67,10 @@ _SIGS = {
     "echo_index_scores_prefill": (C.c_int, [P, P, P, I32, I32, I32, P, I64, P]),
     "echo_topk_workspace_bytes": (SZ, [I32, I32]),
     "echo_topk": (C.c_int, [P, I64, P, I32, I32, I32, P, P, SZ, P]),
+    "echo_topk_subset": (C.c_int, [P, I64, P, I32, I32, I32, P, P, P, P, P]),
+    "echo_union_workspace_bytes": (SZ, [I32]),
+    "echo_union_rows": (C.c_int, [P, I32, I32, I32, P, P, P, SZ, P]),
+    "echo_threshold_ema": (C.c_int, [P, I64, P, I32, I32, F32, P, P, P]),
     "echo_pool_workspace_bytes": (SZ, [I32, I32, I32]),
     "echo_pool_lookup_alloc": (C.c_int, [C.POINTER(Pool), P, P, P, I64, I32, I32, I32, P, P, P,
                                          P, P, SZ, P]),
@@ -187,6 +191,28 @@ def topk(scores, length, max_len, k, idx, ws, ld=None, stream=None):
     ld = scores.shape[-1] if ld is None else ld
     _call("echo_topk", ptr(scores), ld, ptr(length), length.shape[0], max_len, k, ptr(idx),
           ptr(ws), ws.numel() * ws.element_size(), stream_handle(stream))
+
+
+def topk_subset(scores, length, max_len, k, shift, subset, subset_cnt, thr_cnt=None, ld=None,
+                stream=None):
+    ld = scores.shape[-1] if ld is None else ld
+    _call("echo_topk_subset", ptr(scores), ld, ptr(length), length.shape[0], max_len, k,
+          ptr(shift), ptr(subset), ptr(subset_cnt), ptr(thr_cnt), stream_handle(stream))
+
+
+def union_workspace_bytes(n_keys):
+    return lib().echo_union_workspace_bytes(n_keys)
+
+
+def union_rows(idx, n_keys, out, out_cnt, ws, stream=None):
+    _call("echo_union_rows", ptr(idx), idx.shape[0], idx.shape[1], n_keys, ptr(out), ptr(out_cnt),
+          ptr(ws), ws.numel() * ws.element_size(), stream_handle(stream))
+
+
+def threshold_ema(scores, idx, alpha, theta=None, kth=None, ld=None, stream=None):
+    ld = scores.shape[-1] if ld is None else ld
+    _call("echo_threshold_ema", ptr(scores), ld, ptr(idx), idx.shape[0], idx.shape[1], alpha,
+          ptr(theta), ptr(kth), stream_handle(stream))
 
 
 def make_pool(n_gpu, n_host, free, priority, to_host, host_to_gpu, indices_buf, gpu_kv,

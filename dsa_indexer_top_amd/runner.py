@@ -247,3 +247,106 @@ class LoopRunner:
             self.graph.close()
             self.graph = None
         self.host_buf.close()
+
+
+class PrefillChunkRunner:
+    """Device buffers of one request's chunked prefill with its KV offloaded (the inter-query
+    prefetch of the ECHO page's §6.2): all query rows, keys and the token -> host map, the pool
+    with its pinned host backup, and per-chunk scores, subsets, unions and pool-step outputs.
+    run_chunk(c) enqueues, on one stream: the chunk's causal scores; with prefetch, the
+    approximate subsets under the current shift, their union and its prefetch gather; the
+    exact top-k, its union and the guaranteed residency (lookup / evict / allocate + recall);
+    then the shift update from the k-th score of the chunk's last row.  No arithmetic of the
+    method lives here."""
+
+    def __init__(self, q, w, k, req_to_host, pool, host_kv, chunk, topk, prefetch=False,
+                 alpha=0.5):
+        import torch
+        self.torch = torch
+        n = q.shape[0]
+        self.n, self.chunk, self.topk, self.prefetch, self.alpha = n, chunk, topk, prefetch, alpha
+        self.q, self.w, self.k = _dev(q), _dev(w), _dev(k)
+        self.req_to_host = _dev(req_to_host)
+        names = ("free", "priority", "to_host", "host_to_gpu", "indices_buf", "gpu_kv")
+        self.live = {nm: _dev(getattr(pool, nm)) for nm in names}
+        self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.host_buf = B.HostBuffer(host_kv.nbytes)
+        self.host_buf.array.view(np.uint16).reshape(host_kv.shape)[...] = host_kv
+        self.n_gpu, self.n_host = len(pool.free), len(pool.host_to_gpu)
+        L = self.live
+        self.pool = B.make_pool(self.n_gpu, self.n_host, L["free"], L["priority"], L["to_host"],
+                                L["host_to_gpu"], L["indices_buf"], L["gpu_kv"],
+                                self.host_buf.dev_ptr, self.status)
+        i32, f32, dev = torch.int32, torch.float32, "cuda"
+        self.n_seg = max(1, -(-n // 4096))
+        self.scores = torch.empty((chunk, n), dtype=f32, device=dev)
+        self.lens = torch.empty(chunk, dtype=i32, device=dev)
+        self.subset = torch.empty((chunk, topk), dtype=i32, device=dev)
+        self.subset_cnt = torch.empty(chunk, dtype=i32, device=dev)
+        self.thr_cnt = torch.empty(chunk, dtype=i32, device=dev)
+        self.idx = torch.empty((chunk, topk), dtype=i32, device=dev)
+        self.pre = torch.empty((self.n_seg, 4096), dtype=i32, device=dev)
+        self.pre_cnt = torch.empty(self.n_seg, dtype=i32, device=dev)
+        self.uni = torch.empty((self.n_seg, 4096), dtype=i32, device=dev)
+        self.uni_cnt = torch.empty(self.n_seg, dtype=i32, device=dev)
+        self.seg_begin = torch.zeros(self.n_seg, dtype=torch.int64, device=dev)
+        self.slot = torch.empty((self.n_seg, 4096), dtype=i32, device=dev)
+        self.miss_host = torch.empty(self.n_seg * 4096, dtype=i32, device=dev)
+        self.miss_slot = torch.empty(self.n_seg * 4096, dtype=i32, device=dev)
+        self.n_miss = torch.zeros(1, dtype=i32, device=dev)
+        self.free_list = torch.empty(self.n_gpu, dtype=i32, device=dev)
+        self.free_count = torch.zeros(2, dtype=i32, device=dev)
+        self.n_prefetched = torch.zeros(1, dtype=i32, device=dev)
+        self.theta = torch.full((1,), float("nan"), dtype=f32, device=dev)
+        self.kth = torch.empty(1, dtype=f32, device=dev)
+        self.ws_union = torch.empty(max(B.union_workspace_bytes(n), 256), dtype=torch.uint8, device=dev)
+        self.ws_topk = torch.empty(max(B.topk_workspace_bytes(chunk, n), 256), dtype=torch.uint8, device=dev)
+        self.ws_pool = torch.empty(max(B.pool_workspace_bytes(self.n_seg, 4096, self.n_gpu), 256),
+                                   dtype=torch.uint8, device=dev)
+        self.main = torch.cuda.Stream()
+
+    def run_chunk(self, c, step_id):
+        t = self.torch
+        t0 = c * self.chunk
+        t1 = min(self.n, t0 + self.chunk)
+        rows = t1 - t0
+        st = self.main
+        with t.cuda.stream(st):
+            self.lens[:rows].copy_(t.arange(t0 + 1, t1 + 1, dtype=t.int32))
+            self.n_prefetched.zero_()
+        sc = self.scores[:rows]
+        B.index_scores_prefill(self.q[t0:t1], self.w[t0:t1], self.k[:t1], sc, q_pos0=t0,
+                               ld=self.n, stream=st)
+        lens = self.lens[:rows]
+        if self.prefetch:
+            B.topk_subset(sc, lens, t1, self.topk, self.theta, self.subset[:rows],
+                          self.subset_cnt[:rows], self.thr_cnt[:rows], ld=self.n, stream=st)
+            B.union_rows(self.subset[:rows], t1, self.pre, self.pre_cnt, self.ws_union, stream=st)
+            B.prefetch_begin(self.pool, self.free_list, self.free_count, stream=st)
+            B.prefetch_gather(self.pool, self.seg_begin, self.req_to_host, self.pre, self.pre_cnt,
+                              4096, self.free_list, self.free_count, self.n_prefetched, stream=st)
+        B.topk(sc, lens, t1, self.topk, self.idx[:rows], self.ws_topk, ld=self.n, stream=st)
+        B.union_rows(self.idx[:rows], t1, self.uni, self.uni_cnt, self.ws_union, stream=st)
+        B.pool_lookup_alloc(self.pool, self.uni, self.seg_begin, self.req_to_host, step_id,
+                            self.slot, self.miss_host, self.miss_slot, self.n_miss, self.ws_pool,
+                            stream=st)
+        B.recall(self.pool, self.miss_host, self.miss_slot, self.n_miss, self.n_seg * 4096,
+                 stream=st)
+        B.threshold_ema(sc[rows - 1:rows], self.idx[rows - 1:rows], self.alpha, self.theta,
+                        self.kth, ld=self.n, stream=st)
+        return rows
+
+    def results(self, rows):
+        self.torch.cuda.synchronize()
+        h = lambda x: x.cpu().numpy()
+        return dict(scores=h(self.scores[:rows]), subset=h(self.subset[:rows]),
+                    subset_cnt=h(self.subset_cnt[:rows]), thr_cnt=h(self.thr_cnt[:rows]),
+                    idx=h(self.idx[:rows]), pre=h(self.pre), pre_cnt=h(self.pre_cnt),
+                    uni=h(self.uni), uni_cnt=h(self.uni_cnt), slot=h(self.slot),
+                    n_miss=int(h(self.n_miss)[0]), n_prefetched=int(h(self.n_prefetched)[0]),
+                    theta=float(h(self.theta)[0]), kth=float(h(self.kth)[0]),
+                    status=int(h(self.status)[0]),
+                    pool={nm: h(x) for nm, x in self.live.items()})
+
+    def close(self):
+        self.host_buf.close()

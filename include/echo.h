@@ -183,6 +183,44 @@ int echo_topk(const float *scores, int64_t ld, const int32_t *len, int32_t n_row
               void *stream);
 
 /*
+ * Approximate top-k subset per row for the inter-query prefetch of a chunked prefill (§6.2).
+ * Every score of row r (scores[r*ld + s], s < len[r]) is shifted, x = fl32(score - shift), and
+ * mapped by the top 8 bits of its order key (sign-flipped, -0 as +0) to one of 256 bins.  The
+ * highest bins whose total stays <= k are taken whole and the next bin down is the threshold
+ * bin.  subset[r*k + j] lists the tokens of the taken bins in ascending order, -1 padded to k;
+ * subset_cnt[r] is their number (<= k, and > k - the threshold bin's size when there is one);
+ * thr_cnt[r] (optional) is the threshold bin's size (0 when every bin fits).  The subset lies
+ * inside the row's exact top-k.  shift [1] is a device float, the prediction of the k-th score
+ * (NULL or NaN = 0: no prediction yet).  len[r] above max_len is clamped.  1 <= k <= ECHO_MAX_TOPK.
+ */
+int echo_topk_subset(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
+                     int32_t max_len, int32_t k, const float *shift, int32_t *subset,
+                     int32_t *subset_cnt, int32_t *thr_cnt, void *stream);
+
+/*
+ * Union of index lists (§6.2: a query block's prefetch set is the union of its rows' subsets, and
+ * its guaranteed recall covers the union of its rows' exact top-k).  Entries of idx [n_rows, k]
+ * in [0, n_keys) are collected (others, -1 included, are ignored) and listed in ascending order
+ * in segments of 4096 consecutive keys: out[s*4096 + j] for the union's keys in
+ * [4096 s, 4096 s + 4096), -1 padded; out_cnt[s] their number; n_seg = ceil(n_keys / 4096)
+ * (1 when n_keys = 0).  The segments are 4096-wide selection rows with key_begin 0 for
+ * echo_pool_lookup_alloc (k = 4096) and candidate rows for echo_prefetch_gather (cap = 4096).
+ * ws: echo_union_workspace_bytes(n_keys) bytes (a bitmap, cleared by the call).
+ */
+size_t echo_union_workspace_bytes(int32_t n_keys);
+int echo_union_rows(const int32_t *idx, int32_t n_rows, int32_t k, int32_t n_keys, int32_t *out,
+                    int32_t *out_cnt, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * k-th score and its EMA (§6.1, §6.2): for each row r, kth[r] = the smallest score among the
+ * selected tokens idx[r*k + j] >= 0 (NaN when there is none), and theta[r] = kth[r] if theta[r]
+ * is NaN, else fmaf(alpha, theta[r], (1 - alpha) * kth[r]); a row with no selection keeps theta.
+ * Either output may be NULL (not both).  0 <= alpha <= 1.
+ */
+int echo_threshold_ema(const float *scores, int64_t ld, const int32_t *idx, int32_t n_rows,
+                       int32_t k, float alpha, float *theta, float *kth, void *stream);
+
+/*
  * Residency lookup + eviction + allocation for the selected tokens (§5.2 free/allocate and
  * the lookup half of recall), without the row copy.  For the entries idx[r*k + j] >= 0 taken
  * in (r, j) order: h = req_to_host[key_begin[r] + idx]; hit iff host_to_gpu[h] != ECHO_INF.

@@ -71,6 +71,9 @@ inline unsigned __float_as_uint(float f) { unsigned x; memcpy(&x, &f, 4); return
 inline int __ffsll(unsigned long long x) { return x ? __builtin_ctzll(x) + 1 : 0; }
 inline int __ffsll(long long x) { return __ffsll(static_cast<unsigned long long>(x)); }
 inline int __popcll(unsigned long long x) { return __builtin_popcountll(x); }
+inline int __popc(unsigned x) { return __builtin_popcount(x); }
+inline int __ffs(unsigned x) { return x ? __builtin_ctz(x) + 1 : 0; }
+inline int __ffs(int x) { return __ffs(static_cast<unsigned>(x)); }
 inline int __clzll(long long x) { return x ? __builtin_clzll(static_cast<unsigned long long>(x)) : 64; }
 
 using std::max;

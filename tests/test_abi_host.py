@@ -171,6 +171,28 @@ def test_decode_append_and_ema_argument_errors():
         assert "ema_alpha" in _err()
 
 
+def test_interquery_argument_errors():
+    L = B.lib()
+    # echo_topk_subset(scores, ld, len, n_rows, max_len, k, shift, subset, cnt, thr, stream)
+    assert L.echo_topk_subset(FAKE, 64, FAKE, -1, 64, 8, None, FAKE, FAKE, None, None) == B.ECHO_EINVAL
+    for k in (0, 4097):
+        assert L.echo_topk_subset(FAKE, 64, FAKE, 1, 64, k, None, FAKE, FAKE, None, None) == B.ECHO_EUNSUPPORTED
+    assert L.echo_topk_subset(FAKE, 32, FAKE, 1, 64, 8, None, FAKE, FAKE, None, None) == B.ECHO_EINVAL
+    assert L.echo_topk_subset(FAKE, 64, FAKE, 1, 64, 8, None, None, FAKE, None, None) == B.ECHO_EINVAL
+    assert L.echo_topk_subset(None, 64, None, 0, 64, 8, None, None, None, None, None) == B.ECHO_OK
+    # echo_union_rows(idx, n_rows, k, n_keys, out, cnt, ws, ws_bytes, stream)
+    assert L.echo_union_rows(FAKE, 2, 8, -1, FAKE, FAKE, FAKE, 1 << 20, None) == B.ECHO_EINVAL
+    assert L.echo_union_rows(None, 2, 8, 100, FAKE, FAKE, FAKE, 1 << 20, None) == B.ECHO_EINVAL
+    need = L.echo_union_workspace_bytes(9000)
+    assert need == 3 * 4096 // 8 and L.echo_union_workspace_bytes(0) == 512
+    assert L.echo_union_workspace_bytes(-1) == 0
+    assert L.echo_union_rows(FAKE, 2, 8, 9000, FAKE, FAKE, FAKE, need - 1, None) == B.ECHO_EWORKSPACE
+    # echo_threshold_ema(scores, ld, idx, n_rows, k, alpha, theta, kth, stream)
+    assert L.echo_threshold_ema(FAKE, 64, FAKE, 1, 8, 1.5, FAKE, None, None) == B.ECHO_EINVAL
+    assert L.echo_threshold_ema(FAKE, 64, FAKE, 1, 0, 0.5, FAKE, None, None) == B.ECHO_EUNSUPPORTED
+    assert L.echo_threshold_ema(FAKE, 64, FAKE, 1, 8, 0.5, None, None, None) == B.ECHO_EINVAL
+
+
 def test_workspace_sizes():
     L = B.lib()
     assert L.echo_pool_workspace_bytes(-1, 8, 8) == 0
