@@ -173,6 +173,62 @@ def loop_measure(torch, B, gen, batch=8, length=65536, n_steps=16, topk=2048, dr
             "steps": steps}
 
 
+def prefill_offload_measure(torch, B, gen, n=32768, chunk=2048, topk=2048, seed=4):
+    """Chunked prefill of one request with its KV offloaded and the inter-query prefetch
+    (§6.2): per 2048-row chunk, the causal scores, the approximate subsets under the EMA shift,
+    the prefetch of their union, the exact top-k and the guaranteed residency of its union.
+    32768 tokens, integer grid, top-2048, a GPU pool of 32768 slots, empty at the start.
+    Reports per chunk the time of the chunk's enqueues (HIP events on their stream), the
+    median threshold-bin size with the shift and, from one extra launch on the same scores,
+    without it, the subset's median share of k, the rows prefetched and the misses left for
+    the guaranteed recall."""
+    from dsa_indexer_top_amd.runner import PrefillChunkRunner
+    q, w, k = gen.make_prefill_inputs(n, seed=seed)
+    req_to_host = np.random.default_rng(seed).permutation(n).astype(np.int32)
+    host_kv = gen.fill_latent_rows(seed, np.empty((n, 576), np.uint16))
+    INF = 2**31 - 1
+    pool = gen.PoolArrays(np.ones(n, np.uint8), np.full(n, -1, np.int32), np.full(n, INF, np.int32),
+                          np.full(n, INF, np.int32), np.full(n, -1, np.int32),
+                          np.full((n, 576), 0xFFFF, np.uint16), step_id=1)
+    rn = PrefillChunkRunner(q, w, k, req_to_host, pool, host_kv, chunk, topk, prefetch=True)
+    plain_thr = torch.empty(chunk, dtype=torch.int32, device="cuda")
+    plain_sub = torch.empty((chunk, topk), dtype=torch.int32, device="cuda")
+    plain_cnt = torch.empty(chunk, dtype=torch.int32, device="cuda")
+    chunks = []
+    try:
+        for c in range(-(-n // chunk)):
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            shift = float(rn.theta.cpu()[0])
+            s.record(rn.main)
+            rows = rn.run_chunk(c, 1 + c)
+            e.record(rn.main)
+            torch.cuda.synchronize()
+            t1 = min(n, (c + 1) * chunk)
+            B.topk_subset(rn.scores[:rows], rn.lens[:rows], t1, topk, None, plain_sub[:rows],
+                          plain_cnt[:rows], plain_thr[:rows], ld=n, stream=rn.main)
+            got = rn.results(rows)
+            assert got["status"] == 0, "pool status in the chunked prefill"
+            full = np.minimum(np.arange(c * chunk + 1, t1 + 1), topk)
+            chunks.append({"us": round(s.elapsed_time(e) * 1000.0, 1),
+                           "thr_bin_median_shifted": int(np.median(got["thr_cnt"])),
+                           "thr_bin_median_unshifted": int(np.median(plain_thr[:rows].cpu().numpy())),
+                           "subset_share_median": round(float(np.median(got["subset_cnt"] / full)), 4),
+                           "union": int(got["uni_cnt"].sum()), "prefetched": got["n_prefetched"],
+                           "misses_after_prefetch": got["n_miss"],
+                           "shift": None if np.isnan(shift) else round(shift, 4)})
+    finally:
+        rn.close()
+    later = chunks[2:]
+    return {"workload": "chunked prefill with offload: %d tokens, chunks of %d rows, top-%d, "
+                        "integer grid, GPU pool %d slots (empty at the start)" % (n, chunk, topk, n),
+            "timing": "HIP events around each chunk's enqueues on their stream",
+            "thr_bin_median_shifted": int(np.median([x["thr_bin_median_shifted"] for x in later])),
+            "thr_bin_median_unshifted": int(np.median([x["thr_bin_median_unshifted"] for x in later])),
+            "chunks": chunks}
+
+
 def cpu_baseline(inp, host_kv, pool_arrays, min_s=10.0, budget_s=30.0):
     """The oracle, as it is, timed on the host cores on a bounded sample of the same workload:
     the whole oracle decode step (float64 scores, exact top-k, canonical pool step with the
@@ -397,6 +453,12 @@ def main():
         log("prefill %.1f us = %.0f TFLOP/s (%.1f%% of fp8 peak), top-k rows %.1f us" % (
             out["prefill"]["us_per_launch"], out["prefill"]["achieved"],
             100 * out["prefill"]["frac"], out["prefill"]["topk_rows_us"]))
+    if not args.no_prefill:
+        log("chunked prefill with offload and inter-query prefetch ...")
+        out["prefill_offload"] = prefill_offload_measure(torch, B, gen)
+        log("chunked prefill: threshold bin median %d shifted vs %d unshifted" % (
+            out["prefill_offload"]["thr_bin_median_shifted"],
+            out["prefill_offload"]["thr_bin_median_unshifted"]))
     if not args.no_loop:
         log("decode loop (EMA threshold, new tokens every step) ...")
         out["loop"] = loop_measure(torch, B, gen)
