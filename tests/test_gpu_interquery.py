@@ -41,10 +41,27 @@ def test_topk_subset_exact(k, ties):
             assert g_thr[r] == want_thr, (shift, r)
 
 
+def test_topk_subset_clamps_and_ld():
+    # lengths above max_len are clamped; ld wider than the rows; a shift of +inf and -inf
+    announce("topk subset clamps")
+    s = gen.random_scores(76, 3, 600, ld=640)
+    lens = np.array([10000, 600, -5], np.int32)
+    for shift in (float("inf"), float("-inf"), 0.5):
+        sh = torch.tensor([shift], dtype=torch.float32, device="cuda")
+        sub = torch.empty((3, 32), dtype=torch.int32, device="cuda")
+        cnt = torch.empty(3, dtype=torch.int32, device="cuda")
+        B.topk_subset(dev(s), dev(lens), 600, 32, sh, sub, cnt)
+        g_sub, g_cnt = host(sub), host(cnt)
+        for r, L in enumerate([600, 600, 0]):
+            want, _, S = iq.approx_subset(s[r, :L], 32, shift)
+            assert g_cnt[r] == S and np.array_equal(g_sub[r, :S], want), (shift, r)
+
+
 def test_union_rows_exact():
     announce("union rows")
     rng = np.random.default_rng(72)
-    for n_keys, n_rows, k in [(1, 3, 4), (4096, 5, 300), (4097, 7, 700), (20000, 40, 512)]:
+    for n_keys, n_rows, k in [(0, 2, 4), (1, 3, 4), (4096, 5, 300), (4097, 7, 700),
+                              (20000, 40, 512), (9000, 0, 8)]:
         idx = rng.integers(-3, n_keys + 5, (n_rows, k)).astype(np.int32)
         n_seg = max(1, -(-n_keys // 4096))
         out = torch.empty((n_seg, 4096), dtype=torch.int32, device="cuda")
