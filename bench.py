@@ -290,6 +290,10 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-loop", action="store_true", help="skip the decode-loop measurement")
     ap.add_argument("--prefetch", choices=("auto", "on", "off"), default="auto")
+    ap.add_argument("--reserve", type=int, default=None,
+                    help="free GPU slots in the starting pool (default: the workload's own)")
+    ap.add_argument("--percentile", type=float, default=None,
+                    help="prefetch threshold percentile of the score sample (default 95)")
     ap.add_argument("--probe", choices=("score", "copy", "prefill"), default=None,
                     help="short program for hardware-counter runs, then exit: 20 launches of the "
                          "scoring kernel on the workload, 20 device copies of 256 MiB, or 3 causal "
@@ -356,9 +360,10 @@ def main():
     tws = torch.empty(B.topk_workspace_bytes(n_rows, max_len), dtype=torch.uint8, device="cuda")
     B.index_scores(dq, dw, dk, dks, dkb, dkl, max_len, sc)
     B.topk(sc, dkl, max_len, cfg.topk, sel, tws)
-    pool = gen.make_pool_state(inp, sel.cpu().numpy(), host_kv)
+    pool = gen.make_pool_state(inp, sel.cpu().numpy(), host_kv, reserve=args.reserve)
     del sc, sel, tws
-    rn = DecodeRunner(inp, pool, host_buf=hb, prefetch=prefetch)
+    pf = None if args.percentile is None else dict(percentile=args.percentile)
+    rn = DecodeRunner(inp, pool, host_buf=hb, prefetch=prefetch, pf=pf)
     rn.capture()
     log("setup done in %.1fs" % (time.perf_counter() - t_setup))
 
@@ -426,6 +431,7 @@ def main():
         "config": {"workload": args.workload, "description": WORKLOADS[args.workload],
                    "batch": n_rows, "tokens": tokens, "topk": rn.topk, "n_gpu_slots": rn.n_gpu,
                    "n_host_slots": rn.n_host, "prefetch": bool(prefetch),
+                   "free_slots_at_start": int(pool.free.sum()),
                    "timing": "HIP events around each graph replay on its stream; pool restored "
                              "from a pristine copy between replays, outside the events"},
         "roofline": {"bound": "hbm",
