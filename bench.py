@@ -453,26 +453,35 @@ def main():
         "counters": {"n_miss": n_miss, "prefetch_demand": int(res["counters"][1]),
                      "prefetched": int(res["counters"][2])},
     }
+    # secondary measurements: a Python error in one of them is recorded in its place, so the
+    # headline line above is always printed
+    def section(name, fn, summary):
+        try:
+            out[name] = fn()
+            log(summary(out[name]))
+        except Exception as e:                       # noqa: BLE001
+            out[name] = {"error": "%s: %s" % (type(e).__name__, e)}
+            log("%s failed: %s" % (name, out[name]["error"]))
+            torch.cuda.synchronize()
+
     if not args.no_prefill:
         log("prefill indexer (32768^2) ...")
-        out["prefill"] = prefill_measure(torch, B, gen)
-        log("prefill %.1f us = %.0f TFLOP/s (%.1f%% of fp8 peak), top-k rows %.1f us" % (
-            out["prefill"]["us_per_launch"], out["prefill"]["achieved"],
-            100 * out["prefill"]["frac"], out["prefill"]["topk_rows_us"]))
-    if not args.no_prefill:
+        section("prefill", lambda: prefill_measure(torch, B, gen),
+                lambda p: "prefill %.1f us = %.0f TFLOP/s (%.1f%% of fp8 peak), top-k rows %.1f us"
+                % (p["us_per_launch"], p["achieved"], 100 * p["frac"], p["topk_rows_us"]))
         log("chunked prefill with offload and inter-query prefetch ...")
-        out["prefill_offload"] = prefill_offload_measure(torch, B, gen)
-        log("chunked prefill: threshold bin median %d shifted vs %d unshifted" % (
-            out["prefill_offload"]["thr_bin_median_shifted"],
-            out["prefill_offload"]["thr_bin_median_unshifted"]))
+        section("prefill_offload", lambda: prefill_offload_measure(torch, B, gen),
+                lambda p: "chunked prefill: threshold bin median %d shifted vs %d unshifted"
+                % (p["thr_bin_median_shifted"], p["thr_bin_median_unshifted"]))
     if not args.no_loop:
         log("decode loop (EMA threshold, new tokens every step) ...")
-        out["loop"] = loop_measure(torch, B, gen)
-        log("loop: median %.1f us/step, hit rate %.3f" % (out["loop"]["us_per_step_median"],
-                                                          out["loop"]["hit_rate_median"]))
+        section("loop", lambda: loop_measure(torch, B, gen),
+                lambda p: "loop: median %.1f us/step, hit rate %.3f"
+                % (p["us_per_step_median"], p["hit_rate_median"]))
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        out["cpu_baseline"] = cpu_baseline(inp, host_kv, pool)
+        section("cpu_baseline", lambda: cpu_baseline(inp, host_kv, pool),
+                lambda p: "cpu baseline %.3g %s on %d threads" % (p["value"], p["unit"], p["cores"]))
     rn.close()
     hb.close()
     print(json.dumps(out), flush=True)
