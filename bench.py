@@ -451,7 +451,10 @@ def main():
                          "topk": round(t_topk, 2), "recall": round(t_recall, 2),
                          "wall_per_step_incl_restore": round(wall / args.steps * 1e6, 2)},
         "counters": {"n_miss": n_miss, "prefetch_demand": int(res["counters"][1]),
-                     "prefetched": int(res["counters"][2])},
+                     "prefetched": int(res["counters"][2]),
+                     # prefetched rows keep priority 0 unless the step selects them; the starting
+                     # pool's priorities are a permutation, so at most one other slot holds 0
+                     "prefetched_unselected_approx": int((res["pool"]["priority"] == 0).sum())},
     }
     # secondary measurements: a Python error in one of them is recorded in its place, so the
     # headline line above is always printed

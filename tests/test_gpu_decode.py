@@ -275,3 +275,27 @@ def test_prefetch_is_lossless(side_stream):
     rb = b["pool"]["gpu_kv"][b["topk_slot"][rows, cols]]
     assert np.array_equal(ra, rb)
     _check_topk_tolerance(inp, scores, b, rows=[0, 5])
+
+
+def test_prefetch_lossless_over_chunk_counts():
+    # the prefetch races the scoring of later ranges and the other requests' gathers; whatever
+    # the number of ranges, the selection and the selected rows must not change
+    announce("prefetch lossless, chunk counts 1..8")
+    cfg = gen.DecodeConfig("c", 4, 9000, 256, "int", False, 0.5, 6, reserve=1500,
+                           prefetch=True, seed=53)
+    inp, host_kv, scores, idx, pool = _setup(cfg)
+    moved = 0
+    for n_chunks in range(1, 9):
+        pf = dict(n_chunks=n_chunks, n_sample=1024, percentile=96.0, cap=512, cap_div=16)
+        rn = DecodeRunner(inp, pool, host_kv, prefetch=True, pf=pf)
+        rn.run_eager()
+        got = rn.results()
+        rn.close()
+        assert got["status"] == 0, n_chunks
+        assert np.array_equal(got["topk_idx"], idx), n_chunks
+        for r in range(len(inp.key_len)):
+            L = int(inp.key_len[r])
+            assert np.array_equal(got["scores"][r, :L].astype(np.float64), scores[r]), (n_chunks, r)
+        _check_invariants(inp, host_kv, got)
+        moved += int(got["counters"][2])
+    assert moved > 0
