@@ -218,10 +218,22 @@ def prefill_offload_measure(torch, B, gen, n=32768, chunk=2048, topk=2048, seed=
                            "union": int(got["uni_cnt"].sum()), "prefetched": got["n_prefetched"],
                            "misses_after_prefetch": got["n_miss"],
                            "shift": None if np.isnan(shift) else round(shift, 4)})
+        # the approximate top-k alone on the last chunk's scores: HBM-bound, 4 B per score read
+        # by its histogram pass (the ordered pass re-reads them: overhead, not algorithmic)
+        rows = n - (len(chunks) - 1) * chunk
+        t_sub = kernel_time_us(torch, rn.main, lambda: B.topk_subset(
+            rn.scores[:rows], rn.lens[:rows], n, topk, rn.theta, rn.subset[:rows],
+            rn.subset_cnt[:rows], None, ld=n, stream=rn.main), 20)
+        n_scores = int(rn.lens[:rows].sum().item())
+        sub_gbs = 4.0 * n_scores / (t_sub / 1e6) / 1e9
     finally:
         rn.close()
     later = chunks[2:]
-    return {"workload": "chunked prefill with offload: %d tokens, chunks of %d rows, top-%d, "
+    return {"subset_kernel": {"kernel": "topk_subset_kernel", "bound": "hbm",
+                              "us_per_launch": round(t_sub, 1), "scores": n_scores,
+                              "achieved": round(sub_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(sub_gbs / HBM_PEAK_GBS, 4)},
+            "workload": "chunked prefill with offload: %d tokens, chunks of %d rows, top-%d, "
                         "integer grid, GPU pool %d slots (empty at the start)" % (n, chunk, topk, n),
             "timing": "HIP events around each chunk's enqueues on their stream",
             "thr_bin_median_shifted": int(np.median([x["thr_bin_median_shifted"] for x in later])),
