@@ -4,6 +4,7 @@ metadata array, every row, per-entry slots, miss lists and status are equal."""
 import numpy as np
 import pytest
 import torch
+from hypothesis import given, settings, strategies as hs, HealthCheck
 
 import oracle
 from oracle import INF
@@ -119,3 +120,21 @@ def test_pool_second_step_all_hits():
     s1, _ = oracle.pool_step(st, host_kv, sel, kb, r2h, 10**6)
     got, want = _compare((s1, host_kv, sel, kb, r2h), step_id=10**6 + 1)
     assert want.n_miss == 0
+
+
+@settings(max_examples=40, deadline=None, derandomize=True,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.function_scoped_fixture])
+@given(hs.data())
+def test_pool_step_properties(data):
+    # random small pools (every fill level, heavy priority ties, k from 1), against the oracle:
+    # bit-exact state or the same status with the pool untouched
+    n_gpu = data.draw(hs.integers(1, 96), label="n_gpu")
+    n_occ = data.draw(hs.integers(0, n_gpu), label="n_occ")
+    rows = data.draw(hs.integers(1, 4), label="rows")
+    k = data.draw(hs.integers(1, 40), label="k")
+    L = data.draw(hs.integers(1, 60), label="L")
+    n_host = max(rows * L, n_occ) + data.draw(hs.integers(0, 50), label="extra_host")
+    levels = data.draw(hs.integers(1, 8), label="levels")
+    seed = data.draw(hs.integers(0, 2**31 - 1), label="seed")
+    announce("pool property", n_gpu, n_occ, rows, k, L, levels)
+    _compare(_random_case(seed, n_gpu, n_host, n_occ, rows, k, L, levels))
