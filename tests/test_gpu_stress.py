@@ -19,9 +19,13 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-4
 
 
-def test_stress_b64_128k_full_step():
-    cfg = gen.CONFIGS["b64_128k"]
-    announce("stress b64_128k: drawing inputs")
+SMALL = gen.DecodeConfig("stress_small", 4, 6000, 256, "general", True, 0.5, 8, reserve=1024,
+                         prefetch=True, seed=5)
+
+
+@pytest.mark.parametrize("cfg", [SMALL, gen.CONFIGS["b64_128k"]], ids=["small", "full"])
+def test_stress_step(cfg):
+    announce("stress %s: drawing inputs" % cfg.name)
     inp = gen.make_decode_inputs(cfg)
     hb = B.HostBuffer(inp.n_host * 576 * 2)
     try:
@@ -39,7 +43,7 @@ def test_stress_b64_128k_full_step():
         want_idx = sel.cpu().numpy()
         del dq, dw, dk, dks, dkb, dkl, sc, sel, tws
         pool = gen.make_pool_state(inp, want_idx, host_kv)
-        announce("stress b64_128k: captured step with prefetch")
+        announce("stress %s: captured step with prefetch" % cfg.name)
         rn = DecodeRunner(inp, pool, host_buf=hb, prefetch=True)
         try:
             rn.capture()
@@ -61,8 +65,8 @@ def test_stress_b64_128k_full_step():
         oracle.check_pool_invariants(st, host_kv, hosts, got["topk_slot"][rows, cols])
         # sampled requests against the oracle: scores within 1e-4 T, and the selection differing
         # from the oracle's only by tokens within that tolerance of its k-th score
-        announce("stress b64_128k: oracle on sampled requests")
-        for r in (0, 37, 63):
+        announce("stress %s: oracle on sampled requests" % cfg.name)
+        for r in sorted({0, min(n_rows - 1, n_rows // 2 + 5), n_rows - 1}):
             sl = slice(r, r + 1)
             args = (inp.q[sl], inp.w[sl], inp.k, inp.k_scale, inp.key_begin[sl], inp.key_len[sl])
             s, T = oracle.index_scores(*args)[0], oracle.error_scale(*args)[0]
