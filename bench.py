@@ -122,7 +122,16 @@ def prefill_measure(torch, B, gen, reps=5):
             "topk_rows_us": round(t_topk, 1)}
 
 
-def loop_measure(torch, B, gen, batch=8, length=65536, n_steps=16, topk=2048, drift=0.05):
+def oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        return 1
+
+
+def loop_measure(torch, B, gen, batch=8, length=65536, n_steps=16, topk=2048, drift=0.05,
+                 cpu=True):
     """Decode steps in a row: every step appends one token per request (key, host row written
     through, GPU slot) and runs the decode step with prefetch against the EMA estimate of the
     k-th score (alpha = 0.5).  8 requests x 65536 tokens, integer grid, top-2048, a full pool of
@@ -162,7 +171,23 @@ def loop_measure(torch, B, gen, batch=8, length=65536, n_steps=16, topk=2048, dr
     finally:
         rn.close()
     later = steps[1:]
-    return {"workload": "%d requests x %d tokens, %d steps, top-%d, integer grid, q drift %.2f, "
+    out = {}
+    if cpu:
+        # the oracle's loop on the first step of the same workload (append, scores, top-k, pool
+        # step, EMA), as it is, on the host cores
+        import oracle
+        from oracle import multistep as ms
+        cache = ms.KeyCache(m.k, m.k_scale, m.key_begin, m.key_len, m.req_to_host, m.capacity)
+        p = m.pool
+        st = oracle.PoolState(p.free, p.priority, p.to_host, p.host_to_gpu, p.indices_buf, p.gpu_kv)
+        t0 = time.perf_counter()
+        ms.decode_loop(cache, st, host_kv, m.steps[:1], topk, reserve=reserve)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(batch * (length + 1) / dt, 1), "unit": "indexed tokens/s",
+                               "cores": int(oracle_threads()), "kind": "oracle",
+                               "seconds": round(dt, 3),
+                               "sample": "the oracle's loop on the first step of this workload"}
+    out.update({"workload": "%d requests x %d tokens, %d steps, top-%d, integer grid, q drift %.2f, "
                         "full pool N_G=%d with %d slots kept free for prefetch, prefetch against "
                         "the EMA estimate" % (batch, length, n_steps, topk, drift, n_gpu, reserve),
             "timing": "one captured graph (echo_step_advance + echo_decode_append + "
@@ -170,10 +195,13 @@ def loop_measure(torch, B, gen, batch=8, length=65536, n_steps=16, topk=2048, dr
                       "events around each replay",
             "us_per_step_median": round(float(np.median([x["us"] for x in later])), 1),
             "hit_rate_median": round(float(np.median([x["hit_rate"] for x in later])), 4),
-            "steps": steps}
+            "indexed_tokens_per_s": round(batch * (length + n_steps / 2) /
+                                          (float(np.median([x["us"] for x in later])) / 1e6), 1),
+            "steps": steps})
+    return out
 
 
-def prefill_offload_measure(torch, B, gen, n=32768, chunk=2048, topk=2048, seed=4):
+def prefill_offload_measure(torch, B, gen, n=32768, chunk=2048, topk=2048, seed=4, cpu=True):
     """Chunked prefill of one request with its KV offloaded and the inter-query prefetch
     (§6.2): per 2048-row chunk, the causal scores, the approximate subsets under the EMA shift,
     the prefetch of their union, the exact top-k and the guaranteed residency of its union.
@@ -229,7 +257,24 @@ def prefill_offload_measure(torch, B, gen, n=32768, chunk=2048, topk=2048, seed=
     finally:
         rn.close()
     later = chunks[2:]
-    return {"subset_kernel": {"kernel": "topk_subset_kernel", "bound": "hbm",
+    pairs = n * (n + 1) // 2
+    total_us = sum(x["us"] for x in chunks)
+    extra = {"pairs_per_s": round(pairs / (total_us / 1e6), 1), "unit": "causal (query, key) pairs/s",
+             "us_total": round(total_us, 1)}
+    if cpu:
+        # the oracle's chunk loop, as it is, on the first chunk of the same request
+        import oracle
+        from oracle import interquery as iq
+        st = oracle.PoolState.empty(n, n)
+        t0 = time.perf_counter()
+        iq.prefill_chunk_loop(q[:chunk], w[:chunk], k[:chunk], req_to_host, st, host_kv, chunk,
+                              topk, step0=1)
+        dt = time.perf_counter() - t0
+        extra["cpu_baseline"] = {"value": round(chunk * (chunk + 1) / 2 / dt, 1),
+                                 "unit": "causal (query, key) pairs/s", "cores": int(oracle_threads()),
+                                 "kind": "oracle", "seconds": round(dt, 3),
+                                 "sample": "the oracle's chunk loop on the first %d rows" % chunk}
+    return {**extra, "subset_kernel": {"kernel": "topk_subset_kernel", "bound": "hbm",
                               "us_per_launch": round(t_sub, 1), "scores": n_scores,
                               "achieved": round(sub_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                               "frac": round(sub_gbs / HBM_PEAK_GBS, 4)},
@@ -498,12 +543,13 @@ def main():
                 lambda p: "prefill %.1f us = %.0f TFLOP/s (%.1f%% of fp8 peak), top-k rows %.1f us"
                 % (p["us_per_launch"], p["achieved"], 100 * p["frac"], p["topk_rows_us"]))
         log("chunked prefill with offload and inter-query prefetch ...")
-        section("prefill_offload", lambda: prefill_offload_measure(torch, B, gen),
+        section("prefill_offload", lambda: prefill_offload_measure(torch, B, gen,
+                                                                   cpu=not args.no_cpu_baseline),
                 lambda p: "chunked prefill: threshold bin median %d shifted vs %d unshifted"
                 % (p["thr_bin_median_shifted"], p["thr_bin_median_unshifted"]))
     if not args.no_loop:
         log("decode loop (EMA threshold, new tokens every step) ...")
-        section("loop", lambda: loop_measure(torch, B, gen),
+        section("loop", lambda: loop_measure(torch, B, gen, cpu=not args.no_cpu_baseline),
                 lambda p: "loop: median %.1f us/step, hit rate %.3f"
                 % (p["us_per_step_median"], p["hit_rate_median"]))
     if not args.no_cpu_baseline:
