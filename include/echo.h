@@ -191,7 +191,9 @@ int echo_topk(const float *scores, int64_t ld, const int32_t *len, int32_t n_row
  * subset_cnt[r] is their number (<= k, and > k - the threshold bin's size when there is one);
  * thr_cnt[r] (optional) is the threshold bin's size (0 when every bin fits).  The subset lies
  * inside the row's exact top-k.  shift [1] is a device float, the prediction of the k-th score
- * (NULL or NaN = 0: no prediction yet).  len[r] above max_len is clamped.  1 <= k <= ECHO_MAX_TOPK.
+ * (NULL or NaN = 0: no prediction yet).  len[r] above max_len is clamped; ld >= max_len.
+ * 1 <= k <= ECHO_MAX_TOPK.  ECHO_EINVAL for negative sizes, ld < max_len or NULL pointers
+ * (thr_cnt and shift may be NULL); ECHO_EUNSUPPORTED for k outside the range.
  */
 int echo_topk_subset(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
                      int32_t max_len, int32_t k, const float *shift, int32_t *subset,
@@ -205,7 +207,9 @@ int echo_topk_subset(const float *scores, int64_t ld, const int32_t *len, int32_
  * [4096 s, 4096 s + 4096), -1 padded; out_cnt[s] their number; n_seg = ceil(n_keys / 4096)
  * (1 when n_keys = 0).  The segments are 4096-wide selection rows with key_begin 0 for
  * echo_pool_lookup_alloc (k = 4096) and candidate rows for echo_prefetch_gather (cap = 4096).
- * ws: echo_union_workspace_bytes(n_keys) bytes (a bitmap, cleared by the call).
+ * ws: echo_union_workspace_bytes(n_keys) bytes (a bitmap, cleared by the call).  ECHO_EINVAL
+ * for negative sizes or NULL pointers, ECHO_EWORKSPACE for a short workspace,
+ * ECHO_EUNSUPPORTED above 2^30 keys.
  */
 size_t echo_union_workspace_bytes(int32_t n_keys);
 int echo_union_rows(const int32_t *idx, int32_t n_rows, int32_t k, int32_t n_keys, int32_t *out,
