@@ -365,7 +365,10 @@ int echo_decode_select(const echo_decode_args *a, const echo_pool *pool,
  * is nonzero afterwards.  new_host[r] must lie in [0, n_host), be distinct and not be resident
  * (ECHO_ST_BAD_HOST / ECHO_ST_DUP_HOST otherwise; the pool is then left untouched, the key
  * cache and host rows are still written).  Pure enqueue on `stream`; workspace:
- * echo_append_workspace_bytes(n_rows, pool->n_gpu).
+ * echo_append_workspace_bytes(n_rows, pool->n_gpu).  Argument errors (nothing enqueued):
+ * ECHO_EINVAL for NULL inputs, an incomplete pool, capacity or n_k below 1, or k_scale and
+ * new_scale not both given or both NULL; ECHO_EUNSUPPORTED for n_rows outside [1, 65535] or more
+ * than 2^22 GPU slots; ECHO_EWORKSPACE for a short workspace.
  */
 typedef struct {
   int32_t n_rows;
