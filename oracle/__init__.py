@@ -11,13 +11,16 @@ Citations name the web page and the section on it:
 * "ECHO page" = the blog review "OSDI'26 | ECHO：稀疏 attention 省了算力，
   却把 HBM 撑爆了" (marsggbo.github.io, 2026-07-29), sections numbered as on
   that page (§2 concepts, §5.1 metadata, §5.2 in-graph operations, §6.1
-  intra-query prefetching, §6.2 inter-query prefetching).
+  intra-query prefetching, §6.2 inter-query prefetching, §6.3 the indexer
+  kernel with a copy stage).
 
 Modules: fp8 (E4M3FN decoding), scores (indexer scores and their error
 scale), topk (exact top-k, sample threshold), pool (the residency step),
 decode (one whole step), multistep (steps in a row: new tokens with
 write-through, the EMA threshold), interquery (the chunked prefill's
-approximate top-k subsets under the shifted histogram, and its unions).
+approximate top-k subsets under the shifted histogram, and its unions),
+prefetch (the threshold prefetch over token ranges of a single scoring
+launch, and a whole step with it).
 
 Readings of points the page leaves open are listed in each module's docstring.
 Parity status of every function is stated in its docstring ("pinned by ...").
@@ -33,6 +36,7 @@ from .decode import decode_step
 from .multistep import (KeyCache, ST_CACHE_FULL, append_tokens, kth_scores, ema_update,
                         decode_loop)
 from .interquery import approx_subset, union_segments, prefill_chunk_loop
+from .prefetch import range_cap, range_prefetch, decode_step_prefetched
 
 __all__ = [
     "E4M3FN_TABLE", "decode_e4m3fn", "index_scores", "error_scale",
@@ -41,5 +45,6 @@ __all__ = [
     "PoolState", "pool_step", "allocate_with_ranks", "metadata_bytes",
     "check_pool_invariants", "PoolInvariantError", "decode_step", "KeyCache",
     "ST_CACHE_FULL", "append_tokens", "kth_scores", "ema_update", "decode_loop",
-    "approx_subset", "union_segments", "prefill_chunk_loop",
+    "approx_subset", "union_segments", "prefill_chunk_loop", "range_cap",
+    "range_prefetch", "decode_step_prefetched",
 ]
