@@ -16,16 +16,18 @@ function of the inputs alone):
 * Ranges.  Request r's tokens [0, L_r) are cut into ranges of R tokens, x = 0, 1, ...
   (one workgroup each on the GPU).  n_ranges_r = ceil(L_r / R).
 * Cap.  Request r may move cap_r = min(cap, ceil(L_r / cap_div)) rows (the page's bound in
-  proportion to the context).  Its ranges share it evenly: each moves at most
-  capw_r = min(ceil(cap_r / n_ranges_r), max_per_range) rows.
+  proportion to the context), at most max_per_range (128) per range:
+  c_r = min(cap_r, 128 * n_ranges_r).  Its ranges split c_r evenly: range x moves at most
+  m_x = floor((x + 1) c_r / n_ranges_r) - floor(x c_r / n_ranges_r) rows (the shares differ by
+  at most one and add up to c_r; a range's share is 0 when c_r < n_ranges_r).
 * Qualifying tokens.  s in the range, ascending, with float32 score > float32 theta_r (strict;
   a NaN threshold passes nothing), whose host index h = req_to_host[key_begin_r + s] lies in
   [0, N_H) and is not resident (HostTokenToGPU[h] = INF) before the prefetch.  The first
-  capw_r qualifying tokens of each range move; demand_r counts all qualifying tokens.
+  m_x qualifying tokens of each range move; demand_r counts all qualifying tokens.
 * Slots.  The pool's free slots before the prefetch, ascending, form a list F.  Request r owns
-  the entries from O_r = sum over r' < r of capw_r' * n_ranges_r'; its range x owns entries
-  O_r + x * capw_r + i for i < capw_r, and its i-th moved token takes entry i if the list is
-  that long (otherwise it does not move).
+  c_r entries from O_r = sum over r' < r of c_r'; its range x owns the m_x entries from
+  O_r + floor(x c_r / n_ranges_r), and its i-th moved token takes entry i of those if the list
+  is that long (otherwise it does not move).
 * A moved token: Free = 0, ToHost = h, HostToGPU[h] = slot, priority 0 (below every step
   stamp, so it goes first when space is short and it was not selected), and its row is copied
   from the host backup bit for bit.  Nothing is evicted.
@@ -45,13 +47,18 @@ from .topk import topk_rows
 from .pool import pool_step
 
 
-def range_cap(L, cap, cap_div, range_len, max_per_range=128):
-    """Rows one range of a request of L tokens may move (module notes: Cap)."""
+def request_cap(L, cap, cap_div, range_len, max_per_range=128):
+    """c_r: rows a request of L tokens may move over all its ranges (module notes: Cap)."""
     if L <= 0:
         return 0
-    cap_r = min(cap, -(-L // cap_div))
     n_ranges = -(-L // range_len)
-    return min(-(-cap_r // n_ranges), max_per_range)
+    return min(cap, -(-L // cap_div), max_per_range * n_ranges)
+
+
+def range_share(c, n_ranges, x):
+    """(first entry, count) of range x's share of a request's c rows (module notes)."""
+    first = x * c // n_ranges
+    return first, (x + 1) * c // n_ranges - first
 
 
 def range_prefetch(scores, theta, key_begin, key_len, req_to_host, state, host_kv, cap, cap_div,
@@ -70,10 +77,11 @@ def range_prefetch(scores, theta, key_begin, key_len, req_to_host, state, host_k
     offset = 0
     for r in range(n):
         L = max(int(key_len[r]), 0)
-        capw = range_cap(L, cap, cap_div, range_len, max_per_range)
+        c = request_cap(L, cap, cap_div, range_len, max_per_range)
         n_ranges = -(-L // range_len) if L > 0 else 0
         s32 = np.asarray(scores[r][:L], np.float64).astype(np.float32)
         for x in range(n_ranges):
+            first, share = range_share(c, n_ranges, x)
             taken = 0
             for s in range(x * range_len, min(L, (x + 1) * range_len)):
                 if not s32[s] > theta32[r]:
@@ -82,8 +90,8 @@ def range_prefetch(scores, theta, key_begin, key_len, req_to_host, state, host_k
                 if h < 0 or h >= state.n_host or state.host_to_gpu[h] != INF:
                     continue
                 demand[r] += 1
-                entry = offset + x * capw + taken
-                if taken < capw and entry < len(free_list):
+                entry = offset + first + taken
+                if taken < share and entry < len(free_list):
                     slot = int(free_list[entry])
                     new.free[slot] = 0
                     new.to_host[slot] = h
@@ -92,7 +100,7 @@ def range_prefetch(scores, theta, key_begin, key_len, req_to_host, state, host_k
                     new.gpu_kv[slot] = host_kv[h]
                     moved.append((r, s, h, slot))
                     taken += 1
-        offset += capw * n_ranges
+        offset += c
     return new, moved, demand
 
 

@@ -69,18 +69,26 @@ def test_worked_example():
         assert np.array_equal(new.gpu_kv[slot], host_kv[h])
     # the slots that held tokens before are untouched, and the input state is not modified
     assert new.to_host[0] == 2 and new.to_host[3] == 9 and new.priority[3] == 7
-    assert st.free.sum() == 6
+    assert st.free.sum() == 12
     oracle.check_pool_invariants(new, host_kv)
 
 
-def test_range_cap_cases():
-    assert pfo.range_cap(0, 10, 1, 128) == 0
-    assert pfo.range_cap(5, 3, 1, 2) == 1            # ceil(3 / 3)
-    assert pfo.range_cap(3, 3, 1, 2) == 2            # ceil(3 / 2)
-    assert pfo.range_cap(65536, 2048, 64, 512) == 8  # 1024 rows over 128 ranges
-    assert pfo.range_cap(131072, 2048, 64, 8192) == 128
-    assert pfo.range_cap(1000, 10 ** 6, 1, 8192) == 128   # clamped per range
-    assert pfo.range_cap(1, 5, 1000, 128) == 1       # ceil(1 / 1000) = 1
+def test_request_cap_and_shares():
+    assert pfo.request_cap(0, 10, 1, 128) == 0
+    assert pfo.request_cap(65536, 2048, 64, 512) == 1024        # ceil(65536 / 64)
+    assert pfo.request_cap(131072, 2048, 64, 8192) == 2048      # the cap
+    assert pfo.request_cap(1000, 10 ** 6, 1, 8192) == 128       # 128 in its one range
+    assert pfo.request_cap(1, 5, 1000, 128) == 1                # ceil(1 / 1000) = 1
+    # shares: consecutive, differing by at most one, adding up to c, for any c and n
+    for c in (0, 1, 3, 7, 64, 127, 128, 1000):
+        for n in (1, 2, 3, 4, 7, 128):
+            if c > 128 * n:
+                continue
+            sh = [pfo.range_share(c, n, x) for x in range(n)]
+            assert sum(m for _, m in sh) == c
+            assert all(sh[x][0] + sh[x][1] == sh[x + 1][0] for x in range(n - 1))
+            assert max(m for _, m in sh) - min(m for _, m in sh) <= 1
+            assert max(m for _, m in sh) <= 128
 
 
 def _random_case(seed, n_rows=5, n_gpu=400, resident=0.3, free=0.5):
@@ -128,12 +136,14 @@ def test_structure_of_what_moves(seed):
         qual_all = [s for s in range(L) if np.float32(scores[r][s]) > theta[r]
                     and st.host_to_gpu[r2h[kb[r] + s]] == oracle.INF]
         assert demand[r] == len(qual_all)
-        capw = pfo.range_cap(L, cap, cap_div, R)
-        for x in range(-(-L // R)):
+        c = pfo.request_cap(L, cap, cap_div, R)
+        n_rng = -(-L // R)
+        assert sum(len(v) for (rr, _), v in by_range.items() if rr == r) <= c
+        for x in range(n_rng):
             qual = [s for s in qual_all if s // R == x]
             got = by_range.get((r, x), [])
-            # a prefix of the range's qualifying tokens in token order, at most capw long
-            assert got == qual[: len(got)] and len(got) <= capw
+            # a prefix of the range's qualifying tokens in token order, within its share
+            assert got == qual[: len(got)] and len(got) <= pfo.range_share(c, n_rng, x)[1]
     # nothing resident before changed
     occ = np.flatnonzero(st.free == 0)
     assert np.array_equal(new.to_host[occ], st.to_host[occ])
