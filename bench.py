@@ -286,6 +286,81 @@ def prefill_offload_measure(torch, B, gen, n=32768, chunk=2048, topk=2048, seed=
             "chunks": chunks}
 
 
+def prefetch_modes_measure(torch, B, gen, inp, hb, sel, reserve, steps=20, warmup=3,
+                           kernel_reps=10):
+    """The captured decode step on one starting pool (the workload's inputs, `reserve` slots
+    free) with prefetch off, ranged (scoring in n_chunks launches, each gathering the range
+    before it) and fused (one scoring launch whose workgroups each carry a host-gather wave).
+    Per mode: the step's mean and median replay time, the guaranteed-recall misses, the
+    prefetch demand and the rows prefetched.  Also the fused scoring launch alone
+    (echo_index_scores_fused, the pool restored before every launch, outside its events)
+    against the plain scoring launch on the same inputs."""
+    from dsa_indexer_top_amd.runner import DecodeRunner, DEFAULT_PREFETCH
+    host_kv = hb.array.view(np.uint16).reshape(inp.n_host, 576)
+    pool = gen.make_pool_state(inp, sel, host_kv, reserve=reserve)
+    tokens = int(inp.key_len.astype(np.int64).sum())
+    out = {"reserve": reserve, "free_slots_at_start": int(pool.free.sum()),
+           "cap": DEFAULT_PREFETCH["cap"], "cap_div": DEFAULT_PREFETCH["cap_div"]}
+    for mode in ("off", "ranged", "fused"):
+        rn = DecodeRunner(inp, pool, host_buf=hb, prefetch=mode)
+        try:
+            rn.capture()
+            for _ in range(warmup):
+                rn.restore()
+                rn.replay()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            torch.cuda.synchronize()
+            for s_, e_ in ev:
+                rn.restore()
+                s_.record(rn.main)
+                rn.replay()
+                e_.record(rn.main)
+            torch.cuda.synchronize()
+            t = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+            res = rn.results()
+            out[mode] = {"us_per_step": round(float(t.mean()), 2),
+                         "us_per_step_median": round(float(np.median(t)), 2),
+                         "indexed_tokens_per_s": round(tokens / (float(t.mean()) / 1e6), 1),
+                         "status": res["status"], "n_miss": int(res["counters"][0]),
+                         "prefetch_demand": int(res["counters"][1]),
+                         "prefetched": int(res["counters"][2])}
+            if mode == "fused":
+                # the fused scoring launch alone, from the same starting pool every time
+                theta = torch.empty(rn.n_rows, dtype=torch.float32, device="cuda")
+                B.prefetch_threshold(rn.q, rn.w, rn.k, rn.k_scale, rn.key_begin, rn.key_len,
+                                     DEFAULT_PREFETCH["n_sample"], DEFAULT_PREFETCH["percentile"],
+                                     theta, stream=rn.main)
+                npf = torch.zeros(1, dtype=torch.int32, device="cuda")
+                ws = torch.empty(B.fused_workspace_bytes(rn.n_rows, rn.n_gpu), dtype=torch.uint8,
+                                 device="cuda")
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(kernel_reps)]
+                for s_, e_ in ev:
+                    rn.restore()
+                    s_.record(rn.main)
+                    B.index_scores_fused(rn.q, rn.w, rn.k, rn.k_scale, rn.key_begin, rn.key_len,
+                                         rn.max_len, rn.scores, theta, rn.req_to_host, rn.pool,
+                                         DEFAULT_PREFETCH["cap"], DEFAULT_PREFETCH["cap_div"], 0,
+                                         npf, None, ws, stream=rn.main)
+                    e_.record(rn.main)
+                torch.cuda.synchronize()
+                tf = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+                t_plain = kernel_time_us(torch, rn.main, lambda: B.index_scores(
+                    rn.q, rn.w, rn.k, rn.k_scale, rn.key_begin, rn.key_len, rn.max_len,
+                    rn.scores, stream=rn.main), kernel_reps)
+                moved = int(npf.cpu()[0])
+                out["fused_launches_alone"] = {
+                    "us_median": round(float(np.median(tf)), 2),
+                    "plain_scoring_us": round(t_plain, 2), "rows_moved": moved,
+                    "host_bytes_moved": moved * 576 * 2,
+                    "note": "free-slot count and list, the fused kernel and the totals; the "
+                            "threshold (sample percentile) computed once beforehand"}
+        finally:
+            rn.close()
+    return out
+
+
 def cpu_baseline(inp, host_kv, pool_arrays, min_s=10.0, budget_s=30.0):
     """The oracle, as it is, timed on the host cores on a bounded sample of the same workload:
     the whole oracle decode step (float64 scores, exact top-k, canonical pool step with the
@@ -346,7 +421,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-loop", action="store_true", help="skip the decode-loop measurement")
-    ap.add_argument("--prefetch", choices=("auto", "on", "off"), default="auto")
+    ap.add_argument("--prefetch", choices=("auto", "on", "off", "ranged", "fused"), default="auto",
+                    help="prefetch of the headline step (on = ranged)")
+    ap.add_argument("--no-prefetch-modes", action="store_true",
+                    help="skip the off / ranged / fused prefetch comparison")
     ap.add_argument("--reserve", type=int, default=None,
                     help="free GPU slots in the starting pool (default: the workload's own)")
     ap.add_argument("--percentile", type=float, default=None,
@@ -375,7 +453,8 @@ def main():
         log("copy probe: 20 x 256 MiB device copies")
         return
     cfg = gen.CONFIGS[args.workload]
-    prefetch = cfg.prefetch if args.prefetch == "auto" else args.prefetch == "on"
+    prefetch = (cfg.prefetch if args.prefetch == "auto" else
+                {"on": "ranged", "off": False}.get(args.prefetch, args.prefetch))
     if args.probe == "prefill":
         pc = gen.PREFILL["prefill_32k"]
         n = pc["n"]
@@ -417,7 +496,8 @@ def main():
     tws = torch.empty(B.topk_workspace_bytes(n_rows, max_len), dtype=torch.uint8, device="cuda")
     B.index_scores(dq, dw, dk, dks, dkb, dkl, max_len, sc)
     B.topk(sc, dkl, max_len, cfg.topk, sel, tws)
-    pool = gen.make_pool_state(inp, sel.cpu().numpy(), host_kv, reserve=args.reserve)
+    sel_idx = sel.cpu().numpy()
+    pool = gen.make_pool_state(inp, sel_idx, host_kv, reserve=args.reserve)
     del sc, sel, tws
     pf = None if args.percentile is None else dict(percentile=args.percentile)
     rn = DecodeRunner(inp, pool, host_buf=hb, prefetch=prefetch, pf=pf)
@@ -497,7 +577,8 @@ def main():
         "data": "synthetic (seeded)",
         "config": {"workload": args.workload, "description": WORKLOADS[args.workload],
                    "batch": n_rows, "tokens": tokens, "topk": rn.topk, "n_gpu_slots": rn.n_gpu,
-                   "n_host_slots": rn.n_host, "prefetch": bool(prefetch),
+                   "n_host_slots": rn.n_host,
+                   "prefetch": ("off", "ranged", "fused")[B.prefetch_mode(prefetch)],
                    "free_slots_at_start": int(pool.free.sum()),
                    "timing": "HIP events around each graph replay on its stream; pool restored "
                              "from a pristine copy between replays, outside the events"},
@@ -552,6 +633,15 @@ def main():
         section("loop", lambda: loop_measure(torch, B, gen, cpu=not args.no_cpu_baseline),
                 lambda p: "loop: median %.1f us/step, hit rate %.3f"
                 % (p["us_per_step_median"], p["hit_rate_median"]))
+    if not args.no_prefetch_modes:
+        log("prefetch off / ranged / fused on one starting pool ...")
+        pf_reserve = args.reserve if args.reserve is not None else max(cfg.reserve, n_rows * cfg.topk)
+        section("prefetch_modes", lambda: prefetch_modes_measure(torch, B, gen, inp, hb, sel_idx,
+                                                                 pf_reserve),
+                lambda p: "prefetch modes: off %.1f, ranged %.1f, fused %.1f us/step; fused "
+                "launches alone %.1f us vs plain scoring %.1f us" % (
+                    p["off"]["us_per_step"], p["ranged"]["us_per_step"], p["fused"]["us_per_step"],
+                    p["fused_launches_alone"]["us_median"], p["fused_launches_alone"]["plain_scoring_us"]))
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         section("cpu_baseline", lambda: cpu_baseline(inp, host_kv, pool),

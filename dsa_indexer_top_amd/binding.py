@@ -15,6 +15,8 @@ LIB_PATH = os.path.join(_PKG, "libecho.so")
 ECHO_OK, ECHO_EINVAL, ECHO_EUNSUPPORTED, ECHO_EHIP, ECHO_EWORKSPACE = 0, -1, -2, -3, -4
 ST_EXHAUSTED, ST_BAD_HOST, ST_DUP_HOST, ST_CACHE_FULL = 1, 2, 4, 8
 RECALL_GATHER, RECALL_MEMCPY = 0, 1
+PREFETCH_OFF, PREFETCH_RANGED, PREFETCH_FUSED = 0, 1, 2
+FUSED_MAX_RANGE, FUSED_MAX_PER_RANGE = 8192, 128
 INF = 0x7FFFFFFF
 ROW_ELEMS = 576
 
@@ -39,7 +41,8 @@ class DecodeArgs(C.Structure):
                 ("key_len", P), ("req_to_host", P), ("n_rows", I32), ("max_key_len", I32),
                 ("topk", I32), ("step_id", I32), ("prefetch", I32), ("n_chunks", I32),
                 ("n_sample", I32), ("percentile", F32), ("cap", I32), ("cap_div", I32),
-                ("theta_ema", P), ("ema_alpha", F32), ("step_dev", P), ("reserve_free", I32)]
+                ("theta_ema", P), ("ema_alpha", F32), ("step_dev", P), ("reserve_free", I32),
+                ("pf_range", I32)]
 
 
 class DecodeOut(C.Structure):
@@ -64,6 +67,9 @@ _SIGS = {
     "echo_index_scores_prefetch": (C.c_int, [P, P, P, P, P, P, I32, I32, I32, I32, P, I64,
                                              P, P, P, P, P, P, I32, I32, P]),
     "echo_prefetch_threshold": (C.c_int, [P, P, P, P, P, P, I32, I32, F32, P, P]),
+    "echo_fused_workspace_bytes": (SZ, [I32, I32]),
+    "echo_index_scores_fused": (C.c_int, [P, P, P, P, P, P, I32, I32, P, I64, P, P,
+                                          C.POINTER(Pool), I32, I32, I32, P, P, P, SZ, P]),
     "echo_index_scores_prefill": (C.c_int, [P, P, P, I32, I32, I32, P, I64, P]),
     "echo_topk_workspace_bytes": (SZ, [I32, I32]),
     "echo_topk": (C.c_int, [P, I64, P, I32, I32, I32, P, P, SZ, P]),
@@ -157,6 +163,31 @@ def index_scores_prefetch(q, w, k, k_scale, key_begin, key_len, max_key_len, tok
           ptr(key_len), q.shape[0], max_key_len, tok_lo, tok_hi, ptr(scores), ld, ptr(theta),
           ptr(req_to_host), ptr(host_to_gpu), ptr(cand), ptr(cand_cnt), ptr(total_cnt), cap,
           cap_div, stream_handle(stream))
+
+
+def fused_workspace_bytes(n_q, n_gpu):
+    return lib().echo_fused_workspace_bytes(n_q, n_gpu)
+
+
+def index_scores_fused(q, w, k, k_scale, key_begin, key_len, max_key_len, scores, theta,
+                       req_to_host, pool, cap, cap_div, range_len, n_prefetched, demand, ws,
+                       ld=None, stream=None):
+    ld = scores.shape[-1] if ld is None else ld
+    _call("echo_index_scores_fused", ptr(q), ptr(w), ptr(k), ptr(k_scale), ptr(key_begin),
+          ptr(key_len), q.shape[0], max_key_len, ptr(scores), ld, ptr(theta), ptr(req_to_host),
+          C.byref(pool), cap, cap_div, range_len, ptr(n_prefetched), ptr(demand), ptr(ws),
+          ws.numel() * ws.element_size(), stream_handle(stream))
+
+
+def prefetch_mode(prefetch):
+    """PREFETCH_* code of False / True / "ranged" / "fused" (or the code itself)."""
+    if prefetch in (False, None, 0, "off"):
+        return PREFETCH_OFF
+    if prefetch in (True, 1, "ranged"):
+        return PREFETCH_RANGED
+    if prefetch in (2, "fused"):
+        return PREFETCH_FUSED
+    raise ValueError("prefetch mode %r" % (prefetch,))
 
 
 def prefetch_begin(pool, free_list, free_count, stream=None):

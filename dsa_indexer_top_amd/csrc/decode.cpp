@@ -12,8 +12,11 @@
 //        -> top-k finish + lookup of the rest (+ staging of the split's misses from host memory)
 //        -> evict-1 (+ staging of the finish's misses) -> evict-2 + allocate -> recall scatter
 //
-// With prefetch, scoring is split into n_chunks token ranges: the launch of range c also
+// With ranged prefetch, scoring is split into n_chunks token ranges: the launch of range c also
 // gathers range c-1's candidates, and a gather launch for the last range precedes the split.
+// With fused prefetch (§6.3), one launch scores and gathers: every workgroup has a wave that
+// moves its range's over-threshold rows from host memory while the other waves score; the
+// pool statistics then run ahead of it, with the free-slot list.
 // With the EMA threshold (§6.1) a last small launch takes each request's k-th score and updates
 // the caller's estimate for the next step.
 #include <algorithm>
@@ -37,10 +40,11 @@ struct DecodeWs {
   int32_t *free_list;  // [n_gpu]
   int32_t *free_count; // [2]
   uint16_t *stage;     // [n_rows * topk][ROW] recalled rows before they go to their slots
+  FusedWs fz;          // fused prefetch
 };
 
 static size_t decode_ws_layout(const echo_decode_args *a, int32_t n_gpu, void *base, DecodeWs *w) {
-  const bool pf = a->prefetch != 0;
+  const bool pf = a->prefetch == ECHO_PREFETCH_RANGED, fz = a->prefetch == ECHO_PREFETCH_FUSED;
   const size_t nr = static_cast<size_t>(a->n_rows), nc = pf ? static_cast<size_t>(a->n_chunks) : 0;
   size_t off = 0;
   auto take = [&](size_t b) { size_t o = off; off += al(b); return o; };
@@ -52,9 +56,10 @@ static size_t decode_ws_layout(const echo_decode_args *a, int32_t n_gpu, void *b
   const size_t zero_end = o_pool + static_cast<size_t>(pw.zero_words) * 4;
   const size_t o_split = take(topk_split_ws_bytes(a->n_rows, a->max_key_len, a->topk));
   const size_t o_st = take(nr * static_cast<size_t>(a->topk) * ROW * 2);
-  size_t o_th = 0, o_c = 0, o_fl = 0, o_fc = 0;
+  size_t o_th = 0, o_c = 0, o_fl = 0, o_fc = 0, o_fz = 0;
+  if (pf || fz) o_th = take(nr * 4);
+  if (fz) o_fz = take(fused_ws_layout(a->n_rows, n_gpu, nullptr, nullptr));
   if (pf) {
-    o_th = take(nr * 4);
     o_c = take(nc * nr * static_cast<size_t>(a->cap) * 4);
     o_fl = take(static_cast<size_t>(n_gpu) * 4);
     o_fc = take(2 * 4);
@@ -72,6 +77,7 @@ static size_t decode_ws_layout(const echo_decode_args *a, int32_t n_gpu, void *b
     w->cand = reinterpret_cast<int32_t *>(b + o_c);
     w->free_list = reinterpret_cast<int32_t *>(b + o_fl);
     w->free_count = reinterpret_cast<int32_t *>(b + o_fc);
+    if (fz) fused_ws_layout(a->n_rows, n_gpu, b + o_fz, &w->fz);
   }
   return off;
 }
@@ -91,8 +97,15 @@ static int validate(const echo_decode_args *a, const echo_pool *pool, const echo
       !pool->host_to_gpu || !pool->indices_buf || !pool->gpu_kv || !pool->host_kv || !pool->status)
     return fail(ECHO_EINVAL, "echo_decode_select: incomplete pool");
   if (pool->n_gpu > (1 << 22)) return fail(ECHO_EUNSUPPORTED, "echo_decode_select: more than 4M GPU slots");
+  if (a->prefetch < ECHO_PREFETCH_OFF || a->prefetch > ECHO_PREFETCH_FUSED)
+    return fail(ECHO_EUNSUPPORTED, "echo_decode_select: prefetch mode %d", a->prefetch);
+  if (a->prefetch == ECHO_PREFETCH_RANGED && (a->n_chunks < 1 || a->n_chunks > 16))
+    return fail(ECHO_EUNSUPPORTED, "echo_decode_select: n_chunks %d outside [1, 16]", a->n_chunks);
+  if (a->prefetch == ECHO_PREFETCH_FUSED && a->pf_range != 0 &&
+      (a->pf_range % 128 != 0 || a->pf_range < 128 || a->pf_range > ECHO_FUSED_MAX_RANGE))
+    return fail(ECHO_EUNSUPPORTED, "echo_decode_select: pf_range %d is not 0 or a multiple of 128 in [128, %d]",
+                a->pf_range, ECHO_FUSED_MAX_RANGE);
   if (a->prefetch) {
-    if (a->n_chunks < 1 || a->n_chunks > 16) return fail(ECHO_EUNSUPPORTED, "echo_decode_select: n_chunks %d outside [1, 16]", a->n_chunks);
     if (a->n_sample < 64 || a->n_sample > 4096 || (a->n_sample & (a->n_sample - 1)))
       return fail(ECHO_EUNSUPPORTED, "echo_decode_select: n_sample must be a power of two in [64, 4096]");
     if (!(a->percentile > 0.f && a->percentile <= 100.f)) return fail(ECHO_EINVAL, "echo_decode_select: percentile outside (0, 100]");
@@ -114,7 +127,7 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
   if (!ws || ws_bytes < need) return fail(ECHO_EWORKSPACE, "echo_decode_select: workspace %zu < %zu", ws_bytes, need);
   W.pool.reserve = static_cast<uint32_t>(a->reserve_free);
   const int32_t n_ent = a->n_rows * a->topk;
-  const bool pf = a->prefetch != 0;
+  const bool pf = a->prefetch == ECHO_PREFETCH_RANGED, fz = a->prefetch == ECHO_PREFETCH_FUSED;
   const int nc = pf ? a->n_chunks : 1;
 
   if ((rc = launch_zero2_i32(o->counters, 8, reinterpret_cast<int32_t *>(W.hist0), W.zero_words, m))) return rc;
@@ -128,11 +141,19 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
   // prefetch threshold: the caller's EMA estimate (§6.1), or a sample percentile of this
   // step's scores when there is no history
   const float *theta = a->theta_ema ? a->theta_ema : W.theta;
-  if (pf) {
-    if (!a->theta_ema &&
-        (rc = launch_prefetch_threshold(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len,
-                                        a->n_rows, a->n_sample, a->percentile, W.theta, m)))
+  if ((pf || fz) && !a->theta_ema &&
+      (rc = launch_prefetch_threshold(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len,
+                                      a->n_rows, a->n_sample, a->percentile, W.theta, m)))
+    return rc;
+  if (fz) {
+    const int32_t range = fused_range(static_cast<int64_t>(a->n_rows) * a->max_key_len, a->max_key_len,
+                                      a->pf_range);
+    if ((rc = launch_fused_prefetch(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len, a->n_rows,
+                                    a->max_key_len, o->scores, a->max_key_len, theta, a->req_to_host,
+                                    pool, a->cap, a->cap_div, range, W.fz, W.hist0, &W.pool, stamp,
+                                    o->counters + 1, o->counters + 2, m)))
       return rc;
+  } else if (pf) {
     if ((rc = launch_prefetch_begin(pool, W.free_list, W.free_count, m))) return rc;
     const int32_t span = (a->max_key_len + nc - 1) / nc;
     for (int c = 0; c < nc; ++c) {
@@ -197,7 +218,7 @@ struct echo_graph_s : GraphHandle {};
 
 extern "C" size_t echo_decode_workspace_bytes(const echo_decode_args *a, int32_t n_gpu) {
   if (!a || n_gpu < 0 || a->n_rows < 0 || a->topk < 0 || a->max_key_len < 0) return 0;
-  if (a->prefetch && (a->n_chunks < 1 || a->cap < 0)) return 0;
+  if (a->prefetch == ECHO_PREFETCH_RANGED && (a->n_chunks < 1 || a->cap < 0)) return 0;
   return decode_ws_layout(a, n_gpu, nullptr, nullptr);
 }
 

@@ -179,6 +179,30 @@ int launch_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
                            const int32_t *cand_cnt, int32_t n_q, int32_t cap,
                            const int32_t *free_list, int32_t *free_count, int32_t *n_prefetched,
                            const PoolFastWs *pw, Stamp stamp, hipStream_t st);
+// Scoring with the prefetch in the same kernel (score_fused.hip).  Workspace: counts and the
+// ascending list of free slots, slice offsets and per-request totals.
+struct FusedWs {
+  int32_t *chunk_free;   // [ceil(n_gpu / 4096)] free slots per chunk
+  int32_t *free_list;    // [n_gpu] ascending
+  int32_t *slice_off;    // [n_q] first free_list entry of each request's slices
+  int32_t *counts;       // [2]: 0 length of free_list
+  int32_t *demand;       // [n_q] tokens above the threshold and not resident
+  int32_t *taken;        // [n_q] rows prefetched
+};
+size_t fused_ws_layout(int32_t n_q, int32_t n_gpu, void *base, FusedWs *w);
+// Tokens per range (one workgroup each): pf_range when nonzero, else enough workgroups to put
+// several on every CU.
+int32_t fused_range(int64_t total_tokens, int32_t max_len, int32_t pf_range);
+// hist0 (optional): the top-k digit-0 histograms, as launch_score_decode; stats (optional): the
+// pool-step statistics, computed ahead of the kernel and kept current for the slots it fills;
+// demand_out / taken_out (optional): the step's totals.
+int launch_fused_prefetch(const uint8_t *q, const float *w, const uint8_t *k, const float *k_scale,
+                          const int64_t *key_begin, const int32_t *key_len, int32_t n_q,
+                          int32_t max_len, float *scores, int64_t ld, const float *theta,
+                          const int32_t *req_to_host, const echo_pool *pool, int32_t cap,
+                          int32_t cap_div, int32_t range, const FusedWs &Z, uint32_t *hist0,
+                          const PoolFastWs *stats, Stamp stamp, int32_t *demand_out,
+                          int32_t *taken_out, hipStream_t st);
 int launch_zero_i32(int32_t *p, int64_t n, hipStream_t st);
 int launch_zero2_i32(int32_t *p, int64_t n, int32_t *q, int64_t m, hipStream_t st);
 int launch_sum_i32(const int32_t *v, int32_t n, int32_t *out, hipStream_t st);

@@ -7,7 +7,8 @@ import numpy as np
 
 from . import binding as B
 
-DEFAULT_PREFETCH = dict(n_chunks=4, n_sample=4096, percentile=95.0, cap=2048, cap_div=1024)
+DEFAULT_PREFETCH = dict(n_chunks=4, n_sample=4096, percentile=95.0, cap=2048, cap_div=1024,
+                        range=0)
 
 
 def _dev(a):
@@ -17,10 +18,12 @@ def _dev(a):
 
 class DecodeRunner:
     """inp: inputs.DecodeInputs; pool: inputs.PoolArrays; host_kv: uint16 [N_H, 576] numpy
-    array, or a binding.HostBuffer already holding it (pass host_buf=...)."""
+    array, or a binding.HostBuffer already holding it (pass host_buf=...).  prefetch: False,
+    True / "ranged" or "fused"; theta (optional, float32 [B]): a given per-request threshold
+    in place of the sample percentile (the step's EMA estimate; restored by restore())."""
 
     def __init__(self, inp, pool, host_kv=None, host_buf=None, prefetch=False, pf=None,
-                 topk=None, step_id=None, reserve=0):
+                 topk=None, step_id=None, reserve=0, theta=None, alpha=0.5):
         import torch
         self.torch = torch
         cfg = inp.cfg
@@ -67,9 +70,16 @@ class DecodeRunner:
             self.q.data_ptr(), self.w.data_ptr(), self.k.data_ptr(),
             None if self.k_scale is None else self.k_scale.data_ptr(),
             self.key_begin.data_ptr(), self.key_len.data_ptr(), self.req_to_host.data_ptr(),
-            self.n_rows, self.max_len, self.topk, self.step_id, 1 if prefetch else 0,
+            self.n_rows, self.max_len, self.topk, self.step_id, B.prefetch_mode(prefetch),
             p["n_chunks"], p["n_sample"], p["percentile"], p["cap"], p["cap_div"])
         self.args.reserve_free = reserve
+        self.args.pf_range = p["range"]
+        self.theta0 = self.theta = None
+        if theta is not None:
+            self.theta0 = _dev(np.asarray(theta, np.float32))
+            self.theta = self.theta0.clone()
+            self.args.theta_ema = self.theta.data_ptr()
+            self.args.ema_alpha = alpha
         nbytes = B.decode_workspace_bytes(self.args, self.n_gpu)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
         self.main = torch.cuda.Stream()
@@ -82,6 +92,8 @@ class DecodeRunner:
             for n, t in self.pristine.items():
                 self.live[n].copy_(t)
             self.status.zero_()
+            if self.theta is not None:
+                self.theta.copy_(self.theta0)
 
     def run_eager(self):
         B.decode_select(self.args, self.pool, self.out, self.ws, self.main, self.side)
@@ -174,10 +186,11 @@ class LoopRunner:
             self.q.data_ptr(), self.w.data_ptr(), self.k.data_ptr(),
             None if self.k_scale is None else self.k_scale.data_ptr(),
             self.key_begin.data_ptr(), self.key_len.data_ptr(), self.req_to_host.data_ptr(),
-            B_, cap, topk, 0, 1 if prefetch else 0, p["n_chunks"], p["n_sample"],
+            B_, cap, topk, 0, B.prefetch_mode(prefetch), p["n_chunks"], p["n_sample"],
             p["percentile"], p["cap"], p["cap_div"],
             self.theta.data_ptr() if ema else None, alpha)
         self.args.reserve_free = reserve
+        self.args.pf_range = p["range"]
         self.app = B.AppendArgs(
             B_, cap, self.k.shape[0], self.new_k.data_ptr(),
             None if self.new_scale is None else self.new_scale.data_ptr(),

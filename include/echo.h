@@ -10,7 +10,9 @@
  *         buffer, the two slot<->host maps with an infinity sentinel);
  *   §5.2  the in-graph allocate / free / recall operations, with the recall copying rows
  *         straight out of host memory from a GPU kernel;
- *   §6.1  threshold prefetch during scoring, made lossless by the guaranteed recall.
+ *   §6.1  threshold prefetch during scoring, made lossless by the guaranteed recall;
+ *   §6.3  the indexer kernel whose threshold test feeds a queue that a copy stage in the same
+ *         kernel drains from host memory.
  *
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless marked [host].  The caller owns every buffer and
@@ -41,6 +43,17 @@ extern "C" {
 #define ECHO_ROW_ELEMS 576 /* MLA latent row: 512 compressed + 64 RoPE values (bf16 bits) */
 #define ECHO_INF 0x7FFFFFFF
 #define ECHO_MAX_TOPK 4096
+#define ECHO_FUSED_MAX_RANGE 8192      /* tokens per range of the fused prefetch, at most */
+#define ECHO_FUSED_MAX_PER_RANGE 128   /* rows one range of the fused prefetch moves, at most */
+
+/* Prefetch modes (echo_decode_args.prefetch). */
+enum {
+  ECHO_PREFETCH_OFF = 0,
+  ECHO_PREFETCH_RANGED = 1, /* scoring split into n_chunks launches; each also gathers the
+                               candidates of the range before it */
+  ECHO_PREFETCH_FUSED = 2   /* one launch: scoring waves and a host-gather wave per workgroup
+                               (echo_index_scores_fused) */
+};
 
 enum {
   ECHO_OK = 0,
@@ -145,6 +158,43 @@ int echo_index_scores_prefetch(const uint8_t *q, const float *w, const uint8_t *
                                const float *theta, const int32_t *req_to_host,
                                const int32_t *host_to_gpu, int32_t *cand, int32_t *cand_cnt,
                                int32_t *total_cnt, int32_t cap, int32_t cap_div, void *stream);
+
+/*
+ * Scoring and threshold prefetch in one kernel (§6.3, with the §6.1 threshold and the §5.2
+ * allocate and zero-copy row reads).  Scores every request exactly as echo_index_scores does
+ * (same values), and moves rows of tokens scoring above theta[r] into free GPU slots while the
+ * later keys are still being scored.
+ *   Ranges.  Request r's tokens are cut into n_r = ceil(key_len[r] / range) ranges of `range`
+ *   tokens (one workgroup each; range = 0 picks one; else a multiple of 128 in
+ *   [128, ECHO_FUSED_MAX_RANGE]).  Request r may move c_r = min(cap, ceil(key_len[r] / cap_div),
+ *   ECHO_FUSED_MAX_PER_RANGE * n_r) rows; its range x may move
+ *   m_x = floor((x + 1) c_r / n_r) - floor(x c_r / n_r) of them.
+ *   Which rows.  In each range, the tokens s (ascending) with score > theta[r] (fp32, strict;
+ *   NaN never passes) whose host index h = req_to_host[key_begin[r] + s] is in [0, n_host) and
+ *   not resident (host_to_gpu[h] == ECHO_INF when the call starts) qualify; the first m_x of
+ *   them move.
+ *   Which slots.  The pool's free slots at the start, in ascending order, form a list.
+ *   Request r owns the c_r list entries from O_r = sum over r' < r of c_r'; its range x owns
+ *   entries O_r + floor(x c_r / n_r) + i, i < m_x, and its i-th moved token takes entry i while
+ *   that entry exists (a short list leaves later ranges without slots).
+ *   Each moved token: free = 0, gpu_to_host = h, host_to_gpu[h] = slot, priority 0, and its
+ *   row copied from host_kv.  Nothing is evicted; nothing moves when the status word is
+ *   nonzero.  The result depends on the inputs alone (no timing).
+ *   Outputs: *n_prefetched = rows moved; *demand (or NULL) = qualifying tokens, before caps.
+ *   Workspace: echo_fused_workspace_bytes(n_q, pool->n_gpu) bytes.  Host indices are unique
+ *   across requests (caller precondition).
+ * Errors: EINVAL for negative sizes, ld < max_key_len, cap < 0, cap_div < 1, NULL pointers or
+ * an incomplete pool; EUNSUPPORTED for n_q > 65535, max_key_len or n_gpu above 2^22, or a bad
+ * range; EWORKSPACE for a short workspace.
+ */
+size_t echo_fused_workspace_bytes(int32_t n_q, int32_t n_gpu);
+int echo_index_scores_fused(const uint8_t *q, const float *w, const uint8_t *k,
+                            const float *k_scale, const int64_t *key_begin,
+                            const int32_t *key_len, int32_t n_q, int32_t max_key_len,
+                            float *scores, int64_t ld, const float *theta,
+                            const int32_t *req_to_host, const echo_pool *pool, int32_t cap,
+                            int32_t cap_div, int32_t range, int32_t *n_prefetched,
+                            int32_t *demand, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Per-request prefetch threshold: theta[r] = the nearest-rank `percentile` of the scores of
@@ -306,9 +356,9 @@ typedef struct {
   int32_t max_key_len;
   int32_t topk;
   int32_t step_id;
-  /* prefetch (off when prefetch == 0) */
+  /* prefetch: ECHO_PREFETCH_OFF, _RANGED or _FUSED */
   int32_t prefetch;
-  int32_t n_chunks;          /* scoring split into this many token ranges (1..16) */
+  int32_t n_chunks;          /* RANGED: scoring split into this many token ranges (1..16) */
   int32_t n_sample;          /* threshold sample size (power of two, 64..4096) */
   float percentile;          /* threshold percentile, e.g. 95 */
   int32_t cap;               /* per-request candidate cap bound */
@@ -329,6 +379,8 @@ typedef struct {
      order until reserve_free slots stay free, as far as unprotected slots allow.  0 = evict
      only what the misses need.  0 <= reserve_free <= n_gpu. */
   int32_t reserve_free;
+  /* FUSED: tokens per range (0 = the library picks; else as echo_index_scores_fused) */
+  int32_t pf_range;
 } echo_decode_args;
 
 typedef struct {             /* device outputs of one step */

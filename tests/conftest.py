@@ -15,11 +15,13 @@ def pytest_configure(config):
 
 # GPU test modules run bottom-up: the building blocks (scores, top-k, pool step) before the
 # whole decode step, then the prefill indexer, then what is built on top (steps in a row, the
-# inter-query prefetch, several layers), and the full-size stress step last, so that under -x the first failure names the lowest broken piece and
-# hides no result below it.  Other modules keep their place before these; test_zz_* stay last.
+# inter-query prefetch, several layers, the scoring launch with a host-gather wave), and the
+# full-size stress step last, so that under -x the first failure names the lowest broken piece
+# and hides no result below it.  Other modules keep their place before these; test_zz_* stay
+# last.
 BOTTOM_UP = ("test_gpu_scores.py", "test_gpu_topk.py", "test_gpu_pool.py", "test_gpu_decode.py",
              "test_gpu_prefill.py", "test_gpu_multistep.py", "test_gpu_interquery.py",
-             "test_gpu_layers.py", "test_gpu_stress.py")
+             "test_gpu_layers.py", "test_gpu_fused.py", "test_gpu_stress.py")
 
 
 def _order(item):

@@ -453,6 +453,14 @@ unsigned long long __ballot(bool pred) {
   wave_op(&p, 1, &r, 8, op_ballot, nullptr);
   return r;
 }
+// __builtin_amdgcn_wave_barrier: on the GPU only a compiler ordering point, since a wave's LDS
+// operations execute in order; here the lanes of the wave meet, so an LDS word one lane wrote
+// before it is seen by the others after it, as in lockstep execution.
+static void op_none(const unsigned char *, unsigned char *, size_t, size_t, const void *) {}
+void emu_amdgcn_wave_barrier() {
+  unsigned char p = 0, r;
+  wave_op(&p, 1, &r, 1, op_none, nullptr);
+}
 int emu_readlane_i(int v, int lane) {
   IdxIn a{v, lane};
   int r;

@@ -104,6 +104,7 @@ template <typename T> inline T emu_nontemporal_load(const T *p) { return *p; }
 unsigned long long __ballot(bool pred);
 inline unsigned long long __ballot(int pred) { return __ballot(pred != 0); }
 int emu_readlane_i(int v, int lane);
+void emu_amdgcn_wave_barrier();                                  // lanes of the wave meet
 inline int emu_amdgcn_readlane(int v, int lane) { return emu_readlane_i(v, lane); }
 inline int emu_amdgcn_readfirstlane(int v) { return emu_readlane_i(v, 0); }   // full waves only
 inline void emu_amdgcn_sched_group_barrier(int, int, int) {}                 // scheduling hint

@@ -107,6 +107,12 @@ def test_decode_select_argument_errors():
         (dict(prefetch=1, n_sample=1000), B.ECHO_EUNSUPPORTED),
         (dict(prefetch=1, percentile=0.0), B.ECHO_EINVAL),
         (dict(prefetch=1, cap=0), B.ECHO_EINVAL),
+        (dict(prefetch=3), B.ECHO_EUNSUPPORTED),
+        (dict(prefetch=-1), B.ECHO_EUNSUPPORTED),
+        (dict(prefetch=2, pf_range=100), B.ECHO_EUNSUPPORTED),
+        (dict(prefetch=2, pf_range=8192 + 128), B.ECHO_EUNSUPPORTED),
+        (dict(prefetch=2, cap_div=0), B.ECHO_EINVAL),
+        (dict(prefetch=2, n_sample=100), B.ECHO_EUNSUPPORTED),
     ]
     for kw, code in cases:
         a = _decode_args(**kw)
@@ -193,6 +199,36 @@ def test_interquery_argument_errors():
     assert L.echo_threshold_ema(FAKE, 64, FAKE, 1, 8, 0.5, None, None, None) == B.ECHO_EINVAL
 
 
+def test_fused_prefetch_argument_errors():
+    L = B.lib()
+    p, ws = _pool(), 1 << 30
+
+    def call(n_q=2, max_len=4096, ld=4096, cap=64, cap_div=8, rng=0, pool=p, w=FAKE, nbytes=ws,
+             theta=FAKE):
+        return L.echo_index_scores_fused(FAKE, FAKE, FAKE, None, FAKE, FAKE, n_q, max_len, FAKE, ld,
+                                         theta, FAKE, C.byref(pool) if pool is not None else None,
+                                         cap, cap_div, rng, FAKE, None, w, nbytes, None)
+    assert call(n_q=-1) == B.ECHO_EINVAL and "negative" in _err()
+    assert call(n_q=70000) == B.ECHO_EUNSUPPORTED
+    assert call(max_len=(1 << 22) + 1, ld=(1 << 22) + 1) == B.ECHO_EUNSUPPORTED
+    assert call(ld=100) == B.ECHO_EINVAL and "ld" in _err()
+    assert call(cap=-1) == B.ECHO_EINVAL
+    assert call(cap_div=0) == B.ECHO_EINVAL
+    assert call(pool=None) == B.ECHO_EINVAL
+    assert call(pool=_pool(n_gpu=0)) == B.ECHO_EINVAL
+    assert call(pool=_pool(n_gpu=(1 << 22) + 1)) == B.ECHO_EUNSUPPORTED
+    assert call(w=None) == B.ECHO_EINVAL
+    assert call(theta=None) == B.ECHO_EINVAL and "NULL" in _err()
+    need = L.echo_fused_workspace_bytes(2, p.n_gpu)
+    assert need >= p.n_gpu * 4                       # the free-slot list fits
+    assert call(nbytes=need - 1) == B.ECHO_EWORKSPACE and "workspace" in _err()
+    for rng in (64, 129, 8192 + 128, -128):
+        assert call(rng=rng) == B.ECHO_EUNSUPPORTED, rng
+        assert "range" in _err()
+    assert L.echo_fused_workspace_bytes(-1, 8) == 0
+    assert L.echo_fused_workspace_bytes(8, 1 << 20) > L.echo_fused_workspace_bytes(8, 1 << 16)
+
+
 def test_workspace_sizes():
     L = B.lib()
     assert L.echo_pool_workspace_bytes(-1, 8, 8) == 0
@@ -210,6 +246,9 @@ def test_workspace_sizes():
     a = _decode_args()
     pf = _decode_args(prefetch=1)
     assert L.echo_decode_workspace_bytes(C.byref(pf), 65536) > L.echo_decode_workspace_bytes(C.byref(a), 65536)
+    fz = _decode_args(prefetch=2, n_chunks=0)
+    assert L.echo_decode_workspace_bytes(C.byref(fz), 65536) >= (
+        L.echo_decode_workspace_bytes(C.byref(a), 65536) + L.echo_fused_workspace_bytes(8, 65536))
     assert L.echo_decode_workspace_bytes(C.byref(_decode_args(n_rows=-1)), 65536) == 0
     assert L.echo_decode_workspace_bytes(C.byref(a), -1) == 0
 

@@ -1,10 +1,12 @@
 """The stress decode workload at full size (64 requests x 131072 tokens, general FP8 keys with
 per-token scales, top-2048, half of the selection resident in a pool of 2^20 slots with 131072
 kept free, threshold prefetch from a 4096-score sample, the step captured as one hipGraph), in
-the launch configuration the benchmark times.  The oracle computes sampled requests one by one;
-the rest is checked through properties that hold at any size: the step's selection equals the
-exact top-k of its own scores, every selected token is resident with its row equal to the host
-backup bit for bit, and the pool's maps stay a bijection."""
+the launch configuration the benchmark times, with the ranged prefetch (scoring in several
+launches) and with the fused one (one scoring launch with a host-gather wave per workgroup).
+The oracle computes sampled requests one by one; the rest is checked through properties that
+hold at any size: the step's selection equals the exact top-k of its own scores, every selected
+token is resident with its row equal to the host backup bit for bit, and the pool's maps stay a
+bijection."""
 
 import numpy as np
 import pytest
@@ -43,38 +45,44 @@ def test_stress_step(cfg):
         want_idx = sel.cpu().numpy()
         del dq, dw, dk, dks, dkb, dkl, sc, sel, tws
         pool = gen.make_pool_state(inp, want_idx, host_kv)
-        announce("stress %s: captured step with prefetch" % cfg.name)
-        rn = DecodeRunner(inp, pool, host_buf=hb, prefetch=True)
-        try:
-            rn.capture()
-            rn.replay()
-            got = rn.results()
-        finally:
-            rn.close()
-        assert got["status"] == 0
-        # the step's top-k is the exact top-k of the scores it computed
-        assert np.array_equal(got["topk_idx"], want_idx)
-        assert int(got["counters"][2]) > 0 and int(got["counters"][1]) >= int(got["counters"][2])
-        # every selected token resident, bit for bit; the maps a bijection
-        idx = got["topk_idx"]
-        rows, cols = np.nonzero(idx >= 0)
-        assert len(rows) == n_rows * cfg.topk
-        hosts = inp.req_to_host[inp.key_begin[rows] + idx[rows, cols]]
-        st = oracle.PoolState(*(got["pool"][n] for n in ("free", "priority", "to_host",
-                                                         "host_to_gpu", "indices_buf", "gpu_kv")))
-        oracle.check_pool_invariants(st, host_kv, hosts, got["topk_slot"][rows, cols])
-        # sampled requests against the oracle: scores within 1e-4 T, and the selection differing
-        # from the oracle's only by tokens within that tolerance of its k-th score
-        announce("stress %s: oracle on sampled requests" % cfg.name)
-        for r in sorted({0, min(n_rows - 1, n_rows // 2 + 5), n_rows - 1}):
-            sl = slice(r, r + 1)
-            args = (inp.q[sl], inp.w[sl], inp.k, inp.k_scale, inp.key_begin[sl], inp.key_len[sl])
-            s, T = oracle.index_scores(*args)[0], oracle.error_scale(*args)[0]
-            g = got["scores"][r, :len(s)].astype(np.float64)
-            assert (np.abs(g - s) <= TOL * T).all(), "request %d scores" % r
-            want = oracle.topk_row(s, cfg.topk)
-            kth = want[np.argmin(s[want])]
-            for t in np.setxor1d(idx[r], want):
-                assert abs(s[t] - s[kth]) <= TOL * (T[t] + T[kth]), "request %d token %d" % (r, t)
+        for mode in ("ranged", "fused"):
+            announce("stress %s: captured step with %s prefetch" % (cfg.name, mode))
+            rn = DecodeRunner(inp, pool, host_buf=hb, prefetch=mode)
+            try:
+                rn.capture()
+                rn.replay()
+                got = rn.results()
+            finally:
+                rn.close()
+            _check_step(cfg, inp, host_kv, want_idx, got, mode)
     finally:
         hb.close()
+
+
+def _check_step(cfg, inp, host_kv, want_idx, got, mode):
+    n_rows = len(inp.key_len)
+    assert got["status"] == 0, mode
+    # the step's top-k is the exact top-k of the scores it computed
+    assert np.array_equal(got["topk_idx"], want_idx), mode
+    assert int(got["counters"][2]) > 0 and int(got["counters"][1]) >= int(got["counters"][2]), mode
+    # every selected token resident, bit for bit; the maps a bijection
+    idx = got["topk_idx"]
+    rows, cols = np.nonzero(idx >= 0)
+    assert len(rows) == n_rows * cfg.topk
+    hosts = inp.req_to_host[inp.key_begin[rows] + idx[rows, cols]]
+    st = oracle.PoolState(*(got["pool"][n] for n in ("free", "priority", "to_host",
+                                                     "host_to_gpu", "indices_buf", "gpu_kv")))
+    oracle.check_pool_invariants(st, host_kv, hosts, got["topk_slot"][rows, cols])
+    # sampled requests against the oracle: scores within 1e-4 T, and the selection differing
+    # from the oracle's only by tokens within that tolerance of its k-th score
+    announce("stress %s (%s): oracle on sampled requests" % (cfg.name, mode))
+    for r in sorted({0, min(n_rows - 1, n_rows // 2 + 5), n_rows - 1}):
+        sl = slice(r, r + 1)
+        args = (inp.q[sl], inp.w[sl], inp.k, inp.k_scale, inp.key_begin[sl], inp.key_len[sl])
+        s, T = oracle.index_scores(*args)[0], oracle.error_scale(*args)[0]
+        g = got["scores"][r, :len(s)].astype(np.float64)
+        assert (np.abs(g - s) <= TOL * T).all(), "request %d scores (%s)" % (r, mode)
+        want = oracle.topk_row(s, cfg.topk)
+        kth = want[np.argmin(s[want])]
+        for t in np.setxor1d(idx[r], want):
+            assert abs(s[t] - s[kth]) <= TOL * (T[t] + T[kth]), "request %d token %d" % (r, t)
