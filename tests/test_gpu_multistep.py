@@ -4,8 +4,9 @@ latent row written through to the pinned host backup, a GPU slot by the canonica
 allocation), then runs the decode step with the EMA estimate of the k-th score
 (echo_decode_select with theta_ema).  Integer-grid inputs: bit-exact scores, selections,
 k-th scores, pool contents, K cache and host rows after every step; the estimate within
-float32 rounding of the exact recursion.  With prefetch against the EMA estimate: the same
-selections and resident rows (lossless), nothing prefetched before the first estimate."""
+float32 rounding of the exact recursion.  With prefetch against the EMA estimate, ranged or
+fused into the scoring launch: the same selections and resident rows (lossless), nothing
+prefetched before the first estimate."""
 
 import numpy as np
 import pytest
@@ -118,14 +119,15 @@ def test_multistep_general_fp8_with_scales():
         rn.close()
 
 
-def test_multistep_prefetch_against_ema_is_lossless():
-    announce("multistep prefetch with EMA threshold")
+@pytest.mark.parametrize("mode", ["ranged", "fused"])
+def test_multistep_prefetch_against_ema_is_lossless(mode):
+    announce("multistep %s prefetch with EMA threshold" % mode)
     B_, L, T, k = 3, 2000, 5, 64
     # free room for prefetch: prefetch never evicts
     m, host_kv = gen.make_multistep_inputs(B_, L, T, 2400, seed=43, reserve=1200)
     cache, st = _oracle_start(m)
     _, _, _, recs = ms.decode_loop(cache, st, host_kv, m.steps, k)
-    rn = LoopRunner(m, host_kv, k, prefetch=True, pf=dict(n_chunks=2, cap=256, cap_div=8))
+    rn = LoopRunner(m, host_kv, k, prefetch=mode, pf=dict(n_chunks=2, cap=256, cap_div=8))
     moved = 0
     try:
         for t, s in enumerate(m.steps):
@@ -147,11 +149,12 @@ def test_multistep_prefetch_against_ema_is_lossless():
         rn.close()
 
 
-def test_multistep_full_pool_prefetch_with_reserve():
+@pytest.mark.parametrize("mode", ["ranged", "fused"])
+def test_multistep_full_pool_prefetch_with_reserve(mode):
     # the pool starts full; each step's guaranteed recall leaves free room for the next
     # step's prefetch: the loop without prefetch equals the oracle's loop with that reserve
     # bit for bit, and with prefetch rows move in steady state while the selections stay
-    announce("multistep full pool, reserve for prefetch")
+    announce("multistep full pool, reserve for %s prefetch" % mode)
     B_, L, T, k, R = 3, 2000, 5, 64, 300
     m, host_kv = gen.make_multistep_inputs(B_, L, T, 900, seed=47, drift=0.05)
     cache, st = _oracle_start(m)
@@ -168,7 +171,7 @@ def test_multistep_full_pool_prefetch_with_reserve():
             assert int(got["pool"]["free"].sum()) >= min(R, 900 - B_ * (k + 1))
     finally:
         plain.close()
-    pf = LoopRunner(m, host_kv, k, prefetch=True, pf=dict(n_chunks=2, cap=256, cap_div=8),
+    pf = LoopRunner(m, host_kv, k, prefetch=mode, pf=dict(n_chunks=2, cap=256, cap_div=8),
                     device_step=True, reserve=R)
     moved = 0
     try:
