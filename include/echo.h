@@ -340,6 +340,12 @@ int echo_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
  * captured into one hipGraph (echo_graph_capture_decode).  Work that overlaps the critical
  * path (the pool's priority histogram, prefetch gathers, reading missed rows from host memory
  * into a staging area of the workspace) rides along as extra workgroups of the same launches.
+ * Prefetch (§6.1): ECHO_PREFETCH_RANGED scores in n_chunks launches, each of which also gathers
+ * the candidates of the range before it (which candidates win the cap depends on timing);
+ * ECHO_PREFETCH_FUSED scores in one launch with a host-gather wave per workgroup, with the
+ * rows and slots of echo_index_scores_fused (§6.3; independent of timing).  Either way the
+ * threshold is theta_ema when given, else the sample percentile, and the selection and the
+ * selected rows are those of the step without prefetch.
  * `side_stream` is reserved and ignored (pass NULL or main_stream).  Workspace:
  * echo_decode_workspace_bytes(a, pool->n_gpu) bytes (it includes n_rows * topk staged rows of
  * ECHO_ROW_ELEMS bf16 values).
