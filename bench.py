@@ -13,11 +13,16 @@ the restore is outside the per-step HIP-event timing (it is inside the wall-cloc
 which is reported separately).
 
 Prints ONE JSON line.  --gpus N > 1 is refused: this path runs on one GPU.
+
+The secondary measurements (prefill indexer, chunked prefill with offload, decode loop, prefetch
+modes) each run in a child process of their own (`--section NAME`), so that a failure in one of
+them is recorded in its place and the headline line is still printed.
 """
 
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -33,8 +38,9 @@ WORKLOADS = {
     "b32_ragged": "decode step: 32 requests x U[16384,131072] tokens, general FP8 q/k with "
                   "per-token scale, top-2048, 70% pool hit rate, host pool 8x GPU pool",
     "b64_128k": "decode step: 64 requests x 131072 tokens, general FP8 q/k with per-token "
-                "scale, top-2048, 50% pool hit rate, threshold prefetch overlapped on a side "
-                "stream, N_G=1048576, N_H=8388608",
+                "scale, top-2048, 50% pool hit rate, threshold prefetch from a 4096-score "
+                "sample (ranged; fused with --prefetch fused), 131072 free slots, "
+                "N_G=1048576, N_H=8388608",
     "tiny": "decode step: 1 request x 4096 tokens, integer grid, top-256, half of all tokens resident",
 }
 
@@ -411,6 +417,58 @@ def cpu_baseline(inp, host_kv, pool_arrays, min_s=10.0, budget_s=30.0):
             "kind": "oracle", "seconds": round(dt, 3), "sample": sample}
 
 
+SECTIONS = ("prefill", "prefill_offload", "loop", "prefetch_modes")
+
+
+def run_section(name, args, timeout_s=900):
+    """One secondary measurement in a child process; its JSON (or the failure) as a dict."""
+    cmd = [sys.executable, os.path.abspath(__file__), "--section", name, "--workload", args.workload]
+    if args.reserve is not None:
+        cmd += ["--reserve", str(args.reserve)]
+    if args.no_cpu_baseline:
+        cmd.append("--no-cpu-baseline")
+    try:
+        p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=None, text=True, timeout=timeout_s)
+    except subprocess.TimeoutExpired:
+        return {"error": "section process timed out after %d s" % timeout_s}
+    lines = [ln for ln in p.stdout.splitlines() if ln.startswith("{")]
+    if p.returncode != 0 or not lines:
+        return {"error": "section process exited with status %d" % p.returncode}
+    return json.loads(lines[-1])
+
+
+def child_section(name, args, torch, B, gen):
+    """--section NAME: the measurement alone, printed as one JSON object."""
+    cpu = not args.no_cpu_baseline
+    if name == "prefill":
+        return prefill_measure(torch, B, gen)
+    if name == "prefill_offload":
+        return prefill_offload_measure(torch, B, gen, cpu=cpu)
+    if name == "loop":
+        return loop_measure(torch, B, gen, cpu=cpu)
+    # prefetch_modes: the workload's own inputs, its resident set drawn around the selection
+    cfg = gen.CONFIGS[args.workload]
+    inp = gen.make_decode_inputs(cfg)
+    hb = B.HostBuffer(inp.n_host * 576 * 2)
+    try:
+        gen.fill_latent_rows(cfg.seed, hb.array.view(np.uint16).reshape(inp.n_host, 576))
+        n_rows, max_len = len(inp.key_len), int(inp.key_len.max())
+        dq, dw, dk = (torch.from_numpy(a).cuda() for a in (inp.q, inp.w, inp.k))
+        dks = None if inp.k_scale is None else torch.from_numpy(inp.k_scale).cuda()
+        dkb, dkl = torch.from_numpy(inp.key_begin).cuda(), torch.from_numpy(inp.key_len).cuda()
+        sc = torch.empty((n_rows, max_len), dtype=torch.float32, device="cuda")
+        sel = torch.empty((n_rows, cfg.topk), dtype=torch.int32, device="cuda")
+        tws = torch.empty(B.topk_workspace_bytes(n_rows, max_len), dtype=torch.uint8, device="cuda")
+        B.index_scores(dq, dw, dk, dks, dkb, dkl, max_len, sc)
+        B.topk(sc, dkl, max_len, cfg.topk, sel, tws)
+        sel_idx = sel.cpu().numpy()
+        del dq, dw, dk, dks, dkb, dkl, sc, sel, tws
+        reserve = args.reserve if args.reserve is not None else max(cfg.reserve, n_rows * cfg.topk)
+        return prefetch_modes_measure(torch, B, gen, inp, hb, sel_idx, reserve)
+    finally:
+        hb.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -425,6 +483,9 @@ def main():
                     help="prefetch of the headline step (on = ranged)")
     ap.add_argument("--no-prefetch-modes", action="store_true",
                     help="skip the off / ranged / fused prefetch comparison")
+    ap.add_argument("--section", choices=SECTIONS, default=None,
+                    help="run one secondary measurement alone and print its JSON (the main run "
+                         "starts each of them this way, in a child process)")
     ap.add_argument("--reserve", type=int, default=None,
                     help="free GPU slots in the starting pool (default: the workload's own)")
     ap.add_argument("--percentile", type=float, default=None,
@@ -440,6 +501,47 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.section is None and args.probe is None:
+        # secondary measurements first, each in a child process and before this process touches
+        # the GPU: a failure in one of them (a Python error, a crash, a time-out) is recorded in
+        # its place, and the headline line is always printed
+        extra = {}
+
+        def section(name, fn, summary):
+            try:
+                extra[name] = fn()
+            except Exception as e:                       # noqa: BLE001
+                extra[name] = {"error": "%s: %s" % (type(e).__name__, e)}
+            if "error" in extra[name]:
+                log("%s failed: %s" % (name, extra[name]["error"]))
+                return
+            try:
+                log(summary(extra[name]))
+            except Exception:                            # noqa: BLE001
+                log("%s done" % name)
+
+        if not args.no_prefill:
+            log("prefill indexer (32768^2) ...")
+            section("prefill", lambda: run_section("prefill", args),
+                    lambda p: "prefill %.1f us = %.0f TFLOP/s (%.1f%% of fp8 peak), top-k rows %.1f us"
+                    % (p["us_per_launch"], p["achieved"], 100 * p["frac"], p["topk_rows_us"]))
+            log("chunked prefill with offload and inter-query prefetch ...")
+            section("prefill_offload", lambda: run_section("prefill_offload", args),
+                    lambda p: "chunked prefill: threshold bin median %d shifted vs %d unshifted"
+                    % (p["thr_bin_median_shifted"], p["thr_bin_median_unshifted"]))
+        if not args.no_loop:
+            log("decode loop (EMA threshold, new tokens every step) ...")
+            section("loop", lambda: run_section("loop", args),
+                    lambda p: "loop: median %.1f us/step, hit rate %.3f"
+                    % (p["us_per_step_median"], p["hit_rate_median"]))
+        if not args.no_prefetch_modes:
+            log("prefetch off / ranged / fused on one starting pool ...")
+            section("prefetch_modes", lambda: run_section("prefetch_modes", args),
+                    lambda p: "prefetch modes: off %.1f, ranged %.1f, fused %.1f us/step; fused "
+                    "launches alone %.1f us vs plain scoring %.1f us" % (
+                        p["off"]["us_per_step"], p["ranged"]["us_per_step"], p["fused"]["us_per_step"],
+                        p["fused_launches_alone"]["us_median"], p["fused_launches_alone"]["plain_scoring_us"]))
+
     import torch
     from dsa_indexer_top_amd import binding as B, inputs as gen
     from dsa_indexer_top_amd.runner import DecodeRunner
@@ -451,6 +553,14 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         log("copy probe: 20 x 256 MiB device copies")
+        return
+    if args.section:
+        try:
+            res = child_section(args.section, args, torch, B, gen)
+            torch.cuda.synchronize()
+        except Exception as e:                       # noqa: BLE001
+            res = {"error": "%s: %s" % (type(e).__name__, e)}
+        print(json.dumps(res), flush=True)
         return
     cfg = gen.CONFIGS[args.workload]
     prefetch = (cfg.prefetch if args.prefetch == "auto" else
@@ -496,8 +606,7 @@ def main():
     tws = torch.empty(B.topk_workspace_bytes(n_rows, max_len), dtype=torch.uint8, device="cuda")
     B.index_scores(dq, dw, dk, dks, dkb, dkl, max_len, sc)
     B.topk(sc, dkl, max_len, cfg.topk, sel, tws)
-    sel_idx = sel.cpu().numpy()
-    pool = gen.make_pool_state(inp, sel_idx, host_kv, reserve=args.reserve)
+    pool = gen.make_pool_state(inp, sel.cpu().numpy(), host_kv, reserve=args.reserve)
     del sc, sel, tws
     pf = None if args.percentile is None else dict(percentile=args.percentile)
     rn = DecodeRunner(inp, pool, host_buf=hb, prefetch=prefetch, pf=pf)
@@ -607,45 +716,12 @@ def main():
                      # pool's priorities are a permutation, so at most one other slot holds 0
                      "prefetched_unselected_approx": int((res["pool"]["priority"] == 0).sum())},
     }
-    # secondary measurements: a Python error in one of them is recorded in its place, so the
-    # headline line above is always printed
-    def section(name, fn, summary):
-        try:
-            out[name] = fn()
-            log(summary(out[name]))
-        except Exception as e:                       # noqa: BLE001
-            out[name] = {"error": "%s: %s" % (type(e).__name__, e)}
-            log("%s failed: %s" % (name, out[name]["error"]))
-            torch.cuda.synchronize()
-
-    if not args.no_prefill:
-        log("prefill indexer (32768^2) ...")
-        section("prefill", lambda: prefill_measure(torch, B, gen),
-                lambda p: "prefill %.1f us = %.0f TFLOP/s (%.1f%% of fp8 peak), top-k rows %.1f us"
-                % (p["us_per_launch"], p["achieved"], 100 * p["frac"], p["topk_rows_us"]))
-        log("chunked prefill with offload and inter-query prefetch ...")
-        section("prefill_offload", lambda: prefill_offload_measure(torch, B, gen,
-                                                                   cpu=not args.no_cpu_baseline),
-                lambda p: "chunked prefill: threshold bin median %d shifted vs %d unshifted"
-                % (p["thr_bin_median_shifted"], p["thr_bin_median_unshifted"]))
-    if not args.no_loop:
-        log("decode loop (EMA threshold, new tokens every step) ...")
-        section("loop", lambda: loop_measure(torch, B, gen, cpu=not args.no_cpu_baseline),
-                lambda p: "loop: median %.1f us/step, hit rate %.3f"
-                % (p["us_per_step_median"], p["hit_rate_median"]))
-    if not args.no_prefetch_modes:
-        log("prefetch off / ranged / fused on one starting pool ...")
-        pf_reserve = args.reserve if args.reserve is not None else max(cfg.reserve, n_rows * cfg.topk)
-        section("prefetch_modes", lambda: prefetch_modes_measure(torch, B, gen, inp, hb, sel_idx,
-                                                                 pf_reserve),
-                lambda p: "prefetch modes: off %.1f, ranged %.1f, fused %.1f us/step; fused "
-                "launches alone %.1f us vs plain scoring %.1f us" % (
-                    p["off"]["us_per_step"], p["ranged"]["us_per_step"], p["fused"]["us_per_step"],
-                    p["fused_launches_alone"]["us_median"], p["fused_launches_alone"]["plain_scoring_us"]))
+    out.update(extra)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         section("cpu_baseline", lambda: cpu_baseline(inp, host_kv, pool),
                 lambda p: "cpu baseline %.3g %s on %d threads" % (p["value"], p["unit"], p["cores"]))
+        out["cpu_baseline"] = extra["cpu_baseline"]
     rn.close()
     hb.close()
     print(json.dumps(out), flush=True)
