@@ -61,23 +61,30 @@ def _run_standalone(inp, st, host_kv, theta, cap, cap_div, rng_len, status=0):
     return host(sc), P.state(), int(host(npf)[0]), int(host(dem)[0]), P
 
 
+def _lens_many(n, seed):
+    return np.random.default_rng(seed).integers(0, 260, n).astype(np.int32).tolist()
+
+
 CASES = [
-    # lens, range, cap, cap_div, free share, threshold quantile, special thresholds
-    ([0, 1, 127, 128, 129, 700, 3000], 128, 2048, 4, 0.5, 0.8, {}),
+    # lens, range, cap, cap_div, free share, threshold quantile, special thresholds, n_gpu
+    ([0, 1, 127, 128, 129, 700, 3000], 128, 2048, 4, 0.5, 0.8, {}, None),
     ([0, 1, 127, 128, 129, 700, 3000], 256, 50, 1, 0.5, 0.6,
-     {1: -np.inf, 4: np.nan, 5: np.inf}),
-    ([5000, 2000, 3], 384, 4096, 1, 0.03, 0.5, {}),            # the free list runs short
-    ([8192 + 130, 64], 8192, 4096, 1, 0.6, 0.0, {0: -np.inf}),  # capped at 128 per range
+     {1: -np.inf, 4: np.nan, 5: np.inf}, None),
+    ([5000, 2000, 3], 384, 4096, 1, 0.03, 0.5, {}, None),            # the free list runs short
+    ([8192 + 130, 64], 8192, 4096, 1, 0.6, 0.0, {0: -np.inf}, None),  # 128 per range at most
+    ([300, 129, 1000], 128, 64, 1, 0.0, 0.5, {}, 1003),               # a full pool: nothing moves
+    (_lens_many(300, 9), 128, 40, 3, 0.7, 0.4, {}, 4096 + 77),        # offsets over 300 requests
 ]
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_fused_prefetch_exact(case):
-    lens, R, cap, cap_div, free_frac, qt, specials = CASES[case]
-    announce("fused prefetch standalone", lens, R, cap, cap_div)
+    lens, R, cap, cap_div, free_frac, qt, specials, n_gpu = CASES[case]
+    announce("fused prefetch standalone", len(lens), "requests", R, cap, cap_div, free_frac)
     cfg = gen.DecodeConfig("fz", len(lens), 0, 64, "int", False, 0.5, 1, seed=300 + case)
     inp = gen.make_decode_inputs(cfg, lengths=lens)
-    st, host_kv = _pool_case(inp, 300 + case, max(256, inp.n_host // 2), free_frac, 0.3)
+    n_gpu = n_gpu or max(256, inp.n_host // 2)
+    st, host_kv = _pool_case(inp, 300 + case, n_gpu, free_frac, 0.3)
     scores = oracle.index_scores(inp.q, inp.w, inp.k, None, inp.key_begin, inp.key_len)
     theta = _thetas(scores, qt, specials)
     want, moved, demand = oracle.range_prefetch(scores, theta, inp.key_begin, inp.key_len,
@@ -88,7 +95,7 @@ def test_fused_prefetch_exact(case):
             assert np.array_equal(got_sc[r, :len(s)].astype(np.float64), s), "scores row %d" % r
         assert npf == len(moved) and dem == int(demand.sum())
         assert_pool_equal(got_st, want, "after the fused prefetch")
-        assert len(moved) > 0
+        assert (len(moved) > 0) == (free_frac > 0) and demand.sum() > 0
     finally:
         P.hostbuf.close()
 
@@ -172,7 +179,8 @@ def _as_state(d):
 
 @pytest.mark.parametrize("given_theta", [True, False])
 @pytest.mark.parametrize("lens,k,R,reserve", [([3000, 700, 1, 0], 64, 256, 300),
-                                              ([5000, 4096], 256, 128, 1500)])
+                                              ([5000, 4096], 256, 128, 1500),
+                                              ([2000, 900], 128, 256, 0)])     # a full pool
 def test_decode_step_fused_exact(lens, k, R, reserve, given_theta):
     # the whole step with the fused prefetch: the threshold given (the EMA estimate) or the
     # sample percentile; selection, slots, miss lists, counters and the pool after the step
@@ -194,7 +202,7 @@ def test_decode_step_fused_exact(lens, k, R, reserve, given_theta):
     _, want_idx, mid, moved, demand, want_state, res = oracle.decode_step_prefetched(
         inp.q, inp.w, inp.k, None, inp.key_begin, inp.key_len, inp.req_to_host, st0, host_kv, k,
         pool.step_id, theta, cap, cap_div, R, reserve=reserve)
-    assert len(moved) > 0 and res.status == 0
+    assert (len(moved) > 0) == (reserve > 0) and res.status == 0
     pf = dict(cap=cap, cap_div=cap_div, range=R)
     rn = DecodeRunner(inp, pool, host_kv, prefetch="fused", pf=pf, reserve=reserve,
                       theta=theta if given_theta else None)
