@@ -36,7 +36,8 @@ from .decode import decode_step
 from .multistep import (KeyCache, ST_CACHE_FULL, append_tokens, kth_scores, ema_update,
                         decode_loop)
 from .interquery import approx_subset, union_segments, prefill_chunk_loop
-from .prefetch import request_cap, range_share, range_prefetch, decode_step_prefetched
+from .prefetch import (request_caps, prefetch_candidates, range_prefetch,
+                       check_prefetch_outcome, decode_step_prefetched)
 
 __all__ = [
     "E4M3FN_TABLE", "decode_e4m3fn", "index_scores", "error_scale",
@@ -45,6 +46,6 @@ __all__ = [
     "PoolState", "pool_step", "allocate_with_ranks", "metadata_bytes",
     "check_pool_invariants", "PoolInvariantError", "decode_step", "KeyCache",
     "ST_CACHE_FULL", "append_tokens", "kth_scores", "ema_update", "decode_loop",
-    "approx_subset", "union_segments", "prefill_chunk_loop", "request_cap",
-    "range_share", "range_prefetch", "decode_step_prefetched",
+    "approx_subset", "union_segments", "prefill_chunk_loop", "request_caps",
+    "prefetch_candidates", "range_prefetch", "check_prefetch_outcome", "decode_step_prefetched",
 ]

@@ -10,24 +10,27 @@ ECHO page §6.3: the indexer kernel does this in a single launch; each part of t
 scored, tested against the threshold, and the passing tokens reach a copy stage through a
 bounded queue.
 
-Readings (the page fixes none of these; they are the plainest ones that make the result a
-function of the inputs alone):
+Readings (the page fixes these only in part):
 
 * Ranges.  Request r's tokens [0, L_r) are cut into ranges of R tokens, x = 0, 1, ...
-  (one workgroup each on the GPU).  n_ranges_r = ceil(L_r / R).
-* Cap.  Request r may move cap_r = min(cap, ceil(L_r / cap_div)) rows (the page's bound in
-  proportion to the context), at most max_per_range (128) per range:
-  c_r = min(cap_r, 128 * n_ranges_r).  Its ranges split c_r evenly: range x moves at most
-  m_x = floor((x + 1) c_r / n_ranges_r) - floor(x c_r / n_ranges_r) rows (the shares differ by
-  at most one and add up to c_r; a range's share is 0 when c_r < n_ranges_r).
-* Qualifying tokens.  s in the range, ascending, with float32 score > float32 theta_r (strict;
-  a NaN threshold passes nothing), whose host index h = req_to_host[key_begin_r + s] lies in
-  [0, N_H) and is not resident (HostTokenToGPU[h] = INF) before the prefetch.  The first
-  m_x qualifying tokens of each range move; demand_r counts all qualifying tokens.
-* Slots.  The pool's free slots before the prefetch, ascending, form a list F.  Request r owns
-  c_r entries from O_r = sum over r' < r of c_r'; its range x owns the m_x entries from
-  O_r + floor(x c_r / n_ranges_r), and its i-th moved token takes entry i of those if the list
-  is that long (otherwise it does not move).
+  (one workgroup each on the GPU).
+* Qualifying tokens.  s, with float32 score > float32 theta_r (strict; a NaN threshold passes
+  nothing), whose host index h = req_to_host[key_begin_r + s] lies in [0, N_H) and is not
+  resident (HostTokenToGPU[h] = INF) before the prefetch.  demand_r counts them.  A range asks
+  for places for its first 128 qualifying tokens in token order (its candidates).
+* Cap.  Request r may move c_r = min(cap, ceil(L_r / cap_div), N_G) rows (the page's bound in
+  proportion to the context).  When the caps of all requests add up to C > F, the number of
+  free slots, each becomes floor(c_r * F / C), so that every request keeps a share of the free
+  slots.
+* Places.  The free slots before the prefetch, ascending, form a list.  Request r owns the c_r
+  entries from O_r = sum over r' < r of c_r'.  Its ranges claim them first come, first served
+  (the page's prefetch counter, one per request): a claim takes the next free places of the
+  request, in the token order of the claiming range.  So when a request's candidates fit its
+  cap, every one of them moves, and otherwise exactly c_r do, each range's moved tokens being a
+  token-order prefix of its candidates; the places taken are always the request's first
+  entries; which candidate gets which of them depends on timing.  `range_prefetch` returns the
+  canonical outcome (candidates in request, then token order, take the places in order) with
+  what defines the set of valid outcomes.
 * A moved token: Free = 0, ToHost = h, HostToGPU[h] = slot, priority 0 (below every step
   stamp, so it goes first when space is short and it was not selected), and its row is copied
   from the host backup bit for bit.  Nothing is evicted.
@@ -47,71 +50,127 @@ from .topk import topk_rows
 from .pool import pool_step
 
 
-def request_cap(L, cap, cap_div, range_len, max_per_range=128):
-    """c_r: rows a request of L tokens may move over all its ranges (module notes: Cap)."""
-    if L <= 0:
-        return 0
-    n_ranges = -(-L // range_len)
-    return min(cap, -(-L // cap_div), max_per_range * n_ranges)
+def request_caps(key_len, cap, cap_div, n_free, n_gpu):
+    """(c_r before scaling, c_r after scaling) per request (module notes: Cap)."""
+    c = [0 if L <= 0 else min(cap, -(-int(L) // cap_div), n_gpu) for L in key_len]
+    total = sum(c)
+    if total > n_free:
+        return c, [ci * n_free // total for ci in c]
+    return c, list(c)
 
 
-def range_share(c, n_ranges, x):
-    """(first entry, count) of range x's share of a request's c rows (module notes)."""
-    first = x * c // n_ranges
-    return first, (x + 1) * c // n_ranges - first
+def prefetch_candidates(scores, theta, key_begin, key_len, req_to_host, state, range_len,
+                        per_range=128):
+    """Per request: the qualifying tokens (all of them) and each range's candidates (its first
+    per_range qualifying tokens), as {range: [(token, host index), ...]}, token order."""
+    theta32 = np.asarray(theta, np.float32)
+    qual, cand = [], []
+    for r in range(len(key_len)):
+        L = max(int(key_len[r]), 0)
+        s32 = np.asarray(scores[r][:L], np.float64).astype(np.float32)
+        q, c = [], {}
+        for s in range(L):
+            if not s32[s] > theta32[r]:
+                continue
+            h = int(req_to_host[int(key_begin[r]) + s])
+            if h < 0 or h >= state.n_host or state.host_to_gpu[h] != INF:
+                continue
+            q.append((s, h))
+            lst = c.setdefault(s // range_len, [])
+            if len(lst) < per_range:
+                lst.append((s, h))
+        qual.append(q)
+        cand.append(c)
+    return qual, cand
 
 
 def range_prefetch(scores, theta, key_begin, key_len, req_to_host, state, host_kv, cap, cap_div,
-                   range_len, max_per_range=128):
-    """Moves rows ahead of the top-k as described in the module notes.
+                   range_len, per_range=128):
+    """The canonical outcome of the prefetch (module notes) and what defines the valid ones.
 
     scores: per request, the scores of tokens [0, L_r) (float64, cast to float32 for the test);
     theta: per request threshold (cast to float32).  state is not modified.
-    Returns (new_state, moved, demand): moved lists (request, token, host index, slot) in the
-    order the slots were taken; demand[r] counts the qualifying tokens of request r."""
-    n = len(key_len)
-    theta32 = np.asarray(theta, np.float32)
+    Returns (new_state, moved, demand, info): moved lists (request, token, host index, slot) in
+    the canonical order; demand[r] counts the qualifying tokens of request r; info holds
+    'free_list', 'cap' (scaled c_r), 'offset' (O_r) and 'cand' (per request, range -> the
+    range's candidates)."""
     free_list = np.flatnonzero(state.free == 1)
+    qual, cand = prefetch_candidates(scores, theta, key_begin, key_len, req_to_host, state,
+                                     range_len, per_range)
+    _, caps = request_caps(key_len, cap, cap_div, len(free_list), state.n_gpu)
+    offsets = np.concatenate([[0], np.cumsum(caps)[:-1]]).astype(np.int64) if len(caps) else []
     new = state.copy()
-    moved, demand = [], np.zeros(n, np.int64)
-    offset = 0
-    for r in range(n):
-        L = max(int(key_len[r]), 0)
-        c = request_cap(L, cap, cap_div, range_len, max_per_range)
-        n_ranges = -(-L // range_len) if L > 0 else 0
-        s32 = np.asarray(scores[r][:L], np.float64).astype(np.float32)
-        for x in range(n_ranges):
-            first, share = range_share(c, n_ranges, x)
-            taken = 0
-            for s in range(x * range_len, min(L, (x + 1) * range_len)):
-                if not s32[s] > theta32[r]:
-                    continue
-                h = int(req_to_host[int(key_begin[r]) + s])
-                if h < 0 or h >= state.n_host or state.host_to_gpu[h] != INF:
-                    continue
-                demand[r] += 1
-                entry = offset + first + taken
-                if taken < share and entry < len(free_list):
-                    slot = int(free_list[entry])
-                    new.free[slot] = 0
-                    new.to_host[slot] = h
-                    new.host_to_gpu[h] = slot
-                    new.priority[slot] = 0
-                    new.gpu_kv[slot] = host_kv[h]
-                    moved.append((r, s, h, slot))
-                    taken += 1
-        offset += c
-    return new, moved, demand
+    moved = []
+    for r in range(len(key_len)):
+        flat = [t for x in sorted(cand[r]) for t in cand[r][x]]
+        for i, (s, h) in enumerate(flat[:caps[r]]):
+            slot = int(free_list[offsets[r] + i])
+            new.free[slot] = 0
+            new.to_host[slot] = h
+            new.host_to_gpu[h] = slot
+            new.priority[slot] = 0
+            new.gpu_kv[slot] = host_kv[h]
+            moved.append((r, s, h, slot))
+    demand = np.array([len(q) for q in qual], np.int64)
+    info = dict(free_list=free_list, cap=caps, offset=offsets, cand=cand)
+    return new, moved, demand, info
+
+
+def check_prefetch_outcome(before, after, host_kv, key_begin, req_to_host, info, demand_got=None,
+                           demand=None):
+    """Raises AssertionError unless `after` is a valid outcome of the prefetch from `before`
+    (module notes: Places): per request, min(#candidates, c_r) rows moved, each range's a
+    token-order prefix of its candidates with ascending slots, into exactly the request's first
+    places; maps, priority 0 and rows set; nothing else changed."""
+    new_slots = np.flatnonzero((before.free == 1) & (after.free == 0))
+    assert not np.flatnonzero((before.free == 0) & (after.free == 1)).size, "a slot was freed"
+    where = {}
+    for r, c in enumerate(info["cand"]):
+        for x, lst in c.items():
+            for s, h in lst:
+                where[h] = (r, x, s)
+    got = {}
+    for sl in new_slots:
+        h = int(after.to_host[sl])
+        assert h in where, "slot %d holds a host index that is no candidate" % sl
+        assert after.host_to_gpu[h] == sl and after.priority[sl] == 0, "maps of slot %d" % sl
+        assert np.array_equal(after.gpu_kv[sl], host_kv[h]), "row of slot %d" % sl
+        r, x, s = where[h]
+        got.setdefault(r, {}).setdefault(x, []).append((s, int(sl)))
+    fl = info["free_list"]
+    for r, c in enumerate(info["cand"]):
+        n_cand = sum(len(v) for v in c.values())
+        rows = got.get(r, {})
+        n_moved = sum(len(v) for v in rows.values())
+        assert n_moved == min(n_cand, info["cap"][r]), "request %d moved %d" % (r, n_moved)
+        slots = sorted(sl for v in rows.values() for _, sl in v)
+        o = int(info["offset"][r]) if n_moved else 0
+        assert slots == sorted(int(v) for v in fl[o:o + n_moved]), "request %d places" % r
+        for x, v in rows.items():
+            v.sort()
+            assert [s for s, _ in v] == [s for s, _ in c[x][:len(v)]], "range %d/%d prefix" % (r, x)
+            assert [sl for _, sl in v] == sorted(sl for _, sl in v), "range %d/%d slot order" % (r, x)
+    keep = np.ones(before.n_gpu, bool)
+    keep[new_slots] = False
+    for name in ("free", "priority", "to_host", "indices_buf"):
+        assert np.array_equal(getattr(after, name)[keep], getattr(before, name)[keep]), name
+    assert np.array_equal(after.gpu_kv[keep], before.gpu_kv[keep]), "gpu_kv outside the new slots"
+    moved_h = after.to_host[new_slots]
+    hk = np.ones(before.n_host, bool)
+    hk[moved_h] = False
+    assert np.array_equal(after.host_to_gpu[hk], before.host_to_gpu[hk]), "host_to_gpu"
+    if demand is not None:
+        assert np.array_equal(np.asarray(demand_got), np.asarray(demand)), "demand"
 
 
 def decode_step_prefetched(q, w, k, k_scale, key_begin, key_len, req_to_host, state, host_kv,
                            topk_k, step_id, theta, cap, cap_div, range_len, reserve=0):
     """A whole decode step with the range prefetch ahead of the exact top-k and the guaranteed
-    recall (§4 with §6.1 / §6.3).  Returns (scores, idx, state after the prefetch, moved,
-    demand, final state, PoolStepResult)."""
+    recall (§4 with §6.1 / §6.3), with the canonical prefetch outcome.  Returns (scores, idx,
+    state after the prefetch, moved, demand, info, final state, PoolStepResult)."""
     scores = index_scores(q, w, k, k_scale, key_begin, key_len)
-    mid, moved, demand = range_prefetch(scores, theta, key_begin, key_len, req_to_host, state,
-                                        host_kv, cap, cap_div, range_len)
+    mid, moved, demand, info = range_prefetch(scores, theta, key_begin, key_len, req_to_host,
+                                              state, host_kv, cap, cap_div, range_len)
     idx = topk_rows(scores, topk_k)
     final, res = pool_step(mid, host_kv, idx, key_begin, req_to_host, step_id, reserve=reserve)
-    return scores, idx, mid, moved, demand, final, res
+    return scores, idx, mid, moved, demand, info, final, res

@@ -1,10 +1,11 @@
 """Pins of the oracle's range prefetch (oracle/prefetch.py) against what the ECHO page and the
 mathematics fix: a worked example derived by hand (tests/golden/range_prefetch_example.txt),
-the thresholds that reduce to closed forms (+inf and NaN move nothing; -inf with room to spare
-moves every non-resident token), the structure of what moves (a token-order prefix of each
-range's qualifying tokens, into distinct slots that were free), the pool invariants, and the
-page's losslessness (§6.1): a whole step with the prefetch selects the same tokens and ends
-with the same selected rows resident as a step without it."""
+the caps scaled to the free slots by hand, the thresholds that reduce to closed forms (+inf
+and NaN move nothing; -inf with room to spare moves every non-resident token), the structure of
+what moves, the outcome checker accepting the canonical outcome and other valid ones and
+rejecting planted mistakes, the pool invariants, and the page's losslessness (§6.1): a whole
+step with the prefetch selects the same tokens and ends with the same selected rows resident
+as a step without it."""
 
 import os
 
@@ -45,6 +46,7 @@ def _load_example():
               theta=np.array([float(v) for v in f["theta"].split()], np.float32),
               cap=int(f["cap"]), cap_div=int(f["cap_div"]), range=int(f["range"]),
               moved=[tuple(int(v) for v in m.split(",")) for m in f["moved"].split()],
+              caps=[int(v) for v in f["caps"].split()], offsets=[int(v) for v in f["offsets"].split()],
               demand=np.array(f["demand"].split(), np.int64),
               free_after=np.array(f["free_after"].split(), np.uint8))
     return ex
@@ -58,10 +60,11 @@ def test_worked_example():
     ex = _load_example()
     st = ex["state"]
     host_kv = _host_rows(st.n_host)
-    new, moved, demand = oracle.range_prefetch(ex["scores"], ex["theta"], ex["key_begin"],
-                                               ex["key_len"], ex["req_to_host"], st, host_kv,
-                                               ex["cap"], ex["cap_div"], ex["range"])
+    new, moved, demand, info = oracle.range_prefetch(ex["scores"], ex["theta"], ex["key_begin"],
+                                                     ex["key_len"], ex["req_to_host"], st, host_kv,
+                                                     ex["cap"], ex["cap_div"], ex["range"])
     assert moved == ex["moved"]
+    assert list(info["cap"]) == ex["caps"] and list(info["offset"]) == ex["offsets"]
     assert np.array_equal(demand, ex["demand"])
     assert np.array_equal(new.free, ex["free_after"])
     for r, s, h, slot in moved:
@@ -71,24 +74,48 @@ def test_worked_example():
     assert new.to_host[0] == 2 and new.to_host[3] == 9 and new.priority[3] == 7
     assert st.free.sum() == 12
     oracle.check_pool_invariants(new, host_kv)
+    oracle.check_prefetch_outcome(st, new, host_kv, ex["key_begin"], ex["req_to_host"], info)
+    # another valid outcome: r0's range 1 stops after s2 and range 2 moves s4; places permuted
+    # between ranges
+    alt = _apply(st, host_kv, [(4, 1), (7, 4), (11, 2), (3, 6), (8, 5), (13, 12), (14, 10),
+                               (16, 11)])
+    oracle.check_prefetch_outcome(st, alt, host_kv, ex["key_begin"], ex["req_to_host"], info)
+    canon = [(4, 1), (7, 2), (0, 4), (3, 5), (8, 6), (13, 10), (14, 11), (16, 12)]
+    planted = {
+        "not a prefix of range 1": [(4, 1), (0, 2), (11, 4)] + canon[3:],
+        "range 1's slots out of token order": [(4, 1), (7, 4), (0, 2)] + canon[3:],
+        "a place that is not among r1's first": canon[:3] + [(3, 5), (8, 7)] + canon[5:],
+        "r3 moved too few": canon[:6],
+        "a candidate of r3 moved twice": canon + [(13, 13)],
+    }
+    for what, moves in planted.items():
+        b = _apply(st, host_kv, moves)
+        with pytest.raises(AssertionError):
+            oracle.check_prefetch_outcome(st, b, host_kv, ex["key_begin"], ex["req_to_host"], info)
+            raise RuntimeError("not caught: " + what)
+    b = _apply(st, host_kv, canon)
+    b.gpu_kv[10, 0] ^= 1
+    with pytest.raises(AssertionError):
+        oracle.check_prefetch_outcome(st, b, host_kv, ex["key_begin"], ex["req_to_host"], info)
 
 
-def test_request_cap_and_shares():
-    assert pfo.request_cap(0, 10, 1, 128) == 0
-    assert pfo.request_cap(65536, 2048, 64, 512) == 1024        # ceil(65536 / 64)
-    assert pfo.request_cap(131072, 2048, 64, 8192) == 2048      # the cap
-    assert pfo.request_cap(1000, 10 ** 6, 1, 8192) == 128       # 128 in its one range
-    assert pfo.request_cap(1, 5, 1000, 128) == 1                # ceil(1 / 1000) = 1
-    # shares: consecutive, differing by at most one, adding up to c, for any c and n
-    for c in (0, 1, 3, 7, 64, 127, 128, 1000):
-        for n in (1, 2, 3, 4, 7, 128):
-            if c > 128 * n:
-                continue
-            sh = [pfo.range_share(c, n, x) for x in range(n)]
-            assert sum(m for _, m in sh) == c
-            assert all(sh[x][0] + sh[x][1] == sh[x + 1][0] for x in range(n - 1))
-            assert max(m for _, m in sh) - min(m for _, m in sh) <= 1
-            assert max(m for _, m in sh) <= 128
+def _apply(st, host_kv, moves):
+    """st with host rows h placed in slots (h, slot)."""
+    b = st.copy()
+    for h, slot in moves:
+        b.free[slot], b.to_host[slot], b.host_to_gpu[h], b.priority[slot] = 0, h, slot, 0
+        b.gpu_kv[slot] = host_kv[h]
+    return b
+
+
+def test_caps_scaled_to_the_free_slots():
+    # c_r = min(cap, ceil(L / cap_div), n_gpu); scaled by F / C when they add up to C > F
+    assert oracle.request_caps([5, 3, 0, 8], 3, 1, 12, 14) == ([3, 3, 0, 3], [3, 3, 0, 3])
+    assert oracle.request_caps([5, 3, 0, 8], 3, 1, 5, 14) == ([3, 3, 0, 3], [1, 1, 0, 1])
+    assert oracle.request_caps([65536] * 8, 2048, 64, 16384, 65536)[1] == [1024] * 8
+    assert oracle.request_caps([65536] * 8, 2048, 64, 4000, 65536)[1] == [500] * 8
+    assert oracle.request_caps([10 ** 6], 10 ** 7, 1, 10 ** 6, 2048)[0] == [2048]   # at most N_G
+    assert oracle.request_caps([1], 5, 1000, 10, 10)[0] == [1]                       # ceil(1/1000)
 
 
 def _random_case(seed, n_rows=5, n_gpu=400, resident=0.3, free=0.5):
@@ -120,42 +147,32 @@ def _random_case(seed, n_rows=5, n_gpu=400, resident=0.3, free=0.5):
 def test_structure_of_what_moves(seed):
     st, kb, lens, r2h, scores, theta, host_kv = _random_case(seed)
     cap, cap_div, R = 40, 7, 64
-    new, moved, demand = oracle.range_prefetch(scores, theta, kb, lens, r2h, st, host_kv, cap,
-                                               cap_div, R)
+    new, moved, demand, info = oracle.range_prefetch(scores, theta, kb, lens, r2h, st, host_kv,
+                                                     cap, cap_div, R, per_range=5)
     oracle.check_pool_invariants(new, host_kv)
-    free_before = set(np.flatnonzero(st.free == 1).tolist())
-    slots = [m[3] for m in moved]
-    assert len(set(slots)) == len(slots) and set(slots) <= free_before
-    # the free slots are taken in ascending order along (request, range, rank)
-    assert slots == sorted(slots)
-    by_range = {}
-    for r, s, h, slot in moved:
-        by_range.setdefault((r, s // R), []).append(s)
+    oracle.check_prefetch_outcome(st, new, host_kv, kb, r2h, info)
+    free_before = np.flatnonzero(st.free == 1)
+    assert sum(info["cap"]) <= len(free_before)
     for r in range(len(lens)):
         L = int(lens[r])
-        qual_all = [s for s in range(L) if np.float32(scores[r][s]) > theta[r]
-                    and st.host_to_gpu[r2h[kb[r] + s]] == oracle.INF]
-        assert demand[r] == len(qual_all)
-        c = pfo.request_cap(L, cap, cap_div, R)
-        n_rng = -(-L // R)
-        assert sum(len(v) for (rr, _), v in by_range.items() if rr == r) <= c
-        for x in range(n_rng):
-            qual = [s for s in qual_all if s // R == x]
-            got = by_range.get((r, x), [])
-            # a prefix of the range's qualifying tokens in token order, within its share
-            assert got == qual[: len(got)] and len(got) <= pfo.range_share(c, n_rng, x)[1]
-    # nothing resident before changed
-    occ = np.flatnonzero(st.free == 0)
-    assert np.array_equal(new.to_host[occ], st.to_host[occ])
-    assert np.array_equal(new.priority[occ], st.priority[occ])
+        qual = [s for s in range(L) if np.float32(scores[r][s]) > theta[r]
+                and st.host_to_gpu[r2h[kb[r] + s]] == oracle.INF]
+        assert demand[r] == len(qual)
+        # candidates: each range's first 5 qualifying tokens
+        for x in range(-(-L // R)):
+            qx = [s for s in qual if s // R == x][:5]
+            assert [s for s, _ in info["cand"][r].get(x, [])] == qx
+        mr = [m for m in moved if m[0] == r]
+        n_cand = sum(len(v) for v in info["cand"][r].values())
+        assert len(mr) == min(n_cand, info["cap"][r])
 
 
 def test_infinite_and_nan_thresholds_move_nothing():
     st, kb, lens, r2h, scores, _, host_kv = _random_case(11)
     for t in (np.inf, np.nan):
         theta = np.full(len(lens), t, np.float32)
-        new, moved, demand = oracle.range_prefetch(scores, theta, kb, lens, r2h, st, host_kv,
-                                                   10 ** 6, 1, 128)
+        new, moved, demand, _ = oracle.range_prefetch(scores, theta, kb, lens, r2h, st, host_kv,
+                                                      10 ** 6, 1, 128)
         assert moved == [] and demand.sum() == 0
         for a, b in zip((new.free, new.priority, new.to_host, new.host_to_gpu, new.gpu_kv),
                         (st.free, st.priority, st.to_host, st.host_to_gpu, st.gpu_kv)):
@@ -163,13 +180,13 @@ def test_infinite_and_nan_thresholds_move_nothing():
 
 
 def test_minus_infinity_with_room_moves_every_non_resident_token():
-    # one range per request (R >= L <= 128) and caps above L: every token that is not resident
-    # moves, and afterwards every token of every request is resident with its row
+    # caps above L and room to spare: every token that is not resident moves, and afterwards
+    # every token of every request is resident with its row
     st, kb, lens, r2h, scores, _, host_kv = _random_case(12, n_gpu=2000, free=0.8)
     lens = np.minimum(lens, 128).astype(np.int32)
     theta = np.full(len(lens), -np.inf, np.float32)
-    new, moved, demand = oracle.range_prefetch(scores, theta, kb, lens, r2h, st, host_kv,
-                                               10 ** 6, 1, 128)
+    new, moved, demand, _ = oracle.range_prefetch(scores, theta, kb, lens, r2h, st, host_kv,
+                                                  10 ** 6, 1, 128)
     hosts = np.concatenate([r2h[kb[r]: kb[r] + lens[r]] for r in range(len(lens))]).astype(np.int64)
     non_res = int((st.host_to_gpu[hosts] == oracle.INF).sum())
     assert len(moved) == non_res == demand.sum()
@@ -191,7 +208,7 @@ def test_whole_step_is_lossless(seed):
     _, idx0, final0, res0 = oracle.decode_step(inp.q, inp.w, inp.k, None, inp.key_begin,
                                                inp.key_len, inp.req_to_host, st, host_kv, 32,
                                                pool.step_id)
-    _, idx1, mid, moved, demand, final1, res1 = oracle.decode_step_prefetched(
+    _, idx1, mid, moved, demand, _, final1, res1 = oracle.decode_step_prefetched(
         inp.q, inp.w, inp.k, None, inp.key_begin, inp.key_len, inp.req_to_host, st, host_kv, 32,
         pool.step_id, theta, 64, 4, 128)
     assert len(moved) > 0
