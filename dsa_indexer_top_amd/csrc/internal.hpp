@@ -184,10 +184,12 @@ int launch_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
 struct FusedWs {
   int32_t *chunk_free;   // [ceil(n_gpu / 4096)] free slots per chunk
   int32_t *free_list;    // [n_gpu] ascending
-  int32_t *slice_off;    // [n_q] first free_list entry of each request's slices
+  int32_t *slice_off;    // [n_q] first free_list entry of each request's places
   int32_t *counts;       // [2]: 0 length of free_list
   int32_t *demand;       // [n_q] tokens above the threshold and not resident
   int32_t *taken;        // [n_q] rows prefetched
+  int32_t *cap_eff;      // [n_q] places of each request (its cap, scaled to the free slots)
+  int32_t *claimed;      // [n_q] places claimed so far
 };
 size_t fused_ws_layout(int32_t n_q, int32_t n_gpu, void *base, FusedWs *w);
 // Tokens per range (one workgroup each): pf_range when nonzero, else enough workgroups to put

@@ -12,28 +12,29 @@
 //                  chunk's LDS queue.
 //   gather wave    A software pipeline with one step per chunk period: look the queued tokens
 //                  of the previous chunk up in req_to_host; a period later look their host
-//                  indices up in HostTokenToGPU; a period later give each non-resident one the
-//                  next slot of the range's free-slot slice (up to the range's cap), set both
-//                  maps and priority 0, and queue the row.  Every period it starts reading one
-//                  queued row from mapped host memory and stores the row it started the period
-//                  before.
+//                  indices up in HostTokenToGPU; a period later claim places for the
+//                  non-resident ones from the request's counter; a period later read the
+//                  claimed places' slots from the free-slot list; a period later set both maps
+//                  and priority 0 and queue the rows.  Every period it starts reading one queued
+//                  row from mapped host memory and stores the row it started the period before.
 // The gather wave meets the scoring waves only at the chunk barriers.  A gfx950 workgroup
 // barrier waits for LDS traffic only, so its host reads stay in flight across barriers: the
 // scoring waves wait for the host link only when a read is still outstanding a whole chunk
 // period after it was issued.  After the last chunk the gather wave drains its pipeline alone;
 // no wave ever waits for another outside the barriers.
 //
-// The cap.  Request r may prefetch cap_r = min(cap, ceil(L_r / cap_div)) rows, the page's bound
-// in proportion to the context, at most 128 per token range: c_r = min(cap_r, 128 n_r) over its
-// n_r ranges (one workgroup each).  The ranges split c_r evenly: range x may move
-// floor((x+1) c_r / n_r) - floor(x c_r / n_r) rows, the first qualifying tokens of the range in
-// token order, and owns the entries from floor(x c_r / n_r) on of the request's c_r entries of
-// the ascending free-slot list (request r's entries follow those of requests < r).  No counter
-// is shared between workgroups, so which rows move, and to which slots, depends on the inputs
-// alone.
+// The cap.  Request r may prefetch c_r = min(cap, ceil(L_r / cap_div)) rows, the page's bound
+// in proportion to the context, scaled down in proportion when the requests' caps add up to more
+// than the free slots.  Request r owns c_r consecutive entries of the ascending free-slot list
+// (after those of requests < r); its ranges claim places among them first come, first served,
+// through one counter per request, as the page's prefetch counter does.  At most 128 rows per
+// range (its candidates: the first 128 qualifying tokens).  When a request's candidates fit its
+// cap, every one of them moves, so what moves depends on the inputs alone; which of the
+// request's slots each one gets depends on timing.
 //
 // Launches: free slots per 4096-slot chunk (with the pool-step statistics in the decode step)
-// -> ascending free-slot list, slice offsets -> the fused kernel -> per-step totals.
+// -> ascending free-slot list, every request's places and their offset -> the fused kernel ->
+// per-step totals.
 #include "internal.hpp"
 #include "pool_common.cuh"
 #include "score_tile.cuh"
@@ -47,23 +48,17 @@ constexpr int FZ_CHUNK = 128;                           // tokens per LDS stage
 constexpr int FZ_LOADS = FZ_CHUNK * D / 16 / FZ_ST;     // 16-byte loads per scoring thread = 4
 constexpr int FZ_MAXW = ECHO_FUSED_MAX_PER_RANGE;       // rows per range at most (128)
 constexpr int FZ_UNITS = ROW * 2 / 16;                  // 16-byte units per latent row = 72
-static_assert(FZ_MAXW <= 128, "the gather wave holds two slice entries per lane");
+static_assert(FZ_CHUNK <= 128, "a chunk's queue is two entries per lane of the gather wave");
 static_assert(FZ_UNITS <= 128, "a row is two 16-byte units per lane of the gather wave");
 
 ECHO_DEV int fz_swz(int tok, int seg) { return tok * 128 + ((seg ^ ((tok >> 1) & 7)) << 4); }
 
-// Rows request r may prefetch over all its ranges, c_r (above); <= 128 * 32768.
-ECHO_DEV int32_t fz_request_cap(int32_t L, int32_t cap, int32_t cap_div, int32_t range) {
+// Request r's cap before scaling, c_r (above), at most n_gpu.
+ECHO_DEV int32_t fz_request_cap(int32_t L, int32_t cap, int32_t cap_div, int32_t n_gpu) {
   if (L <= 0) return 0;
   int64_t c = (static_cast<int64_t>(L) + cap_div - 1) / cap_div;
   if (c > cap) c = cap;
-  const int64_t most = static_cast<int64_t>(FZ_MAXW) * ((L + range - 1) / range);
-  return static_cast<int32_t>(c < most ? c : most);
-}
-// Range x's share of c_r: its first entry and its count (<= 128).
-ECHO_DEV void fz_range_share(int32_t c, int32_t n_rng, int32_t x, int32_t &first, int32_t &count) {
-  first = static_cast<int32_t>(static_cast<int64_t>(x) * c / n_rng);
-  count = static_cast<int32_t>(static_cast<int64_t>(x + 1) * c / n_rng) - first;
+  return static_cast<int32_t>(c < n_gpu ? c : n_gpu);
 }
 
 struct FusedArgs {
@@ -77,16 +72,22 @@ struct FusedArgs {
   int32_t n_gpu, n_host;
   const int32_t *free_list;    // ascending free slots
   const int32_t *counts;       // [0]: length of free_list
-  const int32_t *slice_off;    // [n_q] first free_list entry of request r's slices
+  const int32_t *slice_off;    // [n_q] first free_list entry of request r's places
+  const int32_t *cap_eff;      // [n_q] request r's places (its cap, scaled to the free slots)
+  int32_t *claimed;            // [n_q] places claimed so far (zeroed by the list launch)
   int32_t *demand;             // [n_q] qualifying tokens (zeroed by the list launch)
   int32_t *taken;              // [n_q] rows prefetched (zeroed by the list launch)
-  int32_t cap, cap_div, range;
+  int32_t range;
 };
 
 // Pipeline state of the gather wave.  Each lane carries entries e = lane and lane + 64 of a
 // chunk's queue.
 struct FzA { int32_t tok[2], h[2]; };      // token (-1: none), its host index (in flight)
 struct FzB { int32_t h[2], g[2]; };        // host index (-1: none), its slot or INF (in flight)
+struct FzC { int32_t h[2], rank[2], base, want; };   // claim: rank among the claimed (-1: none),
+                                                     // the counter's old value (lane 0, in flight)
+struct FzD { int32_t h[2], slot[2], pos[2], take; }; // slot of the claimed place (in flight), its
+                                                     // position in the row queue
 template <int P> struct FzParity { static constexpr int value = P; };
 
 template <bool HAS_SCALE, bool HIST>
@@ -99,7 +100,6 @@ __global__ __launch_bounds__(FZ_THREADS) void score_fused_kernel(
   __shared__ uint32_t hl[HIST ? 1024 : 1];          // 2048 bins, two 16-bit counters per word
   __shared__ uint8_t qtok[2][FZ_CHUNK];             // queue: token offsets in the chunk, 32 per wave
   __shared__ uint32_t qn[2][FZ_SW];                 // queue length per scoring wave
-  __shared__ int32_t slice[FZ_MAXW];                // this range's free slots
   __shared__ int32_t ring_h[FZ_MAXW], ring_s[FZ_MAXW];   // rows to copy: host index, slot
 
   const int b = blockIdx.x;
@@ -183,37 +183,76 @@ __global__ __launch_bounds__(FZ_THREADS) void score_fused_kernel(
 
   // -------------------------------------------------------------- gather wave
   typedef int v4i __attribute__((ext_vector_type(4)));
-  int32_t first, capw;
-  fz_range_share(fz_request_cap(L, F.cap, F.cap_div, F.range), (L + F.range - 1) / F.range, x, first,
-                 capw);
-  const int64_t sbase = static_cast<int64_t>(F.slice_off[r]) + first;
-  int64_t avail = static_cast<int64_t>(F.counts[0]) - sbase;
-  if (*(volatile const int32_t *)F.status) avail = 0;             // a failed step moves nothing
-  const int32_t slice_n = static_cast<int32_t>(avail < 0 ? 0 : (avail < capw ? avail : capw));
-  for (int i = l; i < slice_n; i += 64) slice[i] = F.free_list[sbase + i];
+  int32_t places = F.cap_eff[r];
+  if (*(volatile const int32_t *)F.status) places = 0;            // a failed step moves nothing
+  const int64_t off = F.slice_off[r];
   const v4i *__restrict__ src = reinterpret_cast<const v4i *>(F.host_kv);
   v4i *__restrict__ dst = reinterpret_cast<v4i *>(F.gpu_kv);
 
   FzA A[2];
   FzB Bs[2];
+  FzC Cs[2];
+  FzD Ds[2];
   v4i cp[2][2];
   int32_t cslot[2] = {-1, -1};
 #pragma unroll
-  for (int p = 0; p < 2; ++p)
+  for (int p = 0; p < 2; ++p) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       A[p].tok[m] = A[p].h[m] = -1;
       Bs[p].h[m] = -1;
       Bs[p].g[m] = 0;
+      Cs[p].h[m] = Cs[p].rank[m] = -1;
+      Ds[p].h[m] = Ds[p].slot[m] = Ds[p].pos[m] = -1;
       cp[p][m] = v4i{0, 0, 0, 0};
     }
-  int32_t taken = 0, rd = 0, demand = 0;
+    Cs[p].base = Cs[p].want = Ds[p].take = 0;
+  }
+  // wanted: places this range has asked for (at most FZ_MAXW, the row queue); queued: rows in
+  // the queue; ready: rows whose slot and maps are set; rd: rows whose copy has started
+  int32_t wanted = 0, queued = 0, ready = 0, rd = 0, demand = 0;
   const uint64_t below = (1ull << l) - 1ull;
 
   // One chunk period w, with the pipeline buffers of parity P.
   auto period = [&](auto P, int32_t w) {
     constexpr int p = decltype(P)::value;
-    // decide: chunk w - 3 (lookups issued in the two periods before)
+    // maps: chunk w - 5's claimed places have their slots (read the period before)
+    if (w >= 5 && w - 5 < n_ch) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int32_t h = Ds[p ^ 1].h[m];
+        if (h >= 0) {
+          const int32_t sl = Ds[p ^ 1].slot[m];
+          F.free_[sl] = 0;
+          F.to_host[sl] = h;
+          F.host_to_gpu[h] = sl;
+          F.priority[sl] = 0;
+          ring_h[Ds[p ^ 1].pos[m]] = h;
+          ring_s[Ds[p ^ 1].pos[m]] = sl;
+        }
+      }
+      ready += Ds[p ^ 1].take;
+      __builtin_amdgcn_wave_barrier();     // the queued rows, written by several lanes, are read below
+    }
+    // slots: chunk w - 4's claim came back; its first `take` places get slots from the list
+    if (w >= 4 && w - 4 < n_ch) {
+      const int32_t base = __builtin_amdgcn_readlane(Cs[p ^ 1].base, 0);
+      const int32_t left = places - base;
+      const int32_t take = Cs[p ^ 1].want < left ? Cs[p ^ 1].want : (left > 0 ? left : 0);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int32_t rk = Cs[p ^ 1].rank[m];
+        Ds[p].h[m] = -1;
+        if (rk >= 0 && rk < take) {
+          Ds[p].h[m] = Cs[p ^ 1].h[m];
+          Ds[p].pos[m] = queued + rk;
+          Ds[p].slot[m] = F.free_list[off + base + rk];
+        }
+      }
+      Ds[p].take = take;
+      queued += take;
+    }
+    // claim: chunk w - 3's non-resident tokens (lookups issued in the two periods before)
     if (w >= 3 && w - 3 < n_ch) {
       bool qual[2];
 #pragma unroll
@@ -222,26 +261,22 @@ __global__ __launch_bounds__(FZ_THREADS) void score_fused_kernel(
       const int32_t n0 = static_cast<int32_t>(__popcll(b0)), nq = n0 + static_cast<int32_t>(__popcll(b1));
       const int32_t rk[2] = {static_cast<int32_t>(__popcll(b0 & below)),
                              n0 + static_cast<int32_t>(__popcll(b1 & below))};
+      const int32_t room = FZ_MAXW - wanted;
+      const int32_t want = places > 0 ? (nq < room ? nq : room) : 0;
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const int32_t i = taken + rk[m];
-        if (qual[m] && i < slice_n) {
-          const int32_t h = Bs[p ^ 1].h[m], s = slice[i];
-          F.free_[s] = 0;
-          F.to_host[s] = h;
-          F.host_to_gpu[h] = s;
-          F.priority[s] = 0;
-          ring_h[i] = h;
-          ring_s[i] = s;
-        }
+        Cs[p].h[m] = Bs[p ^ 1].h[m];
+        Cs[p].rank[m] = qual[m] && rk[m] < want ? rk[m] : -1;
       }
+      Cs[p].want = want;
+      Cs[p].base = 0;
+      if (want > 0 && l == 0) Cs[p].base = atomicAdd(&F.claimed[r], want);
+      wanted += want;
       demand += nq;
-      taken = min(taken + nq, slice_n);
-      __builtin_amdgcn_wave_barrier();     // the queued rows, written by several lanes, are read below
     }
     // copy: start reading the next queued row
     cslot[p] = -1;
-    if (rd < taken) {
+    if (rd < ready) {
       const int32_t h = ring_h[rd];
       cslot[p] = ring_s[rd];
       ++rd;
@@ -292,19 +327,19 @@ __global__ __launch_bounds__(FZ_THREADS) void score_fused_kernel(
     }
   };
   // Periods 0 .. n_ch - 1 follow the chunk barriers, period n_ch the final one; the later
-  // periods drain the pipeline without barriers.  Ends after at most n_ch + 3 + FZ_MAXW + 1
+  // periods drain the pipeline without barriers.  Ends after at most n_ch + 5 + FZ_MAXW + 1
   // periods (one queued row is started per period).
   for (int32_t w = 0;; w += 2) {
     if (w <= n_ch) __syncthreads();
     period(FzParity<0>{}, w);
-    if (w >= n_ch + 2 && rd >= taken && cslot[0] < 0) break;
+    if (w >= n_ch + 4 && rd >= ready && cslot[0] < 0) break;
     if (w + 1 <= n_ch) __syncthreads();
     period(FzParity<1>{}, w + 1);
-    if (w + 1 >= n_ch + 2 && rd >= taken && cslot[1] < 0) break;
+    if (w + 1 >= n_ch + 4 && rd >= ready && cslot[1] < 0) break;
   }
   if (l == 0) {
     if (demand) atomicAdd(&F.demand[r], demand);
-    if (taken) atomicAdd(&F.taken[r], taken);
+    if (ready) atomicAdd(&F.taken[r], ready);
   }
 }
 
@@ -328,13 +363,15 @@ __global__ __launch_bounds__(PF_T) void fz_count_kernel(PoolArgs P, PoolFastWs W
 }
 
 // Blocks c < n_fc: chunk c's free slots, ascending, after those of the chunks before it.  Block
-// n_fc: the list length, every request's slice offset (its ranges' slices, in request order,
-// clamped to n_gpu), and the per-request counters cleared.
+// n_fc: the list length; every request's places c_r, scaled by (free slots) / (sum of c_r) when
+// the caps add up to more than the free slots; their offsets in the list; the per-request
+// counters cleared.
 __global__ __launch_bounds__(PF_T) void fz_list_kernel(
     const uint8_t *__restrict__ free_, int32_t n_gpu, int32_t n_fc,
     const int32_t *__restrict__ chunk_free, int32_t *__restrict__ free_list, int32_t *counts,
     const int32_t *__restrict__ key_len, int32_t n_q, int32_t max_len, int32_t cap,
-    int32_t cap_div, int32_t range, int32_t *slice_off, int32_t *demand, int32_t *taken) {
+    int32_t cap_div, int32_t *slice_off, int32_t *cap_eff, int32_t *claimed, int32_t *demand,
+    int32_t *taken) {
   __shared__ uint32_t tmp[48];
   const int c = blockIdx.x, t = threadIdx.x;
   if (c < n_fc) {
@@ -357,22 +394,30 @@ __global__ __launch_bounds__(PF_T) void fz_list_kernel(
   for (int i = t; i < n_fc; i += PF_T) nf += static_cast<uint32_t>(chunk_free[i]);
   nf = block_sum<PF_T>(nf, tmp);
   if (t == 0) counts[0] = static_cast<int32_t>(nf);
+  auto cap_of = [&](int32_t r) {
+    return fz_request_cap(min(max(key_len[r], 0), max_len), cap, cap_div, n_gpu);   // <= 2^22
+  };
+  int64_t total = 0;                                  // sum of the c_r
+  for (int32_t r0 = 0; r0 < n_q; r0 += PF_T) {
+    const int32_t r = r0 + t;
+    total += block_sum<PF_T>(r < n_q ? static_cast<uint32_t>(cap_of(r)) : 0u, tmp);   // <= 2^30
+  }
   int64_t base = 0;
   for (int32_t r0 = 0; r0 < n_q; r0 += PF_T) {
     const int32_t r = r0 + t;
     uint32_t a = 0;
     if (r < n_q) {
-      const int32_t L = min(max(key_len[r], 0), max_len);
-      a = static_cast<uint32_t>(fz_request_cap(L, cap, cap_div, range));   // <= 128 * 32768
+      int64_t cr = cap_of(r);
+      if (total > nf) cr = cr * static_cast<int64_t>(nf) / total;
+      a = static_cast<uint32_t>(cr);
+      cap_eff[r] = static_cast<int32_t>(cr);
+      claimed[r] = 0;
       demand[r] = 0;
       taken[r] = 0;
     }
     uint32_t tot;
     const uint32_t ex = block_excl_scan<PF_T>(a, tmp, &tot);
-    if (r < n_q) {
-      const int64_t off = base + ex;
-      slice_off[r] = static_cast<int32_t>(off < n_gpu ? off : n_gpu);
-    }
+    if (r < n_q) slice_off[r] = static_cast<int32_t>(base + ex);   // base + ex + cap_eff <= nf
     base += tot;
   }
 }
@@ -412,6 +457,7 @@ size_t fused_ws_layout(int32_t n_q, int32_t n_gpu, void *base, FusedWs *w) {
   auto take = [&](size_t b) { size_t o = off; off += al(b); return o; };
   const size_t o_cf = take(static_cast<size_t>(fz_n_chunks(n_gpu)) * 4), o_fl = take(ng * 4);
   const size_t o_so = take(nq * 4), o_c = take(2 * 4), o_d = take(nq * 4), o_t = take(nq * 4);
+  const size_t o_ce = take(nq * 4), o_cl = take(nq * 4);
   if (w && base) {
     char *b = static_cast<char *>(base);
     w->chunk_free = reinterpret_cast<int32_t *>(b + o_cf);
@@ -420,6 +466,8 @@ size_t fused_ws_layout(int32_t n_q, int32_t n_gpu, void *base, FusedWs *w) {
     w->counts = reinterpret_cast<int32_t *>(b + o_c);
     w->demand = reinterpret_cast<int32_t *>(b + o_d);
     w->taken = reinterpret_cast<int32_t *>(b + o_t);
+    w->cap_eff = reinterpret_cast<int32_t *>(b + o_ce);
+    w->claimed = reinterpret_cast<int32_t *>(b + o_cl);
   }
   return off;
 }
@@ -451,8 +499,8 @@ int launch_fused_prefetch(const uint8_t *q, const float *w, const uint8_t *k, co
   int rc = check_launch("fused_count");
   if (rc) return rc;
   fz_list_kernel<<<n_fc + 1, PF_T, 0, st>>>(pool->gpu_free, pool->n_gpu, n_fc, Z.chunk_free, Z.free_list,
-                                            Z.counts, key_len, n_q, max_len, cap, cap_div, range,
-                                            Z.slice_off, Z.demand, Z.taken);
+                                            Z.counts, key_len, n_q, max_len, cap, cap_div,
+                                            Z.slice_off, Z.cap_eff, Z.claimed, Z.demand, Z.taken);
   if ((rc = check_launch("fused_list"))) return rc;
   const int32_t gx = max_len > 0 ? (max_len + range - 1) / range : 0;
   const int64_t blocks = static_cast<int64_t>(gx) * n_q;
@@ -460,7 +508,7 @@ int launch_fused_prefetch(const uint8_t *q, const float *w, const uint8_t *k, co
   if (blocks > 0) {
     FusedArgs F{theta, req_to_host, pool->host_kv, pool->gpu_kv, pool->gpu_free, pool->gpu_priority,
                 pool->gpu_to_host, pool->host_to_gpu, pool->status, pool->n_gpu, pool->n_host,
-                Z.free_list, Z.counts, Z.slice_off, Z.demand, Z.taken, cap, cap_div, range};
+                Z.free_list, Z.counts, Z.slice_off, Z.cap_eff, Z.claimed, Z.demand, Z.taken, range};
 #define ECHO_FZ(SC, HI)                                                                          \
   score_fused_kernel<SC, HI><<<static_cast<unsigned>(blocks), FZ_THREADS, 0, st>>>(              \
       q, w, k, k_scale, key_begin, key_len, max_len, gx, scores, ld, F, hist0)

@@ -164,22 +164,23 @@ int echo_index_scores_prefetch(const uint8_t *q, const float *w, const uint8_t *
  * allocate and zero-copy row reads).  Scores every request exactly as echo_index_scores does
  * (same values), and moves rows of tokens scoring above theta[r] into free GPU slots while the
  * later keys are still being scored.
- *   Ranges.  Request r's tokens are cut into n_r = ceil(key_len[r] / range) ranges of `range`
- *   tokens (one workgroup each; range = 0 picks one; else a multiple of 128 in
- *   [128, ECHO_FUSED_MAX_RANGE]).  Request r may move c_r = min(cap, ceil(key_len[r] / cap_div),
- *   ECHO_FUSED_MAX_PER_RANGE * n_r) rows; its range x may move
- *   m_x = floor((x + 1) c_r / n_r) - floor(x c_r / n_r) of them.
- *   Which rows.  In each range, the tokens s (ascending) with score > theta[r] (fp32, strict;
- *   NaN never passes) whose host index h = req_to_host[key_begin[r] + s] is in [0, n_host) and
- *   not resident (host_to_gpu[h] == ECHO_INF when the call starts) qualify; the first m_x of
- *   them move.
- *   Which slots.  The pool's free slots at the start, in ascending order, form a list.
- *   Request r owns the c_r list entries from O_r = sum over r' < r of c_r'; its range x owns
- *   entries O_r + floor(x c_r / n_r) + i, i < m_x, and its i-th moved token takes entry i while
- *   that entry exists (a short list leaves later ranges without slots).
+ *   Ranges.  Request r's tokens are cut into ranges of `range` tokens (one workgroup each;
+ *   range = 0 picks one; else a multiple of 128 in [128, ECHO_FUSED_MAX_RANGE]).
+ *   Which rows.  The tokens s with score > theta[r] (fp32, strict; NaN never passes) whose host
+ *   index h = req_to_host[key_begin[r] + s] is in [0, n_host) and not resident
+ *   (host_to_gpu[h] == ECHO_INF when the call starts) qualify.  Each range asks for places for
+ *   its first ECHO_FUSED_MAX_PER_RANGE qualifying tokens in token order (its candidates).
+ *   Cap and places.  Request r may move c_r = min(cap, ceil(key_len[r] / cap_div), n_gpu) rows,
+ *   scaled to floor(c_r * F / C) when the caps add up to C > F, the pool's free slots at the
+ *   start.  Those free slots, ascending, form a list; request r owns c_r entries of it, after
+ *   those of requests < r.  Its ranges claim them first come, first served (one counter per
+ *   request): min(#candidates, c_r) rows move, each range's a token-order prefix of its
+ *   candidates in ascending slots, into the request's first entries.  So when a request's
+ *   candidates fit its cap, all of them move; which of the request's slots each one gets
+ *   depends on timing.
  *   Each moved token: free = 0, gpu_to_host = h, host_to_gpu[h] = slot, priority 0, and its
  *   row copied from host_kv.  Nothing is evicted; nothing moves when the status word is
- *   nonzero.  The result depends on the inputs alone (no timing).
+ *   nonzero.
  *   Outputs: *n_prefetched = rows moved; *demand (or NULL) = qualifying tokens, before caps.
  *   Workspace: echo_fused_workspace_bytes(n_q, pool->n_gpu) bytes.  Host indices are unique
  *   across requests (caller precondition).
@@ -343,7 +344,7 @@ int echo_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
  * Prefetch (§6.1): ECHO_PREFETCH_RANGED scores in n_chunks launches, each of which also gathers
  * the candidates of the range before it (which candidates win the cap depends on timing);
  * ECHO_PREFETCH_FUSED scores in one launch with a host-gather wave per workgroup, with the
- * rows and slots of echo_index_scores_fused (§6.3; independent of timing).  Either way the
+ * rows and slots of echo_index_scores_fused (§6.3).  Either way the
  * threshold is theta_ema when given, else the sample percentile, and the selection and the
  * selected rows are those of the step without prefetch.
  * `side_stream` is reserved and ignored (pass NULL or main_stream).  Workspace:

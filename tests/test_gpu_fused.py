@@ -1,18 +1,22 @@
 """GPU parity of the scoring kernel with the host-gather wave (ECHO page §6.3; the threshold
 prefetch of §6.1 done inside the scoring launch) against the oracle's range prefetch
-(oracle/prefetch.py): the scores and the pool after the prefetch bit-exact on integer-grid
-inputs, for several range lengths, caps, thresholds (including NaN and infinities) and free
-lists that run short; a failed pool (status set) moves nothing.  General FP8 with scales: the
-scores within tolerance and what moved checked through the properties that define it.  The
-whole decode step with the fused prefetch, eager and as one replayed hipGraph, bit-exact against
-the oracle's step (the EMA estimate and the sample percentile as thresholds)."""
+(oracle/prefetch.py).  On integer-grid inputs the scores are bit-exact and the pool after the
+prefetch is a valid outcome (oracle.check_prefetch_outcome): the same demand, per request
+min(#candidates, cap) rows moved, each range's a token-order prefix of its candidates, into
+exactly the request's first places, maps, priorities and rows set, nothing else touched; when a
+request's candidates fit its cap, its moved set is the oracle's exactly.  Cases cover several
+range lengths, caps, thresholds (NaN and infinities), caps scaled to a short free list, a full
+pool and 300 requests; a failed pool (status set) moves nothing.  General FP8 with scales: the
+scores within tolerance and the same properties against the GPU's own scores.  The whole
+decode step with the fused prefetch, eager and as one replayed hipGraph, against the oracle's
+step: selection, misses, counters, and every pool array equal up to which of the prefetched
+slots holds which prefetched row."""
 
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from oracle import prefetch as pfo
 from dsa_indexer_top_amd import binding as B, inputs as gen
 from dsa_indexer_top_amd.runner import DecodeRunner
 from gpu_util import announce, dev, host, DevPool, assert_pool_equal
@@ -87,14 +91,14 @@ def test_fused_prefetch_exact(case):
     st, host_kv = _pool_case(inp, 300 + case, n_gpu, free_frac, 0.3)
     scores = oracle.index_scores(inp.q, inp.w, inp.k, None, inp.key_begin, inp.key_len)
     theta = _thetas(scores, qt, specials)
-    want, moved, demand = oracle.range_prefetch(scores, theta, inp.key_begin, inp.key_len,
-                                                inp.req_to_host, st, host_kv, cap, cap_div, R)
+    want, moved, demand, info = oracle.range_prefetch(scores, theta, inp.key_begin, inp.key_len,
+                                                      inp.req_to_host, st, host_kv, cap, cap_div, R)
     got_sc, got_st, npf, dem, P = _run_standalone(inp, st, host_kv, theta, cap, cap_div, R)
     try:
         for r, s in enumerate(scores):
             assert np.array_equal(got_sc[r, :len(s)].astype(np.float64), s), "scores row %d" % r
         assert npf == len(moved) and dem == int(demand.sum())
-        assert_pool_equal(got_st, want, "after the fused prefetch")
+        oracle.check_prefetch_outcome(st, got_st, host_kv, inp.key_begin, inp.req_to_host, info)
         assert (len(moved) > 0) == (free_frac > 0) and demand.sum() > 0
     finally:
         P.hostbuf.close()
@@ -118,10 +122,11 @@ def test_fused_prefetch_failed_pool_moves_nothing():
 
 
 def test_fused_prefetch_general_fp8_properties():
-    # general FP8 with per-token scales: the scores within 1e-4 T; what moved is, per range, a
-    # token-order prefix of the tokens whose GPU score is above the threshold and that were not
-    # resident, within the range's share, in distinct slots that were free, taken from the
-    # ascending free list in (request, range, rank) order; every moved row equals its host row
+    # general FP8 with per-token scales: the scores within 1e-4 T; what moved is, per request,
+    # min(#candidates, cap) rows (candidates: each range's first 128 tokens whose GPU score is
+    # above the threshold and that were not resident), each range's a token-order prefix in
+    # ascending slots, in exactly the request's first places; every moved row equals its host
+    # row
     announce("fused prefetch general fp8")
     lens, R, cap, cap_div = [3000, 1, 129, 2500], 256, 300, 2
     cfg = gen.DecodeConfig("fzg", len(lens), 0, 64, "general", True, 0.5, 1, seed=320)
@@ -139,29 +144,33 @@ def test_fused_prefetch_general_fp8_properties():
         new = np.flatnonzero((st.free == 1) & (got_st.free == 0))
         assert len(new) == npf > 0
         free_list = np.flatnonzero(st.free == 1)
-        tok_of_host = {int(h): (r, s) for r in range(len(lens)) for s in range(lens[r])
-                       for h in [inp.req_to_host[inp.key_begin[r] + s]]}
-        moved = sorted((tok_of_host[int(got_st.to_host[sl])], int(sl)) for sl in new)
-        assert [sl for _, sl in moved] == sorted(sl for _, sl in moved)   # list order
-        assert all(got_st.priority[sl] == 0 for _, sl in moved)
+        tok_of_host = {int(inp.req_to_host[inp.key_begin[r] + s]): (r, s)
+                       for r in range(len(lens)) for s in range(lens[r])}
+        by_req = {}
+        for sl in new:
+            r, s = tok_of_host[int(got_st.to_host[sl])]
+            assert got_st.priority[sl] == 0 and np.array_equal(got_st.gpu_kv[sl], host_kv[got_st.to_host[sl]])
+            by_req.setdefault(r, []).append((s, int(sl)))
+        caps = oracle.request_caps(lens, cap, cap_div, len(free_list), len(st.free))[1]
         offset, n_dem = 0, 0
         for r in range(len(lens)):
             L = lens[r]
-            c, n_rng = pfo.request_cap(L, cap, cap_div, R), -(-L // R)
+            # candidates from the GPU's own scores: per range the first 128 qualifying tokens
             qual = [s for s in range(L) if got_sc[r, s] > theta[r]
                     and st.host_to_gpu[inp.req_to_host[inp.key_begin[r] + s]] == oracle.INF]
             n_dem += len(qual)
-            for x in range(n_rng):
-                first, share = pfo.range_share(c, n_rng, x)
-                qx = [s for s in qual if s // R == x]
-                gx = [(s, sl) for (rr, s), sl in moved if rr == r and s // R == x]
-                assert [s for s, _ in gx] == qx[:len(gx)] and len(gx) <= share
-                # each range's rows sit in its own entries of the free list, in rank order
-                for i, (_, sl) in enumerate(gx):
-                    assert free_list[offset + first + i] == sl
-                if len(gx) < min(len(qx), share):
-                    assert offset + first + len(gx) >= len(free_list)   # the list ran out
-            offset += c
+            cand = {}
+            for s_ in qual:
+                if len(cand.setdefault(s_ // R, [])) < 128:
+                    cand[s_ // R].append(s_)
+            got = sorted(by_req.get(r, []))
+            assert len(got) == min(sum(map(len, cand.values())), caps[r]), "request %d count" % r
+            assert sorted(sl for _, sl in got) == list(free_list[offset:offset + len(got)])
+            for x, cx in cand.items():
+                gx = [(s_, sl) for s_, sl in got if s_ // R == x]
+                assert [s_ for s_, _ in gx] == cx[:len(gx)], "request %d range %d prefix" % (r, x)
+                assert [sl for _, sl in gx] == sorted(sl for _, sl in gx)
+            offset += caps[r]
         assert dem == n_dem
     finally:
         P.hostbuf.close()
@@ -177,16 +186,38 @@ def _as_state(d):
                             d["indices_buf"], d["gpu_kv"])
 
 
+def _assert_equal_up_to_prefetched(got, want, pf_slots, what):
+    """Every pool array equal, except that the prefetched rows may sit in any of the prefetched
+    slots (which one gets which depends on timing): there, the (host index, priority, row)
+    triples must agree as multisets and the maps must stay inverse."""
+    keep = np.ones(len(want.free), bool)
+    keep[pf_slots] = False
+    for name in ("free", "priority", "to_host", "indices_buf", "gpu_kv"):
+        a, b = getattr(got, name), getattr(want, name)
+        assert np.array_equal(a[keep], b[keep]), "%s: %s outside the prefetched slots" % (what, name)
+    trip = lambda st: sorted((int(st.to_host[s]), int(st.priority[s]), st.gpu_kv[s].tobytes())
+                             for s in pf_slots)
+    assert trip(got) == trip(want), "%s: the prefetched rows" % what
+    hk = np.ones(len(want.host_to_gpu), bool)
+    hk[want.to_host[pf_slots][want.to_host[pf_slots] != oracle.INF]] = False
+    assert np.array_equal(got.host_to_gpu[hk], want.host_to_gpu[hk]), "%s: host_to_gpu" % what
+    for s_ in pf_slots:
+        h = got.to_host[s_]
+        assert h == oracle.INF or got.host_to_gpu[h] == s_, "%s: maps of slot %d" % (what, s_)
+
+
 @pytest.mark.parametrize("given_theta", [True, False])
-@pytest.mark.parametrize("lens,k,R,reserve", [([3000, 700, 1, 0], 64, 256, 300),
-                                              ([5000, 4096], 256, 128, 1500),
-                                              ([2000, 900], 128, 256, 0)])     # a full pool
-def test_decode_step_fused_exact(lens, k, R, reserve, given_theta):
+@pytest.mark.parametrize("lens,k,R,div,reserve", [([3000, 700, 1, 0], 64, 256, 1, 1500),
+                                                  ([5000, 4096], 256, 128, 1, 3000),
+                                                  ([2000, 900], 128, 256, 4, 0)])   # a full pool
+def test_decode_step_fused(lens, k, R, div, reserve, given_theta):
     # the whole step with the fused prefetch: the threshold given (the EMA estimate) or the
-    # sample percentile; selection, slots, miss lists, counters and the pool after the step
-    # bit-exact against the oracle's step; then replayed as one graph from the same start
+    # sample percentile; every request's candidates fit its cap and the misses fit the free
+    # room, so what moves and what the step does afterwards are unique; selection, misses,
+    # counters and the pool after the step against the oracle's step, up to which prefetched
+    # slot holds which prefetched row; then replayed as one graph from the same start
     announce("decode step fused", lens, k, R, reserve, "given theta" if given_theta else "sample theta")
-    cfg = gen.DecodeConfig("fzd", len(lens), 0, k, "int", False, 0.5, 4, seed=330 + k,
+    cfg = gen.DecodeConfig("fzd", len(lens), 0, k, "int", False, 0.5, div, seed=330 + k,
                            reserve=reserve)
     inp = gen.make_decode_inputs(cfg, lengths=lens)
     host_kv = gen.fill_latent_rows(cfg.seed, np.empty((inp.n_host, 576), np.uint16))
@@ -197,14 +228,18 @@ def test_decode_step_fused_exact(lens, k, R, reserve, given_theta):
         theta = _thetas(scores, 0.9, {len(lens) - 1: np.nan})
     else:
         theta = np.array([oracle.sample_threshold(s, 4096, 95.0) for s in scores], np.float32)
-    cap, cap_div = 200, 8
+    cap, cap_div = 2048, 8
     st0 = _oracle_state(pool)
-    _, want_idx, mid, moved, demand, want_state, res = oracle.decode_step_prefetched(
+    _, want_idx, mid, moved, demand, info, want_state, res = oracle.decode_step_prefetched(
         inp.q, inp.w, inp.k, None, inp.key_begin, inp.key_len, inp.req_to_host, st0, host_kv, k,
-        pool.step_id, theta, cap, cap_div, R, reserve=reserve)
+        pool.step_id, theta, cap, cap_div, R)
     assert (len(moved) > 0) == (reserve > 0) and res.status == 0
+    for r, c in enumerate(info["cand"]):                # the preconditions of a unique result
+        assert sum(map(len, c.values())) <= info["cap"][r] or info["cap"][r] == 0
+    assert reserve == 0 or res.n_evicted == 0
+    pf_slots = np.array(sorted(m[3] for m in moved), np.int64)
     pf = dict(cap=cap, cap_div=cap_div, range=R)
-    rn = DecodeRunner(inp, pool, host_kv, prefetch="fused", pf=pf, reserve=reserve,
+    rn = DecodeRunner(inp, pool, host_kv, prefetch="fused", pf=pf,
                       theta=theta if given_theta else None)
     try:
         for mode in ("eager", "graph", "graph again"):
@@ -218,10 +253,17 @@ def test_decode_step_fused_exact(lens, k, R, reserve, given_theta):
             got = rn.results()
             assert got["status"] == 0, mode
             assert np.array_equal(got["topk_idx"], want_idx), mode
-            assert np.array_equal(got["topk_slot"], res.topk_slot), mode
             assert np.array_equal(got["miss_host"], res.miss_host), mode
             assert np.array_equal(got["miss_slot"], res.miss_slot), mode
             assert list(got["counters"][:3]) == [res.n_miss, int(demand.sum()), len(moved)], mode
-            assert_pool_equal(_as_state(got["pool"]), want_state, mode)
+            pf_sel = np.isin(res.topk_slot, pf_slots)
+            assert np.array_equal(got["topk_slot"][~pf_sel], res.topk_slot[~pf_sel]), mode
+            assert np.isin(got["topk_slot"][pf_sel], pf_slots).all(), mode
+            _assert_equal_up_to_prefetched(_as_state(got["pool"]), want_state, pf_slots, mode)
+            idx_ = got["topk_idx"]
+            rows, cols = np.nonzero(idx_ >= 0)
+            hosts = inp.req_to_host[inp.key_begin[rows] + idx_[rows, cols]]
+            oracle.check_pool_invariants(_as_state(got["pool"]), host_kv, hosts,
+                                         got["topk_slot"][rows, cols])
     finally:
         rn.close()
