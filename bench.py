@@ -14,9 +14,10 @@ which is reported separately).
 
 Prints ONE JSON line.  --gpus N > 1 is refused: this path runs on one GPU.
 
-The secondary measurements (prefill indexer, chunked prefill with offload, decode loop, prefetch
-modes) each run in a child process of their own (`--section NAME`), so that a failure in one of
-them is recorded in its place and the headline line is still printed.
+Every measurement (the headline step, the prefill indexer, the chunked prefill with offload, the
+decode loop, the prefetch modes) runs in a child process of its own (`--section NAME`); the
+main process only starts them and prints the one JSON line, so a failure in one of them is
+recorded in its place and the line is still printed.
 """
 
 import argparse
@@ -32,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+METRIC = "indexed tokens/sec (score+top-k+recall) and % of HBM peak at L=64K-128K, 1 GPU"
 WORKLOADS = {
     "b8_64k": "decode step: 8 requests x 65536 tokens, H=64 d=128 FP8 (integer grid) q/k, "
               "top-2048, 90% pool hit rate, N_G=65536, N_H=524288",
@@ -136,21 +138,9 @@ def oracle_threads():
         return 1
 
 
-def loop_measure(torch, B, gen, batch=8, length=65536, n_steps=16, topk=2048, drift=0.05,
-                 cpu=True):
-    """Decode steps in a row: every step appends one token per request (key, host row written
-    through, GPU slot) and runs the decode step with prefetch against the EMA estimate of the
-    k-th score (alpha = 0.5).  8 requests x 65536 tokens, integer grid, top-2048, a full pool of
-    N_G = 65536 slots whose guaranteed recall leaves 8 x 2048 slots free for the next step's
-    prefetch, consecutive queries alike (5% of q's bytes redrawn per step).  The whole step (stamp advance, append, decode step) is one captured graph replayed
-    every step; timed per step with HIP events around the replay on its stream (the upload of
-    the step's query and new tokens precedes the start event).  Reports the pool hit rate of
-    the guaranteed recall, the rows prefetched and the EMA's prediction error per step."""
-    from dsa_indexer_top_amd.runner import LoopRunner
-    n_gpu = batch * length // 8
-    reserve = batch * topk                     # room for a full step of prefetch
-    m, host_kv = gen.make_multistep_inputs(batch, length, n_steps, n_gpu, seed=51, drift=drift)
-    rn = LoopRunner(m, host_kv, topk, prefetch=True, pf=dict(n_chunks=4, cap=2048, cap_div=32),
+def run_loop(torch, LoopRunner, m, host_kv, topk, batch, reserve, mode):
+    """The captured loop step replayed for every step of m; per-step timings and counters."""
+    rn = LoopRunner(m, host_kv, topk, prefetch=mode, pf=dict(n_chunks=4, cap=2048, cap_div=32),
                     device_step=True, reserve=reserve)
     steps = []
     try:
@@ -176,6 +166,27 @@ def loop_measure(torch, B, gen, batch=8, length=65536, n_steps=16, topk=2048, dr
                           "ema_rel_err_median": None if err is None else round(float(np.median(err)), 4)})
     finally:
         rn.close()
+    return steps
+
+
+def loop_measure(torch, B, gen, batch=8, length=65536, n_steps=16, topk=2048, drift=0.05,
+                 cpu=True):
+    """Decode steps in a row: every step appends one token per request (key, host row written
+    through, GPU slot) and runs the decode step with prefetch against the EMA estimate of the
+    k-th score (alpha = 0.5).  8 requests x 65536 tokens, integer grid, top-2048, a full pool of
+    N_G = 65536 slots whose guaranteed recall leaves 8 x 2048 slots free for the next step's
+    prefetch, consecutive queries alike (5% of q's bytes redrawn per step).  The whole step (stamp advance, append, decode step) is one captured graph replayed
+    every step; timed per step with HIP events around the replay on its stream (the upload of
+    the step's query and new tokens precedes the start event).  Reports the pool hit rate of
+    the guaranteed recall, the rows prefetched and the EMA's prediction error per step, with the
+    ranged prefetch (scoring in 4 launches) and again, on the same inputs, with the fused one
+    (one scoring launch with a host-gather wave per workgroup)."""
+    from dsa_indexer_top_amd.runner import LoopRunner
+    n_gpu = batch * length // 8
+    reserve = batch * topk                     # room for a full step of prefetch
+    m, host_kv = gen.make_multistep_inputs(batch, length, n_steps, n_gpu, seed=51, drift=drift)
+    steps = run_loop(torch, LoopRunner, m, host_kv, topk, batch, reserve, "ranged")
+    fused = run_loop(torch, LoopRunner, m, host_kv, topk, batch, reserve, "fused")
     later = steps[1:]
     out = {}
     if cpu:
@@ -203,7 +214,11 @@ def loop_measure(torch, B, gen, batch=8, length=65536, n_steps=16, topk=2048, dr
             "hit_rate_median": round(float(np.median([x["hit_rate"] for x in later])), 4),
             "indexed_tokens_per_s": round(batch * (length + n_steps / 2) /
                                           (float(np.median([x["us"] for x in later])) / 1e6), 1),
-            "steps": steps})
+            "steps": steps,
+            "fused": {"us_per_step_median": round(float(np.median([x["us"] for x in fused[1:]])), 1),
+                      "hit_rate_median": round(float(np.median([x["hit_rate"] for x in fused[1:]])), 4),
+                      "prefetched_median": int(np.median([x["prefetched"] for x in fused[1:]])),
+                      "steps": fused}})
     return out
 
 
@@ -417,14 +432,18 @@ def cpu_baseline(inp, host_kv, pool_arrays, min_s=10.0, budget_s=30.0):
             "kind": "oracle", "seconds": round(dt, 3), "sample": sample}
 
 
-SECTIONS = ("prefill", "prefill_offload", "loop", "prefetch_modes")
+SECTIONS = ("headline", "prefill", "prefill_offload", "loop", "prefetch_modes")
 
 
 def run_section(name, args, timeout_s=900):
-    """One secondary measurement in a child process; its JSON (or the failure) as a dict."""
-    cmd = [sys.executable, os.path.abspath(__file__), "--section", name, "--workload", args.workload]
+    """One measurement in a child process; its JSON (or the failure) as a dict."""
+    cmd = [sys.executable, os.path.abspath(__file__), "--section", name, "--workload", args.workload,
+           "--steps", str(args.steps), "--warmup", str(args.warmup),
+           "--kernel-reps", str(args.kernel_reps), "--prefetch", args.prefetch]
     if args.reserve is not None:
         cmd += ["--reserve", str(args.reserve)]
+    if args.percentile is not None:
+        cmd += ["--percentile", str(args.percentile)]
     if args.no_cpu_baseline:
         cmd.append("--no-cpu-baseline")
     try:
@@ -469,125 +488,9 @@ def child_section(name, args, torch, B, gen):
         hb.close()
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="b8_64k", choices=sorted(WORKLOADS))
-    ap.add_argument("--kernel-reps", type=int, default=50)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--no-loop", action="store_true", help="skip the decode-loop measurement")
-    ap.add_argument("--prefetch", choices=("auto", "on", "off", "ranged", "fused"), default="auto",
-                    help="prefetch of the headline step (on = ranged)")
-    ap.add_argument("--no-prefetch-modes", action="store_true",
-                    help="skip the off / ranged / fused prefetch comparison")
-    ap.add_argument("--section", choices=SECTIONS, default=None,
-                    help="run one secondary measurement alone and print its JSON (the main run "
-                         "starts each of them this way, in a child process)")
-    ap.add_argument("--reserve", type=int, default=None,
-                    help="free GPU slots in the starting pool (default: the workload's own)")
-    ap.add_argument("--percentile", type=float, default=None,
-                    help="prefetch threshold percentile of the score sample (default 95)")
-    ap.add_argument("--probe", choices=("score", "copy", "prefill"), default=None,
-                    help="short program for hardware-counter runs, then exit: 20 launches of the "
-                         "scoring kernel on the workload, 20 device copies of 256 MiB, or 3 causal "
-                         "prefill launches on 32768^2")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py: this decode path runs on one GPU; --gpus %d is not supported "
-              "(the batch shards across GPUs with no exchange, see the design notes)" % args.gpus,
-              file=sys.stderr)
-        sys.exit(2)
-
-    if args.section is None and args.probe is None:
-        # secondary measurements first, each in a child process and before this process touches
-        # the GPU: a failure in one of them (a Python error, a crash, a time-out) is recorded in
-        # its place, and the headline line is always printed
-        extra = {}
-
-        def section(name, fn, summary):
-            try:
-                extra[name] = fn()
-            except Exception as e:                       # noqa: BLE001
-                extra[name] = {"error": "%s: %s" % (type(e).__name__, e)}
-            if "error" in extra[name]:
-                log("%s failed: %s" % (name, extra[name]["error"]))
-                return
-            try:
-                log(summary(extra[name]))
-            except Exception:                            # noqa: BLE001
-                log("%s done" % name)
-
-        if not args.no_prefill:
-            log("prefill indexer (32768^2) ...")
-            section("prefill", lambda: run_section("prefill", args),
-                    lambda p: "prefill %.1f us = %.0f TFLOP/s (%.1f%% of fp8 peak), top-k rows %.1f us"
-                    % (p["us_per_launch"], p["achieved"], 100 * p["frac"], p["topk_rows_us"]))
-            log("chunked prefill with offload and inter-query prefetch ...")
-            section("prefill_offload", lambda: run_section("prefill_offload", args),
-                    lambda p: "chunked prefill: threshold bin median %d shifted vs %d unshifted"
-                    % (p["thr_bin_median_shifted"], p["thr_bin_median_unshifted"]))
-        if not args.no_loop:
-            log("decode loop (EMA threshold, new tokens every step) ...")
-            section("loop", lambda: run_section("loop", args),
-                    lambda p: "loop: median %.1f us/step, hit rate %.3f"
-                    % (p["us_per_step_median"], p["hit_rate_median"]))
-        if not args.no_prefetch_modes:
-            log("prefetch off / ranged / fused on one starting pool ...")
-            section("prefetch_modes", lambda: run_section("prefetch_modes", args),
-                    lambda p: "prefetch modes: off %.1f, ranged %.1f, fused %.1f us/step; fused "
-                    "launches alone %.1f us vs plain scoring %.1f us" % (
-                        p["off"]["us_per_step"], p["ranged"]["us_per_step"], p["fused"]["us_per_step"],
-                        p["fused_launches_alone"]["us_median"], p["fused_launches_alone"]["plain_scoring_us"]))
-
-    import torch
-    from dsa_indexer_top_amd import binding as B, inputs as gen
-    from dsa_indexer_top_amd.runner import DecodeRunner
-
-    if args.probe == "copy":
-        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
-        b = torch.empty_like(a)
-        for _ in range(20):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        log("copy probe: 20 x 256 MiB device copies")
-        return
-    if args.section:
-        try:
-            res = child_section(args.section, args, torch, B, gen)
-            torch.cuda.synchronize()
-        except Exception as e:                       # noqa: BLE001
-            res = {"error": "%s: %s" % (type(e).__name__, e)}
-        print(json.dumps(res), flush=True)
-        return
-    cfg = gen.CONFIGS[args.workload]
-    prefetch = (cfg.prefetch if args.prefetch == "auto" else
-                {"on": "ranged", "off": False}.get(args.prefetch, args.prefetch))
-    if args.probe == "prefill":
-        pc = gen.PREFILL["prefill_32k"]
-        n = pc["n"]
-        q, w, k = gen.make_prefill_inputs(n, seed=pc["seed"])
-        dq, dw, dk = (torch.from_numpy(x).cuda() for x in (q, w, k))
-        sc = torch.empty((n, n), dtype=torch.float32, device="cuda")
-        for _ in range(3):
-            B.index_scores_prefill(dq, dw, dk, sc, ld=n)
-        torch.cuda.synchronize()
-        log("prefill probe: 3 launches of echo_index_scores_prefill on 32768 x 32768")
-        return
-    if args.probe == "score":
-        inp = gen.make_decode_inputs(cfg)
-        dq, dw, dk = (torch.from_numpy(x).cuda() for x in (inp.q, inp.w, inp.k))
-        dks = None if inp.k_scale is None else torch.from_numpy(inp.k_scale).cuda()
-        dkb, dkl = torch.from_numpy(inp.key_begin).cuda(), torch.from_numpy(inp.key_len).cuda()
-        max_len = int(inp.key_len.max())
-        sc = torch.empty((len(inp.key_len), max_len), dtype=torch.float32, device="cuda")
-        for _ in range(20):
-            B.index_scores(dq, dw, dk, dks, dkb, dkl, max_len, sc)
-        torch.cuda.synchronize()
-        log("score probe: 20 launches of echo_index_scores on", args.workload)
-        return
+def headline(args, torch, B, gen, DecodeRunner, cfg, prefetch):
+    """The headline measurement (the captured decode step of the workload) with its roofline,
+    live kernel timings and, unless disabled, the oracle's CPU baseline, as one dict."""
     log("workload", args.workload, "prefetch", prefetch)
     t_setup = time.perf_counter()
     inp = gen.make_decode_inputs(cfg)
@@ -672,7 +575,7 @@ def main():
         t_score, score_gbs, t_topk, t_recall, recall_gbs, link))
 
     out = {
-        "metric": "indexed tokens/sec (score+top-k+recall) and % of HBM peak at L=64K-128K, 1 GPU",
+        "metric": METRIC,
         "value": round(value, 1),
         "unit": "indexed tokens/s",
         "n_gpus": 1,
@@ -716,16 +619,154 @@ def main():
                      # pool's priorities are a permutation, so at most one other slot holds 0
                      "prefetched_unselected_approx": int((res["pool"]["priority"] == 0).sum())},
     }
-    out.update(extra)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        section("cpu_baseline", lambda: cpu_baseline(inp, host_kv, pool),
-                lambda p: "cpu baseline %.3g %s on %d threads" % (p["value"], p["unit"], p["cores"]))
-        out["cpu_baseline"] = extra["cpu_baseline"]
+        try:
+            out["cpu_baseline"] = cpu_baseline(inp, host_kv, pool)
+            log("cpu baseline %.3g %s on %d threads" % (out["cpu_baseline"]["value"],
+                                                         out["cpu_baseline"]["unit"],
+                                                         out["cpu_baseline"]["cores"]))
+        except Exception as e:                       # noqa: BLE001
+            out["cpu_baseline"] = {"error": "%s: %s" % (type(e).__name__, e)}
     rn.close()
     hb.close()
-    print(json.dumps(out), flush=True)
+    return out
 
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="b8_64k", choices=sorted(WORKLOADS))
+    ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-loop", action="store_true", help="skip the decode-loop measurement")
+    ap.add_argument("--prefetch", choices=("auto", "on", "off", "ranged", "fused"), default="auto",
+                    help="prefetch of the headline step (on = ranged)")
+    ap.add_argument("--no-prefetch-modes", action="store_true",
+                    help="skip the off / ranged / fused prefetch comparison")
+    ap.add_argument("--section", choices=SECTIONS, default=None,
+                    help="run one secondary measurement alone and print its JSON (the main run "
+                         "starts each of them this way, in a child process)")
+    ap.add_argument("--reserve", type=int, default=None,
+                    help="free GPU slots in the starting pool (default: the workload's own)")
+    ap.add_argument("--percentile", type=float, default=None,
+                    help="prefetch threshold percentile of the score sample (default 95)")
+    ap.add_argument("--probe", choices=("score", "copy", "prefill"), default=None,
+                    help="short program for hardware-counter runs, then exit: 20 launches of the "
+                         "scoring kernel on the workload, 20 device copies of 256 MiB, or 3 causal "
+                         "prefill launches on 32768^2")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this decode path runs on one GPU; --gpus %d is not supported "
+              "(the batch shards across GPUs with no exchange, see the design notes)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    if args.section is None and args.probe is None:
+        # this process only starts the measurements, each in a child process of its own, and
+        # never touches the GPU: a failure in one of them (a Python error, a crash, a time-out)
+        # is recorded in its place, and the one JSON line is always printed
+        log("headline: workload", args.workload)
+        out = run_section("headline", args, timeout_s=1500)
+        if "error" in out:
+            log("headline failed:", out["error"])
+            out = {"metric": METRIC, "value": None, "unit": "indexed tokens/s", "n_gpus": 1,
+                   "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+                   "scaling": "weak", "vs_baseline": None, "data": "synthetic (seeded)",
+                   "config": {"workload": args.workload}, "error": out["error"]}
+        extra = {}
+
+        def section(name, fn, summary):
+            try:
+                extra[name] = fn()
+            except Exception as e:                       # noqa: BLE001
+                extra[name] = {"error": "%s: %s" % (type(e).__name__, e)}
+            if "error" in extra[name]:
+                log("%s failed: %s" % (name, extra[name]["error"]))
+                return
+            try:
+                log(summary(extra[name]))
+            except Exception:                            # noqa: BLE001
+                log("%s done" % name)
+
+        if not args.no_prefill:
+            log("prefill indexer (32768^2) ...")
+            section("prefill", lambda: run_section("prefill", args),
+                    lambda p: "prefill %.1f us = %.0f TFLOP/s (%.1f%% of fp8 peak), top-k rows %.1f us"
+                    % (p["us_per_launch"], p["achieved"], 100 * p["frac"], p["topk_rows_us"]))
+            log("chunked prefill with offload and inter-query prefetch ...")
+            section("prefill_offload", lambda: run_section("prefill_offload", args),
+                    lambda p: "chunked prefill: threshold bin median %d shifted vs %d unshifted"
+                    % (p["thr_bin_median_shifted"], p["thr_bin_median_unshifted"]))
+        if not args.no_loop:
+            log("decode loop (EMA threshold, new tokens every step) ...")
+            section("loop", lambda: run_section("loop", args),
+                    lambda p: "loop: median %.1f us/step, hit rate %.3f"
+                    % (p["us_per_step_median"], p["hit_rate_median"]))
+        if not args.no_prefetch_modes:
+            log("prefetch off / ranged / fused on one starting pool ...")
+            section("prefetch_modes", lambda: run_section("prefetch_modes", args),
+                    lambda p: "prefetch modes: off %.1f, ranged %.1f, fused %.1f us/step; fused "
+                    "launches alone %.1f us vs plain scoring %.1f us" % (
+                        p["off"]["us_per_step"], p["ranged"]["us_per_step"], p["fused"]["us_per_step"],
+                        p["fused_launches_alone"]["us_median"], p["fused_launches_alone"]["plain_scoring_us"]))
+        out.update(extra)
+        print(json.dumps(out), flush=True)
+        return
+
+    import torch
+    from dsa_indexer_top_amd import binding as B, inputs as gen
+    from dsa_indexer_top_amd.runner import DecodeRunner
+
+    if args.probe == "copy":
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(20):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy probe: 20 x 256 MiB device copies")
+        return
+    cfg = gen.CONFIGS[args.workload]
+    prefetch = (cfg.prefetch if args.prefetch == "auto" else
+                {"on": "ranged", "off": False}.get(args.prefetch, args.prefetch))
+    if args.section:
+        try:
+            if args.section == "headline":
+                res = headline(args, torch, B, gen, DecodeRunner, cfg, prefetch)
+            else:
+                res = child_section(args.section, args, torch, B, gen)
+            torch.cuda.synchronize()
+        except Exception as e:                       # noqa: BLE001
+            res = {"error": "%s: %s" % (type(e).__name__, e)}
+        print(json.dumps(res), flush=True)
+        return
+    if args.probe == "prefill":
+        pc = gen.PREFILL["prefill_32k"]
+        n = pc["n"]
+        q, w, k = gen.make_prefill_inputs(n, seed=pc["seed"])
+        dq, dw, dk = (torch.from_numpy(x).cuda() for x in (q, w, k))
+        sc = torch.empty((n, n), dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            B.index_scores_prefill(dq, dw, dk, sc, ld=n)
+        torch.cuda.synchronize()
+        log("prefill probe: 3 launches of echo_index_scores_prefill on 32768 x 32768")
+        return
+    if args.probe == "score":
+        inp = gen.make_decode_inputs(cfg)
+        dq, dw, dk = (torch.from_numpy(x).cuda() for x in (inp.q, inp.w, inp.k))
+        dks = None if inp.k_scale is None else torch.from_numpy(inp.k_scale).cuda()
+        dkb, dkl = torch.from_numpy(inp.key_begin).cuda(), torch.from_numpy(inp.key_len).cuda()
+        max_len = int(inp.key_len.max())
+        sc = torch.empty((len(inp.key_len), max_len), dtype=torch.float32, device="cuda")
+        for _ in range(20):
+            B.index_scores(dq, dw, dk, dks, dkb, dkl, max_len, sc)
+        torch.cuda.synchronize()
+        log("score probe: 20 launches of echo_index_scores on", args.workload)
+        return
+    raise SystemExit("bench.py: unknown --probe")
 
 if __name__ == "__main__":
     main()
