@@ -15,8 +15,10 @@
 //                  indices up in HostTokenToGPU; a period later claim places for the
 //                  non-resident ones from the request's counter; a period later read the
 //                  claimed places' slots from the free-slot list; a period later set both maps
-//                  and priority 0 and queue the rows.  Every period it starts reading one queued
-//                  row from mapped host memory and stores the row it started the period before.
+//                  and priority 0 and queue the rows.  While the scoring runs, every period it
+//                  starts reading one queued row from mapped host memory and stores the row it
+//                  started the period before; after the last chunk it finishes the pipeline and
+//                  copies the rows still queued eight at a time.
 // The gather wave meets the scoring waves only at the chunk barriers.  A gfx950 workgroup
 // barrier waits for LDS traffic only, so its host reads stay in flight across barriers: the
 // scoring waves wait for the host link only when a read is still outstanding a whole chunk
@@ -48,6 +50,8 @@ constexpr int FZ_CHUNK = 128;                           // tokens per LDS stage
 constexpr int FZ_LOADS = FZ_CHUNK * D / 16 / FZ_ST;     // 16-byte loads per scoring thread = 4
 constexpr int FZ_MAXW = ECHO_FUSED_MAX_PER_RANGE;       // rows per range at most (128)
 constexpr int FZ_UNITS = ROW * 2 / 16;                  // 16-byte units per latent row = 72
+constexpr int FZ_DRAIN = 8;                             // rows per batch once the scoring is over
+constexpr int FZ_DRAIN_UNITS = (FZ_DRAIN * FZ_UNITS + 63) / 64;   // 16-byte units per lane = 9
 static_assert(FZ_CHUNK <= 128, "a chunk's queue is two entries per lane of the gather wave");
 static_assert(FZ_UNITS <= 128, "a row is two 16-byte units per lane of the gather wave");
 
@@ -274,9 +278,9 @@ __global__ __launch_bounds__(FZ_THREADS) void score_fused_kernel(
       wanted += want;
       demand += nq;
     }
-    // copy: start reading the next queued row
+    // copy: while the scoring runs, start reading the next queued row
     cslot[p] = -1;
-    if (rd < ready) {
+    if (w <= n_ch && rd < ready) {
       const int32_t h = ring_h[rd];
       cslot[p] = ring_s[rd];
       ++rd;
@@ -326,16 +330,32 @@ __global__ __launch_bounds__(FZ_THREADS) void score_fused_kernel(
       cslot[p ^ 1] = -1;
     }
   };
-  // Periods 0 .. n_ch - 1 follow the chunk barriers, period n_ch the final one; the later
-  // periods drain the pipeline without barriers.  Ends after at most n_ch + 5 + FZ_MAXW + 1
-  // periods (one queued row is started per period).
+  // Periods 0 .. n_ch - 1 follow the chunk barriers, period n_ch the final one; periods
+  // n_ch + 1 .. n_ch + 4 finish the pipeline without barriers (and start no more single rows).
   for (int32_t w = 0;; w += 2) {
     if (w <= n_ch) __syncthreads();
     period(FzParity<0>{}, w);
-    if (w >= n_ch + 4 && rd >= ready && cslot[0] < 0) break;
+    if (w >= n_ch + 4) break;
     if (w + 1 <= n_ch) __syncthreads();
     period(FzParity<1>{}, w + 1);
-    if (w + 1 >= n_ch + 4 && rd >= ready && cslot[1] < 0) break;
+    if (w + 1 >= n_ch + 4) break;
+  }
+  // The scoring is over: the rows still queued go FZ_DRAIN at a time, all reads in flight
+  // before the first store.
+  for (int32_t b0 = rd; b0 < ready; b0 += FZ_DRAIN) {
+    const int32_t nb = ready - b0 < FZ_DRAIN ? ready - b0 : FZ_DRAIN;
+    v4i v[FZ_DRAIN_UNITS];
+#pragma unroll
+    for (int m = 0; m < FZ_DRAIN_UNITS; ++m) {
+      const int u = l + 64 * m, row = u / FZ_UNITS;
+      if (row < nb)
+        v[m] = __builtin_nontemporal_load(src + static_cast<int64_t>(ring_h[b0 + row]) * FZ_UNITS + u % FZ_UNITS);
+    }
+#pragma unroll
+    for (int m = 0; m < FZ_DRAIN_UNITS; ++m) {
+      const int u = l + 64 * m, row = u / FZ_UNITS;
+      if (row < nb) dst[static_cast<int64_t>(ring_s[b0 + row]) * FZ_UNITS + u % FZ_UNITS] = v[m];
+    }
   }
   if (l == 0) {
     if (demand) atomicAdd(&F.demand[r], demand);
