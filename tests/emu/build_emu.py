@@ -146,7 +146,10 @@ def build(csrc=None, include=None, out=DEFAULT_OUT, sanitizer="address"):
     flags = ["-std=c++17", "-g", "-O1", "-fPIC", "-fno-omit-frame-pointer", "-Wno-unused-variable",
              "-I", cdir]
     if sanitizer == "address":
-        kflags, rflags = ["-fsanitize=address"], ["-fsanitize=address", "-DEMU_ASAN"]
+        # the kernels also under the alignment check: a vector access at an address that is not
+        # a multiple of its size faults on the GPU
+        kflags = ["-fsanitize=address,alignment", "-fno-sanitize-recover=alignment"]
+        rflags = ["-fsanitize=address", "-DEMU_ASAN"]
     elif sanitizer == "thread":
         kflags, rflags = ["-fsanitize=thread"], ["-DEMU_TSAN"]
     else:
@@ -164,7 +167,8 @@ def build(csrc=None, include=None, out=DEFAULT_OUT, sanitizer="address"):
     with cf.ThreadPoolExecutor(max_workers=min(8, len(units))) as ex:
         objs = list(ex.map(compile_one, units))
     lib = os.path.join(out, LIB_NAME)
-    r = subprocess.run([CLANG, "-shared", "-fsanitize=" + sanitizer, "-shared-libsan", "-o", lib, *objs],
+    link_san = "address,alignment" if sanitizer == "address" else sanitizer
+    r = subprocess.run([CLANG, "-shared", "-fsanitize=" + link_san, "-shared-libsan", "-o", lib, *objs],
                        capture_output=True, text=True)
     if r.returncode:
         raise RuntimeError("emulation link failed:\n%s" % r.stderr[-4000:])

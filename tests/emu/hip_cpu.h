@@ -35,10 +35,12 @@ struct dim3 {
   uint32_t x, y, z;
   constexpr dim3(uint32_t a = 1, uint32_t b = 1, uint32_t c = 1) : x(a), y(b), z(c) {}
 };
-struct int4 { int x, y, z, w; };
-struct uint4 { unsigned x, y, z, w; };
-struct float4 { float x, y, z, w; };
-struct int2 { int x, y; };
+// HIP's vector types are aligned to their size; so are these, so that the alignment check of
+// the emulation build sees a misaligned 16-byte access as the GPU would
+struct __attribute__((aligned(16))) int4 { int x, y, z, w; };
+struct __attribute__((aligned(16))) uint4 { unsigned x, y, z, w; };
+struct __attribute__((aligned(16))) float4 { float x, y, z, w; };
+struct __attribute__((aligned(8))) int2 { int x, y; };
 
 typedef int v8i_emu __attribute__((ext_vector_type(8)));
 typedef float v4f_emu __attribute__((ext_vector_type(4)));
