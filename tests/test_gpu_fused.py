@@ -104,6 +104,35 @@ def test_fused_prefetch_exact(case):
         P.hostbuf.close()
 
 
+def test_fused_prefetch_automatic_range():
+    # range = 0 lets the library pick the ranges; with at most 128 qualifying tokens per request
+    # no range can have more than 128 candidates, so the outcome does not depend on the ranges
+    # and the oracle's with one range per request is the reference
+    lens = [3000, 5000, 129, 0]
+    announce("fused prefetch, automatic range", lens)
+    cfg = gen.DecodeConfig("fza", len(lens), 0, 64, "int", False, 0.5, 1, seed=340)
+    inp = gen.make_decode_inputs(cfg, lengths=lens)
+    st, host_kv = _pool_case(inp, 340, 4000, 0.5, 0.3)
+    scores = oracle.index_scores(inp.q, inp.w, inp.k, None, inp.key_begin, inp.key_len)
+    theta = _thetas(scores, 0.98, {})
+    want, moved, demand, info = oracle.range_prefetch(scores, theta, inp.key_begin, inp.key_len,
+                                                      inp.req_to_host, st, host_kv, 200, 16,
+                                                      max(lens))
+    assert all(len(q) <= 128 for c in info["cand"] for q in c.values())
+    got_sc, got_st, npf, dem, P = _run_standalone(inp, st, host_kv, theta, 200, 16, 0)
+    try:
+        for r, s_ in enumerate(scores):
+            assert np.array_equal(got_sc[r, :len(s_)].astype(np.float64), s_), "scores row %d" % r
+        assert npf == len(moved) > 0 and dem == int(demand.sum())
+        # every candidate fits its cap: the moved set is the oracle's; the slots within the
+        # request's places follow the library's own ranges
+        assert all(sum(map(len, c.values())) <= cr for c, cr in zip(info["cand"], info["cap"]))
+        oracle.check_prefetch_outcome(st, got_st, host_kv, inp.key_begin, inp.req_to_host, info,
+                                      slot_order=False)
+    finally:
+        P.hostbuf.close()
+
+
 def test_fused_prefetch_failed_pool_moves_nothing():
     announce("fused prefetch with the status set")
     cfg = gen.DecodeConfig("fz", 3, 0, 64, "int", False, 0.5, 1, seed=310)
