@@ -19,8 +19,9 @@ scale), topk (exact top-k, sample threshold), pool (the residency step),
 decode (one whole step), multistep (steps in a row: new tokens with
 write-through, the EMA threshold), interquery (the chunked prefill's
 approximate top-k subsets under the shifted histogram, and its unions),
-prefetch (the threshold prefetch over token ranges of a single scoring
-launch, and a whole step with it).
+prefetch (what the page fixes about the threshold prefetch: the eligible
+tokens, the bound in proportion to the context, the contract a prefetched pool
+satisfies, and one valid outcome).
 
 Readings of points the page leaves open are listed in each module's docstring.
 Parity status of every function is stated in its docstring ("pinned by ...").
@@ -36,8 +37,8 @@ from .decode import decode_step
 from .multistep import (KeyCache, ST_CACHE_FULL, append_tokens, kth_scores, ema_update,
                         decode_loop)
 from .interquery import approx_subset, union_segments, prefill_chunk_loop
-from .prefetch import (request_caps, prefetch_candidates, range_prefetch,
-                       check_prefetch_outcome, decode_step_prefetched)
+from .prefetch import (prefetch_eligible, prefetch_bound, apply_prefetch, greedy_prefetch,
+                       check_prefetch_contract)
 
 __all__ = [
     "E4M3FN_TABLE", "decode_e4m3fn", "index_scores", "error_scale",
@@ -46,6 +47,6 @@ __all__ = [
     "PoolState", "pool_step", "allocate_with_ranks", "metadata_bytes",
     "check_pool_invariants", "PoolInvariantError", "decode_step", "KeyCache",
     "ST_CACHE_FULL", "append_tokens", "kth_scores", "ema_update", "decode_loop",
-    "approx_subset", "union_segments", "prefill_chunk_loop", "request_caps",
-    "prefetch_candidates", "range_prefetch", "check_prefetch_outcome", "decode_step_prefetched",
+    "approx_subset", "union_segments", "prefill_chunk_loop", "prefetch_eligible",
+    "prefetch_bound", "apply_prefetch", "greedy_prefetch", "check_prefetch_contract",
 ]

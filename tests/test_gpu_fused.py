@@ -1,7 +1,10 @@
 """GPU parity of the scoring kernel with the host-gather wave (ECHO page §6.3; the threshold
-prefetch of §6.1 done inside the scoring launch) against the oracle's range prefetch
-(oracle/prefetch.py).  On integer-grid inputs the scores are bit-exact and the pool after the
-prefetch is a valid outcome (oracle.check_prefetch_outcome): the same demand, per request
+prefetch of §6.1 done inside the scoring launch).  Two checks on what moves: the page's
+contract (oracle.check_prefetch_contract: only eligible tokens, at most the bound per request,
+free slots, priority 0, rows equal to the host, nothing else touched) and, on top of it, the
+kernel's own documented policy (tests/prefetch_policy.py, check_policy_outcome).  On
+integer-grid inputs the scores are bit-exact and the pool after the prefetch is a valid outcome
+of that policy: the same demand, per request
 min(#candidates, cap) rows moved, each range's a token-order prefix of its candidates, into
 exactly the request's first places, maps, priorities and rows set, nothing else touched; when a
 request's candidates fit its cap, its moved set is the oracle's exactly.  Cases cover several
@@ -17,6 +20,7 @@ import pytest
 import torch
 
 import oracle
+import prefetch_policy as pol
 from dsa_indexer_top_amd import binding as B, inputs as gen
 from dsa_indexer_top_amd.runner import DecodeRunner
 from gpu_util import announce, dev, host, DevPool, assert_pool_equal
@@ -91,14 +95,16 @@ def test_fused_prefetch_exact(case):
     st, host_kv = _pool_case(inp, 300 + case, n_gpu, free_frac, 0.3)
     scores = oracle.index_scores(inp.q, inp.w, inp.k, None, inp.key_begin, inp.key_len)
     theta = _thetas(scores, qt, specials)
-    want, moved, demand, info = oracle.range_prefetch(scores, theta, inp.key_begin, inp.key_len,
-                                                      inp.req_to_host, st, host_kv, cap, cap_div, R)
+    want, moved, demand, info = pol.policy_prefetch(scores, theta, inp.key_begin, inp.key_len,
+                                                    inp.req_to_host, st, host_kv, cap, cap_div, R)
     got_sc, got_st, npf, dem, P = _run_standalone(inp, st, host_kv, theta, cap, cap_div, R)
     try:
         for r, s in enumerate(scores):
             assert np.array_equal(got_sc[r, :len(s)].astype(np.float64), s), "scores row %d" % r
         assert npf == len(moved) and dem == int(demand.sum())
-        oracle.check_prefetch_outcome(st, got_st, host_kv, inp.key_begin, inp.req_to_host, info)
+        oracle.check_prefetch_contract(st, got_st, host_kv, info["eligible"],
+                                       oracle.prefetch_bound(lens, cap, cap_div, n_gpu))
+        pol.check_policy_outcome(st, got_st, host_kv, info)
         assert (len(moved) > 0) == (free_frac > 0) and demand.sum() > 0
     finally:
         P.hostbuf.close()
@@ -115,10 +121,12 @@ def test_fused_prefetch_automatic_range():
     st, host_kv = _pool_case(inp, 340, 4000, 0.5, 0.3)
     scores = oracle.index_scores(inp.q, inp.w, inp.k, None, inp.key_begin, inp.key_len)
     theta = _thetas(scores, 0.98, {})
-    want, moved, demand, info = oracle.range_prefetch(scores, theta, inp.key_begin, inp.key_len,
-                                                      inp.req_to_host, st, host_kv, 200, 16,
-                                                      max(lens))
-    assert all(len(q) <= 128 for c in info["cand"] for q in c.values())
+    want, moved, demand, info = pol.policy_prefetch(scores, theta, inp.key_begin, inp.key_len,
+                                                    inp.req_to_host, st, host_kv, 200, 16,
+                                                    max(lens))
+    # the precondition: at most 128 eligible tokens per request, so no range of any length
+    # holds more than 128 candidates
+    assert int(demand.max()) <= 128
     got_sc, got_st, npf, dem, P = _run_standalone(inp, st, host_kv, theta, 200, 16, 0)
     try:
         for r, s_ in enumerate(scores):
@@ -127,8 +135,9 @@ def test_fused_prefetch_automatic_range():
         # every candidate fits its cap: the moved set is the oracle's; the slots within the
         # request's places follow the library's own ranges
         assert all(sum(map(len, c.values())) <= cr for c, cr in zip(info["cand"], info["cap"]))
-        oracle.check_prefetch_outcome(st, got_st, host_kv, inp.key_begin, inp.req_to_host, info,
-                                      slot_order=False)
+        oracle.check_prefetch_contract(st, got_st, host_kv, info["eligible"],
+                                       oracle.prefetch_bound(lens, 200, 16, 4000))
+        pol.check_policy_outcome(st, got_st, host_kv, info, slot_order=False)
     finally:
         P.hostbuf.close()
 
@@ -180,7 +189,13 @@ def test_fused_prefetch_general_fp8_properties():
             r, s = tok_of_host[int(got_st.to_host[sl])]
             assert got_st.priority[sl] == 0 and np.array_equal(got_st.gpu_kv[sl], host_kv[got_st.to_host[sl]])
             by_req.setdefault(r, []).append((s, int(sl)))
-        caps = oracle.request_caps(lens, cap, cap_div, len(free_list), len(st.free))[1]
+        gpu_scores = [got_sc[r, :lens[r]].astype(np.float64) for r in range(len(lens))]
+        oracle.check_prefetch_contract(
+            st, got_st, host_kv,
+            oracle.prefetch_eligible(gpu_scores, theta, inp.key_begin, inp.key_len,
+                                     inp.req_to_host, st),
+            oracle.prefetch_bound(lens, cap, cap_div, len(st.free)))
+        caps = pol.request_caps(lens, cap, cap_div, len(free_list), len(st.free))[1]
         offset, n_dem = 0, 0
         for r in range(len(lens)):
             L = lens[r]
@@ -259,7 +274,7 @@ def test_decode_step_fused(lens, k, R, div, reserve, given_theta):
         theta = np.array([oracle.sample_threshold(s, 4096, 95.0) for s in scores], np.float32)
     cap, cap_div = 2048, 8
     st0 = _oracle_state(pool)
-    _, want_idx, mid, moved, demand, info, want_state, res = oracle.decode_step_prefetched(
+    _, want_idx, mid, moved, demand, info, want_state, res = pol.decode_step_policy(
         inp.q, inp.w, inp.k, None, inp.key_begin, inp.key_len, inp.req_to_host, st0, host_kv, k,
         pool.step_id, theta, cap, cap_div, R)
     assert (len(moved) > 0) == (reserve > 0) and res.status == 0
