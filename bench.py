@@ -350,8 +350,8 @@ def prefetch_modes_measure(torch, B, gen, inp, hb, sel, reserve, steps=20, warmu
                 # the fused scoring launch alone, from the same starting pool every time
                 theta = torch.empty(rn.n_rows, dtype=torch.float32, device="cuda")
                 B.prefetch_threshold(rn.q, rn.w, rn.k, rn.k_scale, rn.key_begin, rn.key_len,
-                                     DEFAULT_PREFETCH["n_sample"], DEFAULT_PREFETCH["percentile"],
-                                     theta, stream=rn.main)
+                                     rn.max_len, DEFAULT_PREFETCH["n_sample"],
+                                     DEFAULT_PREFETCH["percentile"], theta, stream=rn.main)
                 npf = torch.zeros(1, dtype=torch.int32, device="cuda")
                 ws = torch.empty(B.fused_workspace_bytes(rn.n_rows, rn.n_gpu), dtype=torch.uint8,
                                  device="cuda")

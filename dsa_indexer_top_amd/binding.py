@@ -65,8 +65,8 @@ _SIGS = {
     "echo_status_clear": (C.c_int, [P, P]),
     "echo_index_scores": (C.c_int, [P, P, P, P, P, P, I32, I32, P, I64, P]),
     "echo_index_scores_prefetch": (C.c_int, [P, P, P, P, P, P, I32, I32, I32, I32, P, I64,
-                                             P, P, P, P, P, P, I32, I32, P]),
-    "echo_prefetch_threshold": (C.c_int, [P, P, P, P, P, P, I32, I32, F32, P, P]),
+                                             P, P, P, I32, P, P, P, I32, I32, P]),
+    "echo_prefetch_threshold": (C.c_int, [P, P, P, P, P, P, I32, I32, I32, F32, P, P]),
     "echo_fused_workspace_bytes": (SZ, [I32, I32]),
     "echo_index_scores_fused": (C.c_int, [P, P, P, P, P, P, I32, I32, P, I64, P, P,
                                           C.POINTER(Pool), I32, I32, I32, P, P, P, SZ, P]),
@@ -161,8 +161,8 @@ def index_scores_prefetch(q, w, k, k_scale, key_begin, key_len, max_key_len, tok
     ld = scores.shape[-1] if ld is None else ld
     _call("echo_index_scores_prefetch", ptr(q), ptr(w), ptr(k), ptr(k_scale), ptr(key_begin),
           ptr(key_len), q.shape[0], max_key_len, tok_lo, tok_hi, ptr(scores), ld, ptr(theta),
-          ptr(req_to_host), ptr(host_to_gpu), ptr(cand), ptr(cand_cnt), ptr(total_cnt), cap,
-          cap_div, stream_handle(stream))
+          ptr(req_to_host), ptr(host_to_gpu), host_to_gpu.shape[0], ptr(cand), ptr(cand_cnt),
+          ptr(total_cnt), cap, cap_div, stream_handle(stream))
 
 
 def fused_workspace_bytes(n_q, n_gpu):
@@ -202,10 +202,11 @@ def prefetch_gather(pool, key_begin, req_to_host, cand, cand_cnt, cap, free_list
           ptr(n_prefetched), stream_handle(stream))
 
 
-def prefetch_threshold(q, w, k, k_scale, key_begin, key_len, n_sample, percentile, theta,
-                       stream=None):
+def prefetch_threshold(q, w, k, k_scale, key_begin, key_len, max_key_len, n_sample, percentile,
+                       theta, stream=None):
     _call("echo_prefetch_threshold", ptr(q), ptr(w), ptr(k), ptr(k_scale), ptr(key_begin),
-          ptr(key_len), q.shape[0], n_sample, percentile, ptr(theta), stream_handle(stream))
+          ptr(key_len), q.shape[0], max_key_len, n_sample, percentile, ptr(theta),
+          stream_handle(stream))
 
 
 def index_scores_prefill(q, w, k, scores, q_pos0=0, ld=None, stream=None):

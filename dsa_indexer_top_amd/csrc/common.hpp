@@ -138,6 +138,33 @@ ECHO_DEV void group_excl_scan(const uint32_t (&cnt)[J], uint32_t (&base)[J], uin
   __syncthreads();
 }
 
+// Bin of the m-th smallest key in a 2048-bin histogram, the count below it and the bin's own
+// count.  NT threads.
+template <int NT>
+ECHO_DEV void pick2048(const uint32_t *hist, uint32_t m, uint32_t *tmp, uint32_t &bin, uint32_t &below,
+                       uint32_t &count) {
+  constexpr int PER = 2048 / NT;
+  const int t = threadIdx.x;
+  uint32_t v[PER], local = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) { v[i] = hist[t * PER + i]; local += v[i]; }
+  uint32_t total;
+  const uint32_t before = block_excl_scan<NT>(local, tmp, &total);
+  if (before < m && m <= before + local) {
+    uint32_t cum = before;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (cum < m && m <= cum + v[i]) { tmp[40] = t * PER + i; tmp[41] = cum; tmp[42] = v[i]; break; }
+      cum += v[i];
+    }
+  }
+  __syncthreads();
+  bin = tmp[40];
+  below = tmp[41];
+  count = tmp[42];
+  __syncthreads();
+}
+
 // LDS histogram add with the wave's most common bin peeled off first: the keys being
 // counted (top bits of scores, step-stamp priorities) concentrate in few bins, and
 // same-address LDS atomics within one instruction serialise.

@@ -143,7 +143,8 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
   const float *theta = a->theta_ema ? a->theta_ema : W.theta;
   if ((pf || fz) && !a->theta_ema &&
       (rc = launch_prefetch_threshold(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len,
-                                      a->n_rows, a->n_sample, a->percentile, W.theta, m)))
+                                      a->n_rows, a->max_key_len, a->n_sample, a->percentile,
+                                      W.theta, m)))
     return rc;
   if (fz) {
     const int32_t range = fused_range(static_cast<int64_t>(a->n_rows) * a->max_key_len, a->max_key_len,
@@ -167,7 +168,8 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
       const int32_t lo = c * span, hi = (c + 1 == nc) ? a->max_key_len : (c + 1) * span;
       PrefetchArgs P{theta, a->req_to_host, pool->host_to_gpu,
                      W.cand + static_cast<int64_t>(c) * a->n_rows * a->cap,
-                     W.cand_cnt + static_cast<int64_t>(c) * a->n_rows, W.total_cnt, a->cap, a->cap_div};
+                     W.cand_cnt + static_cast<int64_t>(c) * a->n_rows, W.total_cnt, a->cap, a->cap_div,
+                     pool->n_host};
       if ((rc = launch_score_decode(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len, a->n_rows,
                                     a->max_key_len, lo, hi, o->scores, a->max_key_len, &P, W.hist0,
                                     &side, m)))

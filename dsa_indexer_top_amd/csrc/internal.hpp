@@ -23,6 +23,7 @@ struct PrefetchArgs {
   int32_t *total_cnt;        // [n_q] over-threshold non-resident tokens of the step so far
   int32_t cap;
   int32_t cap_div;
+  int32_t n_host;            // host indices outside [0, n_host) never qualify
 };
 
 struct PoolArgs {
@@ -168,8 +169,8 @@ int launch_recall_scatter(const echo_pool *pool, const PoolFastWs &W, const int3
 
 int launch_prefetch_threshold(const uint8_t *q, const float *w, const uint8_t *k,
                               const float *k_scale, const int64_t *key_begin,
-                              const int32_t *key_len, int32_t n_q, int32_t n_sample,
-                              float percentile, float *theta, hipStream_t st);
+                              const int32_t *key_len, int32_t n_q, int32_t max_len,
+                              int32_t n_sample, float percentile, float *theta, hipStream_t st);
 int launch_prefetch_begin(const echo_pool *pool, int32_t *free_list, int32_t *free_count,
                           hipStream_t st);
 // pw (optional): pool-step statistics (free count, priority histograms) updated for the slots

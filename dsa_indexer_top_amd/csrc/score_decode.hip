@@ -15,7 +15,9 @@
 //
 // Prefetch candidates: each call appends to its own list (cand, cand_cnt), so a later kernel
 // sees a complete list; the per-request cap is a counter shared by all calls of one step
-// (total_cnt).
+// (total_cnt).  A workgroup collects its qualifying tokens in LDS (one LDS atomic per wave and
+// chunk) and publishes them at its end with at most two global atomics, so the step's counters
+// see one update per workgroup instead of one per token.
 //
 // Side work (SIDE): the launch may carry extra leading workgroups that do independent pool
 // work (priority statistics, a previous range's prefetch gather) while the scoring workgroups
@@ -35,6 +37,7 @@ constexpr int SD_LOADS = SD_UNITS / SD_THREADS;                  // per thread p
 ECHO_DEV int swz(int tok, int seg) { return tok * 128 + ((seg ^ ((tok >> 1) & 7)) << 4); }
 
 constexpr int SD_SCORE_WORDS = 2 * SD_CHUNK * D / 4;               // the LDS double buffer
+constexpr int SD_PF_LIST = 128;          // qualifying tokens a workgroup lists, at most
 
 template <bool HAS_SCALE, bool PREFETCH, bool HIST, bool SIDE>
 __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
@@ -46,6 +49,7 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
   constexpr int WORDS = SD_SCORE_WORDS + (HIST ? 2048 : 0);
   constexpr int ALL = SIDE && SIDE_LDS_WORDS > WORDS ? SIDE_LDS_WORDS : WORDS;
   __shared__ __attribute__((aligned(16))) uint32_t smem[ALL];
+  __shared__ int32_t pf_list[PREFETCH ? SD_PF_LIST + 2 : 1];   // tokens, then count and base
   int b = blockIdx.x;
   if constexpr (SIDE) {
     if (side_work(side, b, smem)) return;
@@ -92,6 +96,8 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
 
   if constexpr (HIST)
     for (int b = threadIdx.x; b < 2048; b += SD_THREADS) hl[b] = 0;   // ordered by the first barrier
+  if constexpr (PREFETCH)
+    if (threadIdx.x == 0) pf_list[SD_PF_LIST] = 0;                    // ordered by the first barrier
   fetch(t_begin);
   int buf = 0;
   for (int32_t c0 = t_begin; c0 < t_end; c0 += SD_CHUNK) {
@@ -115,29 +121,56 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
     const int32_t t_out = c0 + wv * 32 + g * 16 + j;
     const bool writer = g < 2 && t_out < t_end;
     float s_out = (g == 0) ? part[0] : part[1];
+    bool qual = false;
     if (writer) {
       if constexpr (HAS_SCALE) s_out *= k_scale[kb + t_out];
       srow[t_out] = s_out;
       if constexpr (PREFETCH) {
         if (s_out > theta) {
           const int32_t h = pf.req_to_host[kb + t_out];
-          if (pf.host_to_gpu[h] == INF) {
-            if (atomicAdd(&pf.total_cnt[r], 1) < cap_r) {
-              const int32_t pos = atomicAdd(&pf.cand_cnt[r], 1);
-              pf.cand[static_cast<int64_t>(r) * pf.cap + pos] = t_out;
-            }
-          }
+          qual = h >= 0 && h < pf.n_host && pf.host_to_gpu[h] == INF;
         }
+      }
+    }
+    if constexpr (PREFETCH) {
+      // the wave's qualifying tokens take consecutive places of the workgroup's LDS list
+      const uint64_t mq = __ballot(qual);
+      if (mq) {
+        const int lead = __ffsll(static_cast<unsigned long long>(mq)) - 1;
+        int32_t base = 0;
+        if (l == lead) base = atomicAdd(&pf_list[SD_PF_LIST], static_cast<int32_t>(__popcll(mq)));
+        base = __builtin_amdgcn_readlane(base, lead);
+        const int at = base + static_cast<int>(__popcll(mq & ((1ull << l) - 1ull)));
+        if (qual && at < SD_PF_LIST) pf_list[at] = t_out;
       }
     }
     if constexpr (HIST) hist_add_peeled(hl, (~f32_key(s_out)) >> 21, writer);
     buf ^= 1;
   }
+  if constexpr (HIST || PREFETCH) __syncthreads();
   if constexpr (HIST) {
-    __syncthreads();
     uint32_t *gh = hist0 + static_cast<int64_t>(r) * 2048;
     for (int b = threadIdx.x; b < 2048; b += SD_THREADS)
       if (hl[b]) atomicAdd(&gh[b], hl[b]);
+  }
+  if constexpr (PREFETCH) {
+    // every qualifying token counts towards the request's demand (total_cnt); the workgroup
+    // lists as many of its listed ones as the cap still allows
+    if (threadIdx.x == 0) {
+      const int32_t n_q = pf_list[SD_PF_LIST];
+      int32_t take = 0, pos = 0;
+      if (n_q > 0) {
+        const int32_t before = atomicAdd(&pf.total_cnt[r], n_q);
+        take = max(0, min(min(n_q, SD_PF_LIST), cap_r - before));
+        if (take > 0) pos = atomicAdd(&pf.cand_cnt[r], take);
+      }
+      pf_list[SD_PF_LIST] = take;
+      pf_list[SD_PF_LIST + 1] = pos;
+    }
+    __syncthreads();
+    const int32_t take = pf_list[SD_PF_LIST], pos = pf_list[SD_PF_LIST + 1];
+    for (int i = threadIdx.x; i < take; i += SD_THREADS)
+      pf.cand[static_cast<int64_t>(r) * pf.cap + pos + i] = pf_list[i];
   }
 }
 
@@ -215,8 +248,9 @@ extern "C" int echo_index_scores_prefetch(const uint8_t *q, const float *w, cons
                                           int32_t max_key_len, int32_t tok_lo, int32_t tok_hi,
                                           float *scores, int64_t ld, const float *theta,
                                           const int32_t *req_to_host, const int32_t *host_to_gpu,
-                                          int32_t *cand, int32_t *cand_cnt, int32_t *total_cnt,
-                                          int32_t cap, int32_t cap_div, void *stream) {
+                                          int32_t n_host, int32_t *cand, int32_t *cand_cnt,
+                                          int32_t *total_cnt, int32_t cap, int32_t cap_div,
+                                          void *stream) {
   if (n_q < 0 || max_key_len < 0) return fail(ECHO_EINVAL, "echo_index_scores_prefetch: negative n_q or max_key_len");
   if (ld < max_key_len) return fail(ECHO_EINVAL, "echo_index_scores_prefetch: ld < max_key_len");
   if (n_q > 65535) return fail(ECHO_EUNSUPPORTED, "echo_index_scores_prefetch: n_q > 65535");
@@ -225,7 +259,8 @@ extern "C" int echo_index_scores_prefetch(const uint8_t *q, const float *w, cons
   if (n_q > 0 && (!q || !w || !key_begin || !key_len || !scores || !theta || !req_to_host ||
                   !host_to_gpu || !cand_cnt || !total_cnt || (cap > 0 && !cand) || (max_key_len > 0 && !k)))
     return fail(ECHO_EINVAL, "echo_index_scores_prefetch: NULL pointer");
-  PrefetchArgs pf{theta, req_to_host, host_to_gpu, cand, cand_cnt, total_cnt, cap, cap_div};
+  if (n_host < 0) return fail(ECHO_EINVAL, "echo_index_scores_prefetch: n_host < 0");
+  PrefetchArgs pf{theta, req_to_host, host_to_gpu, cand, cand_cnt, total_cnt, cap, cap_div, n_host};
   return launch_score_decode(q, w, k, k_scale, key_begin, key_len, n_q, max_key_len, tok_lo,
                              tok_hi, scores, ld, &pf, nullptr, nullptr, S(stream));
 }

@@ -38,6 +38,14 @@ constexpr int TS_HW = 2048;                      // LDS histogram window of a sp
 
 ECHO_DEV uint32_t score_key(float x) { return ~f32_key(x); }   // ascending key = descending score
 
+// Staging row named by an early-lookup code (-2 - row), or -1 when the code names none or a row
+// outside the staging area [0, n_stage).  Computed in 64 bits, so no code value overflows.
+ECHO_DEV int32_t staged_row(int32_t code, int64_t n_stage) {
+  if (code > -2) return -1;
+  const int64_t row = -2 - static_cast<int64_t>(code);
+  return row < n_stage ? static_cast<int32_t>(row) : -1;
+}
+
 // keys of elements i0 .. i0+3 of a row (bit e of `valid` marks presence)
 ECHO_DEV void row_load4(const float *row, bool vec, int32_t n, int32_t i0, uint32_t key[4], int &valid) {
   valid = 0;
@@ -52,33 +60,6 @@ ECHO_DEV void row_load4(const float *row, bool vec, int32_t n, int32_t i0, uint3
     key[e] = 0xFFFFFFFFu;
     if (i0 + e < n) { key[e] = score_key(row[i0 + e]); valid |= 1 << e; }
   }
-}
-
-// Bin of the m-th smallest key in a 2048-bin histogram, the count below it and the bin's own
-// count.  NT threads.
-template <int NT>
-ECHO_DEV void pick2048(const uint32_t *hist, uint32_t m, uint32_t *tmp, uint32_t &bin, uint32_t &below,
-                       uint32_t &count) {
-  constexpr int PER = 2048 / NT;
-  const int t = threadIdx.x;
-  uint32_t v[PER], local = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) { v[i] = hist[t * PER + i]; local += v[i]; }
-  uint32_t total;
-  const uint32_t before = block_excl_scan<NT>(local, tmp, &total);
-  if (before < m && m <= before + local) {
-    uint32_t cum = before;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (cum < m && m <= cum + v[i]) { tmp[40] = t * PER + i; tmp[41] = cum; tmp[42] = v[i]; break; }
-      cum += v[i];
-    }
-  }
-  __syncthreads();
-  bin = tmp[40];
-  below = tmp[41];
-  count = tmp[42];
-  __syncthreads();
 }
 
 template <int NT>
@@ -481,8 +462,9 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
   const int64_t kb = key_begin[r];
   const uint32_t sa = early ? PW.stage_a[r] : 0u;
   constexpr int LJ = ECHO_MAX_TOPK / TF_T;          // entries per thread: j = t + TF_T * i
-  int32_t h[LJ], slot[LJ], res[LJ], srow[LJ], code[LJ];
+  int32_t h[LJ], slot[LJ], res[LJ], srow[LJ], code[LJ], early_row[LJ];
   bool cand[LJ], hit[LJ];
+  const int64_t n_stage = static_cast<int64_t>(n_rows) * k;
   // a sure selection carries the split's result; the others are looked up here
 #pragma unroll
   for (int i = 0; i < LJ; ++i) {
@@ -499,7 +481,8 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
 #pragma unroll
   for (int i = 0; i < LJ; ++i) {
     const int32_t j = t + TF_T * i;
-    h[i] = cand[i] ? req_to_host[kb + fin[j]] : (code[i] <= -2 ? PW.stage_h[-2 - code[i]] : -1);
+    early_row[i] = staged_row(code[i], n_stage);
+    h[i] = cand[i] ? req_to_host[kb + fin[j]] : (early_row[i] >= 0 ? PW.stage_h[early_row[i]] : -1);
   }
 #pragma unroll
   for (int i = 0; i < LJ; ++i)
@@ -518,7 +501,8 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
       else { hit[i] = true; res[i] = slot[i]; }
     } else if (j < m) {
       if (code[i] >= 0) res[i] = code[i];                        // hit, protected by the split
-      else if (code[i] <= -2) { res[i] = INF; srow[i] = -2 - code[i]; }   // miss, already queued
+      else if (early_row[i] >= 0) { res[i] = INF; srow[i] = early_row[i]; }   // miss, already queued
+      else if (code[i] <= -2) bad = true;                         // no such staging row
     }
   }
   if (bad) atomicOr(P.status, ECHO_ST_BAD_HOST);

@@ -139,14 +139,17 @@ int echo_index_scores(const uint8_t *q, const float *w, const uint8_t *k, const 
 
 /*
  * Threshold prefetch fused into scoring (§6.1).  Scores tokens [tok_lo, tok_hi) of every
- * request exactly as echo_index_scores does, and in addition appends every scored token s with
- * score > theta[r] that is not resident (host_to_gpu[req_to_host[key_begin[r] + s]] ==
- * ECHO_INF) to this call's list cand[r*cap + j], j < cand_cnt[r], as long as the step-wide
- * per-request counter total_cnt[r] is below cap_r = min(cap, ceil(key_len[r] / cap_div)) (the
- * page's global prefetch counter, bounded in proportion to the context length).  total_cnt
- * keeps counting past the cap (it reports demand).  Which over-threshold tokens win the slots
- * depends on timing; the scores never do.  Because each call has its own list, a consumer on
- * another stream that waits for this call sees a complete list (echo_prefetch_gather).
+ * request exactly as echo_index_scores does, and in addition lists scored tokens s with
+ * score > theta[r] whose host index h = req_to_host[key_begin[r] + s] lies in [0, n_host) and is
+ * not resident (host_to_gpu[h] == ECHO_INF) in this call's list cand[r*cap + j],
+ * j < cand_cnt[r].  Every such token counts in the step-wide per-request counter total_cnt[r]
+ * (the demand); listed tokens are bounded by cap_r = min(cap, ceil(key_len[r] / cap_div)) over
+ * the step (the page's global prefetch counter, bounded in proportion to the context length).
+ * Each workgroup (a run of up to 8192 tokens of one request) collects its qualifying tokens and,
+ * at its end, adds their number to total_cnt[r] and lists the first min(128, that number,
+ * cap_r - the counter before it) it found.  Which qualifying tokens are listed depends on timing;
+ * the scores never do.  Because each call has its own list, a consumer that waits for this call
+ * sees a complete list (echo_prefetch_gather).
  *   theta [n_q] fp32; req_to_host [n_k] int32; host_to_gpu [n_host]; cand [n_q, cap] int32;
  *   cand_cnt [n_q] (zeroed by the caller before this call); total_cnt [n_q] (zeroed once per
  *   step).
@@ -156,8 +159,9 @@ int echo_index_scores_prefetch(const uint8_t *q, const float *w, const uint8_t *
                                const int32_t *key_len, int32_t n_q, int32_t max_key_len,
                                int32_t tok_lo, int32_t tok_hi, float *scores, int64_t ld,
                                const float *theta, const int32_t *req_to_host,
-                               const int32_t *host_to_gpu, int32_t *cand, int32_t *cand_cnt,
-                               int32_t *total_cnt, int32_t cap, int32_t cap_div, void *stream);
+                               const int32_t *host_to_gpu, int32_t n_host, int32_t *cand,
+                               int32_t *cand_cnt, int32_t *total_cnt, int32_t cap,
+                               int32_t cap_div, void *stream);
 
 /*
  * Scoring and threshold prefetch in one kernel (§6.3, with the §6.1 threshold and the §5.2
@@ -199,15 +203,18 @@ int echo_index_scores_fused(const uint8_t *q, const float *w, const uint8_t *k,
 
 /*
  * Per-request prefetch threshold: theta[r] = the nearest-rank `percentile` of the scores of
- * request r at the n_sample positions floor(i * key_len[r] / n_sample), i < n_sample
- * (the stand-in for the page's per-layer EMA prediction of the k-th score, §6.1, on a single
- * step with no history).  theta[r] = +inf when key_len[r] == 0.  n_sample must be a power of
- * two in [64, 4096].  Computes the sampled scores itself from q, w, k, k_scale.
+ * request r at the n_sample positions floor(i * L_r / n_sample), i < n_sample, with
+ * L_r = min(key_len[r], max_key_len) (the stand-in for the page's per-layer EMA prediction of
+ * the k-th score, §6.1, on a single step with no history).  theta[r] = +inf when L_r <= 0.
+ * n_sample must be a power of two in [64, 4096].  Computes the sampled scores itself from q, w,
+ * k, k_scale (as echo_index_scores does).  Errors: EINVAL for negative n_q or max_key_len, a
+ * percentile outside (0, 100] or NULL pointers; EUNSUPPORTED for n_sample outside the range or
+ * n_q > 65535.
  */
 int echo_prefetch_threshold(const uint8_t *q, const float *w, const uint8_t *k,
                             const float *k_scale, const int64_t *key_begin,
-                            const int32_t *key_len, int32_t n_q, int32_t n_sample,
-                            float percentile, float *theta, void *stream);
+                            const int32_t *key_len, int32_t n_q, int32_t max_key_len,
+                            int32_t n_sample, float percentile, float *theta, void *stream);
 
 /*
  * Prefill (causal) indexer scores (§3.4: quadratic in the context).  Query rows t in

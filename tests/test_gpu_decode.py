@@ -195,7 +195,7 @@ def test_prefetch_threshold_matches_sample_percentile():
         theta = torch.empty(4, dtype=torch.float32, device="cuda")
         B.prefetch_threshold(dev(inp.q), dev(inp.w), dev(inp.k),
                              None if inp.k_scale is None else dev(inp.k_scale),
-                             dev(inp.key_begin), dev(inp.key_len), 4096, 95.0, theta)
+                             dev(inp.key_begin), dev(inp.key_len), max(lens), 4096, 95.0, theta)
         got = host(theta)
         scores = oracle.index_scores(inp.q, inp.w, inp.k, inp.k_scale, inp.key_begin, inp.key_len)
         for r in range(4):
@@ -206,6 +206,22 @@ def test_prefetch_threshold_matches_sample_percentile():
                 assert got[r] == want, (r, got[r], want)
             else:
                 assert abs(got[r] - want) <= 1e-3 * (abs(want) + 1), (r, got[r], want)
+        # lengths above max_key_len are clamped: the sample covers the first max_key_len keys
+        clamp = 3000
+        B.prefetch_threshold(dev(inp.q), dev(inp.w), dev(inp.k),
+                             None if inp.k_scale is None else dev(inp.k_scale),
+                             dev(inp.key_begin), dev(inp.key_len), clamp, 4096, 95.0, theta)
+        got = host(theta)
+        for r in range(4):
+            L = min(lens[r], clamp)
+            if L == 0:
+                assert np.isinf(got[r])
+                continue
+            want = oracle.sample_threshold(scores[r][:L], 4096, 95.0)
+            if grid == "int":
+                assert got[r] == want, ("clamped", r, got[r], want)
+            else:
+                assert abs(got[r] - want) <= 1e-3 * (abs(want) + 1), ("clamped", r, got[r], want)
 
 
 def test_fused_prefetch_scoring_candidates():
