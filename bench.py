@@ -51,7 +51,7 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(root, summary="profiles/score_decode_b8_64k_hbm_traffic.md"):
+def measured_traffic(root, summary="profiles/score_decode_hist_b8_64k_hbm_traffic.md"):
     """HBM bytes per scoring launch from the committed hardware-counter summary, or None when
     the summary is missing or the kernel sources changed since the counters were taken."""
     import hashlib
@@ -425,14 +425,99 @@ def cpu_baseline(inp, host_kv, pool_arrays, min_s=10.0, budget_s=30.0):
         sample = ("oracle decode step on requests 0..%d of the workload (%d tokens): scores in "
                   "float64, exact top-k, canonical pool step incl. recall copy" % (n - 1, tokens))
     else:
-        sample = ("%d repetitions of the whole oracle decode step on the workload (%d tokens "
-                  "each): scores in float64, exact top-k, canonical pool step incl. recall copy, "
-                  "from the same pool state" % (reps, tokens // reps))
+        sample = ("%d repetitions of the whole oracle decode step (%d tokens each, float64 "
+                  "scores, exact top-k, pool step with the recall copy)" % (reps, tokens // reps))
     return {"value": tokens / dt, "unit": "indexed tokens/s", "cores": int(cores),
-            "kind": "oracle", "seconds": round(dt, 3), "sample": sample}
+            "cpu_model": cpu_model(), "kind": "oracle", "seconds": round(dt, 3), "sample": sample}
 
 
-SECTIONS = ("headline", "prefill", "prefill_offload", "loop", "prefetch_modes")
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo) and its online core count."""
+    name = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                name = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return "%s (%d cores online)" % (name, os.cpu_count() or 0)
+
+
+SECTIONS = ("headline", "prefill", "prefill_offload", "loop", "prefetch_modes", "c3", "c5")
+# the other decode workloads of the metric's range, each reported by a section of its own
+SIDE_WORKLOADS = {"c3": "b32_ragged", "c5": "b64_128k"}
+
+
+def summarize_extra(extra):
+    """The secondary measurements as they go into the one JSON line: summaries only."""
+    out = {}
+    for name, val in extra.items():
+        if not isinstance(val, dict) or "error" in val:
+            out[name] = val
+        elif name == "loop":
+            out[name] = {k: val.get(k) for k in ("us_per_step_median", "hit_rate_median",
+                                                  "indexed_tokens_per_s")}
+            if "fused" in val:
+                out[name]["fused"] = {k: val["fused"].get(k) for k in
+                                      ("us_per_step_median", "hit_rate_median", "prefetched_median")}
+        elif name == "prefill_offload":
+            out[name] = {k: val.get(k) for k in ("pairs_per_s", "us_total", "thr_bin_median_shifted",
+                                                  "thr_bin_median_unshifted")}
+            if "subset_kernel" in val:
+                out[name]["subset_kernel_frac"] = val["subset_kernel"]["frac"]
+        elif name == "prefetch_modes":
+            out[name] = compact_modes(val)
+            if "fused_launches_alone" in val:
+                out[name]["fused_launches_alone_us"] = val["fused_launches_alone"]["us_median"]
+        else:
+            out[name] = val
+    return out
+
+
+def compact_decode(res):
+    """The figures of one decode-step measurement that the one JSON line carries."""
+    rl, rc, st = res["roofline"], res["recall"], res["step"]
+    return {"workload": res["config"]["workload"], "prefetch": res["config"]["prefetch"],
+            "us_per_step": res["breakdown_us"]["step"], "indexed_tokens_per_s": res["value"],
+            "step_hbm_frac": st["hbm_frac"], "scoring_us": rl["us_per_launch"],
+            "scoring_frac": rl["frac"], "scoring_floor_us": st["scoring_floor_us"],
+            "n_miss": res["counters"]["n_miss"], "prefetched": res["counters"]["prefetched"],
+            "recall_us": rc["us_per_launch"], "recall_gbs": rc["achieved"],
+            "link_gbs": rc["peak_measured_h2d"], "recall_frac_of_link": rc["frac"],
+            "link_floor_us": st["link_floor_us"], "memcpy_recall_us": rc["memcpy_baseline_us_median"]}
+
+
+def compact_modes(pm):
+    """Step time per prefetch mode (one starting pool), with the rows each moved."""
+    return {m: {"us": pm[m]["us_per_step"], "n_miss": pm[m]["n_miss"],
+                "prefetched": pm[m]["prefetched"]} for m in ("off", "ranged", "fused") if m in pm}
+
+
+def modes_for(workload, args, torch, B, gen):
+    """prefetch_modes_measure on the inputs of `workload`, its resident set drawn around the
+    selection."""
+    cfg = gen.CONFIGS[workload]
+    inp = gen.make_decode_inputs(cfg)
+    hb = B.HostBuffer(inp.n_host * 576 * 2)
+    try:
+        gen.fill_latent_rows(cfg.seed, hb.array.view(np.uint16).reshape(inp.n_host, 576))
+        n_rows, max_len = len(inp.key_len), int(inp.key_len.max())
+        dq, dw, dk = (torch.from_numpy(a).cuda() for a in (inp.q, inp.w, inp.k))
+        dks = None if inp.k_scale is None else torch.from_numpy(inp.k_scale).cuda()
+        dkb, dkl = torch.from_numpy(inp.key_begin).cuda(), torch.from_numpy(inp.key_len).cuda()
+        sc = torch.empty((n_rows, max_len), dtype=torch.float32, device="cuda")
+        sel = torch.empty((n_rows, cfg.topk), dtype=torch.int32, device="cuda")
+        tws = torch.empty(B.topk_workspace_bytes(n_rows, max_len), dtype=torch.uint8, device="cuda")
+        B.index_scores(dq, dw, dk, dks, dkb, dkl, max_len, sc)
+        B.topk(sc, dkl, max_len, cfg.topk, sel, tws)
+        sel_idx = sel.cpu().numpy()
+        del dq, dw, dk, dks, dkb, dkl, sc, sel, tws
+        reserve = args.reserve if args.reserve is not None else max(cfg.reserve, n_rows * cfg.topk)
+        return prefetch_modes_measure(torch, B, gen, inp, hb, sel_idx, reserve,
+                                      steps=min(args.steps, 20), warmup=min(args.warmup, 3))
+    finally:
+        hb.close()
 
 
 def run_section(name, args, timeout_s=900):
@@ -458,6 +543,7 @@ def run_section(name, args, timeout_s=900):
 
 def child_section(name, args, torch, B, gen):
     """--section NAME: the measurement alone, printed as one JSON object."""
+    import copy
     cpu = not args.no_cpu_baseline
     if name == "prefill":
         return prefill_measure(torch, B, gen)
@@ -465,27 +551,18 @@ def child_section(name, args, torch, B, gen):
         return prefill_offload_measure(torch, B, gen, cpu=cpu)
     if name == "loop":
         return loop_measure(torch, B, gen, cpu=cpu)
-    # prefetch_modes: the workload's own inputs, its resident set drawn around the selection
-    cfg = gen.CONFIGS[args.workload]
-    inp = gen.make_decode_inputs(cfg)
-    hb = B.HostBuffer(inp.n_host * 576 * 2)
-    try:
-        gen.fill_latent_rows(cfg.seed, hb.array.view(np.uint16).reshape(inp.n_host, 576))
-        n_rows, max_len = len(inp.key_len), int(inp.key_len.max())
-        dq, dw, dk = (torch.from_numpy(a).cuda() for a in (inp.q, inp.w, inp.k))
-        dks = None if inp.k_scale is None else torch.from_numpy(inp.k_scale).cuda()
-        dkb, dkl = torch.from_numpy(inp.key_begin).cuda(), torch.from_numpy(inp.key_len).cuda()
-        sc = torch.empty((n_rows, max_len), dtype=torch.float32, device="cuda")
-        sel = torch.empty((n_rows, cfg.topk), dtype=torch.int32, device="cuda")
-        tws = torch.empty(B.topk_workspace_bytes(n_rows, max_len), dtype=torch.uint8, device="cuda")
-        B.index_scores(dq, dw, dk, dks, dkb, dkl, max_len, sc)
-        B.topk(sc, dkl, max_len, cfg.topk, sel, tws)
-        sel_idx = sel.cpu().numpy()
-        del dq, dw, dk, dks, dkb, dkl, sc, sel, tws
-        reserve = args.reserve if args.reserve is not None else max(cfg.reserve, n_rows * cfg.topk)
-        return prefetch_modes_measure(torch, B, gen, inp, hb, sel_idx, reserve)
-    finally:
-        hb.close()
+    if name in SIDE_WORKLOADS:
+        from dsa_indexer_top_amd.runner import DecodeRunner
+        wl = SIDE_WORKLOADS[name]
+        a2 = copy.copy(args)
+        a2.workload, a2.no_cpu_baseline = wl, True
+        a2.steps, a2.warmup, a2.kernel_reps = min(args.steps, 10), min(args.warmup, 3), min(args.kernel_reps, 10)
+        cfg = gen.CONFIGS[wl]
+        out = compact_decode(headline(a2, torch, B, gen, DecodeRunner, cfg, cfg.prefetch))
+        if name == "c5":
+            out["prefetch_modes"] = compact_modes(modes_for(wl, a2, torch, B, gen))
+        return out
+    return modes_for(args.workload, args, torch, B, gen)
 
 
 def headline(args, torch, B, gen, DecodeRunner, cfg, prefetch):
@@ -545,6 +622,13 @@ def headline(args, torch, B, gen, DecodeRunner, cfg, prefetch):
     # ---- live kernel timings on the main stream (same launch configuration as the step)
     reps = args.kernel_reps
     score_bytes = tokens * 128 + (tokens * 4 if inp.k_scale is not None else 0)
+    # the step's own scoring launch: scores plus the top-k histogram (echo_index_scores_hist),
+    # the kernel the captured step runs for prefetch off
+    hist = torch.zeros((n_rows, 2048), dtype=torch.int32, device="cuda")
+    t_step_score = kernel_time_us(torch, main_s, lambda: B.index_scores_hist(
+        rn.q, rn.w, rn.k, rn.k_scale, rn.key_begin, rn.key_len, rn.max_len, rn.scores, hist,
+        stream=main_s), reps)
+    del hist
     t_score = kernel_time_us(torch, main_s, lambda: B.index_scores(
         rn.q, rn.w, rn.k, rn.k_scale, rn.key_begin, rn.key_len, rn.max_len, rn.scores,
         stream=main_s), reps)
@@ -569,10 +653,12 @@ def headline(args, torch, B, gen, DecodeRunner, cfg, prefetch):
         torch.cuda.synchronize()
         t_memcpy.append((time.perf_counter() - w0) * 1e6)
     link = measure_link_gbs(torch)
-    score_gbs = score_bytes / (t_score / 1e6) / 1e9
+    score_gbs = score_bytes / (t_step_score / 1e6) / 1e9
+    plain_gbs = score_bytes / (t_score / 1e6) / 1e9
     recall_gbs = recall_bytes / (t_recall / 1e6) / 1e9 if t_recall > 0 else 0.0
-    log("scoring %.1f us (%.0f GB/s), top-k %.1f us, recall %.1f us (%.1f GB/s of %.1f link)" % (
-        t_score, score_gbs, t_topk, t_recall, recall_gbs, link))
+    log("step scoring launch %.1f us (%.0f GB/s), plain scoring %.1f us (%.0f GB/s), top-k %.1f us, "
+        "recall %.1f us (%.1f GB/s of %.1f link)" % (t_step_score, score_gbs, t_score, plain_gbs,
+                                                     t_topk, t_recall, recall_gbs, link))
 
     out = {
         "metric": METRIC,
@@ -592,25 +678,32 @@ def headline(args, torch, B, gen, DecodeRunner, cfg, prefetch):
                    "n_host_slots": rn.n_host,
                    "prefetch": ("off", "ranged", "fused")[B.prefetch_mode(prefetch)],
                    "free_slots_at_start": int(pool.free.sum()),
-                   "timing": "HIP events around each graph replay on its stream; pool restored "
-                             "from a pristine copy between replays, outside the events"},
+                   "timing": "HIP events around each graph replay; pool restored between "
+                             "replays outside the events"},
         "roofline": {"bound": "hbm",
-                     "kernel": "score_decode_kernel<false, false, false, false> (echo_index_scores)",
+                     "kernel": "score_decode_kernel<%s, false, true, false> (the step's scoring "
+                               "launch, echo_index_scores_hist)" % str(inp.k_scale is not None).lower(),
                      "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(score_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(os.path.dirname(os.path.abspath(__file__)))
                      if args.workload == "b8_64k" else None,
-                     "bytes_per_launch": score_bytes, "us_per_launch": round(t_score, 2)},
+                     "bytes_per_launch": score_bytes, "us_per_launch": round(t_step_score, 2),
+                     "plain_scoring_us": round(t_score, 2)},
+        # hbm_frac: the step's key bytes / step time / 8 TB/s; link floor: the missed rows over
+        # the measured pinned H2D rate
+        "step": {"hbm_frac": round(score_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "link_floor_us": round(recall_bytes / (link * 1e3), 1) if link else None,
+                 "scoring_floor_us": round(score_bytes / (HBM_PEAK_GBS * 1e3), 1)},
         "recall": {"bound": "host link", "kernel": "recall_gather_kernel",
                    "achieved": round(recall_gbs, 2), "peak_measured_h2d": round(link, 2),
                    "unit": "GB/s", "frac": round(recall_gbs / link, 4) if link else None,
                    "rows": n_miss, "bytes_per_launch": recall_bytes,
                    "us_per_launch": round(t_recall, 2),
-                   "memcpy_baseline_us_median": round(float(np.median(t_memcpy)), 1),
-                   "memcpy_baseline": "host reads the miss list and issues one hipMemcpyAsync "
-                                      "per row; wall clock incl. the host sync"},
+                   # the host reads the miss list and issues one hipMemcpyAsync per row (wall
+                   # clock incl. the host sync)
+                   "memcpy_baseline_us_median": round(float(np.median(t_memcpy)), 1)},
         "breakdown_us": {"step": round(ms * 1e3, 2), "step_median": round(float(np.median(step_ms)) * 1e3, 2),
-                         "score": round(t_score, 2),
+                         "score_step_launch": round(t_step_score, 2), "score": round(t_score, 2),
                          "topk": round(t_topk, 2), "recall": round(t_recall, 2),
                          "wall_per_step_incl_restore": round(wall / args.steps * 1e6, 2)},
         "counters": {"n_miss": n_miss, "prefetch_demand": int(res["counters"][1]),
@@ -647,6 +740,8 @@ def main():
                     help="prefetch of the headline step (on = ranged)")
     ap.add_argument("--no-prefetch-modes", action="store_true",
                     help="skip the off / ranged / fused prefetch comparison")
+    ap.add_argument("--no-side-workloads", action="store_true",
+                    help="skip the ragged 32-request and the 64 x 128K decode steps")
     ap.add_argument("--section", choices=SECTIONS, default=None,
                     help="run one secondary measurement alone and print its JSON (the main run "
                          "starts each of them this way, in a child process)")
@@ -656,8 +751,8 @@ def main():
                     help="prefetch threshold percentile of the score sample (default 95)")
     ap.add_argument("--probe", choices=("score", "copy", "prefill"), default=None,
                     help="short program for hardware-counter runs, then exit: 20 launches of the "
-                         "scoring kernel on the workload, 20 device copies of 256 MiB, or 3 causal "
-                         "prefill launches on 32768^2")
+                         "step's scoring launch on the workload, 20 device copies of 256 MiB, or 3 "
+                         "causal prefill launches on 32768^2")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this decode path runs on one GPU; --gpus %d is not supported "
@@ -692,6 +787,13 @@ def main():
             except Exception:                            # noqa: BLE001
                 log("%s done" % name)
 
+        if not args.no_side_workloads:
+            for name, wl in SIDE_WORKLOADS.items():
+                log("decode step %s (%s) ..." % (wl, name))
+                section(name, lambda name=name: run_section(name, args),
+                        lambda p: "%s: %.1f us/step, scoring %.1f%% of HBM, recall %.1f%% of the link"
+                        % (p["workload"], p["us_per_step"], 100 * p["scoring_frac"],
+                           100 * p["recall_frac_of_link"]))
         if not args.no_prefill:
             log("prefill indexer (32768^2) ...")
             section("prefill", lambda: run_section("prefill", args),
@@ -713,7 +815,11 @@ def main():
                     "launches alone %.1f us vs plain scoring %.1f us" % (
                         p["off"]["us_per_step"], p["ranged"]["us_per_step"], p["fused"]["us_per_step"],
                         p["fused_launches_alone"]["us_median"], p["fused_launches_alone"]["plain_scoring_us"]))
-        out.update(extra)
+        # full details on stderr; the one line keeps the summaries (per-step and per-chunk
+        # arrays stay out of it), the headline's own keys first
+        for name, val in extra.items():
+            log("details %s: %s" % (name, json.dumps(val)))
+        out.update(summarize_extra(extra))
         print(json.dumps(out), flush=True)
         return
 
@@ -761,10 +867,12 @@ def main():
         dkb, dkl = torch.from_numpy(inp.key_begin).cuda(), torch.from_numpy(inp.key_len).cuda()
         max_len = int(inp.key_len.max())
         sc = torch.empty((len(inp.key_len), max_len), dtype=torch.float32, device="cuda")
+        hist = torch.zeros((len(inp.key_len), 2048), dtype=torch.int32, device="cuda")
         for _ in range(20):
-            B.index_scores(dq, dw, dk, dks, dkb, dkl, max_len, sc)
+            B.index_scores_hist(dq, dw, dk, dks, dkb, dkl, max_len, sc, hist)
         torch.cuda.synchronize()
-        log("score probe: 20 launches of echo_index_scores on", args.workload)
+        log("score probe: 20 launches of echo_index_scores_hist (the step's scoring launch) on",
+            args.workload)
         return
     raise SystemExit("bench.py: unknown --probe")
 

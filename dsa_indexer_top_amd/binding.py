@@ -64,6 +64,7 @@ _SIGS = {
     "echo_pool_init": (C.c_int, [C.POINTER(Pool), P]),
     "echo_status_clear": (C.c_int, [P, P]),
     "echo_index_scores": (C.c_int, [P, P, P, P, P, P, I32, I32, P, I64, P]),
+    "echo_index_scores_hist": (C.c_int, [P, P, P, P, P, P, I32, I32, P, I64, P, P]),
     "echo_index_scores_prefetch": (C.c_int, [P, P, P, P, P, P, I32, I32, I32, I32, P, I64,
                                              P, P, P, I32, P, P, P, I32, I32, P]),
     "echo_prefetch_threshold": (C.c_int, [P, P, P, P, P, P, I32, I32, I32, F32, P, P]),
@@ -153,6 +154,13 @@ def index_scores(q, w, k, k_scale, key_begin, key_len, max_key_len, scores, ld=N
     ld = scores.shape[-1] if ld is None else ld
     _call("echo_index_scores", ptr(q), ptr(w), ptr(k), ptr(k_scale), ptr(key_begin),
           ptr(key_len), q.shape[0], max_key_len, ptr(scores), ld, stream_handle(stream))
+
+
+def index_scores_hist(q, w, k, k_scale, key_begin, key_len, max_key_len, scores, hist, ld=None,
+                      stream=None):
+    ld = scores.shape[-1] if ld is None else ld
+    _call("echo_index_scores_hist", ptr(q), ptr(w), ptr(k), ptr(k_scale), ptr(key_begin),
+          ptr(key_len), q.shape[0], max_key_len, ptr(scores), ld, ptr(hist), stream_handle(stream))
 
 
 def index_scores_prefetch(q, w, k, k_scale, key_begin, key_len, max_key_len, tok_lo, tok_hi,

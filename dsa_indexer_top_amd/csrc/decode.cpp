@@ -8,8 +8,9 @@
 // queues inside a graph cost microseconds each, so work that can overlap the critical path
 // rides along in the same launches as extra workgroups instead of on a second stream:
 //
-//   zero -> score (+ pool statistics) -> top-k split + early lookup of the sure selections
-//        -> top-k finish + lookup of the rest (+ staging of the split's misses from host memory)
+//   zero -> score (+ top-k histogram) -> top-k split + early lookup of the sure selections
+//        (+ pool statistics) -> top-k finish + lookup of the rest (+ staging of the split's misses
+//        from host memory)
 //        -> evict-1 (+ staging of the finish's misses) -> evict-2 + allocate -> recall scatter
 //
 // With ranged prefetch, scoring is split into n_chunks token ranges: the launch of range c also
@@ -137,7 +138,10 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
                     pool->indices_buf, pool->status, pool->n_gpu, pool->n_host};
   side.W = W.pool;
   side.stamp = stamp;
-  side.n_stats = W.pool.n_chunks;                   // statistics ride with the first scoring launch
+  // the pool statistics ride in the top-k split launch (fused prefetch: ahead of its kernel)
+  SideWork stats_side = side;
+  stats_side.n_stats = fz ? 0 : W.pool.n_chunks;
+  side.n_stats = 0;
   // prefetch threshold: the caller's EMA estimate (§6.1), or a sample percentile of this
   // step's scores when there is no history
   const float *theta = a->theta_ema ? a->theta_ema : W.theta;
@@ -160,10 +164,11 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
     for (int c = 0; c < nc; ++c) {
       if (c > 0) {                                   // gather range c-1's candidates
         side.n_gather = a->n_rows;
+        // no statistics to keep current: they are taken after the gathers, in the split
         side.G = make_gather_args(pool, a->key_begin, a->req_to_host,
                                   W.cand + static_cast<int64_t>(c - 1) * a->n_rows * a->cap,
                                   W.cand_cnt + static_cast<int64_t>(c - 1) * a->n_rows, a->cap,
-                                  W.free_list, W.free_count, o->counters + 2, &W.pool, stamp);
+                                  W.free_list, W.free_count, o->counters + 2, nullptr, stamp);
       }
       const int32_t lo = c * span, hi = (c + 1 == nc) ? a->max_key_len : (c + 1) * span;
       PrefetchArgs P{theta, a->req_to_host, pool->host_to_gpu,
@@ -174,23 +179,22 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
                                     a->max_key_len, lo, hi, o->scores, a->max_key_len, &P, W.hist0,
                                     &side, m)))
         return rc;
-      side.n_stats = 0;
     }
     // the last range's gather must finish before the top-k split looks selections up
     const int64_t last = static_cast<int64_t>(nc - 1) * a->n_rows;
     if ((rc = launch_prefetch_gather(pool, a->key_begin, a->req_to_host, W.cand + last * a->cap,
                                      W.cand_cnt + last, a->n_rows, a->cap, W.free_list, W.free_count,
-                                     o->counters + 2, &W.pool, stamp, m)))
+                                     o->counters + 2, nullptr, stamp, m)))
       return rc;
   } else {
     if ((rc = launch_score_decode(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len, a->n_rows,
                                   a->max_key_len, 0, a->max_key_len, o->scores, a->max_key_len,
-                                  nullptr, W.hist0, &side, m)))
+                                  nullptr, W.hist0, nullptr, m)))
       return rc;
   }
   if ((rc = launch_topk_split(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,
                               a->topk, W.hist0, W.split, pool, &W.pool, a->key_begin, a->req_to_host,
-                              stamp, m)))
+                              stamp, &stats_side, m)))
     return rc;
   if ((rc = launch_topk_finish(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,
                                a->topk, W.hist0, W.split, o->topk_idx, pool, &W.pool, a->key_begin,

@@ -149,10 +149,12 @@ int launch_pool_step(const echo_pool *pool, const int32_t *idx, const int64_t *k
 // pool workspace's zeroed region must be ready and its histograms must hold every occupied
 // slot.
 size_t topk_split_ws_bytes(int32_t n_rows, int32_t max_len, int32_t k);
+// side (optional, with a pool): pool-statistics workgroups riding along (n_stats leading ones).
 int launch_topk_split(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
                       int32_t max_len, int32_t k, const uint32_t *hist0, void *split_ws,
                       const echo_pool *pool, const PoolFastWs *pw, const int64_t *key_begin,
-                      const int32_t *req_to_host, Stamp stamp, hipStream_t st);
+                      const int32_t *req_to_host, Stamp stamp, const SideWork *side,
+                      hipStream_t st);
 int launch_topk_finish(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
                        int32_t max_len, int32_t k, const uint32_t *hist0, void *split_ws,
                        int32_t *idx, const echo_pool *pool, const PoolFastWs *pw,

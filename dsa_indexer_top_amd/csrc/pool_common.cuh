@@ -17,7 +17,7 @@ constexpr int PF_HIST_WORDS = 32768;          // words of each histogram array (
 // run several times slower than spread ones.  The coarse array uses the same map (1024 of its
 // 32768 words are used).
 ECHO_DEV uint32_t hist_at(uint32_t b) { return (b & 31u) * 1024u + (b >> 5); }
-constexpr int STATS_HW = 8192;               // LDS histogram window (words) of a stats chunk
+constexpr int STATS_HW = 4096;               // LDS histogram window (words) of a stats chunk
 constexpr int STATS_LDS_WORDS = STATS_HW + 48;
 
 // ---------------------------------------------------------------- priority code

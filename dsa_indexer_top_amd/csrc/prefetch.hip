@@ -56,15 +56,16 @@ __global__ __launch_bounds__(PT_THREADS) void prefetch_threshold_kernel(
     load_q_operand(q, w, r, qo);
     for (int t0 = wv; t0 < n_tiles; t0 += PT_WAVES * PT_BATCH) {
       int4 b0[PT_BATCH], b1[PT_BATCH];
-      int64_t pos[PT_BATCH];
+      float sc[PT_BATCH];
 #pragma unroll
-      for (int u = 0; u < PT_BATCH; ++u) {
+      for (int u = 0; u < PT_BATCH; ++u) {            // every load of the batch before any use
         const int tile = t0 + u * PT_WAVES;
         const int i = (tile < n_tiles ? tile : t0) * 16 + j;
-        pos[u] = (static_cast<int64_t>(i) * L) / n_sample;        // sample position < L
-        const int4 *kp = reinterpret_cast<const int4 *>(k + (kb + pos[u]) * D + 32 * g);
+        const int64_t pos = (static_cast<int64_t>(i) * L) / n_sample;   // sample position < L
+        const int4 *kp = reinterpret_cast<const int4 *>(k + (kb + pos) * D + 32 * g);
         b0[u] = kp[0];
         b1[u] = kp[1];
+        sc[u] = k_scale ? k_scale[kb + pos] : 1.f;
       }
 #pragma unroll
       for (int u = 0; u < PT_BATCH; ++u) {
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(PT_THREADS) void prefetch_threshold_kernel(
         if (tile >= n_tiles) break;                // uniform
         float s = reduce_groups(score_tile_partial(
             qo, v8i{b0[u].x, b0[u].y, b0[u].z, b0[u].w, b1[u].x, b1[u].y, b1[u].z, b1[u].w}));
-        if (k_scale) s *= k_scale[kb + pos[u]];
+        if (k_scale) s *= sc[u];
         if (g == 0) skey[tile * 16 + j] = f32_key(s);
       }
     }

@@ -127,16 +127,31 @@ static SplitWs make_split_ws(void *base, int32_t n_rows, int32_t max_len, int32_
 
 // ---------------------------------------------------------------- split
 // LOOKUP: the early residency lookup of the sure selections (see the file comment).
+// Side work (decode step): n_stats leading workgroups compute the pool statistics of one
+// 4096-slot chunk each (free count, priority histograms of every occupied slot) while the
+// other workgroups split; the lookup's subtraction of protected slots commutes with them.
+constexpr int TS_GSCAN = 4 * (TS_T / 64) + TS_T / 64 + 2;
+constexpr int TS_SPLIT_WORDS = 48 + TS_GSCAN + ECHO_MAX_TOPK + TS_HW;
+constexpr int TS_LDS_WORDS = TS_SPLIT_WORDS > STATS_LDS_WORDS ? TS_SPLIT_WORDS : STATS_LDS_WORDS;
+
 template <bool LOOKUP>
 __global__ __launch_bounds__(TS_T) void topk_split_kernel(const float *__restrict__ scores, int64_t ld,
                                                           const int32_t *__restrict__ len, int32_t max_len,
                                                           int32_t k, const uint32_t *__restrict__ hist0,
-                                                          SplitWs W, SplitLookup L) {
-  __shared__ uint32_t tmp[48];
-  __shared__ uint32_t gscan[4 * (TS_T / 64) + TS_T / 64 + 2];
-  __shared__ int32_t sl[LOOKUP ? ECHO_MAX_TOPK : 1];     // this chunk's sure indices, ascending
-  __shared__ uint32_t hl[LOOKUP ? TS_HW : 1];
-  const int r = blockIdx.x / W.nch, c = blockIdx.x % W.nch, t = threadIdx.x;
+                                                          SplitWs W, SplitLookup L, SideWork side) {
+  __shared__ uint32_t lds[LOOKUP ? TS_LDS_WORDS : 48 + TS_GSCAN];
+  int blk = blockIdx.x;
+  if constexpr (LOOKUP) {
+    if (blk < side.n_stats) {
+      stats_chunk<false>(side.P, side.W, stamp_of(side.stamp), blk, lds);
+      return;
+    }
+    blk -= side.n_stats;
+  }
+  uint32_t *tmp = lds, *gscan = lds + 48;
+  int32_t *sl = reinterpret_cast<int32_t *>(lds + 48 + TS_GSCAN);   // this chunk's sure indices, ascending
+  uint32_t *hl = lds + 48 + TS_GSCAN + ECHO_MAX_TOPK;
+  const int r = blk / W.nch, c = blk % W.nch, t = threadIdx.x;
   const int32_t n = min(max(len[r], 0), max_len);
   const int32_t m = min(k, n);
   if (m == n || c * TS_CH >= n) return;
@@ -556,12 +571,16 @@ __global__ __launch_bounds__(TF_T) void topk_finish_kernel(
 int launch_topk_split(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
                       int32_t max_len, int32_t k, const uint32_t *hist0, void *split_ws,
                       const echo_pool *pool, const PoolFastWs *pw, const int64_t *key_begin,
-                      const int32_t *req_to_host, Stamp stamp, hipStream_t st) {
+                      const int32_t *req_to_host, Stamp stamp, const SideWork *side,
+                      hipStream_t st) {
   if (n_rows == 0) return ECHO_OK;
   if ((max_len + TS_CH - 1) / TS_CH > 1024) return fail(ECHO_EUNSUPPORTED, "decode top-k: rows longer than 4M tokens");
   SplitWs W = make_split_ws(split_ws, n_rows, max_len, k);
-  const int64_t blocks = static_cast<int64_t>(W.nch) * n_rows;
+  SideWork no_side{};
+  const SideWork &sw = side && pool ? *side : no_side;
+  const int64_t blocks = static_cast<int64_t>(W.nch) * n_rows + sw.n_stats;
   if (blocks > 0x7FFFFFFF) return fail(ECHO_EUNSUPPORTED, "decode top-k: grid too large");
+  if (sw.n_gather) return fail(ECHO_EINVAL, "decode top-k: the split carries no gathers");
   SplitLookup L{};
   if (pool) {
     L.P = PoolArgs{pool->gpu_free, pool->gpu_priority, pool->gpu_to_host, pool->host_to_gpu,
@@ -570,9 +589,9 @@ int launch_topk_split(const float *scores, int64_t ld, const int32_t *len, int32
     L.key_begin = key_begin;
     L.req_to_host = req_to_host;
     L.stamp = stamp;
-    topk_split_kernel<true><<<static_cast<unsigned>(blocks), TS_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W, L);
+    topk_split_kernel<true><<<static_cast<unsigned>(blocks), TS_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W, L, sw);
   } else {
-    topk_split_kernel<false><<<static_cast<unsigned>(blocks), TS_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W, L);
+    topk_split_kernel<false><<<static_cast<unsigned>(blocks), TS_T, 0, st>>>(scores, ld, len, max_len, k, hist0, W, L, sw);
   }
   return check_launch("topk_split");
 }

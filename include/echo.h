@@ -138,6 +138,19 @@ int echo_index_scores(const uint8_t *q, const float *w, const uint8_t *k, const 
                       int32_t max_key_len, float *scores, int64_t ld, void *stream);
 
 /*
+ * echo_index_scores plus, in the same launch, the first radix pass of the exact top-k (§2):
+ * hist[r*2048 + b] += the number of tokens s < key_len[r] of request r whose score's order key
+ * has top 11 bits b, where the order key is ~key(score) and key(x) maps a float to uint32 in
+ * increasing order (-0 counted as +0): bin 0 holds the highest scores.  hist [n_q, 2048] is
+ * accumulated (zero it first).  The decode step's scoring launch is this one.  Errors as
+ * echo_index_scores, and EINVAL for a NULL hist.
+ */
+int echo_index_scores_hist(const uint8_t *q, const float *w, const uint8_t *k,
+                           const float *k_scale, const int64_t *key_begin, const int32_t *key_len,
+                           int32_t n_q, int32_t max_key_len, float *scores, int64_t ld,
+                           uint32_t *hist, void *stream);
+
+/*
  * Threshold prefetch fused into scoring (§6.1).  Scores tokens [tok_lo, tok_hi) of every
  * request exactly as echo_index_scores does, and in addition lists scored tokens s with
  * score > theta[r] whose host index h = req_to_host[key_begin[r] + s] lies in [0, n_host) and is

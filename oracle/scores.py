@@ -87,5 +87,14 @@ def prefill_scores_rows(q, w, k, rows, k_scale=None):
     Returns a list of float64 arrays, row t having length t + 1.
     """
     rows = np.asarray(rows, dtype=np.int64)
-    return index_scores(q[rows], np.asarray(w)[rows], k, k_scale,
-                        np.zeros(len(rows), dtype=np.int64), rows + 1)
+    k_dec = decode_e4m3fn(k)                       # [T, D], decoded once for every row
+    sc = None if k_scale is None else np.asarray(k_scale, dtype=np.float64)
+    q_dec = decode_e4m3fn(q[rows])                 # [rows, H, D]
+    w64 = np.asarray(w, dtype=np.float64)[rows]
+    out = []
+    for i, t in enumerate(rows):
+        dots = k_dec[:t + 1] @ q_dec[i].T          # [t+1, H]: q[h] . k[s], exact
+        if sc is not None:
+            dots = dots * sc[:t + 1, None]
+        out.append(np.maximum(dots, 0.0) @ w64[i])
+    return out

@@ -179,7 +179,7 @@ def test_decode_b32_ragged_general_tolerance():
     rn.replay()
     got = rn.results()
     assert got["status"] == 0
-    _check_topk_tolerance(inp, scores, got, rows=[0, 5, 17, 31])
+    _check_topk_tolerance(inp, scores, got, rows=range(len(inp.key_len)))   # all 32 requests
     _check_invariants(inp, host_kv, got)
     if np.array_equal(got["topk_idx"], idx):           # same set: the pool must match exactly
         _check_pool_exact(inp, host_kv, idx, pool, got)

@@ -77,4 +77,32 @@ def test_scores_b32_ragged_full_tolerance():
     announce("scores b32_ragged full size")
     inp = gen.make_decode_inputs(gen.CONFIGS["b32_ragged"])
     got = _run_scores(inp)
-    _check(inp, got, rows=[0, 7, 13, 31], exact=False)
+    _check(inp, got, exact=False)                      # every one of the 32 requests
+
+
+def _hist_of(scores_f32):
+    """2048-bin histogram of the top 11 bits of the descending-order key (bin 0 = highest)."""
+    key = ~oracle.topk.f32_order_key(np.asarray(scores_f32, np.float32))
+    return np.bincount((key >> 21).astype(np.int64), minlength=2048)
+
+
+@pytest.mark.parametrize("grid,lens", [("int", [4096, 1, 0, 130, 70000]),
+                                       ("general", [5000, 129, 9000])])
+def test_scores_with_topk_histogram(grid, lens):
+    # echo_index_scores_hist (the decode step's scoring launch): the same scores, and per request
+    # the histogram of the top 11 bits of the descending-order key of exactly those scores,
+    # added to what the histogram held (accumulated twice here)
+    announce("scores + histogram", grid, lens)
+    cfg = gen.DecodeConfig("h", len(lens), 0, 16, grid, grid == "general", 0.5, 2, seed=211)
+    inp = gen.make_decode_inputs(cfg, lengths=lens)
+    d = decode_inputs_to_dev(inp)
+    max_len = max(lens)
+    sc = torch.full((len(lens), max_len), float("nan"), dtype=torch.float32, device="cuda")
+    hist = torch.zeros((len(lens), 2048), dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        B.index_scores_hist(d["q"], d["w"], d["k"], d["k_scale"], d["key_begin"], d["key_len"],
+                            max_len, sc, hist)
+    got, gh = host(sc), host(hist)
+    _check(inp, got, exact=grid == "int")
+    for r, L in enumerate(lens):
+        assert np.array_equal(gh[r], 2 * _hist_of(got[r, :L])), "histogram of request %d" % r

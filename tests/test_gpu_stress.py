@@ -3,10 +3,11 @@ per-token scales, top-2048, half of the selection resident in a pool of 2^20 slo
 kept free, threshold prefetch from a 4096-score sample, the step captured as one hipGraph), in
 the launch configuration the benchmark times, with the ranged prefetch (scoring in several
 launches) and with the fused one (one scoring launch with a host-gather wave per workgroup).
-The oracle computes sampled requests one by one; the rest is checked through properties that
-hold at any size: the step's selection equals the exact top-k of its own scores, every selected
-token is resident with its row equal to the host backup bit for bit, and the pool's maps stay a
-bijection."""
+Every request is checked against the oracle (scores within 1e-4 T, the selection differing from
+the oracle's only by tokens within that tolerance of its k-th score), and through properties
+that hold at any size: the step's selection equals the exact top-k of its own scores, every
+selected token is resident with its row equal to the host backup bit for bit, and the pool's
+maps stay a bijection."""
 
 import numpy as np
 import pytest
@@ -45,6 +46,13 @@ def test_stress_step(cfg):
         want_idx = sel.cpu().numpy()
         del dq, dw, dk, dks, dkb, dkl, sc, sel, tws
         pool = gen.make_pool_state(inp, want_idx, host_kv)
+        announce("stress %s: the oracle's scores of every request" % cfg.name)
+        ref = []
+        for r in range(n_rows):
+            sl = slice(r, r + 1)
+            args = (inp.q[sl], inp.w[sl], inp.k, inp.k_scale, inp.key_begin[sl], inp.key_len[sl])
+            s = oracle.index_scores(*args)[0]
+            ref.append((s, oracle.error_scale(*args)[0], oracle.topk_row(s, cfg.topk)))
         for mode in ("ranged", "fused"):
             announce("stress %s: captured step with %s prefetch" % (cfg.name, mode))
             rn = DecodeRunner(inp, pool, host_buf=hb, prefetch=mode)
@@ -54,12 +62,12 @@ def test_stress_step(cfg):
                 got = rn.results()
             finally:
                 rn.close()
-            _check_step(cfg, inp, host_kv, want_idx, got, mode)
+            _check_step(cfg, inp, host_kv, want_idx, got, mode, ref)
     finally:
         hb.close()
 
 
-def _check_step(cfg, inp, host_kv, want_idx, got, mode):
+def _check_step(cfg, inp, host_kv, want_idx, got, mode, ref):
     n_rows = len(inp.key_len)
     assert got["status"] == 0, mode
     # the step's top-k is the exact top-k of the scores it computed
@@ -73,16 +81,12 @@ def _check_step(cfg, inp, host_kv, want_idx, got, mode):
     st = oracle.PoolState(*(got["pool"][n] for n in ("free", "priority", "to_host",
                                                      "host_to_gpu", "indices_buf", "gpu_kv")))
     oracle.check_pool_invariants(st, host_kv, hosts, got["topk_slot"][rows, cols])
-    # sampled requests against the oracle: scores within 1e-4 T, and the selection differing
-    # from the oracle's only by tokens within that tolerance of its k-th score
-    announce("stress %s (%s): oracle on sampled requests" % (cfg.name, mode))
-    for r in sorted({0, min(n_rows - 1, n_rows // 2 + 5), n_rows - 1}):
-        sl = slice(r, r + 1)
-        args = (inp.q[sl], inp.w[sl], inp.k, inp.k_scale, inp.key_begin[sl], inp.key_len[sl])
-        s, T = oracle.index_scores(*args)[0], oracle.error_scale(*args)[0]
+    # every request against the oracle: scores within 1e-4 T, and the selection differing from
+    # the oracle's only by tokens within that tolerance of its k-th score
+    for r in range(n_rows):
+        s, T, want = ref[r]
         g = got["scores"][r, :len(s)].astype(np.float64)
         assert (np.abs(g - s) <= TOL * T).all(), "request %d scores (%s)" % (r, mode)
-        want = oracle.topk_row(s, cfg.topk)
         kth = want[np.argmin(s[want])]
         for t in np.setxor1d(idx[r], want):
             assert abs(s[t] - s[kth]) <= TOL * (T[t] + T[kth]), "request %d token %d" % (r, t)

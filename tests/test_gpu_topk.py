@@ -67,6 +67,6 @@ def test_topk_decode_shapes_full():
     announce("topk 64 x 131072 k=2048")
     sc = gen.random_scores(11, 64, 131072, tie_frac=0.05)
     got = _run(sc, [131072] * 64, 2048)
-    for r in (0, 17, 63):
-        assert np.array_equal(got[r], oracle.topk_row(sc[r], 2048))
+    for r in range(64):                                  # every row against the oracle
+        assert np.array_equal(got[r], oracle.topk_row(sc[r], 2048)), r
     assert (np.diff(got, axis=1) > 0).all()
