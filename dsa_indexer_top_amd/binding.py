@@ -81,6 +81,8 @@ _SIGS = {
     "echo_pool_workspace_bytes": (SZ, [I32, I32, I32]),
     "echo_pool_lookup_alloc": (C.c_int, [C.POINTER(Pool), P, P, P, I64, I32, I32, I32, P, P, P,
                                          P, P, SZ, P]),
+    "echo_pool_lookup_alloc_static": (C.c_int, [C.POINTER(Pool), P, P, P, I64, I32, I32, I32, P,
+                                                P, P, P, P]),
     "echo_recall": (C.c_int, [C.POINTER(Pool), P, P, P, I32, I32, P]),
     "echo_prefetch_begin": (C.c_int, [C.POINTER(Pool), P, P, P]),
     "echo_prefetch_gather": (C.c_int, [C.POINTER(Pool), P, P, P, P, I32, I32, P, P, P, P]),
@@ -101,6 +103,7 @@ _SIGS = {
 }
 
 EXPORTED = sorted(_SIGS)
+STATIC_SCRATCH_BYTES = 16 << 20      # echo.h ECHO_STATIC_SCRATCH_BYTES
 
 _lib = None
 
@@ -278,6 +281,13 @@ def pool_lookup_alloc(pool, idx, key_begin, req_to_host, step_id, topk_slot, mis
     _call("echo_pool_lookup_alloc", C.byref(pool), ptr(idx), ptr(key_begin), ptr(req_to_host),
           req_to_host.shape[0], idx.shape[0], idx.shape[1], step_id, ptr(topk_slot), ptr(miss_host), ptr(miss_slot),
           ptr(n_miss), ptr(ws), ws.numel() * ws.element_size(), stream_handle(stream))
+
+
+def pool_lookup_alloc_static(pool, idx, key_begin, req_to_host, step_id, topk_slot, miss_host,
+                             miss_slot, n_miss, stream=None):
+    _call("echo_pool_lookup_alloc_static", C.byref(pool), ptr(idx), ptr(key_begin),
+          ptr(req_to_host), req_to_host.shape[0], idx.shape[0], idx.shape[1], step_id,
+          ptr(topk_slot), ptr(miss_host), ptr(miss_slot), ptr(n_miss), stream_handle(stream))
 
 
 def recall(pool, miss_host, miss_slot, n_miss, max_miss, mode=RECALL_GATHER, stream=None):

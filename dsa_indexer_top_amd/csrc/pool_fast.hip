@@ -25,6 +25,7 @@
 //            the fixed-length lists.
 // Eviction and allocation touch metadata only; rows are copied by the recall gather.
 #include <algorithm>
+#include <mutex>
 
 #include "internal.hpp"
 #include "pool_common.cuh"
@@ -628,6 +629,69 @@ extern "C" int echo_pool_lookup_alloc(const echo_pool *pool, const int32_t *idx,
     return fail(ECHO_EINVAL, "echo_pool_lookup_alloc: NULL pointer");
   return launch_pool_step(pool, idx, key_begin, req_to_host, n_k, n_rows, k, Stamp{step_id, nullptr}, topk_slot,
                           miss_host, miss_slot, n_miss, ws, ws_bytes, S(stream));
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+// For callers that cannot allocate (code under graph capture, tight serving loops): the same
+// pool step with its workspace in a fixed device array.  Each GPU holds its own copy of the array
+// until the process ends; host code reaches it only through the address hipGetSymbolAddress
+// gives on that device, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[ECHO_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[MAX_DEVICES];                      // per device, set on its first call
+}  // namespace
+
+// Device address of the calling device's scratch array (nullptr after setting the error text).
+static void *scratch_of_current_device(const char *fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(ECHO_EHIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= MAX_DEVICES) {
+    fail(ECHO_EUNSUPPORTED, "%s: device %d outside [0, %d)", fn, dev, MAX_DEVICES);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      fail(ECHO_EHIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+      return nullptr;
+    }
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
+extern "C" int echo_pool_lookup_alloc_static(const echo_pool *pool, const int32_t *idx,
+                                             const int64_t *key_begin, const int32_t *req_to_host,
+                                             int64_t n_k, int32_t n_rows, int32_t k, int32_t step_id,
+                                             int32_t *topk_slot, int32_t *miss_host,
+                                             int32_t *miss_slot, int32_t *n_miss, void *stream) {
+  static const char *fn = "echo_pool_lookup_alloc_static";
+  int rc = check_pool(pool, fn);
+  if (rc) return rc;
+  if (n_rows < 0 || k < 1 || k > ECHO_MAX_TOPK || n_k < 0) return fail(ECHO_EINVAL, "%s: bad n_rows/k/n_k", fn);
+  if (static_cast<int64_t>(n_rows) * k > (1LL << 30)) return fail(ECHO_EUNSUPPORTED, "%s: too many entries", fn);
+  if (!idx || !key_begin || !req_to_host || !topk_slot || !miss_host || !miss_slot || !n_miss)
+    return fail(ECHO_EINVAL, "%s: NULL pointer", fn);
+  const size_t need = pool_fast_ws_bytes(n_rows, k, pool->n_gpu);
+  if (need > ECHO_STATIC_SCRATCH_BYTES)
+    return fail(ECHO_EUNSUPPORTED, "%s: %d rows x top-%d over %d GPU slots need %zu bytes of scratch, "
+                "more than the fixed %zu (use echo_pool_lookup_alloc with a workspace)", fn, n_rows, k,
+                pool->n_gpu, need, static_cast<size_t>(ECHO_STATIC_SCRATCH_BYTES));
+  void *ws = scratch_of_current_device(fn);
+  if (!ws) return ECHO_EHIP;
+  // the step clears the part of the workspace that must start at zero with a kernel of its own
+  return launch_pool_step(pool, idx, key_begin, req_to_host, n_k, n_rows, k, Stamp{step_id, nullptr},
+                          topk_slot, miss_host, miss_slot, n_miss, ws, ECHO_STATIC_SCRATCH_BYTES,
+                          S(stream));
 }
 
 extern "C" int echo_pool_init(echo_pool *pool, void *stream) {

@@ -325,6 +325,24 @@ int echo_pool_lookup_alloc(const echo_pool *pool, const int32_t *idx, const int6
                            void *stream);
 
 /*
+ * echo_pool_lookup_alloc without a workspace argument, for callers that cannot allocate
+ * (code under hipGraph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, results and errors as echo_pool_lookup_alloc; its workspace is a fixed device array
+ * of ECHO_STATIC_SCRATCH_BYTES inside the library, one per GPU, held until the process ends.
+ * Sizes whose echo_pool_workspace_bytes(n_rows, k, pool->n_gpu) exceeds that are rejected with
+ * ECHO_EUNSUPPORTED (nothing enqueued).  Allocates nothing; launch on a stream of the current
+ * device.  Every call on one GPU shares that GPU's array: calls that overlap in time on one GPU
+ * (other streams, other threads) race and give undefined results.  Each call clears what must
+ * start at zero itself.
+ */
+#define ECHO_STATIC_SCRATCH_BYTES (16u << 20)
+int echo_pool_lookup_alloc_static(const echo_pool *pool, const int32_t *idx,
+                                  const int64_t *key_begin, const int32_t *req_to_host, int64_t n_k,
+                                  int32_t n_rows, int32_t k, int32_t step_id, int32_t *topk_slot,
+                                  int32_t *miss_host, int32_t *miss_slot, int32_t *n_miss,
+                                  void *stream);
+
+/*
  * Recall (§5.2): gpu_kv[miss_slot[i]] = host_kv[miss_host[i]] bitwise (1152 bytes) for
  * i < *n_miss (n_miss is read on the device; max_miss bounds it).
  *   ECHO_RECALL_GATHER: one kernel reads the rows straight from mapped pinned host memory.

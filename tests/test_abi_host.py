@@ -62,6 +62,27 @@ def test_prefill_and_topk_argument_errors():
     assert L.echo_topk(None, 64, FAKE, 1, 64, 8, FAKE, None, 0, None) == B.ECHO_EINVAL
 
 
+def test_static_pool_entry_point_errors():
+    # the no-allocation variant rejects, before touching the runtime, what the plain entry point
+    # rejects, and any size whose workspace would not fit its fixed scratch array
+    L = B.lib()
+    none = C.POINTER(B.Pool)()
+    args = (FAKE, FAKE, FAKE, 4096, 1, 8, 3, FAKE, FAKE, FAKE, FAKE, None)
+    assert L.echo_pool_lookup_alloc_static(none, *args) == B.ECHO_EINVAL
+    bad_k = (FAKE, FAKE, FAKE, 4096, 1, 5000, 3, FAKE, FAKE, FAKE, FAKE, None)
+    assert L.echo_pool_lookup_alloc_static(C.byref(_pool()), *bad_k) == B.ECHO_EINVAL
+    assert L.echo_pool_lookup_alloc_static(C.byref(_pool()), FAKE, FAKE, FAKE, 4096, 1, 8, 3, FAKE,
+                                           FAKE, None, FAKE, None) == B.ECHO_EINVAL
+    # the largest pool the array serves: the bench's biggest workload (64 x top-2048 over 2^20
+    # slots) fits; 4M slots do not
+    assert B.lib().echo_pool_workspace_bytes(64, 2048, 1 << 20) <= B.STATIC_SCRATCH_BYTES
+    big = _pool(n_gpu=1 << 22)
+    assert B.lib().echo_pool_workspace_bytes(64, 2048, 1 << 22) > B.STATIC_SCRATCH_BYTES
+    too_big = (FAKE, FAKE, FAKE, 4096, 64, 2048, 3, FAKE, FAKE, FAKE, FAKE, None)
+    assert L.echo_pool_lookup_alloc_static(C.byref(big), *too_big) == B.ECHO_EUNSUPPORTED
+    assert "scratch" in _err()
+
+
 def test_pool_entry_point_errors():
     L = B.lib()
     none = C.POINTER(B.Pool)()
