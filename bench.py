@@ -444,7 +444,8 @@ def cpu_model():
     return "%s (%d cores online)" % (name, os.cpu_count() or 0)
 
 
-SECTIONS = ("headline", "prefill", "prefill_offload", "loop", "prefetch_modes", "c3", "c5")
+SECTIONS = ("headline", "prefill", "prefill_offload", "loop", "prefetch_modes", "c3", "c5",
+            "layers")
 # the other decode workloads of the metric's range, each reported by a section of its own
 SIDE_WORKLOADS = {"c3": "b32_ragged", "c5": "b64_128k"}
 
@@ -541,6 +542,83 @@ def run_section(name, args, timeout_s=900):
     return json.loads(lines[-1])
 
 
+def layers_measure(torch, B, gen, n_layers=61, batch=4, length=16384, topk=2048, page=64,
+                   steps=10, warmup=2):
+    """The decode step of every layer of a 61-layer model in one captured graph (ECHO page §5.1:
+    a GPU pool per layer, one host pool per model): per layer its own indexer inputs, its
+    indexer-K cache in 64-token pages scattered in a random order, its own pool (N_G = N_H / 8,
+    90% of the selection resident), its slice of one pinned host allocation.  Timed with HIP
+    events around each replay of the whole graph; every layer's pool restored before each
+    replay, outside the events."""
+    from dsa_indexer_top_amd.runner import DecodeRunner
+    row_bytes = 576 * 2
+    cfgs = [gen.DecodeConfig("layer%d" % ell, batch, length, topk, "int", False, 0.9, 8,
+                             seed=700 + ell) for ell in range(n_layers)]
+    inps = [gen.make_decode_inputs(c) for c in cfgs]
+    for inp in inps[1:]:
+        inp.req_to_host[:] = inps[0].req_to_host          # one token, one host row, every layer
+    n_host = inps[0].n_host
+    hb = B.HostBuffer(n_layers * n_host * row_bytes)
+    runners = []
+    try:
+        host_all = hb.array.view(np.uint16).reshape(n_layers, n_host, 576)
+        for ell, inp in enumerate(inps):
+            gen.fill_latent_rows(800 + ell, host_all[ell])
+            dq, dw, dk = (torch.from_numpy(a).cuda() for a in (inp.q, inp.w, inp.k))
+            dkb, dkl = torch.from_numpy(inp.key_begin).cuda(), torch.from_numpy(inp.key_len).cuda()
+            sc = torch.empty((batch, length), dtype=torch.float32, device="cuda")
+            sel = torch.empty((batch, topk), dtype=torch.int32, device="cuda")
+            tws = torch.empty(B.topk_workspace_bytes(batch, length), dtype=torch.uint8, device="cuda")
+            B.index_scores(dq, dw, dk, None, dkb, dkl, length, sc)
+            B.topk(sc, dkl, length, topk, sel, tws)
+            pool = gen.make_pool_state(inp, sel.cpu().numpy(), host_all[ell])
+            del dq, dw, dk, dkb, dkl, sc, sel, tws
+            pk = gen.page_key_cache(inp.k, None, inp.key_begin, inp.key_len, page, seed=ell)
+            rn = DecodeRunner(inp, pool, host_buf=hb, pages=pk)
+            rn.pool.host_kv = hb.dev_ptr + ell * n_host * row_bytes
+            runners.append(rn)
+        stream = runners[0].main
+        torch.cuda.synchronize()
+
+        def enqueue(st):
+            for rn in runners:
+                B.decode_select(rn.args, rn.pool, rn.out, rn.ws, st)
+
+        g = B.CapturedGraph(enqueue, stream)
+        try:
+            times = []
+            for it in range(warmup + steps):
+                for rn in runners:
+                    rn.restore()
+                torch.cuda.synchronize()
+                s_ = torch.cuda.Event(enable_timing=True)
+                e_ = torch.cuda.Event(enable_timing=True)
+                s_.record(stream)
+                g.launch(stream)
+                e_.record(stream)
+                torch.cuda.synchronize()
+                if it >= warmup:
+                    times.append(s_.elapsed_time(e_) * 1000.0)
+            for rn in runners:
+                assert int(rn.status.cpu()[0]) == 0, "pool status of a layer"
+            n_miss = sum(int(rn.counters.cpu()[0]) for rn in runners)
+        finally:
+            g.close()
+    finally:
+        for rn in runners:
+            rn.close()
+        hb.close()
+    t = float(np.median(times))
+    tokens = n_layers * batch * length
+    return {"workload": "%d layers x %d requests x %d tokens, top-%d, integer grid, indexer keys "
+                        "in %d-token pages, N_G = N_H/8 per layer, 90%% of the selection resident"
+                        % (n_layers, batch, length, topk, page, ),
+            "us_per_model_step": round(t, 1), "us_per_layer": round(t / n_layers, 2),
+            "indexed_tokens_per_s": round(tokens / (t / 1e6), 1), "misses_all_layers": n_miss,
+            "host_pool_bytes": n_layers * n_host * row_bytes,
+            "timing": "HIP events around each replay of the one graph of all layers' steps"}
+
+
 def child_section(name, args, torch, B, gen):
     """--section NAME: the measurement alone, printed as one JSON object."""
     import copy
@@ -551,6 +629,8 @@ def child_section(name, args, torch, B, gen):
         return prefill_offload_measure(torch, B, gen, cpu=cpu)
     if name == "loop":
         return loop_measure(torch, B, gen, cpu=cpu)
+    if name == "layers":
+        return layers_measure(torch, B, gen)
     if name in SIDE_WORKLOADS:
         from dsa_indexer_top_amd.runner import DecodeRunner
         wl = SIDE_WORKLOADS[name]
@@ -681,7 +761,7 @@ def headline(args, torch, B, gen, DecodeRunner, cfg, prefetch):
                    "timing": "HIP events around each graph replay; pool restored between "
                              "replays outside the events"},
         "roofline": {"bound": "hbm",
-                     "kernel": "score_decode_kernel<%s, false, true, false> (the step's scoring "
+                     "kernel": "score_decode_kernel<%s, false, true, false, false> (the step's scoring "
                                "launch, echo_index_scores_hist)" % str(inp.k_scale is not None).lower(),
                      "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(score_gbs / HBM_PEAK_GBS, 4),
@@ -740,6 +820,8 @@ def main():
                     help="prefetch of the headline step (on = ranged)")
     ap.add_argument("--no-prefetch-modes", action="store_true",
                     help="skip the off / ranged / fused prefetch comparison")
+    ap.add_argument("--no-layers", action="store_true",
+                    help="skip the 61-layer decode step in one graph")
     ap.add_argument("--no-side-workloads", action="store_true",
                     help="skip the ragged 32-request and the 64 x 128K decode steps")
     ap.add_argument("--section", choices=SECTIONS, default=None,
@@ -794,6 +876,11 @@ def main():
                         lambda p: "%s: %.1f us/step, scoring %.1f%% of HBM, recall %.1f%% of the link"
                         % (p["workload"], p["us_per_step"], 100 * p["scoring_frac"],
                            100 * p["recall_frac_of_link"]))
+        if not args.no_layers:
+            log("61 layers in one graph, paged indexer keys ...")
+            section("layers", lambda: run_section("layers", args),
+                    lambda p: "layers: %.1f us per model step, %.2f us per layer"
+                    % (p["us_per_model_step"], p["us_per_layer"]))
         if not args.no_prefill:
             log("prefill indexer (32768^2) ...")
             section("prefill", lambda: run_section("prefill", args),

@@ -42,7 +42,7 @@ class DecodeArgs(C.Structure):
                 ("topk", I32), ("step_id", I32), ("prefetch", I32), ("n_chunks", I32),
                 ("n_sample", I32), ("percentile", F32), ("cap", I32), ("cap_div", I32),
                 ("theta_ema", P), ("ema_alpha", F32), ("step_dev", P), ("reserve_free", I32),
-                ("pf_range", I32)]
+                ("pf_range", I32), ("k_page_table", P), ("k_page_size", I32), ("k_max_pages", I32)]
 
 
 class DecodeOut(C.Structure):
@@ -65,6 +65,7 @@ _SIGS = {
     "echo_status_clear": (C.c_int, [P, P]),
     "echo_index_scores": (C.c_int, [P, P, P, P, P, P, I32, I32, P, I64, P]),
     "echo_index_scores_hist": (C.c_int, [P, P, P, P, P, P, I32, I32, P, I64, P, P]),
+    "echo_index_scores_paged": (C.c_int, [P, P, P, P, P, I32, I32, P, I32, I32, P, I64, P]),
     "echo_index_scores_prefetch": (C.c_int, [P, P, P, P, P, P, I32, I32, I32, I32, P, I64,
                                              P, P, P, I32, P, P, P, I32, I32, P]),
     "echo_prefetch_threshold": (C.c_int, [P, P, P, P, P, P, I32, I32, I32, F32, P, P]),
@@ -157,6 +158,14 @@ def index_scores(q, w, k, k_scale, key_begin, key_len, max_key_len, scores, ld=N
     ld = scores.shape[-1] if ld is None else ld
     _call("echo_index_scores", ptr(q), ptr(w), ptr(k), ptr(k_scale), ptr(key_begin),
           ptr(key_len), q.shape[0], max_key_len, ptr(scores), ld, stream_handle(stream))
+
+
+def index_scores_paged(q, w, k_pages, k_scale_pages, page_table, page_size, key_len, max_key_len,
+                       scores, ld=None, stream=None):
+    ld = scores.shape[-1] if ld is None else ld
+    _call("echo_index_scores_paged", ptr(q), ptr(w), ptr(k_pages), ptr(k_scale_pages),
+          ptr(page_table), page_size, page_table.shape[1], ptr(key_len), q.shape[0], max_key_len,
+          ptr(scores), ld, stream_handle(stream))
 
 
 def index_scores_hist(q, w, k, k_scale, key_begin, key_len, max_key_len, scores, hist, ld=None,

@@ -116,6 +116,14 @@ static int validate(const echo_decode_args *a, const echo_pool *pool, const echo
     return fail(ECHO_EINVAL, "echo_decode_select: ema_alpha outside [0, 1]");
   if (a->reserve_free < 0 || a->reserve_free > pool->n_gpu)
     return fail(ECHO_EINVAL, "echo_decode_select: reserve_free outside [0, n_gpu]");
+  if (a->k_page_table) {
+    KeyPages kp;
+    int rc = key_pages_of(a->k_page_table, a->k_page_size, a->k_max_pages, a->max_key_len,
+                          "echo_decode_select", &kp);
+    if (rc) return rc;
+    if (a->prefetch == ECHO_PREFETCH_FUSED)
+      return fail(ECHO_EUNSUPPORTED, "echo_decode_select: the fused prefetch reads a contiguous key cache only");
+  }
   return ECHO_OK;
 }
 
@@ -133,6 +141,12 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
 
   if ((rc = launch_zero2_i32(o->counters, 8, reinterpret_cast<int32_t *>(W.hist0), W.zero_words, m))) return rc;
   const Stamp stamp{a->step_id, a->step_dev};
+  KeyPages pages{nullptr, 0, 0};
+  if (a->k_page_table &&
+      (rc = key_pages_of(a->k_page_table, a->k_page_size, a->k_max_pages, a->max_key_len,
+                         "echo_decode_select", &pages)))
+    return rc;
+  const KeyPages *kp = a->k_page_table ? &pages : nullptr;
   SideWork side{};
   side.P = PoolArgs{pool->gpu_free, pool->gpu_priority, pool->gpu_to_host, pool->host_to_gpu,
                     pool->indices_buf, pool->status, pool->n_gpu, pool->n_host};
@@ -148,7 +162,7 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
   if ((pf || fz) && !a->theta_ema &&
       (rc = launch_prefetch_threshold(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len,
                                       a->n_rows, a->max_key_len, a->n_sample, a->percentile,
-                                      W.theta, m)))
+                                      W.theta, kp, m)))
     return rc;
   if (fz) {
     const int32_t range = fused_range(static_cast<int64_t>(a->n_rows) * a->max_key_len, a->max_key_len,
@@ -174,10 +188,10 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
       PrefetchArgs P{theta, a->req_to_host, pool->host_to_gpu,
                      W.cand + static_cast<int64_t>(c) * a->n_rows * a->cap,
                      W.cand_cnt + static_cast<int64_t>(c) * a->n_rows, W.total_cnt, a->cap, a->cap_div,
-                     pool->n_host};
+                     pool->n_host, c, nc, W.cand_cnt, a->n_rows};
       if ((rc = launch_score_decode(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len, a->n_rows,
                                     a->max_key_len, lo, hi, o->scores, a->max_key_len, &P, W.hist0,
-                                    &side, m)))
+                                    &side, kp, m)))
         return rc;
     }
     // the last range's gather must finish before the top-k split looks selections up
@@ -189,7 +203,7 @@ static int decode_select_impl(const echo_decode_args *a, const echo_pool *pool,
   } else {
     if ((rc = launch_score_decode(a->q, a->w, a->k, a->k_scale, a->key_begin, a->key_len, a->n_rows,
                                   a->max_key_len, 0, a->max_key_len, o->scores, a->max_key_len,
-                                  nullptr, W.hist0, nullptr, m)))
+                                  nullptr, W.hist0, nullptr, kp, m)))
       return rc;
   }
   if ((rc = launch_topk_split(o->scores, a->max_key_len, a->key_len, a->n_rows, a->max_key_len,

@@ -14,6 +14,25 @@ struct Stamp {
 };
 ECHO_DEV int32_t stamp_of(const Stamp &s) { return s.dev ? *s.dev : s.value; }
 
+// Paged indexer-K cache: token t of request r lives at row (table[r * max_pages + t / P] * P +
+// t % P) of k and k_scale, P = 1 << shift tokens per page; table == nullptr for the contiguous
+// layout (row key_begin[r] + t).
+struct KeyPages {
+  const int32_t *table;
+  int32_t shift;
+  int32_t max_pages;
+};
+ECHO_DEV int64_t key_row(const KeyPages &kp, int r, int64_t kb, int32_t t) {
+  if (!kp.table) return kb + t;
+  const int64_t page = kp.table[static_cast<int64_t>(r) * kp.max_pages + (t >> kp.shift)];
+  return (page << kp.shift) | (t & ((1 << kp.shift) - 1));
+}
+
+// Page arguments of a paged key cache, checked (page size a power of two in [16, 65536],
+// max_pages * page_size >= max_key_len); fn names the entry point in the error text.
+int key_pages_of(const int32_t *page_table, int32_t page_size, int32_t max_pages, int32_t max_key_len,
+                 const char *fn, KeyPages *kp);
+
 struct PrefetchArgs {
   const float *theta;        // [n_q]
   const int32_t *req_to_host;// [n_k]
@@ -24,6 +43,11 @@ struct PrefetchArgs {
   int32_t cap;
   int32_t cap_div;
   int32_t n_host;            // host indices outside [0, n_host) never qualify
+  int32_t call, n_calls;     // the calls of a step share cap_r: calls 0..c together list at
+                             // most floor(cap_r (c+1) / n), so an early call cannot take the
+                             // whole cap and a share left unused passes on to later calls
+  const int32_t *before_cnt; // [call][ld_before] the list lengths of the step's earlier calls
+  int32_t ld_before;
 };
 
 struct PoolArgs {
@@ -42,7 +66,7 @@ int launch_score_decode(const uint8_t *q, const float *w, const uint8_t *k, cons
                         const int64_t *key_begin, const int32_t *key_len, int32_t n_q,
                         int32_t max_len, int32_t tok_lo, int32_t tok_hi, float *scores,
                         int64_t ld, const PrefetchArgs *pf, uint32_t *hist0, const struct SideWork *side,
-                        hipStream_t st);
+                        const KeyPages *kp, hipStream_t st);
 
 size_t topk_ws_bytes(int32_t n_rows, int32_t max_len);
 // hist0: optional digit-0 histograms from launch_score_decode
@@ -172,7 +196,8 @@ int launch_recall_scatter(const echo_pool *pool, const PoolFastWs &W, const int3
 int launch_prefetch_threshold(const uint8_t *q, const float *w, const uint8_t *k,
                               const float *k_scale, const int64_t *key_begin,
                               const int32_t *key_len, int32_t n_q, int32_t max_len,
-                              int32_t n_sample, float percentile, float *theta, hipStream_t st);
+                              int32_t n_sample, float percentile, float *theta, const KeyPages *kp,
+                              hipStream_t st);
 int launch_prefetch_begin(const echo_pool *pool, int32_t *free_list, int32_t *free_count,
                           hipStream_t st);
 // pw (optional): pool-step statistics (free count, priority histograms) updated for the slots

@@ -66,21 +66,67 @@ ECHO_DEV void block_min_max(uint32_t &lo, uint32_t &hi, uint32_t *tmp) {
   __syncthreads();
 }
 
+// Block-wide min of lo, max of hi and sum of cnt (NT threads, tmp >= 3 * NT / 64 words).
+template <int NT>
+ECHO_DEV void block_min_max_cnt(uint32_t &lo, uint32_t &hi, uint32_t &cnt, uint32_t *tmp) {
+  constexpr int NW = NT / 64;
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  cnt = wave_sum(cnt);
+  const int w = threadIdx.x >> 6;
+  if (lane_id() == 0) { tmp[w] = lo; tmp[NW + w] = hi; tmp[2 * NW + w] = cnt; }
+  __syncthreads();
+  lo = tmp[0];
+  hi = tmp[NW];
+  cnt = tmp[2 * NW];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) { lo = min(lo, tmp[i]); hi = max(hi, tmp[NW + i]); cnt += tmp[2 * NW + i]; }
+  __syncthreads();
+}
+
+// One bin per active lane added to (SUB: subtracted from) the global fine and coarse
+// histograms directly, the wave's most common bin (the first active lane's) in one atomic.
+template <bool SUB>
+ECHO_DEV void hist_global_add_peeled(uint32_t *fine, uint32_t *coarse, uint32_t bin, bool act) {
+  const uint64_t m_act = __ballot(act);
+  if (!m_act) return;
+  const int leader = __ffsll(static_cast<unsigned long long>(m_act)) - 1;
+  const uint32_t lead = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(bin), leader));
+  const uint32_t n = static_cast<uint32_t>(__popcll(__ballot(act && bin == lead)));
+  const bool own = act && bin != lead;
+  const uint32_t b = lane_id() == leader ? lead : bin, v = lane_id() == leader ? n : 1u;
+  if (lane_id() == leader || own) {
+    if (SUB) { atomicSub(&fine[hist_at(b)], v); atomicSub(&coarse[hist_at(b >> 5)], v); }
+    else { atomicAdd(&fine[hist_at(b)], v); atomicAdd(&coarse[hist_at(b >> 5)], v); }
+  }
+}
+
+// Bins a workgroup adds with direct global atomics rather than through its LDS histogram: the
+// LDS path clears, fills and scans a window of the bin range, a fixed cost of several
+// barriers that few bins do not repay (measured on MI355X in the decode step's top-k finish).
+constexpr uint32_t HIST_DIRECT_MAX = 512;
+
 // Adds (SUB: subtracts) a workgroup's priority bins to the global fine/coarse histograms: the
 // bins are counted in LDS first (h: HW words of two 16-bit counters, HW a multiple of 16;
 // bins[i] == 0xFFFFFFFF for none) and only non-empty bins reach global memory; 16 consecutive
 // lanes sum one coarse bin.  A bin range wider than the LDS window is done in several passes.
-// NT threads.
+// A workgroup with at most HIST_DIRECT_MAX bins adds them directly instead.  NT threads; tmp
+// >= 3 * NT / 64 words.
 template <int NT, int NB, bool SUB, int HW>
 ECHO_DEV void hist_flush_bins(const uint32_t (&bins)[NB], uint32_t *h, uint32_t *tmp, uint32_t *fine,
                               uint32_t *coarse) {
   static_assert(HW % 16 == 0, "whole coarse bins per pass");
-  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0, cnt = 0;
 #pragma unroll
   for (int i = 0; i < NB; ++i)
-    if (bins[i] != 0xFFFFFFFFu) { lo = min(lo, bins[i]); hi = max(hi, bins[i]); }
-  block_min_max<NT>(lo, hi, tmp);
+    if (bins[i] != 0xFFFFFFFFu) { lo = min(lo, bins[i]); hi = max(hi, bins[i]); ++cnt; }
+  block_min_max_cnt<NT>(lo, hi, cnt, tmp);
   if (lo > hi) return;                                  // uniform: no bin in this workgroup
+  if (cnt <= HIST_DIRECT_MAX) {                         // uniform
+#pragma unroll
+    for (int i = 0; i < NB; ++i) hist_global_add_peeled<SUB>(fine, coarse, bins[i], bins[i] != 0xFFFFFFFFu);
+    return;
+  }
   const int w_lo = static_cast<int>(lo >> 1) & ~15, w_hi = static_cast<int>(hi >> 1) | 15;
   for (int base = w_lo; base <= w_hi; base += HW) {
     const int top = min(w_hi, base + HW - 1);           // words [base, top] in this pass
@@ -176,6 +222,9 @@ ECHO_DEV void stats_chunk(const PoolArgs &P, const PoolFastWs &W, int32_t step_i
 // ---------------------------------------------------------------- prefetch gather of one request
 constexpr int PG_THREADS = 256;
 constexpr int PG_BATCH = 128;
+constexpr int PG_ROUND = 32;                                  // rows per round of host reads
+constexpr int PG_PER = PG_ROUND * (ROW * 2 / 16) / PG_THREADS;  // 16-byte reads per thread = 9
+static_assert(PG_PER * PG_THREADS == PG_ROUND * (ROW * 2 / 16), "whole rows per round");
 constexpr int PG_LDS_WORDS = 2 * PG_BATCH + 48 + 2;
 
 // Request r's candidates take the next free slots (in list order) and their rows are copied
@@ -222,11 +271,23 @@ ECHO_DEV void gather_request(const GatherArgs &G, int r, uint32_t *lds) {
       s_slot[t] = slot;
     }
     __syncthreads();
-    for (int u = threadIdx.x; u < m * UNITS; u += PG_THREADS) {
-      const int t = u / UNITS, part = u % UNITS;
-      if (s_host[t] >= 0)
-        dst[static_cast<int64_t>(s_slot[t]) * UNITS + part] =
-            __builtin_nontemporal_load(src + static_cast<int64_t>(s_host[t]) * UNITS + part);
+    // rows in rounds of PG_ROUND, every host read of a round in flight before its first store
+    for (int r0 = 0; r0 < m; r0 += PG_ROUND) {
+      v4i v[PG_PER];
+      int64_t d_off[PG_PER];
+#pragma unroll
+      for (int i = 0; i < PG_PER; ++i) {
+        const int u = threadIdx.x + i * PG_THREADS;
+        const int t = r0 + u / UNITS, part = u % UNITS;
+        d_off[i] = -1;
+        if (t < m && s_host[t] >= 0) {
+          v[i] = __builtin_nontemporal_load(src + static_cast<int64_t>(s_host[t]) * UNITS + part);
+          d_off[i] = static_cast<int64_t>(s_slot[t]) * UNITS + part;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < PG_PER; ++i)
+        if (d_off[i] >= 0) dst[d_off[i]] = v[i];
     }
     __syncthreads();
   }

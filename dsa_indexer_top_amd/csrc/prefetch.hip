@@ -38,7 +38,7 @@ __global__ __launch_bounds__(PT_THREADS) void prefetch_threshold_kernel(
     const uint8_t *__restrict__ q, const float *__restrict__ w, const uint8_t *__restrict__ k,
     const float *__restrict__ k_scale, const int64_t *__restrict__ key_begin,
     const int32_t *__restrict__ key_len, int32_t max_len, int32_t n_sample, int32_t rank,
-    float *__restrict__ theta) {
+    float *__restrict__ theta, KeyPages kp) {
   __shared__ uint32_t skey[PT_MAX_SAMPLE];        // order keys of the sampled scores
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t tmp[48];
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(PT_THREADS) void prefetch_threshold_kernel(
     if (threadIdx.x == 0) theta[r] = INFINITY;
     return;
   }
-  const int64_t kb = key_begin[r];
+  const int64_t kb = key_begin ? key_begin[r] : 0;
   const int l = lane_id(), j = l & 15, g = l >> 4, wv = threadIdx.x >> 6;
   const int n_tiles = n_sample / 16;              // >= 4; wave wv takes tiles wv, wv + 16, ...
   if (wv < n_tiles) {                              // uniform per wave
@@ -61,11 +61,12 @@ __global__ __launch_bounds__(PT_THREADS) void prefetch_threshold_kernel(
       for (int u = 0; u < PT_BATCH; ++u) {            // every load of the batch before any use
         const int tile = t0 + u * PT_WAVES;
         const int i = (tile < n_tiles ? tile : t0) * 16 + j;
-        const int64_t pos = (static_cast<int64_t>(i) * L) / n_sample;   // sample position < L
-        const int4 *kp = reinterpret_cast<const int4 *>(k + (kb + pos) * D + 32 * g);
-        b0[u] = kp[0];
-        b1[u] = kp[1];
-        sc[u] = k_scale ? k_scale[kb + pos] : 1.f;
+        const int32_t pos = static_cast<int32_t>((static_cast<int64_t>(i) * L) / n_sample);  // < L
+        const int64_t row = key_row(kp, r, kb, pos);
+        const int4 *kr = reinterpret_cast<const int4 *>(k + row * D + 32 * g);
+        b0[u] = kr[0];
+        b1[u] = kr[1];
+        sc[u] = k_scale ? k_scale[row] : 1.f;
       }
 #pragma unroll
       for (int u = 0; u < PT_BATCH; ++u) {
@@ -103,12 +104,14 @@ __global__ __launch_bounds__(PT_THREADS) void prefetch_threshold_kernel(
 int launch_prefetch_threshold(const uint8_t *q, const float *w, const uint8_t *k,
                               const float *k_scale, const int64_t *key_begin,
                               const int32_t *key_len, int32_t n_q, int32_t max_len,
-                              int32_t n_sample, float percentile, float *theta, hipStream_t st) {
+                              int32_t n_sample, float percentile, float *theta, const KeyPages *kp,
+                              hipStream_t st) {
   if (n_q == 0) return ECHO_OK;
   int32_t rank = static_cast<int32_t>(std::ceil(static_cast<double>(percentile) / 100.0 * n_sample));
   rank = std::min(std::max(rank, 1), n_sample);
   prefetch_threshold_kernel<<<n_q, PT_THREADS, 0, st>>>(q, w, k, k_scale, key_begin, key_len,
-                                                        max_len, n_sample, rank, theta);
+                                                        max_len, n_sample, rank, theta,
+                                                        kp ? *kp : KeyPages{nullptr, 0, 0});
   return check_launch("prefetch_threshold");
 }
 
@@ -220,7 +223,7 @@ extern "C" int echo_prefetch_threshold(const uint8_t *q, const float *w, const u
   if (n_q > 0 && (!q || !w || !k || !key_begin || !key_len || !theta))
     return fail(ECHO_EINVAL, "echo_prefetch_threshold: NULL pointer");
   return launch_prefetch_threshold(q, w, k, k_scale, key_begin, key_len, n_q, max_key_len, n_sample,
-                                   percentile, theta, S(stream));
+                                   percentile, theta, nullptr, S(stream));
 }
 
 extern "C" int echo_prefetch_begin(const echo_pool *pool, int32_t *free_list, int32_t *free_count,

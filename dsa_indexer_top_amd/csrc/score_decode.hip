@@ -4,14 +4,19 @@
 // a per-request threshold that are not resident are appended to a capped candidate list.
 //
 // Work split: grid (token range, request).  A workgroup of 4 waves streams its token range in
-// chunks of 128 tokens (16 KB).  Each thread fetches 4 x 16 B of the chunk with fully
+// chunks of 256 tokens (32 KB).  Each thread fetches 8 x 16 B of the chunk with fully
 // coalesced global loads (the next chunk is fetched into registers while the current one is
 // computed), and writes them into an LDS double buffer whose 16-byte segments are XOR-swizzled
-// by token so the MFMA-layout reads below are bank-conflict free.
+// by token so the MFMA-layout reads below are bank-conflict free.  Each wave scores one
+// 64-token group of the chunk.
 //
 // Contraction (score_tile.cuh): v_mfma_f32_16x16x128_f8f6f4, A = q of 16 heads held in VGPRs
-// for the whole kernel, B = k of 16 tokens read from LDS; four MFMAs cover the 64 heads and
-// the ReLU * w head reduction is 16 FMAs per lane plus a two-step cross-lane sum.
+// for the whole kernel, B = k of 16 tokens read from LDS; four MFMAs cover the 64 heads (issued
+// before their epilogue) and the ReLU * w head reduction is 16 FMAs per lane.  The four tiles'
+// partials of a group are summed over the lane groups by a butterfly of three lane swaps, after
+// which every lane holds one token's score, so the whole wave writes 64 scores at once.
+// Measured on MI355X at 8 x 65536 tokens against the former 128-token stages with one
+// cross-lane sum per tile: 12.6 us instead of 13.1 us for the scoring alone.
 //
 // Prefetch candidates: each call appends to its own list (cand, cand_cnt), so a later kernel
 // sees a complete list; the per-request cap is a counter shared by all calls of one step
@@ -30,22 +35,23 @@
 namespace echo {
 
 constexpr int SD_THREADS = 256;
-constexpr int SD_CHUNK = 128;                                    // tokens per LDS stage
+constexpr int SD_CHUNK = 256;                                    // tokens per LDS stage
 constexpr int SD_UNITS = SD_CHUNK * D / 16;                      // 16-byte units per chunk
-constexpr int SD_LOADS = SD_UNITS / SD_THREADS;                  // per thread per chunk = 4
+constexpr int SD_LOADS = SD_UNITS / SD_THREADS;                  // per thread per chunk = 8
+static_assert(SD_CHUNK == 64 * (SD_THREADS / 64), "one 64-token group per wave per chunk");
 
 ECHO_DEV int swz(int tok, int seg) { return tok * 128 + ((seg ^ ((tok >> 1) & 7)) << 4); }
 
 constexpr int SD_SCORE_WORDS = 2 * SD_CHUNK * D / 4;               // the LDS double buffer
 constexpr int SD_PF_LIST = 128;          // qualifying tokens a workgroup lists, at most
 
-template <bool HAS_SCALE, bool PREFETCH, bool HIST, bool SIDE>
+template <bool HAS_SCALE, bool PREFETCH, bool HIST, bool SIDE, bool PAGED>
 __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
     const uint8_t *__restrict__ q, const float *__restrict__ w, const uint8_t *__restrict__ k,
     const float *__restrict__ k_scale, const int64_t *__restrict__ key_begin,
     const int32_t *__restrict__ key_len, int32_t max_len, int32_t tok_lo, int32_t tok_hi,
     int32_t tokens_per_wg, int32_t gx, float *__restrict__ scores, int64_t ld, PrefetchArgs pf,
-    uint32_t *__restrict__ hist0, SideWork side) {
+    uint32_t *__restrict__ hist0, SideWork side, KeyPages kp) {
   constexpr int WORDS = SD_SCORE_WORDS + (HIST ? 2048 : 0);
   constexpr int ALL = SIDE && SIDE_LDS_WORDS > WORDS ? SIDE_LDS_WORDS : WORDS;
   __shared__ __attribute__((aligned(16))) uint32_t smem[ALL];
@@ -56,23 +62,24 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
     b -= side.n_stats + side.n_gather;
   }
   const int r = b / gx;
-  const int32_t L = min(max(key_len[r], 0), max_len);
+  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
+  const int j = l & 15, g = l >> 4;
+  const int tsel = group_tile_sel();              // the tile whose score this lane ends up with
+  // the request's length and key offset, and its q operand, all requested before the first
+  // wait, so their latencies overlap (the q loads of a workgroup with no tokens are wasted)
+  const int32_t len_r = key_len[r];
+  const int64_t kb = key_begin ? key_begin[r] : 0;   // no key_begin for a paged key cache
+  QOperand qo;
+  load_q_operand(q, w, r, qo);
+  const int32_t L = min(max(len_r, 0), max_len);
   const int32_t hi = min(L, tok_hi);
   const int32_t t_begin = tok_lo + (b % gx) * tokens_per_wg;
   if (t_begin >= hi) return;
   const int32_t t_end = min(hi, t_begin + tokens_per_wg);
-  const int64_t kb = key_begin[r];
-  const uint8_t *__restrict__ kr = k + kb * D;
   float *__restrict__ srow = scores + static_cast<int64_t>(r) * ld;
 
   uint8_t (*lds)[SD_CHUNK * D] = reinterpret_cast<uint8_t (*)[SD_CHUNK * D]>(smem);
   uint32_t *hl = smem + SD_SCORE_WORDS;
-
-  const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
-  const int j = l & 15, g = l >> 4;
-
-  QOperand qo;
-  load_q_operand(q, w, r, qo);
 
   float theta = 0.f;
   int32_t cap_r = 0;
@@ -88,7 +95,8 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
       const int e = tid + m * SD_THREADS;
       const int32_t t = c0 + (e >> 3);
       if (t < t_end)
-        pre[m] = *reinterpret_cast<const int4 *>(kr + static_cast<int64_t>(t) * D + ((e & 7) << 4));
+        pre[m] = *reinterpret_cast<const int4 *>(k + (PAGED ? key_row(kp, r, kb, t) : kb + t) * D +
+                                                 ((e & 7) << 4));
       else
         pre[m] = int4{0, 0, 0, 0};
     }
@@ -110,20 +118,20 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
     __syncthreads();
     if (c0 + SD_CHUNK < t_end) fetch(c0 + SD_CHUNK);
 
-    float part[2];
+    float part[4];
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      const int tt = wv * 32 + tile * 16 + j;
+    for (int tile = 0; tile < 4; ++tile) {
+      const int tt = wv * 64 + tile * 16 + j;
       const int4 b0 = *reinterpret_cast<const int4 *>(sb + swz(tt, 2 * g));
       const int4 b1 = *reinterpret_cast<const int4 *>(sb + swz(tt, 2 * g + 1));
-      part[tile] = reduce_groups(score_tile_partial(qo, v8i{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w}));
+      part[tile] = score_tile_partial_mf(qo, v8i{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w});
     }
-    const int32_t t_out = c0 + wv * 32 + g * 16 + j;
-    const bool writer = g < 2 && t_out < t_end;
-    float s_out = (g == 0) ? part[0] : part[1];
+    float s_out = butterfly4(part);
+    const int32_t t_out = c0 + wv * 64 + tsel * 16 + j;
+    const bool writer = t_out < t_end;
     bool qual = false;
     if (writer) {
-      if constexpr (HAS_SCALE) s_out *= k_scale[kb + t_out];
+      if constexpr (HAS_SCALE) s_out *= k_scale[PAGED ? key_row(kp, r, kb, t_out) : kb + t_out];
       srow[t_out] = s_out;
       if constexpr (PREFETCH) {
         if (s_out > theta) {
@@ -155,14 +163,32 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
   }
   if constexpr (PREFETCH) {
     // every qualifying token counts towards the request's demand (total_cnt); the workgroup
-    // lists as many of its listed ones as the cap still allows
+    // lists as many of its listed ones as this call's share of the cap still allows (the
+    // cumulative share less what the step's earlier calls listed), claimed with a
+    // compare-and-swap on the call's list count (each failure means another workgroup took
+    // places, so the loop ends after at most `share` rounds)
     if (threadIdx.x == 0) {
       const int32_t n_q = pf_list[SD_PF_LIST];
       int32_t take = 0, pos = 0;
       if (n_q > 0) {
-        const int32_t before = atomicAdd(&pf.total_cnt[r], n_q);
-        take = max(0, min(min(n_q, SD_PF_LIST), cap_r - before));
-        if (take > 0) pos = atomicAdd(&pf.cand_cnt[r], take);
+        atomicAdd(&pf.total_cnt[r], n_q);
+        int32_t share = static_cast<int32_t>(static_cast<int64_t>(cap_r) * (pf.call + 1) / pf.n_calls);
+        for (int c = 0; c < pf.call; ++c) share -= pf.before_cnt[static_cast<int64_t>(c) * pf.ld_before + r];
+        const int32_t want = min(n_q, SD_PF_LIST);
+        int32_t cur = *reinterpret_cast<volatile int32_t *>(&pf.cand_cnt[r]);
+        while (true) {
+          take = min(want, share - cur);
+          if (take <= 0) {
+            take = 0;
+            break;
+          }
+          const int32_t seen = atomicCAS(&pf.cand_cnt[r], cur, cur + take);
+          if (seen == cur) {
+            pos = cur;
+            break;
+          }
+          cur = seen;
+        }
       }
       pf_list[SD_PF_LIST] = take;
       pf_list[SD_PF_LIST + 1] = pos;
@@ -174,14 +200,15 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
   }
 }
 
-// Tokens per workgroup: about four workgroups per CU, whole chunks each; with the top-k
-// histogram at least 1024 tokens, so that its global flush stays rare (measured on MI355X at
-// 8 x 65536 tokens: 512 workgroups of 1024 tokens 13.9 us, 1024 of 512 tokens 14.5 us).
+// Tokens per workgroup: about one workgroup per CU for small launches, and at most 2048 tokens
+// (measured on MI355X, scoring alone: 8 x 65536 tokens 12.6 us with 2048 per workgroup against
+// 12.8 with 1024 and 20.7 with 4096; 64 x 131072 207 us with 2048, 210 with 8192, 242 with
+// 32768), whole chunks each.
 static int32_t pick_tokens_per_wg(int64_t total_tokens, int32_t max_len, bool hist) {
-  int64_t target = total_tokens / (256 * 4);
-  if (hist && target < 1024) target = 1024;
+  (void)hist;
+  const int64_t target = total_tokens / 256;
   int32_t t = SD_CHUNK;
-  while (t < target && t < 8192) t <<= 1;
+  while (t < target && t < 2048) t <<= 1;
   if (t > max_len) t = ((max_len + SD_CHUNK - 1) / SD_CHUNK) * SD_CHUNK;
   return t < SD_CHUNK ? SD_CHUNK : t;
 }
@@ -190,7 +217,7 @@ int launch_score_decode(const uint8_t *q, const float *w, const uint8_t *k, cons
                         const int64_t *key_begin, const int32_t *key_len, int32_t n_q,
                         int32_t max_len, int32_t tok_lo, int32_t tok_hi, float *scores,
                         int64_t ld, const PrefetchArgs *pf, uint32_t *hist0, const SideWork *side,
-                        hipStream_t st) {
+                        const KeyPages *kp, hipStream_t st) {
   tok_hi = tok_hi < max_len ? tok_hi : max_len;
   const int n_side = side ? side->n_stats + side->n_gather : 0;
   const bool scoring = n_q > 0 && tok_hi > tok_lo;
@@ -204,10 +231,18 @@ int launch_score_decode(const uint8_t *q, const float *w, const uint8_t *k, cons
   const PrefetchArgs &p = pf ? *pf : none;
   SideWork no_side{};
   const SideWork &sw = side ? *side : no_side;
+  const KeyPages pages = kp ? *kp : KeyPages{nullptr, 0, 0};
 #define ECHO_SD(SC, PF, HI, SI)                                                                 \
-  score_decode_kernel<SC, PF, HI, SI><<<static_cast<unsigned>(blocks), SD_THREADS, 0, st>>>(     \
-      q, w, k, k_scale, key_begin, key_len, max_len, tok_lo, scoring ? tok_hi : tok_lo, tpw, gx,  \
-      scores, ld, p, hist0, sw)
+  do {                                                                                          \
+    if (pages.table)                                                                            \
+      score_decode_kernel<SC, PF, HI, SI, true><<<static_cast<unsigned>(blocks), SD_THREADS, 0, st>>>( \
+          q, w, k, k_scale, key_begin, key_len, max_len, tok_lo, scoring ? tok_hi : tok_lo, tpw, gx, \
+          scores, ld, p, hist0, sw, pages);                                                     \
+    else                                                                                        \
+      score_decode_kernel<SC, PF, HI, SI, false><<<static_cast<unsigned>(blocks), SD_THREADS, 0, st>>>( \
+          q, w, k, k_scale, key_begin, key_len, max_len, tok_lo, scoring ? tok_hi : tok_lo, tpw, gx, \
+          scores, ld, p, hist0, sw, pages);                                                     \
+  } while (0)
   const bool sc = k_scale != nullptr, pfo = pf != nullptr, hi = hist0 != nullptr, si = n_side > 0;
   if (si) {
     // side work rides only with the decode step's scoring (histogram on)
@@ -242,7 +277,41 @@ extern "C" int echo_index_scores(const uint8_t *q, const float *w, const uint8_t
   if (n_q > 0 && (!q || !w || !key_begin || !key_len || !scores || (max_key_len > 0 && !k)))
     return fail(ECHO_EINVAL, "echo_index_scores: NULL pointer");
   return launch_score_decode(q, w, k, k_scale, key_begin, key_len, n_q, max_key_len, 0,
-                             max_key_len, scores, ld, nullptr, nullptr, nullptr, S(stream));
+                             max_key_len, scores, ld, nullptr, nullptr, nullptr, nullptr, S(stream));
+}
+
+// Checks the page arguments of a paged key cache and fills kp; EINVAL/EUNSUPPORTED on error.
+int echo::key_pages_of(const int32_t *page_table, int32_t page_size, int32_t max_pages,
+                       int32_t max_key_len, const char *fn, KeyPages *kp) {
+  if (!page_table) return fail(ECHO_EINVAL, "%s: NULL page table", fn);
+  if (page_size < 16 || page_size > (1 << 16) || (page_size & (page_size - 1)))
+    return fail(ECHO_EUNSUPPORTED, "%s: page size %d is not a power of two in [16, 65536]", fn, page_size);
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  if (max_pages < 1 || static_cast<int64_t>(max_pages) * page_size < max_key_len)
+    return fail(ECHO_EINVAL, "%s: %d pages of %d tokens cannot hold max_key_len %d", fn, max_pages,
+                page_size, max_key_len);
+  *kp = KeyPages{page_table, shift, max_pages};
+  return ECHO_OK;
+}
+
+extern "C" int echo_index_scores_paged(const uint8_t *q, const float *w, const uint8_t *k_pages,
+                                       const float *k_scale_pages, const int32_t *page_table,
+                                       int32_t page_size, int32_t max_pages,
+                                       const int32_t *key_len, int32_t n_q, int32_t max_key_len,
+                                       float *scores, int64_t ld, void *stream) {
+  static const char *fn = "echo_index_scores_paged";
+  if (n_q < 0 || max_key_len < 0) return fail(ECHO_EINVAL, "%s: negative n_q or max_key_len", fn);
+  if (ld < max_key_len) return fail(ECHO_EINVAL, "%s: ld %lld < max_key_len %d", fn, (long long)ld, max_key_len);
+  if (n_q > 65535) return fail(ECHO_EUNSUPPORTED, "%s: n_q %d > 65535", fn, n_q);
+  if (n_q > 0 && (!q || !w || !key_len || !scores || (max_key_len > 0 && !k_pages)))
+    return fail(ECHO_EINVAL, "%s: NULL pointer", fn);
+  KeyPages kp{};
+  int rc = key_pages_of(page_table, page_size, max_pages, max_key_len, fn, &kp);
+  if (rc) return rc;
+  // a request's key rows come from its pages (no key_begin)
+  return launch_score_decode(q, w, k_pages, k_scale_pages, nullptr, key_len, n_q, max_key_len, 0,
+                             max_key_len, scores, ld, nullptr, nullptr, nullptr, &kp, S(stream));
 }
 
 extern "C" int echo_index_scores_hist(const uint8_t *q, const float *w, const uint8_t *k,
@@ -255,7 +324,7 @@ extern "C" int echo_index_scores_hist(const uint8_t *q, const float *w, const ui
   if (n_q > 0 && (!q || !w || !key_begin || !key_len || !scores || !hist || (max_key_len > 0 && !k)))
     return fail(ECHO_EINVAL, "echo_index_scores_hist: NULL pointer");
   return launch_score_decode(q, w, k, k_scale, key_begin, key_len, n_q, max_key_len, 0,
-                             max_key_len, scores, ld, nullptr, hist, nullptr, S(stream));
+                             max_key_len, scores, ld, nullptr, hist, nullptr, nullptr, S(stream));
 }
 
 extern "C" int echo_index_scores_prefetch(const uint8_t *q, const float *w, const uint8_t *k,
@@ -276,7 +345,8 @@ extern "C" int echo_index_scores_prefetch(const uint8_t *q, const float *w, cons
                   !host_to_gpu || !cand_cnt || !total_cnt || (cap > 0 && !cand) || (max_key_len > 0 && !k)))
     return fail(ECHO_EINVAL, "echo_index_scores_prefetch: NULL pointer");
   if (n_host < 0) return fail(ECHO_EINVAL, "echo_index_scores_prefetch: n_host < 0");
-  PrefetchArgs pf{theta, req_to_host, host_to_gpu, cand, cand_cnt, total_cnt, cap, cap_div, n_host};
+  PrefetchArgs pf{theta, req_to_host, host_to_gpu, cand, cand_cnt, total_cnt, cap, cap_div, n_host, 0, 1,
+                  nullptr, 0};
   return launch_score_decode(q, w, k, k_scale, key_begin, key_len, n_q, max_key_len, tok_lo,
-                             tok_hi, scores, ld, &pf, nullptr, nullptr, S(stream));
+                             tok_hi, scores, ld, &pf, nullptr, nullptr, nullptr, S(stream));
 }

@@ -39,12 +39,9 @@ constexpr int PF_LOADS = PF_UNITS / PF_THREADS;         // 2 per thread
 constexpr int PF_BUFS = 3;                              // stage buffers in LDS (72 KB)
 static_assert(PF_STAGE % 64 == 0 && PF_UNITS % PF_THREADS == 0, "stage shape");
 
-typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 ECHO_DEV int pswz(int tok, int seg) { return tok * 128 + ((seg ^ ((tok >> 1) & 7)) << 4); }
 
-// ReLU(x) as an integer max on the bits: -0 and every negative float map to +0.
-ECHO_DEV float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 ECHO_DEV v4f unit_mfma(const v8i &qa, const v8i &bv) {
   const v4f z = {0.f, 0.f, 0.f, 0.f};
@@ -62,14 +59,6 @@ ECHO_DEV v8i tile_b(const uint8_t *sb, int tt, int g) {
   return v8i{b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 }
 
-ECHO_DEV float swap_sum32(float a, float b) {
-  const v2u s = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-ECHO_DEV float swap_sum16(float a, float b) {
-  const v2u s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
 
 // One 64-key group of a wave: 16 units (4 tiles x 4 head blocks), one MFMA and 8 VALU
 // instructions each.  The MFMA of unit u+2 is issued before the epilogue of unit u, so the

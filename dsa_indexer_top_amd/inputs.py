@@ -37,6 +37,8 @@ Value recipes:
                 random unselected tokens, occupied slots take distinct
                 random priorities from a permutation of [0, N_G) and the
                 step stamp is N_G; free slots hold the poison pattern
+  paged keys:   a request's keys copied into fixed-size pages handed out in a
+                seeded random order (page_key_cache)
 """
 
 from dataclasses import dataclass, field
@@ -51,7 +53,7 @@ POISON = 0xFFFF
 INF = 2**31 - 1
 
 _TAGS = {"q": 1, "w": 2, "k": 3, "scale": 4, "len": 5, "perm": 6, "kv": 7,
-         "hit": 8, "fill": 9, "slots": 10, "prio": 11, "scores": 12, "step": 13}
+         "hit": 8, "fill": 9, "slots": 10, "prio": 11, "scores": 12, "step": 13, "pages": 14}
 
 
 def rng_for(seed, tag):
@@ -378,3 +380,44 @@ def make_multistep_inputs(batch, length, n_steps, n_gpu, grid="int", k_scale=Fal
             step_id=n_gpu + t))
     return MultiStepInputs(k, ks, key_begin, np.full(batch, length, np.int32), req_to_host,
                            cap, n_host, n_gpu, pool, steps), host_kv
+
+
+class PagedKeys:
+    """A request-contiguous key cache laid out in fixed-size pages: k_pages [n_pages * P, 128]
+    (and k_scale_pages [n_pages * P] or None), page_table [n_rows, max_pages] int32 (page ids,
+    -1 past a request's last page).  Pages are handed out in a seeded random order, so that a
+    request's pages are scattered as in a paged cache that has been allocated from and freed."""
+
+    def __init__(self, k_pages, k_scale_pages, page_table, page_size):
+        self.k_pages, self.k_scale_pages = k_pages, k_scale_pages
+        self.page_table, self.page_size = page_table, page_size
+
+
+def page_key_cache(k, k_scale, key_begin, key_len, page_size, seed, spare_pages=3):
+    """The keys of `key_begin`/`key_len` (rows of k, k_scale) copied into pages of `page_size`
+    tokens; the tail of a request's last page and the spare pages hold random bytes (never
+    read).  No arithmetic of the method: a layout change only."""
+    rng = rng_for(seed, "pages")
+    n_rows = len(key_len)
+    per = [-(-int(L) // page_size) for L in key_len]
+    max_pages = max(1, max(per) if per else 1)
+    n_pages = sum(per) + spare_pages
+    order = rng.permutation(n_pages).astype(np.int32)
+    k_pages = rng.integers(0, 256, (n_pages * page_size, k.shape[1]), dtype=np.uint8)
+    k_pages[(k_pages & 0x7F) == 0x7F] = 0                   # no NaN codes, even where unread
+    ks_pages = None
+    if k_scale is not None:
+        ks_pages = rng.uniform(0.5, 2.0, n_pages * page_size).astype(np.float32)
+    table = np.full((n_rows, max_pages), -1, np.int32)
+    nxt = 0
+    for r in range(n_rows):
+        L, b = int(key_len[r]), int(key_begin[r])
+        for j in range(per[r]):
+            p = int(order[nxt])
+            nxt += 1
+            table[r, j] = p
+            n = min(page_size, L - j * page_size)
+            k_pages[p * page_size:p * page_size + n] = k[b + j * page_size:b + j * page_size + n]
+            if ks_pages is not None:
+                ks_pages[p * page_size:p * page_size + n] = k_scale[b + j * page_size:b + j * page_size + n]
+    return PagedKeys(k_pages, ks_pages, table, page_size)

@@ -20,10 +20,11 @@ class DecodeRunner:
     """inp: inputs.DecodeInputs; pool: inputs.PoolArrays; host_kv: uint16 [N_H, 576] numpy
     array, or a binding.HostBuffer already holding it (pass host_buf=...).  prefetch: False,
     True / "ranged" or "fused"; theta (optional, float32 [B]): a given per-request threshold
-    in place of the sample percentile (the step's EMA estimate; restored by restore())."""
+    in place of the sample percentile (the step's EMA estimate; restored by restore()).
+    pages (optional, inputs.PagedKeys of inp's keys): the step reads a paged key cache."""
 
     def __init__(self, inp, pool, host_kv=None, host_buf=None, prefetch=False, pf=None,
-                 topk=None, step_id=None, reserve=0, theta=None, alpha=0.5):
+                 topk=None, step_id=None, reserve=0, theta=None, alpha=0.5, pages=None):
         import torch
         self.torch = torch
         cfg = inp.cfg
@@ -32,8 +33,15 @@ class DecodeRunner:
         self.max_len = int(inp.key_len.max())
         self.topk = cfg.topk if topk is None else topk
         self.step_id = pool.step_id if step_id is None else step_id
-        self.q, self.w, self.k = _dev(inp.q), _dev(inp.w), _dev(inp.k)
-        self.k_scale = None if inp.k_scale is None else _dev(inp.k_scale)
+        self.q, self.w = _dev(inp.q), _dev(inp.w)
+        self.page_table = None
+        if pages is None:
+            self.k = _dev(inp.k)
+            self.k_scale = None if inp.k_scale is None else _dev(inp.k_scale)
+        else:
+            self.k = _dev(pages.k_pages)
+            self.k_scale = None if pages.k_scale_pages is None else _dev(pages.k_scale_pages)
+            self.page_table = _dev(pages.page_table)
         self.key_begin, self.key_len = _dev(inp.key_begin), _dev(inp.key_len)
         self.req_to_host = _dev(inp.req_to_host)
         # pool + pristine copy
@@ -74,6 +82,10 @@ class DecodeRunner:
             p["n_chunks"], p["n_sample"], p["percentile"], p["cap"], p["cap_div"])
         self.args.reserve_free = reserve
         self.args.pf_range = p["range"]
+        if pages is not None:
+            self.args.k_page_table = self.page_table.data_ptr()
+            self.args.k_page_size = pages.page_size
+            self.args.k_max_pages = self.page_table.shape[1]
         self.theta0 = self.theta = None
         if theta is not None:
             self.theta0 = _dev(np.asarray(theta, np.float32))

@@ -138,6 +138,20 @@ int echo_index_scores(const uint8_t *q, const float *w, const uint8_t *k, const 
                       int32_t max_key_len, float *scores, int64_t ld, void *stream);
 
 /*
+ * echo_index_scores over a paged key cache (§5.1: per-layer caches in fixed-size pages): the key
+ * (and key scale) of token s of request r is row page_table[r * max_pages + s / page_size] *
+ * page_size + s % page_size of k_pages (k_scale_pages; NULL = scale 1).  Same scores as
+ * echo_index_scores over the same keys laid out contiguously.  page_size is a power of two in
+ * [16, 65536]; max_pages * page_size >= max_key_len.  Errors as echo_index_scores, EINVAL for a
+ * NULL page table or too few pages, EUNSUPPORTED for a bad page size.
+ */
+int echo_index_scores_paged(const uint8_t *q, const float *w, const uint8_t *k_pages,
+                            const float *k_scale_pages, const int32_t *page_table,
+                            int32_t page_size, int32_t max_pages, const int32_t *key_len,
+                            int32_t n_q, int32_t max_key_len, float *scores, int64_t ld,
+                            void *stream);
+
+/*
  * echo_index_scores plus, in the same launch, the first radix pass of the exact top-k (§2):
  * hist[r*2048 + b] += the number of tokens s < key_len[r] of request r whose score's order key
  * has top 11 bits b, where the order key is ~key(score) and key(x) maps a float to uint32 in
@@ -384,7 +398,11 @@ int echo_prefetch_gather(const echo_pool *pool, const int64_t *key_begin,
  * ECHO_PREFETCH_FUSED scores in one launch with a host-gather wave per workgroup, with the
  * rows and slots of echo_index_scores_fused (§6.3).  Either way the
  * threshold is theta_ema when given, else the sample percentile, and the selection and the
- * selected rows are those of the step without prefetch.
+ * selected rows are those of the step without prefetch.  With prefetch on, the rest of the
+ * pool is not reproducible from run to run: which unselected candidates move, the free slot
+ * each takes, and so the slots the guaranteed recall then finds free and the contents of
+ * topk_slot / miss_slot / indices_buf, depend on the order in which workgroups finish.  The
+ * pool invariants (maps a bijection, every resident row equal to its host row) always hold.
  * `side_stream` is reserved and ignored (pass NULL or main_stream).  Workspace:
  * echo_decode_workspace_bytes(a, pool->n_gpu) bytes (it includes n_rows * topk staged rows of
  * ECHO_ROW_ELEMS bf16 values).
@@ -403,7 +421,10 @@ typedef struct {
   int32_t step_id;
   /* prefetch: ECHO_PREFETCH_OFF, _RANGED or _FUSED */
   int32_t prefetch;
-  int32_t n_chunks;          /* RANGED: scoring split into this many token ranges (1..16) */
+  int32_t n_chunks;          /* RANGED: scoring split into this many token ranges (1..16); ranges
+                                0..c together list at most floor(cap_r (c+1) / n) of a request's
+                                cap (a share left unused passes on), so the gathers spread over
+                                the later launches */
   int32_t n_sample;          /* threshold sample size (power of two, 64..4096) */
   float percentile;          /* threshold percentile, e.g. 95 */
   int32_t cap;               /* per-request candidate cap bound */
@@ -426,6 +447,15 @@ typedef struct {
   int32_t reserve_free;
   /* FUSED: tokens per range (0 = the library picks; else as echo_index_scores_fused) */
   int32_t pf_range;
+  /* Paged indexer-K cache (§5.1: the caches are kept per layer in fixed-size pages; NULL = the
+     contiguous layout).  With a page table, token s of request r has its key at row
+     k_page_table[r * k_max_pages + s / k_page_size] * k_page_size + s % k_page_size of k (and
+     k_scale); key_begin then only offsets req_to_host.  k_page_size is a power of two in
+     [16, 65536], k_max_pages * k_page_size >= max_key_len.  Not with ECHO_PREFETCH_FUSED
+     (EUNSUPPORTED). */
+  const int32_t *k_page_table;
+  int32_t k_page_size;
+  int32_t k_max_pages;
 } echo_decode_args;
 
 typedef struct {             /* device outputs of one step */

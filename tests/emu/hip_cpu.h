@@ -99,6 +99,11 @@ inline int atomicAdd(int *p, unsigned v) { return atomicAdd<int>(p, static_cast<
 inline unsigned atomicSub(unsigned *p, int v) { return atomicSub<unsigned>(p, static_cast<unsigned>(v)); }
 inline int atomicSub(int *p, unsigned v) { return atomicSub<int>(p, static_cast<int>(v)); }
 inline int atomicOr(int *p, unsigned v) { return atomicOr<int>(p, static_cast<int>(v)); }
+// compare-and-swap: returns the old value; stores v when it equalled expected
+template <typename T> inline T atomicCAS(T *p, T expected, T v) {
+  __atomic_compare_exchange_n(p, &expected, v, false, __ATOMIC_RELAXED, __ATOMIC_RELAXED);
+  return expected;
+}
 
 template <typename T> inline T emu_nontemporal_load(const T *p) { return *p; }
 

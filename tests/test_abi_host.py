@@ -50,6 +50,25 @@ def test_index_scores_argument_errors():
     assert "NULL" in _err()
 
 
+def test_paged_key_cache_argument_errors():
+    L = B.lib()
+    ok = dict(page_size=64, max_pages=4)
+    call = lambda ps, mp, tbl=FAKE, ml=256: L.echo_index_scores_paged(
+        FAKE, FAKE, FAKE, None, tbl, ps, mp, FAKE, 2, ml, FAKE, 256, None)
+    assert call(48, 4) == B.ECHO_EUNSUPPORTED and "power of two" in _err()
+    assert call(8, 64) == B.ECHO_EUNSUPPORTED
+    assert call(64, 3) == B.ECHO_EINVAL and "pages" in _err()      # 3 x 64 < 256
+    assert call(64, 4, tbl=None) == B.ECHO_EINVAL and "page table" in _err()
+    # the decode step: the same checks, and no fused prefetch over pages
+    pool, out = _pool(), _out()
+    for ps, mp, mode, code in ((48, 4, 0, B.ECHO_EUNSUPPORTED), (64, 1, 0, B.ECHO_EINVAL),
+                               (64, 1024, 2, B.ECHO_EUNSUPPORTED)):
+        a = _decode_args(max_key_len=256, prefetch=mode)
+        a.k_page_table, a.k_page_size, a.k_max_pages = FAKE, ps, mp
+        assert L.echo_decode_select(C.byref(a), C.byref(pool), C.byref(out), FAKE, 1 << 40,
+                                    None, None) == code, (ps, mp, mode)
+
+
 def test_prefill_and_topk_argument_errors():
     L = B.lib()
     assert L.echo_index_scores_prefill(FAKE, FAKE, FAKE, -1, 8, 0, FAKE, 8, None) == B.ECHO_EINVAL

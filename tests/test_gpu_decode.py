@@ -315,3 +315,101 @@ def test_prefetch_lossless_over_chunk_counts():
         _check_invariants(inp, host_kv, got)
         moved += int(got["counters"][2])
     assert moved > 0
+
+
+def test_ranged_prefetch_share_passes_on():
+    # the ranged prefetch's launches share a request's cap cumulatively: ranges 0..c list at
+    # most floor(cap_r (c+1) / n) rows.  Request 0 and 2 have their first half resident, so
+    # their first ranges have no demand and pass their share on; request 1 has its second half
+    # resident, so its demand sits in the first ranges and is held to their shares.
+    announce("ranged prefetch: cumulative share of the cap")
+    n_req, L, n_chunks, cap = 3, 8192, 4, 100
+    cfg = gen.DecodeConfig("share", n_req, L, 256, "int", False, 0.5, 1, seed=59)
+    inp = gen.make_decode_inputs(cfg)
+    host_kv = gen.fill_latent_rows(cfg.seed, np.empty((inp.n_host, 576), np.uint16))
+    scores = oracle.index_scores(inp.q, inp.w, inp.k, None, inp.key_begin, inp.key_len)
+    idx = oracle.topk_rows(scores, cfg.topk)
+    half = L // 2
+    resident = [np.arange(half), np.arange(half, L), np.arange(half)]
+    n_res = n_req * half
+    n_gpu = n_res + 6000
+    rng = np.random.default_rng(59)
+    hosts = np.concatenate([inp.req_to_host[inp.key_begin[r] + resident[r]] for r in range(n_req)])
+    slots = rng.permutation(n_gpu)[:n_res]
+    free = np.ones(n_gpu, np.uint8)
+    priority = np.full(n_gpu, -1, np.int32)
+    to_host = np.full(n_gpu, gen.INF, np.int32)
+    h2g = np.full(inp.n_host, gen.INF, np.int32)
+    free[slots], to_host[slots], h2g[hosts] = 0, hosts, slots
+    priority[slots] = rng.permutation(n_res).astype(np.int32)
+    gpu_kv = np.full((n_gpu, 576), gen.POISON, np.uint16)
+    gpu_kv[slots] = host_kv[hosts]
+    pool = gen.PoolArrays(free, priority, to_host, h2g, np.full(n_gpu, -1, np.int32), gpu_kv,
+                          step_id=n_res + 1)
+    theta = np.array([np.quantile(s, 0.97) for s in scores], np.float32)
+    span = -(-L // n_chunks)
+    want_demand = want_moved = 0
+    for r in range(n_req):
+        hosts_r = inp.req_to_host[inp.key_begin[r] + np.arange(L)]
+        elig = (scores[r] > theta[r]) & (h2g[hosts_r] == gen.INF)
+        per_range = [int(elig[c * span:(c + 1) * span].sum()) for c in range(n_chunks)]
+        assert max(per_range) <= 128            # every workgroup lists all of its own
+        cap_r, listed = min(cap, L), 0
+        for c, e in enumerate(per_range):
+            listed += min(e, cap_r * (c + 1) // n_chunks - listed)
+        want_demand += sum(per_range)
+        want_moved += listed
+    pf = dict(n_chunks=n_chunks, cap=cap, cap_div=1)
+    rn = DecodeRunner(inp, pool, host_kv, prefetch="ranged", pf=pf, theta=theta)
+    try:
+        rn.run_eager()
+        got = rn.results()
+    finally:
+        rn.close()
+    assert got["status"] == 0
+    assert np.array_equal(got["topk_idx"], idx)
+    assert int(got["counters"][1]) == want_demand
+    assert int(got["counters"][2]) == want_moved
+    assert want_moved > n_req * cap // 2         # more than fixed halves would have moved
+    _check_invariants(inp, host_kv, got)
+
+
+@pytest.mark.parametrize("prefetch", [False, "ranged"])
+def test_decode_step_paged_keys_matches_contiguous(prefetch):
+    # the decode step over a paged indexer-K cache (128-token pages in a random order, general
+    # FP8 keys with scales, the threshold sampled from the pages too): scores, selection, misses
+    # and every pool array bit for bit those of the step over the contiguous cache, and the
+    # selection the oracle's up to the tolerance
+    announce("decode step paged keys, prefetch", prefetch)
+    cfg = gen.DecodeConfig("pg", 5, 0, 256, "general", True, 0.5, 4, reserve=800,
+                           prefetch=bool(prefetch), seed=61)
+    inp = gen.make_decode_inputs(cfg, lengths=[9000, 1, 4500, 128, 3333])
+    host_kv = gen.fill_latent_rows(cfg.seed, np.empty((inp.n_host, 576), np.uint16))
+    scores = oracle.index_scores(inp.q, inp.w, inp.k, inp.k_scale, inp.key_begin, inp.key_len)
+    idx = oracle.topk_rows(scores, cfg.topk)
+    pool = gen.make_pool_state(inp, idx, host_kv)
+    pk = gen.page_key_cache(inp.k, inp.k_scale, inp.key_begin, inp.key_len, 128, seed=3)
+    pf = dict(n_chunks=3, n_sample=1024, percentile=90.0, cap=400, cap_div=16)
+    got = []
+    for pages in (None, pk):
+        rn = DecodeRunner(inp, pool, host_kv, prefetch=prefetch, pf=pf, pages=pages)
+        try:
+            rn.capture()
+            rn.replay()
+            got.append(rn.results())
+        finally:
+            rn.close()
+    a, b = got
+    assert a["status"] == b["status"] == 0
+    assert np.array_equal(a["topk_idx"], b["topk_idx"])
+    for r, L in enumerate(inp.key_len):                 # entries past a request's length are unset
+        assert np.array_equal(a["scores"][r, :L], b["scores"][r, :L]), r
+    if not prefetch:                       # which candidates win the prefetch depends on timing
+        for key in ("topk_slot", "miss_host", "miss_slot", "counters"):
+            assert np.array_equal(a[key], b[key]), key
+        for n in a["pool"]:
+            assert np.array_equal(a["pool"][n], b["pool"][n]), n
+    else:
+        assert b["counters"][2] > 0
+    _check_topk_tolerance(inp, scores, b, rows=range(len(inp.key_len)))
+    _check_invariants(inp, host_kv, b)

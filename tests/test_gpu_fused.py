@@ -311,3 +311,56 @@ def test_decode_step_fused(lens, k, R, div, reserve, given_theta):
                                          got["topk_slot"][rows, cols])
     finally:
         rn.close()
+
+
+@pytest.mark.parametrize("mode", ["fused", "ranged"])
+def test_decode_step_prefetch_then_evict(mode):
+    # the prefetch fills the few free slots with candidates; the guaranteed recall then has
+    # more misses than free slots left and evicts, the prefetched rows (priority 0) first.
+    # Which rows stay resident then depends on timing; the selection, the scores, every selected
+    # row resident bit for bit and the pool invariants must not, eager and over graph replays,
+    # and they must equal the step without prefetch
+    announce("decode step, %s prefetch, then eviction" % mode)
+    lens, k, reserve = [6000, 3000, 5000], 256, 400
+    cfg = gen.DecodeConfig("pfe", len(lens), 0, k, "int", False, 0.3, 4, seed=77, reserve=reserve)
+    inp = gen.make_decode_inputs(cfg, lengths=lens)
+    host_kv = gen.fill_latent_rows(cfg.seed, np.empty((inp.n_host, 576), np.uint16))
+    scores = oracle.index_scores(inp.q, inp.w, inp.k, None, inp.key_begin, inp.key_len)
+    idx = oracle.topk_rows(scores, k)
+    pool = gen.make_pool_state(inp, idx, host_kv)
+    assert int(pool.free.sum()) == reserve
+    theta = _thetas(scores, 0.9, {})
+    off = DecodeRunner(inp, pool, host_kv)
+    try:
+        off.run_eager()
+        base = off.results()
+    finally:
+        off.close()
+    assert base["status"] == 0 and np.array_equal(base["topk_idx"], idx)
+    rn = DecodeRunner(inp, pool, host_kv, prefetch=mode, theta=theta,
+                      pf=dict(n_chunks=3, cap=2048, cap_div=4, range=256))
+    try:
+        for run in ("eager", "graph", "graph again"):
+            if run == "eager":
+                rn.run_eager()
+            else:
+                if rn.graph is None:
+                    rn.capture()
+                rn.restore()
+                rn.replay()
+            got = rn.results()
+            assert got["status"] == 0, run
+            assert np.array_equal(got["topk_idx"], idx), run
+            for r, L in enumerate(lens):
+                assert np.array_equal(got["scores"][r, :L].astype(np.float64), scores[r]), (run, r)
+            n_miss, moved = int(got["counters"][0]), int(got["counters"][2])
+            assert moved > 0, run
+            assert n_miss > reserve - moved, run            # the recall had to evict
+            rows, cols = np.nonzero(idx >= 0)
+            hosts = inp.req_to_host[inp.key_begin[rows] + idx[rows, cols]]
+            oracle.check_pool_invariants(_as_state(got["pool"]), host_kv, hosts,
+                                         got["topk_slot"][rows, cols])
+            sel = got["pool"]["gpu_kv"][got["topk_slot"][rows, cols]]
+            assert np.array_equal(sel, base["pool"]["gpu_kv"][base["topk_slot"][rows, cols]]), run
+    finally:
+        rn.close()

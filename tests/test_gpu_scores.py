@@ -106,3 +106,28 @@ def test_scores_with_topk_histogram(grid, lens):
     _check(inp, got, exact=grid == "int")
     for r, L in enumerate(lens):
         assert np.array_equal(gh[r], 2 * _hist_of(got[r, :L])), "histogram of request %d" % r
+
+
+@pytest.mark.parametrize("grid,lens,page", [("int", [4096, 1, 0, 130, 70000, 3000], 64),
+                                            ("int", [5000, 129, 257], 16),
+                                            ("general", [9000, 1, 300], 256),
+                                            ("general", [3000, 4096, 4097], 4096)])
+def test_scores_paged_key_cache(grid, lens, page):
+    # a paged indexer-K cache (pages of `page` tokens in a random order): the same scores as the
+    # contiguous layout, bit for bit (same kernel arithmetic), and the oracle's (bit-exact on the
+    # integer grid, within 1e-4 T otherwise)
+    announce("scores paged", grid, lens, page)
+    cfg = gen.DecodeConfig("p", len(lens), 0, 16, grid, grid == "general", 0.5, 2, seed=221 + page)
+    inp = gen.make_decode_inputs(cfg, lengths=lens)
+    pk = gen.page_key_cache(inp.k, inp.k_scale, inp.key_begin, inp.key_len, page, seed=7)
+    d = decode_inputs_to_dev(inp)
+    max_len = max(lens)
+    sc = torch.full((len(lens), max_len), float("nan"), dtype=torch.float32, device="cuda")
+    B.index_scores_paged(d["q"], d["w"], dev(pk.k_pages),
+                         None if pk.k_scale_pages is None else dev(pk.k_scale_pages),
+                         dev(pk.page_table), page, d["key_len"], max_len, sc)
+    got = host(sc)
+    contiguous = _run_scores(inp, ld=max_len)
+    for r, L in enumerate(lens):
+        assert np.array_equal(got[r, :L], contiguous[r, :L]), "request %d" % r
+    _check(inp, got, exact=grid == "int")
