@@ -180,13 +180,14 @@ def loop_measure(torch, B, gen, batch=8, length=65536, n_steps=16, topk=2048, dr
     the step's query and new tokens precedes the start event).  Reports the pool hit rate of
     the guaranteed recall, the rows prefetched and the EMA's prediction error per step, with the
     ranged prefetch (scoring in 4 launches) and again, on the same inputs, with the fused one
-    (one scoring launch with a host-gather wave per workgroup)."""
+    (one scoring launch with a host-gather wave per workgroup) and with prefetch off."""
     from dsa_indexer_top_amd.runner import LoopRunner
     n_gpu = batch * length // 8
     reserve = batch * topk                     # room for a full step of prefetch
     m, host_kv = gen.make_multistep_inputs(batch, length, n_steps, n_gpu, seed=51, drift=drift)
     steps = run_loop(torch, LoopRunner, m, host_kv, topk, batch, reserve, "ranged")
     fused = run_loop(torch, LoopRunner, m, host_kv, topk, batch, reserve, "fused")
+    off = run_loop(torch, LoopRunner, m, host_kv, topk, batch, reserve, False)
     later = steps[1:]
     out = {}
     if cpu:
@@ -218,7 +219,10 @@ def loop_measure(torch, B, gen, batch=8, length=65536, n_steps=16, topk=2048, dr
             "fused": {"us_per_step_median": round(float(np.median([x["us"] for x in fused[1:]])), 1),
                       "hit_rate_median": round(float(np.median([x["hit_rate"] for x in fused[1:]])), 4),
                       "prefetched_median": int(np.median([x["prefetched"] for x in fused[1:]])),
-                      "steps": fused}})
+                      "steps": fused},
+            "off": {"us_per_step_median": round(float(np.median([x["us"] for x in off[1:]])), 1),
+                    "hit_rate_median": round(float(np.median([x["hit_rate"] for x in off[1:]])), 4),
+                    "steps": off}})
     return out
 
 
@@ -462,6 +466,8 @@ def summarize_extra(extra):
             if "fused" in val:
                 out[name]["fused"] = {k: val["fused"].get(k) for k in
                                       ("us_per_step_median", "hit_rate_median", "prefetched_median")}
+            if "off" in val:
+                out[name]["off"] = {k: val["off"].get(k) for k in ("us_per_step_median", "hit_rate_median")}
         elif name == "prefill_offload":
             out[name] = {k: val.get(k) for k in ("pairs_per_s", "us_total", "thr_bin_median_shifted",
                                                   "thr_bin_median_unshifted")}
@@ -893,8 +899,10 @@ def main():
         if not args.no_loop:
             log("decode loop (EMA threshold, new tokens every step) ...")
             section("loop", lambda: run_section("loop", args),
-                    lambda p: "loop: median %.1f us/step, hit rate %.3f"
-                    % (p["us_per_step_median"], p["hit_rate_median"]))
+                    lambda p: "loop: ranged %.1f us/step (hit rate %.3f), fused %.1f, prefetch off "
+                    "%.1f (hit rate %.3f)" % (p["us_per_step_median"], p["hit_rate_median"],
+                                              p["fused"]["us_per_step_median"], p["off"]["us_per_step_median"],
+                                              p["off"]["hit_rate_median"]))
         if not args.no_prefetch_modes:
             log("prefetch off / ranged / fused on one starting pool ...")
             section("prefetch_modes", lambda: run_section("prefetch_modes", args),

@@ -19,10 +19,14 @@
 // cross-lane sum per tile: 12.6 us instead of 13.1 us for the scoring alone.
 //
 // Prefetch candidates: each call appends to its own list (cand, cand_cnt), so a later kernel
-// sees a complete list; the per-request cap is a counter shared by all calls of one step
-// (total_cnt).  A workgroup collects its qualifying tokens in LDS (one LDS atomic per wave and
-// chunk) and publishes them at its end with at most two global atomics, so the step's counters
-// see one update per workgroup instead of one per token.
+// sees a complete list, and the calls of a step share each request's cap cumulatively.  A
+// workgroup collects its over-threshold tokens in LDS (one LDS atomic per wave and chunk) and
+// looks their residency up only at its end, with all of those loads in flight together, so the
+// streaming loop never waits on a lookup (measured on MI355X at 64 x 131072 tokens: per-chunk
+// lookups made each ranged scoring launch about twice as long as plain scoring).  The eligible
+// ones are then published with one atomic for the demand and one compare-and-swap claim on
+// the call's list, so the step's counters see one update per workgroup instead of one per
+// token.
 //
 // Side work (SIDE): the launch may carry extra leading workgroups that do independent pool
 // work (priority statistics, a previous range's prefetch gather) while the scoring workgroups
@@ -43,7 +47,11 @@ static_assert(SD_CHUNK == 64 * (SD_THREADS / 64), "one 64-token group per wave p
 ECHO_DEV int swz(int tok, int seg) { return tok * 128 + ((seg ^ ((tok >> 1) & 7)) << 4); }
 
 constexpr int SD_SCORE_WORDS = 2 * SD_CHUNK * D / 4;               // the LDS double buffer
-constexpr int SD_PF_LIST = 128;          // qualifying tokens a workgroup lists, at most
+constexpr int SD_PF_OVER = 1024;         // over-threshold tokens a workgroup holds for lookup
+constexpr int SD_PF_PER = SD_PF_OVER / SD_THREADS;
+// LDS words of the prefetch list: over-threshold tokens, then their count, the count of
+// eligible tokens past the list, the compacted count and the claim (count, base)
+constexpr int SD_PF_WORDS = SD_PF_OVER + 5;
 
 template <bool HAS_SCALE, bool PREFETCH, bool HIST, bool SIDE, bool PAGED>
 __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
@@ -55,7 +63,7 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
   constexpr int WORDS = SD_SCORE_WORDS + (HIST ? 2048 : 0);
   constexpr int ALL = SIDE && SIDE_LDS_WORDS > WORDS ? SIDE_LDS_WORDS : WORDS;
   __shared__ __attribute__((aligned(16))) uint32_t smem[ALL];
-  __shared__ int32_t pf_list[PREFETCH ? SD_PF_LIST + 2 : 1];   // tokens, then count and base
+  __shared__ int32_t pf_list[PREFETCH ? SD_PF_WORDS : 1];
   int b = blockIdx.x;
   if constexpr (SIDE) {
     if (side_work(side, b, smem)) return;
@@ -105,7 +113,7 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
   if constexpr (HIST)
     for (int b = threadIdx.x; b < 2048; b += SD_THREADS) hl[b] = 0;   // ordered by the first barrier
   if constexpr (PREFETCH)
-    if (threadIdx.x == 0) pf_list[SD_PF_LIST] = 0;                    // ordered by the first barrier
+    if (threadIdx.x < 3) pf_list[SD_PF_OVER + threadIdx.x] = 0;       // ordered by the first barrier
   fetch(t_begin);
   int buf = 0;
   for (int32_t c0 = t_begin; c0 < t_end; c0 += SD_CHUNK) {
@@ -129,27 +137,31 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
     float s_out = butterfly4(part);
     const int32_t t_out = c0 + wv * 64 + tsel * 16 + j;
     const bool writer = t_out < t_end;
-    bool qual = false;
     if (writer) {
       if constexpr (HAS_SCALE) s_out *= k_scale[PAGED ? key_row(kp, r, kb, t_out) : kb + t_out];
       srow[t_out] = s_out;
-      if constexpr (PREFETCH) {
-        if (s_out > theta) {
-          const int32_t h = pf.req_to_host[kb + t_out];
-          qual = h >= 0 && h < pf.n_host && pf.host_to_gpu[h] == INF;
-        }
-      }
     }
     if constexpr (PREFETCH) {
-      // the wave's qualifying tokens take consecutive places of the workgroup's LDS list
-      const uint64_t mq = __ballot(qual);
-      if (mq) {
-        const int lead = __ffsll(static_cast<unsigned long long>(mq)) - 1;
+      // over-threshold tokens take consecutive places of the workgroup's LDS list; their
+      // residency is looked up at the workgroup's end, all at once, so no chunk waits on it.
+      // Past the list's end (more than SD_PF_OVER such tokens) a token is looked up here and
+      // only counted towards the demand.
+      const bool over = writer && s_out > theta;
+      const uint64_t mo = __ballot(over);
+      if (mo) {
+        const int lead = __ffsll(static_cast<unsigned long long>(mo)) - 1;
         int32_t base = 0;
-        if (l == lead) base = atomicAdd(&pf_list[SD_PF_LIST], static_cast<int32_t>(__popcll(mq)));
+        if (l == lead) base = atomicAdd(&pf_list[SD_PF_OVER], static_cast<int32_t>(__popcll(mo)));
         base = __builtin_amdgcn_readlane(base, lead);
-        const int at = base + static_cast<int>(__popcll(mq & ((1ull << l) - 1ull)));
-        if (qual && at < SD_PF_LIST) pf_list[at] = t_out;
+        const int at = base + static_cast<int>(__popcll(mo & ((1ull << l) - 1ull)));
+        if (over) {
+          if (at < SD_PF_OVER) {
+            pf_list[at] = t_out;
+          } else {
+            const int32_t h = pf.req_to_host[kb + t_out];
+            if (h >= 0 && h < pf.n_host && pf.host_to_gpu[h] == INF) atomicAdd(&pf_list[SD_PF_OVER + 1], 1);
+          }
+        }
       }
     }
     if constexpr (HIST) hist_add_peeled(hl, (~f32_key(s_out)) >> 21, writer);
@@ -162,19 +174,49 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
       if (hl[b]) atomicAdd(&gh[b], hl[b]);
   }
   if constexpr (PREFETCH) {
-    // every qualifying token counts towards the request's demand (total_cnt); the workgroup
-    // lists as many of its listed ones as this call's share of the cap still allows (the
-    // cumulative share less what the step's earlier calls listed), claimed with a
-    // compare-and-swap on the call's list count (each failure means another workgroup took
-    // places, so the loop ends after at most `share` rounds)
+    // residency of the listed over-threshold tokens: every load in flight before the first use
+    const int32_t n_over = min(pf_list[SD_PF_OVER], SD_PF_OVER);
+    int32_t tok[SD_PF_PER], hh[SD_PF_PER];
+#pragma unroll
+    for (int i = 0; i < SD_PF_PER; ++i) {
+      const int e = threadIdx.x + i * SD_THREADS;
+      tok[i] = e < n_over ? pf_list[e] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < SD_PF_PER; ++i) hh[i] = tok[i] >= 0 ? pf.req_to_host[kb + tok[i]] : -1;
+    bool el[SD_PF_PER];
+#pragma unroll
+    for (int i = 0; i < SD_PF_PER; ++i) el[i] = hh[i] >= 0 && hh[i] < pf.n_host;
+#pragma unroll
+    for (int i = 0; i < SD_PF_PER; ++i) el[i] = el[i] && pf.host_to_gpu[hh[i]] == INF;
+    __syncthreads();                                 // every list entry read before compaction
+    // the eligible ones move to the front of the list (in no particular order)
+#pragma unroll
+    for (int i = 0; i < SD_PF_PER; ++i) {
+      const uint64_t me = __ballot(el[i]);
+      if (me) {
+        const int lead = __ffsll(static_cast<unsigned long long>(me)) - 1;
+        int32_t base = 0;
+        if (l == lead) base = atomicAdd(&pf_list[SD_PF_OVER + 2], static_cast<int32_t>(__popcll(me)));
+        base = __builtin_amdgcn_readlane(base, lead);
+        if (el[i]) pf_list[base + static_cast<int>(__popcll(me & ((1ull << l) - 1ull)))] = tok[i];
+      }
+    }
+    __syncthreads();
+    // every eligible token counts towards the request's demand (total_cnt); the workgroup
+    // lists as many of them as this call's share of the cap still allows (the cumulative
+    // share less what the step's earlier calls listed), claimed with a compare-and-swap on the
+    // call's list count (each failure means another workgroup took places, so the loop ends
+    // after at most `share` rounds)
     if (threadIdx.x == 0) {
-      const int32_t n_q = pf_list[SD_PF_LIST];
+      const int32_t n_listed = pf_list[SD_PF_OVER + 2];
+      const int32_t n_q = n_listed + pf_list[SD_PF_OVER + 1];
       int32_t take = 0, pos = 0;
       if (n_q > 0) {
         atomicAdd(&pf.total_cnt[r], n_q);
         int32_t share = static_cast<int32_t>(static_cast<int64_t>(cap_r) * (pf.call + 1) / pf.n_calls);
         for (int c = 0; c < pf.call; ++c) share -= pf.before_cnt[static_cast<int64_t>(c) * pf.ld_before + r];
-        const int32_t want = min(n_q, SD_PF_LIST);
+        const int32_t want = n_listed;
         int32_t cur = *reinterpret_cast<volatile int32_t *>(&pf.cand_cnt[r]);
         while (true) {
           take = min(want, share - cur);
@@ -190,11 +232,11 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
           cur = seen;
         }
       }
-      pf_list[SD_PF_LIST] = take;
-      pf_list[SD_PF_LIST + 1] = pos;
+      pf_list[SD_PF_OVER + 3] = take;
+      pf_list[SD_PF_OVER + 4] = pos;
     }
     __syncthreads();
-    const int32_t take = pf_list[SD_PF_LIST], pos = pf_list[SD_PF_LIST + 1];
+    const int32_t take = pf_list[SD_PF_OVER + 3], pos = pf_list[SD_PF_OVER + 4];
     for (int i = threadIdx.x; i < take; i += SD_THREADS)
       pf.cand[static_cast<int64_t>(r) * pf.cap + pos + i] = pf_list[i];
   }

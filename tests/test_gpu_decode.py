@@ -224,28 +224,28 @@ def test_prefetch_threshold_matches_sample_percentile():
                 assert abs(got[r] - want) <= 1e-3 * (abs(want) + 1), ("clamped", r, got[r], want)
 
 
-def test_fused_prefetch_scoring_candidates():
-    announce("fused prefetch scoring")
-    cfg = gen.DecodeConfig("p", 3, 0, 64, "int", False, 0.5, 4, seed=43)
-    lens = [9000, 300, 20000]
+def _prefetch_scoring_case(lens, quantile, cap, cap_div, seed):
+    # the scoring launch lists over-threshold non-resident tokens up to the cap and counts all
+    # of them as demand
+    cfg = gen.DecodeConfig("p", len(lens), 0, 64, "int", False, 0.5, 4, seed=seed)
     inp = gen.make_decode_inputs(cfg, lengths=lens)
     rng = np.random.default_rng(5)
     h2g = np.full(inp.n_host, gen.INF, np.int32)
     res = rng.permutation(inp.n_host)[: inp.n_host // 3]
     h2g[res] = np.arange(len(res))                      # a third of the tokens resident
     scores = oracle.index_scores(inp.q, inp.w, inp.k, None, inp.key_begin, inp.key_len)
-    theta = np.array([np.quantile(s, 0.9) for s in scores], np.float32)
-    cap, cap_div = 4096, 8
+    theta = np.array([np.quantile(s, quantile) for s in scores], np.float32)
     d = {n: dev(getattr(inp, n)) for n in ("q", "w", "k", "key_begin", "key_len", "req_to_host")}
-    sc = torch.empty((3, max(lens)), dtype=torch.float32, device="cuda")
-    cand = torch.full((3, cap), -1, dtype=torch.int32, device="cuda")
-    cnt = torch.zeros(3, dtype=torch.int32, device="cuda")
-    tot = torch.zeros(3, dtype=torch.int32, device="cuda")
+    n = len(lens)
+    sc = torch.empty((n, max(lens)), dtype=torch.float32, device="cuda")
+    cand = torch.full((n, cap), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(n, dtype=torch.int32, device="cuda")
+    tot = torch.zeros(n, dtype=torch.int32, device="cuda")
     B.index_scores_prefetch(d["q"], d["w"], d["k"], None, d["key_begin"], d["key_len"], max(lens),
                             0, max(lens), sc, dev(theta), d["req_to_host"], dev(h2g), cand, cnt,
                             tot, cap, cap_div)
     got_s, got_c, got_n, got_t = host(sc), host(cand), host(cnt), host(tot)
-    for r in range(3):
+    for r in range(n):
         L = lens[r]
         s = scores[r]
         assert np.array_equal(got_s[r, :L].astype(np.float64), s)
@@ -253,10 +253,25 @@ def test_fused_prefetch_scoring_candidates():
         eligible = np.flatnonzero((s > theta[r]) & (h2g[hosts] == gen.INF))
         cap_r = min(cap, -(-L // cap_div))
         assert got_t[r] == len(eligible)
+        # a workgroup lists at least the eligible ones among its first 1024 over-threshold
+        # tokens; here that is more than the cap wherever the eligible tokens are
         assert got_n[r] == min(cap_r, len(eligible))
         listed = got_c[r, :got_n[r]]
         assert len(set(listed.tolist())) == len(listed)
         assert set(listed.tolist()) <= set(eligible.tolist())
+
+
+def test_fused_prefetch_scoring_candidates():
+    announce("prefetch scoring candidates")
+    _prefetch_scoring_case([9000, 300, 20000], 0.9, 4096, 8, 43)
+
+
+def test_prefetch_scoring_list_overflow_b8_64k():
+    # 2048 tokens per workgroup at this size; at the 0.2 quantile about 1600 of them are over
+    # the threshold, more than a workgroup's list holds: the ones past it are looked up in the
+    # streaming loop and only counted towards the demand, which stays exact
+    announce("prefetch scoring, list overflow, 8 x 65536")
+    _prefetch_scoring_case([65536] * 8, 0.2, 4096, 64, 44)
 
 
 @pytest.mark.parametrize("side_stream", [True, False])
@@ -353,7 +368,8 @@ def test_ranged_prefetch_share_passes_on():
         hosts_r = inp.req_to_host[inp.key_begin[r] + np.arange(L)]
         elig = (scores[r] > theta[r]) & (h2g[hosts_r] == gen.INF)
         per_range = [int(elig[c * span:(c + 1) * span].sum()) for c in range(n_chunks)]
-        assert max(per_range) <= 128            # every workgroup lists all of its own
+        over = [int((scores[r][c * span:(c + 1) * span] > theta[r]).sum()) for c in range(n_chunks)]
+        assert max(over) <= 1024                # every workgroup lists all of its own
         cap_r, listed = min(cap, L), 0
         for c, e in enumerate(per_range):
             listed += min(e, cap_r * (c + 1) // n_chunks - listed)
