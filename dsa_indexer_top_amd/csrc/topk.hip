@@ -353,6 +353,234 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(
   }
 }
 
+// ---- rows of at most TK_BATCH (32768) scores: the row is read once, into registers
+//
+// The first digit is a linear bin of the score value between the row's minimum and maximum
+// rather than the top 11 bits of its order key: scores of one row sit in a few exponents, so the
+// top bits put most of them into a few dozen bins (contended LDS atomics, thousands of
+// candidates in the threshold bin), while value bins spread them (about 15 candidates per row
+// on the 32768^2 prefill).  The bin is a monotone function of the score (subtraction and
+// multiplication by a positive constant round monotonically), so every element of a lower bin
+// is selected for sure.  After the pick a thread keeps only two bit masks of its 32 elements
+// (lower bins, threshold bin); the threshold bin's keys are copied to LDS and resolved exactly
+// by three radix passes, the few of them a thread owns are read again for the output, and the
+// ties at the exact threshold key go to the lowest indices through an ordered block scan (only
+// when not all of them are taken).  Measured on MI355X over the 32768 causal rows of the
+// prefill: 2.49 ms against 2.56 ms for topk_row_kernel, which reads each row twice.
+
+// values of elements i0 .. i0+3 of a row (-0 folded to +0); returns the presence bits
+ECHO_DEV uint32_t row_value(const float *s, bool vec, int32_t n, int32_t i0, float (&x)[4]) {
+  if (vec && i0 + 3 < n) {
+    const float4 v = *reinterpret_cast<const float4 *>(s + i0);
+    x[0] = v.x + 0.0f; x[1] = v.y + 0.0f; x[2] = v.z + 0.0f; x[3] = v.w + 0.0f;
+    return 0xFu;
+  }
+  uint32_t valid = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = 0.f;
+    if (i0 + e < n) {
+      x[e] = s[i0 + e] + 0.0f;
+      valid |= 1u << e;
+    }
+  }
+  return valid;
+}
+
+// bin of a value: 0 for the row's largest scores, TK_BINS - 1 for its smallest
+ECHO_DEV uint32_t value_bin(float x, float lo, float scale) {
+  if (!(scale > 0.f)) return TK_BINS - 1;          // one bin (non-finite or empty span)
+  const float f = (x - lo) * scale;
+  const int b = f >= 2047.0f ? 2047 : static_cast<int>(f);
+  return static_cast<uint32_t>(TK_BINS - 1 - max(b, 0));
+}
+
+constexpr int TK_RC = 4096;                         // threshold-bin elements resolved in LDS
+
+// Order key of element i of a row (-0 folded to +0; ascending key = descending score).
+ECHO_DEV uint32_t row_key(const float *row, int32_t i) { return ~f32_key(row[i]); }
+
+__global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(
+    const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ len, int32_t max_len,
+    int32_t k, int32_t *__restrict__ idx) {
+  __shared__ uint32_t hist[TK_BINS];
+  __shared__ uint32_t tmp[48];
+  __shared__ uint32_t gscan[TK_SCAN_LDS];
+  __shared__ float red[2 * (TK_THREADS / 64)];
+  __shared__ uint32_t cand_key[TK_RC];
+  const int r = blockIdx.x;
+  const int t = threadIdx.x;
+  const int w = t >> 6, l = lane_id();
+  const int32_t n = min(max(len[r], 0), min(max_len, TK_BATCH));
+  const int32_t m = min(k, n);
+  int32_t *out = idx + static_cast<int64_t>(r) * k;
+  for (int j = m + t; j < k; j += TK_THREADS) out[j] = -1;
+  if (m == n) {                                   // every token is selected
+    for (int j = t; j < n; j += TK_THREADS) out[j] = j;
+    return;
+  }
+  const float *row = scores + static_cast<int64_t>(r) * ld;
+  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+  // element (j, e) of this thread is row index j * TK_STEP + t * TK_PER + e, bit 4j + e
+  uint32_t lt_m = 0, b0_m = 0;                     // bins below b0; bin b0
+  float lo, scale;
+  uint32_t b0, k_rem, c0;
+  {
+    float x[TK_J][4];
+    uint32_t vm = 0;
+#pragma unroll
+    for (int j = 0; j < TK_J; ++j) vm |= row_value(row, vec, n, j * TK_STEP + t * TK_PER, x[j]) << (4 * j);
+    // row minimum and maximum
+    lo = INFINITY;
+    float hi = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < TK_J; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((vm >> (4 * j + e)) & 1) { lo = fminf(lo, x[j][e]); hi = fmaxf(hi, x[j][e]); }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      lo = fminf(lo, __shfl_xor(lo, o));
+      hi = fmaxf(hi, __shfl_xor(hi, o));
+    }
+    if (l == 0) { red[w] = lo; red[TK_THREADS / 64 + w] = hi; }
+    for (int b = t; b < TK_BINS; b += TK_THREADS) hist[b] = 0;
+    if (t == 0) tmp[44] = 0;
+    __syncthreads();
+    lo = red[0];
+    hi = red[TK_THREADS / 64];
+#pragma unroll
+    for (int i = 1; i < TK_THREADS / 64; ++i) { lo = fminf(lo, red[i]); hi = fmaxf(hi, red[TK_THREADS / 64 + i]); }
+    // a non-finite span (or one value) puts everything into one bin: still exact, only slower
+    const float span = hi - lo;
+    scale = (span > 0.f && span < INFINITY) ? 2047.0f / span : 0.f;
+    // 1. value-bin histogram (the bins are spread, so plain LDS atomics)
+#pragma unroll
+    for (int j = 0; j < TK_J; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((vm >> (4 * j + e)) & 1) atomicAdd(&hist[value_bin(x[j][e], lo, scale)], 1u);
+    __syncthreads();
+    uint32_t below0;
+    tk_pick(hist, TK_BINS, static_cast<uint32_t>(m), tmp, b0, below0);
+    k_rem = static_cast<uint32_t>(m) - below0;
+    c0 = hist[b0];
+#pragma unroll
+    for (int j = 0; j < TK_J; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((vm >> (4 * j + e)) & 1) {
+          const uint32_t bj = value_bin(x[j][e], lo, scale);
+          if (bj < b0) lt_m |= 1u << (4 * j + e);
+          else if (bj == b0) b0_m |= 1u << (4 * j + e);
+        }
+    // the threshold bin's keys go to LDS (in no particular order) when they fit
+    if (c0 != k_rem && c0 <= TK_RC) {
+#pragma unroll
+      for (int j = 0; j < TK_J; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool act = (b0_m >> (4 * j + e)) & 1;
+          const uint64_t ma = __ballot(act);
+          if (ma) {
+            const int lead = __ffsll(static_cast<unsigned long long>(ma)) - 1;
+            uint32_t base = 0;
+            if (l == lead) base = atomicAdd(&tmp[44], static_cast<uint32_t>(__popcll(ma)));
+            base = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(base), lead));
+            if (act) cand_key[base + static_cast<uint32_t>(__popcll(ma & ((1ull << l) - 1ull)))] = ~f32_key(x[j][e]);
+          }
+        }
+    }
+  }
+  const bool all_b0 = c0 == k_rem;                 // the whole threshold bin is selected
+  const bool in_lds = !all_b0 && c0 <= TK_RC;
+
+  // 2. the threshold key among the bin's elements: three radix passes over their order keys,
+  //    from LDS when they fit, else read again from the row (cached)
+  uint32_t prefix = 0, mask = 0, n_eq = 0;
+  if (!all_b0) {
+    for (int d = 0; d < 3; ++d) {
+      const int sh = d == 0 ? 21 : d == 1 ? 10 : 0;
+      const uint32_t dm = d == 2 ? 0x3FFu : 0x7FFu;
+      __syncthreads();
+      for (int b = t; b < TK_BINS; b += TK_THREADS) hist[b] = 0;
+      __syncthreads();
+      if (in_lds) {
+        for (uint32_t base = 0; base < c0; base += TK_THREADS) {
+          const uint32_t c = base + t;
+          const uint32_t kk = c < c0 ? cand_key[c] : 0u;
+          hist_add_peeled(hist, (kk >> sh) & dm, c < c0 && (kk & mask) == prefix);
+        }
+      } else {
+        for (int j = 0; j < TK_J; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool in = (b0_m >> (4 * j + e)) & 1;
+            const uint32_t kk = in ? row_key(row, j * TK_STEP + t * TK_PER + e) : 0u;
+            hist_add_peeled(hist, (kk >> sh) & dm, in && (kk & mask) == prefix);
+          }
+      }
+      __syncthreads();
+      uint32_t b, below;
+      tk_pick(hist, d == 2 ? 1024 : 2048, k_rem, tmp, b, below);
+      k_rem -= below;
+      prefix |= b << sh;
+      mask |= dm << sh;
+      if (d == 2) n_eq = hist[b];                  // keys equal to the threshold key
+    }
+  }
+
+  // 3. output in index order: bins below b0, then in b0 the keys below the threshold key and
+  //    the first k_rem keys equal to it (ranked in index order only when not all are taken)
+  uint32_t take_m = lt_m, eq_m = 0;
+  if (all_b0) {
+    take_m |= b0_m;
+  } else {
+    for (int j = 0; j < TK_J; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((b0_m >> (4 * j + e)) & 1) {
+          const uint32_t kk = row_key(row, j * TK_STEP + t * TK_PER + e);
+          if (kk < prefix) take_m |= 1u << (4 * j + e);
+          else if (kk == prefix) eq_m |= 1u << (4 * j + e);
+        }
+  }
+  const bool rank_ties = !all_b0 && n_eq != k_rem;
+  if (!rank_ties) {
+    take_m |= eq_m;
+  } else {
+    uint32_t eqc[TK_J], eqo[TK_J], tot;
+#pragma unroll
+    for (int j = 0; j < TK_J; ++j) eqc[j] = __popc((eq_m >> (4 * j)) & 0xFu);
+    group_excl_scan<TK_THREADS, TK_J>(eqc, eqo, gscan, &tot);
+#pragma unroll
+    for (int j = 0; j < TK_J; ++j) {
+      uint32_t er = eqo[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((eq_m >> (4 * j + e)) & 1) {
+          if (er < k_rem) take_m |= 1u << (4 * j + e);
+          ++er;
+        }
+    }
+  }
+  uint32_t takec[TK_J], poso[TK_J], tot2;
+#pragma unroll
+  for (int j = 0; j < TK_J; ++j) takec[j] = __popc((take_m >> (4 * j)) & 0xFu);
+  group_excl_scan<TK_THREADS, TK_J>(takec, poso, gscan, &tot2);
+#pragma unroll
+  for (int j = 0; j < TK_J; ++j) {
+    uint32_t pos = poso[j];
+    const int32_t i0 = j * TK_STEP + t * TK_PER;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((take_m >> (4 * j + e)) & 1) {
+        if (pos < static_cast<uint32_t>(k)) out[pos] = i0 + e;
+        ++pos;
+      }
+  }
+}
+
 size_t topk_ws_bytes(int32_t, int32_t) { return 256; }
 
 int launch_topk_rows(const float *scores, int64_t ld, const int32_t *len, int32_t n_rows,
@@ -361,6 +589,8 @@ int launch_topk_rows(const float *scores, int64_t ld, const int32_t *len, int32_
   if (n_rows == 0) return ECHO_OK;
   if (hist0)
     topk_row_kernel<true><<<n_rows, TK_THREADS, 0, st>>>(scores, ld, len, max_len, k, hist0, idx);
+  else if (max_len <= TK_BATCH)
+    topk_row_reg_kernel<<<n_rows, TK_THREADS, 0, st>>>(scores, ld, len, max_len, k, idx);
   else
     topk_row_kernel<false><<<n_rows, TK_THREADS, 0, st>>>(scores, ld, len, max_len, k, nullptr, idx);
   return check_launch("topk");

@@ -61,6 +61,15 @@ def test_topk_extreme_values():
     sc[1, ::3] = np.float32(1e-40)      # subnormals
     sc[1, 1::3] = -np.float32(1e-40)
     _check(sc, [6000, 6000], 150)
+    # infinities, and a row whose span overflows to infinity
+    sc = gen.random_scores(6, 3, 7000)
+    sc[0, 10:40] = np.inf
+    sc[0, 50:5000:7] = -np.inf
+    sc[1, :3000:2] = -np.inf
+    sc[2, 0] = np.float32(3e38)
+    sc[2, 1] = np.float32(-3e38)
+    _check(sc, [7000, 7000, 7000], 200)
+    _check(sc, [7000, 7000, 7000], 4000)
 
 
 def test_topk_decode_shapes_full():
