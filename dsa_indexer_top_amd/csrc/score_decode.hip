@@ -97,6 +97,7 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
   }
 
   int4 pre[SD_LOADS];
+  float pre_sc = 1.f;                  // the key scale of the token this lane scores, one chunk ahead
   auto fetch = [&](int32_t c0) {
 #pragma unroll
     for (int m = 0; m < SD_LOADS; ++m) {
@@ -107,6 +108,12 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
                                                  ((e & 7) << 4));
       else
         pre[m] = int4{0, 0, 0, 0};
+    }
+    if constexpr (HAS_SCALE) {
+      // fetched with the keys, so the multiply never waits on a load of its own (a wait there
+      // would also wait for the next chunk's keys)
+      const int32_t t = c0 + wv * 64 + tsel * 16 + j;
+      pre_sc = t < t_end ? k_scale[PAGED ? key_row(kp, r, kb, t) : kb + t] : 1.f;
     }
   };
 
@@ -123,6 +130,7 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
       const int e = tid + m * SD_THREADS;
       *reinterpret_cast<int4 *>(sb + swz(e >> 3, e & 7)) = pre[m];
     }
+    const float sc = pre_sc;
     __syncthreads();
     if (c0 + SD_CHUNK < t_end) fetch(c0 + SD_CHUNK);
 
@@ -138,7 +146,7 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
     const int32_t t_out = c0 + wv * 64 + tsel * 16 + j;
     const bool writer = t_out < t_end;
     if (writer) {
-      if constexpr (HAS_SCALE) s_out *= k_scale[PAGED ? key_row(kp, r, kb, t_out) : kb + t_out];
+      if constexpr (HAS_SCALE) s_out *= sc;
       srow[t_out] = s_out;
     }
     if constexpr (PREFETCH) {
