@@ -536,6 +536,8 @@ def run_section(name, args, timeout_s=900):
         cmd += ["--reserve", str(args.reserve)]
     if args.percentile is not None:
         cmd += ["--percentile", str(args.percentile)]
+    if args.cap_div is not None:
+        cmd += ["--cap-div", str(args.cap_div)]
     if args.no_cpu_baseline:
         cmd.append("--no-cpu-baseline")
     try:
@@ -674,7 +676,12 @@ def headline(args, torch, B, gen, DecodeRunner, cfg, prefetch):
     B.topk(sc, dkl, max_len, cfg.topk, sel, tws)
     pool = gen.make_pool_state(inp, sel.cpu().numpy(), host_kv, reserve=args.reserve)
     del sc, sel, tws
-    pf = None if args.percentile is None else dict(percentile=args.percentile)
+    pf = {}
+    if args.percentile is not None:
+        pf["percentile"] = args.percentile
+    if args.cap_div is not None:
+        pf["cap_div"] = args.cap_div
+    pf = pf or None
     rn = DecodeRunner(inp, pool, host_buf=hb, prefetch=prefetch, pf=pf)
     rn.capture()
     log("setup done in %.1fs" % (time.perf_counter() - t_setup))
@@ -835,6 +842,8 @@ def main():
                          "starts each of them this way, in a child process)")
     ap.add_argument("--reserve", type=int, default=None,
                     help="free GPU slots in the starting pool (default: the workload's own)")
+    ap.add_argument("--cap-div", type=int, default=None,
+                    help="prefetch cap divisor: a request prefetches at most ceil(L / cap_div) rows")
     ap.add_argument("--percentile", type=float, default=None,
                     help="prefetch threshold percentile of the score sample (default 95)")
     ap.add_argument("--probe", choices=("score", "copy", "prefill"), default=None,

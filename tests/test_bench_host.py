@@ -25,7 +25,7 @@ def test_more_than_one_gpu_is_refused():
 
 def _args(**kw):
     a = dict(workload="tiny", reserve=None, no_cpu_baseline=True, steps=3, warmup=2,
-             kernel_reps=4, prefetch="fused", percentile=None)
+             kernel_reps=4, prefetch="fused", percentile=None, cap_div=None)
     a.update(kw)
     return types.SimpleNamespace(**a)
 
