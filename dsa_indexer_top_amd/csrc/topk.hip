@@ -363,10 +363,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(
 // multiplication by a positive constant round monotonically), so every element of a lower bin
 // is selected for sure.  After the pick a thread keeps only two bit masks of its 32 elements
 // (lower bins, threshold bin); the threshold bin's keys are copied to LDS and resolved exactly
-// by three radix passes, the few of them a thread owns are read again for the output, and the
-// ties at the exact threshold key go to the lowest indices through an ordered block scan (only
-// when not all of them are taken).  Measured on MI355X over the 32768 causal rows of the
-// prefill: 2.49 ms against 2.56 ms for topk_row_kernel, which reads each row twice.
+// by one wave when at most 64 (pairwise ranks, no barrier), else by three radix passes; the few
+// of them a thread owns are read again for the output, and the ties at the exact threshold key
+// go to the lowest indices through an ordered block scan (only when not all of them are
+// taken).  Measured on MI355X over the 32768 causal rows of the prefill: 2.10 ms against 2.56 ms
+// for topk_row_kernel, which reads each row twice (2.49 ms with the radix passes always).
 
 // values of elements i0 .. i0+3 of a row (-0 folded to +0); returns the presence bits
 ECHO_DEV uint32_t row_value(const float *s, bool vec, int32_t n, int32_t i0, float (&x)[4]) {
@@ -495,10 +496,36 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(
   const bool all_b0 = c0 == k_rem;                 // the whole threshold bin is selected
   const bool in_lds = !all_b0 && c0 <= TK_RC;
 
-  // 2. the threshold key among the bin's elements: three radix passes over their order keys,
-  //    from LDS when they fit, else read again from the row (cached)
+  // 2. the threshold key among the bin's elements.  At most 64 of them (the usual case): one
+  //    wave ranks them by comparing every pair, with no barrier in between.  Otherwise three
+  //    radix passes over their order keys, from LDS when they fit, else read again from the
+  //    row (cached).
   uint32_t prefix = 0, mask = 0, n_eq = 0;
-  if (!all_b0) {
+  if (in_lds && c0 <= 64) {
+    __syncthreads();                               // the bin's keys are in LDS
+    if (w == 0) {
+      const uint32_t key = l < static_cast<int>(c0) ? cand_key[l] : ~0u;
+      uint32_t less = 0, eq = 0;
+      for (uint32_t i = 0; i < c0; ++i) {
+        const uint32_t o = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(key), static_cast<int>(i)));
+        less += o < key;
+        eq += o == key;
+      }
+      // the threshold key: k_rem - 1 keys of the bin are below it, or tied with it
+      const bool thr = l < static_cast<int>(c0) && less < k_rem && k_rem <= less + eq;
+      const uint64_t mt = __ballot(thr);
+      const int lead = __ffsll(static_cast<unsigned long long>(mt)) - 1;
+      if (l == lead) {
+        tmp[45] = key;
+        tmp[46] = k_rem - less;                    // ties to take at the threshold key
+        tmp[47] = eq;
+      }
+    }
+    __syncthreads();
+    prefix = tmp[45];
+    k_rem = tmp[46];
+    n_eq = tmp[47];
+  } else if (!all_b0) {
     for (int d = 0; d < 3; ++d) {
       const int sh = d == 0 ? 21 : d == 1 ? 10 : 0;
       const uint32_t dm = d == 2 ? 0x3FFu : 0x7FFu;
