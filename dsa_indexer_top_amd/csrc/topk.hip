@@ -366,8 +366,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(
 // by one wave when at most 64 (pairwise ranks, no barrier), else by three radix passes; the few
 // of them a thread owns are read again for the output, and the ties at the exact threshold key
 // go to the lowest indices through an ordered block scan (only when not all of them are
-// taken).  Measured on MI355X over the 32768 causal rows of the prefill: 2.10 ms against 2.56 ms
-// for topk_row_kernel, which reads each row twice (2.49 ms with the radix passes always).
+// taken).  Measured on MI355X over the 32768 causal rows of the prefill: 1.52 ms against 2.56 ms
+// for topk_row_kernel, which reads each row twice.
 
 // values of elements i0 .. i0+3 of a row (-0 folded to +0); returns the presence bits
 ECHO_DEV uint32_t row_value(const float *s, bool vec, int32_t n, int32_t i0, float (&x)[4]) {
@@ -401,7 +401,12 @@ constexpr int TK_RC = 4096;                         // threshold-bin elements re
 // Order key of element i of a row (-0 folded to +0; ascending key = descending score).
 ECHO_DEV uint32_t row_key(const float *row, int32_t i) { return ~f32_key(row[i]); }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(
+// J groups of four elements per thread: rows of at most J * 4096 scores.  J = 4 fits in 64
+// VGPRs, so two workgroups (rows) share a CU; J = 8 takes the rows above 16384 on their own.
+// (Measured on MI355X over the 32768 causal prefill rows: 1.52 ms against 2.10 ms with every
+// row in the J = 8 kernel.)
+template <int J, int WAVES_PER_SIMD>
+__global__ __launch_bounds__(TK_THREADS, WAVES_PER_SIMD) void topk_row_reg_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ len, int32_t max_len,
     int32_t k, int32_t *__restrict__ idx) {
   __shared__ uint32_t hist[TK_BINS];
@@ -413,6 +418,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(
   const int t = threadIdx.x;
   const int w = t >> 6, l = lane_id();
   const int32_t n = min(max(len[r], 0), min(max_len, TK_BATCH));
+  // rows of up to 16384 scores belong to the J = 4 launch, longer ones to the J = 8 launch
+  if ((J == 4) != (n <= 4 * TK_STEP)) return;
   const int32_t m = min(k, n);
   int32_t *out = idx + static_cast<int64_t>(r) * k;
   for (int j = m + t; j < k; j += TK_THREADS) out[j] = -1;
@@ -427,15 +434,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(
   float lo, scale;
   uint32_t b0, k_rem, c0;
   {
-    float x[TK_J][4];
+    float x[J][4];
     uint32_t vm = 0;
 #pragma unroll
-    for (int j = 0; j < TK_J; ++j) vm |= row_value(row, vec, n, j * TK_STEP + t * TK_PER, x[j]) << (4 * j);
+    for (int j = 0; j < J; ++j) vm |= row_value(row, vec, n, j * TK_STEP + t * TK_PER, x[j]) << (4 * j);
     // row minimum and maximum
     lo = INFINITY;
     float hi = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < TK_J; ++j)
+    for (int j = 0; j < J; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if ((vm >> (4 * j + e)) & 1) { lo = fminf(lo, x[j][e]); hi = fmaxf(hi, x[j][e]); }
@@ -457,7 +464,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(
     scale = (span > 0.f && span < INFINITY) ? 2047.0f / span : 0.f;
     // 1. value-bin histogram (the bins are spread, so plain LDS atomics)
 #pragma unroll
-    for (int j = 0; j < TK_J; ++j)
+    for (int j = 0; j < J; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if ((vm >> (4 * j + e)) & 1) atomicAdd(&hist[value_bin(x[j][e], lo, scale)], 1u);
@@ -467,7 +474,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(
     k_rem = static_cast<uint32_t>(m) - below0;
     c0 = hist[b0];
 #pragma unroll
-    for (int j = 0; j < TK_J; ++j)
+    for (int j = 0; j < J; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if ((vm >> (4 * j + e)) & 1) {
@@ -478,7 +485,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(
     // the threshold bin's keys go to LDS (in no particular order) when they fit
     if (c0 != k_rem && c0 <= TK_RC) {
 #pragma unroll
-      for (int j = 0; j < TK_J; ++j)
+      for (int j = 0; j < J; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool act = (b0_m >> (4 * j + e)) & 1;
@@ -539,7 +546,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(
           hist_add_peeled(hist, (kk >> sh) & dm, c < c0 && (kk & mask) == prefix);
         }
       } else {
-        for (int j = 0; j < TK_J; ++j)
+        for (int j = 0; j < J; ++j)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const bool in = (b0_m >> (4 * j + e)) & 1;
@@ -563,7 +570,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(
   if (all_b0) {
     take_m |= b0_m;
   } else {
-    for (int j = 0; j < TK_J; ++j)
+    for (int j = 0; j < J; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if ((b0_m >> (4 * j + e)) & 1) {
@@ -576,12 +583,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(
   if (!rank_ties) {
     take_m |= eq_m;
   } else {
-    uint32_t eqc[TK_J], eqo[TK_J], tot;
+    uint32_t eqc[J], eqo[J], tot;
 #pragma unroll
-    for (int j = 0; j < TK_J; ++j) eqc[j] = __popc((eq_m >> (4 * j)) & 0xFu);
-    group_excl_scan<TK_THREADS, TK_J>(eqc, eqo, gscan, &tot);
+    for (int j = 0; j < J; ++j) eqc[j] = __popc((eq_m >> (4 * j)) & 0xFu);
+    group_excl_scan<TK_THREADS, J>(eqc, eqo, gscan, &tot);
 #pragma unroll
-    for (int j = 0; j < TK_J; ++j) {
+    for (int j = 0; j < J; ++j) {
       uint32_t er = eqo[j];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -591,12 +598,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_reg_kernel(
         }
     }
   }
-  uint32_t takec[TK_J], poso[TK_J], tot2;
+  uint32_t takec[J], poso[J], tot2;
 #pragma unroll
-  for (int j = 0; j < TK_J; ++j) takec[j] = __popc((take_m >> (4 * j)) & 0xFu);
-  group_excl_scan<TK_THREADS, TK_J>(takec, poso, gscan, &tot2);
+  for (int j = 0; j < J; ++j) takec[j] = __popc((take_m >> (4 * j)) & 0xFu);
+  group_excl_scan<TK_THREADS, J>(takec, poso, gscan, &tot2);
 #pragma unroll
-  for (int j = 0; j < TK_J; ++j) {
+  for (int j = 0; j < J; ++j) {
     uint32_t pos = poso[j];
     const int32_t i0 = j * TK_STEP + t * TK_PER;
 #pragma unroll
@@ -616,8 +623,11 @@ int launch_topk_rows(const float *scores, int64_t ld, const int32_t *len, int32_
   if (n_rows == 0) return ECHO_OK;
   if (hist0)
     topk_row_kernel<true><<<n_rows, TK_THREADS, 0, st>>>(scores, ld, len, max_len, k, hist0, idx);
-  else if (max_len <= TK_BATCH)
-    topk_row_reg_kernel<<<n_rows, TK_THREADS, 0, st>>>(scores, ld, len, max_len, k, idx);
+  else if (max_len <= TK_BATCH) {
+    topk_row_reg_kernel<4, 8><<<n_rows, TK_THREADS, 0, st>>>(scores, ld, len, max_len, k, idx);
+    if (max_len > 4 * TK_STEP)
+      topk_row_reg_kernel<8, 4><<<n_rows, TK_THREADS, 0, st>>>(scores, ld, len, max_len, k, idx);
+  }
   else
     topk_row_kernel<false><<<n_rows, TK_THREADS, 0, st>>>(scores, ld, len, max_len, k, nullptr, idx);
   return check_launch("topk");

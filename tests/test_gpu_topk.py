@@ -36,6 +36,7 @@ def _check(scores, lens, k):
 @pytest.mark.parametrize("lens,k,ties", [
     ([1], 1, 0.0), ([0, 5, 4096], 256, 0.0), ([4095, 4096, 4097, 10000], 2048, 0.5),
     ([3000, 2048, 2047, 1], 2048, 0.9), ([65536] * 2, 2048, 0.3), ([8193, 12000], 7, 1.0),
+    ([16384, 16385, 32768, 9000, 1, 20000], 2048, 0.3),
     ([100000], 4096, 0.2)])
 def test_topk_random_with_ties(lens, k, ties):
     announce("topk", lens, k, ties)
