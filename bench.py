@@ -429,9 +429,9 @@ def cpu_baseline(inp, host_kv, pool_arrays, min_s=10.0, budget_s=30.0):
         sample = ("oracle decode step on requests 0..%d of the workload (%d tokens): scores in "
                   "float64, exact top-k, canonical pool step incl. recall copy" % (n - 1, tokens))
     else:
-        sample = ("%d repetitions of the whole oracle decode step (%d tokens each, float64 "
-                  "scores, exact top-k, pool step with the recall copy)" % (reps, tokens // reps))
-    return {"value": tokens / dt, "unit": "indexed tokens/s", "cores": int(cores),
+        sample = ("%d x the whole oracle decode step, %d tokens each (fp64 scores, exact top-k, "
+                  "pool step, recall copy)" % (reps, tokens // reps))
+    return {"value": round(tokens / dt, 1), "unit": "indexed tokens/s", "cores": int(cores),
             "cpu_model": cpu_model(), "kind": "oracle", "seconds": round(dt, 3), "sample": sample}
 
 
@@ -480,6 +480,68 @@ def summarize_extra(extra):
         else:
             out[name] = val
     return out
+
+
+# the keys of the headline measurement the one JSON line keeps (the rest goes to stderr)
+LINE_KEYS = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+             "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "error")
+
+
+def one_line(out, extra):
+    """The one JSON line: the contract's keys, the roofline, the step's link and HBM figures,
+    the CPU baseline and one short entry per secondary measurement, kept under 2000 characters
+    so that a reader of the output's tail gets it whole."""
+    line = {k: out[k] for k in LINE_KEYS if k in out}
+    cfg = out.get("config", {})
+    line["config"] = {k: cfg[k] for k in ("workload", "batch", "tokens", "topk", "prefetch",
+                                          "n_gpu_slots", "n_host_slots", "free_slots_at_start")
+                      if k in cfg}
+    if "roofline" in out:
+        rl = out["roofline"]
+        line["roofline"] = {k: rl[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic",
+                                               "us_per_launch") if k in rl}
+        line["roofline"]["kernel"] = "score_decode_kernel (the step's scoring launch)"
+    if "step" in out:
+        line["step"] = {k: out["step"][k] for k in ("hbm_frac", "link_floor_us") if k in out["step"]}
+    if "recall" in out:
+        rc = out["recall"]
+        line["recall"] = {"achieved_gbs": rc.get("achieved"), "link_gbs": rc.get("peak_measured_h2d"),
+                          "frac": rc.get("frac"), "rows": rc.get("rows"),
+                          "memcpy_baseline_us": rc.get("memcpy_baseline_us_median")}
+    if "cpu_baseline" in out:
+        line["cpu_baseline"] = {k: v for k, v in out["cpu_baseline"].items() if k != "seconds"}
+        if isinstance(line["cpu_baseline"].get("cpu_model"), str):
+            line["cpu_baseline"]["cpu_model"] = line["cpu_baseline"]["cpu_model"][:60]
+    short = {}
+    for name, val in extra.items():
+        if not isinstance(val, dict) or "error" in val:
+            short[name] = val
+        elif name in SIDE_WORKLOADS:
+            short[name] = {k: val.get(k) for k in ("us_per_step", "scoring_frac", "recall_frac_of_link")}
+            if name == "c5":
+                short[name]["memcpy_recall_us"] = val.get("memcpy_recall_us")
+            if "prefetch_modes" in val:
+                short[name]["modes_us"] = {m: v.get("us") for m, v in val["prefetch_modes"].items()}
+        elif name == "layers":
+            short[name] = {k: val.get(k) for k in ("us_per_model_step", "us_per_layer")}
+        elif name == "prefill":
+            short[name] = {k: val.get(k) for k in ("frac", "us_per_launch", "topk_rows_us")}
+        elif name == "prefill_offload":
+            short[name] = {k: val.get(k) for k in ("pairs_per_s", "thr_bin_median_shifted",
+                                                    "thr_bin_median_unshifted")}
+        elif name == "loop":
+            short[name] = {"ranged_us": val.get("us_per_step_median"), "hit_rate": val.get("hit_rate_median")}
+            for m in ("fused", "off"):
+                if isinstance(val.get(m), dict):
+                    short[name][m + "_us"] = val[m].get("us_per_step_median")
+            if isinstance(val.get("off"), dict):
+                short[name]["off_hit_rate"] = val["off"].get("hit_rate_median")
+        elif name == "prefetch_modes":
+            short[name] = {m: v["us"] for m, v in val.items() if isinstance(v, dict) and "us" in v}
+        else:
+            short[name] = val
+    line.update(short)
+    return line
 
 
 def compact_decode(res):
@@ -921,10 +983,10 @@ def main():
                         p["fused_launches_alone"]["us_median"], p["fused_launches_alone"]["plain_scoring_us"]))
         # full details on stderr; the one line keeps the summaries (per-step and per-chunk
         # arrays stay out of it), the headline's own keys first
+        log("details headline: %s" % json.dumps(out))
         for name, val in extra.items():
             log("details %s: %s" % (name, json.dumps(val)))
-        out.update(summarize_extra(extra))
-        print(json.dumps(out), flush=True)
+        print(json.dumps(one_line(out, summarize_extra(extra))), flush=True)
         return
 
     import torch
