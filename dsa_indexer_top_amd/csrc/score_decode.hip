@@ -273,7 +273,11 @@ int launch_score_decode(const uint8_t *q, const float *w, const uint8_t *k, cons
   const bool scoring = n_q > 0 && tok_hi > tok_lo;
   if (!scoring && n_side == 0) return ECHO_OK;
   const int32_t span = scoring ? tok_hi - tok_lo : 1;
-  const int32_t tpw = pick_tokens_per_wg(static_cast<int64_t>(n_q) * span, span, hist0 != nullptr);
+  int32_t tpw = pick_tokens_per_wg(static_cast<int64_t>(n_q) * span, span, hist0 != nullptr);
+  // a prefetching range launch of at least 512 x 4096 tokens runs one round of 4096-token
+  // workgroups instead of two of 2048, so it has one tail, not two (64 x 131072 tokens in four
+  // ranges, measured on MI355X: 1909 us per step against 1919)
+  if (pf && tpw == 2048 && static_cast<int64_t>(n_q) * span >= 512 * 4096) tpw = 4096;
   const int32_t gx = (span + tpw - 1) / tpw;
   const int64_t blocks = static_cast<int64_t>(n_side) + (scoring ? static_cast<int64_t>(gx) * n_q : 0);
   if (blocks > 0x7FFFFFFF) return fail(ECHO_EUNSUPPORTED, "score_decode: grid too large");
