@@ -80,3 +80,28 @@ def test_topk_decode_shapes_full():
     for r in range(64):                                  # every row against the oracle
         assert np.array_equal(got[r], oracle.topk_row(sc[r], 2048)), r
     assert (np.diff(got, axis=1) > 0).all()
+
+
+def test_topk_threshold_bin_paths():
+    # rows whose threshold bin (a linear bin of the value between the row's extremes) holds at
+    # most 64 elements, up to 4096 (resolved in LDS) and more (resolved from the row again)
+    announce("topk threshold-bin paths")
+    rng = np.random.default_rng(77)
+    n, k = 20000, 2048
+    rows = []
+    r0 = rng.standard_normal(n).astype(np.float32)                 # a few elements per bin
+    rows.append(r0)
+    # 600 distinct values in one bin, at the threshold: about 1700 scores lie above them
+    r1 = rng.standard_normal(n).astype(np.float32)
+    r1[rng.permutation(n)[:600]] = np.float32(1.35) + rng.random(600).astype(np.float32) * np.float32(1e-4)
+    rows.append(r1)
+    # 6000 distinct values in one bin, at the threshold: about 900 scores lie above them
+    r2 = rng.standard_normal(n).astype(np.float32) * np.float32(50)
+    r2[rng.permutation(n)[:6000]] = np.float32(75.0) + rng.random(6000).astype(np.float32) * np.float32(1e-3)
+    rows.append(r2)
+    r3 = np.full(n, 3.0, np.float32)                                 # 3000 ties straddling k
+    r3[:n - 3000] = rng.standard_normal(n - 3000).astype(np.float32)
+    r3[rng.permutation(n)[:500]] = np.float32(9.0)
+    rows.append(r3)
+    sc = np.stack(rows)
+    _check(sc, [n] * len(rows), k)
