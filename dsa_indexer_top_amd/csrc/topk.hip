@@ -16,6 +16,7 @@
 // If b0 holds more candidates than fit in LDS, digits 1-2 and the ordered output are done
 // with further passes over the row instead (same result, slower).
 #include <algorithm>
+#include <type_traits>
 
 #include "internal.hpp"
 
@@ -57,14 +58,15 @@ int launch_zero_i32(int32_t *p, int64_t n, hipStream_t st) {
 
 // Block-wide: the bin holding the k_rem-th smallest key of `hist` (nb bins) and the count of
 // keys in lower bins.  1024 threads, nb in {1024, 2048}.
+template <int NT = TK_THREADS>
 ECHO_DEV void tk_pick(const uint32_t *hist, int nb, uint32_t k_rem, uint32_t *tmp, uint32_t &bin,
                       uint32_t &below) {
-  const int per = nb / TK_THREADS;
+  const int per = nb / NT;
   const int t = threadIdx.x;
   uint32_t local = 0;
   for (int i = 0; i < per; ++i) local += hist[t * per + i];
   uint32_t total;
-  const uint32_t before = block_excl_scan<TK_THREADS>(local, tmp, &total);
+  const uint32_t before = block_excl_scan<NT>(local, tmp, &total);
   if (before < k_rem && k_rem <= before + local) {
     uint32_t cum = before;
     for (int i = 0; i < per; ++i) {
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(
 // by one wave when at most 64 (pairwise ranks, no barrier), else by three radix passes; the few
 // of them a thread owns are read again for the output, and the ties at the exact threshold key
 // go to the lowest indices through an ordered block scan (only when not all of them are
-// taken).  Measured on MI355X over the 32768 causal rows of the prefill: 1.52 ms against 2.56 ms
+// taken).  Measured on MI355X over the 32768 causal rows of the prefill: 1.21 ms against 2.56 ms
 // for topk_row_kernel, which reads each row twice.
 
 // values of elements i0 .. i0+3 of a row (-0 folded to +0); returns the presence bits
@@ -401,43 +403,46 @@ constexpr int TK_RC = 4096;                         // threshold-bin elements re
 // Order key of element i of a row (-0 folded to +0; ascending key = descending score).
 ECHO_DEV uint32_t row_key(const float *row, int32_t i) { return ~f32_key(row[i]); }
 
-// J groups of four elements per thread: rows of at most J * 4096 scores.  J = 4 fits in 64
-// VGPRs, so two workgroups (rows) share a CU; J = 8 takes the rows above 16384 on their own.
-// (Measured on MI355X over the 32768 causal prefill rows: 1.52 ms against 2.10 ms with every
-// row in the J = 8 kernel.)
-template <int J, int WAVES_PER_SIMD>
-__global__ __launch_bounds__(TK_THREADS, WAVES_PER_SIMD) void topk_row_reg_kernel(
+// NT threads with J groups of four elements each: rows of at most 4 * NT * J scores.  Both
+// instances run two workgroups (rows) per CU: J = 4 (rows of up to 16384 scores) fits in 63
+// VGPRs; J = 8 is held to 64 and spills some 46 VGPRs, which still pays: measured on MI355X over
+// the 32768 causal prefill rows, 1.21 ms against 1.53 ms with the J = 8 rows one per CU (and
+// 2.10 ms with every row one per CU).
+template <int NT, int J, int WAVES_PER_SIMD>
+__global__ __launch_bounds__(NT, WAVES_PER_SIMD) void topk_row_reg_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ len, int32_t max_len,
     int32_t k, int32_t *__restrict__ idx) {
+  constexpr int STEP = NT * TK_PER;                // elements per group of the whole workgroup
+  typedef typename std::conditional<(J * 4 <= 32), uint32_t, uint64_t>::type Mask;
   __shared__ uint32_t hist[TK_BINS];
   __shared__ uint32_t tmp[48];
   __shared__ uint32_t gscan[TK_SCAN_LDS];
-  __shared__ float red[2 * (TK_THREADS / 64)];
+  __shared__ float red[2 * (NT / 64)];
   __shared__ uint32_t cand_key[TK_RC];
   const int r = blockIdx.x;
   const int t = threadIdx.x;
   const int w = t >> 6, l = lane_id();
   const int32_t n = min(max(len[r], 0), min(max_len, TK_BATCH));
-  // rows of up to 16384 scores belong to the J = 4 launch, longer ones to the J = 8 launch
-  if ((J == 4) != (n <= 4 * TK_STEP)) return;
+  // rows of up to 4 * STEP scores belong to the J = 4 launch, longer ones to the J = 8 launch
+  if ((J == 4) != (n <= 4 * STEP)) return;
   const int32_t m = min(k, n);
   int32_t *out = idx + static_cast<int64_t>(r) * k;
-  for (int j = m + t; j < k; j += TK_THREADS) out[j] = -1;
+  for (int j = m + t; j < k; j += NT) out[j] = -1;
   if (m == n) {                                   // every token is selected
-    for (int j = t; j < n; j += TK_THREADS) out[j] = j;
+    for (int j = t; j < n; j += NT) out[j] = j;
     return;
   }
   const float *row = scores + static_cast<int64_t>(r) * ld;
   const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
-  // element (j, e) of this thread is row index j * TK_STEP + t * TK_PER + e, bit 4j + e
-  uint32_t lt_m = 0, b0_m = 0;                     // bins below b0; bin b0
+  // element (j, e) of this thread is row index j * STEP + t * TK_PER + e, bit 4j + e
+  Mask lt_m = 0, b0_m = 0;                         // bins below b0; bin b0
   float lo, scale;
   uint32_t b0, k_rem, c0;
   {
     float x[J][4];
-    uint32_t vm = 0;
+    Mask vm = 0;
 #pragma unroll
-    for (int j = 0; j < J; ++j) vm |= row_value(row, vec, n, j * TK_STEP + t * TK_PER, x[j]) << (4 * j);
+    for (int j = 0; j < J; ++j) vm |= static_cast<Mask>(row_value(row, vec, n, j * STEP + t * TK_PER, x[j])) << (4 * j);
     // row minimum and maximum
     lo = INFINITY;
     float hi = -INFINITY;
@@ -451,18 +456,22 @@ __global__ __launch_bounds__(TK_THREADS, WAVES_PER_SIMD) void topk_row_reg_kerne
       lo = fminf(lo, __shfl_xor(lo, o));
       hi = fmaxf(hi, __shfl_xor(hi, o));
     }
-    if (l == 0) { red[w] = lo; red[TK_THREADS / 64 + w] = hi; }
-    for (int b = t; b < TK_BINS; b += TK_THREADS) hist[b] = 0;
+    if (l == 0) { red[w] = lo; red[NT / 64 + w] = hi; }
+    for (int b = t; b < TK_BINS; b += NT) hist[b] = 0;
     if (t == 0) tmp[44] = 0;
     __syncthreads();
     lo = red[0];
-    hi = red[TK_THREADS / 64];
+    hi = red[NT / 64];
 #pragma unroll
-    for (int i = 1; i < TK_THREADS / 64; ++i) { lo = fminf(lo, red[i]); hi = fmaxf(hi, red[TK_THREADS / 64 + i]); }
+    for (int i = 1; i < NT / 64; ++i) { lo = fminf(lo, red[i]); hi = fmaxf(hi, red[NT / 64 + i]); }
     // a non-finite span (or one value) puts everything into one bin: still exact, only slower
     const float span = hi - lo;
     scale = (span > 0.f && span < INFINITY) ? 2047.0f / span : 0.f;
-    // 1. value-bin histogram (the bins are spread, so plain LDS atomics)
+    // 1. value-bin histogram (the bins are spread, so plain LDS atomics).  The empty asm steps
+    // here and before the masks keep the compiler from holding each value's bin across the
+    // phases, which at J = 8 would double the registers the values take.
+#pragma unroll
+    for (int j = 0; j < J; ++j) asm volatile("" : "+v"(x[j][0]), "+v"(x[j][1]), "+v"(x[j][2]), "+v"(x[j][3]));
 #pragma unroll
     for (int j = 0; j < J; ++j)
 #pragma unroll
@@ -470,17 +479,19 @@ __global__ __launch_bounds__(TK_THREADS, WAVES_PER_SIMD) void topk_row_reg_kerne
         if ((vm >> (4 * j + e)) & 1) atomicAdd(&hist[value_bin(x[j][e], lo, scale)], 1u);
     __syncthreads();
     uint32_t below0;
-    tk_pick(hist, TK_BINS, static_cast<uint32_t>(m), tmp, b0, below0);
+    tk_pick<NT>(hist, TK_BINS, static_cast<uint32_t>(m), tmp, b0, below0);
     k_rem = static_cast<uint32_t>(m) - below0;
     c0 = hist[b0];
+#pragma unroll
+    for (int j = 0; j < J; ++j) asm volatile("" : "+v"(x[j][0]), "+v"(x[j][1]), "+v"(x[j][2]), "+v"(x[j][3]));
 #pragma unroll
     for (int j = 0; j < J; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if ((vm >> (4 * j + e)) & 1) {
           const uint32_t bj = value_bin(x[j][e], lo, scale);
-          if (bj < b0) lt_m |= 1u << (4 * j + e);
-          else if (bj == b0) b0_m |= 1u << (4 * j + e);
+          if (bj < b0) lt_m |= Mask(1) << (4 * j + e);
+          else if (bj == b0) b0_m |= Mask(1) << (4 * j + e);
         }
     // the threshold bin's keys go to LDS (in no particular order) when they fit
     if (c0 != k_rem && c0 <= TK_RC) {
@@ -537,10 +548,10 @@ __global__ __launch_bounds__(TK_THREADS, WAVES_PER_SIMD) void topk_row_reg_kerne
       const int sh = d == 0 ? 21 : d == 1 ? 10 : 0;
       const uint32_t dm = d == 2 ? 0x3FFu : 0x7FFu;
       __syncthreads();
-      for (int b = t; b < TK_BINS; b += TK_THREADS) hist[b] = 0;
+      for (int b = t; b < TK_BINS; b += NT) hist[b] = 0;
       __syncthreads();
       if (in_lds) {
-        for (uint32_t base = 0; base < c0; base += TK_THREADS) {
+        for (uint32_t base = 0; base < c0; base += NT) {
           const uint32_t c = base + t;
           const uint32_t kk = c < c0 ? cand_key[c] : 0u;
           hist_add_peeled(hist, (kk >> sh) & dm, c < c0 && (kk & mask) == prefix);
@@ -550,13 +561,13 @@ __global__ __launch_bounds__(TK_THREADS, WAVES_PER_SIMD) void topk_row_reg_kerne
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const bool in = (b0_m >> (4 * j + e)) & 1;
-            const uint32_t kk = in ? row_key(row, j * TK_STEP + t * TK_PER + e) : 0u;
+            const uint32_t kk = in ? row_key(row, j * STEP + t * TK_PER + e) : 0u;
             hist_add_peeled(hist, (kk >> sh) & dm, in && (kk & mask) == prefix);
           }
       }
       __syncthreads();
       uint32_t b, below;
-      tk_pick(hist, d == 2 ? 1024 : 2048, k_rem, tmp, b, below);
+      tk_pick<NT>(hist, d == 2 ? 1024 : 2048, k_rem, tmp, b, below);
       k_rem -= below;
       prefix |= b << sh;
       mask |= dm << sh;
@@ -566,7 +577,7 @@ __global__ __launch_bounds__(TK_THREADS, WAVES_PER_SIMD) void topk_row_reg_kerne
 
   // 3. output in index order: bins below b0, then in b0 the keys below the threshold key and
   //    the first k_rem keys equal to it (ranked in index order only when not all are taken)
-  uint32_t take_m = lt_m, eq_m = 0;
+  Mask take_m = lt_m, eq_m = 0;
   if (all_b0) {
     take_m |= b0_m;
   } else {
@@ -574,9 +585,9 @@ __global__ __launch_bounds__(TK_THREADS, WAVES_PER_SIMD) void topk_row_reg_kerne
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if ((b0_m >> (4 * j + e)) & 1) {
-          const uint32_t kk = row_key(row, j * TK_STEP + t * TK_PER + e);
-          if (kk < prefix) take_m |= 1u << (4 * j + e);
-          else if (kk == prefix) eq_m |= 1u << (4 * j + e);
+          const uint32_t kk = row_key(row, j * STEP + t * TK_PER + e);
+          if (kk < prefix) take_m |= Mask(1) << (4 * j + e);
+          else if (kk == prefix) eq_m |= Mask(1) << (4 * j + e);
         }
   }
   const bool rank_ties = !all_b0 && n_eq != k_rem;
@@ -585,27 +596,27 @@ __global__ __launch_bounds__(TK_THREADS, WAVES_PER_SIMD) void topk_row_reg_kerne
   } else {
     uint32_t eqc[J], eqo[J], tot;
 #pragma unroll
-    for (int j = 0; j < J; ++j) eqc[j] = __popc((eq_m >> (4 * j)) & 0xFu);
-    group_excl_scan<TK_THREADS, J>(eqc, eqo, gscan, &tot);
+    for (int j = 0; j < J; ++j) eqc[j] = __popc(static_cast<uint32_t>((eq_m >> (4 * j)) & 0xFu));
+    group_excl_scan<NT, J>(eqc, eqo, gscan, &tot);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       uint32_t er = eqo[j];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if ((eq_m >> (4 * j + e)) & 1) {
-          if (er < k_rem) take_m |= 1u << (4 * j + e);
+          if (er < k_rem) take_m |= Mask(1) << (4 * j + e);
           ++er;
         }
     }
   }
   uint32_t takec[J], poso[J], tot2;
 #pragma unroll
-  for (int j = 0; j < J; ++j) takec[j] = __popc((take_m >> (4 * j)) & 0xFu);
-  group_excl_scan<TK_THREADS, J>(takec, poso, gscan, &tot2);
+  for (int j = 0; j < J; ++j) takec[j] = __popc(static_cast<uint32_t>((take_m >> (4 * j)) & 0xFu));
+  group_excl_scan<NT, J>(takec, poso, gscan, &tot2);
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     uint32_t pos = poso[j];
-    const int32_t i0 = j * TK_STEP + t * TK_PER;
+    const int32_t i0 = j * STEP + t * TK_PER;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if ((take_m >> (4 * j + e)) & 1) {
@@ -624,9 +635,9 @@ int launch_topk_rows(const float *scores, int64_t ld, const int32_t *len, int32_
   if (hist0)
     topk_row_kernel<true><<<n_rows, TK_THREADS, 0, st>>>(scores, ld, len, max_len, k, hist0, idx);
   else if (max_len <= TK_BATCH) {
-    topk_row_reg_kernel<4, 8><<<n_rows, TK_THREADS, 0, st>>>(scores, ld, len, max_len, k, idx);
-    if (max_len > 4 * TK_STEP)
-      topk_row_reg_kernel<8, 4><<<n_rows, TK_THREADS, 0, st>>>(scores, ld, len, max_len, k, idx);
+    topk_row_reg_kernel<1024, 4, 8><<<n_rows, 1024, 0, st>>>(scores, ld, len, max_len, k, idx);
+    if (max_len > 16384)
+      topk_row_reg_kernel<1024, 8, 8><<<n_rows, 1024, 0, st>>>(scores, ld, len, max_len, k, idx);
   }
   else
     topk_row_kernel<false><<<n_rows, TK_THREADS, 0, st>>>(scores, ld, len, max_len, k, nullptr, idx);
