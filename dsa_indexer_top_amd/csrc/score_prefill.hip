@@ -5,9 +5,9 @@
 // lim_t = min(n_k, q_pos0 + t + 1); the diagonal is included.
 //
 // Work split: one query per wave (its 64 x 128 FP8 q and 64 weights stay in VGPRs in MFMA
-// layout), 12 consecutive queries per 768-thread workgroup (3 waves per SIMD; a wave needs
-// about 150 VGPRs).  The workgroup streams the keys [0, lim of its last query) through three
-// LDS buffers of 192-key stages (24 KB each, filled with coalesced 16-byte loads into the
+// layout), 16 consecutive queries per 1024-thread workgroup (4 waves per SIMD; a wave needs
+// about 110 VGPRs).  The workgroup streams the keys [0, lim of its last query) through three
+// LDS buffers of 256-key stages (32 KB each, filled with coalesced 16-byte loads into the
 // swizzled layout the decode kernel uses; one barrier per stage): while stage n is scored,
 // stage n+1 is already in LDS and stage n+2 in registers.  Workgroups are launched heaviest
 // (latest queries) first.
@@ -20,8 +20,8 @@
 //   * the epilogue is two VALU instructions per element: the ReLU is an integer max on the
 //     float's bits (a negative float, -0 included, has its sign bit set and so is below 0 as an
 //     int32; this avoids the NaN canonicalisation an IEEE float max costs), then one FMA;
-//   * the MFMA of unit u+2 is issued before the epilogue of unit u, across tile, group and
-//     stage boundaries, so the matrix core multiplies while the VALU reduces;
+//   * the MFMA of unit u+PF_AHEAD is issued before the epilogue of unit u, across tile, group
+//     and stage boundaries, so the matrix core multiplies while the VALU reduces;
 //   * the four tiles' per-lane-group partial sums are combined with one butterfly of gfx950
 //     lane swaps (3 swaps + 3 adds per 64 keys), after which the 64 lanes hold 64 consecutive
 //     scores of the group.
@@ -31,12 +31,13 @@
 
 namespace echo {
 
-constexpr int PF_THREADS = 768;
-constexpr int PF_QPB = PF_THREADS / 64;                 // 12 queries per workgroup
-constexpr int PF_STAGE = 192;                           // keys per LDS stage (3 groups of 64)
-constexpr int PF_UNITS = PF_STAGE * D / 16;             // 1536 x 16 B
+constexpr int PF_THREADS = 1024;
+constexpr int PF_QPB = PF_THREADS / 64;                 // 16 queries per workgroup
+constexpr int PF_STAGE = 256;                           // keys per LDS stage (4 groups of 64)
+constexpr int PF_UNITS = PF_STAGE * D / 16;             // 2048 x 16 B
 constexpr int PF_LOADS = PF_UNITS / PF_THREADS;         // 2 per thread
-constexpr int PF_BUFS = 3;                              // stage buffers in LDS (72 KB)
+constexpr int PF_BUFS = 3;                              // stage buffers in LDS (96 KB)
+constexpr int PF_AHEAD = 2;                             // MFMAs in flight ahead of the epilogue
 static_assert(PF_STAGE % 64 == 0 && PF_UNITS % PF_THREADS == 0, "stage shape");
 
 
@@ -61,35 +62,49 @@ ECHO_DEV v8i tile_b(const uint8_t *sb, int tt, int g) {
 
 
 // One 64-key group of a wave: 16 units (4 tiles x 4 head blocks), one MFMA and 8 VALU
-// instructions each.  The MFMA of unit u+2 is issued before the epilogue of unit u, so the
-// matrix core multiplies while the VALU reduces and an epilogue never waits on the MFMA just
-// issued; ca and cb carry the two accumulator sets in flight and bt the B operand of the
-// current tile, from group to group and from stage to stage.  gb is the group's 64 keys in
-// LDS, nb the next group's (possibly in the next stage's buffer).  On entry ca, cb hold units
-// 0 and 1 of this group, on return those of the next one.  The body has no branch, so the
-// scheduling barriers hold within one basic block.  Returns this lane's score: key
-// 16*tsel + l%16 of the group.
+// instructions each.  The MFMA of unit u+PF_AHEAD is issued before the epilogue of unit u, so
+// the matrix core multiplies while the VALU reduces and an epilogue never waits on the MFMA
+// just issued; c[] carries the accumulator sets in flight (c[0] the oldest) and bt the B
+// operand of the current tile, from group to group and from stage to stage.  gb is the
+// group's 64 keys in LDS, nb the next group's (possibly in the next stage's buffer).  On entry
+// c[] holds units 0 .. PF_AHEAD-1 of this group, on return those of the next one.
+//
+// The order is pinned with empty asm statements, which the compiler keeps in program order
+// and which emit nothing: each MFMA takes its B operand from one, hands its result to the
+// next, and the epilogue reads its accumulators from that one and hands its sum to the next
+// unit's first.  Without them the compiler issued 12 of a group's 16 MFMAs back to back
+// before any epilogue, holding 12 accumulator sets (154 VGPRs, so 3 waves per SIMD instead
+// of 4).  The distance from an MFMA to the first read of its result stays PF_AHEAD units
+// (at least 17 instructions), beyond the result's latency.
 ECHO_DEV float prefill_group(const QOperand &qo, const uint8_t *gb, const uint8_t *nb, int j,
-                             int g, v8i &bt, v4f &ca, v4f &cb) {
+                             int g, v8i &bt, v4f (&c)[PF_AHEAD]) {
   float p[4];
+  float acc = 0.f;                    // the running sum of the previous unit
 #pragma unroll
   for (int tile = 0; tile < 4; ++tile) {
-    const v8i bn = tile < 3 ? tile_b(gb, (tile + 1) * 16 + j, g) : tile_b(nb, j, g);
-    float acc = 0.f;
+    v8i bn = tile < 3 ? tile_b(gb, (tile + 1) * 16 + j, g) : tile_b(nb, j, g);
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
-      // unit u+2 is head block hb+2 of this tile, or hb-2 of the next one
-      const v4f cn = unit_mfma(qo.qa[(hb + 2) & 3], hb < 2 ? bt : bn);
-      acc = unit_epilogue(qo.wr[hb], ca, acc);
-      ca = cb;
-      cb = cn;
-      // keep this order: hoisting every MFMA of the group to the top, which the scheduler
-      // otherwise does, holds 16 accumulator sets and spills the q operand
-      __builtin_amdgcn_sched_barrier(0);
+      // unit u+PF_AHEAD is head block hb+PF_AHEAD of this tile, or of the next one
+      const bool this_tile = hb + PF_AHEAD < 4;
+      v8i bb = this_tile ? bt : bn;
+      asm volatile("" : "+v"(bb), "+v"(acc));
+      if (hb == 0) {                  // the previous tile's sum is complete
+        if (tile > 0) p[tile - 1] = acc;
+        acc = 0.f;
+      }
+      v4f cn = unit_mfma(qo.qa[(hb + PF_AHEAD) & 3], bb);
+      if (this_tile) bt = bb; else bn = bb;
+      v4f co = c[0];
+      asm volatile("" : "+v"(cn), "+v"(co));
+      acc = unit_epilogue(qo.wr[hb], co, acc);
+#pragma unroll
+      for (int i = 0; i + 1 < PF_AHEAD; ++i) c[i] = c[i + 1];
+      c[PF_AHEAD - 1] = cn;
     }
-    p[tile] = acc;
     bt = bn;
   }
+  p[3] = acc;
   // lanes of groups {g, g^2} exchange so each keeps two tiles summed over both groups, then
   // groups {g, g^1} exchange so each keeps one tile summed over all four
   const float a = swap_sum32(p[0], p[2]);
@@ -156,11 +171,13 @@ __global__ __launch_bounds__(PF_THREADS) void score_prefill_kernel(
 
   const int ngw = (lim + 63) >> 6;                // 64-key groups this wave scores
   v8i bt = {0, 0, 0, 0, 0, 0, 0, 0};
-  v4f ca = {0.f, 0.f, 0.f, 0.f}, cb = ca;
+  v4f c[PF_AHEAD];
+#pragma unroll
+  for (int i = 0; i < PF_AHEAD; ++i) c[i] = v4f{0.f, 0.f, 0.f, 0.f};
   if (ngw > 0) {
     bt = tile_b(lds[0], j, g);
-    ca = unit_mfma(qo.qa[0], bt);
-    cb = unit_mfma(qo.qa[1], bt);
+#pragma unroll
+    for (int i = 0; i < PF_AHEAD; ++i) c[i] = unit_mfma(qo.qa[i], bt);
   }
   int cur = 0;
   for (int32_t c0 = 0; c0 < wg_lim; c0 += PF_STAGE) {
@@ -174,7 +191,7 @@ __global__ __launch_bounds__(PF_THREADS) void score_prefill_kernel(
       const int gi = G - G0;
       const uint8_t *gb = lds[cur] + gi * 64 * D;
       const uint8_t *nb = gi == PF_STAGE / 64 - 1 ? lds[nxt] : gb + 64 * D;
-      const float v = prefill_group(qo, gb, nb, j, g, bt, ca, cb);
+      const float v = prefill_group(qo, gb, nb, j, g, bt, c);
       const int32_t s = G * 64 + tsel * 16 + j;      // the group crossing lim is masked here
       if (s < lim) srow[s] = v;
     }

@@ -86,12 +86,16 @@ def _name_start(s, end):
 
 
 SHARED = re.compile(r"__shared__\s+([^;]*?)\b([A-Za-z_]\w*)\s*((?:\[[^\]]*\])*)\s*;")
+# An empty asm statement with register operands only pins the order of GPU instructions; the
+# CPU build drops it (x86 has no register class for an 8 x 32-bit operand).
+PIN = re.compile(r'asm\s+volatile\s*\(\s*""\s*:[^;]*\)\s*;')
 
 
 def transform(src):
     src = src.replace("#include <hip/hip_runtime.h>", '#include "hip_cpu.h"')
     src = src.replace("__builtin_amdgcn_", "emu_amdgcn_")
     src = src.replace("__builtin_nontemporal_load", "emu_nontemporal_load")
+    src = PIN.sub("((void)0);", src)
     src = SHARED.sub(lambda m: "static %s%s%s; static const bool %s_emu_lds = "
                      "(emu::lds_register(&%s, sizeof(%s)), true);" % (
                          m.group(1), m.group(2), m.group(3), m.group(2), m.group(2), m.group(2)),
