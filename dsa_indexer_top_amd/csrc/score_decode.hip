@@ -213,9 +213,15 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
     __syncthreads();
     // every eligible token counts towards the request's demand (total_cnt); the workgroup
     // lists as many of them as this call's share of the cap still allows (the cumulative
-    // share less what the step's earlier calls listed), claimed with a compare-and-swap on the
-    // call's list count (each failure means another workgroup took places, so the loop ends
-    // after at most `share` rounds)
+    // share less what the step's earlier calls listed).  It reserves places [pos, pos + want)
+    // with one atomic add on the call's list count, fills those below the share and gives the
+    // rest back.  The reserved runs are disjoint, so the places filled are exactly
+    // [0, min(share, all wants)); a workgroup that reserves after the one crossing the share
+    // gets pos >= share, since that one gives back only what lies past the share; and once
+    // every workgroup is done the count is the number listed.  (A compare-and-swap loop here
+    // made the request's workgroups, which end together, wait for one another: measured on
+    // MI355X at 64 x 131072 tokens in four ranges with a 98.4th-percentile threshold, each
+    // range's launch took about 66 us against 51 us with no token over the threshold.)
     if (threadIdx.x == 0) {
       const int32_t n_listed = pf_list[SD_PF_OVER + 2];
       const int32_t n_q = n_listed + pf_list[SD_PF_OVER + 1];
@@ -225,19 +231,10 @@ __global__ __launch_bounds__(SD_THREADS, 2) void score_decode_kernel(
         int32_t share = static_cast<int32_t>(static_cast<int64_t>(cap_r) * (pf.call + 1) / pf.n_calls);
         for (int c = 0; c < pf.call; ++c) share -= pf.before_cnt[static_cast<int64_t>(c) * pf.ld_before + r];
         const int32_t want = n_listed;
-        int32_t cur = *reinterpret_cast<volatile int32_t *>(&pf.cand_cnt[r]);
-        while (true) {
-          take = min(want, share - cur);
-          if (take <= 0) {
-            take = 0;
-            break;
-          }
-          const int32_t seen = atomicCAS(&pf.cand_cnt[r], cur, cur + take);
-          if (seen == cur) {
-            pos = cur;
-            break;
-          }
-          cur = seen;
+        if (want > 0) {
+          pos = atomicAdd(&pf.cand_cnt[r], want);
+          take = max(0, min(want, share - pos));
+          if (take < want) atomicSub(&pf.cand_cnt[r], want - take);
         }
       }
       pf_list[SD_PF_OVER + 3] = take;

@@ -174,9 +174,10 @@ int echo_index_scores_hist(const uint8_t *q, const float *w, const uint8_t *k,
  * the step (the page's global prefetch counter, bounded in proportion to the context length).
  * Each workgroup (a run of at most 4096 tokens of one request) collects its qualifying tokens
  * (at most 1024 of them for listing; any further ones are counted only) and, at its end, adds
- * their number to total_cnt[r] and lists as many as cap_r still allows, claiming places in the
- * list with a compare-and-swap on cand_cnt[r].  Which qualifying tokens are listed, and in
- * which order, depends on timing; the scores never do.  Because each call has its own list, a
+ * their number to total_cnt[r] and lists as many as cap_r still allows, reserving places in
+ * the list with an atomic add on cand_cnt[r] and giving back those past the cap (so cand_cnt[r]
+ * may run past the count while the call runs; after it, it is the number listed).  Which
+ * qualifying tokens are listed, and in which order, depends on timing; the scores never do.  Because each call has its own list, a
  * consumer that waits for this call sees a complete list (echo_prefetch_gather).
  *   theta [n_q] fp32; req_to_host [n_k] int32; host_to_gpu [n_host]; cand [n_q, cap] int32;
  *   cand_cnt [n_q] (zeroed by the caller before this call); total_cnt [n_q] (zeroed once per
