@@ -24,9 +24,9 @@
 // looks their residency up only at its end, with all of those loads in flight together, so the
 // streaming loop never waits on a lookup (measured on MI355X at 64 x 131072 tokens: per-chunk
 // lookups made each ranged scoring launch about twice as long as plain scoring).  The eligible
-// ones are then published with one atomic for the demand and one compare-and-swap claim on
-// the call's list, so the step's counters see one update per workgroup instead of one per
-// token.
+// ones are then published with one atomic for the demand and one atomic add that reserves
+// places on the call's list, so the step's counters see one update per workgroup instead of
+// one per token.
 //
 // Side work (SIDE): the launch may carry extra leading workgroups that do independent pool
 // work (priority statistics, a previous range's prefetch gather) while the scoring workgroups
