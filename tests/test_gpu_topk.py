@@ -84,7 +84,8 @@ def test_topk_decode_shapes_full():
 
 def test_topk_threshold_bin_paths():
     # rows whose threshold bin (a linear bin of the value between the row's extremes) holds at
-    # most 64 elements, up to 4096 (resolved in LDS) and more (resolved from the row again)
+    # most 64 elements, up to 4096 (resolved in LDS) and more (resolved from the row again), in
+    # both classes of rows (20000 scores and 16000 scores)
     announce("topk threshold-bin paths")
     rng = np.random.default_rng(77)
     n, k = 20000, 2048
@@ -103,5 +104,15 @@ def test_topk_threshold_bin_paths():
     r3[:n - 3000] = rng.standard_normal(n - 3000).astype(np.float32)
     r3[rng.permutation(n)[:500]] = np.float32(9.0)
     rows.append(r3)
+    # 2000 distinct values in one bin, at the threshold: about 460 scores lie above them
+    r4 = rng.standard_normal(n).astype(np.float32)
+    r4[rng.permutation(n)[:2000]] = np.float32(2.0) + rng.random(2000).astype(np.float32) * np.float32(1e-4)
+    rows.append(r4)
     sc = np.stack(rows)
     _check(sc, [n] * len(rows), k)
+    # such a bin in a row of 16000 scores: 2000 distinct values at the threshold, about 150
+    # scores above them
+    m = 16000
+    r5 = rng.standard_normal(m).astype(np.float32)
+    r5[rng.permutation(m)[:2000]] = np.float32(2.3) + rng.random(2000).astype(np.float32) * np.float32(1e-4)
+    _check(r5[None, :], [m], k)
