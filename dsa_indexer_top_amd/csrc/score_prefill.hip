@@ -4,16 +4,16 @@
 // Query rows t in [0, n_q) sit at absolute positions q_pos0 + t and see keys [0, lim_t),
 // lim_t = min(n_k, q_pos0 + t + 1); the diagonal is included.
 //
-// Work split: one query per wave (its 64 x 128 FP8 q and 64 weights stay in VGPRs in MFMA
-// layout), 16 consecutive queries per 1024-thread workgroup (4 waves per SIMD; a wave needs
-// about 110 VGPRs).  The workgroup streams the keys [0, lim of its last query) through three
-// LDS buffers of 256-key stages (32 KB each, filled with coalesced 16-byte loads into the
-// swizzled layout the decode kernel uses; one barrier per stage): while stage n is scored,
-// stage n+1 is already in LDS and stage n+2 in registers.  Workgroups are launched heaviest
-// (latest queries) first.
+// Work split: two consecutive queries per wave (their 64 x 128 FP8 q and 64 weights stay in
+// VGPRs in MFMA layout, and each B operand read from LDS serves both), 24 queries per
+// 768-thread workgroup (3 waves per SIMD).  The workgroup streams the keys [0, lim of its last
+// query) through three LDS buffers of 192-key stages (24 KB each, filled with coalesced 16-byte
+// loads into the swizzled layout the decode kernel uses; one barrier per stage): while stage n
+// is scored, stage n+1 is already in LDS and stage n+2 in registers.  Workgroups are launched
+// heaviest (latest queries) first.
 //
-// Per 64-key group a wave runs 16 units (four 16-key tiles x four 16-head blocks), each one
-// v_mfma_f32_16x16x128_f8f6f4 and its epilogue.  The kernel is bound by the ratio of epilogue
+// Per 64-key group a wave runs 32 units (four 16-key tiles x four 16-head blocks x two
+// queries), each one v_mfma_f32_16x16x128_f8f6f4 and its epilogue.  The kernel is bound by the ratio of epilogue
 // VALU work to MFMA work: every (head, key) product needs its ReLU and its weighted add, while
 // one MFMA covers 16 heads x 16 keys x 128 bytes in the time of about 8 wave-wide VALU
 // instructions.  So:
@@ -31,12 +31,13 @@
 
 namespace echo {
 
-constexpr int PF_THREADS = 1024;
-constexpr int PF_QPB = PF_THREADS / 64;                 // 16 queries per workgroup
-constexpr int PF_STAGE = 256;                           // keys per LDS stage (4 groups of 64)
-constexpr int PF_UNITS = PF_STAGE * D / 16;             // 2048 x 16 B
+constexpr int PF_THREADS = 768;
+constexpr int PF_QPW = 2;                               // queries per wave
+constexpr int PF_QPB = PF_THREADS / 64 * PF_QPW;        // 24 queries per workgroup
+constexpr int PF_STAGE = 192;                           // keys per LDS stage (3 groups of 64)
+constexpr int PF_UNITS = PF_STAGE * D / 16;             // 1536 x 16 B
 constexpr int PF_LOADS = PF_UNITS / PF_THREADS;         // 2 per thread
-constexpr int PF_BUFS = 3;                              // stage buffers in LDS (96 KB)
+constexpr int PF_BUFS = 3;                              // stage buffers in LDS (72 KB)
 constexpr int PF_AHEAD = 2;                             // MFMAs in flight ahead of the epilogue
 static_assert(PF_STAGE % 64 == 0 && PF_UNITS % PF_THREADS == 0, "stage shape");
 
@@ -61,55 +62,64 @@ ECHO_DEV v8i tile_b(const uint8_t *sb, int tt, int g) {
 }
 
 
-// One 64-key group of a wave: 16 units (4 tiles x 4 head blocks), one MFMA and 8 VALU
-// instructions each.  The MFMA of unit u+PF_AHEAD is issued before the epilogue of unit u, so
-// the matrix core multiplies while the VALU reduces and an epilogue never waits on the MFMA
-// just issued; c[] carries the accumulator sets in flight (c[0] the oldest) and bt the B
-// operand of the current tile, from group to group and from stage to stage.  gb is the
-// group's 64 keys in LDS, nb the next group's (possibly in the next stage's buffer).  On entry
-// c[] holds units 0 .. PF_AHEAD-1 of this group, on return those of the next one.
+// One 64-key group of a wave: 32 units (4 tiles x 4 head blocks x the wave's 2 queries), one
+// MFMA and 8 VALU instructions each, the two queries alternating so that each B operand read
+// from LDS serves two MFMAs.  The MFMA of unit u+PF_AHEAD is issued before the epilogue of unit
+// u, so the matrix core multiplies while the VALU reduces and an epilogue never waits on the
+// MFMA just issued; c[] carries the accumulator sets in flight (c[0] the oldest) and bt the B
+// operand of the current tile, from group to group and from stage to stage.  gb is the group's
+// 64 keys in LDS, nb the next group's (possibly in the next stage's buffer).  On entry c[]
+// holds units 0 .. PF_AHEAD-1 of this group, on return those of the next one.  v[q] returns
+// query q's score of key 16*tsel + l%16 of the group; each query's sum is taken in the same
+// order as with one query per wave.
 //
 // The order is pinned with empty asm statements, which the compiler keeps in program order
 // and which emit nothing: each MFMA takes its B operand from one, hands its result to the
 // next, and the epilogue reads its accumulators from that one and hands its sum to the next
-// unit's first.  Without them the compiler issued 12 of a group's 16 MFMAs back to back
-// before any epilogue, holding 12 accumulator sets (154 VGPRs, so 3 waves per SIMD instead
-// of 4).  The distance from an MFMA to the first read of its result stays PF_AHEAD units
-// (at least 17 instructions), beyond the result's latency.
-ECHO_DEV float prefill_group(const QOperand &qo, const uint8_t *gb, const uint8_t *nb, int j,
-                             int g, v8i &bt, v4f (&c)[PF_AHEAD]) {
-  float p[4];
-  float acc = 0.f;                    // the running sum of the previous unit
+// unit's first.  Without them the compiler issued most of a group's MFMAs back to back before
+// any epilogue, holding as many accumulator sets.  The distance from an MFMA to the first read
+// of its result stays PF_AHEAD units (at least 17 instructions), beyond the result's latency.
+ECHO_DEV void prefill_group(const QOperand (&qo)[PF_QPW], const uint8_t *gb, const uint8_t *nb,
+                            int j, int g, v8i &bt, v4f (&c)[PF_AHEAD], float (&v)[PF_QPW]) {
+  static_assert(PF_AHEAD == PF_QPW, "unit u+PF_AHEAD is the same query's next head block");
+  float p[PF_QPW][4];
+  float acc[PF_QPW] = {0.f, 0.f};      // the running sums of the previous units
 #pragma unroll
   for (int tile = 0; tile < 4; ++tile) {
     v8i bn = tile < 3 ? tile_b(gb, (tile + 1) * 16 + j, g) : tile_b(nb, j, g);
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
-      // unit u+PF_AHEAD is head block hb+PF_AHEAD of this tile, or of the next one
-      const bool this_tile = hb + PF_AHEAD < 4;
-      v8i bb = this_tile ? bt : bn;
-      asm volatile("" : "+v"(bb), "+v"(acc));
-      if (hb == 0) {                  // the previous tile's sum is complete
-        if (tile > 0) p[tile - 1] = acc;
-        acc = 0.f;
-      }
-      v4f cn = unit_mfma(qo.qa[(hb + PF_AHEAD) & 3], bb);
-      if (this_tile) bt = bb; else bn = bb;
-      v4f co = c[0];
-      asm volatile("" : "+v"(cn), "+v"(co));
-      acc = unit_epilogue(qo.wr[hb], co, acc);
 #pragma unroll
-      for (int i = 0; i + 1 < PF_AHEAD; ++i) c[i] = c[i + 1];
-      c[PF_AHEAD - 1] = cn;
+      for (int qi = 0; qi < PF_QPW; ++qi) {
+        // unit u+PF_AHEAD is head block hb+1 of the same query, in this tile or the next one
+        const bool this_tile = hb + 1 < 4;
+        v8i bb = this_tile ? bt : bn;
+        asm volatile("" : "+v"(bb), "+v"(acc[qi]));
+        if (hb == 0) {                  // this query's sum of the previous tile is complete
+          if (tile > 0) p[qi][tile - 1] = acc[qi];
+          acc[qi] = 0.f;
+        }
+        v4f cn = unit_mfma(qo[qi].qa[(hb + 1) & 3], bb);
+        if (this_tile) bt = bb; else bn = bb;
+        v4f co = c[0];
+        asm volatile("" : "+v"(cn), "+v"(co));
+        acc[qi] = unit_epilogue(qo[qi].wr[hb], co, acc[qi]);
+#pragma unroll
+        for (int i = 0; i + 1 < PF_AHEAD; ++i) c[i] = c[i + 1];
+        c[PF_AHEAD - 1] = cn;
+      }
     }
     bt = bn;
   }
-  p[3] = acc;
   // lanes of groups {g, g^2} exchange so each keeps two tiles summed over both groups, then
   // groups {g, g^1} exchange so each keeps one tile summed over all four
-  const float a = swap_sum32(p[0], p[2]);
-  const float b = swap_sum32(p[1], p[3]);
-  return swap_sum16(a, b);
+#pragma unroll
+  for (int qi = 0; qi < PF_QPW; ++qi) {
+    p[qi][3] = acc[qi];
+    const float a = swap_sum32(p[qi][0], p[qi][2]);
+    const float b = swap_sum32(p[qi][1], p[qi][3]);
+    v[qi] = swap_sum16(a, b);
+  }
 }
 
 __global__ __launch_bounds__(PF_THREADS) void score_prefill_kernel(
@@ -120,9 +130,12 @@ __global__ __launch_bounds__(PF_THREADS) void score_prefill_kernel(
   const int blk = nblk - 1 - static_cast<int>(blockIdx.x);     // heaviest first
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
   const int j = l & 15, g = l >> 4;
-  const int32_t t = blk * PF_QPB + __builtin_amdgcn_readfirstlane(wv);    // one query per wave
-  const bool active = t < n_q;
-  const int32_t lim = active ? min(n_k, q_pos0 + t + 1) : 0;
+  // the wave's queries t0 and t0 + 1 (a query past n_q scores with a copy of t0's operand and
+  // writes nothing)
+  const int32_t t0 = blk * PF_QPB + PF_QPW * __builtin_amdgcn_readfirstlane(wv);
+  int32_t lim[PF_QPW];
+#pragma unroll
+  for (int qi = 0; qi < PF_QPW; ++qi) lim[qi] = t0 + qi < n_q ? min(n_k, q_pos0 + t0 + qi + 1) : 0;
   const int32_t t_last = min(n_q - 1, blk * PF_QPB + PF_QPB - 1);
   const int32_t wg_lim = min(n_k, q_pos0 + t_last + 1);
   if (wg_lim <= 0) return;
@@ -137,9 +150,14 @@ __global__ __launch_bounds__(PF_THREADS) void score_prefill_kernel(
   const int flip16 = __builtin_amdgcn_readfirstlane(static_cast<int>(p16[0]));
   const int tsel = ((((g >> 1) ^ flip32) & 1) << 1) | ((g ^ flip16) & 1);
 
-  QOperand qo;
-  if (active) load_q_operand(q, w, t, qo);
-  float *__restrict__ srow = scores + static_cast<int64_t>(active ? t : 0) * ld;
+  QOperand qo[PF_QPW];
+  float *__restrict__ srow[PF_QPW];
+#pragma unroll
+  for (int qi = 0; qi < PF_QPW; ++qi) {
+    const int32_t tq = t0 + qi < n_q ? t0 + qi : min(t0, n_q - 1);
+    load_q_operand(q, w, tq, qo[qi]);
+    srow[qi] = scores + static_cast<int64_t>(tq) * ld;
+  }
 
   int4 pre[PF_LOADS];
   auto fetch = [&](int32_t c0) {
@@ -169,7 +187,7 @@ __global__ __launch_bounds__(PF_THREADS) void score_prefill_kernel(
   __syncthreads();
   if (PF_STAGE < wg_lim) fetch(PF_STAGE);
 
-  const int ngw = (lim + 63) >> 6;                // 64-key groups this wave scores
+  const int ngw = (max(lim[0], lim[1]) + 63) >> 6;   // 64-key groups this wave scores
   v8i bt = {0, 0, 0, 0, 0, 0, 0, 0};
   v4f c[PF_AHEAD];
 #pragma unroll
@@ -177,7 +195,7 @@ __global__ __launch_bounds__(PF_THREADS) void score_prefill_kernel(
   if (ngw > 0) {
     bt = tile_b(lds[0], j, g);
 #pragma unroll
-    for (int i = 0; i < PF_AHEAD; ++i) c[i] = unit_mfma(qo.qa[i], bt);
+    for (int i = 0; i < PF_AHEAD; ++i) c[i] = unit_mfma(qo[i].qa[0], bt);
   }
   int cur = 0;
   for (int32_t c0 = 0; c0 < wg_lim; c0 += PF_STAGE) {
@@ -191,9 +209,12 @@ __global__ __launch_bounds__(PF_THREADS) void score_prefill_kernel(
       const int gi = G - G0;
       const uint8_t *gb = lds[cur] + gi * 64 * D;
       const uint8_t *nb = gi == PF_STAGE / 64 - 1 ? lds[nxt] : gb + 64 * D;
-      const float v = prefill_group(qo, gb, nb, j, g, bt, c);
+      float v[PF_QPW];
+      prefill_group(qo, gb, nb, j, g, bt, c, v);
       const int32_t s = G * 64 + tsel * 16 + j;      // the group crossing lim is masked here
-      if (s < lim) srow[s] = v;
+#pragma unroll
+      for (int qi = 0; qi < PF_QPW; ++qi)
+        if (s < lim[qi]) srow[qi][s] = v[qi];
     }
     cur = nxt;
   }
