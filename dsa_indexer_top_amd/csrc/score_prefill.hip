@@ -130,8 +130,8 @@ __global__ __launch_bounds__(PF_THREADS) void score_prefill_kernel(
   const int blk = nblk - 1 - static_cast<int>(blockIdx.x);     // heaviest first
   const int tid = threadIdx.x, wv = tid >> 6, l = tid & 63;
   const int j = l & 15, g = l >> 4;
-  // the wave's queries t0 and t0 + 1 (a query past n_q scores with a copy of t0's operand and
-  // writes nothing)
+  // the wave's queries t0 and t0 + 1 (a query past n_q scores with a copy of the operand of
+  // query min(t0, n_q - 1) and writes nothing)
   const int32_t t0 = blk * PF_QPB + PF_QPW * __builtin_amdgcn_readfirstlane(wv);
   int32_t lim[PF_QPW];
 #pragma unroll
