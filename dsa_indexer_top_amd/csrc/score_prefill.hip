@@ -83,7 +83,7 @@ ECHO_DEV void prefill_group(const QOperand (&qo)[PF_QPW], const uint8_t *gb, con
                             int j, int g, v8i &bt, v4f (&c)[PF_AHEAD], float (&v)[PF_QPW]) {
   static_assert(PF_AHEAD == PF_QPW, "unit u+PF_AHEAD is the same query's next head block");
   float p[PF_QPW][4];
-  float acc[PF_QPW] = {0.f, 0.f};      // the running sums of the previous units
+  float acc[PF_QPW] = {};              // the running sums of the previous units
 #pragma unroll
   for (int tile = 0; tile < 4; ++tile) {
     v8i bn = tile < 3 ? tile_b(gb, (tile + 1) * 16 + j, g) : tile_b(nb, j, g);
@@ -187,7 +187,10 @@ __global__ __launch_bounds__(PF_THREADS) void score_prefill_kernel(
   __syncthreads();
   if (PF_STAGE < wg_lim) fetch(PF_STAGE);
 
-  const int ngw = (max(lim[0], lim[1]) + 63) >> 6;   // 64-key groups this wave scores
+  int32_t lim_w = 0;                              // the furthest limit of the wave's queries
+#pragma unroll
+  for (int qi = 0; qi < PF_QPW; ++qi) lim_w = max(lim_w, lim[qi]);
+  const int ngw = (lim_w + 63) >> 6;              // 64-key groups this wave scores
   v8i bt = {0, 0, 0, 0, 0, 0, 0, 0};
   v4f c[PF_AHEAD];
 #pragma unroll
