@@ -403,12 +403,16 @@ constexpr int TK_RC = 4096;                         // threshold-bin elements re
 // Order key of element i of a row (-0 folded to +0; ascending key = descending score).
 ECHO_DEV uint32_t row_key(const float *row, int32_t i) { return ~f32_key(row[i]); }
 
-// NT threads with J groups of four elements each: rows of at most 4 * NT * J scores.  Both
-// instances run two workgroups (rows) per CU: J = 4 (rows of up to 16384 scores) fits in 63
-// VGPRs; J = 8 is held to 64 and spills some 46 VGPRs, which still pays: measured on MI355X over
-// the 32768 causal prefill rows, 1.21 ms against 1.53 ms with the J = 8 rows one per CU (and
-// 2.10 ms with every row one per CU).
-template <int NT, int J, int WAVES_PER_SIMD>
+// NT threads with J groups of four elements each: rows of at most 4 * NT * J scores; a launch
+// takes the rows longer than N_LO that fit (the launches of a call split the rows between
+// them; a compile-time N_LO lets the compiler drop the range checks of the groups every such
+// row fills).  Every instance holds its values in at most 64 VGPRs, so 32 waves share a CU: two
+// rows of 1024 threads, four of 512.  NT = 512, J = 4 takes rows of up to 8192 scores; NT =
+// 1024 with J = 4 rows of up to 16384, in 63 VGPRs; J = 8 the longer ones, held to 64 VGPRs
+// with some 46 spilled, which still pays: measured on MI355X over the 32768 causal prefill
+// rows, 1.21 ms against 1.53 ms with the J = 8 rows one per CU (and 2.10 ms with every row one
+// per CU).
+template <int NT, int J, int WAVES_PER_SIMD, int N_LO>
 __global__ __launch_bounds__(NT, WAVES_PER_SIMD) void topk_row_reg_kernel(
     const float *__restrict__ scores, int64_t ld, const int32_t *__restrict__ len, int32_t max_len,
     int32_t k, int32_t *__restrict__ idx) {
@@ -423,8 +427,7 @@ __global__ __launch_bounds__(NT, WAVES_PER_SIMD) void topk_row_reg_kernel(
   const int t = threadIdx.x;
   const int w = t >> 6, l = lane_id();
   const int32_t n = min(max(len[r], 0), min(max_len, TK_BATCH));
-  // rows of up to 4 * STEP scores belong to the J = 4 launch, longer ones to the J = 8 launch
-  if ((J == 4) != (n <= 4 * STEP)) return;
+  if (n <= N_LO || n > J * STEP) return;           // another launch's row
   const int32_t m = min(k, n);
   int32_t *out = idx + static_cast<int64_t>(r) * k;
   for (int j = m + t; j < k; j += NT) out[j] = -1;
@@ -635,9 +638,11 @@ int launch_topk_rows(const float *scores, int64_t ld, const int32_t *len, int32_
   if (hist0)
     topk_row_kernel<true><<<n_rows, TK_THREADS, 0, st>>>(scores, ld, len, max_len, k, hist0, idx);
   else if (max_len <= TK_BATCH) {
-    topk_row_reg_kernel<1024, 4, 8><<<n_rows, 1024, 0, st>>>(scores, ld, len, max_len, k, idx);
+    topk_row_reg_kernel<512, 4, 8, -1><<<n_rows, 512, 0, st>>>(scores, ld, len, max_len, k, idx);
+    if (max_len > 8192)
+      topk_row_reg_kernel<1024, 4, 8, 8192><<<n_rows, 1024, 0, st>>>(scores, ld, len, max_len, k, idx);
     if (max_len > 16384)
-      topk_row_reg_kernel<1024, 8, 8><<<n_rows, 1024, 0, st>>>(scores, ld, len, max_len, k, idx);
+      topk_row_reg_kernel<1024, 8, 8, 16384><<<n_rows, 1024, 0, st>>>(scores, ld, len, max_len, k, idx);
   }
   else
     topk_row_kernel<false><<<n_rows, TK_THREADS, 0, st>>>(scores, ld, len, max_len, k, nullptr, idx);
