@@ -37,6 +37,7 @@ def _check(scores, lens, k):
     ([1], 1, 0.0), ([0, 5, 4096], 256, 0.0), ([4095, 4096, 4097, 10000], 2048, 0.5),
     ([3000, 2048, 2047, 1], 2048, 0.9), ([65536] * 2, 2048, 0.3), ([8193, 12000], 7, 1.0),
     ([16384, 16385, 32768, 9000, 1, 20000], 2048, 0.3),
+    ([2047, 2048, 2049, 8191, 8192, 8193, 16383], 700, 0.2),
     ([100000], 4096, 0.2)])
 def test_topk_random_with_ties(lens, k, ties):
     announce("topk", lens, k, ties)
