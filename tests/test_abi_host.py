@@ -81,6 +81,17 @@ def test_prefill_and_topk_argument_errors():
     assert L.echo_topk(None, 64, FAKE, 1, 64, 8, FAKE, None, 0, None) == B.ECHO_EINVAL
 
 
+def test_empty_calls_are_no_ops():
+    # no queries, no keys or no rows: ECHO_OK with nothing enqueued and nothing read or written
+    # (the pointers here are never valid, and no HIP runtime call is made)
+    L = B.lib()
+    assert L.echo_index_scores_prefill(FAKE, FAKE, FAKE, 0, 8, 0, FAKE, 8, None) == B.ECHO_OK
+    assert L.echo_index_scores_prefill(FAKE, FAKE, FAKE, 8, 0, 0, FAKE, 0, None) == B.ECHO_OK
+    assert L.echo_topk(FAKE, 64, FAKE, 0, 64, 8, FAKE, None, 0, None) == B.ECHO_OK
+    assert L.echo_index_scores(FAKE, FAKE, FAKE, None, FAKE, FAKE, 0, 16, FAKE, 16, None) == B.ECHO_OK
+    assert L.echo_index_scores(FAKE, FAKE, FAKE, None, FAKE, FAKE, 4, 0, FAKE, 0, None) == B.ECHO_OK
+
+
 def test_static_pool_entry_point_errors():
     # the no-allocation variant rejects, before touching the runtime, what the plain entry point
     # rejects, and any size whose workspace would not fit its fixed scratch array
