@@ -99,7 +99,8 @@ def test_decode_tiny_eager_exact():
 @pytest.mark.parametrize("one_stream", [False, True])
 @pytest.mark.parametrize("lens,k,hit,div", [([1, 300, 5000], 256, 0.6, 4),
                                             ([2048, 2047, 2049], 2048, 0.25, 1),
-                                            ([0, 70, 4097], 64, 0.6, 4)])
+                                            ([0, 70, 4097], 64, 0.6, 4),
+                                            ([0, 1, 0], 64, 0.6, 4)])
 def test_decode_small_ragged_exact(lens, k, hit, div, one_stream):
     announce("decode small ragged", lens, k, "one stream" if one_stream else "two streams")
     cfg = gen.DecodeConfig("s", len(lens), 0, k, "int", False, hit, div, seed=31 + k)
